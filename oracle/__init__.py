@@ -1,0 +1,160 @@
+"""fp64 CPU oracle for paged-attention decode.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+benchmark's CPU-baseline leg use it; the product path never imports it. It
+shares no code with the HIP library (``pa_oracle.c`` includes nothing from it
+and is built by gcc, not hipcc).
+
+Functions take numpy arrays in the layouts the decode problem fixes:
+q [B, Tq, Hq, D]; caches [num_blocks, block_size, Hkv, D]; int8 scales
+[num_blocks, block_size, Hkv]; block_table [B, max_blocks] int32; seq_lens [B]
+int32. bfloat16 data is passed as its uint16 bit patterns.
+
+Pins (see ``tests/test_oracle_pins.py``): Decimal brute force, closed forms
+(single key, constant V, zero query), dense contiguous attention, block-table
+permutation, GQA = repeated-KV MHA, causal = virtual batch, split = unsplit,
+prefix sharing, linearity, torch SDPA in fp64, int8 round trip and bound.
+Every function here is pinned by at least one of them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pa_oracle.c")
+_LIB = os.path.join(_HERE, "_pa_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+DTYPE_CODE = {"f32": 0, "bf16": 1, "i8": 2}
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain IEEE arithmetic, no fast-math)."""
+    if not force and os.path.exists(_LIB):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-fPIC",
+           "-shared", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB):
+                build()
+            lib = ctypes.CDLL(_LIB)
+            P, I, I64, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+            lib.pa_oracle_cache_write.argtypes = [P, P, I, P, I64, P, P, I, P, P, I64, I, I, I]
+            lib.pa_oracle_cache_write.restype = I
+            dec = [P, I, I, I, I, I, I, P, P, I, P, P, I, P, I, P, F]
+            lib.pa_oracle_decode.argtypes = dec + [P, I64, P, P, I]
+            lib.pa_oracle_decode.restype = I
+            lib.pa_oracle_decode_split.argtypes = dec + [I, P, I64, P, P, I]
+            lib.pa_oracle_decode_split.restype = I
+            lib.pa_oracle_max_threads.restype = I
+            _lib = lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def max_threads() -> int:
+    return int(_load().pa_oracle_max_threads())
+
+
+def _dtype_of(a: np.ndarray) -> str:
+    if a.dtype == np.float32:
+        return "f32"
+    if a.dtype == np.uint16:
+        return "bf16"
+    if a.dtype == np.int8:
+        return "i8"
+    raise TypeError("unsupported array dtype %s" % a.dtype)
+
+
+def alloc_cache(num_blocks: int, block_size: int, Hkv: int, D: int, cache_dtype: str):
+    """Zeroed host cache arrays (k, v, k_scale, v_scale) in the cache layout."""
+    npdt = {"f32": np.float32, "bf16": np.uint16, "i8": np.int8}[cache_dtype]
+    shape = (num_blocks, block_size, Hkv, D)
+    k = np.zeros(shape, npdt)
+    v = np.zeros(shape, npdt)
+    ks = vs = None
+    if cache_dtype == "i8":
+        ks = np.zeros(shape[:3], np.float32)
+        vs = np.zeros(shape[:3], np.float32)
+    return k, v, ks, vs
+
+
+def cache_write(k_src: np.ndarray, v_src: np.ndarray, slot_mapping: np.ndarray, k_cache: np.ndarray,
+                v_cache: np.ndarray, k_scale: Optional[np.ndarray] = None,
+                v_scale: Optional[np.ndarray] = None) -> None:
+    """Store source rows [N, Hkv, D] into the paged caches at slot_mapping (in place)."""
+    lib = _load()
+    src_dt = _dtype_of(k_src)
+    cache_dt = _dtype_of(k_cache)
+    assert k_src.dtype == v_src.dtype and k_cache.dtype == v_cache.dtype
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    nb, bs, Hkv, D = k_cache.shape
+    k_src = _c(k_src, k_src.dtype)
+    v_src = _c(v_src, v_src.dtype)
+    slots = _c(slot_mapping, np.int64)
+    N = slots.shape[0]
+    assert k_src.shape == (N, Hkv, D) and v_src.shape == (N, Hkv, D)
+    rc = lib.pa_oracle_cache_write(_ptr(k_src), _ptr(v_src), DTYPE_CODE[src_dt], _ptr(slots), N,
+                                   _ptr(k_cache), _ptr(v_cache), DTYPE_CODE[cache_dt], _ptr(k_scale),
+                                   _ptr(v_scale), nb, bs, Hkv, D)
+    if rc != 0:
+        raise ValueError("oracle cache_write failed: %d" % rc)
+
+
+def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_table: np.ndarray,
+           seq_lens: np.ndarray, softmax_scale: float, k_scale: Optional[np.ndarray] = None,
+           v_scale: Optional[np.ndarray] = None, partition_size: int = 0,
+           rows: Optional[Sequence[int]] = None, nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """fp64 decode. Returns (out [B, Tq, Hq, D], lse [B, Tq, Hq]).
+
+    partition_size > 0 runs the split-K path (partials merged by log-sum-exp)
+    instead of the plain definition. rows (flat ids (b*Tq + t)*Hq + h) limits
+    the work to those rows; the other entries are NaN.
+    """
+    lib = _load()
+    q = np.ascontiguousarray(q)
+    B, Tq, Hq, D = q.shape
+    nb, bs, Hkv, D2 = k_cache.shape
+    assert D2 == D and v_cache.shape == k_cache.shape
+    table = _c(block_table, np.int32)
+    lens = _c(seq_lens, np.int32)
+    assert table.shape[0] == B and lens.shape == (B,)
+    kv_dt = _dtype_of(k_cache)
+    out = np.full((B, Tq, Hq, D), np.nan)
+    lse = np.full((B, Tq, Hq), np.nan)
+    rows_arr = None if rows is None else _c(rows, np.int64)
+    nrows = 0 if rows_arr is None else rows_arr.shape[0]
+    common = [_ptr(q), DTYPE_CODE[_dtype_of(q)], B, Tq, Hq, Hkv, D, _ptr(np.ascontiguousarray(k_cache)),
+              _ptr(np.ascontiguousarray(v_cache)), DTYPE_CODE[kv_dt], _ptr(k_scale), _ptr(v_scale), bs,
+              _ptr(table), table.shape[1], _ptr(lens), ctypes.c_float(softmax_scale)]
+    if partition_size > 0:
+        rc = lib.pa_oracle_decode_split(*common, partition_size, _ptr(rows_arr), nrows, _ptr(out), _ptr(lse),
+                                        nthreads)
+    else:
+        rc = lib.pa_oracle_decode(*common, _ptr(rows_arr), nrows, _ptr(out), _ptr(lse), nthreads)
+    if rc != 0:
+        raise ValueError("oracle decode failed: %d" % rc)
+    return out, lse

@@ -1,0 +1,330 @@
+/*
+ * Paged-attention decode oracle: plain, slow, fp64 CPU code.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the independent reference the HIP
+ * kernels are checked against. Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load it; the product path never does. It
+ * includes no header and shares no code with the GPU library.
+ *
+ * What it computes, and where the pages say so:
+ *  - PagedAttention: each sequence's keys and values live in fixed-size blocks
+ *    reached through a per-sequence block table (nvllm page, "About": the
+ *    PagedAttention citation; 1Cat-vLLM docs index, feature list: "efficient
+ *    management of attention key and value memory with PagedAttention").
+ *  - Decode attention verified against an exact-softmax oracle (vllm-sm70
+ *    page, "Why", Attention bullet). The softmax here is materialised in full
+ *    over all visible keys, in fp64, never computed online.
+ *  - Speculative positions as a virtual batch (same bullet): query token t of
+ *    Tq new tokens sees keys 0 .. L_b - Tq + t, i.e. it is a one-token decode
+ *    of a sequence of length L_b - Tq + t + 1.
+ *  - Split-K with a log-sum-exp merge (same bullet, "split-K paged decode";
+ *    nvllm page, "Acknowledgments", b12x: "split-KV merge"): decode_split
+ *    below follows those steps and must equal the plain definition.
+ *  - int8 KV cache (vllm-sm70 page, "Why" and model table: int8 KV cache):
+ *    symmetric, one fp32 scale per (token, kv head) = max|x| / 127.
+ *
+ * Readings where the pages are silent (each also listed with the tests):
+ *  - seq_lens counts the Tq new tokens, whose K/V are already in the cache;
+ *  - query head h uses kv head h / (Hq / Hkv) (contiguous groups);
+ *  - a row with no visible key gives out = 0 and lse = -inf;
+ *  - int8: s = fp32(amax / 127); code = clamp(rint_half_even(fp32(x / s)),
+ *    -127, 127); amax = 0 gives s = 0 and all codes 0;
+ *  - the dequantised key/value is code * scale, formed exactly in fp64.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_F32 = 0, OR_BF16 = 1, OR_I8 = 2 };
+
+static float bits_to_float(uint32_t u) {
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static uint32_t float_to_bits(float f) {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return u;
+}
+
+/* bfloat16 is the top half of an IEEE binary32: widening is exact. */
+static double bf16_to_double(uint16_t b) { return (double)bits_to_float((uint32_t)b << 16); }
+
+/* binary32 -> bfloat16, round to nearest, ties to even (finite inputs; a NaN
+ * keeps a quiet-NaN pattern). */
+static uint16_t float_to_bf16_rne(float f) {
+    uint32_t u = float_to_bits(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+/* One element of a query or a source row, as the value it stands for. */
+static double elem(const void* base, int dtype, int64_t i) {
+    switch (dtype) {
+    case OR_F32: return (double)((const float*)base)[i];
+    case OR_BF16: return bf16_to_double(((const uint16_t*)base)[i]);
+    default: return NAN;
+    }
+}
+
+/* Element d of cache row `row` (row = (block * bs + offset) * Hkv + g),
+ * dequantised: for int8 the exact product code * scale in fp64. */
+static double cache_elem(const void* cache, int dtype, const float* scale, int64_t row, int D, int d) {
+    int64_t i = row * (int64_t)D + d;
+    switch (dtype) {
+    case OR_F32: return (double)((const float*)cache)[i];
+    case OR_BF16: return bf16_to_double(((const uint16_t*)cache)[i]);
+    case OR_I8: return (double)((const int8_t*)cache)[i] * (double)scale[row];
+    default: return NAN;
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Cache writer. For every source token i with slot_mapping[i] >= 0 and every
+ * kv head g, row x = src[i, g, :] goes to cache row (slot / bs, slot % bs, g).
+ * f32->f32 and bf16->bf16 copy bits; bf16->f32 widens; f32->bf16 rounds to
+ * nearest even; ->int8 quantises symmetrically per (token, kv head).
+ * Returns 0, or -1 on an unsupported dtype pair.
+ */
+int pa_oracle_cache_write(const void* k_src, const void* v_src, int src_dtype, const int64_t* slot_mapping,
+                          int64_t num_tokens, void* k_cache, void* v_cache, int cache_dtype, float* k_scale,
+                          float* v_scale, int64_t num_blocks, int block_size, int Hkv, int D) {
+    if (src_dtype != OR_F32 && src_dtype != OR_BF16) return -1;
+    if (cache_dtype != OR_F32 && cache_dtype != OR_BF16 && cache_dtype != OR_I8) return -1;
+    for (int which = 0; which < 2; ++which) {
+        const void* src = which ? v_src : k_src;
+        void* cache = which ? v_cache : k_cache;
+        float* scale = which ? v_scale : k_scale;
+        for (int64_t i = 0; i < num_tokens; ++i) {
+            int64_t slot = slot_mapping[i];
+            if (slot < 0) continue;
+            if (slot >= num_blocks * block_size) return -2;
+            int64_t blk = slot / block_size, off = slot % block_size;
+            for (int g = 0; g < Hkv; ++g) {
+                int64_t s0 = (i * Hkv + g) * (int64_t)D;
+                int64_t row = (blk * block_size + off) * Hkv + g;
+                int64_t d0 = row * (int64_t)D;
+                if (cache_dtype == OR_I8) {
+                    float amax = 0.0f;
+                    for (int d = 0; d < D; ++d) {
+                        float x = (float)elem(src, src_dtype, s0 + d); /* exact: source is f32 or bf16 */
+                        float ax = fabsf(x);
+                        if (ax > amax) amax = ax;
+                    }
+                    float s = amax / 127.0f; /* binary32 division, correctly rounded */
+                    scale[row] = s;
+                    for (int d = 0; d < D; ++d) {
+                        float x = (float)elem(src, src_dtype, s0 + d);
+                        int c = 0;
+                        if (amax != 0.0f) {
+                            float qf = x / s; /* binary32 quotient first */
+                            float r = rintf(qf); /* then nearest integer, ties to even */
+                            if (r > 127.0f) r = 127.0f;
+                            if (r < -127.0f) r = -127.0f;
+                            c = (int)r;
+                        }
+                        ((int8_t*)cache)[d0 + d] = (int8_t)c;
+                    }
+                } else if (cache_dtype == src_dtype) {
+                    size_t eb = cache_dtype == OR_F32 ? 4 : 2;
+                    memcpy((char*)cache + d0 * eb, (const char*)src + s0 * eb, (size_t)D * eb);
+                } else if (cache_dtype == OR_F32) { /* bf16 -> f32 */
+                    for (int d = 0; d < D; ++d) ((float*)cache)[d0 + d] = (float)elem(src, src_dtype, s0 + d);
+                } else { /* f32 -> bf16 */
+                    for (int d = 0; d < D; ++d)
+                        ((uint16_t*)cache)[d0 + d] = float_to_bf16_rne(((const float*)src)[s0 + d]);
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/* Shared argument bundle for the two decode entry points. */
+typedef struct {
+    const void* q;
+    int q_dtype, B, Tq, Hq, Hkv, D;
+    const void *k_cache, *v_cache;
+    int kv_dtype;
+    const float *k_scale, *v_scale;
+    int block_size;
+    const int32_t* block_table;
+    int max_blocks;
+    const int32_t* seq_lens;
+    float softmax_scale;
+} args_t;
+
+/* Logits of query row (b, t, h) against its first n keys, in key order. */
+static void row_logits(const args_t* a, int b, int t, int h, int64_t n, double* s) {
+    int G = a->Hq / a->Hkv, g = h / G;
+    const int64_t qoff = (((int64_t)b * a->Tq + t) * a->Hq + h) * a->D;
+    for (int64_t j = 0; j < n; ++j) {
+        int64_t blk = a->block_table[(int64_t)b * a->max_blocks + j / a->block_size];
+        int64_t row = (blk * a->block_size + j % a->block_size) * a->Hkv + g;
+        double dot = 0.0;
+        for (int d = 0; d < a->D; ++d)
+            dot += elem(a->q, a->q_dtype, qoff + d) * cache_elem(a->k_cache, a->kv_dtype, a->k_scale, row, a->D, d);
+        s[j] = (double)a->softmax_scale * dot;
+    }
+}
+
+static void value_row_axpy(const args_t* a, int b, int g, int64_t j, double w, double* acc) {
+    int64_t blk = a->block_table[(int64_t)b * a->max_blocks + j / a->block_size];
+    int64_t row = (blk * a->block_size + j % a->block_size) * a->Hkv + g;
+    for (int d = 0; d < a->D; ++d) acc[d] += w * cache_elem(a->v_cache, a->kv_dtype, a->v_scale, row, a->D, d);
+}
+
+/* Number of keys query token t of sequence b sees (causal inside the Tq new
+ * tokens, which are the last Tq positions of the sequence). */
+static int64_t visible_keys(const args_t* a, int b, int t) {
+    return (int64_t)a->seq_lens[b] - a->Tq + t + 1;
+}
+
+/* Plain definition: out = softmax(scale * q K^T) V over the visible keys,
+ * softmax materialised in full. `rows` selects flat row ids
+ * ((b * Tq + t) * Hq + h); NULL means every row. out/lse are indexed by the
+ * flat row id. */
+static void decode_row_plain(const args_t* a, int64_t r, double* out, double* lse) {
+    int h = (int)(r % a->Hq), t = (int)((r / a->Hq) % a->Tq), b = (int)(r / ((int64_t)a->Hq * a->Tq));
+    int G = a->Hq / a->Hkv, g = h / G;
+    double* o = out + r * a->D;
+    int64_t n = visible_keys(a, b, t);
+    for (int d = 0; d < a->D; ++d) o[d] = 0.0;
+    if (n <= 0) {
+        lse[r] = -INFINITY;
+        return;
+    }
+    double* s = (double*)malloc((size_t)n * sizeof(double));
+    row_logits(a, b, t, h, n, s);
+    double M = -INFINITY;
+    for (int64_t j = 0; j < n; ++j)
+        if (s[j] > M) M = s[j];
+    double Z = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        s[j] = exp(s[j] - M); /* unnormalised weight */
+        Z += s[j];
+    }
+    for (int64_t j = 0; j < n; ++j) value_row_axpy(a, b, g, j, s[j], o);
+    for (int d = 0; d < a->D; ++d) o[d] /= Z;
+    lse[r] = M + log(Z);
+    free(s);
+}
+
+/* Split path: keys of a row split into partitions [iP, (i+1)P); each keeps
+ * its own max m_i, sum l_i and normalised output o_i; the merge weighs o_i by
+ * l_i * exp(m_i - M). Exact in real arithmetic, so it must equal the plain
+ * definition up to rounding. */
+static void decode_row_split(const args_t* a, int64_t r, int P, double* out, double* lse) {
+    int h = (int)(r % a->Hq), t = (int)((r / a->Hq) % a->Tq), b = (int)(r / ((int64_t)a->Hq * a->Tq));
+    int G = a->Hq / a->Hkv, g = h / G;
+    double* o = out + r * a->D;
+    int64_t n = visible_keys(a, b, t);
+    for (int d = 0; d < a->D; ++d) o[d] = 0.0;
+    if (n <= 0) {
+        lse[r] = -INFINITY;
+        return;
+    }
+    int64_t np = (n + P - 1) / P;
+    double* s = (double*)malloc((size_t)n * sizeof(double));
+    double* m = (double*)malloc((size_t)np * sizeof(double));
+    double* l = (double*)malloc((size_t)np * sizeof(double));
+    double* op = (double*)calloc((size_t)np * a->D, sizeof(double));
+    row_logits(a, b, t, h, n, s);
+    for (int64_t i = 0; i < np; ++i) {
+        int64_t j0 = i * P, j1 = j0 + P < n ? j0 + P : n;
+        m[i] = -INFINITY;
+        for (int64_t j = j0; j < j1; ++j)
+            if (s[j] > m[i]) m[i] = s[j];
+        l[i] = 0.0;
+        for (int64_t j = j0; j < j1; ++j) {
+            double w = exp(s[j] - m[i]);
+            l[i] += w;
+            value_row_axpy(a, b, g, j, w, op + i * a->D);
+        }
+        for (int d = 0; d < a->D; ++d) op[i * a->D + d] /= l[i];
+    }
+    double M = -INFINITY;
+    for (int64_t i = 0; i < np; ++i)
+        if (m[i] > M) M = m[i];
+    double W = 0.0;
+    for (int64_t i = 0; i < np; ++i) {
+        double w = l[i] * exp(m[i] - M);
+        W += w;
+        for (int d = 0; d < a->D; ++d) o[d] += w * op[i * a->D + d];
+    }
+    for (int d = 0; d < a->D; ++d) o[d] /= W;
+    lse[r] = M + log(W);
+    free(s);
+    free(m);
+    free(l);
+    free(op);
+}
+
+static int check_args(const args_t* a) {
+    if (!a->q || !a->k_cache || !a->v_cache || !a->block_table || !a->seq_lens) return -1;
+    if (a->B < 0 || a->Tq < 1 || a->Hq < 1 || a->Hkv < 1 || a->D < 1 || a->block_size < 1) return -2;
+    if (a->Hq % a->Hkv) return -2;
+    if (a->kv_dtype == OR_I8 && (!a->k_scale || !a->v_scale)) return -1;
+    return 0;
+}
+
+static int run(const args_t* a, const int64_t* rows, int64_t num_rows, int split_P, double* out, double* lse,
+               int nthreads) {
+    int rc = check_args(a);
+    if (rc) return rc;
+    int64_t total = (int64_t)a->B * a->Tq * a->Hq;
+    int64_t cnt = rows ? num_rows : total;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t k = 0; k < cnt; ++k) {
+        int64_t r = rows ? rows[k] : k;
+        if (r < 0 || r >= total) continue;
+        if (split_P > 0)
+            decode_row_split(a, r, split_P, out, lse);
+        else
+            decode_row_plain(a, r, out, lse);
+    }
+    return 0;
+}
+
+#define ORACLE_ARGS                                                                                            \
+    const void *q, int q_dtype, int B, int Tq, int Hq, int Hkv, int D, const void *k_cache, const void *v_cache, \
+        int kv_dtype, const float *k_scale, const float *v_scale, int block_size, const int32_t *block_table,    \
+        int max_blocks, const int32_t *seq_lens, float softmax_scale
+#define ORACLE_PACK                                                                                                \
+    args_t a = {q,       q_dtype,  B,          Tq,         Hq,         Hkv,      D, k_cache, v_cache, kv_dtype, \
+                k_scale, v_scale,  block_size, block_table, max_blocks, seq_lens, softmax_scale}
+
+/* out: fp64 [B*Tq*Hq, D]; lse: fp64 [B*Tq*Hq]. rows: optional flat row ids. */
+int pa_oracle_decode(ORACLE_ARGS, const int64_t* rows, int64_t num_rows, double* out, double* lse, int nthreads) {
+    ORACLE_PACK;
+    return run(&a, rows, num_rows, 0, out, lse, nthreads);
+}
+
+int pa_oracle_decode_split(ORACLE_ARGS, int partition_size, const int64_t* rows, int64_t num_rows, double* out,
+                           double* lse, int nthreads) {
+    ORACLE_PACK;
+    if (partition_size < 1) return -2;
+    return run(&a, rows, num_rows, partition_size, out, lse, nthreads);
+}
+
+int pa_oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

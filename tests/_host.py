@@ -1,0 +1,44 @@
+"""Host-side test plumbing: oracle caches for a generated workload, poisoning."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from workloads import BLOCK_SIZE, Workload
+
+POISON_CODE = 127
+
+
+def poison_host(w: Workload, k, v, ks, vs) -> None:
+    """Fill every cache slot that holds no source row with poison.
+
+    Float caches get NaN; int8 caches get code 127 with a NaN scale. A decode
+    that reads any of these slots produces NaN.
+    """
+    slots = w.unused_slots()
+    blk, off = slots // BLOCK_SIZE, slots % BLOCK_SIZE
+    for c in (k, v):
+        if c.dtype == np.float32:
+            c[blk, off] = np.nan
+        elif c.dtype == np.uint16:
+            c[blk, off] = 0x7FC0  # bfloat16 quiet NaN
+        else:
+            c[blk, off] = POISON_CODE
+    for s in (ks, vs):
+        if s is not None:
+            s[blk, off] = np.nan
+
+
+def oracle_cache(w: Workload, poison: bool = True):
+    """(k, v, k_scale, v_scale) written by the oracle's cache writer."""
+    sp = w.spec
+    k, v, ks, vs = oracle.alloc_cache(w.num_blocks, BLOCK_SIZE, sp.Hkv, sp.D, sp.cache_dtype)
+    oracle.cache_write(w.k_src, w.v_src, w.slot_mapping, k, v, ks, vs)
+    if poison:
+        poison_host(w, k, v, ks, vs)
+    return k, v, ks, vs
+
+
+def oracle_decode(w: Workload, cache, **kw):
+    k, v, ks, vs = cache
+    return oracle.decode(w.q_array(), k, v, w.block_table, w.seq_lens, w.softmax_scale, ks, vs, **kw)

@@ -1,0 +1,132 @@
+"""Independent references that pin the oracle (test helpers only).
+
+Nothing here is shared with the oracle's C code or with the HIP library:
+  - ``brute_decode``: pure-Python ``decimal`` arithmetic at 50 significant
+    digits (``Decimal.exp`` is correctly rounded), gathering each key through
+    the block table with its own loops;
+  - ``dense_decode``: numpy fp64 attention on keys/values first gathered into
+    contiguous arrays by fancy indexing, softmax via numpy;
+  - ``sdpa_decode``: torch's ``scaled_dot_product_attention`` on CPU in float64
+    with an explicit causal mask and KV heads repeated per query group.
+"""
+from __future__ import annotations
+
+import decimal
+from decimal import Decimal
+from typing import Optional
+
+import numpy as np
+
+from workloads import bf16_bits_to_f32
+
+
+def as_f64(a: np.ndarray, scale: Optional[np.ndarray] = None) -> np.ndarray:
+    """Values of a cache/query array as float64 (int8 times its row scale)."""
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f32(a).reshape(a.shape).astype(np.float64)
+    if a.dtype == np.int8:
+        assert scale is not None
+        return a.astype(np.float64) * scale.astype(np.float64)[..., None]
+    return a.astype(np.float64)
+
+
+def gather(cache64: np.ndarray, table_row: np.ndarray, n: int) -> np.ndarray:
+    """Contiguous [n, Hkv, D] keys/values of one sequence (fancy indexing)."""
+    bs = cache64.shape[1]
+    j = np.arange(n)
+    return cache64[table_row[j // bs], j % bs]
+
+
+def dense_decode(q, k_cache, v_cache, table, seq_lens, scale, k_scale=None, v_scale=None):
+    q64 = as_f64(q)
+    K = as_f64(k_cache, k_scale)
+    V = as_f64(v_cache, v_scale)
+    B, Tq, Hq, D = q64.shape
+    Hkv = K.shape[2]
+    G = Hq // Hkv
+    out = np.zeros((B, Tq, Hq, D))
+    lse = np.full((B, Tq, Hq), -np.inf)
+    for b in range(B):
+        L = int(seq_lens[b])
+        Kb = gather(K, table[b], max(L, 0))
+        Vb = gather(V, table[b], max(L, 0))
+        for t in range(Tq):
+            n = L - Tq + t + 1
+            if n <= 0:
+                continue
+            for h in range(Hq):
+                s = float(np.float32(scale)) * (Kb[:n, h // G, :] @ q64[b, t, h])
+                m = s.max()
+                w = np.exp(s - m)
+                out[b, t, h] = (w @ Vb[:n, h // G, :]) / w.sum()
+                lse[b, t, h] = m + np.log(w.sum())
+    return out, lse
+
+
+def sdpa_decode(q, k_cache, v_cache, table, seq_lens, scale, k_scale=None, v_scale=None):
+    import torch
+    import torch.nn.functional as F
+
+    q64 = torch.from_numpy(as_f64(q))
+    K = as_f64(k_cache, k_scale)
+    V = as_f64(v_cache, v_scale)
+    B, Tq, Hq, D = q64.shape
+    Hkv = K.shape[2]
+    G = Hq // Hkv
+    out = np.zeros((B, Tq, Hq, D))
+    for b in range(B):
+        L = int(seq_lens[b])
+        Kb = torch.from_numpy(gather(K, table[b], L)).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        Vb = torch.from_numpy(gather(V, table[b], L)).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        qb = q64[b].permute(1, 0, 2)  # [Hq, Tq, D]
+        pos = torch.arange(L)
+        mask = pos[None, :] <= (L - Tq + torch.arange(Tq))[:, None]  # [Tq, L]
+        o = F.scaled_dot_product_attention(qb[None], Kb[None].contiguous(), Vb[None].contiguous(),
+                                           attn_mask=mask[None, None], scale=float(np.float32(scale)))
+        out[b] = o[0].permute(1, 0, 2).numpy()
+    return out
+
+
+def brute_decode(q, k_cache, v_cache, table, seq_lens, scale, k_scale=None, v_scale=None, digits=50):
+    """Decimal brute force. Every input value is converted exactly to Decimal."""
+    ctx = decimal.Context(prec=digits)
+    B, Tq, Hq, D = q.shape
+    nb, bs, Hkv, _ = k_cache.shape
+    G = Hq // Hkv
+    qv = as_f64(q)
+    kv = as_f64(k_cache, k_scale)  # exact: int8 code * fp32 scale fits a double
+    vv = as_f64(v_cache, v_scale)
+    sc = Decimal(float(np.float32(scale)))
+    out = np.zeros((B, Tq, Hq, D))
+    lse = np.full((B, Tq, Hq), -np.inf)
+    for b in range(B):
+        L = int(seq_lens[b])
+        for t in range(Tq):
+            n = L - Tq + t + 1
+            if n <= 0:
+                continue
+            for h in range(Hq):
+                g = h // G
+                qd = [Decimal(float(x)) for x in qv[b, t, h]]
+                logits = []
+                for j in range(n):
+                    blk = int(table[b][j // bs])
+                    off = j % bs
+                    krow = kv[blk, off, g]
+                    acc = Decimal(0)
+                    for d in range(D):
+                        acc = ctx.add(acc, ctx.multiply(qd[d], Decimal(float(krow[d]))))
+                    logits.append(ctx.multiply(sc, acc))
+                M = max(logits)
+                w = [ctx.exp(ctx.subtract(s, M)) for s in logits]
+                Z = Decimal(0)
+                for x in w:
+                    Z = ctx.add(Z, x)
+                for d in range(D):
+                    acc = Decimal(0)
+                    for j in range(n):
+                        blk = int(table[b][j // bs])
+                        acc = ctx.add(acc, ctx.multiply(w[j], Decimal(float(vv[blk, j % bs, g, d]))))
+                    out[b, t, h, d] = float(ctx.divide(acc, Z))
+                lse[b, t, h] = float(ctx.add(M, ctx.ln(Z)))
+    return out, lse

@@ -1,0 +1,352 @@
+"""Pins of the fp64 oracle against facts fixed outside it (CPU only).
+
+Each test checks the oracle against something it does not share code with:
+Decimal brute force, closed forms, dense attention via numpy, torch SDPA,
+invariances (block permutation, GQA as repeated MHA, causal rows as a virtual
+batch, split = unsplit, shared prefix = private copies, linearity, poison), and
+hand-derived int8 quantiser cases. A dropped term, wrong sign or index, or a
+transposed operand in the oracle fails at least one of them.
+"""
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from _host import oracle_cache, oracle_decode, poison_host
+from _refs import as_f64, brute_decode, dense_decode, sdpa_decode
+from workloads import BLOCK_SIZE, SPECS, bf16_bits, bf16_bits_to_f32, generate, scaled
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def small(name="gqa_bf16", **kw):
+    base = dict(B=2, Tq=1, Hq=4, Hkv=2, D=16, seq_lens=(20, 60))
+    base.update(kw)
+    return scaled(name, **base)
+
+
+# ---------------------------------------------------------------- brute force
+def test_brute_force_tiny_workload():
+    """The tiny fp32 workload at full size against 50-digit Decimal arithmetic."""
+    w = generate("tiny_f32")
+    cache = oracle_cache(w)
+    out, lse = oracle_decode(w, cache)
+    bo, bl = brute_decode(w.q_array(), cache[0], cache[1], w.block_table, w.seq_lens, w.softmax_scale)
+    assert np.max(np.abs(out - bo)) <= 1e-12
+    assert np.max(np.abs(lse - bl)) <= 1e-12
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_brute_force_random_tiny(case):
+    rng = np.random.default_rng(100 + case)
+    dtype = ["f32", "bf16", "i8"][case % 3]
+    Hkv = [1, 2][case % 2]
+    G = [1, 3, 2][case % 3]
+    Tq = 1 + case % 3
+    spec = scaled("gqa_bf16", B=2, Tq=Tq, Hq=Hkv * G, Hkv=Hkv, D=[4, 8][case % 2],
+                  seq_lens=(Tq, 40), q_dtype="bf16" if case % 2 else "f32",
+                  src_dtype="f32", cache_dtype=dtype)
+    lens = rng.integers(Tq, 41, size=2)
+    w = generate(spec, seed=case, seq_lens=lens)
+    cache = oracle_cache(w)
+    out, lse = oracle_decode(w, cache)
+    bo, bl = brute_decode(w.q_array(), cache[0], cache[1], w.block_table, w.seq_lens, w.softmax_scale,
+                          cache[2], cache[3])
+    assert np.max(np.abs(out - bo)) <= 1e-12
+    assert np.max(np.abs(lse - bl)) <= 1e-12
+
+
+# ---------------------------------------------------------------- closed forms
+def test_single_key_returns_its_value_row():
+    w = generate(small(seq_lens=(1, 1), B=3), seed=1)
+    cache = oracle_cache(w)
+    out, lse = oracle_decode(w, cache)
+    V = as_f64(cache[1])
+    K = as_f64(cache[0])
+    G = w.spec.G
+    for b in range(w.spec.B):
+        blk = w.block_table[b, 0]
+        for h in range(w.spec.Hq):
+            assert np.array_equal(out[b, 0, h], V[blk, 0, h // G])
+            s = float(np.float32(w.softmax_scale)) * float(np.dot(w.q[b, 0, h].astype(np.float64), K[blk, 0, h // G]))
+            assert abs(lse[b, 0, h] - s) <= 1e-12 * max(1.0, abs(s))
+
+
+def test_constant_values_return_the_constant():
+    w = generate(small(src_dtype="f32", cache_dtype="f32", q_dtype="f32"), seed=2)
+    c = np.linspace(-3, 3, w.spec.Hkv * w.spec.D, dtype=np.float32).reshape(w.spec.Hkv, w.spec.D)
+    w.v_src[:] = c[None]
+    cache = oracle_cache(w)
+    out, _ = oracle_decode(w, cache)
+    G = w.spec.G
+    for h in range(w.spec.Hq):
+        assert np.max(np.abs(out[:, :, h] - c[h // G].astype(np.float64))) <= 1e-12
+
+
+@pytest.mark.parametrize("how", ["zero_query", "zero_scale"])
+def test_uniform_weights_give_the_mean(how):
+    w = generate(small(Tq=2, src_dtype="f32", cache_dtype="f32", q_dtype="f32"), seed=3)
+    if how == "zero_query":
+        w.q[:] = 0.0
+    else:
+        w.softmax_scale = 0.0
+    cache = oracle_cache(w)
+    out, lse = oracle_decode(w, cache)
+    V = as_f64(cache[1])
+    G = w.spec.G
+    for b in range(w.spec.B):
+        L = int(w.seq_lens[b])
+        for t in range(w.spec.Tq):
+            n = L - w.spec.Tq + t + 1
+            rows = [V[w.block_table[b, j // 16], j % 16] for j in range(n)]
+            mean = np.mean(np.stack(rows), axis=0)
+            for h in range(w.spec.Hq):
+                assert np.max(np.abs(out[b, t, h] - mean[h // G])) <= 1e-12
+                assert abs(lse[b, t, h] - np.log(n)) <= 1e-12
+
+
+# ------------------------------------------------------------ library / dense
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
+def test_paged_equals_dense_contiguous(dtype):
+    spec = scaled("gqa_bf16", B=3, Tq=2, Hq=8, Hkv=2, D=32, seq_lens=(2, 200), src_dtype="f32",
+                  cache_dtype=dtype, q_dtype="bf16")
+    w = generate(spec, seed=4)
+    cache = oracle_cache(w)
+    out, lse = oracle_decode(w, cache)
+    do, dl = dense_decode(w.q_array(), cache[0], cache[1], w.block_table, w.seq_lens, w.softmax_scale,
+                          cache[2], cache[3])
+    assert np.max(np.abs(out - do)) <= 1e-13
+    assert np.max(np.abs(lse - dl)) <= 1e-12
+
+
+def test_matches_torch_sdpa_fp64_causal():
+    spec = scaled("verify_bf16", B=2, Tq=3, Hq=6, Hkv=2, D=16, seq_lens=(3, 90), shared_prefix=0)
+    w = generate(spec, seed=5)
+    cache = oracle_cache(w)
+    out, _ = oracle_decode(w, cache)
+    ref = sdpa_decode(w.q_array(), cache[0], cache[1], w.block_table, w.seq_lens, w.softmax_scale)
+    assert np.max(np.abs(out - ref)) <= 1e-12
+
+
+# ------------------------------------------------------------------ invariants
+def test_block_permutation_is_bitwise_invariant():
+    w = generate(small(B=3, seq_lens=(30, 100)), seed=6)
+    k, v, ks, vs = oracle_cache(w)
+    out, lse = oracle_decode(w, (k, v, ks, vs))
+    perm = np.random.default_rng(7).permutation(w.num_blocks)  # new id of old block i is perm[i]
+    k2, v2 = np.empty_like(k), np.empty_like(v)
+    k2[perm], v2[perm] = k, v
+    w.block_table = perm[w.block_table].astype(np.int32)
+    out2, lse2 = oracle_decode(w, (k2, v2, None, None))
+    assert np.array_equal(out, out2, equal_nan=True) and np.array_equal(lse, lse2)
+
+
+def test_gqa_equals_repeated_kv_mha():
+    spec = small(Hq=6, Hkv=2, Tq=2, D=8, cache_dtype="i8", src_dtype="f32")
+    w = generate(spec, seed=8)
+    k, v, ks, vs = oracle_cache(w)
+    out, lse = oracle_decode(w, (k, v, ks, vs))
+    G = spec.G
+    rep = lambda a: np.ascontiguousarray(np.repeat(a, G, axis=2))
+    out2, lse2 = oracle.decode(w.q_array(), rep(k), rep(v), w.block_table, w.seq_lens, w.softmax_scale,
+                               rep(ks), rep(vs))
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+def test_causal_rows_are_a_virtual_batch():
+    spec = scaled("verify_bf16", B=2, Tq=8, Hq=4, Hkv=2, D=16, seq_lens=(8, 70), shared_prefix=0)
+    w = generate(spec, seed=9)
+    cache = oracle_cache(w)
+    out, lse = oracle_decode(w, cache)
+    for t in range(8):
+        lens_t = (w.seq_lens - 8 + t + 1).astype(np.int32)
+        o1, l1 = oracle.decode(w.q_array()[:, t:t + 1], cache[0], cache[1], w.block_table, lens_t,
+                               w.softmax_scale)
+        assert np.array_equal(out[:, t], o1[:, 0]) and np.array_equal(lse[:, t], l1[:, 0])
+
+
+@pytest.mark.parametrize("P", [16, 64, 512, 2048, 4096])
+def test_split_equals_unsplit(P):
+    spec = scaled("long64k_bf16", B=2, Tq=2, Hq=6, Hkv=2, D=32, seq_lens=(900, 3000), peaked_frac=0.01,
+                  cache_dtype="bf16")
+    w = generate(spec, seed=10)
+    cache = oracle_cache(w)
+    out, lse = oracle_decode(w, cache)
+    o2, l2 = oracle_decode(w, cache, partition_size=P)
+    assert np.max(np.abs(out - o2)) <= 1e-13
+    assert np.max(np.abs(lse - l2)) <= 1e-12
+
+
+def test_shared_prefix_equals_private_copies():
+    spec = scaled("verify_i8", B=3, Tq=8, Hq=6, Hkv=2, D=16, seq_lens=(80, 200), shared_prefix=64)
+    w = generate(spec, seed=11)
+    k, v, ks, vs = oracle_cache(w)
+    out, lse = oracle_decode(w, (k, v, ks, vs))
+    # give every sequence private copies of the prefix blocks
+    nshared = 64 // BLOCK_SIZE
+    extra = w.spec.B * nshared
+    grow = lambda a: np.concatenate([a, np.zeros((extra,) + a.shape[1:], a.dtype)])
+    k2, v2, ks2, vs2 = grow(k), grow(v), grow(ks), grow(vs)
+    table = w.block_table.copy()
+    nxt = w.num_blocks
+    for b in range(w.spec.B):
+        for j in range(nshared):
+            src = table[b, j]
+            for a2, a in ((k2, k), (v2, v), (ks2, ks), (vs2, vs)):
+                a2[nxt] = a[src]
+            table[b, j] = nxt
+            nxt += 1
+    out2, lse2 = oracle.decode(w.q_array(), k2, v2, table, w.seq_lens, w.softmax_scale, ks2, vs2)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+def test_linear_in_values():
+    spec = small(src_dtype="f32", cache_dtype="f32", q_dtype="f32", Tq=2)
+    w = generate(spec, seed=12)
+    rng = np.random.default_rng(13)
+    V1 = (rng.integers(-64, 64, size=w.v_src.shape) / 16).astype(np.float32)
+    V2 = (rng.integers(-64, 64, size=w.v_src.shape) / 16).astype(np.float32)
+    outs = []
+    for V in (V1, V2, 2 * V1 + 0.5 * V2):  # exact in fp32
+        w.v_src = V
+        outs.append(oracle_decode(w, oracle_cache(w))[0])
+    assert np.max(np.abs(outs[2] - (2 * outs[0] + 0.5 * outs[1]))) <= 1e-12
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
+def test_poisoned_slots_are_never_read(dtype):
+    spec = small(B=3, Tq=2, seq_lens=(5, 77), cache_dtype=dtype, src_dtype="f32")
+    w = generate(spec, seed=14)
+    clean = oracle_decode(w, oracle_cache(w, poison=False))
+    dirty = oracle_decode(w, oracle_cache(w, poison=True))
+    assert np.all(np.isfinite(dirty[0]))
+    assert np.array_equal(clean[0], dirty[0]) and np.array_equal(clean[1], dirty[1])
+
+
+def test_rows_without_keys_are_zero_with_minus_inf_lse():
+    spec = small(B=3, Tq=4, seq_lens=(0, 6))
+    w = generate(spec, seed=15, seq_lens=[0, 2, 6])
+    out, lse = oracle_decode(w, oracle_cache(w))
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+    # sequence 1 has 2 tokens and 4 query tokens: rows t = 0, 1 see n <= 0 keys
+    assert np.all(out[1, :2] == 0) and np.all(np.isneginf(lse[1, :2]))
+    assert np.all(np.isfinite(lse[1, 2:])) and np.all(np.isfinite(lse[2]))
+
+
+# ----------------------------------------------------------------- cache writer
+def _write_rows(x: np.ndarray, cache_dtype: str, src_dtype: str = "f32"):
+    """Quantise/copy rows x [N, 1, D] into a 1-kv-head cache; return cache and scales."""
+    N, _, D = x.shape
+    nb = (N + BLOCK_SIZE - 1) // BLOCK_SIZE
+    k, v, ks, vs = oracle.alloc_cache(nb, BLOCK_SIZE, 1, D, cache_dtype)
+    src = x if src_dtype == "f32" else bf16_bits(x).reshape(x.shape)
+    oracle.cache_write(src, src, np.arange(N), k, v, ks, vs)
+    k = k.reshape(nb * BLOCK_SIZE, D)[:N]
+    if ks is not None:
+        ks = ks.reshape(-1)[:N]
+    return k, ks
+
+
+def test_int8_golden_cases():
+    with open(os.path.join(GOLDEN, "int8_quantizer_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        x = np.asarray(c["x"], np.float32)[None, None, :]
+        codes, scale = _write_rows(x, "i8")
+        assert scale[0] == np.float32(c["scale"]), c["why"]
+        assert codes[0].tolist() == c["codes"], c["why"]
+
+
+def test_int8_round_trip_and_error_bound():
+    rng = np.random.default_rng(16)
+    x = rng.standard_normal((4096, 1, 256), dtype=np.float32)
+    x[:64] *= np.float32(1e-30)  # tiny magnitudes
+    x[64:128] *= np.float32(1e30)  # huge magnitudes
+    codes, s = _write_rows(x, "i8")
+    assert codes.min() >= -127 and codes.max() <= 127
+    # error bound: |x - code*s| <= s * (1/2 + 2^-18)
+    err = np.abs(x[:, 0].astype(np.float64) - codes.astype(np.float64) * s[:, None].astype(np.float64))
+    assert np.all(err <= s[:, None].astype(np.float64) * (0.5 + 2.0 ** -18))
+    # each row uses the full code range
+    assert np.all(np.abs(codes).max(axis=1) == 127)
+    # dequantise (fp32 product, and exactly) and quantise again: identical codes and scale
+    for deq in (codes.astype(np.float32) * s[:, None], (codes.astype(np.float64) * s[:, None]).astype(np.float32)):
+        c2, s2 = _write_rows(deq[:, None, :].astype(np.float32), "i8")
+        assert np.array_equal(c2, codes) and np.array_equal(s2, s)
+
+
+def test_int8_quotient_is_rounded_to_fp32_first():
+    """Where the exact quotient x/s lies just off a half-integer but its fp32
+    rounding lands on it, the code follows the fp32 quotient (ties to even)."""
+    rng = np.random.default_rng(17)
+    found = 0
+    for _ in range(200000):
+        s = np.float32(rng.uniform(0.01, 0.05))
+        k = int(rng.integers(-120, 120))
+        # the fp32 neighbour of (k + 0.5) * s whose exact quotient is not k + 0.5
+        base = np.float32((k + 0.5) * float(s))
+        for x in (base, np.nextafter(base, np.float32(np.inf)), np.nextafter(base, np.float32(-np.inf))):
+            qf = np.float32(x) / s  # binary32 quotient
+            exact = Fraction(float(x)) / Fraction(float(s))
+            if float(qf) == k + 0.5 and exact != Fraction(2 * k + 1, 2):
+                amax = np.float32(127) * s  # forces the row scale close to s
+                row = np.array([x, amax], np.float32)
+                if np.float32(row.__abs__().max() / np.float32(127)) != s:
+                    continue
+                codes, scale = _write_rows(row[None, None, :], "i8")
+                assert scale[0] == s
+                half_even = k if k % 2 == 0 else k + 1
+                assert codes[0, 0] == half_even
+                found += 1
+        if found >= 5:
+            break
+    assert found >= 1
+
+
+def test_bf16_and_f32_copies():
+    rng = np.random.default_rng(18)
+    x = rng.standard_normal((40, 1, 64), dtype=np.float32) * np.float32(3.7)
+    import torch
+
+    # f32 -> bf16 rounds to nearest even like torch's conversion
+    got, _ = _write_rows(x, "bf16")
+    want = torch.from_numpy(x[:, 0]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+    # f32 -> f32 and bf16 -> bf16 copy bits; bf16 -> f32 widens exactly
+    got, _ = _write_rows(x, "f32")
+    assert np.array_equal(got.view(np.uint32), x[:, 0].view(np.uint32))
+    got, _ = _write_rows(x, "bf16", src_dtype="bf16")
+    assert np.array_equal(got, bf16_bits(x[:, 0]))
+    got, _ = _write_rows(x, "f32", src_dtype="bf16")
+    assert np.array_equal(got, bf16_bits_to_f32(bf16_bits(x[:, 0])).reshape(40, 64))
+
+
+def test_slot_placement_and_skipped_slots():
+    rng = np.random.default_rng(19)
+    nb, Hkv, D = 6, 2, 8
+    N = 20
+    x = rng.standard_normal((N, Hkv, D), dtype=np.float32)
+    slots = rng.permutation(nb * BLOCK_SIZE)[:N].astype(np.int64)
+    slots[[3, 11]] = -1
+    k, v, _, _ = oracle.alloc_cache(nb, BLOCK_SIZE, Hkv, D, "f32")
+    k[:] = 7.0
+    oracle.cache_write(x, -x, slots, k, v)
+    flat = k.reshape(nb * BLOCK_SIZE, Hkv, D)
+    for i in range(N):
+        if slots[i] >= 0:
+            assert np.array_equal(flat[slots[i]], x[i])
+            assert np.array_equal(v.reshape(-1, Hkv, D)[slots[i]], -x[i])
+    untouched = np.setdiff1d(np.arange(nb * BLOCK_SIZE), slots[slots >= 0])
+    assert np.all(flat[untouched] == 7.0)
+
+
+def test_oracle_rejects_bad_arguments():
+    w = generate(small(), seed=20)
+    k, v, ks, vs = oracle_cache(w)
+    with pytest.raises(ValueError):
+        oracle.decode(w.q_array(), *oracle.alloc_cache(4, 16, 2, 16, "i8")[:2], w.block_table, w.seq_lens, 0.25)
