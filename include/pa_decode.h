@@ -1,0 +1,168 @@
+/*
+ * pa_decode.h — C ABI of the MI355X (gfx950) paged-attention decode library.
+ *
+ * The operation is PagedAttention decode: each sequence's new query tokens
+ * attend to that sequence's keys and values, which sit in fixed-size blocks
+ * of a shared pool reached through a per-sequence block table (nvllm page,
+ * "About", the PagedAttention citation; 1Cat-vLLM docs index, feature list).
+ * The decode is split along the context ("split-K paged decode with an int8
+ * KV cache", vllm-sm70 page, "Why", Attention bullet) and the partitions are
+ * merged by their log-sum-exp ("split-KV merge", nvllm page,
+ * "Acknowledgments", b12x). Several query tokens per sequence (speculative
+ * verification, 8 target tokens per step: vllm-sm12x-nvfp4-dflash2 page,
+ * "What makes this stack different") are a causal "virtual batch": query
+ * token t of Tq sees keys 0 .. L_b - Tq + t.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless marked (host). Every buffer belongs
+ *    to the caller; the library never allocates or frees device memory,
+ *    never synchronises, never reads device data on the host, and launches
+ *    only on `stream` (a hipStream_t; NULL = the null stream). The calls are
+ *    therefore safe to record in a HIP graph (the vLLM-fork pages run decode
+ *    under full graph capture and keep graph-held buffers at fixed addresses:
+ *    nvllm "Roadmap", vllm-sm70 "Changes relative to 1Cat-vLLM").
+ *  - Return 0 on success or a negative PA_ERR_* code; nothing is thrown
+ *    across the ABI. pa_last_error() gives a message for the calling thread's
+ *    last failure. Arguments are checked on the host before any launch, so a
+ *    rejected call has no effect. Device-side contracts (valid block ids,
+ *    0 <= seq_lens[b] <= max_seq_len, distinct slots) are trusted; breaking
+ *    them is undefined behaviour (an out-of-range block id reads out of
+ *    bounds). Asynchronous device faults appear at the caller's next sync.
+ *  - Layouts are dense row-major with the innermost dimension last:
+ *      q        [B, Tq, Hq, D]
+ *      caches   [num_blocks, block_size, Hkv, D]   (K and V separately)
+ *      scales   [num_blocks, block_size, Hkv]      fp32, int8 caches only
+ *      table    [B, max_blocks_per_seq]            int32 physical block ids
+ *      out      [B, Tq, Hq, D]
+ *      lse      [B, Tq, Hq]                        fp32, natural log
+ *    Query head h reads kv head h / (Hq / Hkv).
+ *  - Supported: block_size 16; D in {64, 128, 256}; 1 <= Tq <= 16;
+ *    Hq % Hkv == 0 and Hq / Hkv <= 64; q in {f32, bf16}; caches in
+ *    {f32, bf16, i8}; out in {f32, bf16}. q, caches and out must be 16-byte
+ *    aligned.
+ */
+#ifndef PA_DECODE_H
+#define PA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2 } pa_dtype;
+
+enum {
+    PA_OK = 0,
+    PA_ERR_NULL = -1,        /* a required pointer is NULL */
+    PA_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+    PA_ERR_DTYPE = -3,       /* a dtype or dtype combination is not supported */
+    PA_ERR_UNSUPPORTED = -4, /* a valid but unimplemented shape (D, block_size, Tq, group) */
+    PA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than pa_decode_workspace_bytes */
+    PA_ERR_LAUNCH = -6,      /* the HIP launch itself failed */
+    PA_ERR_ALIGN = -7        /* a pointer is not 16-byte aligned */
+};
+
+/*
+ * pa_cache_write — store new tokens' key/value rows into the paged caches.
+ *
+ * Defines the cache contents every decode reads (the block pool of
+ * PagedAttention; the int8 KV cache of the vllm-sm70 page, "Why"). For each
+ * token i < num_tokens with slot = slot_mapping[i] >= 0 and each kv head g,
+ * row src[i, g, :] goes to cache row (slot / block_size, slot % block_size,
+ * g). A negative slot skips the token: padded rows must not write into other
+ * requests' slots (vllm-sm70 page, "Known limitations", fixed defects).
+ *   k_src, v_src   [num_tokens, Hkv, D] in src_dtype (f32 or bf16)
+ *   slot_mapping   [num_tokens] int64, slot = block * block_size + offset
+ *   k_cache, v_cache  caches in cache_dtype; k_scale, v_scale required iff
+ *                  cache_dtype == PA_I8 (else pass NULL)
+ * Conversions: same dtype copies bits; bf16 -> f32 widens exactly;
+ * f32 -> bf16 rounds to nearest even; -> i8 is symmetric per (token, kv
+ * head): s = fp32(max|x| / 127), code = clamp(rint_even(fp32(x / s)), -127,
+ * 127), and s = 0 with all codes 0 for an all-zero row. Bit-exact.
+ * Slots must lie in [0, num_blocks * block_size) and be distinct within one
+ * call. num_tokens == 0 is a no-op.
+ */
+int pa_cache_write(const void* k_src, const void* v_src, pa_dtype src_dtype, const int64_t* slot_mapping,
+                   int64_t num_tokens, void* k_cache, void* v_cache, pa_dtype cache_dtype, float* k_scale,
+                   float* v_scale, int64_t num_blocks, int32_t block_size, int32_t Hkv, int32_t D, void* stream);
+
+/*
+ * pa_decode — paged attention of B sequences' Tq query tokens.
+ *
+ * For every b, t, h with n = seq_lens[b] - Tq + t + 1 visible keys:
+ *   out[b,t,h,:] = sum_j softmax_j(softmax_scale * q[b,t,h,:] . K_j) V_j,
+ *   lse[b,t,h]   = log sum_j exp(softmax_scale * q . K_j),
+ * where K_j, V_j are the rows of logical position j of sequence b, read
+ * through block_table[b][j / block_size] (int8: code * scale). n <= 0 gives
+ * out = 0 and lse = -inf. seq_lens counts the Tq new tokens, whose K/V must
+ * already be in the cache (pa_cache_write). Arithmetic is fp32 (bf16/int8
+ * operands, fp32 accumulation).
+ *   q              [B, Tq, Hq, D] in q_dtype
+ *   block_table    [B, max_blocks_per_seq] int32; entries for logical blocks
+ *                  < ceil(seq_lens[b] / block_size) must be in [0, num_blocks)
+ *   seq_lens       [B] int32, each in [0, max_seq_len]
+ *   max_seq_len    (host) an upper bound of seq_lens; it sizes the grid, so
+ *                  no device data is read on the host.
+ *                  max_blocks_per_seq * block_size >= max_seq_len is required.
+ *   partition_size tokens per split-K partition, a multiple of block_size,
+ *                  or 0 to let pa_choose_partition_size pick it.
+ *   out, lse       outputs; lse may be NULL.
+ *   workspace      device scratch of workspace_bytes >= pa_decode_workspace_bytes
+ *                  (may be NULL when that size is 0).
+ *   num_partitions (host, out) NP = ceil(max_seq_len / P).
+ * When *num_partitions == 1 the kernel writes out/lse directly. Otherwise it
+ * writes per-partition results to the workspace and leaves out/lse untouched:
+ * the caller must then run pa_decode_splitk_reduce on the same stream.
+ */
+int pa_decode(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D,
+              const void* k_cache, const void* v_cache, pa_dtype kv_dtype, const float* k_scale,
+              const float* v_scale, int64_t num_blocks, int32_t block_size, const int32_t* block_table,
+              int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+              int32_t partition_size, void* out, pa_dtype out_dtype, float* lse, void* workspace,
+              size_t workspace_bytes, int32_t* num_partitions, void* stream);
+
+/*
+ * pa_decode_splitk_reduce — merge split-K partials by log-sum-exp.
+ *
+ * The split-KV merge (nvllm page, "Acknowledgments", b12x): with partial
+ * outputs o_i (normalised within partition i) and partial log-sum-exps
+ * lse_i, M = max_i lse_i, w_i = exp(lse_i - M),
+ *   out = sum_i w_i o_i / sum_i w_i,  lse = M + log sum_i w_i.
+ * Partitions with lse_i = -inf weigh 0; a row whose partitions are all -inf
+ * gives out = 0, lse = -inf.
+ * Workspace layout (fp32, written by pa_decode, also fillable by a caller
+ * that merges partials from elsewhere): o [B, Tq, Hq, NP, D] at offset 0,
+ * then lse [B, Tq, Hq, NP] at the next 256-byte boundary. Row (b, t, h)
+ * reads partitions i < ceil(max(n, 0) / partition_size) with
+ * n = seq_lens[b] - Tq + t + 1, which are exactly the ones pa_decode writes.
+ */
+int pa_decode_splitk_reduce(const void* workspace, int32_t num_partitions, int32_t partition_size, int32_t B,
+                            int32_t Tq, int32_t Hq, int32_t D, const int32_t* seq_lens, void* out,
+                            pa_dtype out_dtype, float* lse, void* stream);
+
+/* Bytes of workspace pa_decode needs (0 when one partition covers
+ * max_seq_len). partition_size 0 means the heuristic's choice, as in
+ * pa_decode; the caller must pass the same arguments to both. Returns 0 for
+ * invalid arguments (pa_decode then reports the error). */
+size_t pa_decode_workspace_bytes(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
+                                 int32_t max_seq_len, int32_t partition_size);
+
+/* The partition size pa_decode uses for partition_size == 0: a multiple of
+ * 16 chosen so that the grid (partitions x kv heads x sequences x query
+ * groups) fills the GPU's compute units while keeping the split-K workspace
+ * small (the stream-K rationale of the nvllm page, "SM120 Stream-K Decode
+ * Optimization": split the long dimension when the batch alone cannot fill
+ * the machine). Returns a negative PA_ERR_* code for invalid arguments. */
+int32_t pa_choose_partition_size(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
+                                 int32_t max_seq_len);
+
+/* Message for the calling thread's last non-zero return ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_DECODE_H */

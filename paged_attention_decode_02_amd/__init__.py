@@ -1,0 +1,202 @@
+"""Python binding of libpa_decode.so, the gfx950 paged-attention decode library.
+
+Argument marshalling only: every step of the decode runs in the HIP kernels
+behind the C ABI (``include/pa_decode.h``). torch provides device memory and
+the current stream; tensors must live on the GPU. If the shared library has
+not been built the functions raise; there is no fallback.
+
+    cache_write(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None)
+    out, lse = decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len,
+                      softmax_scale, k_scale=None, v_scale=None, partition_size=0)
+    np_ = decode_partials(...)        # the split-K kernel alone
+    splitk_reduce(workspace, np_, partition_size, seq_lens, out, lse)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "PaError", "cache_write", "decode", "decode_partials", "splitk_reduce", "workspace_bytes",
+    "choose_partition_size", "library_path", "load", "DTYPE_CODE",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "_lib", "libpa_decode.so")
+_lock = threading.Lock()
+_lib = None
+
+DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.int8: 2}
+
+EXPORTS = (
+    "pa_cache_write", "pa_decode", "pa_decode_splitk_reduce", "pa_decode_workspace_bytes",
+    "pa_choose_partition_size", "pa_last_error",
+)
+
+
+class PaError(RuntimeError):
+    """A non-zero return from the C ABI; ``code`` is the PA_ERR_* value."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__("pa error %d: %s" % (code, msg))
+        self.code = code
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libpa_decode.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libpa_decode.so is not built (%s); run __graft_entry__.build()" % _LIB_PATH)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I32, I64, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        lib.pa_cache_write.argtypes = [P, P, I32, P, I64, P, P, I32, P, P, I64, I32, I32, I32, P]
+        lib.pa_cache_write.restype = ctypes.c_int
+        lib.pa_decode.argtypes = [P, I32, I32, I32, I32, I32, I32, P, P, I32, P, P, I64, I32, P, I32, P, I32, F,
+                                  I32, P, I32, P, P, SZ, ctypes.POINTER(I32), P]
+        lib.pa_decode.restype = ctypes.c_int
+        lib.pa_decode_splitk_reduce.argtypes = [P, I32, I32, I32, I32, I32, I32, P, P, I32, P, P]
+        lib.pa_decode_splitk_reduce.restype = ctypes.c_int
+        lib.pa_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32]
+        lib.pa_decode_workspace_bytes.restype = SZ
+        lib.pa_choose_partition_size.argtypes = [I32, I32, I32, I32, I32, I32, I32]
+        lib.pa_choose_partition_size.restype = I32
+        lib.pa_last_error.argtypes = []
+        lib.pa_last_error.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        msg = load().pa_last_error()
+        raise PaError(rc, msg.decode() if msg else "")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: Optional[torch.Tensor], name: str):
+    if t is not None:
+        if not t.is_cuda:
+            raise ValueError("%s must be a GPU tensor" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _code(t: torch.Tensor) -> int:
+    try:
+        return DTYPE_CODE[t.dtype]
+    except KeyError:
+        raise ValueError("unsupported dtype %s" % t.dtype)
+
+
+def cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                v_cache: torch.Tensor, k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                stream=None) -> None:
+    """Store rows k, v [N, Hkv, D] at slot_mapping [N] (int64) in the paged caches."""
+    for t, n in ((k, "k"), (v, "v"), (slot_mapping, "slot_mapping"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _dev(t, n)
+    if slot_mapping.dtype != torch.int64:
+        raise ValueError("slot_mapping must be int64")
+    nb, bs, Hkv, D = k_cache.shape
+    _check(load().pa_cache_write(_ptr(k), _ptr(v), _code(k), _ptr(slot_mapping), slot_mapping.numel(),
+                                 _ptr(k_cache), _ptr(v_cache), _code(k_cache), _ptr(k_scale), _ptr(v_scale), nb, bs,
+                                 Hkv, D, _stream(stream)))
+
+
+def workspace_bytes(B: int, Tq: int, Hq: int, Hkv: int, D: int, kv_dtype: torch.dtype, max_seq_len: int,
+                    partition_size: int = 0) -> int:
+    return int(load().pa_decode_workspace_bytes(B, Tq, Hq, Hkv, D, DTYPE_CODE[kv_dtype], max_seq_len,
+                                                partition_size))
+
+
+def choose_partition_size(B: int, Tq: int, Hq: int, Hkv: int, D: int, kv_dtype: torch.dtype,
+                          max_seq_len: int) -> int:
+    P = int(load().pa_choose_partition_size(B, Tq, Hq, Hkv, D, DTYPE_CODE[kv_dtype], max_seq_len))
+    if P < 0:
+        _check(P)
+    return P
+
+
+def decode_partials(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, softmax_scale: float,
+                    out: torch.Tensor, lse: Optional[torch.Tensor] = None, k_scale=None, v_scale=None,
+                    partition_size: int = 0, workspace: Optional[torch.Tensor] = None, stream=None) -> int:
+    """Launch the split-K decode kernel only; returns the partition count NP.
+
+    NP == 1: out/lse are written. NP > 1: partials are in ``workspace`` and
+    splitk_reduce must follow on the same stream.
+    """
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_table, "block_table"),
+                 (seq_lens, "seq_lens"), (out, "out"), (lse, "lse"), (k_scale, "k_scale"), (v_scale, "v_scale"),
+                 (workspace, "workspace")):
+        _dev(t, n)
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    B, Tq, Hq, D = q.shape
+    nb, bs, Hkv, _ = k_cache.shape
+    np_ = ctypes.c_int32(0)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().pa_decode(_ptr(q), _code(q), B, Tq, Hq, Hkv, D, _ptr(k_cache), _ptr(v_cache), _code(k_cache),
+                            _ptr(k_scale), _ptr(v_scale), nb, bs, _ptr(block_table), block_table.shape[1],
+                            _ptr(seq_lens), int(max_seq_len), float(softmax_scale), int(partition_size), _ptr(out),
+                            _code(out), _ptr(lse), _ptr(workspace), ws_bytes, ctypes.byref(np_), _stream(stream)))
+    return int(np_.value)
+
+
+def splitk_reduce(workspace: torch.Tensor, num_partitions: int, partition_size: int, seq_lens: torch.Tensor,
+                  out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Merge split-K partials (layout of include/pa_decode.h) into out/lse."""
+    for t, n in ((workspace, "workspace"), (seq_lens, "seq_lens"), (out, "out"), (lse, "lse")):
+        _dev(t, n)
+    B, Tq, Hq, D = out.shape
+    _check(load().pa_decode_splitk_reduce(_ptr(workspace), int(num_partitions), int(partition_size), B, Tq, Hq, D,
+                                          _ptr(seq_lens), _ptr(out), _code(out), _ptr(lse), _stream(stream)))
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+           seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: float, k_scale: Optional[torch.Tensor] = None,
+           v_scale: Optional[torch.Tensor] = None, partition_size: int = 0, out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           out_dtype: torch.dtype = torch.float32, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Paged decode of q [B, Tq, Hq, D]; returns (out [B, Tq, Hq, D], lse [B, Tq, Hq]).
+
+    Runs the split-K kernel and, when it used more than one partition, the
+    log-sum-exp reduce. Missing out/lse/workspace tensors are allocated with
+    torch (the C ABI itself never allocates).
+    """
+    B, Tq, Hq, D = q.shape
+    nb, bs, Hkv, _ = k_cache.shape
+    if out is None:
+        out = torch.empty((B, Tq, Hq, D), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=q.device)
+    P = partition_size or choose_partition_size(B, Tq, Hq, Hkv, D, k_cache.dtype, max_seq_len)
+    if workspace is None:
+        nbytes = workspace_bytes(B, Tq, Hq, Hkv, D, k_cache.dtype, max_seq_len, P)
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    np_ = decode_partials(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, softmax_scale, out, lse,
+                          k_scale, v_scale, P, workspace, stream)
+    if np_ > 1:
+        splitk_reduce(workspace, np_, P, seq_lens, out, lse, stream)
+    return out, lse

@@ -1,0 +1,261 @@
+// Host side of the C ABI declared in include/pa_decode.h: argument checks,
+// the split-K partition heuristic, and dispatch to the gfx950 kernels. No
+// device memory is allocated and no device data is read here, so every entry
+// point can be recorded in a HIP graph.
+#include "../../include/pa_decode.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "pa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return PA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_d(int32_t D) { return D == 64 || D == 128 || D == 256; }
+
+constexpr int kBlock = 16;
+constexpr int kMaxTq = 16;
+constexpr int kMaxGroup = 64;
+constexpr int kCUs = 256;          // MI355X compute units
+constexpr int kWavesPerCU = 8;     // target resident decode waves per CU
+constexpr int kMinPartition = 256; // tokens; bounds the split-K partial traffic
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Head-chunk width of the VALU decode for a query group of G heads, and the
+// number of chunks a kv head's group is split into.
+void head_chunks(int32_t G, int* GT, int* nchunk) {
+    int gt;
+    if (G <= 8) {
+        gt = G;
+        while (!pa::decode_valu_has_gt(gt)) ++gt;  // 3 -> 4, 5 -> 6, 7 -> 8
+    } else {
+        gt = 8;
+    }
+    *GT = gt;
+    *nchunk = (G + gt - 1) / gt;
+}
+
+int32_t partition_for(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t max_seq_len) {
+    if (max_seq_len <= kBlock) return kBlock;
+    int GT, nchunk;
+    head_chunks(Hq / Hkv, &GT, &nchunk);
+    const int64_t per_partition = (int64_t)B * Tq * Hkv * nchunk;  // workgroups per partition index
+    const int64_t target = (int64_t)kCUs * kWavesPerCU;
+    int64_t want_np = (target + per_partition - 1) / per_partition;
+    if (want_np < 1) want_np = 1;
+    int64_t P = (max_seq_len + want_np - 1) / want_np;
+    P = (P + kBlock - 1) / kBlock * kBlock;
+    if (P < kMinPartition) P = kMinPartition;
+    const int64_t whole = ((int64_t)max_seq_len + kBlock - 1) / kBlock * kBlock;
+    if (P >= whole) P = whole;  // one partition covers everything
+    return (int32_t)P;
+}
+
+int check_dims(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D) {
+    if (B < 0) return fail(PA_ERR_SHAPE, "B=%d must be >= 0", B);
+    if (Tq < 1) return fail(PA_ERR_SHAPE, "Tq=%d must be >= 1", Tq);
+    if (Tq > kMaxTq) return fail(PA_ERR_UNSUPPORTED, "Tq=%d exceeds %d", Tq, kMaxTq);
+    if (Hq < 1 || Hkv < 1) return fail(PA_ERR_SHAPE, "Hq=%d and Hkv=%d must be >= 1", Hq, Hkv);
+    if (Hq % Hkv) return fail(PA_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (Hq / Hkv > kMaxGroup) return fail(PA_ERR_UNSUPPORTED, "group Hq/Hkv=%d exceeds %d", Hq / Hkv, kMaxGroup);
+    if (D < 1) return fail(PA_ERR_SHAPE, "D=%d must be >= 1", D);
+    if (!supported_d(D)) return fail(PA_ERR_UNSUPPORTED, "D=%d not in {64, 128, 256}", D);
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_err.c_str(); }
+
+int32_t pa_choose_partition_size(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
+                                 int32_t max_seq_len) {
+    int rc = check_dims(B, Tq, Hq, Hkv, D);
+    if (rc) return rc;
+    if (kv_dtype != PA_F32 && kv_dtype != PA_BF16 && kv_dtype != PA_I8)
+        return fail(PA_ERR_DTYPE, "kv dtype %d not supported", (int)kv_dtype);
+    if (max_seq_len < 0) return fail(PA_ERR_SHAPE, "max_seq_len=%d must be >= 0", max_seq_len);
+    ok();
+    return partition_for(B, Tq, Hq, Hkv, max_seq_len);
+}
+
+size_t pa_decode_workspace_bytes(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
+                                 int32_t max_seq_len, int32_t partition_size) {
+    if (check_dims(B, Tq, Hq, Hkv, D) || max_seq_len < 0 || partition_size < 0 || partition_size % kBlock)
+        return 0;
+    if (kv_dtype != PA_F32 && kv_dtype != PA_BF16 && kv_dtype != PA_I8) return 0;
+    const int32_t P = partition_size ? partition_size : partition_for(B, Tq, Hq, Hkv, max_seq_len);
+    const int64_t NP = max_seq_len > 0 ? ((int64_t)max_seq_len + P - 1) / P : 1;
+    if (NP <= 1) return 0;
+    const size_t rows = (size_t)B * Tq * Hq;
+    return align256(rows * NP * D * sizeof(float)) + align256(rows * NP * sizeof(float));
+}
+
+int pa_cache_write(const void* k_src, const void* v_src, pa_dtype src_dtype, const int64_t* slot_mapping,
+                   int64_t num_tokens, void* k_cache, void* v_cache, pa_dtype cache_dtype, float* k_scale,
+                   float* v_scale, int64_t num_blocks, int32_t block_size, int32_t Hkv, int32_t D, void* stream) {
+    if (src_dtype != PA_F32 && src_dtype != PA_BF16)
+        return fail(PA_ERR_DTYPE, "source dtype %d not in {f32, bf16}", (int)src_dtype);
+    if (cache_dtype != PA_F32 && cache_dtype != PA_BF16 && cache_dtype != PA_I8)
+        return fail(PA_ERR_DTYPE, "cache dtype %d not in {f32, bf16, i8}", (int)cache_dtype);
+    if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens=%lld must be >= 0", (long long)num_tokens);
+    if (num_blocks < 1) return fail(PA_ERR_SHAPE, "num_blocks=%lld must be >= 1", (long long)num_blocks);
+    if (block_size < 1 || Hkv < 1 || D < 1)
+        return fail(PA_ERR_SHAPE, "block_size=%d, Hkv=%d, D=%d must be >= 1", block_size, Hkv, D);
+    if (block_size != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size=%d (only 16)", block_size);
+    if (!supported_d(D)) return fail(PA_ERR_UNSUPPORTED, "D=%d not in {64, 128, 256}", D);
+    if (!k_cache || !v_cache) return fail(PA_ERR_NULL, "k_cache/v_cache is NULL");
+    if (cache_dtype == PA_I8 && (!k_scale || !v_scale)) return fail(PA_ERR_NULL, "int8 cache needs k_scale and v_scale");
+    if (num_tokens == 0) return ok();
+    if (!k_src || !v_src || !slot_mapping) return fail(PA_ERR_NULL, "k_src/v_src/slot_mapping is NULL");
+    if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PA_ERR_ALIGN, "sources and caches must be 16-byte aligned");
+    pa::CacheWriteParams p{};
+    p.k_src = k_src;
+    p.v_src = v_src;
+    p.src_bf16 = src_dtype == PA_BF16;
+    p.slots = slot_mapping;
+    p.num_tokens = num_tokens;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.Hkv = Hkv;
+    p.D = D;
+    hipError_t e = pa::launch_cache_write((int)cache_dtype, p, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "cache_write launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int pa_decode(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D,
+              const void* k_cache, const void* v_cache, pa_dtype kv_dtype, const float* k_scale,
+              const float* v_scale, int64_t num_blocks, int32_t block_size, const int32_t* block_table,
+              int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+              int32_t partition_size, void* out, pa_dtype out_dtype, float* lse, void* workspace,
+              size_t workspace_bytes, int32_t* num_partitions, void* stream) {
+    if (!num_partitions) return fail(PA_ERR_NULL, "num_partitions is NULL");
+    int rc = check_dims(B, Tq, Hq, Hkv, D);
+    if (rc) return rc;
+    if (q_dtype != PA_F32 && q_dtype != PA_BF16) return fail(PA_ERR_DTYPE, "q dtype %d not in {f32, bf16}", (int)q_dtype);
+    if (kv_dtype != PA_F32 && kv_dtype != PA_BF16 && kv_dtype != PA_I8)
+        return fail(PA_ERR_DTYPE, "kv dtype %d not in {f32, bf16, i8}", (int)kv_dtype);
+    if (out_dtype != PA_F32 && out_dtype != PA_BF16)
+        return fail(PA_ERR_DTYPE, "out dtype %d not in {f32, bf16}", (int)out_dtype);
+    if (block_size < 1) return fail(PA_ERR_SHAPE, "block_size=%d must be >= 1", block_size);
+    if (block_size != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size=%d (only 16)", block_size);
+    if (num_blocks < 1) return fail(PA_ERR_SHAPE, "num_blocks=%lld must be >= 1", (long long)num_blocks);
+    if (max_blocks_per_seq < 1) return fail(PA_ERR_SHAPE, "max_blocks_per_seq=%d must be >= 1", max_blocks_per_seq);
+    if (max_seq_len < 0) return fail(PA_ERR_SHAPE, "max_seq_len=%d must be >= 0", max_seq_len);
+    if ((int64_t)max_blocks_per_seq * block_size < max_seq_len)
+        return fail(PA_ERR_SHAPE, "block table too short: %d blocks * %d < max_seq_len %d", max_blocks_per_seq,
+                    block_size, max_seq_len);
+    if (partition_size < 0 || partition_size % kBlock)
+        return fail(PA_ERR_SHAPE, "partition_size=%d must be 0 or a positive multiple of %d", partition_size, kBlock);
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
+        return fail(PA_ERR_NULL, "q, caches, block_table, seq_lens and out must be non-NULL");
+    if (kv_dtype == PA_I8 && (!k_scale || !v_scale)) return fail(PA_ERR_NULL, "int8 caches need k_scale and v_scale");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return fail(PA_ERR_ALIGN, "q, caches and out must be 16-byte aligned");
+
+    const int32_t P = partition_size ? partition_size : partition_for(B, Tq, Hq, Hkv, max_seq_len);
+    const int64_t NP64 = max_seq_len > 0 ? ((int64_t)max_seq_len + P - 1) / P : 1;
+    if (NP64 > 0x7FFFFFFF) return fail(PA_ERR_SHAPE, "too many partitions");
+    const int32_t NP = (int32_t)NP64;
+    const size_t need = pa_decode_workspace_bytes(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len, P);
+    if (NP > 1 && (!workspace || workspace_bytes < need))
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+    *num_partitions = NP;
+    if (B == 0) return ok();
+
+    const int32_t G = Hq / Hkv;
+    int GT, nchunk;
+    head_chunks(G, &GT, &nchunk);
+    pa::DecodeParams p{};
+    p.q = q;
+    p.q_bf16 = q_dtype == PA_BF16;
+    p.B = B;
+    p.Tq = Tq;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.G = G;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.block_table = block_table;
+    p.max_blocks = max_blocks_per_seq;
+    p.seq_lens = seq_lens;
+    p.qk_scale_log2 = softmax_scale * 1.4426950408889634f;
+    p.P = P;
+    p.NP = NP;
+    p.nchunk = nchunk;
+    p.out = out;
+    p.out_bf16 = out_dtype == PA_BF16;
+    p.lse = lse;
+    if (NP > 1) {
+        const size_t rows = (size_t)B * Tq * Hq;
+        p.ws_o = reinterpret_cast<float*>(workspace);
+        p.ws_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + align256(rows * NP * D * sizeof(float)));
+    }
+    hipError_t e = pa::launch_decode_valu((int)kv_dtype, D, GT, p, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int pa_decode_splitk_reduce(const void* workspace, int32_t num_partitions, int32_t partition_size, int32_t B,
+                            int32_t Tq, int32_t Hq, int32_t D, const int32_t* seq_lens, void* out,
+                            pa_dtype out_dtype, float* lse, void* stream) {
+    if (B < 0 || Tq < 1 || Hq < 1) return fail(PA_ERR_SHAPE, "B=%d, Tq=%d, Hq=%d out of range", B, Tq, Hq);
+    if (!supported_d(D)) return fail(PA_ERR_UNSUPPORTED, "D=%d not in {64, 128, 256}", D);
+    if (num_partitions < 1) return fail(PA_ERR_SHAPE, "num_partitions=%d must be >= 1", num_partitions);
+    if (partition_size < kBlock || partition_size % kBlock)
+        return fail(PA_ERR_SHAPE, "partition_size=%d must be a positive multiple of %d", partition_size, kBlock);
+    if (out_dtype != PA_F32 && out_dtype != PA_BF16)
+        return fail(PA_ERR_DTYPE, "out dtype %d not in {f32, bf16}", (int)out_dtype);
+    if (!workspace || !seq_lens || !out) return fail(PA_ERR_NULL, "workspace, seq_lens and out must be non-NULL");
+    if (B == 0) return ok();
+    const size_t rows = (size_t)B * Tq * Hq;
+    pa::ReduceParams p{};
+    p.ws_o = reinterpret_cast<const float*>(workspace);
+    p.ws_lse = reinterpret_cast<const float*>(reinterpret_cast<const char*>(workspace) +
+                                              align256(rows * num_partitions * D * sizeof(float)));
+    p.NP = num_partitions;
+    p.P = partition_size;
+    p.B = B;
+    p.Tq = Tq;
+    p.Hq = Hq;
+    p.D = D;
+    p.seq_lens = seq_lens;
+    p.out = out;
+    p.out_bf16 = out_dtype == PA_BF16;
+    p.lse = lse;
+    hipError_t e = pa::launch_splitk_reduce(p, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "reduce launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

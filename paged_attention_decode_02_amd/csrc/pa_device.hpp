@@ -1,0 +1,126 @@
+// Device-side helpers shared by the gfx950 paged-attention kernels:
+// element types of the KV cache, raw vector loads, element conversion, and
+// wavefront reductions built on DPP lane permutes (64-lane waves, rows of 16).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum KvType : int { KV_F32 = 0, KV_BF16 = 1, KV_I8 = 2 };
+
+constexpr int kBlockSize = 16;  // tokens per KV block
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int KVT>
+struct Elt {
+    static constexpr int bytes = KVT == KV_F32 ? 4 : (KVT == KV_BF16 ? 2 : 1);
+};
+
+// ---------------------------------------------------------------- raw loads
+// Load NB bytes (NB in {2, 4, 8, 16, 32, 64}) from a 16-byte-aligned (NB>=16)
+// or NB-aligned address into dwords; a 2-byte load fills the low half.
+template <int NB>
+struct Raw {
+    static constexpr int kDwords = NB >= 4 ? NB / 4 : 1;
+    uint32_t w[kDwords];
+};
+
+template <int NB>
+__device__ __forceinline__ void load_raw(Raw<NB>& r, const void* p) {
+    if constexpr (NB >= 16) {
+        const uint4* s = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+        for (int i = 0; i < NB / 16; ++i) {
+            uint4 v = s[i];
+            r.w[4 * i + 0] = v.x;
+            r.w[4 * i + 1] = v.y;
+            r.w[4 * i + 2] = v.z;
+            r.w[4 * i + 3] = v.w;
+        }
+    } else if constexpr (NB == 8) {
+        uint2 v = *reinterpret_cast<const uint2*>(p);
+        r.w[0] = v.x;
+        r.w[1] = v.y;
+    } else if constexpr (NB == 4) {
+        r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else {
+        static_assert(NB == 2, "unsupported load width");
+        r.w[0] = *reinterpret_cast<const uint16_t*>(p);
+    }
+}
+
+// Element e of a raw vector as fp32 (int8: the code itself, exact).
+template <int KVT, int NB>
+__device__ __forceinline__ float elem_f32(const Raw<NB>& r, int e) {
+    if constexpr (KVT == KV_F32) {
+        return __uint_as_float(r.w[e]);
+    } else if constexpr (KVT == KV_BF16) {
+        uint32_t w = r.w[e >> 1];
+        return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    } else {
+        return (float)(int8_t)(r.w[e >> 2] >> (8 * (e & 3)));
+    }
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x0040u);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// ------------------------------------------------------------ lane permutes
+// DPP controls (GCN/CDNA encoding).
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7-i inside each half row
+constexpr int kDppRowMirror = 0x140;      // lane i <-> 15-i inside each row
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a row; every lane of the row gets the same bits
+// (each step adds two partial sums whose order does not change the result).
+__device__ __forceinline__ float row_sum16(float x) {
+    x += dpp_f32<kDppQuadXor1>(x);
+    x += dpp_f32<kDppQuadXor2>(x);
+    x += dpp_f32<kDppRowHalfMirror>(x);
+    x += dpp_f32<kDppRowMirror>(x);
+    return x;
+}
+
+__device__ __forceinline__ float row_max16(float x) {
+    x = fmaxf(x, dpp_f32<kDppQuadXor1>(x));
+    x = fmaxf(x, dpp_f32<kDppQuadXor2>(x));
+    x = fmaxf(x, dpp_f32<kDppRowHalfMirror>(x));
+    x = fmaxf(x, dpp_f32<kDppRowMirror>(x));
+    return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+    x = row_max16(x);
+    x = fmaxf(x, __shfl_xor(x, 16));
+    x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+    x = row_sum16(x);
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+__device__ __forceinline__ float exp2_guarded(float x) {  // exp2 with exp2(-inf) = 0
+    return x == -INFINITY ? 0.0f : exp2f(x);
+}
+
+}  // namespace pa

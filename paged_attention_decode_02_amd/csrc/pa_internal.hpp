@@ -1,0 +1,63 @@
+// Host <-> device parameter blocks and internal launcher declarations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct DecodeParams {
+    const void* q;
+    int q_bf16;  // 0: fp32 queries, 1: bf16 queries
+    int B, Tq, Hq, Hkv, G;
+    const void* k_cache;
+    const void* v_cache;
+    const float* k_scale;
+    const float* v_scale;
+    const int32_t* block_table;
+    int max_blocks;
+    const int32_t* seq_lens;
+    float qk_scale_log2;  // softmax_scale * log2(e)
+    int P;                // partition size in tokens (multiple of 16)
+    int NP;               // partitions per row
+    int nchunk;           // head chunks per kv head (G split into chunks of GT)
+    void* out;
+    int out_bf16;
+    float* lse;
+    float* ws_o;    // [B, Tq, Hq, NP, D] when NP > 1
+    float* ws_lse;  // [B, Tq, Hq, NP]
+};
+
+struct ReduceParams {
+    const float* ws_o;
+    const float* ws_lse;
+    int NP, P, B, Tq, Hq, D;
+    const int32_t* seq_lens;
+    void* out;
+    int out_bf16;
+    float* lse;
+};
+
+struct CacheWriteParams {
+    const void* k_src;
+    const void* v_src;
+    int src_bf16;
+    const int64_t* slots;
+    int64_t num_tokens;
+    void* k_cache;
+    void* v_cache;
+    float* k_scale;
+    float* v_scale;
+    int Hkv, D;
+};
+
+// Launchers return hipSuccess or the launch error.
+hipError_t launch_decode_valu(int kv_type, int D, int GT, const DecodeParams& p, hipStream_t stream);
+hipError_t launch_splitk_reduce(const ReduceParams& p, hipStream_t stream);
+hipError_t launch_cache_write(int cache_type, const CacheWriteParams& p, hipStream_t stream);
+
+// Valid head-chunk widths of the VALU decode instances.
+bool decode_valu_has_gt(int GT);
+
+}  // namespace pa

@@ -1,0 +1,240 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances: max|out - oracle| <= 1e-2 for fp32/bf16 caches and <= 2e-2 for
+int8 caches (fp32 accumulation over bf16/int8 operands); cache bytes and
+block indexing are bit-exact. The oracle runs on the oracle writer's caches,
+the GPU on pa_cache_write's caches, after checking the two are identical.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import paged_attention_decode_02_amd as pa
+from _gpu import cache_bytes_equal, dev, dev_to_host, gpu_cache, gpu_decode, gpu_inputs, host_to_dev
+from _host import oracle_cache, oracle_decode
+from workloads import BLOCK_SIZE, SPECS, generate, scaled
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-2, "bf16": 1e-2, "i8": 2e-2}
+LSE_TOL = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def check(w, got, ref, tag=""):
+    out, lse = got
+    rout, rlse = ref
+    o = dev_to_host(out).astype(np.float64) if out.dtype != torch.bfloat16 else \
+        dev_to_host(out.float())
+    l = dev_to_host(lse).astype(np.float64)
+    err = float(np.max(np.abs(o - rout))) if o.size else 0.0
+    finite = np.isfinite(rlse)
+    lerr = float(np.max(np.abs(l[finite] - rlse[finite]))) if finite.any() else 0.0
+    say("%s %s: max|out-oracle| = %.3e  max|lse-oracle| = %.3e" % (w.spec.name, tag, err, lerr))
+    assert np.all(np.isfinite(o)), "non-finite output"
+    assert np.array_equal(np.isneginf(l), np.isneginf(rlse)), "rows without keys must give lse = -inf"
+    assert err <= TOL[w.spec.cache_dtype], err
+    assert lerr <= LSE_TOL, lerr
+    return err
+
+
+def run_workload(w, partition_size=0, check_cache=True):
+    say("workload %s B=%d Tq=%d Hq=%d Hkv=%d D=%d max_len=%d P=%d" % (
+        w.spec.name, w.spec.B, w.spec.Tq, w.spec.Hq, w.spec.Hkv, w.spec.D, w.max_seq_len, partition_size))
+    host = oracle_cache(w)
+    cache = gpu_cache(w)
+    if check_cache:
+        assert cache_bytes_equal(cache, host), "pa_cache_write differs from the oracle writer"
+    got = gpu_decode(w, cache, partition_size)
+    ref = oracle_decode(w, host)
+    return check(w, got, ref, "P=%d" % partition_size), cache, host, got
+
+
+# ------------------------------------------------------------ full workloads
+@pytest.mark.parametrize("name", ["tiny_f32", "gqa_bf16", "long64k_bf16", "int8_250k", "verify_bf16", "verify_i8"])
+def test_named_workload_full_size(name):
+    w = generate(name)
+    run_workload(w, partition_size=SPECS[name].partition_size)
+    if SPECS[name].partition_size:
+        # also the heuristic's partition size (the benchmark's launch)
+        cache = gpu_cache(w)
+        ref = oracle_decode(w, oracle_cache(w))
+        check(w, gpu_decode(w, cache, 0), ref, "P=heuristic")
+
+
+# ------------------------------------------------------------ dtype / shape grid
+@pytest.mark.parametrize("kv", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("qdt", ["f32", "bf16"])
+def test_dtype_and_head_dim_grid(kv, D, qdt):
+    spec = scaled("gqa_bf16", B=3, Tq=1, Hq=12, Hkv=2, D=D, seq_lens=(1, 700), q_dtype=qdt, src_dtype="f32",
+                  cache_dtype=kv)
+    w = generate(spec, seed=D + len(kv))
+    run_workload(w, partition_size=128)
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 24])
+def test_group_sizes(G):
+    spec = scaled("gqa_bf16", B=2, Tq=1, Hq=2 * G, Hkv=2, D=128, seq_lens=(50, 600))
+    run_workload(generate(spec, seed=G), partition_size=256)
+
+
+@pytest.mark.parametrize("P", [16, 64, 256, 512, 2048, 8192])
+def test_partition_sizes(P):
+    spec = scaled("long64k_bf16", B=2, Tq=1, Hq=12, Hkv=2, D=256, seq_lens=(3000, 6000), peaked_frac=0.01)
+    run_workload(generate(spec, seed=1), partition_size=P)
+
+
+@pytest.mark.parametrize("Tq", [2, 3, 8, 16])
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+def test_query_tokens_causal(Tq, kv):
+    spec = scaled("verify_bf16", B=3, Tq=Tq, Hq=8, Hkv=2, D=128, seq_lens=(Tq, 900), shared_prefix=0,
+                  cache_dtype=kv)
+    run_workload(generate(spec, seed=Tq), partition_size=256)
+
+
+def test_empty_and_short_rows():
+    spec = scaled("verify_bf16", B=5, Tq=4, Hq=4, Hkv=2, D=64, seq_lens=(0, 40), shared_prefix=0)
+    w = generate(spec, seed=3, seq_lens=[0, 1, 3, 4, 37])
+    for P in (16, 0):
+        run_workload(w, partition_size=P)
+
+
+def test_bf16_output():
+    spec = scaled("gqa_bf16", B=2, Tq=1, Hq=8, Hkv=2, D=128, seq_lens=(100, 900))
+    w = generate(spec, seed=4)
+    host = oracle_cache(w)
+    cache = gpu_cache(w)
+    out, lse = gpu_decode(w, cache, 256, out_dtype=torch.bfloat16)
+    rout, _ = oracle_decode(w, host)
+    o = out.float().cpu().numpy()
+    # bf16 output adds at most half a bf16 ulp of |out| to the fp32 error
+    assert np.all(np.abs(o - rout) <= 1e-2 + np.abs(rout) * 2.0 ** -8)
+
+
+# ------------------------------------------------------------ exact indexing
+def test_index_probe_exact():
+    """V rows encode their logical position; one key per row dominates by a
+    logit margin of 128, so every other weight underflows to exactly 0 and the
+    output must decode to that key's position exactly."""
+    B, Hq, Hkv, D = 24, 4, 2, 64
+    rng = np.random.default_rng(5)
+    lens = rng.integers(1, 3000, size=B)
+    lens[:4] = [1, 16, 17, 2047]
+    spec = scaled("gqa_bf16", B=B, Tq=1, Hq=Hq, Hkv=Hkv, D=D, seq_lens=(1, 3000), src_dtype="f32",
+                  cache_dtype="bf16", q_dtype="bf16")
+    w = generate(spec, seed=5, seq_lens=lens)
+    chosen = np.array([int(rng.integers(0, L)) for L in lens])
+    chosen[:4] = [0, 15, 16, 2046]
+    k = np.zeros_like(w.k_src)
+    v = np.zeros_like(w.v_src)
+    v[:, :, 0] = (w.row_pos >> 8)[:, None]
+    v[:, :, 1] = (w.row_pos & 255)[:, None]
+    for b in range(B):
+        i = np.nonzero((w.row_seq == b) & (w.row_pos == chosen[b]))[0][0]
+        k[i, :, 0] = 1024.0
+    w.k_src, w.v_src = k, v
+    w.q[:] = 0.0
+    w.q[..., 0] = 1.0
+    w.q_bits = None
+    w.spec = scaled(w.spec, q_dtype="f32")
+    w.softmax_scale = 0.125
+    cache = gpu_cache(w)
+    for P in (16, 128, 0):
+        out, _ = gpu_decode(w, cache, P)
+        o = out.cpu().numpy()
+        pos = o[:, 0, :, 0] * 256 + o[:, 0, :, 1]
+        assert np.array_equal(pos, np.repeat(chosen[:, None], Hq, axis=1).astype(np.float32)), P
+        assert np.all(o[:, 0, :, 2:] == 0)
+
+
+def test_single_key_is_exact():
+    spec = scaled("gqa_bf16", B=3, Tq=1, Hq=8, Hkv=2, D=256, seq_lens=(1, 1))
+    w = generate(spec, seed=6)
+    host = oracle_cache(w)
+    cache = gpu_cache(w)
+    out, _ = gpu_decode(w, cache)
+    ref, _ = oracle_decode(w, host)
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
+
+
+def test_permuted_table_and_reruns_are_bitwise_identical():
+    spec = scaled("long64k_bf16", B=2, Tq=1, Hq=12, Hkv=2, D=256, seq_lens=(1000, 3000), peaked_frac=0.01)
+    w = generate(spec, seed=7)
+    cache = gpu_cache(w)
+    a, la = gpu_decode(w, cache, 256)
+    b, lb = gpu_decode(w, cache, 256)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    perm = torch.from_numpy(np.random.default_rng(8).permutation(w.num_blocks)).to(dev())
+    moved = []
+    for c in cache:
+        if c is None:
+            moved.append(None)
+            continue
+        m = torch.empty_like(c)
+        m[perm] = c
+        moved.append(m)
+    w.block_table = perm.cpu().numpy()[w.block_table].astype(np.int32)
+    c2, l2 = gpu_decode(w, tuple(moved), 256)
+    assert torch.equal(a, c2) and torch.equal(la, l2)
+
+
+def test_splitk_reduce_entry_point_matches_decode():
+    """decode_partials + splitk_reduce called separately give decode()'s bits."""
+    spec = scaled("gqa_bf16", B=2, Tq=2, Hq=8, Hkv=2, D=128, seq_lens=(500, 1500))
+    w = generate(spec, seed=9)
+    cache = gpu_cache(w)
+    q, table, lens = gpu_inputs(w)
+    k, v, ks, vs = cache
+    ref, rlse = pa.decode(q, k, v, table, lens, w.max_seq_len, w.softmax_scale, partition_size=256)
+    nbytes = pa.workspace_bytes(2, 2, 8, 2, 128, torch.bfloat16, w.max_seq_len, 256)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev())
+    out = torch.empty_like(ref)
+    lse = torch.empty_like(rlse)
+    np_ = pa.decode_partials(q, k, v, table, lens, w.max_seq_len, w.softmax_scale, out, lse, partition_size=256,
+                             workspace=ws)
+    assert np_ == (w.max_seq_len + 255) // 256
+    pa.splitk_reduce(ws, np_, 256, lens, out, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref) and torch.equal(lse, rlse)
+
+
+def test_cache_write_skips_negative_slots_and_writes_bits():
+    for cache_dtype in ("f32", "bf16", "i8"):
+        for src in ("f32", "bf16"):
+            spec = scaled("gqa_bf16", B=2, Hq=4, Hkv=2, D=64, seq_lens=(30, 70), src_dtype=src,
+                          cache_dtype=cache_dtype)
+            w = generate(spec, seed=10)
+            w.slot_mapping = w.slot_mapping.copy()
+            w.slot_mapping[::7] = -1
+            host = oracle_cache(w, poison=False)
+            cache = gpu_cache(w)
+            # skipped rows' slots stay poisoned on the GPU; compare only written slots
+            written = w.slot_mapping[w.slot_mapping >= 0]
+            blk, off = written // BLOCK_SIZE, written % BLOCK_SIZE
+            for g, h in zip(cache, host):
+                if g is None:
+                    continue
+                a = dev_to_host(g)[blk, off]
+                hb = h[blk, off]
+                if a.dtype == np.float32:
+                    assert np.array_equal(a.view(np.uint32), hb.view(np.uint32))
+                else:
+                    assert np.array_equal(a, hb)
+            # slots of skipped rows were never written: still poison
+            sk_rows = np.arange(w.slot_mapping.size)[::7]
+            b_ = w.row_seq[sk_rows]
+            p_ = w.row_pos[sk_rows]
+            sslots = w.block_table[b_, p_ // BLOCK_SIZE].astype(np.int64) * BLOCK_SIZE + p_ % BLOCK_SIZE
+            kc = dev_to_host(cache[0]).reshape(-1, spec.Hkv, spec.D)[sslots]
+            if kc.dtype == np.int8:
+                assert np.all(kc == 127)
+            elif kc.dtype == np.uint16:
+                assert np.all(kc == 0x7FC0)
+            else:
+                assert np.all(np.isnan(kc))
