@@ -1,0 +1,295 @@
+"""Paged-attention decode benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole decode hot path over one batch: pa_cache_write
+of the B*Tq new tokens' K/V rows, the split-K decode kernel, and (when there
+is more than one partition) the log-sum-exp reduce. Inputs are synthetic and
+seeded (workloads.generate) and already resident in HBM when timing starts.
+Default workload: long-context decode at 64K tokens per sequence (B=4,
+Hq=24, Hkv=4, D=256, bf16 KV).
+
+Printed: ONE JSON line with the metric (algorithmic KV-read GB/s), the step
+time, a roofline object for the decode kernel (its algorithmic bytes per
+launch over its average launch time, measured with HIP events on the launch
+stream) and a CPU baseline (the fp64 oracle timed on this host on a bounded
+sample of the same workload).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+METRIC = "paged-attn decode KV-read GB/s (% of HBM peak) and µs/step at 64K ctx"
+DEFAULT_WORKLOAD = "long64k_bf16"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w) -> dict:
+    """Bytes the method must move per decode step (the split-K workspace is
+    implementation overhead and is reported apart)."""
+    sp = w.spec
+    elt = {"f32": 4, "bf16": 2, "i8": 1}[sp.cache_dtype]
+    qelt = 4 if sp.q_dtype == "f32" else 2
+    L = w.seq_lens.astype(np.int64)
+    kv = int(L.sum()) * sp.Hkv * sp.D * 2 * elt
+    scales = int(L.sum()) * sp.Hkv * 2 * 4 if sp.cache_dtype == "i8" else 0
+    table = int(((L + 15) // 16).sum()) * 4
+    q = sp.B * sp.Tq * sp.Hq * sp.D * qelt
+    out = sp.B * sp.Tq * sp.Hq * (sp.D + 1) * 4
+    return {"kv": kv, "scales": scales, "table": table, "q": q, "out": out,
+            "total": kv + scales + table + q + out}
+
+
+def kernel_source_digest() -> str:
+    """Digest of the decode kernel's sources (ties committed counters to code)."""
+    h = hashlib.sha256()
+    for f in ("decode_valu.hip", "pa_device.hpp", "pa_internal.hpp"):
+        p = os.path.join(ROOT, "paged_attention_decode_02_amd", "csrc", f)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str):
+    """Per-launch HBM bytes from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on different kernel sources."""
+    p = os.path.join(ROOT, "profiles", "decode_%s_hbm_traffic.md" % workload)
+    if not os.path.exists(p):
+        return None
+    text = open(p).read()
+    m = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
+    if not m or not t or m.group(1) != kernel_source_digest():
+        return None
+    return int(t.group(1))
+
+
+def run_cpu_baseline(w, bytes_per_step: int, budget_s: float) -> dict:
+    import oracle
+    from workloads import BLOCK_SIZE
+
+    sp = w.spec
+    t0 = time.time()
+    k, v, ks, vs = oracle.alloc_cache(w.num_blocks, BLOCK_SIZE, sp.Hkv, sp.D, sp.cache_dtype)
+    oracle.cache_write(w.k_src, w.v_src, w.slot_mapping, k, v, ks, vs)
+    log("cpu baseline: oracle cache built in %.1f s" % (time.time() - t0))
+    rows_total = sp.B * sp.Tq * sp.Hq
+    # rows of sequence-major order, in chunks, until the time budget is used
+    order = np.arange(rows_total, dtype=np.int64)
+    threads = oracle.max_threads()
+    chunk = max(1, min(rows_total, threads))
+    done, spent = 0, 0.0
+    while done < rows_total and spent < budget_s:
+        rows = order[done: done + chunk]
+        t = time.perf_counter()
+        oracle.decode(w.q_array(), k, v, w.block_table, w.seq_lens, w.softmax_scale, ks, vs, rows=rows,
+                      nthreads=threads)
+        spent += time.perf_counter() - t
+        done += rows.size
+        log("cpu baseline: %d/%d rows, %.1f s" % (done, rows_total, spent))
+    # rows of one sequence all cost the same here; scale the sample to a step
+    step_s = spent * rows_total / done
+    return {"value": round(bytes_per_step / step_s / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle", "ms_per_step": round(step_s * 1e3, 3),
+            "sample": "%d of %d (b,t,h) rows of %s, fp64 oracle, %d OpenMP threads, scaled to one step"
+                      % (done, rows_total, sp.name, threads)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--partition-size", type=int, default=0, help="0 = the library's heuristic")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-mb", type=int, default=512, help="flush buffer for the cold-cache side measurement")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="after the benchmark, run 3 plain device copies of this many MiB (a kernel of known "
+                         "traffic for scaling rocprofv3's FETCH_SIZE/WRITE_SIZE counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this decode library runs on a single MI355X "
+              "(sharding across GPUs is described in DESIGN.md, not built); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_attention_decode_02_amd as pa
+    from workloads import BLOCK_SIZE, SPECS, generate
+
+    if not os.path.exists(pa.library_path()):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    pa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = SPECS[args.workload]
+
+    t0 = time.time()
+    w = generate(spec)
+    log("generated %s in %.1f s" % (spec.name, time.time() - t0))
+    sp = w.spec
+    TD = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}
+
+    def up(a, dt):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    shape = (w.num_blocks, BLOCK_SIZE, sp.Hkv, sp.D)
+    kc = torch.zeros(shape, dtype=TD[sp.cache_dtype], device=dev)
+    vc = torch.zeros_like(kc)
+    ks = vs = None
+    if sp.cache_dtype == "i8":
+        ks = torch.zeros(shape[:3], dtype=torch.float32, device=dev)
+        vs = torch.zeros_like(ks)
+    N = w.slot_mapping.shape[0]
+    step = 1 << 20
+    for s in range(0, N, step):
+        e = min(N, s + step)
+        pa.cache_write(up(w.k_src[s:e], sp.src_dtype), up(w.v_src[s:e], sp.src_dtype),
+                       torch.from_numpy(w.slot_mapping[s:e]).to(dev), kc, vc, ks, vs)
+    rows = w.step_rows()
+    new_k = up(w.k_src[rows], sp.src_dtype)
+    new_v = up(w.v_src[rows], sp.src_dtype)
+    new_slots = torch.from_numpy(w.slot_mapping[rows]).to(dev)
+    q = up(w.q_array(), sp.q_dtype)
+    table = torch.from_numpy(w.block_table).to(dev)
+    lens = torch.from_numpy(w.seq_lens).to(dev)
+    P = args.partition_size or pa.choose_partition_size(sp.B, sp.Tq, sp.Hq, sp.Hkv, sp.D, TD[sp.cache_dtype],
+                                                        w.max_seq_len)
+    ws_bytes = pa.workspace_bytes(sp.B, sp.Tq, sp.Hq, sp.Hkv, sp.D, TD[sp.cache_dtype], w.max_seq_len, P)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty((sp.B, sp.Tq, sp.Hq, sp.D), dtype=torch.float32, device=dev)
+    lse = torch.empty((sp.B, sp.Tq, sp.Hq), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    state = {"np": 1}
+
+    def one_step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        pa.cache_write(new_k, new_v, new_slots, kc, vc, ks, vs)
+        if ev is not None:
+            ev[1].record(stream)
+        state["np"] = pa.decode_partials(q, kc, vc, table, lens, w.max_seq_len, w.softmax_scale, out, lse, ks, vs,
+                                         P, ws)
+        if ev is not None:
+            ev[2].record(stream)
+        if state["np"] > 1:
+            pa.splitk_reduce(ws, state["np"], P, lens, out, lse)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, events between the kernels of every step
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        one_step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    cw = [e[0].elapsed_time(e[1]) for e in evs]
+    dk = [e[1].elapsed_time(e[2]) for e in evs]
+    rk = [e[2].elapsed_time(e[3]) for e in evs]
+    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
+
+    # ---- side measurement: every step after a flush of the caches (not the metric)
+    flush = torch.empty(args.flush_mb << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(min(20, args.steps)):
+        flush.fill_(i & 0xFF)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        one_step(e)
+        torch.cuda.synchronize()
+        cold.append(e[1].elapsed_time(e[3]))
+    del flush
+
+    ab = algorithmic_bytes(w)
+    ms_per_step = wall * 1e3 / args.steps
+    value = ab["total"] / (ms_per_step * 1e-3) / 1e9
+    dec_avg_ms = float(np.mean(dk))
+    achieved = ab["total"] / (dec_avg_ms * 1e-3) / 1e9
+    ws_traffic = 0
+    if state["np"] > 1:
+        ws_traffic = 2 * sp.B * sp.Tq * sp.Hq * state["np"] * (sp.D + 1) * 4
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": sp.cache_dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": sp.name, "B": sp.B, "Tq": sp.Tq, "Hq": sp.Hq, "Hkv": sp.Hkv, "D": sp.D,
+            "block_size": BLOCK_SIZE, "seq_lens": "%d..%d" % (w.seq_lens.min(), w.seq_lens.max()),
+            "kv_dtype": sp.cache_dtype, "q_dtype": sp.q_dtype, "partition_size": P,
+            "num_partitions": state["np"], "algorithmic_bytes_per_step": ab["total"],
+            "splitk_workspace_bytes_per_step": ws_traffic,
+        },
+        "breakdown_us": {
+            "cache_write": round(1e3 * float(np.mean(cw)), 2),
+            "decode": round(1e3 * dec_avg_ms, 2),
+            "reduce": round(1e3 * float(np.mean(rk)), 2),
+            "step_events": round(1e3 * float(np.median(step_ms)), 2),
+            "decode_plus_reduce_after_flush": round(1e3 * float(np.median(cold)), 2),
+        },
+        "roofline": {
+            "kernel": "decode_valu_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": committed_traffic(sp.name),
+            "kernel_source_digest": kernel_source_digest(),
+        },
+    }
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = n
+        del src, dst
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = run_cpu_baseline(w, ab["total"], args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

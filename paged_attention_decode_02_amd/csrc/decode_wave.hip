@@ -1,0 +1,606 @@
+// Split-K paged decode on the vector ALUs for bf16 and int8 KV caches
+// (query groups below an MFMA tile): one 64-lane wave per workgroup.
+//
+// A wave handles one split-K partition of P tokens of one kv head g, one
+// query token t of one sequence b, and GT query heads of g's group, so every
+// K/V byte is read once for all GT heads (grouped-query attention). The
+// split-K decode keeps per-partition softmax statistics (vllm-sm70 page,
+// "Why", Attention bullet: split-K paged decode with an int8 KV cache); the
+// log-sum-exp reduce merges partitions. Per 16-token KV block:
+//
+// QK. Row r (16 lanes) of the wave takes tokens r, r+4, r+8, r+12 ("slots");
+// lane c of a row holds D/16 consecutive elements of a key row, so a row
+// reads whole contiguous key rows. Partial dot products use v_dot2 (bf16
+// pairs against bf16 queries; for int8, codes turned into f16 by a byte
+// permute against f16 queries scaled by a power of two). The 4 slots x GT
+// heads partial sums are then reduced across the row by a *transposed*
+// butterfly: four DPP steps (row_mirror, row_half_mirror, quad xor 2, quad
+// xor 1) each add a partner lane's half of the items, so that afterwards each
+// lane owns whole scores of distinct (token, head) items instead of every
+// lane holding every score. This works because the lanes' registers are laid
+// out with the halves swapped between partners: which token a K register holds
+// (load address) and which head a q register holds (query load) depend on
+// the lane's coordinates in the basis {15, 7, 2, 1} of the four DPP pairings.
+//
+// Softmax. Scores are in log2 units against a per-head reference m that is
+// raised only when some score exceeds it by more than 2^8 (then o and l are
+// rescaled); otherwise p = exp2(s - m) <= 256 and the result is exact anyway
+// because o and l share the reference. Each exp is computed once.
+//
+// PV. The probabilities go through a 0.5 KB per-wave LDS buffer to the PV
+// layout, in which a group of lanes takes one whole value row (16-byte or
+// smaller loads, D*elt/4 lanes per token) and lane i owns D/64 (or more)
+// output elements for all GT heads. bf16 values use fp32 FMA; int8 values
+// use v_dot2 over pairs of tokens: the probabilities (times the value scale)
+// as f16 pairs and the codes as (1024 + code + 128) f16 pairs, with
+// 1152 * sum(p) subtracted once at the end.
+//
+// Loads are ping-ponged: the V block is requested before the QK of the same
+// block, the next K block before the PV, so one half-block is always in
+// flight per wave.
+#include "pa_device.hpp"
+#include "pa_internal.hpp"
+
+namespace pa {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf162_t;
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a), __builtin_bit_cast(bf162_t, b), c, false);
+}
+
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+}
+
+constexpr uint32_t kMagic = 0x64646464u;  // f16 0x64xx = 1024 + xx
+constexpr float kCodeBias = 1152.0f;      // 1024 + 128
+
+// Bytes 0,1 (lo) or 2,3 (hi) of biased codes u (= code ^ 0x80) as f16 (1024 + u).
+__device__ __forceinline__ uint32_t f16pair_lo(uint32_t u) { return __builtin_amdgcn_perm(kMagic, u, 0x04010400u); }
+__device__ __forceinline__ uint32_t f16pair_hi(uint32_t u) { return __builtin_amdgcn_perm(kMagic, u, 0x04030402u); }
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+    return (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float add_dpp(float own, float partner_src) {
+    return own + dpp_f32<CTRL>(partner_src);
+}
+
+// Number of (token, head) items a lane owns after the transposed reduction,
+// and how the heads were split at the two quad levels.
+template <int GT>
+struct Split {
+    static constexpr bool kC = GT % 2 == 0;  // level C halves the heads
+    static constexpr int kAfterC = kC ? GT / 2 : GT;
+    static constexpr bool kD = kAfterC % 2 == 0;  // level D halves them again
+    static constexpr int kItems = kD ? kAfterC / 2 : kAfterC;
+};
+
+// Head held in q register h by a lane with quad coordinates (cc, dd).
+template <int GT>
+__device__ __forceinline__ int head_of(int h, int cc, int dd) {
+    if constexpr (Split<GT>::kC) {
+        constexpr int H2 = GT / 2;
+        int half = (h / H2) ^ cc;
+        int hh = h % H2;
+        if constexpr (Split<GT>::kD) hh = (hh + (H2 / 2) * dd) % H2;
+        return half * H2 + hh;
+    } else {
+        return h;
+    }
+}
+
+}  // namespace
+
+template <int KVT, int D, int GT, int QS>
+__global__ __launch_bounds__(64) void decode_wave_kernel(DecodeParams p) {
+    static_assert(KVT == KV_BF16 || KVT == KV_I8, "bf16 or int8 caches");
+    constexpr bool I8 = KVT == KV_I8;
+    constexpr int E = Elt<KVT>::bytes;
+    constexpr int KB = D * E / 16;  // key bytes per lane per token (QK layout)
+    constexpr int KW = KB / 4;      // ... in dwords
+    constexpr int QW = D / 32;      // q dwords (element pairs) per head per lane
+    constexpr int NI = Split<GT>::kItems;
+    constexpr int GP = (GT + 3) / 4 * 4;  // padded heads per token in the LDS p buffer
+    // PV layout: LPT lanes per value row (each >= 4 bytes), TPW rows per wave step
+    constexpr int RB = D * E;  // row bytes
+    constexpr int LPT = RB / 4 >= 64 ? 64 : RB / 4;
+    constexpr int TPW = 64 / LPT;
+    constexpr int VB = RB / LPT;  // value bytes per lane per token
+    constexpr int EV = VB / E;    // value elements per lane per token
+    constexpr int STEPS = kBlockSize / TPW;
+    static_assert(KB >= 4 && VB >= 4, "layout");
+    static_assert(!I8 || STEPS % 2 == 0, "int8 pairs tokens");
+
+    __shared__ __align__(16) float pbuf_f[kBlockSize * GP];  // bf16: p[token][head]
+    uint32_t* pbuf_u = reinterpret_cast<uint32_t*>(pbuf_f);  // int8: f16 pairs [token/2][head]
+
+    const int lane = threadIdx.x;
+    const int r = lane >> 4, c16 = lane & 15;
+    // coordinates of the lane in the basis of the DPP pairings {15, 7, 2, 1}
+    const int b0 = c16 & 1, b1 = (c16 >> 1) & 1, b2 = (c16 >> 2) & 1, b3 = (c16 >> 3) & 1;
+    const int ca = b3, cb = b2 ^ b3, cc = b1 ^ b2, cd = b0 ^ b2;
+    const int sx = 2 * ca + cb;      // slot swap pattern of this lane
+    const int my_tok = 4 * sx + r;   // token (within a block) of the items this lane owns
+    const int vgrp = lane / LPT, vl = lane % LPT;  // PV layout
+
+    int wg = blockIdx.x;
+    const int part = wg % p.NP;
+    wg /= p.NP;
+    const int chunk = wg % p.nchunk;
+    wg /= p.nchunk;
+    const int g = wg % p.Hkv;
+    wg /= p.Hkv;
+    const int t = wg % p.Tq;
+    const int b = wg / p.Tq;
+
+    const int n = p.seq_lens[b] - p.Tq + t + 1;
+    const int start = part * p.P;
+    const int hbase = g * p.G + chunk * GT;
+    const int nh = min(GT, p.G - chunk * GT);
+    const int64_t rowbase = ((int64_t)b * p.Tq + t) * p.Hq + hbase;  // flat row id of head hbase
+    if (start >= n) {
+        if (p.NP == 1) {
+            for (int r2 = 0; r2 < nh; ++r2) {
+                for (int d = lane; d < D; d += 64) {
+                    if (p.out_bf16)
+                        reinterpret_cast<uint16_t*>(p.out)[(rowbase + r2) * D + d] = 0;
+                    else
+                        reinterpret_cast<float*>(p.out)[(rowbase + r2) * D + d] = 0.0f;
+                }
+                if (p.lse != nullptr && lane == 0) p.lse[rowbase + r2] = -INFINITY;
+            }
+        }
+        return;
+    }
+    const int end = min(start + p.P, n);
+
+    // ---------------------------------------------------------------- queries
+    // q register h holds head head_of(h) for the lane's D/16 elements.
+    uint32_t qv[GT][QW];
+    uint32_t ql[QS == 2 ? GT : 1][QW];
+    float qpost;  // factor turning a reduced dot product into log2 units
+    float corr[NI];  // int8: 1152 * sum_d q'[head], in the item layout
+    {
+        float qf[GT][2 * QW];
+        float qmax = 0.0f;
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+            const int hh = head_of<GT>(h, cc, cd);
+            const bool valid = hh < nh;
+            const int64_t off = (rowbase + (valid ? hh : 0)) * D + c16 * (D / 16);
+#pragma unroll
+            for (int e = 0; e < 2 * QW; ++e) {
+                float v = p.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(p.q)[off + e])
+                                   : reinterpret_cast<const float*>(p.q)[off + e];
+                qf[h][e] = valid ? v : 0.0f;
+                qmax = fmaxf(qmax, fabsf(qf[h][e]));
+            }
+        }
+        if constexpr (I8) {
+            // one power-of-two scale for all heads puts max|q| in [2^14, 2^15)
+            qmax = wave_max(qmax);
+            const int e2 = qmax > 0.0f ? 14 - ilogbf(qmax) : 0;
+            const float sc = ldexpf(1.0f, e2);
+            qpost = ldexpf(p.qk_scale_log2, -e2);
+            float qs[GT];
+#pragma unroll
+            for (int h = 0; h < GT; ++h) {
+                qs[h] = 0.0f;
+#pragma unroll
+                for (int i = 0; i < QW; ++i) {
+                    const float x0 = qf[h][2 * i] * sc, x1 = qf[h][2 * i + 1] * sc;
+                    const uint32_t hi = pack_f16(x0, x1);
+                    qv[h][i] = hi;
+                    const half2_t hh = __builtin_bit_cast(half2_t, hi);
+                    float s = (float)hh.x + (float)hh.y;
+                    if constexpr (QS == 2) {
+                        const uint32_t lo = pack_f16(x0 - (float)hh.x, x1 - (float)hh.y);
+                        ql[h][i] = lo;
+                        const half2_t ll = __builtin_bit_cast(half2_t, lo);
+                        s += (float)ll.x + (float)ll.y;
+                    }
+                    qs[h] += s;
+                }
+                // plain sums over the slot levels (heads do not change there)
+                qs[h] += dpp_f32<kDppRowMirror>(qs[h]);
+                qs[h] += dpp_f32<kDppRowHalfMirror>(qs[h]);
+            }
+            // head levels exactly as for the scores
+            float c2[GT];
+#pragma unroll
+            for (int h = 0; h < GT; ++h) c2[h] = qs[h];
+            if constexpr (Split<GT>::kC) {
+#pragma unroll
+                for (int h = 0; h < GT / 2; ++h) c2[h] = add_dpp<kDppQuadXor2>(c2[h], c2[h + GT / 2]);
+            } else {
+#pragma unroll
+                for (int h = 0; h < GT; ++h) c2[h] = add_dpp<kDppQuadXor2>(c2[h], c2[h]);
+            }
+            constexpr int AC = Split<GT>::kAfterC;
+            if constexpr (Split<GT>::kD) {
+#pragma unroll
+                for (int h = 0; h < AC / 2; ++h) c2[h] = add_dpp<kDppQuadXor1>(c2[h], c2[h + AC / 2]);
+            } else {
+#pragma unroll
+                for (int h = 0; h < AC; ++h) c2[h] = add_dpp<kDppQuadXor1>(c2[h], c2[h]);
+            }
+#pragma unroll
+            for (int j = 0; j < NI; ++j) corr[j] = kCodeBias * c2[j];
+        } else {
+            qpost = p.qk_scale_log2;
+#pragma unroll
+            for (int h = 0; h < GT; ++h) {
+#pragma unroll
+                for (int i = 0; i < QW; ++i) {
+                    const float x0 = qf[h][2 * i], x1 = qf[h][2 * i + 1];
+                    const uint32_t hi = pack_bf16(x0, x1);
+                    qv[h][i] = hi;
+                    if constexpr (QS == 2) {
+                        ql[h][i] = pack_bf16(x0 - bf16_to_f32((uint16_t)hi), x1 - bf16_to_f32((uint16_t)(hi >> 16)));
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NI; ++j) corr[j] = 0.0f;
+        }
+    }
+
+    // heads of the lane's items
+    int ihead[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) ihead[j] = head_of<GT>(j, cc, cd);
+
+    // ------------------------------------------------------- partition state
+    float mref[GT];  // per-head reference (log2 units), uniform across the wave
+    float mloc[NI];  // mref of the lane's item heads
+    float lloc[NI];  // partial sums of p over the lane's items
+    float sloc[NI];  // int8: partial sums of the f16 probabilities (times value scales)
+    float o[GT][EV];
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+        mref[h] = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < EV; ++e) o[h][e] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+        mloc[j] = -INFINITY;
+        lloc[j] = 0.0f;
+        sloc[j] = 0.0f;
+    }
+
+    const int32_t* table = p.block_table + (int64_t)b * p.max_blocks;
+    const int64_t tok_stride = (int64_t)p.Hkv * D * E;  // bytes between consecutive tokens of a block
+    const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (int64_t)g * D * E;
+    const char* vbase = reinterpret_cast<const char*>(p.v_cache) + (int64_t)g * D * E;
+    const int j0 = start / kBlockSize, jend = (end + kBlockSize - 1) / kBlockSize;
+
+    // int8: value probabilities are scaled by 2^vsh so that p * v_scale * 2^vsh
+    // stays below 2^15 (f16) for every token of the partition (p <= 2^8)
+    float vsh = 1.0f, vsh_inv = 1.0f;
+    if constexpr (I8) {
+        float vmax = 0.0f;
+        for (int j = j0 + (lane >> 4); j < jend; j += 4) {
+            const int64_t ph = table[j];
+            const float sv = p.v_scale[(ph * kBlockSize + c16) * p.Hkv + g];
+            const int pos = j * kBlockSize + c16;
+            if (pos < end) vmax = fmaxf(vmax, sv);
+        }
+        vmax = wave_max(vmax);
+        const int e2 = vmax > 0.0f ? 6 - ilogbf(vmax) : 0;
+        vsh = ldexpf(1.0f, e2);
+        vsh_inv = ldexpf(1.0f, -e2);
+    }
+
+    // K registers: register s holds slot s ^ sx (token 4 * (s ^ sx) + r)
+    Raw<KB> kr[4];
+    Raw<VB> vr[STEPS];
+    int64_t phys = table[j0];
+    auto load_k = [&](int64_t ph) {
+        const char* base = kbase + ph * kBlockSize * tok_stride + c16 * KB;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) load_raw<KB>(kr[s], base + (4 * (s ^ sx) + r) * tok_stride);
+    };
+    auto load_v = [&](int64_t ph) {
+        const char* base = vbase + ph * kBlockSize * tok_stride + vl * VB;
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) load_raw<VB>(vr[st], base + (st * TPW + vgrp) * tok_stride);
+    };
+    load_k(phys);
+
+    for (int j = j0; j < jend; ++j) {
+        const int pos0 = j * kBlockSize;
+        load_v(phys);
+        const int64_t phys_next = (j + 1 < jend) ? (int64_t)table[j + 1] : phys;
+
+        // ---------------------------------------------------------------- QK
+        float ps[4][GT];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int h = 0; h < GT; ++h) {
+                float acc = 0.0f;
+                if constexpr (I8) {
+#pragma unroll
+                    for (int w = 0; w < KW; ++w) {
+                        const uint32_t u = kr[s].w[w] ^ 0x80808080u;
+                        acc = dot2_f16(qv[h][2 * w], f16pair_lo(u), acc);
+                        acc = dot2_f16(qv[h][2 * w + 1], f16pair_hi(u), acc);
+                        if constexpr (QS == 2) {
+                            acc = dot2_f16(ql[h][2 * w], f16pair_lo(u), acc);
+                            acc = dot2_f16(ql[h][2 * w + 1], f16pair_hi(u), acc);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int w = 0; w < KW; ++w) {
+                        acc = dot2_bf16(qv[h][w], kr[s].w[w], acc);
+                        if constexpr (QS == 2) acc = dot2_bf16(ql[h][w], kr[s].w[w], acc);
+                    }
+                }
+                ps[s][h] = acc;
+            }
+        }
+        // next block's keys go out now; they are not needed before the next QK
+        if (j + 1 < jend) load_k(phys_next);
+
+        // transposed reduction across the row
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int h = 0; h < GT; ++h) ps[s][h] = add_dpp<kDppRowMirror>(ps[s][h], ps[s + 2][h]);
+#pragma unroll
+        for (int h = 0; h < GT; ++h) ps[0][h] = add_dpp<kDppRowHalfMirror>(ps[0][h], ps[1][h]);
+        float x[GT];
+#pragma unroll
+        for (int h = 0; h < GT; ++h) x[h] = ps[0][h];
+        if constexpr (Split<GT>::kC) {
+#pragma unroll
+            for (int h = 0; h < GT / 2; ++h) x[h] = add_dpp<kDppQuadXor2>(x[h], x[h + GT / 2]);
+        } else {
+#pragma unroll
+            for (int h = 0; h < GT; ++h) x[h] = add_dpp<kDppQuadXor2>(x[h], x[h]);
+        }
+        constexpr int AC = Split<GT>::kAfterC;
+        if constexpr (Split<GT>::kD) {
+#pragma unroll
+            for (int h = 0; h < AC / 2; ++h) x[h] = add_dpp<kDppQuadXor1>(x[h], x[h + AC / 2]);
+        } else {
+#pragma unroll
+            for (int h = 0; h < AC; ++h) x[h] = add_dpp<kDppQuadXor1>(x[h], x[h]);
+        }
+
+        // scores of the lane's items, log2 units; masked past the end
+        const bool tok_ok = pos0 + my_tok < end;
+        float ksc = qpost;
+        if constexpr (I8) ksc *= p.k_scale[(phys * kBlockSize + my_tok) * p.Hkv + g];
+        float sc[NI];
+        bool raise = false;
+#pragma unroll
+        for (int j2 = 0; j2 < NI; ++j2) {
+            const bool ok = tok_ok && ihead[j2] < nh;
+            sc[j2] = ok ? (x[j2] - corr[j2]) * ksc : -INFINITY;
+            raise |= sc[j2] > mloc[j2] + 8.0f;
+        }
+
+        // ------------------------------------------- raise the references (rare)
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+#pragma unroll
+            for (int h = 0; h < GT; ++h) {
+                float v = -INFINITY;
+#pragma unroll
+                for (int j2 = 0; j2 < NI; ++j2) v = ihead[j2] == h ? fmaxf(v, sc[j2]) : v;
+                const float bm = wave_max(v);
+                const float mn = fmaxf(mref[h], bm);
+                const float base = mn == -INFINITY ? 0.0f : mn;
+                const float alpha = exp2_guarded(mref[h] - base);
+                mref[h] = mn;
+#pragma unroll
+                for (int e = 0; e < EV; ++e) o[h][e] *= alpha;
+#pragma unroll
+                for (int j2 = 0; j2 < NI; ++j2) {
+                    if (ihead[j2] == h) {
+                        lloc[j2] *= alpha;
+                        sloc[j2] *= alpha;
+                        mloc[j2] = mn;
+                    }
+                }
+            }
+        }
+
+        // ------------------------------------------------- probabilities -> LDS
+        float sv = 1.0f;
+        if constexpr (I8) sv = p.v_scale[(phys * kBlockSize + my_tok) * p.Hkv + g] * vsh;
+#pragma unroll
+        for (int j2 = 0; j2 < NI; ++j2) {
+            const float base = mloc[j2] == -INFINITY ? 0.0f : mloc[j2];
+            const float pr = sc[j2] == -INFINITY ? 0.0f : exp2f(sc[j2] - base);
+            lloc[j2] += pr;
+            if constexpr (I8) {
+                const _Float16 ph = (_Float16)(tok_ok ? pr * sv : 0.0f);
+                sloc[j2] += (float)ph;
+                reinterpret_cast<_Float16*>(pbuf_u)[((my_tok >> 1) * GP + ihead[j2]) * 2 + (my_tok & 1)] = ph;
+            } else {
+                pbuf_f[my_tok * GP + ihead[j2]] = pr;
+            }
+        }
+        __syncthreads();
+
+        // ---------------------------------------------------------------- PV
+        if constexpr (I8) {
+#pragma unroll
+            for (int st = 0; st < STEPS; st += 2) {
+                const int tk = st * TPW + vgrp;  // tokens tk and tk + TPW share a p pair when TPW == 1
+                // token pair (tk, tk + TPW): the LDS pairs are (2k, 2k + 1); with TPW > 1
+                // the two tokens of a lane are not adjacent, so read them separately
+                uint32_t pp[GT];
+                if constexpr (TPW == 1) {
+#pragma unroll
+                    for (int h = 0; h < GT; ++h) pp[h] = pbuf_u[(tk >> 1) * GP + h];
+                } else {
+                    const _Float16* ph = reinterpret_cast<const _Float16*>(pbuf_u);
+                    const int t1 = tk + TPW;
+#pragma unroll
+                    for (int h = 0; h < GT; ++h) {
+                        const uint16_t lo = __builtin_bit_cast(uint16_t, ph[((tk >> 1) * GP + h) * 2 + (tk & 1)]);
+                        const uint16_t hi = __builtin_bit_cast(uint16_t, ph[((t1 >> 1) * GP + h) * 2 + (t1 & 1)]);
+                        pp[h] = (uint32_t)lo | ((uint32_t)hi << 16);
+                    }
+                }
+#pragma unroll
+                for (int w = 0; w < VB / 4; ++w) {
+                    // codes are always finite and masked tokens carry p = 0: no select
+                    const uint32_t A = vr[st].w[w];
+                    const uint32_t B = vr[st + 1].w[w];
+                    const uint32_t x0 = __builtin_amdgcn_perm(B, A, 0x05010400u) ^ 0x80808080u;  // a0 b0 a1 b1
+                    const uint32_t x1 = __builtin_amdgcn_perm(B, A, 0x07030602u) ^ 0x80808080u;  // a2 b2 a3 b3
+                    const uint32_t f0 = f16pair_lo(x0), f1 = f16pair_hi(x0);
+                    const uint32_t f2 = f16pair_lo(x1), f3 = f16pair_hi(x1);
+#pragma unroll
+                    for (int h = 0; h < GT; ++h) {
+                        o[h][4 * w + 0] = dot2_f16(pp[h], f0, o[h][4 * w + 0]);
+                        o[h][4 * w + 1] = dot2_f16(pp[h], f1, o[h][4 * w + 1]);
+                        o[h][4 * w + 2] = dot2_f16(pp[h], f2, o[h][4 * w + 2]);
+                        o[h][4 * w + 3] = dot2_f16(pp[h], f3, o[h][4 * w + 3]);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st) {
+                const int tk = st * TPW + vgrp;
+                const bool ok = pos0 + tk < end;
+                float pr[GT];
+#pragma unroll
+                for (int h = 0; h < GT; ++h) pr[h] = pbuf_f[tk * GP + h];
+#pragma unroll
+                for (int e = 0; e < EV; ++e) {
+                    const float v = ok ? elem_f32<KV_BF16>(vr[st], e) : 0.0f;
+#pragma unroll
+                    for (int h = 0; h < GT; ++h) o[h][e] = fmaf(pr[h], v, o[h][e]);
+                }
+            }
+        }
+        __syncthreads();
+        phys = phys_next;
+    }
+
+    // ------------------------------------------------------------ epilogue
+    // lane groups of the PV layout hold disjoint token subsets: add them
+    if constexpr (TPW > 1) {
+#pragma unroll
+        for (int h = 0; h < GT; ++h)
+#pragma unroll
+            for (int e = 0; e < EV; ++e) {
+                float v = o[h][e];
+                for (int off = LPT; off < 64; off <<= 1) v += __shfl_xor(v, off);
+                o[h][e] = v;
+            }
+    }
+    float lh[GT], sh[GT];
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+        float v = 0.0f, w2 = 0.0f;
+#pragma unroll
+        for (int j2 = 0; j2 < NI; ++j2) {
+            v += ihead[j2] == h ? lloc[j2] : 0.0f;
+            w2 += ihead[j2] == h ? sloc[j2] : 0.0f;
+        }
+        // lanes that duplicate an item (plain butterfly levels) count it more than once
+        lh[h] = wave_sum(v);
+        sh[h] = I8 ? wave_sum(w2) : 0.0f;
+    }
+    // duplication factor of the plain levels
+    constexpr int DUP = (Split<GT>::kC ? 1 : 2) * (Split<GT>::kD ? 1 : 2);
+    if (vgrp != 0) return;
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+        if (h >= nh) break;
+        const float l = lh[h] * (1.0f / DUP);
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        const float lse2 = l > 0.0f ? (mref[h] + log2f(l)) * kLn2 : -INFINITY;
+        float val[EV];
+#pragma unroll
+        for (int e = 0; e < EV; ++e) {
+            float acc = o[h][e];
+            if constexpr (I8) acc = (acc - kCodeBias * sh[h] * (1.0f / DUP)) * vsh_inv;
+            val[e] = acc * inv;
+        }
+        const int64_t rowid = rowbase + h;
+        const int d0 = vl * EV;
+        if (p.NP == 1) {
+            if (p.out_bf16) {
+                uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + rowid * D + d0;
+#pragma unroll
+                for (int e = 0; e < EV; ++e) dst[e] = f32_to_bf16(val[e]);
+            } else {
+                float* dst = reinterpret_cast<float*>(p.out) + rowid * D + d0;
+#pragma unroll
+                for (int e = 0; e < EV; ++e) dst[e] = val[e];
+            }
+            if (p.lse != nullptr && vl == 0) p.lse[rowid] = lse2;
+        } else {
+            float* dst = p.ws_o + (rowid * p.NP + part) * D + d0;
+#pragma unroll
+            for (int e = 0; e < EV; ++e) dst[e] = val[e];
+            if (vl == 0) p.ws_lse[rowid * p.NP + part] = lse2;
+        }
+    }
+}
+
+namespace {
+template <int KVT, int D, int GT, int QS>
+hipError_t launch_one(const DecodeParams& p, hipStream_t s) {
+    const int64_t grid = (int64_t)p.NP * p.nchunk * p.Hkv * p.Tq * p.B;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((decode_wave_kernel<KVT, D, GT, QS>), dim3((unsigned)grid), dim3(64), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int KVT, int D, int QS>
+hipError_t by_gt(int GT, const DecodeParams& p, hipStream_t s) {
+    switch (GT) {
+    case 1: return launch_one<KVT, D, 1, QS>(p, s);
+    case 2: return launch_one<KVT, D, 2, QS>(p, s);
+    case 4: return launch_one<KVT, D, 4, QS>(p, s);
+    case 6: return launch_one<KVT, D, 6, QS>(p, s);
+    case 8: return launch_one<KVT, D, 8, QS>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int KVT, int QS>
+hipError_t by_d(int D, int GT, const DecodeParams& p, hipStream_t s) {
+    switch (D) {
+    case 64: return by_gt<KVT, 64, QS>(GT, p, s);
+    case 128: return by_gt<KVT, 128, QS>(GT, p, s);
+    case 256: return by_gt<KVT, 256, QS>(GT, p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+}  // namespace
+
+hipError_t launch_decode_wave(int kv_type, int D, int GT, const DecodeParams& p, hipStream_t stream) {
+    const int qs = p.q_bf16 ? 1 : 2;
+    if (kv_type == KV_BF16) return qs == 1 ? by_d<KV_BF16, 1>(D, GT, p, stream) : by_d<KV_BF16, 2>(D, GT, p, stream);
+    if (kv_type == KV_I8) return qs == 1 ? by_d<KV_I8, 1>(D, GT, p, stream) : by_d<KV_I8, 2>(D, GT, p, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pa

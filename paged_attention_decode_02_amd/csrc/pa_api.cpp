@@ -221,7 +221,9 @@ int pa_decode(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq
         p.ws_o = reinterpret_cast<float*>(workspace);
         p.ws_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + align256(rows * NP * D * sizeof(float)));
     }
-    hipError_t e = pa::launch_decode_valu((int)kv_dtype, D, GT, p, (hipStream_t)stream);
+    // fp32 caches take the plain fp32 kernel; bf16 and int8 the packed-dot kernel
+    hipError_t e = kv_dtype == PA_F32 ? pa::launch_decode_valu((int)kv_dtype, D, GT, p, (hipStream_t)stream)
+                                      : pa::launch_decode_wave((int)kv_dtype, D, GT, p, (hipStream_t)stream);
     if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode launch failed: %s", hipGetErrorString(e));
     return ok();
 }

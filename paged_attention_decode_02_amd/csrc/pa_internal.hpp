@@ -54,6 +54,7 @@ struct CacheWriteParams {
 
 // Launchers return hipSuccess or the launch error.
 hipError_t launch_decode_valu(int kv_type, int D, int GT, const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_wave(int kv_type, int D, int GT, const DecodeParams& p, hipStream_t stream);
 hipError_t launch_splitk_reduce(const ReduceParams& p, hipStream_t stream);
 hipError_t launch_cache_write(int cache_type, const CacheWriteParams& p, hipStream_t stream);
 
