@@ -1,9 +1,11 @@
 // Split-K paged decode on the vector ALUs for bf16 and int8 KV caches
-// (query groups below an MFMA tile): one 64-lane wave per workgroup.
+// (query groups below an MFMA tile).
 //
-// A wave handles one split-K partition of P tokens of one kv head g, one
-// query token t of one sequence b, and GT query heads of g's group, so every
-// K/V byte is read once for all GT heads (grouped-query attention). The
+// A workgroup of four 64-lane waves handles one split-K partition of P tokens
+// of one kv head g, one query token t of one sequence b, and GT query heads of
+// g's group, so every K/V byte is read once for all GT heads (grouped-query
+// attention). Wave w takes blocks w, w+4, w+8, ... of the partition with its
+// own softmax state; the four states are merged through LDS at the end. The
 // split-K decode keeps per-partition softmax statistics (vllm-sm70 page,
 // "Why", Attention bullet: split-K paged decode with an int8 KV cache); the
 // log-sum-exp reduce merges partitions. Per 16-token KV block:
@@ -106,8 +108,18 @@ __device__ __forceinline__ int head_of(int h, int cc, int dd) {
 
 }  // namespace
 
+constexpr int kWaves = 4;  // waves per workgroup
+
+// Wave-local ordering of LDS accesses (the wave's LDS operations execute in
+// order; this only keeps the compiler from moving them across).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int KVT, int D, int GT, int QS>
-__global__ __launch_bounds__(64) void decode_wave_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p) {
     static_assert(KVT == KV_BF16 || KVT == KV_I8, "bf16 or int8 caches");
     constexpr bool I8 = KVT == KV_I8;
     constexpr int E = Elt<KVT>::bytes;
@@ -126,10 +138,14 @@ __global__ __launch_bounds__(64) void decode_wave_kernel(DecodeParams p) {
     static_assert(KB >= 4 && VB >= 4, "layout");
     static_assert(!I8 || STEPS % 2 == 0, "int8 pairs tokens");
 
-    __shared__ __align__(16) float pbuf_f[kBlockSize * GP];  // bf16: p[token][head]
-    uint32_t* pbuf_u = reinterpret_cast<uint32_t*>(pbuf_f);  // int8: f16 pairs [token/2][head]
+    __shared__ __align__(16) float pbuf_all[kWaves][kBlockSize * GP];
+    __shared__ __align__(16) float merge_o[kWaves][GT][64 * EV];
+    __shared__ float merge_ml[kWaves][2][GT];
 
-    const int lane = threadIdx.x;
+    const int wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    float* pbuf_f = pbuf_all[wv];                            // bf16: p[token][head]
+    uint32_t* pbuf_u = reinterpret_cast<uint32_t*>(pbuf_f);  // int8: f16 pairs [token/2][head]
     const int r = lane >> 4, c16 = lane & 15;
     // coordinates of the lane in the basis of the DPP pairings {15, 7, 2, 1}
     const int b0 = c16 & 1, b1 = (c16 >> 1) & 1, b2 = (c16 >> 2) & 1, b3 = (c16 >> 3) & 1;
@@ -156,13 +172,13 @@ __global__ __launch_bounds__(64) void decode_wave_kernel(DecodeParams p) {
     if (start >= n) {
         if (p.NP == 1) {
             for (int r2 = 0; r2 < nh; ++r2) {
-                for (int d = lane; d < D; d += 64) {
+                for (int d = threadIdx.x; d < D; d += 64 * kWaves) {
                     if (p.out_bf16)
                         reinterpret_cast<uint16_t*>(p.out)[(rowbase + r2) * D + d] = 0;
                     else
                         reinterpret_cast<float*>(p.out)[(rowbase + r2) * D + d] = 0.0f;
                 }
-                if (p.lse != nullptr && lane == 0) p.lse[rowbase + r2] = -INFINITY;
+                if (p.lse != nullptr && threadIdx.x == 0) p.lse[rowbase + r2] = -INFINITY;
             }
         }
         return;
@@ -176,6 +192,10 @@ __global__ __launch_bounds__(64) void decode_wave_kernel(DecodeParams p) {
     float qpost;  // factor turning a reduced dot product into log2 units
     float corr[NI];  // int8: 1152 * sum_d q'[head], in the item layout
     {
+        // raw loads of the lane's D/16 query elements of each head (16-byte or
+        // smaller vector loads); heads past the group are loaded from head 0
+        // of the chunk and zeroed
+        constexpr int QB = (D / 16) * (QS == 1 ? 2 : 4);
         float qf[GT][2 * QW];
         float qmax = 0.0f;
 #pragma unroll
@@ -183,12 +203,20 @@ __global__ __launch_bounds__(64) void decode_wave_kernel(DecodeParams p) {
             const int hh = head_of<GT>(h, cc, cd);
             const bool valid = hh < nh;
             const int64_t off = (rowbase + (valid ? hh : 0)) * D + c16 * (D / 16);
+            Raw<QB> raw;
+            if constexpr (QS == 1)
+                load_raw<QB>(raw, reinterpret_cast<const uint16_t*>(p.q) + off);
+            else
+                load_raw<QB>(raw, reinterpret_cast<const float*>(p.q) + off);
 #pragma unroll
             for (int e = 0; e < 2 * QW; ++e) {
-                float v = p.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(p.q)[off + e])
-                                   : reinterpret_cast<const float*>(p.q)[off + e];
+                const float v = QS == 1 ? elem_f32<KV_BF16>(raw, e) : elem_f32<KV_F32>(raw, e);
                 qf[h][e] = valid ? v : 0.0f;
                 qmax = fmaxf(qmax, fabsf(qf[h][e]));
+            }
+            if constexpr (!I8 && QS == 1) {
+#pragma unroll
+                for (int i = 0; i < QW; ++i) qv[h][i] = valid ? raw.w[i] : 0u;  // already bf16 pairs
             }
         }
         if constexpr (I8) {
@@ -243,14 +271,14 @@ __global__ __launch_bounds__(64) void decode_wave_kernel(DecodeParams p) {
             for (int j = 0; j < NI; ++j) corr[j] = kCodeBias * c2[j];
         } else {
             qpost = p.qk_scale_log2;
+            if constexpr (QS == 2) {
 #pragma unroll
-            for (int h = 0; h < GT; ++h) {
+                for (int h = 0; h < GT; ++h) {
 #pragma unroll
-                for (int i = 0; i < QW; ++i) {
-                    const float x0 = qf[h][2 * i], x1 = qf[h][2 * i + 1];
-                    const uint32_t hi = pack_bf16(x0, x1);
-                    qv[h][i] = hi;
-                    if constexpr (QS == 2) {
+                    for (int i = 0; i < QW; ++i) {
+                        const float x0 = qf[h][2 * i], x1 = qf[h][2 * i + 1];
+                        const uint32_t hi = pack_bf16(x0, x1);
+                        qv[h][i] = hi;
                         ql[h][i] = pack_bf16(x0 - bf16_to_f32((uint16_t)hi), x1 - bf16_to_f32((uint16_t)(hi >> 16)));
                     }
                 }
@@ -295,7 +323,7 @@ __global__ __launch_bounds__(64) void decode_wave_kernel(DecodeParams p) {
     float vsh = 1.0f, vsh_inv = 1.0f;
     if constexpr (I8) {
         float vmax = 0.0f;
-        for (int j = j0 + (lane >> 4); j < jend; j += 4) {
+        for (int j = j0 + wv + kWaves * (lane >> 4); j < jend; j += 4 * kWaves) {
             const int64_t ph = table[j];
             const float sv = p.v_scale[(ph * kBlockSize + c16) * p.Hkv + g];
             const int pos = j * kBlockSize + c16;
@@ -310,7 +338,8 @@ __global__ __launch_bounds__(64) void decode_wave_kernel(DecodeParams p) {
     // K registers: register s holds slot s ^ sx (token 4 * (s ^ sx) + r)
     Raw<KB> kr[4];
     Raw<VB> vr[STEPS];
-    int64_t phys = table[j0];
+    const int jw = j0 + wv;  // this wave's first block; it takes every kWaves-th block
+    int64_t phys = jw < jend ? (int64_t)table[jw] : 0;
     auto load_k = [&](int64_t ph) {
         const char* base = kbase + ph * kBlockSize * tok_stride + c16 * KB;
 #pragma unroll
@@ -321,12 +350,12 @@ __global__ __launch_bounds__(64) void decode_wave_kernel(DecodeParams p) {
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) load_raw<VB>(vr[st], base + (st * TPW + vgrp) * tok_stride);
     };
-    load_k(phys);
+    if (jw < jend) load_k(phys);
 
-    for (int j = j0; j < jend; ++j) {
+    for (int j = jw; j < jend; j += kWaves) {
         const int pos0 = j * kBlockSize;
         load_v(phys);
-        const int64_t phys_next = (j + 1 < jend) ? (int64_t)table[j + 1] : phys;
+        const int64_t phys_next = (j + kWaves < jend) ? (int64_t)table[j + kWaves] : phys;
 
         // ---------------------------------------------------------------- QK
         float ps[4][GT];
@@ -357,7 +386,7 @@ __global__ __launch_bounds__(64) void decode_wave_kernel(DecodeParams p) {
             }
         }
         // next block's keys go out now; they are not needed before the next QK
-        if (j + 1 < jend) load_k(phys_next);
+        if (j + kWaves < jend) load_k(phys_next);
 
         // transposed reduction across the row
 #pragma unroll
@@ -439,7 +468,7 @@ __global__ __launch_bounds__(64) void decode_wave_kernel(DecodeParams p) {
                 pbuf_f[my_tok * GP + ihead[j2]] = pr;
             }
         }
-        __syncthreads();
+        wave_lds_sync();
 
         // ---------------------------------------------------------------- PV
         if constexpr (I8) {
@@ -496,7 +525,7 @@ __global__ __launch_bounds__(64) void decode_wave_kernel(DecodeParams p) {
                 }
             }
         }
-        __syncthreads();
+        wave_lds_sync();
         phys = phys_next;
     }
 
@@ -527,38 +556,62 @@ __global__ __launch_bounds__(64) void decode_wave_kernel(DecodeParams p) {
     }
     // duplication factor of the plain levels
     constexpr int DUP = (Split<GT>::kC ? 1 : 2) * (Split<GT>::kD ? 1 : 2);
-    if (vgrp != 0) return;
+    // this wave's unnormalised state (values relative to 2^mref) -> LDS
+    if (vgrp == 0) {
 #pragma unroll
-    for (int h = 0; h < GT; ++h) {
-        if (h >= nh) break;
-        const float l = lh[h] * (1.0f / DUP);
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-        const float lse2 = l > 0.0f ? (mref[h] + log2f(l)) * kLn2 : -INFINITY;
-        float val[EV];
+        for (int h = 0; h < GT; ++h) {
 #pragma unroll
-        for (int e = 0; e < EV; ++e) {
-            float acc = o[h][e];
-            if constexpr (I8) acc = (acc - kCodeBias * sh[h] * (1.0f / DUP)) * vsh_inv;
-            val[e] = acc * inv;
-        }
-        const int64_t rowid = rowbase + h;
-        const int d0 = vl * EV;
-        if (p.NP == 1) {
-            if (p.out_bf16) {
-                uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + rowid * D + d0;
-#pragma unroll
-                for (int e = 0; e < EV; ++e) dst[e] = f32_to_bf16(val[e]);
-            } else {
-                float* dst = reinterpret_cast<float*>(p.out) + rowid * D + d0;
-#pragma unroll
-                for (int e = 0; e < EV; ++e) dst[e] = val[e];
+            for (int e = 0; e < EV; ++e) {
+                float acc = o[h][e];
+                if constexpr (I8) acc = (acc - kCodeBias * sh[h] * (1.0f / DUP)) * vsh_inv;
+                merge_o[wv][h][vl * EV + e] = acc;
             }
-            if (p.lse != nullptr && vl == 0) p.lse[rowid] = lse2;
-        } else {
-            float* dst = p.ws_o + (rowid * p.NP + part) * D + d0;
+        }
+    }
+    if (lane == 0) {
 #pragma unroll
-            for (int e = 0; e < EV; ++e) dst[e] = val[e];
-            if (vl == 0) p.ws_lse[rowid * p.NP + part] = lse2;
+        for (int h = 0; h < GT; ++h) {
+            merge_ml[wv][0][h] = mref[h];
+            merge_ml[wv][1][h] = lh[h] * (1.0f / DUP);
+        }
+    }
+    __syncthreads();
+    // wave w merges heads w, w+4, ...: weights 2^(m_w - M) in a fixed order
+    for (int h = wv; h < nh; h += kWaves) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, merge_ml[w][0][h]);
+        const float base = M == -INFINITY ? 0.0f : M;
+        float wt[kWaves], l = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            wt[w] = exp2_guarded(merge_ml[w][0][h] - base);
+            l += merge_ml[w][1][h] * wt[w];
+        }
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        const float lse2 = l > 0.0f ? (M + log2f(l)) * kLn2 : -INFINITY;
+        const int64_t rowid = rowbase + h;
+        for (int d = lane; d < D; d += 64) {
+            // merge_o[w][h] holds element d at index d (lane vl owns elements vl*EV ..)
+            float acc = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) acc += wt[w] * merge_o[w][h][d];
+            const float val = acc * inv;
+            if (p.NP == 1) {
+                if (p.out_bf16)
+                    reinterpret_cast<uint16_t*>(p.out)[rowid * D + d] = f32_to_bf16(val);
+                else
+                    reinterpret_cast<float*>(p.out)[rowid * D + d] = val;
+            } else {
+                p.ws_o[(rowid * p.NP + part) * D + d] = val;
+            }
+        }
+        if (lane == 0) {
+            if (p.NP == 1) {
+                if (p.lse != nullptr) p.lse[rowid] = lse2;
+            } else {
+                p.ws_lse[rowid * p.NP + part] = lse2;
+            }
         }
     }
 }
@@ -569,7 +622,7 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t s) {
     const int64_t grid = (int64_t)p.NP * p.nchunk * p.Hkv * p.Tq * p.B;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((decode_wave_kernel<KVT, D, GT, QS>), dim3((unsigned)grid), dim3(64), 0, s, p);
+    hipLaunchKernelGGL((decode_wave_kernel<KVT, D, GT, QS>), dim3((unsigned)grid), dim3(64 * kWaves), 0, s, p);
     return hipGetLastError();
 }
 

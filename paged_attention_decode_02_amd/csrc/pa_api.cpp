@@ -58,16 +58,22 @@ void head_chunks(int32_t G, int* GT, int* nchunk) {
     *nchunk = (G + gt - 1) / gt;
 }
 
-int32_t partition_for(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t max_seq_len) {
+// Waves per decode workgroup: the fp32-cache kernel uses one, the bf16/int8
+// kernel four (they split a partition and merge in LDS).
+int waves_per_wg(pa_dtype kv_dtype) { return kv_dtype == PA_F32 ? 1 : 4; }
+
+int32_t partition_for(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, pa_dtype kv_dtype, int32_t max_seq_len) {
     if (max_seq_len <= kBlock) return kBlock;
     int GT, nchunk;
     head_chunks(Hq / Hkv, &GT, &nchunk);
+    const int wpw = waves_per_wg(kv_dtype);
+    const int64_t gran = (int64_t)kBlock * wpw;  // one block per wave at least
     const int64_t per_partition = (int64_t)B * Tq * Hkv * nchunk;  // workgroups per partition index
-    const int64_t target = (int64_t)kCUs * kWavesPerCU;
+    const int64_t target = (int64_t)kCUs * kWavesPerCU / wpw;     // workgroups that fill the GPU once
     int64_t want_np = (target + per_partition - 1) / per_partition;
     if (want_np < 1) want_np = 1;
     int64_t P = (max_seq_len + want_np - 1) / want_np;
-    P = (P + kBlock - 1) / kBlock * kBlock;
+    P = (P + gran - 1) / gran * gran;
     if (P < kMinPartition) P = kMinPartition;
     const int64_t whole = ((int64_t)max_seq_len + kBlock - 1) / kBlock * kBlock;
     if (P >= whole) P = whole;  // one partition covers everything
@@ -100,7 +106,7 @@ int32_t pa_choose_partition_size(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv,
         return fail(PA_ERR_DTYPE, "kv dtype %d not supported", (int)kv_dtype);
     if (max_seq_len < 0) return fail(PA_ERR_SHAPE, "max_seq_len=%d must be >= 0", max_seq_len);
     ok();
-    return partition_for(B, Tq, Hq, Hkv, max_seq_len);
+    return partition_for(B, Tq, Hq, Hkv, kv_dtype, max_seq_len);
 }
 
 size_t pa_decode_workspace_bytes(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
@@ -108,7 +114,7 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv,
     if (check_dims(B, Tq, Hq, Hkv, D) || max_seq_len < 0 || partition_size < 0 || partition_size % kBlock)
         return 0;
     if (kv_dtype != PA_F32 && kv_dtype != PA_BF16 && kv_dtype != PA_I8) return 0;
-    const int32_t P = partition_size ? partition_size : partition_for(B, Tq, Hq, Hkv, max_seq_len);
+    const int32_t P = partition_size ? partition_size : partition_for(B, Tq, Hq, Hkv, kv_dtype, max_seq_len);
     const int64_t NP = max_seq_len > 0 ? ((int64_t)max_seq_len + P - 1) / P : 1;
     if (NP <= 1) return 0;
     const size_t rows = (size_t)B * Tq * Hq;
@@ -181,7 +187,7 @@ int pa_decode(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
         return fail(PA_ERR_ALIGN, "q, caches and out must be 16-byte aligned");
 
-    const int32_t P = partition_size ? partition_size : partition_for(B, Tq, Hq, Hkv, max_seq_len);
+    const int32_t P = partition_size ? partition_size : partition_for(B, Tq, Hq, Hkv, kv_dtype, max_seq_len);
     const int64_t NP64 = max_seq_len > 0 ? ((int64_t)max_seq_len + P - 1) / P : 1;
     if (NP64 > 0x7FFFFFFF) return fail(PA_ERR_SHAPE, "too many partitions");
     const int32_t NP = (int32_t)NP64;

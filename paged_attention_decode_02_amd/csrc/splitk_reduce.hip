@@ -4,67 +4,107 @@
 // Partition i of a row carries o_i (normalised within the partition) and its
 // natural-log LSE lse_i. With M = max_i lse_i and w_i = exp(lse_i - M):
 //   out = sum_i w_i o_i / sum_i w_i,   lse = M + log(sum_i w_i).
-// One 256-thread workgroup per (b, t, h) row. Threads are split into
-// 256 / D slices over the partitions; thread (slice, d) owns output element d,
-// so each slice reads a whole D-vector of a partition per step (coalesced).
+// One 1024-thread workgroup per (b, t, h) row. The threads form
+// S = 1024 / (D/4) slices of D/4 threads; thread (slice, q) owns output
+// elements 4q..4q+3 (one 16-byte load per partition) and takes partitions
+// slice, slice + S, ...; the weights of up to 1024 partitions at a time sit in
+// LDS. Slices are combined in a fixed order, so the result is deterministic.
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
 namespace pa {
 
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceParams p) {
-    __shared__ float red[256];
-    __shared__ float red_w[256];
+namespace {
+constexpr int kThreads = 1024;
+constexpr int kChunk = 1024;  // partitions whose weights are staged in LDS at a time
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float r = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[i]);
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float r = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) r += red[i];
+    __syncthreads();
+    return r;
+}
+}  // namespace
+
+__global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(ReduceParams p) {
+    __shared__ float wts[kChunk];
+    __shared__ float red[kThreads / 64];
+    __shared__ float4 part[kThreads];
     const int tid = threadIdx.x;
     const int64_t rowid = blockIdx.x;
-    const int h = (int)(rowid % p.Hq);
     const int t = (int)((rowid / p.Hq) % p.Tq);
     const int b = (int)(rowid / ((int64_t)p.Hq * p.Tq));
-    (void)h;
     const int n = p.seq_lens[b] - p.Tq + t + 1;
     const int np = n > 0 ? min((n + p.P - 1) / p.P, p.NP) : 0;
     const float* lse_row = p.ws_lse + rowid * p.NP;
-    const float* o_row = p.ws_o + rowid * p.NP * p.D;
+    const float4* o_row = reinterpret_cast<const float4*>(p.ws_o + rowid * p.NP * p.D);
 
-    // M = max_i lse_i
     float mx = -INFINITY;
-    for (int i = tid; i < np; i += 256) mx = fmaxf(mx, lse_row[i]);
-    red[tid] = mx;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
-        __syncthreads();
-    }
-    const float M = red[0];
-    __syncthreads();
+    for (int i = tid; i < np; i += kThreads) mx = fmaxf(mx, lse_row[i]);
+    const float M = block_max(mx, red);
     const float mref = M == -INFINITY ? 0.0f : M;
 
-    const int slices = 256 / p.D;  // D in {64, 128, 256}
-    const int slice = tid / p.D, d = tid % p.D;
-    float acc = 0.0f, wsum = 0.0f;
-    if (slice < slices) {
-#pragma unroll 4
-        for (int i = slice; i < np; i += slices) {
-            const float li = lse_row[i];
+    const int DQ = p.D / 4;  // float4 columns
+    const int S = kThreads / DQ;
+    const int slice = tid / DQ, q = tid % DQ;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float wsum = 0.0f;
+    for (int c0 = 0; c0 < np; c0 += kChunk) {
+        const int cn = min(kChunk, np - c0);
+        for (int i = tid; i < cn; i += kThreads) {
+            const float li = lse_row[c0 + i];
             const float w = li == -INFINITY ? 0.0f : __expf(li - mref);
+            wts[i] = w;
             wsum += w;
-            acc = fmaf(w, o_row[(int64_t)i * p.D + d], acc);
         }
+        __syncthreads();
+#pragma unroll 4
+        for (int i = slice; i < cn; i += S) {
+            const float w = wts[i];
+            const float4 v = o_row[(int64_t)(c0 + i) * DQ + q];
+            acc.x = fmaf(w, v.x, acc.x);
+            acc.y = fmaf(w, v.y, acc.y);
+            acc.z = fmaf(w, v.z, acc.z);
+            acc.w = fmaf(w, v.w, acc.w);
+        }
+        __syncthreads();
     }
-    red[tid] = acc;
-    red_w[tid] = wsum;
+    const float W = block_sum(wsum, red);
+    part[tid] = acc;
     __syncthreads();
     if (slice == 0) {
-        for (int s2 = 1; s2 < slices; ++s2) {
-            acc += red[s2 * p.D + d];
-            wsum += red_w[s2 * p.D + d];
+        for (int s = 1; s < S; ++s) {
+            const float4 v = part[s * DQ + q];
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
         }
-        const float val = wsum > 0.0f ? acc / wsum : 0.0f;
-        if (p.out_bf16)
-            reinterpret_cast<uint16_t*>(p.out)[rowid * p.D + d] = f32_to_bf16(val);
-        else
-            reinterpret_cast<float*>(p.out)[rowid * p.D + d] = val;
-        if (d == 0 && p.lse != nullptr) p.lse[rowid] = wsum > 0.0f ? M + __logf(wsum) : -INFINITY;
+        const float inv = W > 0.0f ? 1.0f / W : 0.0f;
+        const float r[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+        const int64_t o0 = rowid * p.D + 4 * q;
+        if (p.out_bf16) {
+            uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + o0;
+            for (int e = 0; e < 4; ++e) dst[e] = f32_to_bf16(r[e]);
+        } else {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + o0) = make_float4(r[0], r[1], r[2], r[3]);
+        }
+        if (q == 0 && p.lse != nullptr) p.lse[rowid] = W > 0.0f ? M + __logf(W) : -INFINITY;
     }
 }
 
@@ -72,7 +112,7 @@ hipError_t launch_splitk_reduce(const ReduceParams& p, hipStream_t stream) {
     const int64_t rows = (int64_t)p.B * p.Tq * p.Hq;
     if (rows <= 0) return hipSuccess;
     if (rows > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)rows), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

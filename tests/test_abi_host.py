@@ -79,12 +79,15 @@ def test_decode_rejects_bad_arguments(lib, over, code):
 
 
 def test_workspace_size_and_partition_choice(lib):
-    # the long-context workload: 4 x 4 kv heads x 128 partitions of 512 tokens
+    # the long-context workload: 4 sequences x 4 kv heads x 32 partitions of 2048
+    # tokens = 512 four-wave workgroups, two resident waves per SIMD
     P = lib.pa_choose_partition_size(4, 1, 24, 4, 256, 1, 65536)
-    assert P == 512
-    need = lib.pa_decode_workspace_bytes(4, 1, 24, 4, 256, 1, 65536, 512)
+    assert P == 2048
+    need = lib.pa_decode_workspace_bytes(4, 1, 24, 4, 256, 1, 65536, 2048)
     rows = 4 * 24
-    assert need == rows * 128 * 256 * 4 + rows * 128 * 4
+    assert need == rows * 32 * 256 * 4 + rows * 32 * 4
+    # the same shape with fp32 caches uses one-wave workgroups: four times as many partitions
+    assert lib.pa_choose_partition_size(4, 1, 24, 4, 256, 0, 65536) == 512
     # one partition covers a short context: no workspace
     assert lib.pa_choose_partition_size(1, 1, 4, 1, 64, 0, 256) == 256
     assert lib.pa_decode_workspace_bytes(1, 1, 4, 1, 64, 0, 256, 0) == 0
