@@ -343,12 +343,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     auto load_k = [&](int64_t ph) {
         const char* base = kbase + ph * kBlockSize * tok_stride + c16 * KB;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) load_raw<KB>(kr[s], base + (4 * (s ^ sx) + r) * tok_stride);
+        for (int s = 0; s < 4; ++s) load_raw<KB, true>(kr[s], base + (4 * (s ^ sx) + r) * tok_stride);
     };
     auto load_v = [&](int64_t ph) {
         const char* base = vbase + ph * kBlockSize * tok_stride + vl * VB;
 #pragma unroll
-        for (int st = 0; st < STEPS; ++st) load_raw<VB>(vr[st], base + (st * TPW + vgrp) * tok_stride);
+        for (int st = 0; st < STEPS; ++st) load_raw<VB, true>(vr[st], base + (st * TPW + vgrp) * tok_stride);
     };
     if (jw < jend) load_k(phys);
 

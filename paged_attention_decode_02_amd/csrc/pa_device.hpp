@@ -29,27 +29,39 @@ struct Raw {
     uint32_t w[kDwords];
 };
 
-template <int NB>
+template <typename T, bool NT>
+__device__ __forceinline__ T ld(const T* p) {
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
+// NT: nontemporal (streaming) loads, for data read exactly once; they keep
+// the caches free for everything else and reach a higher HBM read rate.
+template <int NB, bool NT = false>
 __device__ __forceinline__ void load_raw(Raw<NB>& r, const void* p) {
+    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+    typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
     if constexpr (NB >= 16) {
-        const uint4* s = reinterpret_cast<const uint4*>(p);
+        const u32x4* s = reinterpret_cast<const u32x4*>(p);
 #pragma unroll
         for (int i = 0; i < NB / 16; ++i) {
-            uint4 v = s[i];
+            const u32x4 v = ld<u32x4, NT>(s + i);
             r.w[4 * i + 0] = v.x;
             r.w[4 * i + 1] = v.y;
             r.w[4 * i + 2] = v.z;
             r.w[4 * i + 3] = v.w;
         }
     } else if constexpr (NB == 8) {
-        uint2 v = *reinterpret_cast<const uint2*>(p);
+        const u32x2 v = ld<u32x2, NT>(reinterpret_cast<const u32x2*>(p));
         r.w[0] = v.x;
         r.w[1] = v.y;
     } else if constexpr (NB == 4) {
-        r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+        r.w[0] = ld<uint32_t, NT>(reinterpret_cast<const uint32_t*>(p));
     } else {
         static_assert(NB == 2, "unsupported load width");
-        r.w[0] = *reinterpret_cast<const uint16_t*>(p);
+        r.w[0] = ld<uint16_t, NT>(reinterpret_cast<const uint16_t*>(p));
     }
 }
 
