@@ -55,28 +55,87 @@ def algorithmic_bytes(w) -> dict:
             "total": kv + scales + table + q + out}
 
 
-def kernel_source_digest() -> str:
+DECODE_SOURCES = {
+    # kernel that dominates a step, by cache dtype, and the sources it is built from
+    "f32": ("decode_valu_kernel", ("decode_valu.hip", "pa_device.hpp", "pa_internal.hpp")),
+    "bf16": ("decode_wave_kernel", ("decode_wave.hip", "pa_device.hpp", "pa_internal.hpp")),
+    "i8": ("decode_wave_kernel", ("decode_wave.hip", "pa_device.hpp", "pa_internal.hpp")),
+}
+
+
+def kernel_source_digest(cache_dtype: str) -> str:
     """Digest of the decode kernel's sources (ties committed counters to code)."""
     h = hashlib.sha256()
-    for f in ("decode_valu.hip", "pa_device.hpp", "pa_internal.hpp"):
+    for f in DECODE_SOURCES[cache_dtype][1]:
         p = os.path.join(ROOT, "paged_attention_decode_02_amd", "csrc", f)
-        if os.path.exists(p):
-            h.update(open(p, "rb").read())
+        h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
 
-def committed_traffic(workload: str):
-    """Per-launch HBM bytes from the committed rocprofv3 counter summary, or
-    None when it is missing or was taken on different kernel sources."""
+def committed_traffic(workload: str, cache_dtype: str):
+    """Per-launch HBM bytes (read + write) from the committed rocprofv3 counter
+    summary, or None when it is missing or was taken on other kernel sources."""
     p = os.path.join(ROOT, "profiles", "decode_%s_hbm_traffic.md" % workload)
     if not os.path.exists(p):
         return None
     text = open(p).read()
     m = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
-    if not m or not t or m.group(1) != kernel_source_digest():
+    if not m or not t or m.group(1) != kernel_source_digest(cache_dtype):
         return None
     return int(t.group(1))
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int) -> str:
+    """Markdown summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE).
+
+    Both counters are in KiB per dispatch. Each is scaled by what it reads for
+    the plain device copy of copy_bytes bytes that the run also made (the
+    largest __amd_rocclr_copyBuffer dispatch), so the figures are bytes.
+    """
+    import csv
+    import collections
+
+    from workloads import SPECS, generate
+
+    def load(path, counter):
+        per = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return per
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    copy_f = max(v for k, vs in fetch.items() if "copyBuffer" in k for v in vs)
+    copy_w = max(v for k, vs in write.items() if "copyBuffer" in k for v in vs)
+    kib = copy_bytes / 1024.0
+    ff, fw = kib / copy_f, kib / copy_w
+    spec = SPECS[workload]
+    kname = DECODE_SOURCES[spec.cache_dtype][0]
+    dk = [k for k in fetch if kname in k]
+    assert len(dk) == 1, dk
+    f_kib = sum(fetch[dk[0]]) / len(fetch[dk[0]])
+    w_kib = sum(write[dk[0]]) / len(write[dk[0]])
+    read_b = int(round(f_kib * ff * 1024))
+    write_b = int(round(w_kib * fw * 1024))
+    algo = algorithmic_bytes(generate(spec))["total"]
+    lines = [
+        "# HBM traffic of %s on %s" % (kname, workload), "",
+        "Counters from two rocprofv3 runs (FETCH_SIZE, then WRITE_SIZE) of",
+        "`bench.py --workload %s --steps 5 --warmup 1 --no-cpu-baseline --copy-calibration-mb %d`." % (
+            workload, copy_bytes >> 20), "",
+        "| quantity | value |", "|---|---|",
+        "| copy kernel (%d MiB) FETCH_SIZE / WRITE_SIZE, KiB | %.1f / %.1f |" % (copy_bytes >> 20, copy_f, copy_w),
+        "| scale factors (bytes per counted byte), read / write | %.4f / %.4f |" % (ff, fw),
+        "| decode FETCH_SIZE / WRITE_SIZE per dispatch, KiB (mean of %d) | %.1f / %.1f |" % (
+            len(fetch[dk[0]]), f_kib, w_kib),
+        "| decode HBM read / write per launch, bytes (scaled) | %d / %d |" % (read_b, write_b),
+        "| algorithmic bytes per launch | %d |" % algo,
+        "| traffic / algorithmic | %.4f |" % ((read_b + write_b) / algo), "",
+        "hbm_bytes_per_launch: %d" % (read_b + write_b),
+        "kernel_source_digest: %s" % kernel_source_digest(spec.cache_dtype), "",
+    ]
+    return "\n".join(lines)
 
 
 def run_cpu_baseline(w, bytes_per_step: int, budget_s: float) -> dict:
@@ -123,7 +182,14 @@ def main():
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="after the benchmark, run 3 plain device copies of this many MiB (a kernel of known "
                          "traffic for scaling rocprofv3's FETCH_SIZE/WRITE_SIZE counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM-traffic summary of two rocprofv3 --pmc counter CSVs and exit")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.workload,
+                                 (args.copy_calibration_mb or 512) << 20))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this decode library runs on a single MI355X "
@@ -267,14 +333,14 @@ def main():
             "decode_plus_reduce_after_flush": round(1e3 * float(np.median(cold)), 2),
         },
         "roofline": {
-            "kernel": "decode_valu_kernel",
+            "kernel": DECODE_SOURCES[sp.cache_dtype][0],
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": committed_traffic(sp.name),
-            "kernel_source_digest": kernel_source_digest(),
+            "traffic": committed_traffic(sp.name, sp.cache_dtype),
+            "kernel_source_digest": kernel_source_digest(sp.cache_dtype),
         },
     }
     if args.copy_calibration_mb:
