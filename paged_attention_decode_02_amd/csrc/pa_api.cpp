@@ -62,13 +62,33 @@ void head_chunks(int32_t G, int* GT, int* nchunk) {
 // kernel four (they split a partition and merge in LDS).
 int waves_per_wg(pa_dtype kv_dtype) { return kv_dtype == PA_F32 ? 1 : 4; }
 
+// The matrix-core kernel takes all G*Tq rows of a kv head at once when they
+// fill at least one 16-row MFMA tile (bf16 and int8 caches).
+bool use_mfma(int32_t Tq, int32_t Hq, int32_t Hkv, pa_dtype kv_dtype) {
+    return kv_dtype != PA_F32 && (int64_t)(Hq / Hkv) * Tq >= 16;
+}
+
+// Row tiles per workgroup and row chunks of the matrix-core kernel.
+void row_chunks(int32_t R, int* NT, int* nchunk) {
+    const int tiles = (R + 15) / 16;
+    *NT = tiles <= 4 ? tiles : 4;
+    *nchunk = (tiles + *NT - 1) / *NT;
+}
+
 int32_t partition_for(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, pa_dtype kv_dtype, int32_t max_seq_len) {
     if (max_seq_len <= kBlock) return kBlock;
     int GT, nchunk;
-    head_chunks(Hq / Hkv, &GT, &nchunk);
+    int64_t per_partition;  // workgroups per partition index
+    if (use_mfma(Tq, Hq, Hkv, kv_dtype)) {
+        int NT;
+        row_chunks((Hq / Hkv) * Tq, &NT, &nchunk);
+        per_partition = (int64_t)B * Hkv * nchunk;
+    } else {
+        head_chunks(Hq / Hkv, &GT, &nchunk);
+        per_partition = (int64_t)B * Tq * Hkv * nchunk;
+    }
     const int wpw = waves_per_wg(kv_dtype);
     const int64_t gran = (int64_t)kBlock * wpw;  // one block per wave at least
-    const int64_t per_partition = (int64_t)B * Tq * Hkv * nchunk;  // workgroups per partition index
     const int64_t target = (int64_t)kCUs * kWavesPerCU / wpw;     // workgroups that fill the GPU once
     int64_t want_np = (target + per_partition - 1) / per_partition;
     if (want_np < 1) want_np = 1;
@@ -198,8 +218,12 @@ int pa_decode(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq
     if (B == 0) return ok();
 
     const int32_t G = Hq / Hkv;
+    const bool mfma = use_mfma(Tq, Hq, Hkv, kv_dtype);
     int GT, nchunk;
-    head_chunks(G, &GT, &nchunk);
+    if (mfma)
+        row_chunks(G * Tq, &GT, &nchunk);  // GT = row tiles per workgroup
+    else
+        head_chunks(G, &GT, &nchunk);
     pa::DecodeParams p{};
     p.q = q;
     p.q_bf16 = q_dtype == PA_BF16;
@@ -229,6 +253,7 @@ int pa_decode(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq
     }
     // fp32 caches take the plain fp32 kernel; bf16 and int8 the packed-dot kernel
     hipError_t e = kv_dtype == PA_F32 ? pa::launch_decode_valu((int)kv_dtype, D, GT, p, (hipStream_t)stream)
+                   : mfma             ? pa::launch_decode_mfma((int)kv_dtype, D, GT, p, (hipStream_t)stream)
                                       : pa::launch_decode_wave((int)kv_dtype, D, GT, p, (hipStream_t)stream);
     if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -21,7 +21,7 @@ struct DecodeParams {
     float qk_scale_log2;  // softmax_scale * log2(e)
     int P;                // partition size in tokens (multiple of 16)
     int NP;               // partitions per row
-    int nchunk;           // head chunks per kv head (G split into chunks of GT)
+    int nchunk;           // vector-ALU kernels: head chunks of GT; MFMA kernel: row chunks of 16*NT
     void* out;
     int out_bf16;
     float* lse;
@@ -55,6 +55,8 @@ struct CacheWriteParams {
 // Launchers return hipSuccess or the launch error.
 hipError_t launch_decode_valu(int kv_type, int D, int GT, const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_wave(int kv_type, int D, int GT, const DecodeParams& p, hipStream_t stream);
+// NT: 16-row tiles per workgroup (1..4); p.nchunk = row chunks of 16*NT rows
+hipError_t launch_decode_mfma(int kv_type, int D, int NT, const DecodeParams& p, hipStream_t stream);
 hipError_t launch_splitk_reduce(const ReduceParams& p, hipStream_t stream);
 hipError_t launch_cache_write(int cache_type, const CacheWriteParams& p, hipStream_t stream);
 

@@ -238,3 +238,25 @@ def test_cache_write_skips_negative_slots_and_writes_bits():
                 assert np.all(kc == 0x7FC0)
             else:
                 assert np.all(np.isnan(kc))
+
+
+# ------------------------------------------------------------ matrix-core path
+# G * Tq >= 16 rows per kv head (bf16 / int8 caches) run on the MFMA kernel.
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("G, Tq", [(6, 8), (16, 1), (8, 16), (2, 8), (24, 3)])
+def test_mfma_rows(kv, D, G, Tq):
+    spec = scaled("verify_bf16", B=2, Tq=Tq, Hq=2 * G, Hkv=2, D=D, seq_lens=(Tq, 1300), shared_prefix=0,
+                  cache_dtype=kv, src_dtype="bf16")
+    w = generate(spec, seed=G * 100 + Tq)
+    run_workload(w, partition_size=256)
+
+
+@pytest.mark.parametrize("qdt", ["f32", "bf16"])
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+def test_mfma_query_dtype_and_partitions(qdt, kv):
+    spec = scaled("verify_bf16", B=3, Tq=8, Hq=12, Hkv=2, D=128, seq_lens=(8, 3000), shared_prefix=0,
+                  cache_dtype=kv, q_dtype=qdt, src_dtype="f32")
+    w = generate(spec, seed=11)
+    for P in (16, 64, 1024, 0):
+        run_workload(w, partition_size=P)
