@@ -106,7 +106,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     __shared__ float redist[kW][NT][16];       // per-wave row values moved to the output layout
     __shared__ float red[kW];
 
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l16 = lane & 15, lg = lane >> 4;
 
     int wg = blockIdx.x;

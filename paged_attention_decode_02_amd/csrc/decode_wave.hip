@@ -142,7 +142,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     __shared__ __align__(16) float merge_o[kWaves][GT][64 * EV];
     __shared__ float merge_ml[kWaves][2][GT];
 
-    const int wv = threadIdx.x >> 6;
+    // the wave index is uniform across the wave: saying so keeps the block
+    // loop, the table reads and the base addresses on the scalar unit
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     float* pbuf_f = pbuf_all[wv];                            // bf16: p[token][head]
     uint32_t* pbuf_u = reinterpret_cast<uint32_t*>(pbuf_f);  // int8: f16 pairs [token/2][head]

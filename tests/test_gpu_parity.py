@@ -260,3 +260,48 @@ def test_mfma_query_dtype_and_partitions(qdt, kv):
     w = generate(spec, seed=11)
     for P in (16, 64, 1024, 0):
         run_workload(w, partition_size=P)
+
+
+# ------------------------------------------------------------ graph capture
+@pytest.mark.parametrize("name", ["gqa_bf16", "verify_i8"])
+def test_step_captured_in_a_graph(name):
+    """cache_write + decode + reduce recorded in one HIP graph: every replay
+    (with other eager work and new query values in between) equals an eager
+    run bit for bit. The library allocates and synchronises nothing, so the
+    captured step is the whole step."""
+    sp0 = SPECS[name]
+    spec = scaled(name, seq_lens=(sp0.seq_lens[0] // 8, sp0.seq_lens[1] // 8),
+                  shared_prefix=sp0.shared_prefix // 8 // 16 * 16)
+    w = generate(spec, seed=12)
+    cache = gpu_cache(w)
+    k, v, ks, vs = cache
+    q, table, lens = gpu_inputs(w)
+    rows = w.step_rows()
+    new_k = host_to_dev(w.k_src[rows], spec.src_dtype)
+    new_v = host_to_dev(w.v_src[rows], spec.src_dtype)
+    new_slots = torch.from_numpy(w.slot_mapping[rows]).to(dev())
+    P = pa.choose_partition_size(spec.B, spec.Tq, spec.Hq, spec.Hkv, spec.D, k.dtype, w.max_seq_len)
+    ws = torch.empty(max(256, pa.workspace_bytes(spec.B, spec.Tq, spec.Hq, spec.Hkv, spec.D, k.dtype,
+                                                 w.max_seq_len, P)), dtype=torch.uint8, device=dev())
+    out = torch.empty((spec.B, spec.Tq, spec.Hq, spec.D), dtype=torch.float32, device=dev())
+    lse = torch.empty((spec.B, spec.Tq, spec.Hq), dtype=torch.float32, device=dev())
+
+    def step():
+        pa.cache_write(new_k, new_v, new_slots, k, v, ks, vs)
+        pa.decode(q, k, v, table, lens, w.max_seq_len, w.softmax_scale, ks, vs, partition_size=P, out=out,
+                  lse=lse, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for i in range(4):
+        q.copy_(q.roll(1, dims=2))  # new queries between replays (eager work)
+        g.replay()
+        torch.cuda.synchronize()
+        got_o, got_l = out.clone(), lse.clone()
+        step()  # eager
+        torch.cuda.synchronize()
+        assert torch.equal(got_o, out) and torch.equal(got_l, lse), "replay %d differs from eager" % i
