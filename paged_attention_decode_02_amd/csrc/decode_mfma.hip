@@ -338,6 +338,18 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     load_k(phys);
     for (int j = j0; j < jend; ++j) {
         const int pos0 = j * kBlockSize;
+        // int8 scales of the lane's four tokens first: a load issued after the
+        // prefetches would make its wait drain them (in-order counting)
+        float kraw[4], vraw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            kraw[i] = 1.0f;
+            vraw[i] = 1.0f;
+            if constexpr (I8) {
+                kraw[i] = p.k_scale[(phys * kBlockSize + 4 * lg + i) * p.Hkv + g];
+                vraw[i] = p.v_scale[(phys * kBlockSize + 4 * lg + i) * p.Hkv + g];
+            }
+        }
         load_v(phys);
         const int64_t phys_next = j + 1 < jend ? (int64_t)table[j + 1] : phys;
 
@@ -376,14 +388,16 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
                             av, __builtin_bit_cast(bf16x8, qlds[q2][tile][ks][lane]), s[tile], 0, 0, 0);
             }
         }
-        if (j + 1 < jend) load_k(phys_next);
+        // unconditional (the last iteration re-reads its own block): a load under
+        // a branch makes the wait counts after the join conservative
+        load_k(phys_next);
 
         // ---------------------------------------------------- softmax
         float ksc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             ksc[i] = qpost;
-            if constexpr (I8) ksc[i] *= p.k_scale[(phys * kBlockSize + 4 * lg + i) * p.Hkv + g];
+            if constexpr (I8) ksc[i] *= kraw[i];
         }
         bool raise = false;
         float sc[NT][4];
@@ -432,8 +446,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
             vsc[i] = 1.0f;
             if constexpr (I8) {
                 const bool ok = pos0 + 4 * lg + i < end;
-                const float sv = p.v_scale[(phys * kBlockSize + 4 * lg + i) * p.Hkv + g];
-                vsc[i] = ok ? sv * vsh : 0.0f;
+                vsc[i] = ok ? vraw[i] * vsh : 0.0f;
             }
         }
         uint32_t pa[NT][2];

@@ -356,6 +356,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
 
     for (int j = jw; j < jend; j += kWaves) {
         const int pos0 = j * kBlockSize;
+        // int8 scales of the lane's token first: a load issued after the
+        // prefetches would make its wait drain them (in-order counting)
+        float kscale_raw = 1.0f, vscale_raw = 1.0f;
+        if constexpr (I8) {
+            kscale_raw = p.k_scale[(phys * kBlockSize + my_tok) * p.Hkv + g];
+            vscale_raw = p.v_scale[(phys * kBlockSize + my_tok) * p.Hkv + g];
+        }
         load_v(phys);
         const int64_t phys_next = (j + kWaves < jend) ? (int64_t)table[j + kWaves] : phys;
 
@@ -387,8 +394,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
                 ps[s][h] = acc;
             }
         }
-        // next block's keys go out now; they are not needed before the next QK
-        if (j + kWaves < jend) load_k(phys_next);
+        // next block's keys go out now; they are not needed before the next QK.
+        // Unconditional (the last iteration re-reads its own block): a load
+        // under a branch makes the wait counts after the join conservative.
+        load_k(phys_next);
 
         // transposed reduction across the row
 #pragma unroll
@@ -419,7 +428,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
         // scores of the lane's items, log2 units; masked past the end
         const bool tok_ok = pos0 + my_tok < end;
         float ksc = qpost;
-        if constexpr (I8) ksc *= p.k_scale[(phys * kBlockSize + my_tok) * p.Hkv + g];
+        if constexpr (I8) ksc *= kscale_raw;
         float sc[NI];
         bool raise = false;
 #pragma unroll
@@ -456,7 +465,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
 
         // ------------------------------------------------- probabilities -> LDS
         float sv = 1.0f;
-        if constexpr (I8) sv = p.v_scale[(phys * kBlockSize + my_tok) * p.Hkv + g] * vsh;
+        if constexpr (I8) sv = vscale_raw * vsh;
 #pragma unroll
         for (int j2 = 0; j2 < NI; ++j2) {
             const float base = mloc[j2] == -INFINITY ? 0.0f : mloc[j2];
