@@ -5,27 +5,33 @@
 // G query heads of a kv head times the Tq tokens form G*Tq rows that share
 // every key and value row. The vllm-sm70 page ("Why", Attention bullet) runs
 // such speculative positions as a virtual batch of one-token decodes; here
-// all rows of a kv head are one MFMA operand, so the KV is read once.
+// all rows of a kv head are MFMA operands, so the KV is read once.
 //
 // Workgroup = 4 waves for one split-K partition of one kv head g of one
-// sequence b and up to 16*NT rows r = t*G + h' (query token t, head g*G + h').
-// Row r sees keys 0 .. L_b - Tq + t (causal inside the Tq new tokens).
-// Every wave computes the whole score tile of each 16-token block,
-//   S^T[token][row] = K[token][:] . Q[row][:]   (v_mfma_f32_16x16x32 bf16 / f16),
-// whose result layout (lane l: tokens 4*(l/16)+i of row l%16) is exactly the
-// A-operand layout of the PV product, so probabilities go straight from the
-// softmax into
-//   O[row][d] += P[row][token] V[token][d]      (v_mfma_f32_16x16x16 bf16 / f16)
-// where wave w owns output dims [w*D/4, (w+1)*D/4). The V operand needs 4
-// consecutive tokens of one dim per lane: lanes load 4 dims of one token and a
-// 4x4 transpose inside each lane quad (DPP + byte permutes) regroups them.
-// Queries (as MFMA B operands) are staged once per workgroup in LDS.
+// sequence b and up to 16*NT rows r = t*G + h' (query token t, head g*G + h');
+// row r sees keys 0 .. L_b - Tq + t (causal inside the Tq new tokens).
+// Per 16-token KV block:
+//  - the K tile is staged once in LDS (each wave loads a quarter of it, two
+//    blocks ahead, into registers and stores it one block ahead), laid out as
+//    the A operand of S^T = K Q^T (v_mfma_f32_16x16x32 bf16 / f16);
+//  - wave w < NT owns row tile w: its queries stay in registers as B
+//    operands, it computes S^T for its 16 rows, runs the softmax and writes
+//    the probabilities to LDS. The S^T result layout (lane l: tokens
+//    4*(l/16)+i of row l%16) is exactly the A-operand layout of the PV
+//    product, so no shuffle is needed;
+//  - every wave accumulates O[row][d] += P[row][token] V[token][d]
+//    (v_mfma_f32_16x16x16 bf16 / f16) for its quarter of the output dims,
+//    with its V slice loaded straight into registers and regrouped by a 4x4
+//    transpose inside each lane quad (DPP + byte permutes).
+// The scores of block j+1 are computed while the PV of block j runs, so one
+// workgroup barrier per block covers both the staged keys and the
+// probabilities (double-buffered in LDS).
 // int8 caches: codes become f16 (1024 + code + 128) by a byte permute, queries
 // are scaled into f16 by a power of two, probabilities times the value scale
-// are f16; the code bias is removed once per row (query sums for the scores,
-// probability sums for the outputs).
-// Softmax: log2 units against a per-row reference raised only when beaten by
-// 2^8 (as in the vector-ALU decode).
+// are f16; the code bias is removed once per row. Softmax: log2 units against a
+// per-row reference raised only when beaten by 2^8.
+#include <type_traits>
+
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -61,6 +67,9 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
 }
 
+__device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)w); }
+__device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
 // 4x4 transpose of 16-bit elements inside a lane quad. Lane i (= lane & 3)
 // holds elements (i, 0..3) of a 4x4 tile as two dwords; afterwards lane j
 // holds elements (0..3, j).
@@ -88,26 +97,35 @@ __device__ __forceinline__ uint32_t quad_transpose8(uint32_t w, int i) {
     return __builtin_amdgcn_perm(pu, u, b0 ? 0x03070105u : 0x06020400u);
 }
 
+template <int I>
+using ic = std::integral_constant<int, I>;
+
 }  // namespace
 
 template <int KVT, int D, int NT, int QS>
 __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     static_assert(KVT == KV_BF16 || KVT == KV_I8, "bf16 or int8 caches");
+    static_assert(NT >= 1 && NT <= kW, "one row tile per wave");
     constexpr bool I8 = KVT == KV_I8;
     constexpr int E = Elt<KVT>::bytes;
-    constexpr int KS = D / 32;   // k-steps of the score product
-    constexpr int DW = D / kW;   // output dims per wave
-    constexpr int NDT = DW / 16; // 16-wide output tiles per wave
-    constexpr int NQ = QS == 2 ? 2 : 1;  // query parts (hi, lo) for fp32 queries
+    constexpr int KS = D / 32;                 // k-steps of the score product
+    constexpr int KSW = (KS + kW - 1) / kW;    // k-steps each wave stages
+    constexpr int DW = D / kW;                 // output dims per wave
+    constexpr int NDT = DW / 16;               // 16-wide output tiles per wave
+    constexpr int NQ = QS == 2 ? 2 : 1;        // query parts (hi, lo) for fp32 queries
+    constexpr int KQB = 8 * E;                 // key bytes per lane per k-step
+    constexpr int VB = 4 * E;                  // value bytes per lane per output tile
 
-    // queries as B operands: [part][tile][kstep][lane] of 16 bytes
-    __shared__ __align__(16) u32x4 qlds[NQ][NT][KS][64];
-    __shared__ float qcorr[NT * 16];           // int8: 1152 * sum_d q'[row]
-    __shared__ float redist[kW][NT][16];       // per-wave row values moved to the output layout
+    __shared__ __align__(16) u32x4 kst[2][KS][64];  // staged keys (A operands)
+    __shared__ __align__(16) u32x2 pst[2][NT][64];  // probabilities (A operands of PV)
+    __shared__ float ast[2][NT][16];                // per-row rescale factors
+    __shared__ int araise[2][NT];                   // whether a tile's rows were rescaled
+    __shared__ float fin[2][NT][16];                // epilogue: 1/l and code bias per row
     __shared__ float red[kW];
 
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l16 = lane & 15, lg = lane >> 4;
+    const bool owner = wv < NT;  // computes the scores of row tile wv
 
     int wg = blockIdx.x;
     const int part = wg % p.NP;
@@ -120,8 +138,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     const int G = p.G, Tq = p.Tq, R = G * Tq;
     const int row0 = rc * 16 * NT;
     const int L = p.seq_lens[b];
-    // keys visible to the last (largest t) row of this chunk
-    const int rlast = min(R, row0 + 16 * NT) - 1;
+    const int rlast = min(R, row0 + 16 * NT) - 1;  // largest t is in the last row
     const int n_chunk = L - Tq + rlast / G + 1;
     const int start = part * p.P;
 
@@ -147,57 +164,35 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     }
     const int end = min(start + p.P, n_chunk);
 
-    // ----------------------------------------------------- stage the queries
-    // entry (tile, ks, l): row row0 + 16 tile + l%16, dims 32 ks + 8 (l/16) .. +7
+    // ---------------------------------------------------------------- queries
+    // owner wave: B operand (row 16*wv + l16, dims 32 ks + 8 lg .. +7) per k-step
+    const int myrow = row0 + 16 * wv + l16;
+    const bool row_ok = owner && myrow < R;
+    float qx[KS][8];
     float qmax = 0.0f;
-    for (int e = threadIdx.x; e < NT * KS * 64; e += 64 * kW) {
-        const int l = e & 63, ks = (e >> 6) % KS, tile = (e >> 6) / KS;
-        const int r = row0 + 16 * tile + (l & 15);
-        const int d0 = 32 * ks + 8 * (l >> 4);
-        float x[8];
-        if (r < R) {
-            const int64_t off = row_out(r) * D + d0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        if (row_ok) {
+            const int64_t off = row_out(myrow) * D + 32 * ks + 8 * lg;
             if constexpr (QS == 1) {
                 Raw<16> raw;
                 load_raw<16>(raw, reinterpret_cast<const uint16_t*>(p.q) + off);
 #pragma unroll
-                for (int k = 0; k < 8; ++k) x[k] = elem_f32<KV_BF16>(raw, k);
+                for (int k = 0; k < 8; ++k) qx[ks][k] = elem_f32<KV_BF16>(raw, k);
             } else {
                 Raw<32> raw;
                 load_raw<32>(raw, reinterpret_cast<const float*>(p.q) + off);
 #pragma unroll
-                for (int k = 0; k < 8; ++k) x[k] = elem_f32<KV_F32>(raw, k);
+                for (int k = 0; k < 8; ++k) qx[ks][k] = elem_f32<KV_F32>(raw, k);
             }
         } else {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) x[k] = 0.0f;
+            for (int k = 0; k < 8; ++k) qx[ks][k] = 0.0f;
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) qmax = fmaxf(qmax, fabsf(x[k]));
-        if constexpr (!I8) {
-            u32x4 hi, lo;
-            hi.x = pack_bf16x2(x[0], x[1]);
-            hi.y = pack_bf16x2(x[2], x[3]);
-            hi.z = pack_bf16x2(x[4], x[5]);
-            hi.w = pack_bf16x2(x[6], x[7]);
-            qlds[0][tile][ks][l] = hi;
-            if constexpr (QS == 2) {
-                const uint32_t hw[4] = {hi.x, hi.y, hi.z, hi.w};
-                uint32_t lw[4];
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    lw[k] = pack_bf16x2(x[2 * k] - bf16_to_f32((uint16_t)hw[k]),
-                                        x[2 * k + 1] - bf16_to_f32((uint16_t)(hw[k] >> 16)));
-                lo.x = lw[0];
-                lo.y = lw[1];
-                lo.z = lw[2];
-                lo.w = lw[3];
-                qlds[NQ - 1][tile][ks][l] = lo;
-            }
-        }
+        for (int k = 0; k < 8; ++k) qmax = fmaxf(qmax, fabsf(qx[ks][k]));
     }
-    float qpost = p.qk_scale_log2;
-    float qscale = 1.0f;
+    float qscale = 1.0f, qpost = p.qk_scale_log2;
     if constexpr (I8) {
         // one power of two for the workgroup puts max|q| in [2^14, 2^15)
         qmax = wave_max(qmax);
@@ -207,97 +202,52 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
         const int e2 = qmax > 0.0f ? 14 - ilogbf(qmax) : 0;
         qscale = ldexpf(1.0f, e2);
         qpost = ldexpf(p.qk_scale_log2, -e2);
-        for (int e = threadIdx.x; e < NT * KS * 64; e += 64 * kW) {
-            const int l = e & 63, ks = (e >> 6) % KS, tile = (e >> 6) / KS;
-            const int r = row0 + 16 * tile + (l & 15);
-            const int d0 = 32 * ks + 8 * (l >> 4);
-            float x[8];
-            if (r < R) {
-                const int64_t off = row_out(r) * D + d0;
-                if constexpr (QS == 1) {
-                    Raw<16> raw;
-                    load_raw<16>(raw, reinterpret_cast<const uint16_t*>(p.q) + off);
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) x[k] = elem_f32<KV_BF16>(raw, k) * qscale;
-                } else {
-                    Raw<32> raw;
-                    load_raw<32>(raw, reinterpret_cast<const float*>(p.q) + off);
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) x[k] = elem_f32<KV_F32>(raw, k) * qscale;
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) x[k] = 0.0f;
-            }
-            u32x4 hi;
-            hi.x = pack_f16x2(x[0], x[1]);
-            hi.y = pack_f16x2(x[2], x[3]);
-            hi.z = pack_f16x2(x[4], x[5]);
-            hi.w = pack_f16x2(x[6], x[7]);
-            qlds[0][tile][ks][l] = hi;
-            if constexpr (QS == 2) {
-                const uint32_t hw[4] = {hi.x, hi.y, hi.z, hi.w};
-                uint32_t lw[4];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const float h0 = (float)__builtin_bit_cast(_Float16, (uint16_t)hw[k]);
-                    const float h1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(hw[k] >> 16));
-                    lw[k] = pack_f16x2(x[2 * k] - h0, x[2 * k + 1] - h1);
-                }
-                u32x4 lo;
-                lo.x = lw[0];
-                lo.y = lw[1];
-                lo.z = lw[2];
-                lo.w = lw[3];
-                qlds[NQ - 1][tile][ks][l] = lo;
-            }
-        }
     }
-    __syncthreads();
-    if constexpr (I8) {
-        // row sums of the f16 queries (hi + lo) for the code bias
-        for (int e = threadIdx.x; e < NT * 16; e += 64 * kW) {
-            const int tile = e / 16, rl = e % 16;
-            float s = 0.0f;
-            for (int ks = 0; ks < KS; ++ks)
-                for (int grp = 0; grp < 4; ++grp)
-                    for (int part2 = 0; part2 < NQ; ++part2) {
-                        const u32x4 v = qlds[part2][tile][ks][grp * 16 + rl];
-                        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-                        for (int k = 0; k < 4; ++k)
-                            s += (float)__builtin_bit_cast(_Float16, (uint16_t)w4[k]) +
-                                 (float)__builtin_bit_cast(_Float16, (uint16_t)(w4[k] >> 16));
-                    }
-            qcorr[e] = kCodeBias * s;
+    u32x4 qreg[NQ][KS];
+    float corr = 0.0f;  // int8: 1152 * sum_d q'[row] of the lane's row (after the reduction below)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float x0 = qx[ks][2 * k] * qscale, x1 = qx[ks][2 * k + 1] * qscale;
+            if constexpr (I8) {
+                hi[k] = pack_f16x2(x0, x1);
+                lo[k] = pack_f16x2(x0 - f16lo(hi[k]), x1 - f16hi(hi[k]));
+                corr += f16lo(hi[k]) + f16hi(hi[k]);
+                if constexpr (QS == 2) corr += f16lo(lo[k]) + f16hi(lo[k]);
+            } else {
+                hi[k] = pack_bf16x2(x0, x1);
+                lo[k] = pack_bf16x2(x0 - bf16_to_f32((uint16_t)hi[k]), x1 - bf16_to_f32((uint16_t)(hi[k] >> 16)));
+            }
         }
-        __syncthreads();
+        qreg[0][ks] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (QS == 2) qreg[NQ - 1][ks] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    }
+    if constexpr (I8) {
+        corr += __shfl_xor(corr, 16);
+        corr += __shfl_xor(corr, 32);
+        corr *= kCodeBias;
     }
 
-    // --------------------------------------------------------- per-row state
-    // score layout: lane holds row 16*tile + l16 (tokens 4*lg + i of a block)
-    int nvis[NT];      // keys visible to the lane's row in each tile
-    float mref[NT], lpart[NT], spart[NT], corr[NT];
-#pragma unroll
-    for (int tile = 0; tile < NT; ++tile) {
-        const int r = row0 + 16 * tile + l16;
-        nvis[tile] = r < R ? min(end, L - Tq + r / G + 1) : 0;
-        mref[tile] = -INFINITY;
-        lpart[tile] = 0.0f;
-        spart[tile] = 0.0f;
-        corr[tile] = I8 ? qcorr[16 * tile + l16] : 0.0f;
-    }
-    // output layout: lane holds rows 16*tile + 4*lg + i, dim wv*DW + 16*ndt + l16
+    // ------------------------------------------------------- softmax state
+    // owner, score layout: lane holds row myrow, tokens 4*lg + i of a block
+    const int nvis = row_ok ? min(end, L - Tq + myrow / G + 1) : 0;
+    float mref = -INFINITY, lpart = 0.0f, spart = 0.0f;
+    // output layout: lane holds rows 16*t + 4*lg + i, dim wv*DW + 16*nd + l16
     f32x4 o[NT][NDT];
 #pragma unroll
-    for (int tile = 0; tile < NT; ++tile)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int nd = 0; nd < NDT; ++nd) o[tile][nd] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int nd = 0; nd < NDT; ++nd) o[t][nd] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int32_t* table = p.block_table + (int64_t)b * p.max_blocks;
     const int64_t tok_stride = (int64_t)p.Hkv * D * E;
     const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (int64_t)g * D * E;
     const char* vbase = reinterpret_cast<const char*>(p.v_cache) + (int64_t)g * D * E;
     const int j0 = start / kBlockSize, jend = (end + kBlockSize - 1) / kBlockSize;
+    // physical block of logical block j; past the end the last one (re-read)
+    auto phys_of = [&](int j) -> int64_t { return (int64_t)table[j < jend ? j : jend - 1]; };
 
     // int8: probabilities times value scales are kept below 2^15 (f16) by 2^vsh
     float vsh = 1.0f, vsh_inv = 1.0f;
@@ -317,258 +267,244 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
         vsh_inv = ldexpf(1.0f, -e2);
     }
 
-    constexpr int KB = 8 * E;  // key bytes per lane per k-step
-    constexpr int VB = 4 * E;  // value bytes per lane per output tile
-    Raw<KB> kr[KS];
-    Raw<VB> vr[NDT];
-    const int vtok = 4 * lg + (l16 & 3);  // token this lane loads for the V transpose
-    const int vdim = wv * DW + 4 * (l16 >> 2);
-    auto load_k = [&](int64_t ph) {
+    // ---------------------------------------------------------- pipeline
+    // this wave's quarter of a future K tile, plus (int8) the block's scales for
+    // the lane's four tokens, all loaded together two blocks ahead: a load
+    // issued later would make its wait drain the prefetches (in-order counting)
+    struct KQ {
+        Raw<KQB> k[KSW];
+        float ks[4], vs[4];
+    };
+    KQ kq[2];
+    Raw<VB> vq[2][NDT];  // this wave's V slice of a current/future block
+    auto load_kq = [&](KQ& dst, int64_t ph) {
         const char* base = kbase + (ph * kBlockSize + l16) * tok_stride + 8 * lg * E;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) load_raw<KB, true>(kr[ks], base + 32 * ks * E);
+        for (int i = 0; i < KSW; ++i) {
+            const int ks = wv * KSW + i;
+            if (ks < KS) load_raw<KQB, true>(dst.k[i], base + 32 * ks * E);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            dst.ks[i] = 1.0f;
+            dst.vs[i] = 1.0f;
+            if constexpr (I8) {
+                dst.ks[i] = p.k_scale[(ph * kBlockSize + 4 * lg + i) * p.Hkv + g];
+                dst.vs[i] = p.v_scale[(ph * kBlockSize + 4 * lg + i) * p.Hkv + g];
+            }
+        }
     };
-    auto load_v = [&](int64_t ph) {
+    auto store_kq = [&](const KQ& src, int stage) {
+#pragma unroll
+        for (int i = 0; i < KSW; ++i) {
+            const int ks = wv * KSW + i;
+            if (ks < KS) {
+                u32x4 a;
+                if constexpr (I8) {
+                    const uint32_t u0 = src.k[i].w[0] ^ 0x80808080u, u1 = src.k[i].w[1] ^ 0x80808080u;
+                    a = u32x4{f16pair_lo(u0), f16pair_hi(u0), f16pair_lo(u1), f16pair_hi(u1)};
+                } else {
+                    a = u32x4{src.k[i].w[0], src.k[i].w[1], src.k[i].w[2], src.k[i].w[3]};
+                }
+                kst[stage][ks][lane] = a;
+            }
+        }
+    };
+    const int vtok = 4 * lg + (l16 & 3);  // token this lane loads for the V transpose
+    const int vdim = wv * DW + 4 * (l16 >> 2);
+    auto load_vq = [&](Raw<VB>* dst, int64_t ph) {
         const char* base = vbase + (ph * kBlockSize + vtok) * tok_stride + vdim * E;
 #pragma unroll
-        for (int nd = 0; nd < NDT; ++nd) load_raw<VB, true>(vr[nd], base + 16 * nd * E);
+        for (int nd = 0; nd < NDT; ++nd) load_raw<VB, true>(dst[nd], base + 16 * nd * E);
     };
 
-    int64_t phys = table[j0];
-    load_k(phys);
-    for (int j = j0; j < jend; ++j) {
+    // scores, softmax and probabilities of block j into LDS stage j % 2 (owners only)
+    auto scores = [&](int j, const float* kraw, const float* vraw) {
+        const int stage = j & 1;
         const int pos0 = j * kBlockSize;
-        // int8 scales of the lane's four tokens first: a load issued after the
-        // prefetches would make its wait drain them (in-order counting)
-        float kraw[4], vraw[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            kraw[i] = 1.0f;
-            vraw[i] = 1.0f;
-            if constexpr (I8) {
-                kraw[i] = p.k_scale[(phys * kBlockSize + 4 * lg + i) * p.Hkv + g];
-                vraw[i] = p.v_scale[(phys * kBlockSize + 4 * lg + i) * p.Hkv + g];
-            }
-        }
-        load_v(phys);
-        const int64_t phys_next = j + 1 < jend ? (int64_t)table[j + 1] : phys;
-
-        // ---------------------------------------------------- scores S^T
-        f32x4 s[NT];
-#pragma unroll
-        for (int tile = 0; tile < NT; ++tile) s[tile] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 s = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            if constexpr (I8) {
-                const uint32_t u0 = kr[ks].w[0] ^ 0x80808080u, u1 = kr[ks].w[1] ^ 0x80808080u;
-                u32x4 a;
-                a.x = f16pair_lo(u0);
-                a.y = f16pair_hi(u0);
-                a.z = f16pair_lo(u1);
-                a.w = f16pair_hi(u1);
-                const f16x8 av = __builtin_bit_cast(f16x8, a);
+            const u32x4 a = kst[stage][ks][lane];
 #pragma unroll
-                for (int tile = 0; tile < NT; ++tile)
-#pragma unroll
-                    for (int q2 = 0; q2 < NQ; ++q2)
-                        s[tile] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            av, __builtin_bit_cast(f16x8, qlds[q2][tile][ks][lane]), s[tile], 0, 0, 0);
-            } else {
-                u32x4 a;
-                a.x = kr[ks].w[0];
-                a.y = kr[ks].w[1];
-                a.z = kr[ks].w[2];
-                a.w = kr[ks].w[3];
-                const bf16x8 av = __builtin_bit_cast(bf16x8, a);
-#pragma unroll
-                for (int tile = 0; tile < NT; ++tile)
-#pragma unroll
-                    for (int q2 = 0; q2 < NQ; ++q2)
-                        s[tile] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            av, __builtin_bit_cast(bf16x8, qlds[q2][tile][ks][lane]), s[tile], 0, 0, 0);
+            for (int q2 = 0; q2 < NQ; ++q2) {
+                if constexpr (I8)
+                    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                               __builtin_bit_cast(f16x8, qreg[q2][ks]), s, 0, 0, 0);
+                else
+                    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                __builtin_bit_cast(bf16x8, qreg[q2][ks]), s, 0, 0, 0);
             }
         }
-        // unconditional (the last iteration re-reads its own block): a load under
-        // a branch makes the wait counts after the join conservative
-        load_k(phys_next);
-
-        // ---------------------------------------------------- softmax
-        float ksc[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ksc[i] = qpost;
-            if constexpr (I8) ksc[i] *= kraw[i];
-        }
+        float sc[4];
         bool raise = false;
-        float sc[NT][4];
-#pragma unroll
-        for (int tile = 0; tile < NT; ++tile)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool ok = pos0 + 4 * lg + i < nvis[tile];
-                sc[tile][i] = ok ? (s[tile][i] - corr[tile]) * ksc[i] : -INFINITY;
-                raise |= sc[tile][i] > mref[tile] + 8.0f;
-            }
-        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-            // raise the references of the rows to their block maxima; rescale
-            float alpha[NT];
-#pragma unroll
-            for (int tile = 0; tile < NT; ++tile) {
-                float bm = fmaxf(fmaxf(sc[tile][0], sc[tile][1]), fmaxf(sc[tile][2], sc[tile][3]));
-                bm = fmaxf(bm, __shfl_xor(bm, 16));
-                bm = fmaxf(bm, __shfl_xor(bm, 32));
-                const float mn = fmaxf(mref[tile], bm);
-                const float base = mn == -INFINITY ? 0.0f : mn;
-                alpha[tile] = exp2_guarded(mref[tile] - base);
-                mref[tile] = mn;
-                lpart[tile] *= alpha[tile];
-                spart[tile] *= alpha[tile];
-                if (lg == 0) redist[wv][tile][l16] = alpha[tile];
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-            for (int tile = 0; tile < NT; ++tile) {
-                f32x4 a4;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) a4[i] = redist[wv][tile][4 * lg + i];
-#pragma unroll
-                for (int nd = 0; nd < NDT; ++nd) o[tile][nd] *= a4;
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
-        float vsc[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            vsc[i] = 1.0f;
-            if constexpr (I8) {
-                const bool ok = pos0 + 4 * lg + i < end;
-                vsc[i] = ok ? vraw[i] * vsh : 0.0f;
-            }
+            const bool ok = pos0 + 4 * lg + i < nvis;
+            float ksc = qpost;
+            if constexpr (I8) ksc *= kraw[i];
+            sc[i] = ok ? (s[i] - corr) * ksc : -INFINITY;
+            raise |= sc[i] > mref + 8.0f;
         }
-        uint32_t pa[NT][2];
+        const bool any = __builtin_amdgcn_ballot_w64(raise) != 0;
+        if (any) {
+            float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+            bm = fmaxf(bm, __shfl_xor(bm, 16));
+            bm = fmaxf(bm, __shfl_xor(bm, 32));
+            const float mn = fmaxf(mref, bm);
+            const float base = mn == -INFINITY ? 0.0f : mn;
+            const float alpha = exp2_guarded(mref - base);
+            mref = mn;
+            lpart *= alpha;
+            spart *= alpha;
+            if (lg == 0) ast[stage][wv][l16] = alpha;
+        }
+        if (lane == 0) araise[stage][wv] = any ? 1 : 0;
+        const float base = mref == -INFINITY ? 0.0f : mref;
+        float pr[4];
 #pragma unroll
-        for (int tile = 0; tile < NT; ++tile) {
-            const float base = mref[tile] == -INFINITY ? 0.0f : mref[tile];
-            float pr[4];
+        for (int i = 0; i < 4; ++i) {
+            pr[i] = sc[i] == -INFINITY ? 0.0f : exp2f(sc[i] - base);
+            lpart += pr[i];
+        }
+        u32x2 pa;
+        if constexpr (I8) {
+            float ph2[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                pr[i] = sc[tile][i] == -INFINITY ? 0.0f : exp2f(sc[tile][i] - base);
-                lpart[tile] += pr[i];
+                const bool ok = pos0 + 4 * lg + i < end;
+                ph2[i] = (float)(_Float16)(ok ? pr[i] * vraw[i] * vsh : 0.0f);
+                spart += ph2[i];
             }
-            if constexpr (I8) {
-                float ph[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    ph[i] = (float)(_Float16)(pr[i] * vsc[i]);
-                    spart[tile] += ph[i];
-                }
-                pa[tile][0] = pack_f16x2(ph[0], ph[1]);
-                pa[tile][1] = pack_f16x2(ph[2], ph[3]);
-            } else {
-                pa[tile][0] = pack_bf16x2(pr[0], pr[1]);
-                pa[tile][1] = pack_bf16x2(pr[2], pr[3]);
-            }
+            pa = u32x2{pack_f16x2(ph2[0], ph2[1]), pack_f16x2(ph2[2], ph2[3])};
+        } else {
+            pa = u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
         }
+        pst[stage][wv][lane] = pa;
+    };
 
-        // ---------------------------------------------------- PV
+    // PV of block j (all waves): probabilities from LDS stage j % 2, V from registers
+    auto values = [&](int j, const Raw<VB>* vsrc) {
+        const int stage = j & 1;
+        const int pos0 = j * kBlockSize;
+        u32x2 bop[NDT];
         const bool partial = pos0 + kBlockSize > end;  // tokens past the end may hold anything
 #pragma unroll
         for (int nd = 0; nd < NDT; ++nd) {
-            u32x2 bw;
             if constexpr (I8) {
-                const uint32_t tw = quad_transpose8(vr[nd].w[0], l16 & 3) ^ 0x80808080u;
-                bw.x = f16pair_lo(tw);
-                bw.y = f16pair_hi(tw);
+                const uint32_t tw = quad_transpose8(vsrc[nd].w[0], l16 & 3) ^ 0x80808080u;
+                bop[nd] = u32x2{f16pair_lo(tw), f16pair_hi(tw)};
             } else {
-                u32x2 w;
-                w.x = vr[nd].w[0];
-                w.y = vr[nd].w[1];
-                bw = quad_transpose16(w, l16 & 3);
+                u32x2 w = quad_transpose16(u32x2{vsrc[nd].w[0], vsrc[nd].w[1]}, l16 & 3);
                 if (partial) {
-                    // element k of the operand is token 4*lg + k
-                    const int t0 = pos0 + 4 * lg;
-                    bw.x = (t0 + 0 < end ? bw.x & 0x0000FFFFu : 0u) | (t0 + 1 < end ? bw.x & 0xFFFF0000u : 0u);
-                    bw.y = (t0 + 2 < end ? bw.y & 0x0000FFFFu : 0u) | (t0 + 3 < end ? bw.y & 0xFFFF0000u : 0u);
+                    const int t0 = pos0 + 4 * lg;  // element k is token 4*lg + k
+                    w.x = (t0 + 0 < end ? w.x & 0x0000FFFFu : 0u) | (t0 + 1 < end ? w.x & 0xFFFF0000u : 0u);
+                    w.y = (t0 + 2 < end ? w.y & 0x0000FFFFu : 0u) | (t0 + 3 < end ? w.y & 0xFFFF0000u : 0u);
                 }
+                bop[nd] = w;
             }
+        }
 #pragma unroll
-            for (int tile = 0; tile < NT; ++tile) {
-                u32x2 av;
-                av.x = pa[tile][0];
-                av.y = pa[tile][1];
+        for (int t = 0; t < NT; ++t) {
+            if (araise[stage][t]) {
+                f32x4 a4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a4[i] = ast[stage][t][4 * lg + i];
+#pragma unroll
+                for (int nd = 0; nd < NDT; ++nd) o[t][nd] *= a4;
+            }
+            const u32x2 pa = pst[stage][t][lane];
+#pragma unroll
+            for (int nd = 0; nd < NDT; ++nd) {
                 if constexpr (I8)
-                    o[tile][nd] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                        __builtin_bit_cast(f16x4, av), __builtin_bit_cast(f16x4, bw), o[tile][nd], 0, 0, 0);
+                    o[t][nd] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                        __builtin_bit_cast(f16x4, pa), __builtin_bit_cast(f16x4, bop[nd]), o[t][nd], 0, 0, 0);
                 else
-                    o[tile][nd] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                        __builtin_bit_cast(bf16x4, av), __builtin_bit_cast(bf16x4, bw), o[tile][nd], 0, 0, 0);
+                    o[t][nd] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                        __builtin_bit_cast(bf16x4, pa), __builtin_bit_cast(bf16x4, bop[nd]), o[t][nd], 0, 0, 0);
             }
         }
-        phys = phys_next;
-    }
+    };
 
-    // ------------------------------------------------------------ epilogue
-    // row sums over the four lane groups (score layout)
-    float inv[NT], bias[NT];
-#pragma unroll
-    for (int tile = 0; tile < NT; ++tile) {
-        float l = lpart[tile];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        float sp = spart[tile];
-        sp += __shfl_xor(sp, 16);
-        sp += __shfl_xor(sp, 32);
-        const int r = row0 + 16 * tile + l16;
-        inv[tile] = l > 0.0f ? 1.0f / l : 0.0f;
-        bias[tile] = kCodeBias * sp;
-        if (wv == 0 && lg == 0 && r < R) {
-            const float lse2 = l > 0.0f ? (mref[tile] + log2f(l)) * kLn2 : -INFINITY;
-            const int64_t rid = row_out(r);
-            if (p.NP == 1) {
-                if (p.lse != nullptr) p.lse[rid] = lse2;
-            } else {
-                p.ws_lse[rid * p.NP + part] = lse2;
-            }
-        }
-    }
-    // move 1/l (and the int8 bias) to the output layout through LDS
-#pragma unroll
-    for (int tile = 0; tile < NT; ++tile) {
-        float biasrow[4], invrow[4];
-        if (lg == 0) redist[wv][tile][l16] = inv[tile];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int i = 0; i < 4; ++i) invrow[i] = redist[wv][tile][4 * lg + i];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if constexpr (I8) {
-            if (lg == 0) redist[wv][tile][l16] = bias[tile];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-            for (int i = 0; i < 4; ++i) biasrow[i] = redist[wv][tile][4 * lg + i];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
+    // prologue: K(j0) staged, K(j0+1), K(j0+2) and V(j0), V(j0+1) in registers,
+    // scores of block j0 done
+    {
+        load_kq(kq[0], phys_of(j0));
+        load_kq(kq[1], phys_of(j0 + 1));
+        load_vq(vq[0], phys_of(j0));
+        load_vq(vq[1], phys_of(j0 + 1));
+        float kraw[4], vraw[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = row0 + 16 * tile + 4 * lg + i;
+            kraw[i] = kq[0].ks[i];
+            vraw[i] = kq[0].vs[i];
+        }
+        store_kq(kq[0], j0 & 1);
+        load_kq(kq[0], phys_of(j0 + 2));
+        __syncthreads();
+        if (owner) scores(j0, kraw, vraw);
+    }
+    // iteration j: stage K(j+1), barrier, scores of j+1, PV of j.
+    // kq[(j - j0 + 1) & 1] holds K(j+1), vq[(j - j0) & 1] holds V(j).
+    auto iter = [&](int j, auto xc) {
+        constexpr int X = decltype(xc)::value;  // (j - j0) & 1
+        float kraw[4], vraw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            kraw[i] = kq[1 - X].ks[i];
+            vraw[i] = kq[1 - X].vs[i];
+        }
+        store_kq(kq[1 - X], (j + 1) & 1);
+        load_kq(kq[1 - X], phys_of(j + 3));
+        __syncthreads();
+        if (owner && j + 1 < jend) scores(j + 1, kraw, vraw);
+        values(j, vq[X]);
+        load_vq(vq[X], phys_of(j + 2));
+    };
+    int j = j0;
+    for (; j + 1 < jend; j += 2) {
+        iter(j, ic<0>{});
+        iter(j + 1, ic<1>{});
+    }
+    if (j < jend) iter(j, ic<0>{});
+
+    // ------------------------------------------------------------ epilogue
+    if (owner) {
+        float l = lpart;
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        float sp = spart;
+        sp += __shfl_xor(sp, 16);
+        sp += __shfl_xor(sp, 32);
+        if (lg == 0) {
+            fin[0][wv][l16] = l > 0.0f ? 1.0f / l : 0.0f;
+            fin[1][wv][l16] = kCodeBias * sp;
+            if (myrow < R) {
+                const float lse2 = l > 0.0f ? (mref + log2f(l)) * kLn2 : -INFINITY;
+                const int64_t rid = row_out(myrow);
+                if (p.NP == 1) {
+                    if (p.lse != nullptr) p.lse[rid] = lse2;
+                } else {
+                    p.ws_lse[rid * p.NP + part] = lse2;
+                }
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = row0 + 16 * t + 4 * lg + i;
             if (r >= R) continue;
+            const float inv = fin[0][t][4 * lg + i];
+            const float bias = fin[1][t][4 * lg + i];
             const int64_t rid = row_out(r);
 #pragma unroll
             for (int nd = 0; nd < NDT; ++nd) {
-                float v = o[tile][nd][i];
-                if constexpr (I8) v = (v - biasrow[i]) * vsh_inv;
-                v *= invrow[i];
+                float v = o[t][nd][i];
+                if constexpr (I8) v = (v - bias) * vsh_inv;
+                v *= inv;
                 const int d = wv * DW + 16 * nd + l16;
                 if (p.NP == 1) {
                     if (p.out_bf16)
