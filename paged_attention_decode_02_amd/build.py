@@ -25,6 +25,9 @@ HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 COMMON = [
     "-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the decode rescales them with vector
+    # ALU ops, which would otherwise copy them out of and back into AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-parameter", "-Wno-unknown-pragmas",
 ]
 

@@ -248,6 +248,11 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     const int j0 = start / kBlockSize, jend = (end + kBlockSize - 1) / kBlockSize;
     // physical block of logical block j; past the end the last one (re-read)
     auto phys_of = [&](int j) -> int64_t { return (int64_t)table[j < jend ? j : jend - 1]; };
+    // Inside the block loop the table entries go through the vector memory
+    // path (the workgroup barrier's fences keep the compiler from scalar
+    // loads there), and loads complete in issue order: an entry is therefore
+    // requested one iteration before it is used, ahead of that iteration's
+    // K/V prefetches, so waiting for it never drains them.
 
     // int8: probabilities times value scales are kept below 2^15 (f16) by 2^vsh
     float vsh = 1.0f, vsh_inv = 1.0f;
@@ -282,7 +287,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
         for (int i = 0; i < KSW; ++i) {
             const int ks = wv * KSW + i;
-            if (ks < KS) load_raw<KQB, true>(dst.k[i], base + 32 * ks * E);
+            if (KS % kW == 0 || ks < KS) load_raw<KQB, true>(dst.k[i], base + 32 * ks * E);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -298,7 +303,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
         for (int i = 0; i < KSW; ++i) {
             const int ks = wv * KSW + i;
-            if (ks < KS) {
+            if (KS % kW == 0 || ks < KS) {
                 u32x4 a;
                 if constexpr (I8) {
                     const uint32_t u0 = src.k[i].w[0] ^ 0x80808080u, u1 = src.k[i].w[1] ^ 0x80808080u;
@@ -444,10 +449,13 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
         __syncthreads();
         if (owner) scores(j0, kraw, vraw);
     }
+    int64_t ph2 = phys_of(j0 + 2);  // physical blocks of j+2 and j+3 at iteration j
+    int t3 = (int)phys_of(j0 + 3);
     // iteration j: stage K(j+1), barrier, scores of j+1, PV of j.
     // kq[(j - j0 + 1) & 1] holds K(j+1), vq[(j - j0) & 1] holds V(j).
     auto iter = [&](int j, auto xc) {
         constexpr int X = decltype(xc)::value;  // (j - j0) & 1
+        const int t4 = table[j + 4 < jend ? j + 4 : jend - 1];
         float kraw[4], vraw[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -455,11 +463,14 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
             vraw[i] = kq[1 - X].vs[i];
         }
         store_kq(kq[1 - X], (j + 1) & 1);
-        load_kq(kq[1 - X], phys_of(j + 3));
+        const int64_t ph3 = __builtin_amdgcn_readfirstlane(t3);
+        load_kq(kq[1 - X], ph3);
         __syncthreads();
         if (owner && j + 1 < jend) scores(j + 1, kraw, vraw);
         values(j, vq[X]);
-        load_vq(vq[X], phys_of(j + 2));
+        load_vq(vq[X], ph2);
+        ph2 = ph3;
+        t3 = t4;
     };
     int j = j0;
     for (; j + 1 < jend; j += 2) {
