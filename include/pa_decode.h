@@ -137,6 +137,7 @@ int pa_decode(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq
  * then lse [B, Tq, Hq, NP] at the next 256-byte boundary. Row (b, t, h)
  * reads partitions i < ceil(max(n, 0) / partition_size) with
  * n = seq_lens[b] - Tq + t + 1, which are exactly the ones pa_decode writes.
+ * workspace and out must be 16-byte aligned (PA_ERR_ALIGN otherwise).
  */
 int pa_decode_splitk_reduce(const void* workspace, int32_t num_partitions, int32_t partition_size, int32_t B,
                             int32_t Tq, int32_t Hq, int32_t D, const int32_t* seq_lens, void* out,

@@ -10,45 +10,59 @@
 // requests' slots: vllm-sm70 page, "Known limitations").
 //
 // One wave per (token, kv head); lane c handles D/64 consecutive elements.
+// The source rows are requested before the slot, so both loads are in flight
+// together.
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
 namespace pa {
 
-template <int CT, int D>
+template <int CT, int D, bool SRC_BF16>
 __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
-    constexpr int EPL = D / 64;  // elements per lane
+    constexpr int EPL = D / 64;               // elements per lane
+    constexpr int SB = EPL * (SRC_BF16 ? 2 : 4);  // source bytes per lane
     const int lane = threadIdx.x & 63;
-    const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (token, kv head)
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t pair = (int64_t)blockIdx.x * 4 + wv;  // (token, kv head)
     if (pair >= p.num_tokens * p.Hkv) return;
     const int64_t i = pair / p.Hkv;
     const int g = (int)(pair % p.Hkv);
+    const int64_t src_off = (i * p.Hkv + g) * D + lane * EPL;
+    Raw<SB> raw[2];
+    load_raw<SB>(raw[0], reinterpret_cast<const char*>(p.k_src) + src_off * (SRC_BF16 ? 2 : 4));
+    load_raw<SB>(raw[1], reinterpret_cast<const char*>(p.v_src) + src_off * (SRC_BF16 ? 2 : 4));
     const int64_t slot = p.slots[i];
     if (slot < 0) return;  // wave-uniform
-    const int64_t src_off = (i * p.Hkv + g) * D + lane * EPL;
     const int64_t dst_row = slot * p.Hkv + g;  // (block * 16 + offset) * Hkv + g
     const int64_t dst_off = dst_row * D + lane * EPL;
 
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
-        const void* src = which ? p.v_src : p.k_src;
         void* cache = which ? p.v_cache : p.k_cache;
         float x[EPL];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            x[e] = p.src_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(src)[src_off + e])
-                              : reinterpret_cast<const float*>(src)[src_off + e];
-        }
+        for (int e = 0; e < EPL; ++e) x[e] = elem_f32<SRC_BF16 ? KV_BF16 : KV_F32>(raw[which], e);
         if constexpr (CT == KV_F32) {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) reinterpret_cast<float*>(cache)[dst_off + e] = x[e];
         } else if constexpr (CT == KV_BF16) {
+            uint16_t* dst = reinterpret_cast<uint16_t*>(cache) + dst_off;
+            uint32_t w[(EPL + 1) / 2];
+            if constexpr (SRC_BF16) {  // bit copy
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                reinterpret_cast<uint16_t*>(cache)[dst_off + e] =
-                    p.src_bf16 ? reinterpret_cast<const uint16_t*>(src)[src_off + e]  // bit copy
-                               : f32_to_bf16(x[e]);
+                for (int k = 0; k < (EPL + 1) / 2; ++k) w[k] = raw[which].w[k];
+            } else {
+#pragma unroll
+                for (int k = 0; k < EPL / 2; ++k)
+                    w[k] = (uint32_t)f32_to_bf16(x[2 * k]) | ((uint32_t)f32_to_bf16(x[2 * k + 1]) << 16);
+                if constexpr (EPL == 1) w[0] = f32_to_bf16(x[0]);
             }
+            if constexpr (EPL == 4)
+                *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+            else if constexpr (EPL == 2)
+                *reinterpret_cast<uint32_t*>(dst) = w[0];
+            else
+                *dst = (uint16_t)w[0];
         } else {
             float amax = 0.0f;
 #pragma unroll
@@ -79,19 +93,24 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
 }
 
 namespace {
-template <int CT>
-hipError_t launch_ct(int D, const CacheWriteParams& p, hipStream_t s) {
+template <int CT, bool SB>
+hipError_t launch_src(int D, const CacheWriteParams& p, hipStream_t s) {
     const int64_t pairs = p.num_tokens * p.Hkv;
     const int64_t grid = (pairs + 3) / 4;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     switch (D) {
-    case 64: hipLaunchKernelGGL((cache_write_kernel<CT, 64>), dim3((unsigned)grid), dim3(256), 0, s, p); break;
-    case 128: hipLaunchKernelGGL((cache_write_kernel<CT, 128>), dim3((unsigned)grid), dim3(256), 0, s, p); break;
-    case 256: hipLaunchKernelGGL((cache_write_kernel<CT, 256>), dim3((unsigned)grid), dim3(256), 0, s, p); break;
+    case 64: hipLaunchKernelGGL((cache_write_kernel<CT, 64, SB>), dim3((unsigned)grid), dim3(256), 0, s, p); break;
+    case 128: hipLaunchKernelGGL((cache_write_kernel<CT, 128, SB>), dim3((unsigned)grid), dim3(256), 0, s, p); break;
+    case 256: hipLaunchKernelGGL((cache_write_kernel<CT, 256, SB>), dim3((unsigned)grid), dim3(256), 0, s, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <int CT>
+hipError_t launch_ct(int D, const CacheWriteParams& p, hipStream_t s) {
+    return p.src_bf16 ? launch_src<CT, true>(D, p, s) : launch_src<CT, false>(D, p, s);
 }
 }  // namespace
 

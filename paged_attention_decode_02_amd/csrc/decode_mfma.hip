@@ -384,6 +384,10 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
             pa = u32x2{pack_f16x2(ph2[0], ph2[1]), pack_f16x2(ph2[2], ph2[3])};
         } else {
             pa = u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+            // sum of the rounded weights: the output is normalised by it, so it
+            // stays a convex combination of value rows (l keeps the exact ones)
+            spart += bf16_to_f32((uint16_t)pa.x) + bf16_to_f32((uint16_t)(pa.x >> 16)) +
+                     bf16_to_f32((uint16_t)pa.y) + bf16_to_f32((uint16_t)(pa.y >> 16));
         }
         pst[stage][wv][lane] = pa;
     };
@@ -488,7 +492,8 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
         sp += __shfl_xor(sp, 16);
         sp += __shfl_xor(sp, 32);
         if (lg == 0) {
-            fin[0][wv][l16] = l > 0.0f ? 1.0f / l : 0.0f;
+            const float lnorm = I8 ? l : sp;  // bf16: the sum of the weights the values were multiplied by
+            fin[0][wv][l16] = lnorm > 0.0f ? 1.0f / lnorm : 0.0f;
             fin[1][wv][l16] = kCodeBias * sp;
             if (myrow < R) {
                 const float lse2 = l > 0.0f ? (mref + log2f(l)) * kLn2 : -INFINITY;

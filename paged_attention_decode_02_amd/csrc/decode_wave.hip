@@ -29,13 +29,15 @@
 // rescaled); otherwise p = exp2(s - m) <= 256 and the result is exact anyway
 // because o and l share the reference. Each exp is computed once.
 //
-// PV. The probabilities go through a 0.5 KB per-wave LDS buffer to the PV
-// layout, in which a group of lanes takes one whole value row (16-byte or
-// smaller loads, D*elt/4 lanes per token) and lane i owns D/64 (or more)
-// output elements for all GT heads. bf16 values use fp32 FMA; int8 values
-// use v_dot2 over pairs of tokens: the probabilities (times the value scale)
-// as f16 pairs and the codes as (1024 + code + 128) f16 pairs, with
-// 1152 * sum(p) subtracted once at the end.
+// PV. The probabilities go through a small per-wave LDS buffer, as 16-bit
+// pairs of consecutive tokens, to the PV layout, in which a group of lanes
+// takes one whole value row (16-byte or smaller loads, D*elt/4 lanes per
+// token) and lane i owns D/64 (or more) output elements for all GT heads.
+// Both cache types use v_dot2 over pairs of tokens: bf16 values against bf16
+// weights (the running sum l adds the same rounded weights, so the output is
+// a convex combination of value rows); int8 codes as (1024 + code + 128) f16
+// pairs against f16 weights times the value scale, with 1152 * sum(p)
+// subtracted once at the end.
 //
 // Loads are ping-ponged: the V block is requested before the QK of the same
 // block, the next K block before the PV, so one half-block is always in
@@ -136,18 +138,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     constexpr int EV = VB / E;    // value elements per lane per token
     constexpr int STEPS = kBlockSize / TPW;
     static_assert(KB >= 4 && VB >= 4, "layout");
-    static_assert(!I8 || STEPS % 2 == 0, "int8 pairs tokens");
+    static_assert(STEPS % 2 == 0, "PV pairs tokens");
 
-    __shared__ __align__(16) float pbuf_all[kWaves][kBlockSize * GP];
+    __shared__ __align__(16) uint32_t pbuf_all[kWaves][kBlockSize / 2 * GP];
     __shared__ __align__(16) float merge_o[kWaves][GT][64 * EV];
-    __shared__ float merge_ml[kWaves][2][GT];
+    __shared__ float merge_ml[kWaves][3][GT];  // m, l, sum of the 16-bit weights
 
     // the wave index is uniform across the wave: saying so keeps the block
     // loop, the table reads and the base addresses on the scalar unit
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    float* pbuf_f = pbuf_all[wv];                            // bf16: p[token][head]
-    uint32_t* pbuf_u = reinterpret_cast<uint32_t*>(pbuf_f);  // int8: f16 pairs [token/2][head]
+    // 16-bit weight pairs [token / 2][head] (bf16, or f16 for int8 values)
+    uint32_t* pbuf_u = reinterpret_cast<uint32_t*>(pbuf_all[wv]);
     const int r = lane >> 4, c16 = lane & 15;
     // coordinates of the lane in the basis of the DPP pairings {15, 7, 2, 1}
     const int b0 = c16 & 1, b1 = (c16 >> 1) & 1, b2 = (c16 >> 2) & 1, b3 = (c16 >> 3) & 1;
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     float mref[GT];  // per-head reference (log2 units), uniform across the wave
     float mloc[NI];  // mref of the lane's item heads
     float lloc[NI];  // partial sums of p over the lane's items
-    float sloc[NI];  // int8: partial sums of the f16 probabilities (times value scales)
+    float sloc[NI];  // partial sums of the 16-bit weights (int8: times the value scales)
     float o[GT][EV];
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
@@ -470,43 +472,65 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
         for (int j2 = 0; j2 < NI; ++j2) {
             const float base = mloc[j2] == -INFINITY ? 0.0f : mloc[j2];
             const float pr = sc[j2] == -INFINITY ? 0.0f : exp2f(sc[j2] - base);
-            lloc[j2] += pr;
+            uint16_t* slot16 = reinterpret_cast<uint16_t*>(pbuf_u) + ((my_tok >> 1) * GP + ihead[j2]) * 2 + (my_tok & 1);
             if constexpr (I8) {
+                lloc[j2] += pr;
                 const _Float16 ph = (_Float16)(tok_ok ? pr * sv : 0.0f);
                 sloc[j2] += (float)ph;
-                reinterpret_cast<_Float16*>(pbuf_u)[((my_tok >> 1) * GP + ihead[j2]) * 2 + (my_tok & 1)] = ph;
+                *slot16 = __builtin_bit_cast(uint16_t, ph);
             } else {
-                pbuf_f[my_tok * GP + ihead[j2]] = pr;
+                // bf16 weight (pr is finite and >= 0: plain round to nearest
+                // even). l keeps the exact weights (for the LSE); the output is
+                // normalised by the sum of the rounded ones, so it stays a
+                // convex combination of value rows
+                const uint32_t u = __float_as_uint(pr);
+                const uint32_t pb = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+                lloc[j2] += pr;
+                sloc[j2] += __uint_as_float(pb << 16);
+                *slot16 = (uint16_t)pb;
             }
         }
         wave_lds_sync();
 
         // ---------------------------------------------------------------- PV
-        if constexpr (I8) {
+        // tokens past the end may hold anything (bf16: NaN or Inf times a zero
+        // weight); int8 codes are always finite, so only bf16 needs the mask
+        if constexpr (!I8) {
+            if (pos0 + kBlockSize > end) {
 #pragma unroll
-            for (int st = 0; st < STEPS; st += 2) {
-                const int tk = st * TPW + vgrp;  // tokens tk and tk + TPW share a p pair when TPW == 1
-                // token pair (tk, tk + TPW): the LDS pairs are (2k, 2k + 1); with TPW > 1
-                // the two tokens of a lane are not adjacent, so read them separately
-                uint32_t pp[GT];
-                if constexpr (TPW == 1) {
+                for (int st = 0; st < STEPS; ++st) {
+                    const bool ok = pos0 + st * TPW + vgrp < end;
 #pragma unroll
-                    for (int h = 0; h < GT; ++h) pp[h] = pbuf_u[(tk >> 1) * GP + h];
-                } else {
-                    const _Float16* ph = reinterpret_cast<const _Float16*>(pbuf_u);
-                    const int t1 = tk + TPW;
-#pragma unroll
-                    for (int h = 0; h < GT; ++h) {
-                        const uint16_t lo = __builtin_bit_cast(uint16_t, ph[((tk >> 1) * GP + h) * 2 + (tk & 1)]);
-                        const uint16_t hi = __builtin_bit_cast(uint16_t, ph[((t1 >> 1) * GP + h) * 2 + (t1 & 1)]);
-                        pp[h] = (uint32_t)lo | ((uint32_t)hi << 16);
-                    }
+                    for (int w = 0; w < VB / 4; ++w) vr[st].w[w] = ok ? vr[st].w[w] : 0u;
                 }
+            }
+        }
 #pragma unroll
-                for (int w = 0; w < VB / 4; ++w) {
-                    // codes are always finite and masked tokens carry p = 0: no select
-                    const uint32_t A = vr[st].w[w];
-                    const uint32_t B = vr[st + 1].w[w];
+        for (int st = 0; st < STEPS; st += 2) {
+            // token pair (tk, tk + TPW) against 16-bit weight pairs: the LDS
+            // pairs are tokens (2k, 2k + 1), so with TPW > 1 the lane's two
+            // tokens are read separately
+            const int tk = st * TPW + vgrp;
+            uint32_t pp[GT];
+            if constexpr (TPW == 1) {
+#pragma unroll
+                for (int h = 0; h < GT; ++h) pp[h] = pbuf_u[(tk >> 1) * GP + h];
+            } else {
+                const uint16_t* ph = reinterpret_cast<const uint16_t*>(pbuf_u);
+                const int t1 = tk + TPW;
+#pragma unroll
+                for (int h = 0; h < GT; ++h) {
+                    const uint32_t lo = ph[((tk >> 1) * GP + h) * 2 + (tk & 1)];
+                    const uint32_t hi = ph[((t1 >> 1) * GP + h) * 2 + (t1 & 1)];
+                    pp[h] = lo | (hi << 16);
+                }
+            }
+#pragma unroll
+            for (int w = 0; w < VB / 4; ++w) {
+                const uint32_t A = vr[st].w[w];
+                const uint32_t B = vr[st + 1].w[w];
+                if constexpr (I8) {
+                    // codes as (1024 + code + 128) f16 pairs of the two tokens
                     const uint32_t x0 = __builtin_amdgcn_perm(B, A, 0x05010400u) ^ 0x80808080u;  // a0 b0 a1 b1
                     const uint32_t x1 = __builtin_amdgcn_perm(B, A, 0x07030602u) ^ 0x80808080u;  // a2 b2 a3 b3
                     const uint32_t f0 = f16pair_lo(x0), f1 = f16pair_hi(x0);
@@ -518,21 +542,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
                         o[h][4 * w + 2] = dot2_f16(pp[h], f2, o[h][4 * w + 2]);
                         o[h][4 * w + 3] = dot2_f16(pp[h], f3, o[h][4 * w + 3]);
                     }
-                }
-            }
-        } else {
+                } else {
+                    // bf16 pairs (element e of token tk, element e of token tk + TPW)
+                    const uint32_t e0 = __builtin_amdgcn_perm(B, A, 0x05040100u);
+                    const uint32_t e1 = __builtin_amdgcn_perm(B, A, 0x07060302u);
 #pragma unroll
-            for (int st = 0; st < STEPS; ++st) {
-                const int tk = st * TPW + vgrp;
-                const bool ok = pos0 + tk < end;
-                float pr[GT];
-#pragma unroll
-                for (int h = 0; h < GT; ++h) pr[h] = pbuf_f[tk * GP + h];
-#pragma unroll
-                for (int e = 0; e < EV; ++e) {
-                    const float v = ok ? elem_f32<KV_BF16>(vr[st], e) : 0.0f;
-#pragma unroll
-                    for (int h = 0; h < GT; ++h) o[h][e] = fmaf(pr[h], v, o[h][e]);
+                    for (int h = 0; h < GT; ++h) {
+                        o[h][2 * w + 0] = dot2_bf16(pp[h], e0, o[h][2 * w + 0]);
+                        o[h][2 * w + 1] = dot2_bf16(pp[h], e1, o[h][2 * w + 1]);
+                    }
                 }
             }
         }
@@ -563,7 +581,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
         }
         // lanes that duplicate an item (plain butterfly levels) count it more than once
         lh[h] = wave_sum(v);
-        sh[h] = I8 ? wave_sum(w2) : 0.0f;
+        sh[h] = wave_sum(w2);
     }
     // duplication factor of the plain levels
     constexpr int DUP = (Split<GT>::kC ? 1 : 2) * (Split<GT>::kD ? 1 : 2);
@@ -584,6 +602,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
         for (int h = 0; h < GT; ++h) {
             merge_ml[wv][0][h] = mref[h];
             merge_ml[wv][1][h] = lh[h] * (1.0f / DUP);
+            merge_ml[wv][2][h] = sh[h] * (1.0f / DUP);
         }
     }
     __syncthreads();
@@ -593,13 +612,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) M = fmaxf(M, merge_ml[w][0][h]);
         const float base = M == -INFINITY ? 0.0f : M;
-        float wt[kWaves], l = 0.0f;
+        float wt[kWaves], l = 0.0f, lr = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
             wt[w] = exp2_guarded(merge_ml[w][0][h] - base);
             l += merge_ml[w][1][h] * wt[w];
+            lr += merge_ml[w][2][h] * wt[w];
         }
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        const float lnorm = I8 ? l : lr;  // bf16: the sum of the weights the values were multiplied by
+        const float inv = lnorm > 0.0f ? 1.0f / lnorm : 0.0f;
         const float lse2 = l > 0.0f ? (M + log2f(l)) * kLn2 : -INFINITY;
         const int64_t rowid = rowbase + h;
         for (int d = lane; d < D; d += 64) {

@@ -270,6 +270,7 @@ int pa_decode_splitk_reduce(const void* workspace, int32_t num_partitions, int32
     if (out_dtype != PA_F32 && out_dtype != PA_BF16)
         return fail(PA_ERR_DTYPE, "out dtype %d not in {f32, bf16}", (int)out_dtype);
     if (!workspace || !seq_lens || !out) return fail(PA_ERR_NULL, "workspace, seq_lens and out must be non-NULL");
+    if (!aligned16(workspace) || !aligned16(out)) return fail(PA_ERR_ALIGN, "workspace and out must be 16-byte aligned");
     if (B == 0) return ok();
     const size_t rows = (size_t)B * Tq * Hq;
     pa::ReduceParams p{};

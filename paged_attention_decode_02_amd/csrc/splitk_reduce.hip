@@ -7,8 +7,11 @@
 // One 1024-thread workgroup per (b, t, h) row. The threads form
 // S = 1024 / (D/4) slices of D/4 threads; thread (slice, q) owns output
 // elements 4q..4q+3 (one 16-byte load per partition) and takes partitions
-// slice, slice + S, ...; the weights of up to 1024 partitions at a time sit in
-// LDS. Slices are combined in a fixed order, so the result is deterministic.
+// slice, slice + S, ... . Slices are combined in a fixed order, so the result
+// is deterministic. Every load of the first kPre partitions of a thread is
+// issued before the row's length is known (addresses depend only on the
+// partition count), so the row costs one memory round trip; partitions past
+// the row's visible length are masked afterwards.
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -16,7 +19,7 @@ namespace pa {
 
 namespace {
 constexpr int kThreads = 1024;
-constexpr int kChunk = 1024;  // partitions whose weights are staged in LDS at a time
+constexpr int kPre = 4;  // partitions per thread loaded up front
 
 __device__ __forceinline__ float block_max(float v, float* red) {
     v = wave_max(v);
@@ -42,49 +45,64 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }  // namespace
 
 __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(ReduceParams p) {
-    __shared__ float wts[kChunk];
     __shared__ float red[kThreads / 64];
     __shared__ float4 part[kThreads];
     const int tid = threadIdx.x;
     const int64_t rowid = blockIdx.x;
     const int t = (int)((rowid / p.Hq) % p.Tq);
     const int b = (int)(rowid / ((int64_t)p.Hq * p.Tq));
-    const int n = p.seq_lens[b] - p.Tq + t + 1;
-    const int np = n > 0 ? min((n + p.P - 1) / p.P, p.NP) : 0;
     const float* lse_row = p.ws_lse + rowid * p.NP;
     const float4* o_row = reinterpret_cast<const float4*>(p.ws_o + rowid * p.NP * p.D);
-
-    float mx = -INFINITY;
-    for (int i = tid; i < np; i += kThreads) mx = fmaxf(mx, lse_row[i]);
-    const float M = block_max(mx, red);
-    const float mref = M == -INFINITY ? 0.0f : M;
-
     const int DQ = p.D / 4;  // float4 columns
     const int S = kThreads / DQ;
     const int slice = tid / DQ, q = tid % DQ;
+
+    float4 ov[kPre];
+    float lv[kPre];
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+        const int i = slice + k * S;
+        ov[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        lv[k] = -INFINITY;
+        if (i < p.NP) {
+            ov[k] = o_row[(int64_t)i * DQ + q];
+            lv[k] = lse_row[i];
+        }
+    }
+    float lmax[kPre];
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+        const int i = tid + k * kThreads;
+        lmax[k] = i < p.NP ? lse_row[i] : -INFINITY;
+    }
+    const int n = p.seq_lens[b] - p.Tq + t + 1;
+    const int np = n > 0 ? min((n + p.P - 1) / p.P, p.NP) : 0;
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kPre; ++k)
+        if (tid + k * kThreads < np) mx = fmaxf(mx, lmax[k]);
+    for (int i = tid + kPre * kThreads; i < np; i += kThreads) mx = fmaxf(mx, lse_row[i]);
+    const float M = block_max(mx, red);
+    const float mref = M == -INFINITY ? 0.0f : M;
+
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float wsum = 0.0f;
-    for (int c0 = 0; c0 < np; c0 += kChunk) {
-        const int cn = min(kChunk, np - c0);
-        for (int i = tid; i < cn; i += kThreads) {
-            const float li = lse_row[c0 + i];
-            const float w = li == -INFINITY ? 0.0f : __expf(li - mref);
-            wts[i] = w;
-            wsum += w;
-        }
-        __syncthreads();
-#pragma unroll 4
-        for (int i = slice; i < cn; i += S) {
-            const float w = wts[i];
-            const float4 v = o_row[(int64_t)(c0 + i) * DQ + q];
-            acc.x = fmaf(w, v.x, acc.x);
-            acc.y = fmaf(w, v.y, acc.y);
-            acc.z = fmaf(w, v.z, acc.z);
-            acc.w = fmaf(w, v.w, acc.w);
-        }
-        __syncthreads();
-    }
-    const float W = block_sum(wsum, red);
+    auto add = [&](int i, float li, float4 v) {
+        const bool ok = i < np && li != -INFINITY;  // partials past the row's length are stale
+        const float w = ok ? __expf(li - mref) : 0.0f;
+        if (!ok) v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        acc.x = fmaf(w, v.x, acc.x);
+        acc.y = fmaf(w, v.y, acc.y);
+        acc.z = fmaf(w, v.z, acc.z);
+        acc.w = fmaf(w, v.w, acc.w);
+        wsum += w;
+    };
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) add(slice + k * S, lv[k], ov[k]);
+    for (int i = slice + kPre * S; i < np; i += S) add(i, lse_row[i], o_row[(int64_t)i * DQ + q]);
+    // every thread of a slice holds the slice's weight sum: count it once
+    const float W = block_sum(q == 0 ? wsum : 0.0f, red);
     part[tid] = acc;
     __syncthreads();
     if (slice == 0) {
@@ -99,8 +117,10 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(ReduceParams p)
         const float r[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
         const int64_t o0 = rowid * p.D + 4 * q;
         if (p.out_bf16) {
-            uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + o0;
-            for (int e = 0; e < 4; ++e) dst[e] = f32_to_bf16(r[e]);
+            uint2 packed;
+            packed.x = (uint32_t)f32_to_bf16(r[0]) | ((uint32_t)f32_to_bf16(r[1]) << 16);
+            packed.y = (uint32_t)f32_to_bf16(r[2]) | ((uint32_t)f32_to_bf16(r[3]) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + o0) = packed;
         } else {
             *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + o0) = make_float4(r[0], r[1], r[2], r[3]);
         }

@@ -129,6 +129,9 @@ def test_reduce_rejects_bad_arguments(lib):
     assert lib.pa_decode_splitk_reduce(A, 0, 512, 1, 1, 8, 128, A, A, 0, None, None) == -2
     assert lib.pa_decode_splitk_reduce(A, 4, 100, 1, 1, 8, 128, A, A, 0, None, None) == -2
     assert lib.pa_decode_splitk_reduce(A, 4, 512, 1, 1, 8, 100, A, A, 0, None, None) == -4
+    odd = ctypes.c_void_p(0x1008)
+    assert lib.pa_decode_splitk_reduce(odd, 4, 512, 1, 1, 8, 128, A, A, 0, None, None) == -7
+    assert lib.pa_decode_splitk_reduce(A, 4, 512, 1, 1, 8, 128, A, odd, 0, None, None) == -7
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
