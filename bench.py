@@ -124,9 +124,15 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, copy_bytes
     algo = algorithmic_bytes(generate(spec))["total"]
     lines = [
         "# HBM traffic of %s on %s" % (kname, workload), "",
-        "Counters from two rocprofv3 runs (FETCH_SIZE, then WRITE_SIZE) of",
-        "`bench.py --workload %s --steps 5 --warmup 1 --no-cpu-baseline --copy-calibration-mb %d`." % (
-            workload, copy_bytes >> 20), "",
+        "Counters from two rocprofv3 runs (one MI355X, repository root as the working directory):", "",
+    ] + [
+        "    rocprofv3 --pmc %s --output-format csv -d gpurun_out/pmc_%s -o run -- python -u bench.py "
+        "--workload %s --steps 5 --warmup 1 --no-cpu-baseline --copy-calibration-mb %d" % (
+            c, c.split("_")[0].lower(), workload, copy_bytes >> 20) for c in ("FETCH_SIZE", "WRITE_SIZE")
+    ] + [
+        "",
+        "Both counters are KiB per dispatch; each is scaled by what it reads for a plain device copy of",
+        "%d MiB made in the same run (the largest copy dispatch)." % (copy_bytes >> 20), "",
         "| quantity | value |", "|---|---|",
         "| copy kernel (%d MiB) FETCH_SIZE / WRITE_SIZE, KiB | %.1f / %.1f |" % (copy_bytes >> 20, copy_f, copy_w),
         "| scale factors (bytes per counted byte), read / write | %.4f / %.4f |" % (ff, fw),
@@ -138,6 +144,57 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, copy_bytes
         "hbm_bytes_per_launch: %d" % (read_b + write_b),
         "kernel_source_digest: %s" % kernel_source_digest(spec.cache_dtype), "",
     ]
+    return "\n".join(lines)
+
+
+def summarize_trace(trace_csv: str, workload: str, command: str, tail_cold: int = 20) -> str:
+    """Markdown summary of a rocprofv3 --kernel-trace CSV of one bench.py run.
+
+    Per kernel: dispatch count and mean / median / min / max duration. The last
+    tail_cold dispatches of each library kernel are the bench's cache-flushed
+    side steps; the decode kernel is also summarised without them (the
+    launches the bench's roofline figure covers).
+    """
+    import csv
+    import collections
+
+    dur = collections.defaultdict(list)
+    for r in sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"])):
+        dur[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    total = sum(sum(v) for v in dur.values())
+
+    def short(k):
+        if k.startswith("void pa::") or k.startswith("pa::"):
+            return k.replace("void ", "").split("(")[0]
+        if "copyBuffer" in k:
+            return "device copy (bench set-up)"
+        return "torch kernel (bench set-up, cache flush): " + k.split("<")[0].replace("void ", "")[:48]
+
+    spec_kernel = DECODE_SOURCES[__import__("workloads").SPECS[workload].cache_dtype][0]
+    lines = [
+        "# Kernel durations of bench.py on %s" % workload, "",
+        "Command (one MI355X, repository root as the working directory):", "",
+        "    " + command, "",
+        "Durations in microseconds from `%s` (kernel begin/end timestamps)." % os.path.basename(trace_csv), "",
+        "| kernel | dispatches | mean | median | min | max | share of GPU time |",
+        "|---|---:|---:|---:|---:|---:|---:|",
+    ]
+    for k, v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
+        a = np.array(v)
+        lines.append("| %s | %d | %.2f | %.2f | %.2f | %.2f | %.1f%% |" % (
+            short(k), len(a), a.mean(), np.median(a), a.min(), a.max(), 100.0 * a.sum() / total))
+    dk = [k for k in dur if spec_kernel in k]
+    if len(dk) == 1 and len(dur[dk[0]]) > tail_cold:
+        a = np.array(dur[dk[0]][:-tail_cold])
+        lines += [
+            "",
+            "Without its last %d dispatches (the cache-flushed side steps), %s: %d dispatches, mean %.2f, "
+            "median %.2f, min %.2f, max %.2f." % (tail_cold, short(dk[0]), len(a), a.mean(), np.median(a),
+                                                  a.min(), a.max()),
+            "",
+            "decode_mean_us_warm: %.2f" % a.mean(),
+        ]
+    lines.append("")
     return "\n".join(lines)
 
 
@@ -188,8 +245,14 @@ def main():
                          "traffic for scaling rocprofv3's FETCH_SIZE/WRITE_SIZE counters)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the HBM-traffic summary of two rocprofv3 --pmc counter CSVs and exit")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "COMMAND"),
+                    help="print the kernel-duration summary of a rocprofv3 --kernel-trace CSV made by COMMAND "
+                         "and exit")
     args = ap.parse_args()
 
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace[0], args.workload, args.summarize_trace[1]))
+        return
     if args.summarize_counters:
         print(summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.workload,
                                  (args.copy_calibration_mb or 512) << 20))

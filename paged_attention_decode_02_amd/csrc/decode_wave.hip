@@ -42,6 +42,8 @@
 // Loads are ping-ponged: the V block is requested before the QK of the same
 // block, the next K block before the PV, so one half-block is always in
 // flight per wave.
+#include <type_traits>
+
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -356,7 +358,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     };
     if (jw < jend) load_k(phys);
 
-    for (int j = jw; j < jend; j += kWaves) {
+    // one block of the wave; MORE: a later block follows, whose keys are
+    // requested during this one (the last block is peeled off, so no load is
+    // ever issued under a branch and none reads past the partition)
+    auto block = [&](int j, auto more) {
+        constexpr bool MORE = decltype(more)::value;
         const int pos0 = j * kBlockSize;
         // int8 scales of the lane's token first: a load issued after the
         // prefetches would make its wait drain them (in-order counting)
@@ -366,7 +372,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
             vscale_raw = p.v_scale[(phys * kBlockSize + my_tok) * p.Hkv + g];
         }
         load_v(phys);
-        const int64_t phys_next = (j + kWaves < jend) ? (int64_t)table[j + kWaves] : phys;
+        int64_t phys_next = phys;
+        if constexpr (MORE) phys_next = (int64_t)table[j + kWaves];
 
         // ---------------------------------------------------------------- QK
         float ps[4][GT];
@@ -396,10 +403,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
                 ps[s][h] = acc;
             }
         }
-        // next block's keys go out now; they are not needed before the next QK.
-        // Unconditional (the last iteration re-reads its own block): a load
-        // under a branch makes the wait counts after the join conservative.
-        load_k(phys_next);
+        // next block's keys go out now; they are not needed before the next QK
+        if constexpr (MORE) load_k(phys_next);
 
         // transposed reduction across the row
 #pragma unroll
@@ -556,7 +561,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
         }
         wave_lds_sync();
         phys = phys_next;
-    }
+    };
+    int j = jw;
+    for (; j + kWaves < jend; j += kWaves) block(j, std::true_type{});
+    if (j < jend) block(j, std::false_type{});
 
     // ------------------------------------------------------------ epilogue
     // lane groups of the PV layout hold disjoint token subsets: add them
