@@ -31,6 +31,7 @@
 // are f16; the code bias is removed once per row. Softmax: log2 units against a
 // per-row reference raised only when beaten by 2^8.
 #include <type_traits>
+#include <utility>
 
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
@@ -48,6 +49,7 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 constexpr int kW = 4;  // waves per workgroup
+constexpr int S = 3;   // K/V blocks in flight per wave (register ring depth)
 constexpr uint32_t kMagic = 0x64646464u;
 constexpr float kCodeBias = 1152.0f;  // 1024 + 128
 
@@ -100,6 +102,16 @@ __device__ __forceinline__ uint32_t quad_transpose8(uint32_t w, int i) {
 template <int I>
 using ic = std::integral_constant<int, I>;
 
+// f(ic<0>{}), f(ic<1>{}), ..., f(ic<N-1>{})
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(ic<I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 }  // namespace
 
 template <int KVT, int D, int NT, int QS>
@@ -109,14 +121,22 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     constexpr bool I8 = KVT == KV_I8;
     constexpr int E = Elt<KVT>::bytes;
     constexpr int KS = D / 32;                 // k-steps of the score product
-    constexpr int KSW = (KS + kW - 1) / kW;    // k-steps each wave stages
     constexpr int DW = D / kW;                 // output dims per wave
     constexpr int NDT = DW / 16;               // 16-wide output tiles per wave
     constexpr int NQ = QS == 2 ? 2 : 1;        // query parts (hi, lo) for fp32 queries
-    constexpr int KQB = 8 * E;                 // key bytes per lane per k-step
     constexpr int VB = 4 * E;                  // value bytes per lane per output tile
+    // Global loads: wave w moves rows 4w .. 4w+3 of a block's K and V tiles,
+    // as runs of whole rows (RB bytes each), GB bytes per lane and load
+    constexpr int RB = D * E;                        // bytes of one cache row
+    constexpr int GB = RB / 16 >= 16 ? 16 : RB / 16;  // bytes per lane per load
+    constexpr int NL = RB / 16 / GB;                 // loads per lane per tile
+    // LDS tiles, row-major; keys as 16-bit elements (int8 codes widened to
+    // f16), values as stored; the row pads spread the operand reads over banks
+    constexpr int KRS = 2 * D + 16;  // bytes per staged key row
+    constexpr int VRS = RB + 32;     // bytes per staged value row
 
-    __shared__ __align__(16) u32x4 kst[2][KS][64];  // staged keys (A operands)
+    __shared__ __align__(16) unsigned char kst[2][kBlockSize][KRS];  // staged keys
+    __shared__ __align__(16) unsigned char vst[2][kBlockSize][VRS];  // staged values
     __shared__ __align__(16) u32x2 pst[2][NT][64];  // probabilities (A operands of PV)
     __shared__ float ast[2][NT][16];                // per-row rescale factors
     __shared__ int araise[2][NT];                   // whether a tile's rows were rescaled
@@ -246,7 +266,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (int64_t)g * D * E;
     const char* vbase = reinterpret_cast<const char*>(p.v_cache) + (int64_t)g * D * E;
     const int j0 = start / kBlockSize, jend = (end + kBlockSize - 1) / kBlockSize;
-    // physical block of logical block j; past the end the last one (re-read)
+    // physical block of logical block j (clamped to the partition)
     auto phys_of = [&](int j) -> int64_t { return (int64_t)table[j < jend ? j : jend - 1]; };
     // Inside the block loop the table entries go through the vector memory
     // path (the workgroup barrier's fences keep the compiler from scalar
@@ -273,21 +293,26 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     }
 
     // ---------------------------------------------------------- pipeline
-    // this wave's quarter of a future K tile, plus (int8) the block's scales for
-    // the lane's four tokens, all loaded together two blocks ahead: a load
-    // issued later would make its wait drain the prefetches (in-order counting)
-    struct KQ {
-        Raw<KQB> k[KSW];
+    // Register ring of S blocks: block j (this wave's rows of the K and V
+    // tiles, plus (int8) the scales of the lane's four score tokens, all
+    // requested together: a load issued later would make its wait drain the
+    // prefetches) lives in slot (j - j0) % S. Iteration j stages K(j + 1) and
+    // V(j) in LDS and then requests block j + S into V(j)'s slot.
+    struct Blk {
+        Raw<GB> k[NL], v[NL];
         float ks[4], vs[4];
     };
-    KQ kq[2];
-    Raw<VB> vq[2][NDT];  // this wave's V slice of a current/future block
-    auto load_kq = [&](KQ& dst, int64_t ph) {
-        const char* base = kbase + (ph * kBlockSize + l16) * tok_stride + 8 * lg * E;
+    Blk ring[S];
+    // lane's share of a tile: load i covers bytes x = (i * 64 + lane) * GB of
+    // the wave's four rows, i.e. row 4 * wv + x / RB, byte x % RB
+    auto row_of = [&](int i) { return 4 * wv + ((i * 64 + lane) * GB) / RB; };
+    auto col_of = [&](int i) { return ((i * 64 + lane) * GB) % RB; };
+    auto load_blk = [&](Blk& dst, int64_t ph) {
 #pragma unroll
-        for (int i = 0; i < KSW; ++i) {
-            const int ks = wv * KSW + i;
-            if (KS % kW == 0 || ks < KS) load_raw<KQB, true>(dst.k[i], base + 32 * ks * E);
+        for (int i = 0; i < NL; ++i) {
+            const int64_t off = (ph * kBlockSize + row_of(i)) * tok_stride + col_of(i);
+            load_raw<GB, true>(dst.k[i], kbase + off);
+            load_raw<GB, true>(dst.v[i], vbase + off);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -299,29 +324,52 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
             }
         }
     };
-    auto store_kq = [&](const KQ& src, int stage) {
+    auto store_k = [&](const Blk& src, int stage) {
 #pragma unroll
-        for (int i = 0; i < KSW; ++i) {
-            const int ks = wv * KSW + i;
-            if (KS % kW == 0 || ks < KS) {
-                u32x4 a;
-                if constexpr (I8) {
-                    const uint32_t u0 = src.k[i].w[0] ^ 0x80808080u, u1 = src.k[i].w[1] ^ 0x80808080u;
-                    a = u32x4{f16pair_lo(u0), f16pair_hi(u0), f16pair_lo(u1), f16pair_hi(u1)};
-                } else {
-                    a = u32x4{src.k[i].w[0], src.k[i].w[1], src.k[i].w[2], src.k[i].w[3]};
+        for (int i = 0; i < NL; ++i) {
+            unsigned char* dst = &kst[stage][row_of(i)][col_of(i) * (2 / E)];
+            if constexpr (I8) {
+                // codes c -> f16 (1024 + c + 128), two output bytes per code
+                uint32_t f[GB / 2];
+#pragma unroll
+                for (int w = 0; w < GB / 4; ++w) {
+                    const uint32_t u = src.k[i].w[w] ^ 0x80808080u;
+                    f[2 * w] = f16pair_lo(u);
+                    f[2 * w + 1] = f16pair_hi(u);
                 }
-                kst[stage][ks][lane] = a;
+                if constexpr (GB == 16) {
+                    reinterpret_cast<u32x4*>(dst)[0] = u32x4{f[0], f[1], f[2], f[3]};
+                    reinterpret_cast<u32x4*>(dst)[1] = u32x4{f[4], f[5], f[6], f[7]};
+                } else if constexpr (GB == 8) {
+                    *reinterpret_cast<u32x4*>(dst) = u32x4{f[0], f[1], f[2], f[3]};
+                } else {
+                    *reinterpret_cast<u32x2*>(dst) = u32x2{f[0], f[1]};
+                }
+            } else {
+                if constexpr (GB == 16)
+                    *reinterpret_cast<u32x4*>(dst) = u32x4{src.k[i].w[0], src.k[i].w[1], src.k[i].w[2], src.k[i].w[3]};
+                else if constexpr (GB == 8)
+                    *reinterpret_cast<u32x2*>(dst) = u32x2{src.k[i].w[0], src.k[i].w[1]};
+                else
+                    *reinterpret_cast<uint32_t*>(dst) = src.k[i].w[0];
             }
         }
     };
-    const int vtok = 4 * lg + (l16 & 3);  // token this lane loads for the V transpose
-    const int vdim = wv * DW + 4 * (l16 >> 2);
-    auto load_vq = [&](Raw<VB>* dst, int64_t ph) {
-        const char* base = vbase + (ph * kBlockSize + vtok) * tok_stride + vdim * E;
+    auto store_v = [&](const Blk& src, int stage) {
 #pragma unroll
-        for (int nd = 0; nd < NDT; ++nd) load_raw<VB, true>(dst[nd], base + 16 * nd * E);
+        for (int i = 0; i < NL; ++i) {
+            unsigned char* dst = &vst[stage][row_of(i)][col_of(i)];
+            if constexpr (GB == 16)
+                *reinterpret_cast<u32x4*>(dst) = u32x4{src.v[i].w[0], src.v[i].w[1], src.v[i].w[2], src.v[i].w[3]};
+            else if constexpr (GB == 8)
+                *reinterpret_cast<u32x2*>(dst) = u32x2{src.v[i].w[0], src.v[i].w[1]};
+            else
+                *reinterpret_cast<uint32_t*>(dst) = src.v[i].w[0];
+        }
     };
+    // V operand source of this lane: token vtok, VB bytes at dims vdim + 16 nd
+    const int vtok = 4 * lg + (l16 & 3);
+    const int vdim = wv * DW + 4 * (l16 >> 2);
 
     // scores, softmax and probabilities of block j into LDS stage j % 2 (owners only)
     auto scores = [&](int j, const float* kraw, const float* vraw) {
@@ -330,7 +378,8 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
         f32x4 s = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 a = kst[stage][ks][lane];
+            // token l16, 16-bit elements 32 ks + 8 lg .. + 7
+            const u32x4 a = *reinterpret_cast<const u32x4*>(&kst[stage][l16][(32 * ks + 8 * lg) * 2]);
 #pragma unroll
             for (int q2 = 0; q2 < NQ; ++q2) {
                 if constexpr (I8)
@@ -392,10 +441,22 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
         pst[stage][wv][lane] = pa;
     };
 
-    // PV of block j (all waves): probabilities from LDS stage j % 2, V from registers
-    auto values = [&](int j, const Raw<VB>* vsrc) {
+    // PV of block j (all waves): probabilities and values from LDS stage j % 2
+    auto values = [&](int j) {
         const int stage = j & 1;
         const int pos0 = j * kBlockSize;
+        Raw<VB> vsrc[NDT];
+#pragma unroll
+        for (int nd = 0; nd < NDT; ++nd) {
+            const unsigned char* src = &vst[stage][vtok][(vdim + 16 * nd) * E];
+            if constexpr (VB == 8) {
+                const u32x2 w = *reinterpret_cast<const u32x2*>(src);
+                vsrc[nd].w[0] = w.x;
+                vsrc[nd].w[1] = w.y;
+            } else {
+                vsrc[nd].w[0] = *reinterpret_cast<const uint32_t*>(src);
+            }
+        }
         u32x2 bop[NDT];
         const bool partial = pos0 + kBlockSize > end;  // tokens past the end may hold anything
 #pragma unroll
@@ -435,53 +496,54 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
         }
     };
 
-    // prologue: K(j0) staged, K(j0+1), K(j0+2) and V(j0), V(j0+1) in registers,
-    // scores of block j0 done
+    // prologue: blocks j0 .. j0 + S - 1 requested, K(j0) staged, scores of
+    // block j0 done. Unconditional (a partition of fewer than S blocks
+    // re-reads its last one): the loop's wait counts assume all S in flight.
     {
-        load_kq(kq[0], phys_of(j0));
-        load_kq(kq[1], phys_of(j0 + 1));
-        load_vq(vq[0], phys_of(j0));
-        load_vq(vq[1], phys_of(j0 + 1));
+#pragma unroll
+        for (int x = 0; x < S; ++x) load_blk(ring[x], phys_of(j0 + x));
         float kraw[4], vraw[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            kraw[i] = kq[0].ks[i];
-            vraw[i] = kq[0].vs[i];
+            kraw[i] = ring[0].ks[i];
+            vraw[i] = ring[0].vs[i];
         }
-        store_kq(kq[0], j0 & 1);
-        load_kq(kq[0], phys_of(j0 + 2));
+        store_k(ring[0], j0 & 1);
         __syncthreads();
         if (owner) scores(j0, kraw, vraw);
     }
-    int64_t ph2 = phys_of(j0 + 2);  // physical blocks of j+2 and j+3 at iteration j
-    int t3 = (int)phys_of(j0 + 3);
-    // iteration j: stage K(j+1), barrier, scores of j+1, PV of j.
-    // kq[(j - j0 + 1) & 1] holds K(j+1), vq[(j - j0) & 1] holds V(j).
-    auto iter = [&](int j, auto xc) {
-        constexpr int X = decltype(xc)::value;  // (j - j0) & 1
-        const int t4 = table[j + 4 < jend ? j + 4 : jend - 1];
+    int tp = (int)phys_of(j0 + S);  // physical block of j + S at iteration j, not yet uniform
+    // iteration j: stage K(j+1) and V(j), barrier, scores of j+1, PV of j.
+    // FULL: every block this iteration requests lies inside the partition.
+    auto iter = [&](int j, auto xc, auto full) __attribute__((always_inline)) {
+        constexpr int X = decltype(xc)::value;  // slot of block j: (j - j0) % S
+        constexpr int Y = (X + 1) % S;          // slot of block j + 1
+        constexpr bool FULL = decltype(full)::value;
+        const int tnext = table[j + 1 + S < jend ? j + 1 + S : jend - 1];
         float kraw[4], vraw[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            kraw[i] = kq[1 - X].ks[i];
-            vraw[i] = kq[1 - X].vs[i];
+            kraw[i] = ring[Y].ks[i];
+            vraw[i] = ring[Y].vs[i];
         }
-        store_kq(kq[1 - X], (j + 1) & 1);
-        const int64_t ph3 = __builtin_amdgcn_readfirstlane(t3);
-        load_kq(kq[1 - X], ph3);
+        if (FULL || j + 1 < jend) store_k(ring[Y], (j + 1) & 1);
+        store_v(ring[X], j & 1);
+        const int64_t ph = __builtin_amdgcn_readfirstlane(tp);
+        if (FULL || j + S < jend) load_blk(ring[X], ph);
         __syncthreads();
-        if (owner && j + 1 < jend) scores(j + 1, kraw, vraw);
-        values(j, vq[X]);
-        load_vq(vq[X], ph2);
-        ph2 = ph3;
-        t3 = t4;
+        if (owner && (FULL || j + 1 < jend)) scores(j + 1, kraw, vraw);
+        values(j);
+        tp = tnext;
+        // keep the next iteration's table wait behind this iteration's work
+        __builtin_amdgcn_sched_barrier(0);
     };
     int j = j0;
-    for (; j + 1 < jend; j += 2) {
-        iter(j, ic<0>{});
-        iter(j + 1, ic<1>{});
-    }
-    if (j < jend) iter(j, ic<0>{});
+    for (; j + 2 * S <= jend; j += S)
+        static_for<S>([&](auto xc) __attribute__((always_inline)) { iter(j + decltype(xc)::value, xc, std::true_type{}); });
+    for (; j < jend; j += S)
+        static_for<S>([&](auto xc) __attribute__((always_inline)) {
+            if (j + decltype(xc)::value < jend) iter(j + decltype(xc)::value, xc, std::false_type{});
+        });
 
     // ------------------------------------------------------------ epilogue
     if (owner) {
