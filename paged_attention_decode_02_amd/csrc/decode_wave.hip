@@ -132,18 +132,21 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     constexpr int QW = D / 32;      // q dwords (element pairs) per head per lane
     constexpr int NI = Split<GT>::kItems;
     constexpr int GP = (GT + 3) / 4 * 4;  // padded heads per token in the LDS p buffer
-    // PV layout: LPT lanes per value row (each >= 4 bytes), TPW rows per wave step
+    // PV layout: a lane takes VB bytes of a value row per token, LPT lanes per
+    // row, TPW rows per wave step. 512-byte rows with up to 6 heads use 16-byte
+    // loads (measured faster there; more heads would not fit their outputs in
+    // registers), everything else one row per wave (at least 4 bytes a lane).
     constexpr int RB = D * E;  // row bytes
-    constexpr int LPT = RB / 4 >= 64 ? 64 : RB / 4;
+    constexpr int VB = (RB >= 512 && GT <= 6) ? 16 : (RB / 64 > 4 ? RB / 64 : 4);  // value bytes per lane per token
+    constexpr int LPT = RB / VB;
     constexpr int TPW = 64 / LPT;
-    constexpr int VB = RB / LPT;  // value bytes per lane per token
     constexpr int EV = VB / E;    // value elements per lane per token
     constexpr int STEPS = kBlockSize / TPW;
     static_assert(KB >= 4 && VB >= 4, "layout");
     static_assert(STEPS % 2 == 0, "PV pairs tokens");
 
     __shared__ __align__(16) uint32_t pbuf_all[kWaves][kBlockSize / 2 * GP];
-    __shared__ __align__(16) float merge_o[kWaves][GT][64 * EV];
+    __shared__ __align__(16) float merge_o[kWaves][GT][D];
     __shared__ float merge_ml[kWaves][3][GT];  // m, l, sum of the 16-bit weights
 
     // the wave index is uniform across the wave: saying so keeps the block
@@ -159,6 +162,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     const int sx = 2 * ca + cb;      // slot swap pattern of this lane
     const int my_tok = 4 * sx + r;   // token (within a block) of the items this lane owns
     const int vgrp = lane / LPT, vl = lane % LPT;  // PV layout
+    // token of wave step st for this lane: steps 2k and 2k + 1 take adjacent
+    // tokens (one 16-bit weight pair in LDS), the TPW lane groups interleave
+    auto tok_of = [&](int st) { return 2 * TPW * (st >> 1) + 2 * vgrp + (st & 1); };
 
     int wg = blockIdx.x;
     const int part = wg % p.NP;
@@ -354,7 +360,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     auto load_v = [&](int64_t ph) {
         const char* base = vbase + ph * kBlockSize * tok_stride + vl * VB;
 #pragma unroll
-        for (int st = 0; st < STEPS; ++st) load_raw<VB, true>(vr[st], base + (st * TPW + vgrp) * tok_stride);
+        for (int st = 0; st < STEPS; ++st) load_raw<VB, true>(vr[st], base + tok_of(st) * tok_stride);
     };
     if (jw < jend) load_k(phys);
 
@@ -504,7 +510,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
             if (pos0 + kBlockSize > end) {
 #pragma unroll
                 for (int st = 0; st < STEPS; ++st) {
-                    const bool ok = pos0 + st * TPW + vgrp < end;
+                    const bool ok = pos0 + tok_of(st) < end;
 #pragma unroll
                     for (int w = 0; w < VB / 4; ++w) vr[st].w[w] = ok ? vr[st].w[w] : 0u;
                 }
@@ -512,24 +518,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
         }
 #pragma unroll
         for (int st = 0; st < STEPS; st += 2) {
-            // token pair (tk, tk + TPW) against 16-bit weight pairs: the LDS
-            // pairs are tokens (2k, 2k + 1), so with TPW > 1 the lane's two
-            // tokens are read separately
-            const int tk = st * TPW + vgrp;
+            // token pair (tk, tk + 1) against a 16-bit weight pair from LDS
+            const int tk = tok_of(st);
             uint32_t pp[GT];
-            if constexpr (TPW == 1) {
 #pragma unroll
-                for (int h = 0; h < GT; ++h) pp[h] = pbuf_u[(tk >> 1) * GP + h];
-            } else {
-                const uint16_t* ph = reinterpret_cast<const uint16_t*>(pbuf_u);
-                const int t1 = tk + TPW;
-#pragma unroll
-                for (int h = 0; h < GT; ++h) {
-                    const uint32_t lo = ph[((tk >> 1) * GP + h) * 2 + (tk & 1)];
-                    const uint32_t hi = ph[((t1 >> 1) * GP + h) * 2 + (t1 & 1)];
-                    pp[h] = lo | (hi << 16);
-                }
-            }
+            for (int h = 0; h < GT; ++h) pp[h] = pbuf_u[(tk >> 1) * GP + h];
 #pragma unroll
             for (int w = 0; w < VB / 4; ++w) {
                 const uint32_t A = vr[st].w[w];
@@ -548,7 +541,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
                         o[h][4 * w + 3] = dot2_f16(pp[h], f3, o[h][4 * w + 3]);
                     }
                 } else {
-                    // bf16 pairs (element e of token tk, element e of token tk + TPW)
+                    // bf16 pairs (element e of token tk, element e of token tk + 1)
                     const uint32_t e0 = __builtin_amdgcn_perm(B, A, 0x05040100u);
                     const uint32_t e1 = __builtin_amdgcn_perm(B, A, 0x07060302u);
 #pragma unroll
