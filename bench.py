@@ -208,25 +208,27 @@ def run_cpu_baseline(w, bytes_per_step: int, budget_s: float) -> dict:
     oracle.cache_write(w.k_src, w.v_src, w.slot_mapping, k, v, ks, vs)
     log("cpu baseline: oracle cache built in %.1f s" % (time.time() - t0))
     rows_total = sp.B * sp.Tq * sp.Hq
-    # rows of sequence-major order, in chunks, until the time budget is used
-    order = np.arange(rows_total, dtype=np.int64)
+    # (b, t, h) rows in sequence-major order, in chunks of one row per thread,
+    # cycling over the step until the time budget is used (at least one chunk)
     threads = oracle.max_threads()
     chunk = max(1, min(rows_total, threads))
-    done, spent = 0, 0.0
-    while done < rows_total and spent < budget_s:
-        rows = order[done: done + chunk]
+    done, spent, next_log = 0, 0.0, 1.0
+    q = w.q_array()
+    while spent < budget_s:
+        rows = (np.arange(chunk, dtype=np.int64) + done) % rows_total
         t = time.perf_counter()
-        oracle.decode(w.q_array(), k, v, w.block_table, w.seq_lens, w.softmax_scale, ks, vs, rows=rows,
-                      nthreads=threads)
+        oracle.decode(q, k, v, w.block_table, w.seq_lens, w.softmax_scale, ks, vs, rows=rows, nthreads=threads)
         spent += time.perf_counter() - t
         done += rows.size
-        log("cpu baseline: %d/%d rows, %.1f s" % (done, rows_total, spent))
-    # rows of one sequence all cost the same here; scale the sample to a step
+        if spent >= next_log:
+            log("cpu baseline: %d rows (%.2f steps), %.1f s" % (done, done / rows_total, spent))
+            next_log = spent + 1.0
+    # the sample covers whole sequences' rows in proportion; scale it to one step
     step_s = spent * rows_total / done
     return {"value": round(bytes_per_step / step_s / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle", "ms_per_step": round(step_s * 1e3, 3),
-            "sample": "%d of %d (b,t,h) rows of %s, fp64 oracle, %d OpenMP threads, scaled to one step"
-                      % (done, rows_total, sp.name, threads)}
+            "sample": "%d (b,t,h) rows of %s (%.2f steps of %d rows) in %.1f s, fp64 oracle, %d OpenMP threads, "
+                      "scaled to one step" % (done, sp.name, done / rows_total, rows_total, spent, threads)}
 
 
 def main():
