@@ -138,7 +138,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     __shared__ __align__(16) unsigned char kst[2][kBlockSize][KRS];  // staged keys
     __shared__ __align__(16) unsigned char vst[2][kBlockSize][VRS];  // staged values
     __shared__ __align__(16) u32x2 pst[2][NT][64];  // probabilities (A operands of PV)
-    __shared__ float ast[2][NT][16];                // per-row rescale factors
+    __shared__ __align__(16) float ast[2][NT][16];  // per-row rescale factors
     __shared__ int araise[2][NT];                   // whether a tile's rows were rescaled
     __shared__ float fin[2][NT][16];                // epilogue: 1/l and code bias per row
     __shared__ float red[kW];
@@ -375,21 +375,26 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     auto scores = [&](int j, const float* kraw, const float* vraw) {
         const int stage = j & 1;
         const int pos0 = j * kBlockSize;
-        f32x4 s = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        // all K operands requested at once (token l16, 16-bit elements
+        // 32 ks + 8 lg .. + 7), then two independent accumulation chains
+        u32x4 a[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) a[ks] = *reinterpret_cast<const u32x4*>(&kst[stage][l16][(32 * ks + 8 * lg) * 2]);
+        f32x4 s2[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            // token l16, 16-bit elements 32 ks + 8 lg .. + 7
-            const u32x4 a = *reinterpret_cast<const u32x4*>(&kst[stage][l16][(32 * ks + 8 * lg) * 2]);
 #pragma unroll
             for (int q2 = 0; q2 < NQ; ++q2) {
+                f32x4& acc = s2[ks & 1];
                 if constexpr (I8)
-                    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                               __builtin_bit_cast(f16x8, qreg[q2][ks]), s, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a[ks]),
+                                                                 __builtin_bit_cast(f16x8, qreg[q2][ks]), acc, 0, 0, 0);
                 else
-                    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                __builtin_bit_cast(bf16x8, qreg[q2][ks]), s, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[ks]),
+                                                                  __builtin_bit_cast(bf16x8, qreg[q2][ks]), acc, 0, 0, 0);
             }
         }
+        const f32x4 s = s2[0] + s2[1];
         float sc[4];
         bool raise = false;
 #pragma unroll
@@ -474,16 +479,23 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
                 bop[nd] = w;
             }
         }
+        // every tile's flag, factors and weights requested at once
+        int rz[NT];
+        f32x4 a4[NT];
+        u32x2 pw[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            if (araise[stage][t]) {
-                f32x4 a4;
+            rz[t] = araise[stage][t];
+            a4[t] = *reinterpret_cast<const f32x4*>(&ast[stage][t][4 * lg]);
+            pw[t] = pst[stage][t][lane];
+        }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) a4[i] = ast[stage][t][4 * lg + i];
+        for (int t = 0; t < NT; ++t) {
+            if (rz[t]) {
 #pragma unroll
-                for (int nd = 0; nd < NDT; ++nd) o[t][nd] *= a4;
+                for (int nd = 0; nd < NDT; ++nd) o[t][nd] *= a4[t];
             }
-            const u32x2 pa = pst[stage][t][lane];
+            const u32x2 pa = pw[t];
 #pragma unroll
             for (int nd = 0; nd < NDT; ++nd) {
                 if constexpr (I8)
