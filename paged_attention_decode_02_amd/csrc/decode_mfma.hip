@@ -423,7 +423,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
         float pr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            pr[i] = sc[i] == -INFINITY ? 0.0f : exp2f(sc[i] - base);
+            pr[i] = exp2_weight(sc[i] - base);  // sc = -inf gives 0
             lpart += pr[i];
         }
         u32x2 pa;
@@ -437,7 +437,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
             }
             pa = u32x2{pack_f16x2(ph2[0], ph2[1]), pack_f16x2(ph2[2], ph2[3])};
         } else {
-            pa = u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+            pa = u32x2{pack_bf16_rne(pr[0], pr[1]), pack_bf16_rne(pr[2], pr[3])};
             // sum of the rounded weights: the output is normalised by it, so it
             // stays a convex combination of value rows (l keeps the exact ones)
             spart += bf16_to_f32((uint16_t)pa.x) + bf16_to_f32((uint16_t)(pa.x >> 16)) +

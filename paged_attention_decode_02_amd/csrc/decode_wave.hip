@@ -482,7 +482,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
 #pragma unroll
         for (int j2 = 0; j2 < NI; ++j2) {
             const float base = mloc[j2] == -INFINITY ? 0.0f : mloc[j2];
-            const float pr = sc[j2] == -INFINITY ? 0.0f : exp2f(sc[j2] - base);
+            const float pr = exp2_weight(sc[j2] - base);  // sc = -inf gives 0
             uint16_t* slot16 = reinterpret_cast<uint16_t*>(pbuf_u) + ((my_tok >> 1) * GP + ihead[j2]) * 2 + (my_tok & 1);
             if constexpr (I8) {
                 lloc[j2] += pr;
@@ -490,12 +490,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
                 sloc[j2] += (float)ph;
                 *slot16 = __builtin_bit_cast(uint16_t, ph);
             } else {
-                // bf16 weight (pr is finite and >= 0: plain round to nearest
-                // even). l keeps the exact weights (for the LSE); the output is
-                // normalised by the sum of the rounded ones, so it stays a
-                // convex combination of value rows
-                const uint32_t u = __float_as_uint(pr);
-                const uint32_t pb = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+                // bf16 weight (round to nearest even). l keeps the exact
+                // weights (for the LSE); the output is normalised by the sum
+                // of the rounded ones, so it stays a convex combination of
+                // value rows
+                const uint32_t pb = pack_bf16_rne(pr, 0.0f) & 0xFFFFu;
                 lloc[j2] += pr;
                 sloc[j2] += __uint_as_float(pb << 16);
                 *slot16 = (uint16_t)pb;

@@ -135,4 +135,17 @@ __device__ __forceinline__ float exp2_guarded(float x) {  // exp2 with exp2(-inf
     return x == -INFINITY ? 0.0f : exp2f(x);
 }
 
+// Softmax weight 2^x for x <= 8 (log2 units against the running reference):
+// the hardware v_exp_f32 (1 ulp; 2^-inf = 0; results below 2^-126 are
+// negligible against the reference's weight 1).
+__device__ __forceinline__ float exp2_weight(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Two finite floats -> packed bf16 pair (round to nearest even), one
+// v_cvt_pk_bf16_f32 on gfx950; a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
+    typedef __attribute__((ext_vector_type(2))) float f2;
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf2;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, bf2));
+}
+
 }  // namespace pa
