@@ -11,21 +11,20 @@
 // sequence b and up to 16*NT rows r = t*G + h' (query token t, head g*G + h');
 // row r sees keys 0 .. L_b - Tq + t (causal inside the Tq new tokens).
 // Per 16-token KV block:
-//  - the K tile is staged once in LDS (each wave loads a quarter of it, two
-//    blocks ahead, into registers and stores it one block ahead), laid out as
-//    the A operand of S^T = K Q^T (v_mfma_f32_16x16x32 bf16 / f16);
-//  - wave w < NT owns row tile w: its queries stay in registers as B
-//    operands, it computes S^T for its 16 rows, runs the softmax and writes
-//    the probabilities to LDS. The S^T result layout (lane l: tokens
-//    4*(l/16)+i of row l%16) is exactly the A-operand layout of the PV
-//    product, so no shuffle is needed;
+//  - each wave moves 4 rows of the block's K and V tiles (16-byte loads of
+//    whole-row runs) through a 3-block register ring into row-major LDS tiles
+//    (double-buffered, rows padded against bank conflicts);
+//  - wave w < NT owns row tile w: its queries stay in registers as the B
+//    operands of S^T = K Q^T (v_mfma_f32_16x16x32 bf16 / f16, K operands read
+//    from LDS), it runs the softmax and writes 16-bit weights to LDS. The S^T
+//    result layout (lane l: tokens 4*(l/16)+i of row l%16) is exactly the
+//    A-operand layout of the PV product, so no shuffle is needed;
 //  - every wave accumulates O[row][d] += P[row][token] V[token][d]
-//    (v_mfma_f32_16x16x16 bf16 / f16) for its quarter of the output dims,
-//    with its V slice loaded straight into registers and regrouped by a 4x4
-//    transpose inside each lane quad (DPP + byte permutes).
-// The scores of block j+1 are computed while the PV of block j runs, so one
-// workgroup barrier per block covers both the staged keys and the
-// probabilities (double-buffered in LDS).
+//    (v_mfma_f32_16x16x16 bf16 / f16) for its quarter of the output dims; the
+//    V operand (4 tokens of one dim per lane) comes from the transposing LDS
+//    read of gfx950 (bf16) or a byte transpose inside each lane quad (int8).
+// The scores of block j+1 and the PV of block j share one iteration, so one
+// workgroup barrier per block covers the staged tiles and the weights.
 // int8 caches: codes become f16 (1024 + code + 128) by a byte permute, queries
 // are scaled into f16 by a power of two, probabilities times the value scale
 // are f16; the code bias is removed once per row. Softmax: log2 units against a
@@ -72,25 +71,8 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
 __device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)w); }
 __device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
-// 4x4 transpose of 16-bit elements inside a lane quad. Lane i (= lane & 3)
-// holds elements (i, 0..3) of a 4x4 tile as two dwords; afterwards lane j
-// holds elements (0..3, j).
-__device__ __forceinline__ u32x2 quad_transpose16(u32x2 w, int i) {
-    const int b1 = (i >> 1) & 1, b0 = i & 1;
-    const uint32_t send = b1 ? w.x : w.y;
-    const uint32_t recv = dpp_u32<kDppQuadXor2>(send);
-    const uint32_t A = b1 ? recv : w.x;
-    const uint32_t B = b1 ? w.y : recv;
-    const uint32_t pA = dpp_u32<kDppQuadXor1>(A);
-    const uint32_t pB = dpp_u32<kDppQuadXor1>(B);
-    const uint32_t sel = b0 ? 0x03020706u : 0x05040100u;
-    u32x2 r;
-    r.x = __builtin_amdgcn_perm(pA, A, sel);
-    r.y = __builtin_amdgcn_perm(pB, B, sel);
-    return r;
-}
-
-// Same for bytes: lane i holds (i, 0..3) in one dword, afterwards lane j holds (0..3, j).
+// 4x4 transpose of bytes inside a lane quad: lane i (= lane & 3) holds
+// elements (i, 0..3) in one dword, afterwards lane j holds (0..3, j).
 __device__ __forceinline__ uint32_t quad_transpose8(uint32_t w, int i) {
     const int b1 = (i >> 1) & 1, b0 = i & 1;
     const uint32_t recv = dpp_u32<kDppQuadXor2>(w);
@@ -98,6 +80,10 @@ __device__ __forceinline__ uint32_t quad_transpose8(uint32_t w, int i) {
     const uint32_t pu = dpp_u32<kDppQuadXor1>(u);
     return __builtin_amdgcn_perm(pu, u, b0 ? 0x03070105u : 0x06020400u);
 }
+
+// 4 x bf16 in LDS, the operand type of the transposing LDS read
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_gcc;
+typedef __attribute__((address_space(3))) bf16x4_gcc lds_bf16x4;
 
 template <int I>
 using ic = std::integral_constant<int, I>;
@@ -367,7 +353,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
                 *reinterpret_cast<uint32_t*>(dst) = src.v[i].w[0];
         }
     };
-    // V operand source of this lane: token vtok, VB bytes at dims vdim + 16 nd
+    // int8 V operand source of this lane: token vtok, 4 codes at dims vdim + 16 nd
     const int vtok = 4 * lg + (l16 & 3);
     const int vdim = wv * DW + 4 * (l16 >> 2);
 
@@ -450,27 +436,21 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     auto values = [&](int j) {
         const int stage = j & 1;
         const int pos0 = j * kBlockSize;
-        Raw<VB> vsrc[NDT];
-#pragma unroll
-        for (int nd = 0; nd < NDT; ++nd) {
-            const unsigned char* src = &vst[stage][vtok][(vdim + 16 * nd) * E];
-            if constexpr (VB == 8) {
-                const u32x2 w = *reinterpret_cast<const u32x2*>(src);
-                vsrc[nd].w[0] = w.x;
-                vsrc[nd].w[1] = w.y;
-            } else {
-                vsrc[nd].w[0] = *reinterpret_cast<const uint32_t*>(src);
-            }
-        }
         u32x2 bop[NDT];
         const bool partial = pos0 + kBlockSize > end;  // tokens past the end may hold anything
 #pragma unroll
         for (int nd = 0; nd < NDT; ++nd) {
             if constexpr (I8) {
-                const uint32_t tw = quad_transpose8(vsrc[nd].w[0], l16 & 3) ^ 0x80808080u;
+                // codes of token vtok, dims vdim + 16 nd .. + 3, transposed in the lane quad
+                const uint32_t raw = *reinterpret_cast<const uint32_t*>(&vst[stage][vtok][vdim + 16 * nd]);
+                const uint32_t tw = quad_transpose8(raw, l16 & 3) ^ 0x80808080u;
                 bop[nd] = u32x2{f16pair_lo(tw), f16pair_hi(tw)};
             } else {
-                u32x2 w = quad_transpose16(u32x2{vsrc[nd].w[0], vsrc[nd].w[1]}, l16 & 3);
+                // transposing LDS read: lane 4r + c of a 16-lane group names
+                // row (token) 4 lg + r, dims 4c .. 4c + 3 of the 16-dim tile;
+                // lane i receives dim i of the group's 4 tokens
+                const unsigned char* src = &vst[stage][4 * lg + (l16 >> 2)][(wv * DW + 16 * nd + 4 * (l16 & 3)) * 2];
+                u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)src));
                 if (partial) {
                     const int t0 = pos0 + 4 * lg;  // element k is token 4*lg + k
                     w.x = (t0 + 0 < end ? w.x & 0x0000FFFFu : 0u) | (t0 + 1 < end ? w.x & 0xFFFF0000u : 0u);
