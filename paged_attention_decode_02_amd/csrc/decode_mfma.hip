@@ -124,6 +124,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     __shared__ __align__(16) unsigned char kst[2][kBlockSize][KRS];  // staged keys
     __shared__ __align__(16) unsigned char vst[2][kBlockSize][VRS];  // staged values
     __shared__ __align__(16) u32x2 pst[2][NT][64];  // probabilities (A operands of PV)
+    __shared__ __align__(16) float sst[2][32];      // int8: key then value scales of a block's tokens
     __shared__ __align__(16) float ast[2][NT][16];  // per-row rescale factors
     __shared__ int araise[2][NT];                   // whether a tile's rows were rescaled
     __shared__ float fin[2][NT][16];                // epilogue: 1/l and code bias per row
@@ -280,13 +281,13 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
 
     // ---------------------------------------------------------- pipeline
     // Register ring of S blocks: block j (this wave's rows of the K and V
-    // tiles, plus (int8) the scales of the lane's four score tokens, all
-    // requested together: a load issued later would make its wait drain the
-    // prefetches) lives in slot (j - j0) % S. Iteration j stages K(j + 1) and
-    // V(j) in LDS and then requests block j + S into V(j)'s slot.
+    // tiles, plus (int8) the block's key and value scales, all requested
+    // together: a load issued later would make its wait drain the prefetches)
+    // lives in slot (j - j0) % S. Iteration j stages K(j + 1) (wave 0 also its
+    // scales) and V(j) in LDS and then requests block j + S into V(j)'s slot.
     struct Blk {
         Raw<GB> k[NL], v[NL];
-        float ks[4], vs[4];
+        float sc;  // int8: lane l < 16 the key scale, 16 <= l < 32 the value scale of token l % 16
     };
     Blk ring[S];
     // lane's share of a tile: load i covers bytes x = (i * 64 + lane) * GB of
@@ -300,14 +301,11 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
             load_raw<GB, true>(dst.k[i], kbase + off);
             load_raw<GB, true>(dst.v[i], vbase + off);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            dst.ks[i] = 1.0f;
-            dst.vs[i] = 1.0f;
-            if constexpr (I8) {
-                dst.ks[i] = p.k_scale[(ph * kBlockSize + 4 * lg + i) * p.Hkv + g];
-                dst.vs[i] = p.v_scale[(ph * kBlockSize + 4 * lg + i) * p.Hkv + g];
-            }
+        dst.sc = 1.0f;
+        if constexpr (I8) {
+            // one load for the block's 32 scales (lanes 32..63 repeat 0..31)
+            const float* src = (lane & 16) ? p.v_scale : p.k_scale;
+            dst.sc = src[(ph * kBlockSize + l16) * p.Hkv + g];
         }
     };
     auto store_k = [&](const Blk& src, int stage) {
@@ -358,9 +356,15 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     const int vdim = wv * DW + 4 * (l16 >> 2);
 
     // scores, softmax and probabilities of block j into LDS stage j % 2 (owners only)
-    auto scores = [&](int j, const float* kraw, const float* vraw) {
+    auto scores = [&](int j) {
         const int stage = j & 1;
         const int pos0 = j * kBlockSize;
+        // int8: key and value scales of the lane's 4 tokens 4 lg + i
+        f32x4 kraw = f32x4{1.0f, 1.0f, 1.0f, 1.0f}, vraw = kraw;
+        if constexpr (I8) {
+            kraw = *reinterpret_cast<const f32x4*>(&sst[stage][4 * lg]);
+            vraw = *reinterpret_cast<const f32x4*>(&sst[stage][16 + 4 * lg]);
+        }
         // all K operands requested at once (token l16, 16-bit elements
         // 32 ks + 8 lg .. + 7), then two independent accumulation chains
         u32x4 a[KS];
@@ -494,15 +498,10 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     {
 #pragma unroll
         for (int x = 0; x < S; ++x) load_blk(ring[x], phys_of(j0 + x));
-        float kraw[4], vraw[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            kraw[i] = ring[0].ks[i];
-            vraw[i] = ring[0].vs[i];
-        }
         store_k(ring[0], j0 & 1);
+        if (I8 && wv == 0 && lane < 32) sst[j0 & 1][lane] = ring[0].sc;
         __syncthreads();
-        if (owner) scores(j0, kraw, vraw);
+        if (owner) scores(j0);
     }
     int tp = (int)phys_of(j0 + S);  // physical block of j + S at iteration j, not yet uniform
     // iteration j: stage K(j+1) and V(j), barrier, scores of j+1, PV of j.
@@ -512,18 +511,15 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
         constexpr int Y = (X + 1) % S;          // slot of block j + 1
         constexpr bool FULL = decltype(full)::value;
         const int tnext = table[j + 1 + S < jend ? j + 1 + S : jend - 1];
-        float kraw[4], vraw[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            kraw[i] = ring[Y].ks[i];
-            vraw[i] = ring[Y].vs[i];
+        if (FULL || j + 1 < jend) {
+            store_k(ring[Y], (j + 1) & 1);
+            if (I8 && wv == 0 && lane < 32) sst[(j + 1) & 1][lane] = ring[Y].sc;
         }
-        if (FULL || j + 1 < jend) store_k(ring[Y], (j + 1) & 1);
         store_v(ring[X], j & 1);
         const int64_t ph = __builtin_amdgcn_readfirstlane(tp);
         if (FULL || j + S < jend) load_blk(ring[X], ph);
         __syncthreads();
-        if (owner && (FULL || j + 1 < jend)) scores(j + 1, kraw, vraw);
+        if (owner && (FULL || j + 1 < jend)) scores(j + 1);
         values(j);
         tp = tnext;
         // keep the next iteration's table wait behind this iteration's work
