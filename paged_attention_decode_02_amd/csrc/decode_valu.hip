@@ -1,5 +1,4 @@
-// Split-K paged decode on the vector ALUs (gfx950), for query groups smaller
-// than an MFMA tile.
+// Split-K paged decode on the vector ALUs (gfx950) for fp32 caches.
 //
 // One 64-lane wave (= one workgroup) handles one split-K partition of P
 // tokens for one kv head g, one query token t of one sequence b, and GT query
@@ -19,7 +18,10 @@
 //    half 1 those of rows 2 and 3, so the scores only cross between the two
 //    rows of a half (one lane swap).
 // Each half keeps its own running max and sum (online softmax in log2 units);
-// the two halves are merged at the end of the partition.
+// the two halves are merged at the end of the partition. Block j + 1's keys
+// and values are requested before block j is computed.
+#include <type_traits>
+
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -102,10 +104,24 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
     const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (int64_t)g * D * E;
     const char* vbase = reinterpret_cast<const char*>(p.v_cache) + (int64_t)g * D * E;
 
-    const int jend = (end + kBlockSize - 1) / kBlockSize;
-    for (int j = start / kBlockSize; j < jend; ++j) {
-        const int64_t phys = table[j];
-        const int64_t blk_off = phys * kBlockSize * tok_stride;
+    const int j0 = start / kBlockSize, jend = (end + kBlockSize - 1) / kBlockSize;
+
+    // two register buffers of a block's keys (QK layout) and values (PV
+    // layout): block j + 1 is requested before block j is computed
+    Raw<KB> kr[2][4];
+    Raw<VB> vr[2][8];
+    auto load_blk = [&](int x, int j) {  // past the partition: its last block again
+        const int64_t blk_off = (int64_t)table[j < jend ? j : jend - 1] * kBlockSize * tok_stride;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) load_raw<KB>(kr[x][s], kbase + blk_off + (4 * s + row) * tok_stride + c16 * KB);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int tok = 4 * (k >> 1) + 2 * half + (k & 1);
+            load_raw<VB>(vr[x][k], vbase + blk_off + tok * tok_stride + c32 * VB);
+        }
+    };
+    auto block = [&](int j, auto xc) {
+        constexpr int X = decltype(xc)::value;
         const int pos0 = j * kBlockSize;
 
         // ---- QK: scores of tokens 4s + row, in log2 units
@@ -113,17 +129,12 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int tok = 4 * s + row;
-            Raw<KB> kr;
-            load_raw<KB>(kr, kbase + blk_off + tok * tok_stride + c16 * KB);
-            float ks = 1.0f;
-            if constexpr (KVT == KV_I8) ks = p.k_scale[(phys * kBlockSize + tok) * p.Hkv + g];
 #pragma unroll
             for (int r = 0; r < GT; ++r) {
                 float acc = 0.0f;
 #pragma unroll
-                for (int e = 0; e < EK; ++e) acc = fmaf(qf[r][e], elem_f32<KVT>(kr, e), acc);
+                for (int e = 0; e < EK; ++e) acc = fmaf(qf[r][e], elem_f32<KVT>(kr[X][s], e), acc);
                 acc = row_sum16(acc);
-                if constexpr (KVT == KV_I8) acc *= ks;
                 srow[s][r] = (pos0 + tok < end) ? acc : -INFINITY;
             }
         }
@@ -164,24 +175,26 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeParams p) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int tok = 4 * (k >> 1) + 2 * half + (k & 1);
-            Raw<VB> vr;
-            load_raw<VB>(vr, vbase + blk_off + tok * tok_stride + c32 * VB);
             // Slots past the end may hold anything (NaN included): select, never
             // multiply by a zero weight.
             const bool ok = pos0 + tok < end;
-            float vs = 1.0f;
-            if constexpr (KVT == KV_I8) vs = p.v_scale[(phys * kBlockSize + tok) * p.Hkv + g];
-            float pk[GT];
-#pragma unroll
-            for (int r = 0; r < GT; ++r) pk[r] = ok ? sc[k][r] * vs : 0.0f;
 #pragma unroll
             for (int e = 0; e < EV; ++e) {
-                const float v = ok ? elem_f32<KVT>(vr, e) : 0.0f;
+                const float v = ok ? elem_f32<KVT>(vr[X][k], e) : 0.0f;
 #pragma unroll
-                for (int r = 0; r < GT; ++r) o[r][e] = fmaf(pk[r], v, o[r][e]);
+                for (int r = 0; r < GT; ++r) o[r][e] = fmaf(ok ? sc[k][r] : 0.0f, v, o[r][e]);
             }
         }
+    };
+    load_blk(0, j0);
+    int j = j0;
+    for (; j + 1 < jend; j += 2) {
+        load_blk(1, j + 1);
+        block(j, std::integral_constant<int, 0>{});
+        load_blk(0, j + 2);
+        block(j + 1, std::integral_constant<int, 1>{});
     }
+    if (j < jend) block(j, std::integral_constant<int, 0>{});
 
     // ---- merge the two halves, normalise, write
 #pragma unroll
@@ -264,12 +277,8 @@ hipError_t by_d(int D, int GT, const DecodeParams& p, hipStream_t s) {
 bool decode_valu_has_gt(int GT) { return GT == 1 || GT == 2 || GT == 4 || GT == 6 || GT == 8; }
 
 hipError_t launch_decode_valu(int kv_type, int D, int GT, const DecodeParams& p, hipStream_t stream) {
-    switch (kv_type) {
-    case KV_F32: return by_d<KV_F32>(D, GT, p, stream);
-    case KV_BF16: return by_d<KV_BF16>(D, GT, p, stream);
-    case KV_I8: return by_d<KV_I8>(D, GT, p, stream);
-    default: return hipErrorInvalidValue;
-    }
+    if (kv_type != KV_F32) return hipErrorInvalidValue;  // bf16 / int8 caches have their own kernels
+    return by_d<KV_F32>(D, GT, p, stream);
 }
 
 }  // namespace pa

@@ -94,7 +94,9 @@ int32_t partition_for(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, pa_dtype k
     if (want_np < 1) want_np = 1;
     int64_t P = (max_seq_len + want_np - 1) / want_np;
     P = (P + gran - 1) / gran * gran;
-    if (P < kMinPartition) P = kMinPartition;
+    // four-wave workgroups keep partitions long enough to bound the split-K
+    // partials; one-wave (fp32-cache) workgroups split short contexts finely
+    if (wpw > 1 && P < kMinPartition) P = kMinPartition;
     const int64_t whole = ((int64_t)max_seq_len + kBlock - 1) / kBlock * kBlock;
     if (P >= whole) P = whole;  // one partition covers everything
     return (int32_t)P;

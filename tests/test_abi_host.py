@@ -89,8 +89,11 @@ def test_workspace_size_and_partition_choice(lib):
     # the same shape with fp32 caches uses one-wave workgroups: four times as many partitions
     assert lib.pa_choose_partition_size(4, 1, 24, 4, 256, 0, 65536) == 512
     # one partition covers a short context: no workspace
-    assert lib.pa_choose_partition_size(1, 1, 4, 1, 64, 0, 256) == 256
-    assert lib.pa_decode_workspace_bytes(1, 1, 4, 1, 64, 0, 256, 0) == 0
+    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 1, 200) == 208
+    assert lib.pa_decode_workspace_bytes(1, 1, 24, 4, 256, 1, 200, 0) == 0
+    # fp32 caches (one-wave workgroups) split even short contexts into blocks
+    assert lib.pa_choose_partition_size(1, 1, 4, 1, 64, 0, 256) == 16
+    assert lib.pa_decode_workspace_bytes(1, 1, 4, 1, 64, 0, 256, 0) == 4 * 16 * 64 * 4 + 256
     # partitions are multiples of 16 and never longer than needed
     for L in (1, 17, 300, 5000, 250000):
         P = lib.pa_choose_partition_size(1, 1, 24, 4, 256, 2, L)
