@@ -4,8 +4,9 @@
 // Partition i of a row carries o_i (normalised within the partition) and its
 // natural-log LSE lse_i. With M = max_i lse_i and w_i = exp(lse_i - M):
 //   out = sum_i w_i o_i / sum_i w_i,   lse = M + log(sum_i w_i).
-// One 1024-thread workgroup per (b, t, h) row. The threads form
-// S = 1024 / (D/4) slices of D/4 threads; thread (slice, q) owns output
+// One workgroup of T threads per (b, t, h) row (T = 256, or 1024 when a
+// row has more partitions than 256 threads preload). The threads form
+// S = T / (D/4) slices of D/4 threads; thread (slice, q) owns output
 // elements 4q..4q+3 (one 16-byte load per partition) and takes partitions
 // slice, slice + S, ... . Slices are combined in a fixed order, so the result
 // is deterministic. Every load of the first kPre partitions of a thread is
@@ -18,9 +19,9 @@
 namespace pa {
 
 namespace {
-constexpr int kThreads = 1024;
-constexpr int kPre = 4;  // partitions per thread loaded up front
+constexpr int kPre = 8;  // partitions per thread loaded up front
 
+template <int kThreads>
 __device__ __forceinline__ float block_max(float v, float* red) {
     v = wave_max(v);
     const int w = threadIdx.x >> 6;
@@ -32,6 +33,7 @@ __device__ __forceinline__ float block_max(float v, float* red) {
     return r;
 }
 
+template <int kThreads>
 __device__ __forceinline__ float block_sum(float v, float* red) {
     v = wave_sum(v);
     const int w = threadIdx.x >> 6;
@@ -44,6 +46,7 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }
 }  // namespace
 
+template <int kThreads>
 __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(ReduceParams p) {
     __shared__ float red[kThreads / 64];
     __shared__ float4 part[kThreads];
@@ -69,21 +72,16 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(ReduceParams p)
             lv[k] = lse_row[i];
         }
     }
-    float lmax[kPre];
-#pragma unroll
-    for (int k = 0; k < kPre; ++k) {
-        const int i = tid + k * kThreads;
-        lmax[k] = i < p.NP ? lse_row[i] : -INFINITY;
-    }
     const int n = p.seq_lens[b] - p.Tq + t + 1;
     const int np = n > 0 ? min((n + p.P - 1) / p.P, p.NP) : 0;
 
+    // the slices' preloaded partitions are 0 .. kPre * S - 1; the rest is read here
     float mx = -INFINITY;
 #pragma unroll
     for (int k = 0; k < kPre; ++k)
-        if (tid + k * kThreads < np) mx = fmaxf(mx, lmax[k]);
-    for (int i = tid + kPre * kThreads; i < np; i += kThreads) mx = fmaxf(mx, lse_row[i]);
-    const float M = block_max(mx, red);
+        if (slice + k * S < np) mx = fmaxf(mx, lv[k]);
+    for (int i = kPre * S + tid; i < np; i += kThreads) mx = fmaxf(mx, lse_row[i]);
+    const float M = block_max<kThreads>(mx, red);
     const float mref = M == -INFINITY ? 0.0f : M;
 
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -102,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(ReduceParams p)
     for (int k = 0; k < kPre; ++k) add(slice + k * S, lv[k], ov[k]);
     for (int i = slice + kPre * S; i < np; i += S) add(i, lse_row[i], o_row[(int64_t)i * DQ + q]);
     // every thread of a slice holds the slice's weight sum: count it once
-    const float W = block_sum(q == 0 ? wsum : 0.0f, red);
+    const float W = block_sum<kThreads>(q == 0 ? wsum : 0.0f, red);
     part[tid] = acc;
     __syncthreads();
     if (slice == 0) {
@@ -132,7 +130,10 @@ hipError_t launch_splitk_reduce(const ReduceParams& p, hipStream_t stream) {
     const int64_t rows = (int64_t)p.B * p.Tq * p.Hq;
     if (rows <= 0) return hipSuccess;
     if (rows > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
+    if ((int64_t)p.NP * (p.D / 4) <= (int64_t)256 * kPre)
+        hipLaunchKernelGGL(splitk_reduce_kernel<256>, dim3((unsigned)rows), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(splitk_reduce_kernel<1024>, dim3((unsigned)rows), dim3(1024), 0, stream, p);
     return hipGetLastError();
 }
 
