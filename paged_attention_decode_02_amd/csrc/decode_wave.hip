@@ -2,10 +2,14 @@
 // (query groups below an MFMA tile).
 //
 // A workgroup of four 64-lane waves handles one split-K partition of P tokens
-// of one kv head g, one query token t of one sequence b, and GT query heads of
-// g's group, so every K/V byte is read once for all GT heads (grouped-query
-// attention). Wave w takes blocks w, w+4, w+8, ... of the partition with its
-// own softmax state; the four states are merged through LDS at the end. The
+// of hpg kv heads (1, 2 or 4), one query token t of one sequence b, and GT
+// query heads of each kv head's group, so every K/V byte is read once for all
+// GT heads (grouped-query attention). The 4 / hpg waves of a kv head take
+// every (4 / hpg)-th block of the partition, each with its own softmax state,
+// merged through LDS at the end. With hpg = 4 a workgroup reads whole token
+// rows (all kv heads) of each block, and workgroups of every kv head do the
+// same work (the heads' byte offsets in a row map to memory channels
+// differently; one head per workgroup made some workgroups 15% slower). The
 // split-K decode keeps per-partition softmax statistics (vllm-sm70 page,
 // "Why", Attention bullet: split-K paged decode with an int8 KV cache); the
 // log-sum-exp reduce merges partitions. Per 16-token KV block:
@@ -166,13 +170,17 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     // tokens (one 16-bit weight pair in LDS), the TPW lane groups interleave
     auto tok_of = [&](int st) { return 2 * TPW * (st >> 1) + 2 * vgrp + (st & 1); };
 
+    // kv head of this wave and its place among the head's WPH waves
+    const int WPH = kWaves / p.hpg;
+    const int sub = wv % WPH;
     int wg = blockIdx.x;
     const int part = wg % p.NP;
     wg /= p.NP;
     const int chunk = wg % p.nchunk;
     wg /= p.nchunk;
-    const int g = wg % p.Hkv;
-    wg /= p.Hkv;
+    const int ngrp = p.Hkv / p.hpg;
+    const int g = (wg % ngrp) * p.hpg + wv / WPH;
+    wg /= ngrp;
     const int t = wg % p.Tq;
     const int b = wg / p.Tq;
 
@@ -184,13 +192,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     if (start >= n) {
         if (p.NP == 1) {
             for (int r2 = 0; r2 < nh; ++r2) {
-                for (int d = threadIdx.x; d < D; d += 64 * kWaves) {
+                for (int d = sub * 64 + lane; d < D; d += 64 * WPH) {
                     if (p.out_bf16)
                         reinterpret_cast<uint16_t*>(p.out)[(rowbase + r2) * D + d] = 0;
                     else
                         reinterpret_cast<float*>(p.out)[(rowbase + r2) * D + d] = 0.0f;
                 }
-                if (p.lse != nullptr && threadIdx.x == 0) p.lse[rowbase + r2] = -INFINITY;
+                if (p.lse != nullptr && sub == 0 && lane == 0) p.lse[rowbase + r2] = -INFINITY;
             }
         }
         return;
@@ -335,7 +343,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     float vsh = 1.0f, vsh_inv = 1.0f;
     if constexpr (I8) {
         float vmax = 0.0f;
-        for (int j = j0 + wv + kWaves * (lane >> 4); j < jend; j += 4 * kWaves) {
+        for (int j = j0 + sub + WPH * (lane >> 4); j < jend; j += 4 * WPH) {
             const int64_t ph = table[j];
             const float sv = p.v_scale[(ph * kBlockSize + c16) * p.Hkv + g];
             const int pos = j * kBlockSize + c16;
@@ -350,7 +358,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     // K registers: register s holds slot s ^ sx (token 4 * (s ^ sx) + r)
     Raw<KB> kr[4];
     Raw<VB> vr[STEPS];
-    const int jw = j0 + wv;  // this wave's first block; it takes every kWaves-th block
+    const int jw = j0 + sub;  // this wave's first block; it takes every WPH-th block
     int64_t phys = jw < jend ? (int64_t)table[jw] : 0;
     auto load_k = [&](int64_t ph) {
         const char* base = kbase + ph * kBlockSize * tok_stride + c16 * KB;
@@ -379,7 +387,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
         }
         load_v(phys);
         int64_t phys_next = phys;
-        if constexpr (MORE) phys_next = (int64_t)table[j + kWaves];
+        if constexpr (MORE) phys_next = (int64_t)table[j + WPH];
 
         // ---------------------------------------------------------------- QK
         float ps[4][GT];
@@ -555,7 +563,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
         phys = phys_next;
     };
     int j = jw;
-    for (; j + kWaves < jend; j += kWaves) block(j, std::true_type{});
+    for (; j + WPH < jend; j += WPH) block(j, std::true_type{});
     if (j < jend) block(j, std::false_type{});
 
     // ------------------------------------------------------------ epilogue
@@ -606,18 +614,24 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
         }
     }
     __syncthreads();
-    // wave w merges heads w, w+4, ...: weights 2^(m_w - M) in a fixed order
-    for (int h = wv; h < nh; h += kWaves) {
+    // wave sub of a kv head merges its heads sub, sub + WPH, ... over the
+    // head's waves w0 .. w0 + WPH - 1: weights 2^(m_w - M) in a fixed order
+    const int w0 = wv - sub;
+    for (int h = sub; h < nh; h += WPH) {
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, merge_ml[w][0][h]);
+        for (int k = 0; k < kWaves; ++k)
+            if (k < WPH) M = fmaxf(M, merge_ml[w0 + k][0][h]);
         const float base = M == -INFINITY ? 0.0f : M;
         float wt[kWaves], l = 0.0f, lr = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            wt[w] = exp2_guarded(merge_ml[w][0][h] - base);
-            l += merge_ml[w][1][h] * wt[w];
-            lr += merge_ml[w][2][h] * wt[w];
+        for (int k = 0; k < kWaves; ++k) {
+            wt[k] = 0.0f;
+            if (k < WPH) {
+                wt[k] = exp2_guarded(merge_ml[w0 + k][0][h] - base);
+                l += merge_ml[w0 + k][1][h] * wt[k];
+                lr += merge_ml[w0 + k][2][h] * wt[k];
+            }
         }
         const float lnorm = I8 ? l : lr;  // bf16: the sum of the weights the values were multiplied by
         const float inv = lnorm > 0.0f ? 1.0f / lnorm : 0.0f;
@@ -627,7 +641,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
             // merge_o[w][h] holds element d at index d (lane vl owns elements vl*EV ..)
             float acc = 0.0f;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) acc += wt[w] * merge_o[w][h][d];
+            for (int k = 0; k < kWaves; ++k)
+                if (k < WPH) acc += wt[k] * merge_o[w0 + k][h][d];
             const float val = acc * inv;
             if (p.NP == 1) {
                 if (p.out_bf16)
@@ -651,7 +666,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
 namespace {
 template <int KVT, int D, int GT, int QS>
 hipError_t launch_one(const DecodeParams& p, hipStream_t s) {
-    const int64_t grid = (int64_t)p.NP * p.nchunk * p.Hkv * p.Tq * p.B;
+    if (p.hpg < 1 || p.hpg > kWaves || kWaves % p.hpg || p.Hkv % p.hpg) return hipErrorInvalidValue;
+    const int64_t grid = (int64_t)p.NP * p.nchunk * (p.Hkv / p.hpg) * p.Tq * p.B;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((decode_wave_kernel<KVT, D, GT, QS>), dim3((unsigned)grid), dim3(64 * kWaves), 0, s, p);

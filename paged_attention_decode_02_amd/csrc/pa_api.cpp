@@ -39,7 +39,7 @@ constexpr int kBlock = 16;
 constexpr int kMaxTq = 16;
 constexpr int kMaxGroup = 64;
 constexpr int kCUs = 256;          // MI355X compute units
-constexpr int kWavesPerCU = 8;     // target resident decode waves per CU
+constexpr int kWavesPerCU = 8;     // resident one-wave (fp32-cache) workgroups per CU
 constexpr int kMinPartition = 256; // tokens; bounds the split-K partial traffic
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -75,28 +75,59 @@ void row_chunks(int32_t R, int* NT, int* nchunk) {
     *nchunk = (tiles + *NT - 1) / *NT;
 }
 
-int32_t partition_for(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, pa_dtype kv_dtype, int32_t max_seq_len) {
+// Workgroups of the decode resident per CU that the partition heuristic aims
+// for (measured on the named workloads): the bf16 vector-ALU kernel with
+// 512-byte rows streams best with one four-wave workgroup per CU (fewer
+// concurrent streams: 2% faster at 64K than two); small head chunks (D * GT
+// <= 512, few registers) want four, so that short contexts still fill the
+// machine; everything else two (the int8 path is bound by its vector ALU work
+// and needs the second wave per SIMD).
+int wgs_per_cu(pa_dtype kv_dtype, int32_t D, int GT, bool mfma) {
+    if (kv_dtype == PA_F32) return kWavesPerCU;  // one-wave workgroups
+    if (mfma) return 2;
+    if (D * GT <= 512) return 4;
+    if (kv_dtype == PA_BF16 && D >= 256) return 1;
+    return 2;
+}
+
+// kv heads per workgroup of the bf16/int8 vector-ALU decode. Where one
+// workgroup per CU streams best (see wgs_per_cu), a workgroup takes as many
+// kv heads as divide Hkv up to 4, one wave each: it reads whole token rows of
+// every block, and workgroups of different kv heads no longer finish at
+// different times (measured: 3.7% faster at 64K). Elsewhere one kv head, its
+// blocks shared by the four waves (measured faster for int8 and for short
+// contexts, which need the finer split).
+int heads_per_wg(pa_dtype kv_dtype, int32_t D, int GT, int32_t Hkv) {
+    if (wgs_per_cu(kv_dtype, D, GT, false) != 1) return 1;
+    return Hkv % 4 == 0 ? 4 : (Hkv % 2 == 0 ? 2 : 1);
+}
+
+int32_t partition_for(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
+                      int32_t max_seq_len) {
     if (max_seq_len <= kBlock) return kBlock;
-    int GT, nchunk;
+    int GT = 0, nchunk, wph = waves_per_wg(kv_dtype);  // waves per kv head
     int64_t per_partition;  // workgroups per partition index
-    if (use_mfma(Tq, Hq, Hkv, kv_dtype)) {
+    const bool mfma = use_mfma(Tq, Hq, Hkv, kv_dtype);
+    if (mfma) {
         int NT;
         row_chunks((Hq / Hkv) * Tq, &NT, &nchunk);
         per_partition = (int64_t)B * Hkv * nchunk;
     } else {
         head_chunks(Hq / Hkv, &GT, &nchunk);
-        per_partition = (int64_t)B * Tq * Hkv * nchunk;
+        const int hpg = kv_dtype == PA_F32 ? 1 : heads_per_wg(kv_dtype, D, GT, Hkv);
+        per_partition = (int64_t)B * Tq * (Hkv / hpg) * nchunk;
+        if (kv_dtype != PA_F32) wph = 4 / hpg;
     }
     const int wpw = waves_per_wg(kv_dtype);
-    const int64_t gran = (int64_t)kBlock * wpw;  // one block per wave at least
-    const int64_t target = (int64_t)kCUs * kWavesPerCU / wpw;     // workgroups that fill the GPU once
+    const int64_t gran = (int64_t)kBlock * wph;  // one block per wave of a kv head at least
+    const int64_t target = (int64_t)kCUs * wgs_per_cu(kv_dtype, D, GT, mfma);  // workgroups that fill the GPU once
     int64_t want_np = (target + per_partition - 1) / per_partition;
     if (want_np < 1) want_np = 1;
     int64_t P = (max_seq_len + want_np - 1) / want_np;
     P = (P + gran - 1) / gran * gran;
     // four-wave workgroups keep partitions long enough to bound the split-K
     // partials; one-wave (fp32-cache) workgroups split short contexts finely
-    if (wpw > 1 && P < kMinPartition) P = kMinPartition;
+    if (wpw > 1 && P < kMinPartition * wph / 4) P = kMinPartition * wph / 4;
     const int64_t whole = ((int64_t)max_seq_len + kBlock - 1) / kBlock * kBlock;
     if (P >= whole) P = whole;  // one partition covers everything
     return (int32_t)P;
@@ -128,7 +159,7 @@ int32_t pa_choose_partition_size(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv,
         return fail(PA_ERR_DTYPE, "kv dtype %d not supported", (int)kv_dtype);
     if (max_seq_len < 0) return fail(PA_ERR_SHAPE, "max_seq_len=%d must be >= 0", max_seq_len);
     ok();
-    return partition_for(B, Tq, Hq, Hkv, kv_dtype, max_seq_len);
+    return partition_for(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len);
 }
 
 size_t pa_decode_workspace_bytes(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
@@ -136,7 +167,7 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv,
     if (check_dims(B, Tq, Hq, Hkv, D) || max_seq_len < 0 || partition_size < 0 || partition_size % kBlock)
         return 0;
     if (kv_dtype != PA_F32 && kv_dtype != PA_BF16 && kv_dtype != PA_I8) return 0;
-    const int32_t P = partition_size ? partition_size : partition_for(B, Tq, Hq, Hkv, kv_dtype, max_seq_len);
+    const int32_t P = partition_size ? partition_size : partition_for(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len);
     const int64_t NP = max_seq_len > 0 ? ((int64_t)max_seq_len + P - 1) / P : 1;
     if (NP <= 1) return 0;
     const size_t rows = (size_t)B * Tq * Hq;
@@ -209,7 +240,7 @@ int pa_decode(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
         return fail(PA_ERR_ALIGN, "q, caches and out must be 16-byte aligned");
 
-    const int32_t P = partition_size ? partition_size : partition_for(B, Tq, Hq, Hkv, kv_dtype, max_seq_len);
+    const int32_t P = partition_size ? partition_size : partition_for(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len);
     const int64_t NP64 = max_seq_len > 0 ? ((int64_t)max_seq_len + P - 1) / P : 1;
     if (NP64 > 0x7FFFFFFF) return fail(PA_ERR_SHAPE, "too many partitions");
     const int32_t NP = (int32_t)NP64;
@@ -245,6 +276,7 @@ int pa_decode(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq
     p.P = P;
     p.NP = NP;
     p.nchunk = nchunk;
+    p.hpg = (mfma || kv_dtype == PA_F32) ? 1 : heads_per_wg(kv_dtype, D, GT, Hkv);
     p.out = out;
     p.out_bf16 = out_dtype == PA_BF16;
     p.lse = lse;

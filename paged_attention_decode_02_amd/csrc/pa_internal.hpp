@@ -22,6 +22,7 @@ struct DecodeParams {
     int P;                // partition size in tokens (multiple of 16)
     int NP;               // partitions per row
     int nchunk;           // vector-ALU kernels: head chunks of GT; MFMA kernel: row chunks of 16*NT
+    int hpg;              // bf16/int8 vector-ALU kernel: kv heads per workgroup (1, 2 or 4, divides Hkv)
     void* out;
     int out_bf16;
     float* lse;

@@ -79,18 +79,25 @@ def test_decode_rejects_bad_arguments(lib, over, code):
 
 
 def test_workspace_size_and_partition_choice(lib):
-    # the long-context workload: 4 sequences x 4 kv heads x 32 partitions of 2048
-    # tokens = 512 four-wave workgroups, two resident waves per SIMD
+    # the long-context workload: 4 sequences x 64 partitions of 1024 tokens =
+    # 256 four-wave workgroups (one per CU), each wave one of the 4 kv heads
     P = lib.pa_choose_partition_size(4, 1, 24, 4, 256, 1, 65536)
-    assert P == 2048
+    assert P == 1024
     need = lib.pa_decode_workspace_bytes(4, 1, 24, 4, 256, 1, 65536, 2048)
     rows = 4 * 24
     assert need == rows * 32 * 256 * 4 + rows * 32 * 4
-    # the same shape with fp32 caches uses one-wave workgroups: four times as many partitions
+    # int8 caches: two workgroups per CU (the int8 path needs the second wave per SIMD)
+    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 2, 250000) == 1984
+    # small head chunks (batched GQA, D=128, 4 heads): four per CU
+    assert lib.pa_choose_partition_size(8, 1, 32, 8, 128, 1, 3637) == 256
+    # speculative verify on the matrix cores: two per CU
+    assert lib.pa_choose_partition_size(4, 8, 24, 4, 256, 1, 30321) == 960
+    # the same shape with fp32 caches uses one-wave workgroups, eight per CU
     assert lib.pa_choose_partition_size(4, 1, 24, 4, 256, 0, 65536) == 512
     # one partition covers a short context: no workspace
-    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 1, 200) == 208
-    assert lib.pa_decode_workspace_bytes(1, 1, 24, 4, 256, 1, 200, 0) == 0
+    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 1, 48) == 48
+    assert lib.pa_decode_workspace_bytes(1, 1, 24, 4, 256, 1, 48, 0) == 0
+    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 2, 200) == 208
     # fp32 caches (one-wave workgroups) split even short contexts into blocks
     assert lib.pa_choose_partition_size(1, 1, 4, 1, 64, 0, 256) == 16
     assert lib.pa_decode_workspace_bytes(1, 1, 4, 1, 64, 0, 256, 0) == 4 * 16 * 64 * 4 + 256

@@ -90,6 +90,16 @@ def test_partition_sizes(P):
     run_workload(generate(spec, seed=1), partition_size=P)
 
 
+@pytest.mark.parametrize("Hkv", [1, 2, 3, 4, 6, 8])
+@pytest.mark.parametrize("P", [16, 0])
+def test_kv_heads_per_workgroup(Hkv, P):
+    # bf16, D=256, 6 heads per group: a workgroup takes 4, 2 or 1 kv heads
+    # (as many as divide Hkv), one or more waves each; ragged and empty rows
+    spec = scaled("long64k_bf16", B=3, Tq=1, Hq=6 * Hkv, Hkv=Hkv, D=256, seq_lens=(0, 1500), peaked_frac=0.01)
+    w = generate(spec, seed=20 + Hkv, seq_lens=[0, 17, 1500])
+    run_workload(w, partition_size=P)
+
+
 @pytest.mark.parametrize("Tq", [2, 3, 8, 16])
 @pytest.mark.parametrize("kv", ["bf16", "i8"])
 def test_query_tokens_causal(Tq, kv):
