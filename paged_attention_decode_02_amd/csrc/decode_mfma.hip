@@ -48,7 +48,7 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 constexpr int kW = 4;  // waves per workgroup
-constexpr int S = 3;   // K/V blocks in flight per wave (register ring depth)
+constexpr int S2 = 2;  // block pairs in flight per wave (register ring depth)
 constexpr uint32_t kMagic = 0x64646464u;
 constexpr float kCodeBias = 1152.0f;  // 1024 + 128
 
@@ -110,7 +110,6 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     constexpr int DW = D / kW;                 // output dims per wave
     constexpr int NDT = DW / 16;               // 16-wide output tiles per wave
     constexpr int NQ = QS == 2 ? 2 : 1;        // query parts (hi, lo) for fp32 queries
-    constexpr int VB = 4 * E;                  // value bytes per lane per output tile
     // Global loads: wave w moves rows 4w .. 4w+3 of a block's K and V tiles,
     // as runs of whole rows (RB bytes each), GB bytes per lane and load
     constexpr int RB = D * E;                        // bytes of one cache row
@@ -121,10 +120,11 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     constexpr int KRS = 2 * D + 16;  // bytes per staged key row
     constexpr int VRS = RB + 32;     // bytes per staged value row
 
-    __shared__ __align__(16) unsigned char kst[2][kBlockSize][KRS];  // staged keys
-    __shared__ __align__(16) unsigned char vst[2][kBlockSize][VRS];  // staged values
-    __shared__ __align__(16) u32x2 pst[2][NT][64];  // probabilities (A operands of PV)
-    __shared__ __align__(16) float sst[2][32];      // int8: key then value scales of a block's tokens
+    // [stage][block of the pair] ...
+    __shared__ __align__(16) unsigned char kst[2][2][kBlockSize][KRS];  // staged keys
+    __shared__ __align__(16) unsigned char vst[2][2][kBlockSize][VRS];  // staged values
+    __shared__ __align__(16) u32x4 pst[2][NT][64];  // weights of a pair's 32 tokens (A operands of PV)
+    __shared__ __align__(16) float sst[2][2][32];   // int8: key then value scales of a block's tokens
     __shared__ __align__(16) float ast[2][NT][16];  // per-row rescale factors
     __shared__ int araise[2][NT];                   // whether a tile's rows were rescaled
     __shared__ float fin[2][NT][16];                // epilogue: 1/l and code bias per row
@@ -280,16 +280,19 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     }
 
     // ---------------------------------------------------------- pipeline
-    // Register ring of S blocks: block j (this wave's rows of the K and V
-    // tiles, plus (int8) the block's key and value scales, all requested
-    // together: a load issued later would make its wait drain the prefetches)
-    // lives in slot (j - j0) % S. Iteration j stages K(j + 1) (wave 0 also its
-    // scales) and V(j) in LDS and then requests block j + S into V(j)'s slot.
+    // Blocks go in pairs: iteration i takes the 32 tokens of blocks
+    // jp = j0 + 2 i and jp + 1 (the PV contracts 32 tokens per MFMA). Register
+    // ring of S2 pairs: pair i (this wave's rows of both blocks' K and V tiles,
+    // plus (int8) their scales, all requested together: a load issued later
+    // would make its wait drain the prefetches) lives in slot i % S2.
+    // Iteration i stages K(pair i + 1) (wave 0 also its scales) and V(pair i)
+    // in LDS and then requests pair i + S2 into V(pair i)'s slot.
+    const int npair = (jend - j0 + 1) / 2;
     struct Blk {
         Raw<GB> k[NL], v[NL];
         float sc;  // int8: lane l < 16 the key scale, 16 <= l < 32 the value scale of token l % 16
     };
-    Blk ring[S];
+    Blk ring[S2][2];
     // lane's share of a tile: load i covers bytes x = (i * 64 + lane) * GB of
     // the wave's four rows, i.e. row 4 * wv + x / RB, byte x % RB
     auto row_of = [&](int i) { return 4 * wv + ((i * 64 + lane) * GB) / RB; };
@@ -308,10 +311,10 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
             dst.sc = src[(ph * kBlockSize + l16) * p.Hkv + g];
         }
     };
-    auto store_k = [&](const Blk& src, int stage) {
+    auto store_k = [&](const Blk& src, int stage, int h) {
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            unsigned char* dst = &kst[stage][row_of(i)][col_of(i) * (2 / E)];
+            unsigned char* dst = &kst[stage][h][row_of(i)][col_of(i) * (2 / E)];
             if constexpr (I8) {
                 // codes c -> f16 (1024 + c + 128), two output bytes per code
                 uint32_t f[GB / 2];
@@ -338,11 +341,12 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
                     *reinterpret_cast<uint32_t*>(dst) = src.k[i].w[0];
             }
         }
+        if (I8 && wv == 0 && lane < 32) sst[stage][h][lane] = src.sc;
     };
-    auto store_v = [&](const Blk& src, int stage) {
+    auto store_v = [&](const Blk& src, int stage, int h) {
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            unsigned char* dst = &vst[stage][row_of(i)][col_of(i)];
+            unsigned char* dst = &vst[stage][h][row_of(i)][col_of(i)];
             if constexpr (GB == 16)
                 *reinterpret_cast<u32x4*>(dst) = u32x4{src.v[i].w[0], src.v[i].w[1], src.v[i].w[2], src.v[i].w[3]};
             else if constexpr (GB == 8)
@@ -355,49 +359,69 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     const int vtok = 4 * lg + (l16 & 3);
     const int vdim = wv * DW + 4 * (l16 >> 2);
 
-    // scores, softmax and probabilities of block j into LDS stage j % 2 (owners only)
-    auto scores = [&](int j) {
-        const int stage = j & 1;
-        const int pos0 = j * kBlockSize;
-        // int8: key and value scales of the lane's 4 tokens 4 lg + i
-        f32x4 kraw = f32x4{1.0f, 1.0f, 1.0f, 1.0f}, vraw = kraw;
-        if constexpr (I8) {
-            kraw = *reinterpret_cast<const f32x4*>(&sst[stage][4 * lg]);
-            vraw = *reinterpret_cast<const f32x4*>(&sst[stage][16 + 4 * lg]);
+    // scores, softmax and weights of pair i into LDS stage i % 2 (owners only).
+    // Lane l ends with row l16's tokens 4 lg + 0..3 of both blocks, which is
+    // the A-operand layout of a 16x16x32 PV product whose k index 8 lg + e
+    // means token 4 lg + e % 4 of block e / 4 of the pair.
+    auto scores = [&](int i) {
+        const int stage = i & 1;
+        const int jp = j0 + 2 * i;
+        // int8: key and value scales of the lane's 4 tokens in each block
+        f32x4 kraw[2], vraw[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            kraw[h] = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
+            vraw[h] = kraw[h];
+            if constexpr (I8) {
+                kraw[h] = *reinterpret_cast<const f32x4*>(&sst[stage][h][4 * lg]);
+                vraw[h] = *reinterpret_cast<const f32x4*>(&sst[stage][h][16 + 4 * lg]);
+            }
         }
         // all K operands requested at once (token l16, 16-bit elements
-        // 32 ks + 8 lg .. + 7), then two independent accumulation chains
-        u32x4 a[KS];
+        // 32 ks + 8 lg .. + 7), then four independent accumulation chains
+        u32x4 a[2][KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) a[ks] = *reinterpret_cast<const u32x4*>(&kst[stage][l16][(32 * ks + 8 * lg) * 2]);
-        f32x4 s2[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                a[h][ks] = *reinterpret_cast<const u32x4*>(&kst[stage][h][l16][(32 * ks + 8 * lg) * 2]);
+        f32x4 acc[2][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) acc[h][0] = acc[h][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-            for (int q2 = 0; q2 < NQ; ++q2) {
-                f32x4& acc = s2[ks & 1];
-                if constexpr (I8)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a[ks]),
-                                                                 __builtin_bit_cast(f16x8, qreg[q2][ks]), acc, 0, 0, 0);
-                else
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[ks]),
-                                                                  __builtin_bit_cast(bf16x8, qreg[q2][ks]), acc, 0, 0, 0);
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int q2 = 0; q2 < NQ; ++q2) {
+                    f32x4& c = acc[h][ks & 1];
+                    if constexpr (I8)
+                        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a[h][ks]),
+                                                                   __builtin_bit_cast(f16x8, qreg[q2][ks]), c, 0, 0, 0);
+                    else
+                        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[h][ks]),
+                                                                    __builtin_bit_cast(bf16x8, qreg[q2][ks]), c, 0, 0, 0);
+                }
             }
         }
-        const f32x4 s = s2[0] + s2[1];
-        float sc[4];
+        float sc[2][4];
         bool raise = false;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool ok = pos0 + 4 * lg + i < nvis;
-            float ksc = qpost;
-            if constexpr (I8) ksc *= kraw[i];
-            sc[i] = ok ? (s[i] - corr) * ksc : -INFINITY;
-            raise |= sc[i] > mref + 8.0f;
+        for (int h = 0; h < 2; ++h) {
+            const f32x4 s = acc[h][0] + acc[h][1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool ok = (jp + h) * kBlockSize + 4 * lg + e < nvis;
+                float ksc = qpost;
+                if constexpr (I8) ksc *= kraw[h][e];
+                sc[h][e] = ok ? (s[e] - corr) * ksc : -INFINITY;
+                raise |= sc[h][e] > mref + 8.0f;
+            }
         }
         const bool any = __builtin_amdgcn_ballot_w64(raise) != 0;
         if (any) {
-            float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+            float bm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                             fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
             bm = fmaxf(bm, __shfl_xor(bm, 16));
             bm = fmaxf(bm, __shfl_xor(bm, 32));
             const float mn = fmaxf(mref, bm);
@@ -410,63 +434,75 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
         }
         if (lane == 0) araise[stage][wv] = any ? 1 : 0;
         const float base = mref == -INFINITY ? 0.0f : mref;
-        float pr[4];
+        float pr[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pr[i] = exp2_weight(sc[i] - base);  // sc = -inf gives 0
-            lpart += pr[i];
-        }
-        u32x2 pa;
-        if constexpr (I8) {
-            float ph2[4];
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool ok = pos0 + 4 * lg + i < end;
-                ph2[i] = (float)(_Float16)(ok ? pr[i] * vraw[i] * vsh : 0.0f);
-                spart += ph2[i];
+            for (int e = 0; e < 4; ++e) {
+                pr[h][e] = exp2_weight(sc[h][e] - base);  // sc = -inf gives 0
+                lpart += pr[h][e];
             }
-            pa = u32x2{pack_f16x2(ph2[0], ph2[1]), pack_f16x2(ph2[2], ph2[3])};
+        u32x4 pa;
+        if constexpr (I8) {
+            float ph2[2][4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool ok = (jp + h) * kBlockSize + 4 * lg + e < end;
+                    ph2[h][e] = (float)(_Float16)(ok ? pr[h][e] * vraw[h][e] * vsh : 0.0f);
+                    spart += ph2[h][e];
+                }
+            pa = u32x4{pack_f16x2(ph2[0][0], ph2[0][1]), pack_f16x2(ph2[0][2], ph2[0][3]),
+                       pack_f16x2(ph2[1][0], ph2[1][1]), pack_f16x2(ph2[1][2], ph2[1][3])};
         } else {
-            pa = u32x2{pack_bf16_rne(pr[0], pr[1]), pack_bf16_rne(pr[2], pr[3])};
+            pa = u32x4{pack_bf16_rne(pr[0][0], pr[0][1]), pack_bf16_rne(pr[0][2], pr[0][3]),
+                       pack_bf16_rne(pr[1][0], pr[1][1]), pack_bf16_rne(pr[1][2], pr[1][3])};
             // sum of the rounded weights: the output is normalised by it, so it
             // stays a convex combination of value rows (l keeps the exact ones)
-            spart += bf16_to_f32((uint16_t)pa.x) + bf16_to_f32((uint16_t)(pa.x >> 16)) +
-                     bf16_to_f32((uint16_t)pa.y) + bf16_to_f32((uint16_t)(pa.y >> 16));
+#pragma unroll
+            for (int w = 0; w < 4; ++w) spart += bf16_to_f32((uint16_t)pa[w]) + bf16_to_f32((uint16_t)(pa[w] >> 16));
         }
         pst[stage][wv][lane] = pa;
     };
 
-    // PV of block j (all waves): probabilities and values from LDS stage j % 2
-    auto values = [&](int j) {
-        const int stage = j & 1;
-        const int pos0 = j * kBlockSize;
-        u32x2 bop[NDT];
-        const bool partial = pos0 + kBlockSize > end;  // tokens past the end may hold anything
+    // PV of pair i (all waves): weights and values from LDS stage i % 2
+    auto values = [&](int i) {
+        const int stage = i & 1;
+        const int jp = j0 + 2 * i;
+        u32x4 bop[NDT];
 #pragma unroll
         for (int nd = 0; nd < NDT; ++nd) {
-            if constexpr (I8) {
-                // codes of token vtok, dims vdim + 16 nd .. + 3, transposed in the lane quad
-                const uint32_t raw = *reinterpret_cast<const uint32_t*>(&vst[stage][vtok][vdim + 16 * nd]);
-                const uint32_t tw = quad_transpose8(raw, l16 & 3) ^ 0x80808080u;
-                bop[nd] = u32x2{f16pair_lo(tw), f16pair_hi(tw)};
-            } else {
-                // transposing LDS read: lane 4r + c of a 16-lane group names
-                // row (token) 4 lg + r, dims 4c .. 4c + 3 of the 16-dim tile;
-                // lane i receives dim i of the group's 4 tokens
-                const unsigned char* src = &vst[stage][4 * lg + (l16 >> 2)][(wv * DW + 16 * nd + 4 * (l16 & 3)) * 2];
-                u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)src));
-                if (partial) {
-                    const int t0 = pos0 + 4 * lg;  // element k is token 4*lg + k
-                    w.x = (t0 + 0 < end ? w.x & 0x0000FFFFu : 0u) | (t0 + 1 < end ? w.x & 0xFFFF0000u : 0u);
-                    w.y = (t0 + 2 < end ? w.y & 0x0000FFFFu : 0u) | (t0 + 3 < end ? w.y & 0xFFFF0000u : 0u);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int pos0 = (jp + h) * kBlockSize;
+                u32x2 w;
+                if constexpr (I8) {
+                    // codes of token vtok, dims vdim + 16 nd .. + 3, transposed in the lane quad
+                    const uint32_t raw = *reinterpret_cast<const uint32_t*>(&vst[stage][h][vtok][vdim + 16 * nd]);
+                    const uint32_t tw = quad_transpose8(raw, l16 & 3) ^ 0x80808080u;
+                    w = u32x2{f16pair_lo(tw), f16pair_hi(tw)};
+                } else {
+                    // transposing LDS read: lane 4r + c of a 16-lane group names
+                    // row (token) 4 lg + r, dims 4c .. 4c + 3 of the 16-dim tile;
+                    // lane i receives dim i of the group's 4 tokens
+                    const unsigned char* src =
+                        &vst[stage][h][4 * lg + (l16 >> 2)][(wv * DW + 16 * nd + 4 * (l16 & 3)) * 2];
+                    w = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)src));
+                    if (pos0 + kBlockSize > end) {  // tokens past the end may hold anything
+                        const int t0 = pos0 + 4 * lg;  // element k is token 4*lg + k
+                        w.x = (t0 + 0 < end ? w.x & 0x0000FFFFu : 0u) | (t0 + 1 < end ? w.x & 0xFFFF0000u : 0u);
+                        w.y = (t0 + 2 < end ? w.y & 0x0000FFFFu : 0u) | (t0 + 3 < end ? w.y & 0xFFFF0000u : 0u);
+                    }
                 }
-                bop[nd] = w;
+                bop[nd][2 * h] = w.x;
+                bop[nd][2 * h + 1] = w.y;
             }
         }
         // every tile's flag, factors and weights requested at once
         int rz[NT];
         f32x4 a4[NT];
-        u32x2 pw[NT];
+        u32x4 pw[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             rz[t] = araise[stage][t];
@@ -479,58 +515,67 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
                 for (int nd = 0; nd < NDT; ++nd) o[t][nd] *= a4[t];
             }
-            const u32x2 pa = pw[t];
 #pragma unroll
             for (int nd = 0; nd < NDT; ++nd) {
                 if constexpr (I8)
-                    o[t][nd] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                        __builtin_bit_cast(f16x4, pa), __builtin_bit_cast(f16x4, bop[nd]), o[t][nd], 0, 0, 0);
+                    o[t][nd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        __builtin_bit_cast(f16x8, pw[t]), __builtin_bit_cast(f16x8, bop[nd]), o[t][nd], 0, 0, 0);
                 else
-                    o[t][nd] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                        __builtin_bit_cast(bf16x4, pa), __builtin_bit_cast(bf16x4, bop[nd]), o[t][nd], 0, 0, 0);
+                    o[t][nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, pw[t]), __builtin_bit_cast(bf16x8, bop[nd]), o[t][nd], 0, 0, 0);
             }
         }
     };
 
-    // prologue: blocks j0 .. j0 + S - 1 requested, K(j0) staged, scores of
-    // block j0 done. Unconditional (a partition of fewer than S blocks
-    // re-reads its last one): the loop's wait counts assume all S in flight.
+    // prologue: pairs 0 .. S2 - 1 requested, K(pair 0) staged, scores of pair
+    // 0 done. Unconditional (blocks past the partition re-read its last one,
+    // masked by position): the loop's wait counts assume all S2 in flight.
     {
 #pragma unroll
-        for (int x = 0; x < S; ++x) load_blk(ring[x], phys_of(j0 + x));
-        store_k(ring[0], j0 & 1);
-        if (I8 && wv == 0 && lane < 32) sst[j0 & 1][lane] = ring[0].sc;
+        for (int x = 0; x < S2; ++x)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) load_blk(ring[x][h], phys_of(j0 + 2 * x + h));
+        store_k(ring[0][0], 0, 0);
+        store_k(ring[0][1], 0, 1);
         __syncthreads();
-        if (owner) scores(j0);
+        if (owner) scores(0);
     }
-    int tp = (int)phys_of(j0 + S);  // physical block of j + S at iteration j, not yet uniform
-    // iteration j: stage K(j+1) and V(j), barrier, scores of j+1, PV of j.
-    // FULL: every block this iteration requests lies inside the partition.
-    auto iter = [&](int j, auto xc, auto full) __attribute__((always_inline)) {
-        constexpr int X = decltype(xc)::value;  // slot of block j: (j - j0) % S
-        constexpr int Y = (X + 1) % S;          // slot of block j + 1
+    // physical blocks of pair i + S2 at iteration i, not yet uniform
+    int tp0 = (int)phys_of(j0 + 2 * S2), tp1 = (int)phys_of(j0 + 2 * S2 + 1);
+    // iteration i: stage K(pair i+1) and V(pair i), barrier, scores of pair
+    // i+1, PV of pair i. FULL: the pair this iteration requests starts inside
+    // the partition.
+    auto iter = [&](int i, auto xc, auto full) __attribute__((always_inline)) {
+        constexpr int X = decltype(xc)::value;  // slot of pair i: i % S2
+        constexpr int Y = (X + 1) % S2;         // slot of pair i + 1
         constexpr bool FULL = decltype(full)::value;
-        const int tnext = table[j + 1 + S < jend ? j + 1 + S : jend - 1];
-        if (FULL || j + 1 < jend) {
-            store_k(ring[Y], (j + 1) & 1);
-            if (I8 && wv == 0 && lane < 32) sst[(j + 1) & 1][lane] = ring[Y].sc;
+        const int jn = j0 + 2 * (i + 1 + S2);
+        const int tn0 = table[jn < jend ? jn : jend - 1], tn1 = table[jn + 1 < jend ? jn + 1 : jend - 1];
+        if (FULL || i + 1 < npair) {
+            store_k(ring[Y][0], (i + 1) & 1, 0);
+            store_k(ring[Y][1], (i + 1) & 1, 1);
         }
-        store_v(ring[X], j & 1);
-        const int64_t ph = __builtin_amdgcn_readfirstlane(tp);
-        if (FULL || j + S < jend) load_blk(ring[X], ph);
+        store_v(ring[X][0], i & 1, 0);
+        store_v(ring[X][1], i & 1, 1);
+        const int64_t ph0 = __builtin_amdgcn_readfirstlane(tp0), ph1 = __builtin_amdgcn_readfirstlane(tp1);
+        if (FULL || i + S2 < npair) {
+            load_blk(ring[X][0], ph0);
+            load_blk(ring[X][1], ph1);
+        }
         __syncthreads();
-        if (owner && (FULL || j + 1 < jend)) scores(j + 1);
-        values(j);
-        tp = tnext;
+        if (owner && (FULL || i + 1 < npair)) scores(i + 1);
+        values(i);
+        tp0 = tn0;
+        tp1 = tn1;
         // keep the next iteration's table wait behind this iteration's work
         __builtin_amdgcn_sched_barrier(0);
     };
-    int j = j0;
-    for (; j + 2 * S <= jend; j += S)
-        static_for<S>([&](auto xc) __attribute__((always_inline)) { iter(j + decltype(xc)::value, xc, std::true_type{}); });
-    for (; j < jend; j += S)
-        static_for<S>([&](auto xc) __attribute__((always_inline)) {
-            if (j + decltype(xc)::value < jend) iter(j + decltype(xc)::value, xc, std::false_type{});
+    int i = 0;
+    for (; i + 2 * S2 <= npair; i += S2)
+        static_for<S2>([&](auto xc) __attribute__((always_inline)) { iter(i + decltype(xc)::value, xc, std::true_type{}); });
+    for (; i < npair; i += S2)
+        static_for<S2>([&](auto xc) __attribute__((always_inline)) {
+            if (i + decltype(xc)::value < npair) iter(i + decltype(xc)::value, xc, std::false_type{});
         });
 
     // ------------------------------------------------------------ epilogue
