@@ -48,7 +48,6 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 constexpr int kW = 4;  // waves per workgroup
-constexpr int S2 = 2;  // block pairs in flight per wave (register ring depth)
 constexpr uint32_t kMagic = 0x64646464u;
 constexpr float kCodeBias = 1152.0f;  // 1024 + 128
 
@@ -57,7 +56,7 @@ __device__ __forceinline__ uint32_t f16pair_hi(uint32_t u) { return __builtin_am
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -110,6 +109,9 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     constexpr int DW = D / kW;                 // output dims per wave
     constexpr int NDT = DW / 16;               // 16-wide output tiles per wave
     constexpr int NQ = QS == 2 ? 2 : 1;        // query parts (hi, lo) for fp32 queries
+    // block pairs in flight per wave (register ring depth); at least 2, as the
+    // keys of pair i + 1 are staged while pair i's values are
+    constexpr int S2 = 2;
     // Global loads: wave w moves rows 4w .. 4w+3 of a block's K and V tiles,
     // as runs of whole rows (RB bytes each), GB bytes per lane and load
     constexpr int RB = D * E;                        // bytes of one cache row

@@ -94,9 +94,12 @@ constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7-i inside each half row
 constexpr int kDppRowMirror = 0x140;      // lane i <-> 15-i inside each row
 
+// Every control used here names a source lane inside the lane's own row, so
+// no lane keeps an old value: a plain DPP move (no zero-initialised
+// destination needed), which also fuses into a following add.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over the 16 lanes of a row; every lane of the row gets the same bits
