@@ -35,13 +35,14 @@
 //
 // PV. The probabilities go through a small per-wave LDS buffer, as 16-bit
 // pairs of consecutive tokens, to the PV layout, in which a group of lanes
-// takes one whole value row (16-byte or smaller loads, D*elt/4 lanes per
-// token) and lane i owns D/64 (or more) output elements for all GT heads.
-// Both cache types use v_dot2 over pairs of tokens: bf16 values against bf16
-// weights (the running sum l adds the same rounded weights, so the output is
-// a convex combination of value rows); int8 codes as (1024 + code + 128) f16
-// pairs against f16 weights times the value scale, with 1152 * sum(p)
-// subtracted once at the end.
+// takes one whole value row (16-byte loads for 512-byte rows, else one row
+// per wave) and each lane owns its row slice's output elements for all GT
+// heads. Both cache types use v_dot2 over pairs of tokens: bf16 values
+// against bf16 weights (the output is normalised by the sum of the same
+// rounded weights, so it stays a convex combination of value rows; the LSE
+// uses the exact sum); int8 codes as (1024 + code + 128) f16 pairs against
+// f16 weights times the value scale, with 1152 * sum(p) subtracted once at
+// the end.
 //
 // Loads are ping-ponged: the V block is requested before the QK of the same
 // block, the next K block before the PV, so one half-block is always in
