@@ -58,33 +58,39 @@ def algorithmic_bytes(w) -> dict:
             "total": kv + scales + table + q + out}
 
 
-DECODE_SOURCES = {
-    # kernel that dominates a step, by cache dtype, and the sources it is built from
-    "f32": ("decode_valu_kernel", ("decode_valu.hip", "pa_device.hpp", "pa_internal.hpp")),
-    "bf16": ("decode_wave_kernel", ("decode_wave.hip", "pa_device.hpp", "pa_internal.hpp")),
-    "i8": ("decode_wave_kernel", ("decode_wave.hip", "pa_device.hpp", "pa_internal.hpp")),
-}
+_COMMON = ("pa_device.hpp", "pa_internal.hpp")
 
 
-def kernel_source_digest(cache_dtype: str) -> str:
+def decode_kernel(spec) -> tuple:
+    """(name, sources) of the decode kernel that runs the workload: the
+    matrix-core kernel when G*Tq fills a 16-row tile (bf16/int8 caches), the
+    vector-ALU kernel otherwise, the plain kernel for fp32 caches."""
+    if spec.cache_dtype == "f32":
+        return "decode_valu_kernel", ("decode_valu.hip",) + _COMMON
+    if (spec.Hq // spec.Hkv) * spec.Tq >= 16:
+        return "decode_mfma_kernel", ("decode_mfma.hip",) + _COMMON
+    return "decode_wave_kernel", ("decode_wave.hip",) + _COMMON
+
+
+def kernel_source_digest(spec) -> str:
     """Digest of the decode kernel's sources (ties committed counters to code)."""
     h = hashlib.sha256()
-    for f in DECODE_SOURCES[cache_dtype][1]:
+    for f in decode_kernel(spec)[1]:
         p = os.path.join(ROOT, "paged_attention_decode_02_amd", "csrc", f)
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
 
-def committed_traffic(workload: str, cache_dtype: str):
+def committed_traffic(spec):
     """Per-launch HBM bytes (read + write) from the committed rocprofv3 counter
     summary, or None when it is missing or was taken on other kernel sources."""
-    p = os.path.join(ROOT, "profiles", "decode_%s_hbm_traffic.md" % workload)
+    p = os.path.join(ROOT, "profiles", "decode_%s_hbm_traffic.md" % spec.name)
     if not os.path.exists(p):
         return None
     text = open(p).read()
     m = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
-    if not m or not t or m.group(1) != kernel_source_digest(cache_dtype):
+    if not m or not t or m.group(1) != kernel_source_digest(spec):
         return None
     return int(t.group(1))
 
@@ -114,7 +120,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, copy_bytes
     kib = copy_bytes / 1024.0
     ff, fw = kib / copy_f, kib / copy_w
     spec = SPECS[workload]
-    kname = DECODE_SOURCES[spec.cache_dtype][0]
+    kname = decode_kernel(spec)[0]
     dk = [k for k in fetch if kname in k]
     assert len(dk) == 1, dk
     f_kib = sum(fetch[dk[0]]) / len(fetch[dk[0]])
@@ -142,7 +148,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, copy_bytes
         "| algorithmic bytes per launch | %d |" % algo,
         "| traffic / algorithmic | %.4f |" % ((read_b + write_b) / algo), "",
         "hbm_bytes_per_launch: %d" % (read_b + write_b),
-        "kernel_source_digest: %s" % kernel_source_digest(spec.cache_dtype), "",
+        "kernel_source_digest: %s" % kernel_source_digest(spec), "",
     ]
     return "\n".join(lines)
 
@@ -170,7 +176,7 @@ def summarize_trace(trace_csv: str, workload: str, command: str, tail_cold: int 
             return "device copy (bench set-up)"
         return "torch kernel (bench set-up, cache flush): " + k.split("<")[0].replace("void ", "")[:48]
 
-    spec_kernel = DECODE_SOURCES[__import__("workloads").SPECS[workload].cache_dtype][0]
+    spec_kernel = decode_kernel(__import__("workloads").SPECS[workload])[0]
     lines = [
         "# Kernel durations of bench.py on %s" % workload, "",
         "Command (one MI355X, repository root as the working directory):", "",
@@ -435,14 +441,14 @@ def main():
             "decode_plus_reduce_after_flush": round(1e3 * float(np.median(cold)), 2),
         },
         "roofline": {
-            "kernel": DECODE_SOURCES[sp.cache_dtype][0],
+            "kernel": decode_kernel(sp)[0],
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": committed_traffic(sp.name, sp.cache_dtype),
-            "kernel_source_digest": kernel_source_digest(sp.cache_dtype),
+            "traffic": committed_traffic(sp),
+            "kernel_source_digest": kernel_source_digest(sp),
         },
     }
     if args.copy_calibration_mb:
