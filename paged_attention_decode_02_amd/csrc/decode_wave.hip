@@ -67,6 +67,22 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
 }
 
+// First product of a dot-product chain. The VOP3P encoding takes the zero
+// accumulator as an inline constant; written as dot2(a, b, 0.0f) the compiler
+// zeroes a register and uses the accumulate-in-place encoding, one more
+// instruction per chain.
+__device__ __forceinline__ float dot2_bf16_first(uint32_t a, uint32_t b) {
+    float r;
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+__device__ __forceinline__ float dot2_f16_first(uint32_t a, uint32_t b) {
+    float r;
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 constexpr uint32_t kMagic = 0x64646464u;  // f16 0x64xx = 1024 + xx
 constexpr float kCodeBias = 1152.0f;      // 1024 + 128
 
@@ -334,9 +350,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     }
 
     const int32_t* table = p.block_table + (int64_t)b * p.max_blocks;
-    const int64_t tok_stride = (int64_t)p.Hkv * D * E;  // bytes between consecutive tokens of a block
-    const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (int64_t)g * D * E;
-    const char* vbase = reinterpret_cast<const char*>(p.v_cache) + (int64_t)g * D * E;
+    // KV addressing: a buffer resource per block (scalar) plus per-lane
+    // offsets that do not change from block to block; the host keeps a
+    // block's bytes below 2^31
+    const int tok_stride = p.Hkv * D * E;  // bytes between consecutive tokens of a block
+    const int blk_bytes = kBlockSize * tok_stride;
+    const char* kcache = reinterpret_cast<const char*>(p.k_cache);
+    const char* vcache = reinterpret_cast<const char*>(p.v_cache);
     const int j0 = start / kBlockSize, jend = (end + kBlockSize - 1) / kBlockSize;
 
     // int8: value probabilities are scaled by 2^vsh so that p * v_scale * 2^vsh
@@ -359,17 +379,23 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     // K registers: register s holds slot s ^ sx (token 4 * (s ^ sx) + r)
     Raw<KB> kr[4];
     Raw<VB> vr[STEPS];
+    int koff[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) koff[s] = (4 * (s ^ sx) + r) * tok_stride + g * D * E + c16 * KB;
+    const int voff = 2 * vgrp * tok_stride + g * D * E + vl * VB;  // + the step's uniform token offset
+    const int soff = (my_tok * p.Hkv + g) * 4;  // int8 scale of the lane's token within a block's scales
     const int jw = j0 + sub;  // this wave's first block; it takes every WPH-th block
     int64_t phys = jw < jend ? (int64_t)table[jw] : 0;
     auto load_k = [&](int64_t ph) {
-        const char* base = kbase + ph * kBlockSize * tok_stride + c16 * KB;
+        const auto rs = range_rsrc(kcache + ph * blk_bytes, blk_bytes);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) load_raw<KB, true>(kr[s], base + (4 * (s ^ sx) + r) * tok_stride);
+        for (int s = 0; s < 4; ++s) load_buf<KB>(kr[s], rs, koff[s], 0);
     };
     auto load_v = [&](int64_t ph) {
-        const char* base = vbase + ph * kBlockSize * tok_stride + vl * VB;
+        const auto rs = range_rsrc(vcache + ph * blk_bytes, blk_bytes);
 #pragma unroll
-        for (int st = 0; st < STEPS; ++st) load_raw<VB, true>(vr[st], base + tok_of(st) * tok_stride);
+        for (int st = 0; st < STEPS; ++st)
+            load_buf<VB>(vr[st], rs, voff, (2 * TPW * (st >> 1) + (st & 1)) * tok_stride);
     };
     if (jw < jend) load_k(phys);
 
@@ -383,8 +409,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
         // prefetches would make its wait drain them (in-order counting)
         float kscale_raw = 1.0f, vscale_raw = 1.0f;
         if constexpr (I8) {
-            kscale_raw = p.k_scale[(phys * kBlockSize + my_tok) * p.Hkv + g];
-            vscale_raw = p.v_scale[(phys * kBlockSize + my_tok) * p.Hkv + g];
+            const int64_t first = phys * kBlockSize * p.Hkv;  // the block's first scale
+            const int sbytes = kBlockSize * p.Hkv * 4;
+            Raw<4> ks, vs;
+            load_buf<4>(ks, range_rsrc(p.k_scale + first, sbytes), soff, 0);
+            load_buf<4>(vs, range_rsrc(p.v_scale + first, sbytes), soff, 0);
+            kscale_raw = __uint_as_float(ks.w[0]);
+            vscale_raw = __uint_as_float(vs.w[0]);
         }
         load_v(phys);
         int64_t phys_next = phys;
@@ -396,12 +427,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
             for (int h = 0; h < GT; ++h) {
-                float acc = 0.0f;
+                float acc;
                 if constexpr (I8) {
 #pragma unroll
                     for (int w = 0; w < KW; ++w) {
                         const uint32_t u = kr[s].w[w] ^ 0x80808080u;
-                        acc = dot2_f16(qv[h][2 * w], f16pair_lo(u), acc);
+                        acc = w == 0 ? dot2_f16_first(qv[h][0], f16pair_lo(u)) : dot2_f16(qv[h][2 * w], f16pair_lo(u), acc);
                         acc = dot2_f16(qv[h][2 * w + 1], f16pair_hi(u), acc);
                         if constexpr (QS == 2) {
                             acc = dot2_f16(ql[h][2 * w], f16pair_lo(u), acc);
@@ -411,7 +442,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
                 } else {
 #pragma unroll
                     for (int w = 0; w < KW; ++w) {
-                        acc = dot2_bf16(qv[h][w], kr[s].w[w], acc);
+                        acc = w == 0 ? dot2_bf16_first(qv[h][0], kr[s].w[0]) : dot2_bf16(qv[h][w], kr[s].w[w], acc);
                         if constexpr (QS == 2) acc = dot2_bf16(ql[h][w], kr[s].w[w], acc);
                     }
                 }

@@ -94,10 +94,13 @@ int wgs_per_cu(pa_dtype kv_dtype, int32_t D, int GT, bool mfma) {
 // workgroup per CU streams best (see wgs_per_cu), a workgroup takes as many
 // kv heads as divide Hkv up to 4, one wave each: it reads whole token rows of
 // every block, and workgroups of different kv heads no longer finish at
-// different times (measured: 3.7% faster at 64K). Elsewhere one kv head, its
-// blocks shared by the four waves (measured faster for int8 and for short
-// contexts, which need the finer split).
+// different times (measured: 3.7% faster at 64K). int8 with large head
+// chunks takes two kv heads, two waves each (measured at 250K tokens: decode
+// 2.5% faster than one head, 4% faster than four, whose partitions get too
+// many for the reduce). Elsewhere one kv head, its blocks shared by the four
+// waves (short contexts need the finer split).
 int heads_per_wg(pa_dtype kv_dtype, int32_t D, int GT, int32_t Hkv) {
+    if (kv_dtype == PA_I8 && D * GT > 512) return Hkv % 2 == 0 ? 2 : 1;
     if (wgs_per_cu(kv_dtype, D, GT, false) != 1) return 1;
     return Hkv % 4 == 0 ? 4 : (Hkv % 2 == 0 ? 2 : 1);
 }
@@ -227,6 +230,10 @@ int pa_decode(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq
     if (block_size < 1) return fail(PA_ERR_SHAPE, "block_size=%d must be >= 1", block_size);
     if (block_size != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size=%d (only 16)", block_size);
     if (num_blocks < 1) return fail(PA_ERR_SHAPE, "num_blocks=%lld must be >= 1", (long long)num_blocks);
+    // kernels address within one KV block with 32-bit offsets
+    const int64_t blk_bytes = (int64_t)kBlock * Hkv * D * (kv_dtype == PA_F32 ? 4 : kv_dtype == PA_BF16 ? 2 : 1);
+    if (blk_bytes >= ((int64_t)1 << 31))
+        return fail(PA_ERR_UNSUPPORTED, "a KV block of %lld bytes (Hkv=%d) exceeds 2^31", (long long)blk_bytes, Hkv);
     if (max_blocks_per_seq < 1) return fail(PA_ERR_SHAPE, "max_blocks_per_seq=%d must be >= 1", max_blocks_per_seq);
     if (max_seq_len < 0) return fail(PA_ERR_SHAPE, "max_seq_len=%d must be >= 0", max_seq_len);
     if ((int64_t)max_blocks_per_seq * block_size < max_seq_len)

@@ -65,6 +65,40 @@ __device__ __forceinline__ void load_raw(Raw<NB>& r, const void* p) {
     }
 }
 
+// Buffer resource over one contiguous byte range (a KV block, a block's
+// scales): loads then take a 32-bit per-lane offset plus a uniform offset, so
+// the 64-bit address arithmetic is done once per block on the scalar unit
+// instead of per load on the vector ALU. Word 3 is the gfx9 raw-buffer format
+// (32-bit data, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Nontemporal load of NB bytes at rsrc + voff + soff (voff per lane, soff uniform).
+template <int NB>
+__device__ __forceinline__ void load_buf(Raw<NB>& r, __amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+    typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+    constexpr int kNT = 2;  // cache policy: nontemporal
+    if constexpr (NB >= 16) {
+#pragma unroll
+        for (int i = 0; i < NB / 16; ++i) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16 * i, soff, kNT);
+            r.w[4 * i + 0] = v.x;
+            r.w[4 * i + 1] = v.y;
+            r.w[4 * i + 2] = v.z;
+            r.w[4 * i + 3] = v.w;
+        }
+    } else if constexpr (NB == 8) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, kNT);
+        r.w[0] = v.x;
+        r.w[1] = v.y;
+    } else {
+        static_assert(NB == 4, "unsupported load width");
+        r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, kNT);
+    }
+}
+
 // Element e of a raw vector as fp32 (int8: the code itself, exact).
 template <int KVT, int NB>
 __device__ __forceinline__ float elem_f32(const Raw<NB>& r, int e) {

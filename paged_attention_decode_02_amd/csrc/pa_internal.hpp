@@ -34,6 +34,7 @@ struct ReduceParams {
     const float* ws_o;
     const float* ws_lse;
     int NP, P, B, Tq, Hq, D;
+    int cs;  // column splits: workgroups per row, each taking D / cs output elements
     const int32_t* seq_lens;
     void* out;
     int out_bf16;

@@ -4,12 +4,14 @@
 // Partition i of a row carries o_i (normalised within the partition) and its
 // natural-log LSE lse_i. With M = max_i lse_i and w_i = exp(lse_i - M):
 //   out = sum_i w_i o_i / sum_i w_i,   lse = M + log(sum_i w_i).
-// One workgroup of T threads per (b, t, h) row (T = 256, or 1024 when a
-// row has more partitions than 256 threads preload). The threads form
-// S = T / (D/4) slices of D/4 threads; thread (slice, q) owns output
-// elements 4q..4q+3 (one 16-byte load per partition) and takes partitions
-// slice, slice + S, ... . Slices are combined in a fixed order, so the result
-// is deterministic. Every load of the first kPre partitions of a thread is
+// cs workgroups of T threads per (b, t, h) row, each taking C = D/(4 cs)
+// float4 columns (T = 256, or 1024 when a row has more partitions than 256
+// threads preload). The column split keeps a batch of few rows from putting
+// all of a row's partials through one CU. A workgroup's threads form
+// S = T / C slices of C threads; thread (slice, q) owns output elements
+// 4q..4q+3 (one 16-byte load per partition) and takes partitions slice,
+// slice + S, ... . Slices are combined in a fixed order, so the result is
+// deterministic, and every workgroup of a row computes the same M and W. Every load of the first kPre partitions of a thread is
 // issued before the row's length is known (addresses depend only on the
 // partition count), so the row costs one memory round trip; partitions past
 // the row's visible length are masked afterwards.
@@ -19,7 +21,8 @@
 namespace pa {
 
 namespace {
-constexpr int kPre = 8;  // partitions per thread loaded up front
+constexpr int kPre = 8;                   // partitions per thread loaded up front
+constexpr int kSplitMinPartitions = 160;  // column-split the rows above this many partitions
 
 template <int kThreads>
 __device__ __forceinline__ float block_max(float v, float* red) {
@@ -51,14 +54,17 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(ReduceParams p)
     __shared__ float red[kThreads / 64];
     __shared__ float4 part[kThreads];
     const int tid = threadIdx.x;
-    const int64_t rowid = blockIdx.x;
+    const int64_t rowid = blockIdx.x / p.cs;
+    const int csi = blockIdx.x % p.cs;
     const int t = (int)((rowid / p.Hq) % p.Tq);
     const int b = (int)(rowid / ((int64_t)p.Hq * p.Tq));
     const float* lse_row = p.ws_lse + rowid * p.NP;
     const float4* o_row = reinterpret_cast<const float4*>(p.ws_o + rowid * p.NP * p.D);
-    const int DQ = p.D / 4;  // float4 columns
-    const int S = kThreads / DQ;
-    const int slice = tid / DQ, q = tid % DQ;
+    const int DQ = p.D / 4;     // float4 columns of the row
+    const int DQc = DQ / p.cs;  // ... of this workgroup
+    const int S = kThreads / DQc;
+    const int slice = tid / DQc, qc = tid % DQc;
+    const int q = csi * DQc + qc;
 
     float4 ov[kPre];
     float lv[kPre];
@@ -100,12 +106,12 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(ReduceParams p)
     for (int k = 0; k < kPre; ++k) add(slice + k * S, lv[k], ov[k]);
     for (int i = slice + kPre * S; i < np; i += S) add(i, lse_row[i], o_row[(int64_t)i * DQ + q]);
     // every thread of a slice holds the slice's weight sum: count it once
-    const float W = block_sum<kThreads>(q == 0 ? wsum : 0.0f, red);
+    const float W = block_sum<kThreads>(qc == 0 ? wsum : 0.0f, red);
     part[tid] = acc;
     __syncthreads();
     if (slice == 0) {
         for (int s = 1; s < S; ++s) {
-            const float4 v = part[s * DQ + q];
+            const float4 v = part[s * DQc + qc];
             acc.x += v.x;
             acc.y += v.y;
             acc.z += v.z;
@@ -122,18 +128,29 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(ReduceParams p)
         } else {
             *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + o0) = make_float4(r[0], r[1], r[2], r[3]);
         }
+        // the row's first workgroup writes the lse
         if (q == 0 && p.lse != nullptr) p.lse[rowid] = W > 0.0f ? M + __logf(W) : -INFINITY;
     }
 }
 
-hipError_t launch_splitk_reduce(const ReduceParams& p, hipStream_t stream) {
-    const int64_t rows = (int64_t)p.B * p.Tq * p.Hq;
+hipError_t launch_splitk_reduce(const ReduceParams& p0, hipStream_t stream) {
+    const int64_t rows = (int64_t)p0.B * p0.Tq * p0.Hq;
     if (rows <= 0) return hipSuccess;
-    if (rows > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    if ((int64_t)p.NP * (p.D / 4) <= (int64_t)256 * kPre)
-        hipLaunchKernelGGL(splitk_reduce_kernel<256>, dim3((unsigned)rows), dim3(256), 0, stream, p);
+    ReduceParams p = p0;
+    // many partitions per row: split the columns until the grid has 512
+    // workgroups or each takes 4 float4 columns (measured: at 250K tokens and
+    // 24 rows, 252 partitions merge in 9.1 us split, 10.9 unsplit; at 128 or
+    // fewer partitions the split is slower)
+    const int DQ = p.D / 4;
+    p.cs = 1;
+    if (p.NP > kSplitMinPartitions)
+        while (rows * p.cs < 512 && DQ / (2 * p.cs) >= 4) p.cs *= 2;
+    const int64_t grid = rows * p.cs;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    if ((int64_t)p.NP * (DQ / p.cs) <= (int64_t)256 * kPre)
+        hipLaunchKernelGGL(splitk_reduce_kernel<256>, dim3((unsigned)grid), dim3(256), 0, stream, p);
     else
-        hipLaunchKernelGGL(splitk_reduce_kernel<1024>, dim3((unsigned)rows), dim3(1024), 0, stream, p);
+        hipLaunchKernelGGL(splitk_reduce_kernel<1024>, dim3((unsigned)grid), dim3(1024), 0, stream, p);
     return hipGetLastError();
 }
 

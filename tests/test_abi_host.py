@@ -86,8 +86,9 @@ def test_workspace_size_and_partition_choice(lib):
     need = lib.pa_decode_workspace_bytes(4, 1, 24, 4, 256, 1, 65536, 2048)
     rows = 4 * 24
     assert need == rows * 32 * 256 * 4 + rows * 32 * 4
-    # int8 caches: two workgroups per CU (the int8 path needs the second wave per SIMD)
-    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 2, 250000) == 1984
+    # int8 caches: two workgroups per CU (the int8 path needs the second wave
+    # per SIMD), each taking two kv heads: 252 partitions x 2 = 504 workgroups
+    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 2, 250000) == 992
     # small head chunks (batched GQA, D=128, 4 heads): four per CU
     assert lib.pa_choose_partition_size(8, 1, 32, 8, 128, 1, 3637) == 256
     # speculative verify on the matrix cores: two per CU
@@ -97,7 +98,8 @@ def test_workspace_size_and_partition_choice(lib):
     # one partition covers a short context: no workspace
     assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 1, 48) == 48
     assert lib.pa_decode_workspace_bytes(1, 1, 24, 4, 256, 1, 48, 0) == 0
-    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 2, 200) == 208
+    # (two waves per kv head: at least 4 blocks each)
+    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 2, 200) == 128
     # fp32 caches (one-wave workgroups) split even short contexts into blocks
     assert lib.pa_choose_partition_size(1, 1, 4, 1, 64, 0, 256) == 16
     assert lib.pa_decode_workspace_bytes(1, 1, 4, 1, 64, 0, 256, 0) == 4 * 16 * 64 * 4 + 256

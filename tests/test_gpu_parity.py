@@ -100,6 +100,15 @@ def test_kv_heads_per_workgroup(Hkv, P):
     run_workload(w, partition_size=P)
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_reduce_splits_columns_of_few_rows(D):
+    # more than 160 partitions of only 8 rows: the reduce spreads each row's
+    # columns over several workgroups (4 to 16 by D)
+    spec = scaled("gqa_bf16", B=2, Tq=1, Hq=4, Hkv=1, D=D, seq_lens=(2600, 3000))
+    w = generate(spec, seed=30 + D, seq_lens=[2600, 3000])
+    run_workload(w, partition_size=16)
+
+
 @pytest.mark.parametrize("Tq", [2, 3, 8, 16])
 @pytest.mark.parametrize("kv", ["bf16", "i8"])
 def test_query_tokens_causal(Tq, kv):
