@@ -6,14 +6,17 @@ shares no code with the HIP library (``pa_oracle.c`` includes nothing from it
 and is built by gcc, not hipcc).
 
 Functions take numpy arrays in the layouts the decode problem fixes:
-q [B, Tq, Hq, D]; caches [num_blocks, block_size, Hkv, D]; int8 scales
+q [B, Tq, Hq, D]; caches [num_blocks, block_size, Hkv, D]; int8 and FP8 scales
 [num_blocks, block_size, Hkv]; block_table [B, max_blocks] int32; seq_lens [B]
-int32. bfloat16 data is passed as its uint16 bit patterns.
+int32. bfloat16 data is passed as its uint16 bit patterns, FP8 (OCP E4M3) as
+its uint8 codes.
 
 Pins (see ``tests/test_oracle_pins.py``): Decimal brute force, closed forms
 (single key, constant V, zero query), dense contiguous attention, block-table
 permutation, GQA = repeated-KV MHA, causal = virtual batch, split = unsplit,
-prefix sharing, linearity, torch SDPA in fp64, int8 round trip and bound.
+prefix sharing, linearity, torch SDPA in fp64, int8 round trip and bound; FP8:
+hand-derived E4M3 values and roundings, torch's float8_e4m3fn decode and
+(saturated) encode, round trip and error bound.
 Every function here is pinned by at least one of them.
 """
 from __future__ import annotations
@@ -32,7 +35,7 @@ _LIB = os.path.join(_HERE, "_pa_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
-DTYPE_CODE = {"f32": 0, "bf16": 1, "i8": 2}
+DTYPE_CODE = {"f32": 0, "bf16": 1, "i8": 2, "fp8": 3}
 
 
 def build(force: bool = True) -> str:
@@ -63,6 +66,10 @@ def _load():
             lib.pa_oracle_decode_split.argtypes = dec + [I, P, I64, P, P, I]
             lib.pa_oracle_decode_split.restype = I
             lib.pa_oracle_max_threads.restype = I
+            lib.pa_oracle_fp8_value.argtypes = [I]
+            lib.pa_oracle_fp8_value.restype = ctypes.c_double
+            lib.pa_oracle_fp8_encode.argtypes = [F]
+            lib.pa_oracle_fp8_encode.restype = I
             _lib = lib
     return _lib
 
@@ -86,20 +93,32 @@ def _dtype_of(a: np.ndarray) -> str:
         return "bf16"
     if a.dtype == np.int8:
         return "i8"
+    if a.dtype == np.uint8:
+        return "fp8"  # OCP E4M3 codes
     raise TypeError("unsupported array dtype %s" % a.dtype)
 
 
 def alloc_cache(num_blocks: int, block_size: int, Hkv: int, D: int, cache_dtype: str):
     """Zeroed host cache arrays (k, v, k_scale, v_scale) in the cache layout."""
-    npdt = {"f32": np.float32, "bf16": np.uint16, "i8": np.int8}[cache_dtype]
+    npdt = {"f32": np.float32, "bf16": np.uint16, "i8": np.int8, "fp8": np.uint8}[cache_dtype]
     shape = (num_blocks, block_size, Hkv, D)
     k = np.zeros(shape, npdt)
     v = np.zeros(shape, npdt)
     ks = vs = None
-    if cache_dtype == "i8":
+    if cache_dtype in ("i8", "fp8"):
         ks = np.zeros(shape[:3], np.float32)
         vs = np.zeros(shape[:3], np.float32)
     return k, v, ks, vs
+
+
+def fp8_value(code: int) -> float:
+    """The value an OCP E4M3 code stands for (NaN for the NaN codes)."""
+    return float(_load().pa_oracle_fp8_value(int(code)))
+
+
+def fp8_encode(y: float) -> int:
+    """OCP E4M3 code of a binary32 value: nearest finite, ties to even, saturating."""
+    return int(_load().pa_oracle_fp8_encode(ctypes.c_float(y)))
 
 
 def cache_write(k_src: np.ndarray, v_src: np.ndarray, slot_mapping: np.ndarray, k_cache: np.ndarray,

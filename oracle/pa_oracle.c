@@ -22,6 +22,9 @@
  *    below follows those steps and must equal the plain definition.
  *  - int8 KV cache (vllm-sm70 page, "Why" and model table: int8 KV cache):
  *    symmetric, one fp32 scale per (token, kv head) = max|x| / 127.
+ *  - FP8 KV cache (nvllm page, "Acknowledgments": b12x paged attention with
+ *    FP8 KV dequantised inline; vllm-sm12x-nvfp4-dflash2 page, "What makes
+ *    this stack different": FP8 KV as the common pairing with NVFP4 weights).
  *
  * Readings where the pages are silent (each also listed with the tests):
  *  - seq_lens counts the Tq new tokens, whose K/V are already in the cache;
@@ -29,7 +32,15 @@
  *  - a row with no visible key gives out = 0 and lse = -inf;
  *  - int8: s = fp32(amax / 127); code = clamp(rint_half_even(fp32(x / s)),
  *    -127, 127); amax = 0 gives s = 0 and all codes 0;
- *  - the dequantised key/value is code * scale, formed exactly in fp64.
+ *  - the dequantised key/value is code * scale, formed exactly in fp64;
+ *  - FP8 is OCP E4M3 (the vllm-sm70 page names an E4M3 buffer; the pages do
+ *    not spell out the encoding, so the public OCP 8-bit floating-point
+ *    format is taken): sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ *    subnormals at exponent 0, no infinities, S.1111.111 is NaN, largest
+ *    finite magnitude 448. Scale as for int8 but against 448:
+ *    s = fp32(amax / 448); code = the finite E4M3 value nearest to
+ *    y = fp32(x / s), ties to the even code, sign taken from y (so values
+ *    beyond 448 saturate); amax = 0 gives s = 0 and all codes 0.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
  */
@@ -41,7 +52,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_I8 = 2 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_I8 = 2, OR_FP8 = 3 };
 
 static float bits_to_float(uint32_t u) {
     float f;
@@ -67,6 +78,31 @@ static uint16_t float_to_bf16_rne(float f) {
     return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
 }
 
+/* OCP E4M3: the value a code stands for (NaN for S.1111.111), exact in fp64. */
+double pa_oracle_fp8_value(int code) {
+    const int sgn = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double mag = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sgn ? -mag : mag;
+}
+
+/* OCP E4M3 code of a finite binary32 y: among the 127 finite magnitudes the
+ * one nearest to |y| (distances exact in fp64), a tie going to the even
+ * code; the sign bit is y's. Magnitudes past 448 therefore give 448. */
+int pa_oracle_fp8_encode(float y) {
+    const double a = fabs((double)y);
+    int best = 0;
+    double bd = a;  /* distance to code 0 (value 0) */
+    for (int c = 1; c < 127; ++c) {
+        const double d = fabs(pa_oracle_fp8_value(c) - a);
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+            best = c;
+            bd = d;
+        }
+    }
+    return (signbit(y) ? 0x80 : 0) | best;
+}
+
 /* One element of a query or a source row, as the value it stands for. */
 static double elem(const void* base, int dtype, int64_t i) {
     switch (dtype) {
@@ -77,13 +113,14 @@ static double elem(const void* base, int dtype, int64_t i) {
 }
 
 /* Element d of cache row `row` (row = (block * bs + offset) * Hkv + g),
- * dequantised: for int8 the exact product code * scale in fp64. */
+ * dequantised: for int8 and FP8 the exact product value(code) * scale in fp64. */
 static double cache_elem(const void* cache, int dtype, const float* scale, int64_t row, int D, int d) {
     int64_t i = row * (int64_t)D + d;
     switch (dtype) {
     case OR_F32: return (double)((const float*)cache)[i];
     case OR_BF16: return bf16_to_double(((const uint16_t*)cache)[i]);
     case OR_I8: return (double)((const int8_t*)cache)[i] * (double)scale[row];
+    case OR_FP8: return pa_oracle_fp8_value(((const uint8_t*)cache)[i]) * (double)scale[row];
     default: return NAN;
     }
 }
@@ -92,14 +129,14 @@ static double cache_elem(const void* cache, int dtype, const float* scale, int64
  * Cache writer. For every source token i with slot_mapping[i] >= 0 and every
  * kv head g, row x = src[i, g, :] goes to cache row (slot / bs, slot % bs, g).
  * f32->f32 and bf16->bf16 copy bits; bf16->f32 widens; f32->bf16 rounds to
- * nearest even; ->int8 quantises symmetrically per (token, kv head).
+ * nearest even; ->int8 and ->FP8 quantise symmetrically per (token, kv head).
  * Returns 0, or -1 on an unsupported dtype pair.
  */
 int pa_oracle_cache_write(const void* k_src, const void* v_src, int src_dtype, const int64_t* slot_mapping,
                           int64_t num_tokens, void* k_cache, void* v_cache, int cache_dtype, float* k_scale,
                           float* v_scale, int64_t num_blocks, int block_size, int Hkv, int D) {
     if (src_dtype != OR_F32 && src_dtype != OR_BF16) return -1;
-    if (cache_dtype != OR_F32 && cache_dtype != OR_BF16 && cache_dtype != OR_I8) return -1;
+    if (cache_dtype != OR_F32 && cache_dtype != OR_BF16 && cache_dtype != OR_I8 && cache_dtype != OR_FP8) return -1;
     for (int which = 0; which < 2; ++which) {
         const void* src = which ? v_src : k_src;
         void* cache = which ? v_cache : k_cache;
@@ -133,6 +170,20 @@ int pa_oracle_cache_write(const void* k_src, const void* v_src, int src_dtype, c
                             c = (int)r;
                         }
                         ((int8_t*)cache)[d0 + d] = (int8_t)c;
+                    }
+                } else if (cache_dtype == OR_FP8) {
+                    float amax = 0.0f;
+                    for (int d = 0; d < D; ++d) {
+                        float ax = fabsf((float)elem(src, src_dtype, s0 + d));
+                        if (ax > amax) amax = ax;
+                    }
+                    float s = amax / 448.0f; /* binary32 division, correctly rounded */
+                    scale[row] = s;
+                    for (int d = 0; d < D; ++d) {
+                        float x = (float)elem(src, src_dtype, s0 + d);
+                        int c = 0;
+                        if (amax != 0.0f) c = pa_oracle_fp8_encode(x / s); /* binary32 quotient first */
+                        ((uint8_t*)cache)[d0 + d] = (uint8_t)c;
                     }
                 } else if (cache_dtype == src_dtype) {
                     size_t eb = cache_dtype == OR_F32 ? 4 : 2;
@@ -273,7 +324,7 @@ static int check_args(const args_t* a) {
     if (!a->q || !a->k_cache || !a->v_cache || !a->block_table || !a->seq_lens) return -1;
     if (a->B < 0 || a->Tq < 1 || a->Hq < 1 || a->Hkv < 1 || a->D < 1 || a->block_size < 1) return -2;
     if (a->Hq % a->Hkv) return -2;
-    if (a->kv_dtype == OR_I8 && (!a->k_scale || !a->v_scale)) return -1;
+    if ((a->kv_dtype == OR_I8 || a->kv_dtype == OR_FP8) && (!a->k_scale || !a->v_scale)) return -1;
     return 0;
 }
 

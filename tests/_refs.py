@@ -21,12 +21,19 @@ from workloads import bf16_bits_to_f32
 
 
 def as_f64(a: np.ndarray, scale: Optional[np.ndarray] = None) -> np.ndarray:
-    """Values of a cache/query array as float64 (int8 times its row scale)."""
+    """Values of a cache/query array as float64 (int8 codes, or FP8 codes
+    decoded by torch's float8_e4m3fn, times their row scale)."""
     if a.dtype == np.uint16:
         return bf16_bits_to_f32(a).reshape(a.shape).astype(np.float64)
     if a.dtype == np.int8:
         assert scale is not None
         return a.astype(np.float64) * scale.astype(np.float64)[..., None]
+    if a.dtype == np.uint8:
+        import torch
+
+        assert scale is not None
+        vals = torch.from_numpy(np.ascontiguousarray(a)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        return vals * scale.astype(np.float64)[..., None]
     return a.astype(np.float64)
 
 

@@ -3,8 +3,9 @@
 Each test checks the oracle against something it does not share code with:
 Decimal brute force, closed forms, dense attention via numpy, torch SDPA,
 invariances (block permutation, GQA as repeated MHA, causal rows as a virtual
-batch, split = unsplit, shared prefix = private copies, linearity, poison), and
-hand-derived int8 quantiser cases. A dropped term, wrong sign or index, or a
+batch, split = unsplit, shared prefix = private copies, linearity, poison),
+hand-derived int8 and FP8 (OCP E4M3) quantiser cases, and torch's float8_e4m3fn
+conversions. A dropped term, wrong sign or index, or a
 transposed operand in the oracle fails at least one of them.
 """
 from __future__ import annotations
@@ -111,7 +112,7 @@ def test_uniform_weights_give_the_mean(how):
 
 
 # ------------------------------------------------------------ library / dense
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8", "fp8"])
 def test_paged_equals_dense_contiguous(dtype):
     spec = scaled("gqa_bf16", B=3, Tq=2, Hq=8, Hkv=2, D=32, seq_lens=(2, 200), src_dtype="f32",
                   cache_dtype=dtype, q_dtype="bf16")
@@ -218,7 +219,7 @@ def test_linear_in_values():
     assert np.max(np.abs(outs[2] - (2 * outs[0] + 0.5 * outs[1]))) <= 1e-12
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8", "fp8"])
 def test_poisoned_slots_are_never_read(dtype):
     spec = small(B=3, Tq=2, seq_lens=(5, 77), cache_dtype=dtype, src_dtype="f32")
     w = generate(spec, seed=14)
@@ -306,6 +307,125 @@ def test_int8_quotient_is_rounded_to_fp32_first():
         if found >= 5:
             break
     assert found >= 1
+
+
+# --------------------------------------------------------------- FP8 (E4M3)
+def _e4m3_torch_values() -> np.ndarray:
+    import torch
+
+    return torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_fp8_golden_values():
+    with open(os.path.join(GOLDEN, "fp8_e4m3_cases.json")) as f:
+        cases = json.load(f)["values"]
+    for c in cases:
+        got = oracle.fp8_value(c["code"])
+        if c["value"] == "nan":
+            assert np.isnan(got), c["why"]
+        else:
+            want = float(c["value"])
+            assert got == want and np.signbit(got) == np.signbit(want), c["why"]
+
+
+def test_fp8_values_match_torch_e4m3fn():
+    ref = _e4m3_torch_values()
+    for code in range(256):
+        got = oracle.fp8_value(code)
+        if np.isnan(ref[code]):
+            assert np.isnan(got), code
+        else:
+            assert got == ref[code] and np.signbit(got) == np.signbit(ref[code]), code
+
+
+def test_fp8_encoder_matches_torch_saturated_cast():
+    """Nearest-even rounding: every finite value, every midpoint and its fp32
+    neighbours, random and subnormal-range values, and values past 448 (which
+    saturate; torch's cast is applied to the clamped value)."""
+    import torch
+
+    vals = _e4m3_torch_values()
+    fin = np.unique(vals[np.isfinite(vals)])
+    mids = ((fin[:-1] + fin[1:]) / 2).astype(np.float32)
+    rng = np.random.default_rng(40)
+    y = np.concatenate([
+        fin.astype(np.float32), mids, np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(-np.inf)),
+        (rng.standard_normal(3000) * 60).astype(np.float32), (rng.random(1000) * 2.0 ** -5).astype(np.float32),
+        np.array([448.5, 463.9, 464.0, 465.0, 1e6, -450.0, -1e30, 3.4e38], np.float32)]).astype(np.float32)
+    want = torch.from_numpy(np.clip(y, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.fp8_encode(float(v)) for v in y], np.uint8)
+    bad = np.nonzero(got != want)[0]
+    assert len(bad) == 0, [(float(y[i]), int(got[i]), int(want[i])) for i in bad[:5]]
+
+
+def test_fp8_round_trip_of_every_finite_code():
+    for code in range(256):
+        v = oracle.fp8_value(code)
+        if not np.isnan(v):
+            assert oracle.fp8_encode(np.float32(v)) == code, code
+
+
+def test_fp8_golden_rows():
+    with open(os.path.join(GOLDEN, "fp8_e4m3_cases.json")) as f:
+        cases = json.load(f)["rows"]
+    for c in cases:
+        x = np.asarray(c["x"], np.float32)[None, None, :]
+        codes, scale = _write_rows(x, "fp8")
+        assert scale[0] == np.float32(c["scale"]), c["why"]
+        assert codes[0].tolist() == c["codes"], c["why"]
+
+
+def test_fp8_quotient_is_rounded_to_fp32_first():
+    """Where the exact quotient x/s lies just off the midpoint of two E4M3
+    values but its fp32 rounding lands on it, the code is the even neighbour
+    (the fp32 quotient, ties to even), not the side the exact quotient is on."""
+    vals = _e4m3_torch_values()
+    mags = [(c, vals[c]) for c in range(1, 127)]  # ascending finite magnitudes
+    rng = np.random.default_rng(42)
+    found = 0
+    for _ in range(200000):
+        s = np.float32(rng.uniform(0.001, 0.05))
+        i = int(rng.integers(0, len(mags) - 1))
+        (c0, v0), (c1, v1) = mags[i], mags[i + 1]
+        m = (v0 + v1) / 2  # exact in binary
+        base = np.float32(m * float(s))
+        for x in (base, np.nextafter(base, np.float32(np.inf)), np.nextafter(base, np.float32(-np.inf))):
+            if float(np.float32(x) / s) != m:
+                continue
+            exact = Fraction(float(x)) / Fraction(float(s))
+            if exact == Fraction(m):
+                continue
+            even = c0 if c0 % 2 == 0 else c1
+            exact_side = c0 if exact < Fraction(m) else c1
+            if exact_side == even:
+                continue  # both readings agree here
+            amax = np.float32(448.0 * float(s))
+            if np.float32(amax / np.float32(448)) != s or amax < abs(x):
+                continue
+            codes, scale = _write_rows(np.array([[[x, amax]]], np.float32), "fp8")
+            assert scale[0] == s
+            assert codes[0, 0] == even
+            found += 1
+        if found >= 5:
+            break
+    assert found >= 1
+
+
+def test_fp8_quantiser_bound_and_range():
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((2048, 1, 256), dtype=np.float32)
+    x[:32] *= np.float32(1e-30)
+    x[32:64] *= np.float32(1e30)
+    codes, s = _write_rows(x, "fp8")
+    vals = _e4m3_torch_values()[codes]
+    assert np.all(np.isfinite(vals))  # never a NaN code
+    # the largest magnitude of every row maps to +-448
+    assert np.all(np.abs(vals).max(axis=1) == 448.0)
+    # |x/s - value| <= half a step of the E4M3 grid at |x/s| (+ the fp32 quotient's rounding)
+    y = x[:, 0].astype(np.float64) / s[:, None].astype(np.float64)
+    e = np.maximum(np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -30))), -6)
+    half_step = 2.0 ** (e - 4)
+    assert np.all(np.abs(y - vals) <= half_step + np.abs(y) * 2.0 ** -23)
 
 
 def test_bf16_and_f32_copies():
