@@ -88,19 +88,38 @@ double pa_oracle_fp8_value(int code) {
 
 /* OCP E4M3 code of a finite binary32 y: among the 127 finite magnitudes the
  * one nearest to |y| (distances exact in fp64), a tie going to the even
- * code; the sign bit is y's. Magnitudes past 448 therefore give 448. */
-int pa_oracle_fp8_encode(float y) {
+ * code; the sign bit is y's. Magnitudes past 448 therefore give 448. The
+ * magnitudes of codes 0 .. 126 increase with the code, so the two candidates
+ * are found by bisection: the largest code whose value is <= |y| and the
+ * next one. */
+static void fp8_magnitudes(double mag[127]) {
+    for (int c = 0; c < 127; ++c) mag[c] = pa_oracle_fp8_value(c);
+}
+
+static int fp8_encode_with(const double mag[127], float y) {
     const double a = fabs((double)y);
-    int best = 0;
-    double bd = a;  /* distance to code 0 (value 0) */
-    for (int c = 1; c < 127; ++c) {
-        const double d = fabs(pa_oracle_fp8_value(c) - a);
-        if (d < bd || (d == bd && (c & 1) == 0)) {
-            best = c;
-            bd = d;
+    int best;
+    if (a >= mag[126]) {
+        best = 126;
+    } else {
+        int lo = 0, hi = 126;  /* mag[lo] <= a < mag[hi] */
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) / 2;
+            if (mag[mid] <= a)
+                lo = mid;
+            else
+                hi = mid;
         }
+        const double d0 = a - mag[lo], d1 = mag[hi] - a;
+        best = d0 < d1 ? lo : d1 < d0 ? hi : ((lo & 1) == 0 ? lo : hi);
     }
     return (signbit(y) ? 0x80 : 0) | best;
+}
+
+int pa_oracle_fp8_encode(float y) {
+    double mag[127];
+    fp8_magnitudes(mag);
+    return fp8_encode_with(mag, y);
 }
 
 /* One element of a query or a source row, as the value it stands for. */
@@ -137,14 +156,19 @@ int pa_oracle_cache_write(const void* k_src, const void* v_src, int src_dtype, c
                           float* v_scale, int64_t num_blocks, int block_size, int Hkv, int D) {
     if (src_dtype != OR_F32 && src_dtype != OR_BF16) return -1;
     if (cache_dtype != OR_F32 && cache_dtype != OR_BF16 && cache_dtype != OR_I8 && cache_dtype != OR_FP8) return -1;
+    for (int64_t i = 0; i < num_tokens; ++i)
+        if (slot_mapping[i] >= num_blocks * block_size) return -2;
+    double fp8_mag[127];
+    fp8_magnitudes(fp8_mag);
     for (int which = 0; which < 2; ++which) {
         const void* src = which ? v_src : k_src;
         void* cache = which ? v_cache : k_cache;
         float* scale = which ? v_scale : k_scale;
+        /* tokens write distinct slots: independent iterations */
+#pragma omp parallel for schedule(static)
         for (int64_t i = 0; i < num_tokens; ++i) {
             int64_t slot = slot_mapping[i];
             if (slot < 0) continue;
-            if (slot >= num_blocks * block_size) return -2;
             int64_t blk = slot / block_size, off = slot % block_size;
             for (int g = 0; g < Hkv; ++g) {
                 int64_t s0 = (i * Hkv + g) * (int64_t)D;
@@ -182,7 +206,7 @@ int pa_oracle_cache_write(const void* k_src, const void* v_src, int src_dtype, c
                     for (int d = 0; d < D; ++d) {
                         float x = (float)elem(src, src_dtype, s0 + d);
                         int c = 0;
-                        if (amax != 0.0f) c = pa_oracle_fp8_encode(x / s); /* binary32 quotient first */
+                        if (amax != 0.0f) c = fp8_encode_with(fp8_mag, x / s); /* binary32 quotient first */
                         ((uint8_t*)cache)[d0 + d] = (uint8_t)c;
                     }
                 } else if (cache_dtype == src_dtype) {
