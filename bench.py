@@ -50,11 +50,11 @@ def algorithmic_bytes(w) -> dict:
     """Bytes the method must move per decode step (the split-K workspace is
     implementation overhead and is reported apart)."""
     sp = w.spec
-    elt = {"f32": 4, "bf16": 2, "i8": 1}[sp.cache_dtype]
+    elt = {"f32": 4, "bf16": 2, "i8": 1, "fp8": 1}[sp.cache_dtype]
     qelt = 4 if sp.q_dtype == "f32" else 2
     L = w.seq_lens.astype(np.int64)
     kv = int(L.sum()) * sp.Hkv * sp.D * 2 * elt
-    scales = int(L.sum()) * sp.Hkv * 2 * 4 if sp.cache_dtype == "i8" else 0
+    scales = int(L.sum()) * sp.Hkv * 2 * 4 if sp.cache_dtype in ("i8", "fp8") else 0
     table = int(((L + 15) // 16).sum()) * 4
     q = sp.B * sp.Tq * sp.Hq * sp.D * qelt
     out = sp.B * sp.Tq * sp.Hq * (sp.D + 1) * 4
@@ -310,7 +310,7 @@ def main():
     w = generate(spec)
     log("generated %s in %.1f s" % (spec.name, time.time() - t0))
     sp = w.spec
-    TD = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}
+    TD = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "fp8": torch.float8_e4m3fn}
 
     def up(a, dt):
         if dt == "bf16":
@@ -318,10 +318,11 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     shape = (w.num_blocks, BLOCK_SIZE, sp.Hkv, sp.D)
-    kc = torch.zeros(shape, dtype=TD[sp.cache_dtype], device=dev)
+    kc = torch.zeros(shape, dtype=torch.uint8 if sp.cache_dtype == "fp8" else TD[sp.cache_dtype], device=dev)
+    kc = kc.view(TD[sp.cache_dtype])
     vc = torch.zeros_like(kc)
     ks = vs = None
-    if sp.cache_dtype == "i8":
+    if sp.cache_dtype in ("i8", "fp8"):
         ks = torch.zeros(shape[:3], dtype=torch.float32, device=dev)
         vs = torch.zeros_like(ks)
     N = w.slot_mapping.shape[0]

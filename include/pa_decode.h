@@ -38,8 +38,9 @@
  *    Query head h reads kv head h / (Hq / Hkv).
  *  - Supported: block_size 16; D in {64, 128, 256}; 1 <= Tq <= 16;
  *    Hq % Hkv == 0 and Hq / Hkv <= 64; q in {f32, bf16}; caches in
- *    {f32, bf16, i8}; out in {f32, bf16}. q, caches and out must be 16-byte
- *    aligned.
+ *    {f32, bf16, i8, fp8}; out in {f32, bf16}. q, caches and out must be
+ *    16-byte aligned; one KV block (16 * Hkv * D * element bytes) must be
+ *    below 2^31 bytes.
  */
 #ifndef PA_DECODE_H
 #define PA_DECODE_H
@@ -51,7 +52,10 @@
 extern "C" {
 #endif
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2 } pa_dtype;
+/* PA_FP8: OCP FP8 E4M3 codes (sign, 4 exponent bits biased by 7, 3 mantissa
+ * bits, no infinities, largest finite 448), the FP8 KV cache of the nvllm
+ * page ("Acknowledgments", b12x: FP8 KV dequantised inline). */
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2, PA_FP8 = 3 } pa_dtype;
 
 enum {
     PA_OK = 0,
@@ -76,11 +80,14 @@ enum {
  *   k_src, v_src   [num_tokens, Hkv, D] in src_dtype (f32 or bf16)
  *   slot_mapping   [num_tokens] int64, slot = block * block_size + offset
  *   k_cache, v_cache  caches in cache_dtype; k_scale, v_scale required iff
- *                  cache_dtype == PA_I8 (else pass NULL)
+ *                  cache_dtype is PA_I8 or PA_FP8 (else pass NULL)
  * Conversions: same dtype copies bits; bf16 -> f32 widens exactly;
  * f32 -> bf16 rounds to nearest even; -> i8 is symmetric per (token, kv
  * head): s = fp32(max|x| / 127), code = clamp(rint_even(fp32(x / s)), -127,
- * 127), and s = 0 with all codes 0 for an all-zero row. Bit-exact.
+ * 127); -> fp8 likewise against 448: s = fp32(max|x| / 448), code = the
+ * E4M3 value nearest to fp32(x / s), ties to the even code, saturating at
+ * +-448, the sign bit that of the quotient; for both, s = 0 with all codes 0
+ * for an all-zero row. Bit-exact. Source values must be finite.
  * Slots must lie in [0, num_blocks * block_size) and be distinct within one
  * call. num_tokens == 0 is a no-op.
  */
@@ -95,10 +102,12 @@ int pa_cache_write(const void* k_src, const void* v_src, pa_dtype src_dtype, con
  *   out[b,t,h,:] = sum_j softmax_j(softmax_scale * q[b,t,h,:] . K_j) V_j,
  *   lse[b,t,h]   = log sum_j exp(softmax_scale * q . K_j),
  * where K_j, V_j are the rows of logical position j of sequence b, read
- * through block_table[b][j / block_size] (int8: code * scale). n <= 0 gives
+ * through block_table[b][j / block_size] (int8 and fp8: the code's value
+ * times its row's scale). n <= 0 gives
  * out = 0 and lse = -inf. seq_lens counts the Tq new tokens, whose K/V must
- * already be in the cache (pa_cache_write). Arithmetic is fp32 (bf16/int8
- * operands, fp32 accumulation).
+ * already be in the cache (pa_cache_write). Arithmetic is fp32 (16-bit
+ * operands: bf16, int8 codes and fp8 values widened exactly; fp32
+ * accumulation).
  *   q              [B, Tq, Hq, D] in q_dtype
  *   block_table    [B, max_blocks_per_seq] int32; entries for logical blocks
  *                  < ceil(seq_lens[b] / block_size) must be in [0, num_blocks)

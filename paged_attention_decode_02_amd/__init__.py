@@ -30,7 +30,8 @@ _LIB_PATH = os.path.join(_HERE, "_lib", "libpa_decode.so")
 _lock = threading.Lock()
 _lib = None
 
-DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.int8: 2}
+# FP8 caches hold OCP E4M3 codes (torch.float8_e4m3fn storage)
+DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.int8: 2, torch.float8_e4m3fn: 3}
 
 EXPORTS = (
     "pa_cache_write", "pa_decode", "pa_decode_splitk_reduce", "pa_decode_workspace_bytes",

@@ -4,8 +4,12 @@
 // vllm-sm70 page's int8 KV cache ("Why", Attention bullet), here symmetric
 // with one fp32 scale per (token, kv head):
 //   s = fp32(max|x| / 127),  code = clamp(rint_even(fp32(x / s)), -127, 127),
-// and s = 0, codes 0 for an all-zero row. Both divisions are correctly
-// rounded binary32 divisions, so the codes are bit-exact.
+// and s = 0, codes 0 for an all-zero row. The FP8 variant (FP8 KV: nvllm
+// page, "Acknowledgments", b12x) stores OCP E4M3 codes the same way against
+// 448, the largest finite E4M3 magnitude: s = fp32(max|x| / 448), code = the
+// E4M3 value nearest to fp32(x / s), ties to even, saturating. Both
+// divisions are correctly rounded binary32 divisions, so the codes are
+// bit-exact.
 // A negative slot skips the token (padded rows must not write into other
 // requests' slots: vllm-sm70 page, "Known limitations").
 //
@@ -64,21 +68,32 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
             else
                 *dst = (uint16_t)w[0];
         } else {
+            constexpr bool F8 = CT == KV_FP8;
             float amax = 0.0f;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
             amax = wave_max(amax);
-            const float s = __fdiv_rn(amax, 127.0f);
+            const float s = __fdiv_rn(amax, F8 ? 448.0f : 127.0f);
             uint32_t packed = 0;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                int c = 0;
+            if constexpr (F8) {
                 if (amax != 0.0f) {
-                    float r = rintf(__fdiv_rn(x[e], s));
-                    r = fminf(fmaxf(r, -127.0f), 127.0f);
-                    c = (int)r;
+                    float y[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) y[e] = __fdiv_rn(x[e], s);
+                    packed = f32x4_to_fp8x4(y[0], y[1], y[2], y[3]);
+                    if constexpr (EPL < 4) packed &= (1u << (8 * EPL)) - 1u;
                 }
-                packed |= ((uint32_t)c & 0xFFu) << (8 * e);
+            } else {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    int c = 0;
+                    if (amax != 0.0f) {
+                        float r = rintf(__fdiv_rn(x[e], s));
+                        r = fminf(fmaxf(r, -127.0f), 127.0f);
+                        c = (int)r;
+                    }
+                    packed |= ((uint32_t)c & 0xFFu) << (8 * e);
+                }
             }
             int8_t* dst = reinterpret_cast<int8_t*>(cache) + dst_off;
             if constexpr (EPL == 4)
@@ -119,6 +134,7 @@ hipError_t launch_cache_write(int cache_type, const CacheWriteParams& p, hipStre
     case KV_F32: return launch_ct<KV_F32>(p.D, p, stream);
     case KV_BF16: return launch_ct<KV_BF16>(p.D, p, stream);
     case KV_I8: return launch_ct<KV_I8>(p.D, p, stream);
+    case KV_FP8: return launch_ct<KV_FP8>(p.D, p, stream);
     default: return hipErrorInvalidValue;
     }
 }

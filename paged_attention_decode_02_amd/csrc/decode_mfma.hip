@@ -27,7 +27,9 @@
 // workgroup barrier per block covers the staged tiles and the weights.
 // int8 caches: codes become f16 (1024 + code + 128) by a byte permute, queries
 // are scaled into f16 by a power of two, probabilities times the value scale
-// are f16; the code bias is removed once per row. Softmax: log2 units against a
+// are f16; the code bias is removed once per row. FP8 (OCP E4M3) caches: keys
+// are widened to bf16 (exact) against bf16 queries, values to f16 (exact)
+// against f16 probabilities times the value scale. Softmax: log2 units against a
 // per-row reference raised only when beaten by 2^8.
 #include <type_traits>
 #include <utility>
@@ -101,9 +103,11 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 template <int KVT, int D, int NT, int QS>
 __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
-    static_assert(KVT == KV_BF16 || KVT == KV_I8, "bf16 or int8 caches");
+    static_assert(KVT == KV_BF16 || KVT == KV_I8 || KVT == KV_FP8, "bf16, int8 or fp8 caches");
     static_assert(NT >= 1 && NT <= kW, "one row tile per wave");
     constexpr bool I8 = KVT == KV_I8;
+    constexpr bool F8 = KVT == KV_FP8;
+    constexpr bool QNT = I8 || F8;  // codes with a per-(token, kv head) scale; f16 PV
     constexpr int E = Elt<KVT>::bytes;
     constexpr int KS = D / 32;                 // k-steps of the score product
     constexpr int DW = D / kW;                 // output dims per wave
@@ -263,9 +267,9 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     // requested one iteration before it is used, ahead of that iteration's
     // K/V prefetches, so waiting for it never drains them.
 
-    // int8: probabilities times value scales are kept below 2^15 (f16) by 2^vsh
+    // int8 / fp8: probabilities times value scales are kept below 2^15 (f16) by 2^vsh
     float vsh = 1.0f, vsh_inv = 1.0f;
-    if constexpr (I8) {
+    if constexpr (QNT) {
         float vmax = 0.0f;
         for (int j = j0 + (threadIdx.x >> 4); j < jend; j += 4 * kW) {
             const int pos = j * kBlockSize + l16;
@@ -307,7 +311,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
             load_raw<GB, true>(dst.v[i], vbase + off);
         }
         dst.sc = 1.0f;
-        if constexpr (I8) {
+        if constexpr (QNT) {
             // one load for the block's 32 scales (lanes 32..63 repeat 0..31)
             const float* src = (lane & 16) ? p.v_scale : p.k_scale;
             dst.sc = src[(ph * kBlockSize + l16) * p.Hkv + g];
@@ -334,6 +338,24 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
                 } else {
                     *reinterpret_cast<u32x2*>(dst) = u32x2{f[0], f[1]};
                 }
+            } else if constexpr (F8) {
+                // E4M3 codes -> bf16 (exact), two output bytes per code
+                uint32_t f[GB / 2];
+#pragma unroll
+                for (int w = 0; w < GB / 4; ++w) {
+                    const pa_f32x2 lo = fp8x2_to_f32<false>(src.k[i].w[w]);
+                    const pa_f32x2 hi = fp8x2_to_f32<true>(src.k[i].w[w]);
+                    f[2 * w] = pack_bf16_rne(lo.x, lo.y);
+                    f[2 * w + 1] = pack_bf16_rne(hi.x, hi.y);
+                }
+                if constexpr (GB == 16) {
+                    reinterpret_cast<u32x4*>(dst)[0] = u32x4{f[0], f[1], f[2], f[3]};
+                    reinterpret_cast<u32x4*>(dst)[1] = u32x4{f[4], f[5], f[6], f[7]};
+                } else if constexpr (GB == 8) {
+                    *reinterpret_cast<u32x4*>(dst) = u32x4{f[0], f[1], f[2], f[3]};
+                } else {
+                    *reinterpret_cast<u32x2*>(dst) = u32x2{f[0], f[1]};
+                }
             } else {
                 if constexpr (GB == 16)
                     *reinterpret_cast<u32x4*>(dst) = u32x4{src.k[i].w[0], src.k[i].w[1], src.k[i].w[2], src.k[i].w[3]};
@@ -343,7 +365,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
                     *reinterpret_cast<uint32_t*>(dst) = src.k[i].w[0];
             }
         }
-        if (I8 && wv == 0 && lane < 32) sst[stage][h][lane] = src.sc;
+        if (QNT && wv == 0 && lane < 32) sst[stage][h][lane] = src.sc;
     };
     auto store_v = [&](const Blk& src, int stage, int h) {
 #pragma unroll
@@ -374,7 +396,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
         for (int h = 0; h < 2; ++h) {
             kraw[h] = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
             vraw[h] = kraw[h];
-            if constexpr (I8) {
+            if constexpr (QNT) {
                 kraw[h] = *reinterpret_cast<const f32x4*>(&sst[stage][h][4 * lg]);
                 vraw[h] = *reinterpret_cast<const f32x4*>(&sst[stage][h][16 + 4 * lg]);
             }
@@ -415,7 +437,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
             for (int e = 0; e < 4; ++e) {
                 const bool ok = (jp + h) * kBlockSize + 4 * lg + e < nvis;
                 float ksc = qpost;
-                if constexpr (I8) ksc *= kraw[h][e];
+                if constexpr (QNT) ksc *= kraw[h][e];
                 sc[h][e] = ok ? (s[e] - corr) * ksc : -INFINITY;
                 raise |= sc[h][e] > mref + 8.0f;
             }
@@ -445,7 +467,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
                 lpart += pr[h][e];
             }
         u32x4 pa;
-        if constexpr (I8) {
+        if constexpr (QNT) {
             float ph2[2][4];
 #pragma unroll
             for (int h = 0; h < 2; ++h)
@@ -484,6 +506,18 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
                     const uint32_t raw = *reinterpret_cast<const uint32_t*>(&vst[stage][h][vtok][vdim + 16 * nd]);
                     const uint32_t tw = quad_transpose8(raw, l16 & 3) ^ 0x80808080u;
                     w = u32x2{f16pair_lo(tw), f16pair_hi(tw)};
+                } else if constexpr (F8) {
+                    // as for int8, then the 4 tokens' codes of one dim as two exact f16 pairs
+                    const uint32_t raw = *reinterpret_cast<const uint32_t*>(&vst[stage][h][vtok][vdim + 16 * nd]);
+                    const uint32_t tw = quad_transpose8(raw, l16 & 3);
+                    const pa_f32x2 lo = fp8x2_to_f32<false>(tw), hi = fp8x2_to_f32<true>(tw);
+                    w = u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo.x, lo.y)),
+                              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi.x, hi.y))};
+                    if (pos0 + kBlockSize > end) {  // tokens past the end may hold NaN codes
+                        const int t0 = pos0 + 4 * lg;  // element k is token 4*lg + k
+                        w.x = (t0 + 0 < end ? w.x & 0x0000FFFFu : 0u) | (t0 + 1 < end ? w.x & 0xFFFF0000u : 0u);
+                        w.y = (t0 + 2 < end ? w.y & 0x0000FFFFu : 0u) | (t0 + 3 < end ? w.y & 0xFFFF0000u : 0u);
+                    }
                 } else {
                     // transposing LDS read: lane 4r + c of a 16-lane group names
                     // row (token) 4 lg + r, dims 4c .. 4c + 3 of the 16-dim tile;
@@ -519,7 +553,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
             }
 #pragma unroll
             for (int nd = 0; nd < NDT; ++nd) {
-                if constexpr (I8)
+                if constexpr (QNT)
                     o[t][nd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                         __builtin_bit_cast(f16x8, pw[t]), __builtin_bit_cast(f16x8, bop[nd]), o[t][nd], 0, 0, 0);
                 else
@@ -589,7 +623,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
         sp += __shfl_xor(sp, 16);
         sp += __shfl_xor(sp, 32);
         if (lg == 0) {
-            const float lnorm = I8 ? l : sp;  // bf16: the sum of the weights the values were multiplied by
+            const float lnorm = QNT ? l : sp;  // bf16: the sum of the weights the values were multiplied by
             fin[0][wv][l16] = lnorm > 0.0f ? 1.0f / lnorm : 0.0f;
             fin[1][wv][l16] = kCodeBias * sp;
             if (myrow < R) {
@@ -617,6 +651,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
             for (int nd = 0; nd < NDT; ++nd) {
                 float v = o[t][nd][i];
                 if constexpr (I8) v = (v - bias) * vsh_inv;
+                if constexpr (F8) v *= vsh_inv;
                 v *= inv;
                 const int d = wv * DW + 16 * nd + l16;
                 if (p.NP == 1) {
@@ -668,6 +703,7 @@ hipError_t launch_decode_mfma(int kv_type, int D, int NT, const DecodeParams& p,
     const int qs = p.q_bf16 ? 1 : 2;
     if (kv_type == KV_BF16) return qs == 1 ? by_d<KV_BF16, 1>(D, NT, p, stream) : by_d<KV_BF16, 2>(D, NT, p, stream);
     if (kv_type == KV_I8) return qs == 1 ? by_d<KV_I8, 1>(D, NT, p, stream) : by_d<KV_I8, 2>(D, NT, p, stream);
+    if (kv_type == KV_FP8) return qs == 1 ? by_d<KV_FP8, 1>(D, NT, p, stream) : by_d<KV_FP8, 2>(D, NT, p, stream);
     return hipErrorInvalidValue;
 }
 

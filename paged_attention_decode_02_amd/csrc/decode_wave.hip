@@ -1,5 +1,5 @@
-// Split-K paged decode on the vector ALUs for bf16 and int8 KV caches
-// (query groups below an MFMA tile).
+// Split-K paged decode on the vector ALUs for bf16, int8 and FP8 (OCP E4M3)
+// KV caches (query groups below an MFMA tile).
 //
 // A workgroup of four 64-lane waves handles one split-K partition of P tokens
 // of hpg kv heads (1, 2 or 4), one query token t of one sequence b, and GT
@@ -18,7 +18,9 @@
 // lane c of a row holds D/16 consecutive elements of a key row, so a row
 // reads whole contiguous key rows. Partial dot products use v_dot2 (bf16
 // pairs against bf16 queries; for int8, codes turned into f16 by a byte
-// permute against f16 queries scaled by a power of two). The 4 slots x GT
+// permute against f16 queries scaled by a power of two; for FP8, codes
+// widened to fp32 pairs by the hardware conversion and packed to bf16, exact,
+// against bf16 queries). The 4 slots x GT
 // heads partial sums are then reduced across the row by a *transposed*
 // butterfly: four DPP steps (row_mirror, row_half_mirror, quad xor 2, quad
 // xor 1) each add a partner lane's half of the items, so that afterwards each
@@ -42,7 +44,8 @@
 // rounded weights, so it stays a convex combination of value rows; the LSE
 // uses the exact sum); int8 codes as (1024 + code + 128) f16 pairs against
 // f16 weights times the value scale, with 1152 * sum(p) subtracted once at
-// the end.
+// the end; FP8 values as exact f16 pairs against f16 weights times the value
+// scale.
 //
 // Loads are ping-ponged: the V block is requested before the QK of the same
 // block, the next K block before the PV, so one half-block is always in
@@ -145,8 +148,10 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 template <int KVT, int D, int GT, int QS>
 __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p) {
-    static_assert(KVT == KV_BF16 || KVT == KV_I8, "bf16 or int8 caches");
+    static_assert(KVT == KV_BF16 || KVT == KV_I8 || KVT == KV_FP8, "bf16, int8 or fp8 caches");
     constexpr bool I8 = KVT == KV_I8;
+    constexpr bool F8 = KVT == KV_FP8;
+    constexpr bool QNT = I8 || F8;  // codes with a per-(token, kv head) scale
     constexpr int E = Elt<KVT>::bytes;
     constexpr int KB = D * E / 16;  // key bytes per lane per token (QK layout)
     constexpr int KW = KB / 4;      // ... in dwords
@@ -359,10 +364,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     const char* vcache = reinterpret_cast<const char*>(p.v_cache);
     const int j0 = start / kBlockSize, jend = (end + kBlockSize - 1) / kBlockSize;
 
-    // int8: value probabilities are scaled by 2^vsh so that p * v_scale * 2^vsh
-    // stays below 2^15 (f16) for every token of the partition (p <= 2^8)
+    // int8 / fp8: value probabilities are scaled by 2^vsh so that
+    // p * v_scale * 2^vsh stays below 2^15 (f16) for every token of the
+    // partition (p <= 2^8)
     float vsh = 1.0f, vsh_inv = 1.0f;
-    if constexpr (I8) {
+    if constexpr (QNT) {
         float vmax = 0.0f;
         for (int j = j0 + sub + WPH * (lane >> 4); j < jend; j += 4 * WPH) {
             const int64_t ph = table[j];
@@ -383,7 +389,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
 #pragma unroll
     for (int s = 0; s < 4; ++s) koff[s] = (4 * (s ^ sx) + r) * tok_stride + g * D * E + c16 * KB;
     const int voff = 2 * vgrp * tok_stride + g * D * E + vl * VB;  // + the step's uniform token offset
-    const int soff = (my_tok * p.Hkv + g) * 4;  // int8 scale of the lane's token within a block's scales
+    const int soff = (my_tok * p.Hkv + g) * 4;  // scale of the lane's token within a block's scales
     const int jw = j0 + sub;  // this wave's first block; it takes every WPH-th block
     int64_t phys = jw < jend ? (int64_t)table[jw] : 0;
     auto load_k = [&](int64_t ph) {
@@ -405,10 +411,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     auto block = [&](int j, auto more) {
         constexpr bool MORE = decltype(more)::value;
         const int pos0 = j * kBlockSize;
-        // int8 scales of the lane's token first: a load issued after the
-        // prefetches would make its wait drain them (in-order counting)
+        // int8 / fp8 scales of the lane's token first: a load issued after
+        // the prefetches would make its wait drain them (in-order counting)
         float kscale_raw = 1.0f, vscale_raw = 1.0f;
-        if constexpr (I8) {
+        if constexpr (QNT) {
             const int64_t first = phys * kBlockSize * p.Hkv;  // the block's first scale
             const int sbytes = kBlockSize * p.Hkv * 4;
             Raw<4> ks, vs;
@@ -437,6 +443,20 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
                         if constexpr (QS == 2) {
                             acc = dot2_f16(ql[h][2 * w], f16pair_lo(u), acc);
                             acc = dot2_f16(ql[h][2 * w + 1], f16pair_hi(u), acc);
+                        }
+                    }
+                } else if constexpr (F8) {
+#pragma unroll
+                    for (int w = 0; w < KW; ++w) {
+                        // four codes -> two exact bf16 pairs (elements 4w .. 4w + 3)
+                        const pa_f32x2 lo = fp8x2_to_f32<false>(kr[s].w[w]);
+                        const pa_f32x2 hi = fp8x2_to_f32<true>(kr[s].w[w]);
+                        const uint32_t k01 = pack_bf16_rne(lo.x, lo.y), k23 = pack_bf16_rne(hi.x, hi.y);
+                        acc = w == 0 ? dot2_bf16_first(qv[h][0], k01) : dot2_bf16(qv[h][2 * w], k01, acc);
+                        acc = dot2_bf16(qv[h][2 * w + 1], k23, acc);
+                        if constexpr (QS == 2) {
+                            acc = dot2_bf16(ql[h][2 * w], k01, acc);
+                            acc = dot2_bf16(ql[h][2 * w + 1], k23, acc);
                         }
                     }
                 } else {
@@ -481,7 +501,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
         // scores of the lane's items, log2 units; masked past the end
         const bool tok_ok = pos0 + my_tok < end;
         float ksc = qpost;
-        if constexpr (I8) ksc *= kscale_raw;
+        if constexpr (QNT) ksc *= kscale_raw;
         float sc[NI];
         bool raise = false;
 #pragma unroll
@@ -518,13 +538,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
 
         // ------------------------------------------------- probabilities -> LDS
         float sv = 1.0f;
-        if constexpr (I8) sv = vscale_raw * vsh;
+        if constexpr (QNT) sv = vscale_raw * vsh;
 #pragma unroll
         for (int j2 = 0; j2 < NI; ++j2) {
             const float base = mloc[j2] == -INFINITY ? 0.0f : mloc[j2];
             const float pr = exp2_weight(sc[j2] - base);  // sc = -inf gives 0
             uint16_t* slot16 = reinterpret_cast<uint16_t*>(pbuf_u) + ((my_tok >> 1) * GP + ihead[j2]) * 2 + (my_tok & 1);
-            if constexpr (I8) {
+            if constexpr (QNT) {
                 lloc[j2] += pr;
                 const _Float16 ph = (_Float16)(tok_ok ? pr * sv : 0.0f);
                 sloc[j2] += (float)ph;
@@ -544,7 +564,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
 
         // ---------------------------------------------------------------- PV
         // tokens past the end may hold anything (bf16: NaN or Inf times a zero
-        // weight); int8 codes are always finite, so only bf16 needs the mask
+        // weight; fp8: NaN codes); int8 codes are always finite
         if constexpr (!I8) {
             if (pos0 + kBlockSize > end) {
 #pragma unroll
@@ -572,6 +592,22 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
                     const uint32_t x1 = __builtin_amdgcn_perm(B, A, 0x07030602u) ^ 0x80808080u;  // a2 b2 a3 b3
                     const uint32_t f0 = f16pair_lo(x0), f1 = f16pair_hi(x0);
                     const uint32_t f2 = f16pair_lo(x1), f3 = f16pair_hi(x1);
+#pragma unroll
+                    for (int h = 0; h < GT; ++h) {
+                        o[h][4 * w + 0] = dot2_f16(pp[h], f0, o[h][4 * w + 0]);
+                        o[h][4 * w + 1] = dot2_f16(pp[h], f1, o[h][4 * w + 1]);
+                        o[h][4 * w + 2] = dot2_f16(pp[h], f2, o[h][4 * w + 2]);
+                        o[h][4 * w + 3] = dot2_f16(pp[h], f3, o[h][4 * w + 3]);
+                    }
+                } else if constexpr (F8) {
+                    // element e of tokens tk and tk + 1 as an f16 pair (exact:
+                    // every finite E4M3 value is an f16; round-toward-zero packing)
+                    const pa_f32x2 a01 = fp8x2_to_f32<false>(A), a23 = fp8x2_to_f32<true>(A);
+                    const pa_f32x2 b01 = fp8x2_to_f32<false>(B), b23 = fp8x2_to_f32<true>(B);
+                    const uint32_t f0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a01.x, b01.x));
+                    const uint32_t f1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a01.y, b01.y));
+                    const uint32_t f2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a23.x, b23.x));
+                    const uint32_t f3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a23.y, b23.y));
 #pragma unroll
                     for (int h = 0; h < GT; ++h) {
                         o[h][4 * w + 0] = dot2_f16(pp[h], f0, o[h][4 * w + 0]);
@@ -633,6 +669,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
             for (int e = 0; e < EV; ++e) {
                 float acc = o[h][e];
                 if constexpr (I8) acc = (acc - kCodeBias * sh[h] * (1.0f / DUP)) * vsh_inv;
+                if constexpr (F8) acc *= vsh_inv;
                 merge_o[wv][h][vl * EV + e] = acc;
             }
         }
@@ -665,7 +702,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
                 lr += merge_ml[w0 + k][2][h] * wt[k];
             }
         }
-        const float lnorm = I8 ? l : lr;  // bf16: the sum of the weights the values were multiplied by
+        const float lnorm = QNT ? l : lr;  // bf16: the sum of the weights the values were multiplied by
         const float inv = lnorm > 0.0f ? 1.0f / lnorm : 0.0f;
         const float lse2 = l > 0.0f ? (M + log2f(l)) * kLn2 : -INFINITY;
         const int64_t rowid = rowbase + h;
@@ -733,6 +770,7 @@ hipError_t launch_decode_wave(int kv_type, int D, int GT, const DecodeParams& p,
     const int qs = p.q_bf16 ? 1 : 2;
     if (kv_type == KV_BF16) return qs == 1 ? by_d<KV_BF16, 1>(D, GT, p, stream) : by_d<KV_BF16, 2>(D, GT, p, stream);
     if (kv_type == KV_I8) return qs == 1 ? by_d<KV_I8, 1>(D, GT, p, stream) : by_d<KV_I8, 2>(D, GT, p, stream);
+    if (kv_type == KV_FP8) return qs == 1 ? by_d<KV_FP8, 1>(D, GT, p, stream) : by_d<KV_FP8, 2>(D, GT, p, stream);
     return hipErrorInvalidValue;
 }
 

@@ -64,6 +64,11 @@ int waves_per_wg(pa_dtype kv_dtype) { return kv_dtype == PA_F32 ? 1 : 4; }
 
 // The matrix-core kernel takes all G*Tq rows of a kv head at once when they
 // fill at least one 16-row MFMA tile (bf16 and int8 caches).
+bool kv_supported(pa_dtype t) { return t == PA_F32 || t == PA_BF16 || t == PA_I8 || t == PA_FP8; }
+
+// caches stored as 8-bit codes with one fp32 scale per (token, kv head)
+bool quantised(pa_dtype t) { return t == PA_I8 || t == PA_FP8; }
+
 bool use_mfma(int32_t Tq, int32_t Hq, int32_t Hkv, pa_dtype kv_dtype) {
     return kv_dtype != PA_F32 && (int64_t)(Hq / Hkv) * Tq >= 16;
 }
@@ -100,7 +105,7 @@ int wgs_per_cu(pa_dtype kv_dtype, int32_t D, int GT, bool mfma) {
 // many for the reduce). Elsewhere one kv head, its blocks shared by the four
 // waves (short contexts need the finer split).
 int heads_per_wg(pa_dtype kv_dtype, int32_t D, int GT, int32_t Hkv) {
-    if (kv_dtype == PA_I8 && D * GT > 512) return Hkv % 2 == 0 ? 2 : 1;
+    if ((kv_dtype == PA_I8 || kv_dtype == PA_FP8) && D * GT > 512) return Hkv % 2 == 0 ? 2 : 1;
     if (wgs_per_cu(kv_dtype, D, GT, false) != 1) return 1;
     return Hkv % 4 == 0 ? 4 : (Hkv % 2 == 0 ? 2 : 1);
 }
@@ -158,8 +163,7 @@ int32_t pa_choose_partition_size(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv,
                                  int32_t max_seq_len) {
     int rc = check_dims(B, Tq, Hq, Hkv, D);
     if (rc) return rc;
-    if (kv_dtype != PA_F32 && kv_dtype != PA_BF16 && kv_dtype != PA_I8)
-        return fail(PA_ERR_DTYPE, "kv dtype %d not supported", (int)kv_dtype);
+    if (!kv_supported(kv_dtype)) return fail(PA_ERR_DTYPE, "kv dtype %d not supported", (int)kv_dtype);
     if (max_seq_len < 0) return fail(PA_ERR_SHAPE, "max_seq_len=%d must be >= 0", max_seq_len);
     ok();
     return partition_for(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len);
@@ -169,7 +173,7 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv,
                                  int32_t max_seq_len, int32_t partition_size) {
     if (check_dims(B, Tq, Hq, Hkv, D) || max_seq_len < 0 || partition_size < 0 || partition_size % kBlock)
         return 0;
-    if (kv_dtype != PA_F32 && kv_dtype != PA_BF16 && kv_dtype != PA_I8) return 0;
+    if (!kv_supported(kv_dtype)) return 0;
     const int32_t P = partition_size ? partition_size : partition_for(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len);
     const int64_t NP = max_seq_len > 0 ? ((int64_t)max_seq_len + P - 1) / P : 1;
     if (NP <= 1) return 0;
@@ -182,8 +186,8 @@ int pa_cache_write(const void* k_src, const void* v_src, pa_dtype src_dtype, con
                    float* v_scale, int64_t num_blocks, int32_t block_size, int32_t Hkv, int32_t D, void* stream) {
     if (src_dtype != PA_F32 && src_dtype != PA_BF16)
         return fail(PA_ERR_DTYPE, "source dtype %d not in {f32, bf16}", (int)src_dtype);
-    if (cache_dtype != PA_F32 && cache_dtype != PA_BF16 && cache_dtype != PA_I8)
-        return fail(PA_ERR_DTYPE, "cache dtype %d not in {f32, bf16, i8}", (int)cache_dtype);
+    if (!kv_supported(cache_dtype))
+        return fail(PA_ERR_DTYPE, "cache dtype %d not in {f32, bf16, i8, fp8}", (int)cache_dtype);
     if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens=%lld must be >= 0", (long long)num_tokens);
     if (num_blocks < 1) return fail(PA_ERR_SHAPE, "num_blocks=%lld must be >= 1", (long long)num_blocks);
     if (block_size < 1 || Hkv < 1 || D < 1)
@@ -191,7 +195,8 @@ int pa_cache_write(const void* k_src, const void* v_src, pa_dtype src_dtype, con
     if (block_size != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size=%d (only 16)", block_size);
     if (!supported_d(D)) return fail(PA_ERR_UNSUPPORTED, "D=%d not in {64, 128, 256}", D);
     if (!k_cache || !v_cache) return fail(PA_ERR_NULL, "k_cache/v_cache is NULL");
-    if (cache_dtype == PA_I8 && (!k_scale || !v_scale)) return fail(PA_ERR_NULL, "int8 cache needs k_scale and v_scale");
+    if (quantised(cache_dtype) && (!k_scale || !v_scale))
+        return fail(PA_ERR_NULL, "int8/fp8 caches need k_scale and v_scale");
     if (num_tokens == 0) return ok();
     if (!k_src || !v_src || !slot_mapping) return fail(PA_ERR_NULL, "k_src/v_src/slot_mapping is NULL");
     if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -223,8 +228,7 @@ int pa_decode(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq
     int rc = check_dims(B, Tq, Hq, Hkv, D);
     if (rc) return rc;
     if (q_dtype != PA_F32 && q_dtype != PA_BF16) return fail(PA_ERR_DTYPE, "q dtype %d not in {f32, bf16}", (int)q_dtype);
-    if (kv_dtype != PA_F32 && kv_dtype != PA_BF16 && kv_dtype != PA_I8)
-        return fail(PA_ERR_DTYPE, "kv dtype %d not in {f32, bf16, i8}", (int)kv_dtype);
+    if (!kv_supported(kv_dtype)) return fail(PA_ERR_DTYPE, "kv dtype %d not in {f32, bf16, i8, fp8}", (int)kv_dtype);
     if (out_dtype != PA_F32 && out_dtype != PA_BF16)
         return fail(PA_ERR_DTYPE, "out dtype %d not in {f32, bf16}", (int)out_dtype);
     if (block_size < 1) return fail(PA_ERR_SHAPE, "block_size=%d must be >= 1", block_size);
@@ -243,7 +247,8 @@ int pa_decode(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq
         return fail(PA_ERR_SHAPE, "partition_size=%d must be 0 or a positive multiple of %d", partition_size, kBlock);
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
         return fail(PA_ERR_NULL, "q, caches, block_table, seq_lens and out must be non-NULL");
-    if (kv_dtype == PA_I8 && (!k_scale || !v_scale)) return fail(PA_ERR_NULL, "int8 caches need k_scale and v_scale");
+    if (quantised(kv_dtype) && (!k_scale || !v_scale))
+        return fail(PA_ERR_NULL, "int8/fp8 caches need k_scale and v_scale");
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
         return fail(PA_ERR_ALIGN, "q, caches and out must be 16-byte aligned");
 
@@ -292,7 +297,7 @@ int pa_decode(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq
         p.ws_o = reinterpret_cast<float*>(workspace);
         p.ws_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + align256(rows * NP * D * sizeof(float)));
     }
-    // fp32 caches take the plain fp32 kernel; bf16 and int8 the packed-dot kernel
+    // fp32 caches take the plain fp32 kernel; bf16, int8 and fp8 the packed-dot kernel
     hipError_t e = kv_dtype == PA_F32 ? pa::launch_decode_valu((int)kv_dtype, D, GT, p, (hipStream_t)stream)
                    : mfma             ? pa::launch_decode_mfma((int)kv_dtype, D, GT, p, (hipStream_t)stream)
                                       : pa::launch_decode_wave((int)kv_dtype, D, GT, p, (hipStream_t)stream);

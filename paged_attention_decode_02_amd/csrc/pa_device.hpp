@@ -8,7 +8,7 @@
 
 namespace pa {
 
-enum KvType : int { KV_F32 = 0, KV_BF16 = 1, KV_I8 = 2 };
+enum KvType : int { KV_F32 = 0, KV_BF16 = 1, KV_I8 = 2, KV_FP8 = 3 };  // KV_FP8: OCP E4M3 codes
 
 constexpr int kBlockSize = 16;  // tokens per KV block
 constexpr int kWave = 64;
@@ -113,6 +113,29 @@ __device__ __forceinline__ float elem_f32(const Raw<NB>& r, int e) {
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// ------------------------------------------------------------ FP8 (E4M3)
+typedef __attribute__((ext_vector_type(2))) float pa_f32x2;
+
+// Two OCP E4M3 codes of w as fp32 (bytes 0, 1, or with HI bytes 2, 3);
+// exact for every finite code. (gfx950's fp8 -> 16-bit conversions are not
+// used: a probe of all 256 codes found their second element wrong.)
+template <bool HI>
+__device__ __forceinline__ pa_f32x2 fp8x2_to_f32(uint32_t w) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+}
+
+// Four fp32 values -> four OCP E4M3 codes (byte i = code of v[i]), nearest
+// even, saturating at +-448: the hardware pack rounds to nearest even but
+// sends magnitudes from 464 up to NaN, so the inputs are clamped first.
+__device__ __forceinline__ uint32_t f32x4_to_fp8x4(float a, float b, float c, float d) {
+    a = fminf(fmaxf(a, -448.0f), 448.0f);
+    b = fminf(fmaxf(b, -448.0f), 448.0f);
+    c = fminf(fmaxf(c, -448.0f), 448.0f);
+    d = fminf(fmaxf(d, -448.0f), 448.0f);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
 
 // fp32 -> bf16, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {

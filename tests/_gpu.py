@@ -2,7 +2,8 @@
 
 The device caches are first filled with poison, then written by the library's
 pa_cache_write, so every slot that holds no source row stays poisoned (NaN for
-float caches; code 127 with a NaN scale for int8) exactly as the oracle's
+float caches; code 127 with a NaN scale for int8 and FP8, where 127 is an
+E4M3 NaN) exactly as the oracle's
 host caches are (tests/_host.py).
 """
 from __future__ import annotations
@@ -14,7 +15,7 @@ import paged_attention_decode_02_amd as pa
 from _host import POISON_CODE
 from workloads import BLOCK_SIZE, Workload
 
-TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "fp8": torch.float8_e4m3fn}
 
 
 def dev():
@@ -32,6 +33,8 @@ def dev_to_host(t: torch.Tensor) -> np.ndarray:
     t = t.detach().cpu()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
     return t.numpy()
 
 
@@ -39,8 +42,8 @@ def poisoned_cache(w: Workload):
     sp = w.spec
     shape = (w.num_blocks, BLOCK_SIZE, sp.Hkv, sp.D)
     dt = TORCH_DT[sp.cache_dtype]
-    if sp.cache_dtype == "i8":
-        k = torch.full(shape, POISON_CODE, dtype=dt, device=dev())
+    if sp.cache_dtype in ("i8", "fp8"):
+        k = torch.full(shape, POISON_CODE, dtype=torch.uint8, device=dev()).view(dt)
         ks = torch.full(shape[:3], float("nan"), dtype=torch.float32, device=dev())
         return k, k.clone(), ks, ks.clone()
     if sp.cache_dtype == "bf16":

@@ -57,6 +57,7 @@ def decode_args(**over):
     (dict(out=None), -1),
     (dict(num_partitions=None), -1),
     (dict(kv_dtype=2), -1),  # int8 without scales
+    (dict(kv_dtype=3), -1),  # fp8 without scales
     (dict(q_dtype=2), -3),
     (dict(kv_dtype=7), -3),
     (dict(out_dtype=2), -3),
@@ -89,6 +90,9 @@ def test_workspace_size_and_partition_choice(lib):
     # int8 caches: two workgroups per CU (the int8 path needs the second wave
     # per SIMD), each taking two kv heads: 252 partitions x 2 = 504 workgroups
     assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 2, 250000) == 992
+    # fp8 caches take the int8 launch shape
+    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 3, 250000) == 992
+    assert lib.pa_choose_partition_size(4, 8, 24, 4, 256, 3, 30321) == 960
     # small head chunks (batched GQA, D=128, 4 heads): four per CU
     assert lib.pa_choose_partition_size(8, 1, 32, 8, 128, 1, 3637) == 256
     # speculative verify on the matrix cores: two per CU
@@ -120,6 +124,7 @@ def test_workspace_size_and_partition_choice(lib):
     (dict(block_size=8), -4),
     (dict(k_cache=None), -1),
     (dict(cache_dtype=2), -1),
+    (dict(cache_dtype=3), -1),  # fp8 without scales
     (dict(num_tokens=-1), -2),
     (dict(k_src=ctypes.c_void_p(0x1008)), -7),
 ])

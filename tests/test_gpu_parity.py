@@ -1,11 +1,13 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
 Tolerances: max|out - oracle| <= 1e-2 for fp32/bf16 caches and <= 2e-2 for
-int8 caches (fp32 accumulation over bf16/int8 operands); cache bytes and
+int8 and FP8 caches (fp32 accumulation over 16-bit operands); cache bytes and
 block indexing are bit-exact. The oracle runs on the oracle writer's caches,
 the GPU on pa_cache_write's caches, after checking the two are identical.
 """
 from __future__ import annotations
+
+import os
 
 import numpy as np
 import pytest
@@ -18,7 +20,9 @@ from workloads import BLOCK_SIZE, SPECS, generate, scaled
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-2, "bf16": 1e-2, "i8": 2e-2}
+# fp8: the int8 bound (the oracle dequantises the same codes, so the bound
+# covers only the kernel's 16-bit operands and fp32 sums, as for int8)
+TOL = {"f32": 1e-2, "bf16": 1e-2, "i8": 2e-2, "fp8": 2e-2}
 LSE_TOL = 1e-3
 
 
@@ -56,7 +60,8 @@ def run_workload(w, partition_size=0, check_cache=True):
 
 
 # ------------------------------------------------------------ full workloads
-@pytest.mark.parametrize("name", ["tiny_f32", "gqa_bf16", "long64k_bf16", "int8_250k", "verify_bf16", "verify_i8"])
+@pytest.mark.parametrize("name", ["tiny_f32", "gqa_bf16", "long64k_bf16", "int8_250k", "verify_bf16", "verify_i8",
+                                  "fp8_250k", "verify_fp8"])
 def test_named_workload_full_size(name):
     w = generate(name)
     run_workload(w, partition_size=SPECS[name].partition_size)
@@ -68,7 +73,7 @@ def test_named_workload_full_size(name):
 
 
 # ------------------------------------------------------------ dtype / shape grid
-@pytest.mark.parametrize("kv", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("kv", ["f32", "bf16", "i8", "fp8"])
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("qdt", ["f32", "bf16"])
 def test_dtype_and_head_dim_grid(kv, D, qdt):
@@ -92,10 +97,13 @@ def test_partition_sizes(P):
 
 @pytest.mark.parametrize("Hkv", [1, 2, 3, 4, 6, 8])
 @pytest.mark.parametrize("P", [16, 0])
-def test_kv_heads_per_workgroup(Hkv, P):
-    # bf16, D=256, 6 heads per group: a workgroup takes 4, 2 or 1 kv heads
-    # (as many as divide Hkv), one or more waves each; ragged and empty rows
-    spec = scaled("long64k_bf16", B=3, Tq=1, Hq=6 * Hkv, Hkv=Hkv, D=256, seq_lens=(0, 1500), peaked_frac=0.01)
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_kv_heads_per_workgroup(Hkv, P, kv):
+    # D=256, 6 heads per group: a workgroup takes 4 (bf16) or 2 (int8, fp8)
+    # kv heads, or fewer as Hkv allows, one or more waves each; ragged and
+    # empty rows
+    spec = scaled("long64k_bf16", B=3, Tq=1, Hq=6 * Hkv, Hkv=Hkv, D=256, seq_lens=(0, 1500), peaked_frac=0.01,
+                  cache_dtype=kv)
     w = generate(spec, seed=20 + Hkv, seq_lens=[0, 17, 1500])
     run_workload(w, partition_size=P)
 
@@ -110,7 +118,7 @@ def test_reduce_splits_columns_of_few_rows(D):
 
 
 @pytest.mark.parametrize("Tq", [2, 3, 8, 16])
-@pytest.mark.parametrize("kv", ["bf16", "i8"])
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
 def test_query_tokens_causal(Tq, kv):
     spec = scaled("verify_bf16", B=3, Tq=Tq, Hq=8, Hkv=2, D=128, seq_lens=(Tq, 900), shared_prefix=0,
                   cache_dtype=kv)
@@ -223,8 +231,37 @@ def test_splitk_reduce_entry_point_matches_decode():
     assert torch.equal(out, ref) and torch.equal(lse, rlse)
 
 
+def test_fp8_cache_write_of_hand_derived_rows():
+    """The hand-derived E4M3 rows (ties to even, subnormals, saturation, signed
+    zero, all-zero row) written by the GPU equal the oracle writer's bits."""
+    import json
+    import oracle
+
+    with open(os.path.join(os.path.dirname(__file__), "golden", "fp8_e4m3_cases.json")) as f:
+        rows = json.load(f)["rows"]
+    D = 64
+    x = np.zeros((len(rows), 1, D), np.float32)
+    for i, c in enumerate(rows):
+        x[i, 0, :len(c["x"])] = c["x"]
+    N = len(rows)
+    hk, hv, hks, hvs = oracle.alloc_cache(1, BLOCK_SIZE, 1, D, "fp8")
+    oracle.cache_write(x, x, np.arange(N), hk, hv, hks, hvs)
+    k = torch.zeros((1, BLOCK_SIZE, 1, D), dtype=torch.uint8, device=dev()).view(torch.float8_e4m3fn)
+    v = k.clone()
+    ks = torch.zeros((1, BLOCK_SIZE, 1), dtype=torch.float32, device=dev())
+    vs = ks.clone()
+    src = torch.from_numpy(x).to(dev())
+    pa.cache_write(src, src, torch.arange(N, dtype=torch.int64, device=dev()), k, v, ks, vs)
+    torch.cuda.synchronize()
+    assert np.array_equal(dev_to_host(k)[0, :N], hk[0, :N])
+    assert np.array_equal(dev_to_host(v)[0, :N], hv[0, :N])
+    assert np.array_equal(ks.cpu().numpy()[0, :N].view(np.uint32), hks[0, :N].view(np.uint32))
+    for i, c in enumerate(rows):
+        assert dev_to_host(k)[0, i, 0, :len(c["codes"])].tolist() == c["codes"], c["why"]
+
+
 def test_cache_write_skips_negative_slots_and_writes_bits():
-    for cache_dtype in ("f32", "bf16", "i8"):
+    for cache_dtype in ("f32", "bf16", "i8", "fp8"):
         for src in ("f32", "bf16"):
             spec = scaled("gqa_bf16", B=2, Hq=4, Hkv=2, D=64, seq_lens=(30, 70), src_dtype=src,
                           cache_dtype=cache_dtype)
@@ -251,7 +288,7 @@ def test_cache_write_skips_negative_slots_and_writes_bits():
             p_ = w.row_pos[sk_rows]
             sslots = w.block_table[b_, p_ // BLOCK_SIZE].astype(np.int64) * BLOCK_SIZE + p_ % BLOCK_SIZE
             kc = dev_to_host(cache[0]).reshape(-1, spec.Hkv, spec.D)[sslots]
-            if kc.dtype == np.int8:
+            if kc.dtype in (np.int8, np.uint8):
                 assert np.all(kc == 127)
             elif kc.dtype == np.uint16:
                 assert np.all(kc == 0x7FC0)
@@ -260,8 +297,8 @@ def test_cache_write_skips_negative_slots_and_writes_bits():
 
 
 # ------------------------------------------------------------ matrix-core path
-# G * Tq >= 16 rows per kv head (bf16 / int8 caches) run on the MFMA kernel.
-@pytest.mark.parametrize("kv", ["bf16", "i8"])
+# G * Tq >= 16 rows per kv head (bf16 / int8 / fp8 caches) run on the MFMA kernel.
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("G, Tq", [(6, 8), (16, 1), (8, 16), (2, 8), (24, 3)])
 def test_mfma_rows(kv, D, G, Tq):
@@ -272,7 +309,7 @@ def test_mfma_rows(kv, D, G, Tq):
 
 
 @pytest.mark.parametrize("qdt", ["f32", "bf16"])
-@pytest.mark.parametrize("kv", ["bf16", "i8"])
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
 def test_mfma_query_dtype_and_partitions(qdt, kv):
     spec = scaled("verify_bf16", B=3, Tq=8, Hq=12, Hkv=2, D=128, seq_lens=(8, 3000), shared_prefix=0,
                   cache_dtype=kv, q_dtype=qdt, src_dtype="f32")
