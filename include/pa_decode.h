@@ -168,6 +168,34 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv,
 int32_t pa_choose_partition_size(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
                                  int32_t max_seq_len);
 
+/*
+ * pa_decode_check — debug-time validation of the device data pa_decode
+ * trusts (block and slot ids out of range, and padded rows written into other
+ * requests' slots, are the defects the vllm-sm70 page reports: "Changes
+ * relative to 1Cat-vLLM", "Known limitations").
+ * Reads seq_lens[b] for b < B and block_table[b][j] for logical blocks
+ * j < min(ceil(seq_lens[b] / 16), max_blocks_per_seq), on `stream`, and
+ * writes status[0] = the number of violations (seq_lens[b] outside
+ * [0, max_seq_len], or a block id outside [0, num_blocks)) and status[1] =
+ * the smallest flat index of one (b * (max_blocks_per_seq + 1) + j for table
+ * entry j, b * (max_blocks_per_seq + 1) + max_blocks_per_seq for seq_lens[b]),
+ * or -1. status: device int32[2]. Every read stays in bounds whatever the
+ * values; nothing else is read or written. Runs as one workgroup: a debug aid,
+ * not part of the decode step.
+ */
+int pa_decode_check(const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t B,
+                    int32_t max_seq_len, int64_t num_blocks, int32_t* status, void* stream);
+
+/*
+ * pa_cache_write_check — debug-time validation of slot_mapping for
+ * pa_cache_write: status[0] = the number of tokens whose slot is
+ * >= num_blocks * block_size, status[1] = the first such token index or -1
+ * (negative slots mean "skip" and are valid). Duplicate slots are not
+ * detected. status: device int32[2].
+ */
+int pa_cache_write_check(const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks, int32_t block_size,
+                         int32_t* status, void* stream);
+
 /* Message for the calling thread's last non-zero return ("" if none). */
 const char* pa_last_error(void);
 

@@ -35,7 +35,7 @@ DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.int8: 2, torch.float8_e
 
 EXPORTS = (
     "pa_cache_write", "pa_decode", "pa_decode_splitk_reduce", "pa_decode_workspace_bytes",
-    "pa_choose_partition_size", "pa_last_error",
+    "pa_choose_partition_size", "pa_decode_check", "pa_cache_write_check", "pa_last_error",
 )
 
 
@@ -72,6 +72,10 @@ def load():
         lib.pa_decode_workspace_bytes.restype = SZ
         lib.pa_choose_partition_size.argtypes = [I32, I32, I32, I32, I32, I32, I32]
         lib.pa_choose_partition_size.restype = I32
+        lib.pa_decode_check.argtypes = [P, I32, P, I32, I32, I64, P, P]
+        lib.pa_decode_check.restype = ctypes.c_int
+        lib.pa_cache_write_check.argtypes = [P, I64, I64, I32, P, P]
+        lib.pa_cache_write_check.restype = ctypes.c_int
         lib.pa_last_error.argtypes = []
         lib.pa_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -172,6 +176,33 @@ def splitk_reduce(workspace: torch.Tensor, num_partitions: int, partition_size: 
     B, Tq, Hq, D = out.shape
     _check(load().pa_decode_splitk_reduce(_ptr(workspace), int(num_partitions), int(partition_size), B, Tq, Hq, D,
                                           _ptr(seq_lens), _ptr(out), _code(out), _ptr(lse), _stream(stream)))
+
+
+def decode_check(block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, num_blocks: int,
+                 status: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Debug check of the block table and lengths pa_decode trusts; returns the
+    device int32[2] status (violations, first flat index or -1), unsynchronised."""
+    for t, n in ((block_table, "block_table"), (seq_lens, "seq_lens"), (status, "status")):
+        _dev(t, n)
+    if status is None:
+        status = torch.empty(2, dtype=torch.int32, device=block_table.device)
+    B, max_blocks = block_table.shape
+    _check(load().pa_decode_check(_ptr(block_table), max_blocks, _ptr(seq_lens), B, int(max_seq_len),
+                                  int(num_blocks), _ptr(status), _stream(stream)))
+    return status
+
+
+def cache_write_check(slot_mapping: torch.Tensor, num_blocks: int, block_size: int = 16,
+                      status: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Debug check of slot_mapping for pa_cache_write; returns the device int32[2]
+    status (slots past the cache, first token index or -1), unsynchronised."""
+    for t, n in ((slot_mapping, "slot_mapping"), (status, "status")):
+        _dev(t, n)
+    if status is None:
+        status = torch.empty(2, dtype=torch.int32, device=slot_mapping.device)
+    _check(load().pa_cache_write_check(_ptr(slot_mapping), slot_mapping.numel(), int(num_blocks), int(block_size),
+                                       _ptr(status), _stream(stream)))
+    return status
 
 
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,

@@ -159,6 +159,41 @@ extern "C" {
 
 const char* pa_last_error(void) { return g_err.c_str(); }
 
+int pa_decode_check(const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t B,
+                    int32_t max_seq_len, int64_t num_blocks, int32_t* status, void* stream) {
+    if (!block_table || !seq_lens || !status) return fail(PA_ERR_NULL, "block_table, seq_lens and status must be non-NULL");
+    if (B < 0 || max_blocks_per_seq < 1 || max_seq_len < 0 || num_blocks < 1)
+        return fail(PA_ERR_SHAPE, "B=%d, max_blocks_per_seq=%d, max_seq_len=%d, num_blocks=%lld out of range", B,
+                    max_blocks_per_seq, max_seq_len, (long long)num_blocks);
+    pa::DecodeCheckParams p{};
+    p.block_table = block_table;
+    p.max_blocks = max_blocks_per_seq;
+    p.seq_lens = seq_lens;
+    p.B = B;
+    p.max_seq_len = max_seq_len;
+    p.num_blocks = num_blocks;
+    p.status = status;
+    hipError_t e = pa::launch_decode_check(p, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode_check launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int pa_cache_write_check(const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks, int32_t block_size,
+                         int32_t* status, void* stream) {
+    if (!status || (num_tokens > 0 && !slot_mapping)) return fail(PA_ERR_NULL, "slot_mapping and status must be non-NULL");
+    if (num_tokens < 0 || num_blocks < 1 || block_size < 1)
+        return fail(PA_ERR_SHAPE, "num_tokens=%lld, num_blocks=%lld, block_size=%d out of range", (long long)num_tokens,
+                    (long long)num_blocks, block_size);
+    pa::SlotsCheckParams p{};
+    p.slots = slot_mapping;
+    p.num_tokens = num_tokens;
+    p.num_slots = num_blocks * block_size;
+    p.status = status;
+    hipError_t e = pa::launch_slots_check(p, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "cache_write_check launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int32_t pa_choose_partition_size(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
                                  int32_t max_seq_len) {
     int rc = check_dims(B, Tq, Hq, Hkv, D);

@@ -54,6 +54,23 @@ struct CacheWriteParams {
     int Hkv, D;
 };
 
+struct DecodeCheckParams {
+    const int32_t* block_table;
+    int max_blocks;
+    const int32_t* seq_lens;
+    int B;
+    int max_seq_len;
+    int64_t num_blocks;
+    int32_t* status;  // [2]: violations, flat index of the first one (-1: none)
+};
+
+struct SlotsCheckParams {
+    const int64_t* slots;
+    int64_t num_tokens;
+    int64_t num_slots;  // num_blocks * block_size
+    int32_t* status;
+};
+
 // Launchers return hipSuccess or the launch error.
 hipError_t launch_decode_valu(int kv_type, int D, int GT, const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_wave(int kv_type, int D, int GT, const DecodeParams& p, hipStream_t stream);
@@ -61,6 +78,8 @@ hipError_t launch_decode_wave(int kv_type, int D, int GT, const DecodeParams& p,
 hipError_t launch_decode_mfma(int kv_type, int D, int NT, const DecodeParams& p, hipStream_t stream);
 hipError_t launch_splitk_reduce(const ReduceParams& p, hipStream_t stream);
 hipError_t launch_cache_write(int cache_type, const CacheWriteParams& p, hipStream_t stream);
+hipError_t launch_decode_check(const DecodeCheckParams& p, hipStream_t stream);
+hipError_t launch_slots_check(const SlotsCheckParams& p, hipStream_t stream);
 
 // Valid head-chunk widths of the VALU decode instances.
 bool decode_valu_has_gt(int GT);

@@ -151,6 +151,16 @@ def test_reduce_rejects_bad_arguments(lib):
     assert lib.pa_decode_splitk_reduce(A, 4, 512, 1, 1, 8, 128, A, odd, 0, None, None) == -7
 
 
+def test_checks_reject_bad_arguments(lib):
+    assert lib.pa_decode_check(None, 4, A, 2, 64, 16, A, None) == -1
+    assert lib.pa_decode_check(A, 4, A, 2, 64, 16, None, None) == -1
+    assert lib.pa_decode_check(A, 0, A, 2, 64, 16, A, None) == -2
+    assert lib.pa_decode_check(A, 4, A, -1, 64, 16, A, None) == -2
+    assert lib.pa_cache_write_check(A, 5, 4, 16, None, None) == -1
+    assert lib.pa_cache_write_check(A, -1, 4, 16, A, None) == -2
+    assert lib.pa_cache_write_check(A, 5, 0, 16, A, None) == -2
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(pa, "_LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(pa, "_lib", None)

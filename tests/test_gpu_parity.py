@@ -231,6 +231,37 @@ def test_splitk_reduce_entry_point_matches_decode():
     assert torch.equal(out, ref) and torch.equal(lse, rlse)
 
 
+def test_input_checks_find_planted_violations():
+    """pa_decode_check / pa_cache_write_check: clean inputs give (0, -1);
+    planted out-of-range block ids, lengths and slots are counted and the
+    first one is named. Only the table, lengths and slots are read."""
+    spec = scaled("gqa_bf16", B=3, Hq=4, Hkv=2, D=64, seq_lens=(40, 300))
+    w = generate(spec, seed=12)
+    q, table, lens = gpu_inputs(w)
+    nb, mb = w.num_blocks, w.block_table.shape[1]
+    st = pa.decode_check(table, lens, w.max_seq_len, nb)
+    assert st.cpu().tolist() == [0, -1]
+    bad_t = w.block_table.copy()
+    used1 = (int(w.seq_lens[1]) + 15) // 16
+    bad_t[1, used1 - 1] = nb  # one past the pool, in a used block of sequence 1
+    bad_t[2, 0] = -3
+    bad_t[0, mb - 1] = 10 ** 6  # past sequence 0's end (if unused): not read, not counted
+    bad_l = w.seq_lens.copy()
+    bad_l[2] = w.max_seq_len + 1  # longer than max_seq_len (its table row stays in bounds)
+    st = pa.decode_check(torch.from_numpy(bad_t).to(dev()), torch.from_numpy(bad_l).to(dev()), w.max_seq_len, nb)
+    flagged = [1 * (mb + 1) + used1 - 1, 2 * (mb + 1) + 0, 2 * (mb + 1) + mb]
+    if (int(w.seq_lens[0]) + 15) // 16 >= mb:  # sequence 0 uses its last entry
+        flagged.append(mb - 1)
+    got = st.cpu().tolist()
+    assert got == [len(flagged), min(flagged)], (got, flagged)
+    slots = torch.from_numpy(w.slot_mapping.copy()).to(dev())
+    assert pa.cache_write_check(slots, nb).cpu().tolist() == [0, -1]
+    slots[5] = nb * 16
+    slots[9] = -1  # skip: valid
+    slots[11] = nb * 16 + 100
+    assert pa.cache_write_check(slots, nb).cpu().tolist() == [2, 5]
+
+
 def test_fp8_cache_write_of_hand_derived_rows():
     """The hand-derived E4M3 rows (ties to even, subnormals, saturation, signed
     zero, all-zero row) written by the GPU equal the oracle writer's bits."""
