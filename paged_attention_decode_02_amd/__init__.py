@@ -88,10 +88,14 @@ def _check(rc: int):
         raise PaError(rc, msg.decode() if msg else "")
 
 
+def _L():
+    """The loaded library (the lock is taken only on the first call)."""
+    return _lib if _lib is not None else load()
+
+
 def _ptr(t: Optional[torch.Tensor]):
-    if t is None:
-        return None
-    return ctypes.c_void_p(t.data_ptr())
+    # a plain int: ctypes converts it for the c_void_p parameter
+    return None if t is None else t.data_ptr()
 
 
 def _dev(t: Optional[torch.Tensor], name: str):
@@ -102,9 +106,16 @@ def _dev(t: Optional[torch.Tensor], name: str):
             raise ValueError("%s must be contiguous" % name)
 
 
-def _stream(stream) -> ctypes.c_void_p:
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, t: Optional[torch.Tensor] = None) -> int:
+    """hipStream_t of `stream`, or of the current stream of t's device."""
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None and t is not None:
+        return _raw_stream(t.get_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _code(t: torch.Tensor) -> int:
@@ -124,9 +135,9 @@ def cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_
     if slot_mapping.dtype != torch.int64:
         raise ValueError("slot_mapping must be int64")
     nb, bs, Hkv, D = k_cache.shape
-    _check(load().pa_cache_write(_ptr(k), _ptr(v), _code(k), _ptr(slot_mapping), slot_mapping.numel(),
-                                 _ptr(k_cache), _ptr(v_cache), _code(k_cache), _ptr(k_scale), _ptr(v_scale), nb, bs,
-                                 Hkv, D, _stream(stream)))
+    _check(_L().pa_cache_write(_ptr(k), _ptr(v), _code(k), _ptr(slot_mapping), slot_mapping.numel(),
+                               _ptr(k_cache), _ptr(v_cache), _code(k_cache), _ptr(k_scale), _ptr(v_scale), nb, bs,
+                               Hkv, D, _stream(stream, k_cache)))
 
 
 def workspace_bytes(B: int, Tq: int, Hq: int, Hkv: int, D: int, kv_dtype: torch.dtype, max_seq_len: int,
@@ -161,10 +172,10 @@ def decode_partials(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int
     nb, bs, Hkv, _ = k_cache.shape
     np_ = ctypes.c_int32(0)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load().pa_decode(_ptr(q), _code(q), B, Tq, Hq, Hkv, D, _ptr(k_cache), _ptr(v_cache), _code(k_cache),
-                            _ptr(k_scale), _ptr(v_scale), nb, bs, _ptr(block_table), block_table.shape[1],
-                            _ptr(seq_lens), int(max_seq_len), float(softmax_scale), int(partition_size), _ptr(out),
-                            _code(out), _ptr(lse), _ptr(workspace), ws_bytes, ctypes.byref(np_), _stream(stream)))
+    _check(_L().pa_decode(_ptr(q), _code(q), B, Tq, Hq, Hkv, D, _ptr(k_cache), _ptr(v_cache), _code(k_cache),
+                          _ptr(k_scale), _ptr(v_scale), nb, bs, _ptr(block_table), block_table.shape[1],
+                          _ptr(seq_lens), int(max_seq_len), float(softmax_scale), int(partition_size), _ptr(out),
+                          _code(out), _ptr(lse), _ptr(workspace), ws_bytes, ctypes.byref(np_), _stream(stream, q)))
     return int(np_.value)
 
 
@@ -174,8 +185,8 @@ def splitk_reduce(workspace: torch.Tensor, num_partitions: int, partition_size: 
     for t, n in ((workspace, "workspace"), (seq_lens, "seq_lens"), (out, "out"), (lse, "lse")):
         _dev(t, n)
     B, Tq, Hq, D = out.shape
-    _check(load().pa_decode_splitk_reduce(_ptr(workspace), int(num_partitions), int(partition_size), B, Tq, Hq, D,
-                                          _ptr(seq_lens), _ptr(out), _code(out), _ptr(lse), _stream(stream)))
+    _check(_L().pa_decode_splitk_reduce(_ptr(workspace), int(num_partitions), int(partition_size), B, Tq, Hq, D,
+                                        _ptr(seq_lens), _ptr(out), _code(out), _ptr(lse), _stream(stream, out)))
 
 
 def decode_check(block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, num_blocks: int,
@@ -188,7 +199,7 @@ def decode_check(block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len:
         status = torch.empty(2, dtype=torch.int32, device=block_table.device)
     B, max_blocks = block_table.shape
     _check(load().pa_decode_check(_ptr(block_table), max_blocks, _ptr(seq_lens), B, int(max_seq_len),
-                                  int(num_blocks), _ptr(status), _stream(stream)))
+                                  int(num_blocks), _ptr(status), _stream(stream, status)))
     return status
 
 
@@ -201,7 +212,7 @@ def cache_write_check(slot_mapping: torch.Tensor, num_blocks: int, block_size: i
     if status is None:
         status = torch.empty(2, dtype=torch.int32, device=slot_mapping.device)
     _check(load().pa_cache_write_check(_ptr(slot_mapping), slot_mapping.numel(), int(num_blocks), int(block_size),
-                                       _ptr(status), _stream(stream)))
+                                       _ptr(status), _stream(stream, status)))
     return status
 
 
