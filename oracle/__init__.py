@@ -35,7 +35,7 @@ _LIB = os.path.join(_HERE, "_pa_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
-DTYPE_CODE = {"f32": 0, "bf16": 1, "i8": 2, "fp8": 3}
+DTYPE_CODE = {"f32": 0, "bf16": 1, "i8": 2, "fp8": 3, "nvfp4": 4}
 
 
 def build(force: bool = True) -> str:
@@ -70,6 +70,12 @@ def _load():
             lib.pa_oracle_fp8_value.restype = ctypes.c_double
             lib.pa_oracle_fp8_encode.argtypes = [F]
             lib.pa_oracle_fp8_encode.restype = I
+            lib.pa_oracle_e2m1_value.argtypes = [I]
+            lib.pa_oracle_e2m1_value.restype = ctypes.c_double
+            lib.pa_oracle_e2m1_encode.argtypes = [F]
+            lib.pa_oracle_e2m1_encode.restype = I
+            lib.pa_oracle_nvfp4_row_bytes.argtypes = [I]
+            lib.pa_oracle_nvfp4_row_bytes.restype = I
             _lib = lib
     return _lib
 
@@ -86,6 +92,24 @@ def max_threads() -> int:
     return int(_load().pa_oracle_max_threads())
 
 
+NVFP4_HEAD_DIMS = (64, 128, 256)  # where a row's byte count (48, 80, 144) differs from D
+
+
+def nvfp4_row_bytes(D: int) -> int:
+    """Bytes of one NVFP4 cache row: D/2 code bytes, D/16 block scales, padding to 16."""
+    if D not in NVFP4_HEAD_DIMS:
+        raise ValueError("NVFP4 caches need D in %s" % (NVFP4_HEAD_DIMS,))
+    return (D // 2 + D // 16 + 15) // 16 * 16
+
+
+def _cache_dtype(cache: np.ndarray, D: int) -> str:
+    """Cache dtype; uint8 rows of nvfp4_row_bytes(D) bytes (not D) are NVFP4."""
+    if cache.dtype == np.uint8 and D in NVFP4_HEAD_DIMS and cache.shape[-1] != D:
+        assert cache.shape[-1] == nvfp4_row_bytes(D), cache.shape
+        return "nvfp4"
+    return _dtype_of(cache)
+
+
 def _dtype_of(a: np.ndarray) -> str:
     if a.dtype == np.float32:
         return "f32"
@@ -100,12 +124,12 @@ def _dtype_of(a: np.ndarray) -> str:
 
 def alloc_cache(num_blocks: int, block_size: int, Hkv: int, D: int, cache_dtype: str):
     """Zeroed host cache arrays (k, v, k_scale, v_scale) in the cache layout."""
-    npdt = {"f32": np.float32, "bf16": np.uint16, "i8": np.int8, "fp8": np.uint8}[cache_dtype]
-    shape = (num_blocks, block_size, Hkv, D)
+    npdt = {"f32": np.float32, "bf16": np.uint16, "i8": np.int8, "fp8": np.uint8, "nvfp4": np.uint8}[cache_dtype]
+    shape = (num_blocks, block_size, Hkv, nvfp4_row_bytes(D) if cache_dtype == "nvfp4" else D)
     k = np.zeros(shape, npdt)
     v = np.zeros(shape, npdt)
     ks = vs = None
-    if cache_dtype in ("i8", "fp8"):
+    if cache_dtype in ("i8", "fp8", "nvfp4"):
         ks = np.zeros(shape[:3], np.float32)
         vs = np.zeros(shape[:3], np.float32)
     return k, v, ks, vs
@@ -121,16 +145,27 @@ def fp8_encode(y: float) -> int:
     return int(_load().pa_oracle_fp8_encode(ctypes.c_float(y)))
 
 
+def e2m1_value(code: int) -> float:
+    """The value an FP4 E2M1 code (0..15) stands for."""
+    return float(_load().pa_oracle_e2m1_value(int(code)))
+
+
+def e2m1_encode(y: float) -> int:
+    """FP4 E2M1 code of a binary32 value: nearest, ties to even, saturating at 6."""
+    return int(_load().pa_oracle_e2m1_encode(ctypes.c_float(y)))
+
+
 def cache_write(k_src: np.ndarray, v_src: np.ndarray, slot_mapping: np.ndarray, k_cache: np.ndarray,
                 v_cache: np.ndarray, k_scale: Optional[np.ndarray] = None,
                 v_scale: Optional[np.ndarray] = None) -> None:
     """Store source rows [N, Hkv, D] into the paged caches at slot_mapping (in place)."""
     lib = _load()
     src_dt = _dtype_of(k_src)
-    cache_dt = _dtype_of(k_cache)
+    cache_dt = _cache_dtype(k_cache, k_src.shape[-1])
     assert k_src.dtype == v_src.dtype and k_cache.dtype == v_cache.dtype
     assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
-    nb, bs, Hkv, D = k_cache.shape
+    nb, bs, Hkv, _ = k_cache.shape
+    D = k_src.shape[-1]
     k_src = _c(k_src, k_src.dtype)
     v_src = _c(v_src, v_src.dtype)
     slots = _c(slot_mapping, np.int64)
@@ -156,12 +191,12 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_table:
     lib = _load()
     q = np.ascontiguousarray(q)
     B, Tq, Hq, D = q.shape
-    nb, bs, Hkv, D2 = k_cache.shape
-    assert D2 == D and v_cache.shape == k_cache.shape
+    nb, bs, Hkv, _ = k_cache.shape
+    assert v_cache.shape == k_cache.shape
     table = _c(block_table, np.int32)
     lens = _c(seq_lens, np.int32)
     assert table.shape[0] == B and lens.shape == (B,)
-    kv_dt = _dtype_of(k_cache)
+    kv_dt = _cache_dtype(k_cache, D)
     out = np.full((B, Tq, Hq, D), np.nan)
     lse = np.full((B, Tq, Hq), np.nan)
     rows_arr = None if rows is None else _c(rows, np.int64)

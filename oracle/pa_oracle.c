@@ -25,6 +25,8 @@
  *  - FP8 KV cache (nvllm page, "Acknowledgments": b12x paged attention with
  *    FP8 KV dequantised inline; vllm-sm12x-nvfp4-dflash2 page, "What makes
  *    this stack different": FP8 KV as the common pairing with NVFP4 weights).
+ *  - NVFP4 KV cache (vllm-sm12x-nvfp4-dflash2 page, "What makes this stack
+ *    different": target weights, draft weights and the KV cache all NVFP4).
  *
  * Readings where the pages are silent (each also listed with the tests):
  *  - seq_lens counts the Tq new tokens, whose K/V are already in the cache;
@@ -41,6 +43,19 @@
  *    s = fp32(amax / 448); code = the finite E4M3 value nearest to
  *    y = fp32(x / s), ties to the even code, sign taken from y (so values
  *    beyond 448 saturate); amax = 0 gives s = 0 and all codes 0.
+ *  - NVFP4 is taken from NVIDIA's public description of the format (the
+ *    pages only name it): FP4 E2M1 elements (sign, 2 exponent bits with bias
+ *    1, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) in blocks of
+ *    16 consecutive elements, each block with an E4M3 scale, and a second
+ *    fp32 scale, here one per (token, kv head) as for int8 and FP8. For a row
+ *    x: S = fp32(amax / (6 * 448)); per block, u = fp32(fp32(amax_b / 6) / S),
+ *    s_b = its E4M3 code (the FP8 rule above), d_b = fp32(value(s_b) * S);
+ *    code = the E2M1 value nearest to fp32(x / d_b), ties to the even code,
+ *    the sign bit that of the quotient (magnitudes past 6 saturate), or 0
+ *    where d_b = 0; amax = 0 gives S = 0 and every code and block scale 0.
+ *    Dequantised value: value(code) * value(s_b) * S, exact in fp64. A cache
+ *    row is D/2 bytes of code pairs (element 2i in the low nibble of byte i),
+ *    then the D/16 block scales, then zero bytes up to a multiple of 16.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
  */
@@ -52,7 +67,11 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_I8 = 2, OR_FP8 = 3 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_I8 = 2, OR_FP8 = 3, OR_NVFP4 = 4 };
+
+/* Bytes of one NVFP4 cache row: D/2 code bytes, D/16 block scales, padding
+ * to a multiple of 16. */
+int pa_oracle_nvfp4_row_bytes(int D) { return (D / 2 + D / 16 + 15) / 16 * 16; }
 
 static float bits_to_float(uint32_t u) {
     float f;
@@ -122,6 +141,29 @@ int pa_oracle_fp8_encode(float y) {
     return fp8_encode_with(mag, y);
 }
 
+/* FP4 E2M1: the value a 4-bit code stands for. */
+double pa_oracle_e2m1_value(int code) {
+    const int sgn = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    const double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return sgn ? -mag : mag;
+}
+
+/* E2M1 code of a finite binary32 y: the magnitude (codes 0..7, increasing)
+ * nearest to |y|, a tie going to the even code; the sign bit is y's. */
+int pa_oracle_e2m1_encode(float y) {
+    const double a = fabs((double)y);
+    int best = 0;
+    double bd = a;
+    for (int c = 1; c < 8; ++c) {
+        const double d = fabs(pa_oracle_e2m1_value(c) - a);
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+            best = c;
+            bd = d;
+        }
+    }
+    return (signbit(y) ? 8 : 0) | best;
+}
+
 /* One element of a query or a source row, as the value it stands for. */
 static double elem(const void* base, int dtype, int64_t i) {
     switch (dtype) {
@@ -140,6 +182,11 @@ static double cache_elem(const void* cache, int dtype, const float* scale, int64
     case OR_BF16: return bf16_to_double(((const uint16_t*)cache)[i]);
     case OR_I8: return (double)((const int8_t*)cache)[i] * (double)scale[row];
     case OR_FP8: return pa_oracle_fp8_value(((const uint8_t*)cache)[i]) * (double)scale[row];
+    case OR_NVFP4: {
+        const uint8_t* r = (const uint8_t*)cache + row * (int64_t)pa_oracle_nvfp4_row_bytes(D);
+        const int code = (d & 1) ? r[d / 2] >> 4 : r[d / 2] & 15;
+        return pa_oracle_e2m1_value(code) * pa_oracle_fp8_value(r[D / 2 + d / 16]) * (double)scale[row];
+    }
     default: return NAN;
     }
 }
@@ -148,14 +195,18 @@ static double cache_elem(const void* cache, int dtype, const float* scale, int64
  * Cache writer. For every source token i with slot_mapping[i] >= 0 and every
  * kv head g, row x = src[i, g, :] goes to cache row (slot / bs, slot % bs, g).
  * f32->f32 and bf16->bf16 copy bits; bf16->f32 widens; f32->bf16 rounds to
- * nearest even; ->int8 and ->FP8 quantise symmetrically per (token, kv head).
+ * nearest even; ->int8, ->FP8 and ->NVFP4 quantise symmetrically per
+ * (token, kv head).
  * Returns 0, or -1 on an unsupported dtype pair.
  */
 int pa_oracle_cache_write(const void* k_src, const void* v_src, int src_dtype, const int64_t* slot_mapping,
                           int64_t num_tokens, void* k_cache, void* v_cache, int cache_dtype, float* k_scale,
                           float* v_scale, int64_t num_blocks, int block_size, int Hkv, int D) {
     if (src_dtype != OR_F32 && src_dtype != OR_BF16) return -1;
-    if (cache_dtype != OR_F32 && cache_dtype != OR_BF16 && cache_dtype != OR_I8 && cache_dtype != OR_FP8) return -1;
+    if (cache_dtype != OR_F32 && cache_dtype != OR_BF16 && cache_dtype != OR_I8 && cache_dtype != OR_FP8 &&
+        cache_dtype != OR_NVFP4)
+        return -1;
+    if (cache_dtype == OR_NVFP4 && D % 16) return -1;
     for (int64_t i = 0; i < num_tokens; ++i)
         if (slot_mapping[i] >= num_blocks * block_size) return -2;
     double fp8_mag[127];
@@ -208,6 +259,35 @@ int pa_oracle_cache_write(const void* k_src, const void* v_src, int src_dtype, c
                         int c = 0;
                         if (amax != 0.0f) c = fp8_encode_with(fp8_mag, x / s); /* binary32 quotient first */
                         ((uint8_t*)cache)[d0 + d] = (uint8_t)c;
+                    }
+                } else if (cache_dtype == OR_NVFP4) {
+                    const int rb = pa_oracle_nvfp4_row_bytes(D);
+                    uint8_t* r = (uint8_t*)cache + row * (int64_t)rb;
+                    memset(r, 0, (size_t)rb);
+                    float amax = 0.0f;
+                    for (int d = 0; d < D; ++d) {
+                        float ax = fabsf((float)elem(src, src_dtype, s0 + d));
+                        if (ax > amax) amax = ax;
+                    }
+                    const float S = amax / 2688.0f; /* 6 * 448, binary32 division */
+                    scale[row] = S;
+                    if (amax != 0.0f) {
+                        for (int b0 = 0; b0 < D; b0 += 16) {
+                            float bmax = 0.0f;
+                            for (int d = b0; d < b0 + 16; ++d) {
+                                float ax = fabsf((float)elem(src, src_dtype, s0 + d));
+                                if (ax > bmax) bmax = ax;
+                            }
+                            const float t = bmax / 6.0f;
+                            const int sb = fp8_encode_with(fp8_mag, t / S);
+                            r[D / 2 + b0 / 16] = (uint8_t)sb;
+                            const float db = (float)fp8_mag[sb & 127] * S; /* binary32 product */
+                            for (int d = b0; d < b0 + 16; ++d) {
+                                const float x = (float)elem(src, src_dtype, s0 + d);
+                                const int c = db != 0.0f ? pa_oracle_e2m1_encode(x / db) : 0;
+                                r[d / 2] |= (uint8_t)((d & 1) ? c << 4 : c);
+                            }
+                        }
                     }
                 } else if (cache_dtype == src_dtype) {
                     size_t eb = cache_dtype == OR_F32 ? 4 : 2;
@@ -348,7 +428,8 @@ static int check_args(const args_t* a) {
     if (!a->q || !a->k_cache || !a->v_cache || !a->block_table || !a->seq_lens) return -1;
     if (a->B < 0 || a->Tq < 1 || a->Hq < 1 || a->Hkv < 1 || a->D < 1 || a->block_size < 1) return -2;
     if (a->Hq % a->Hkv) return -2;
-    if ((a->kv_dtype == OR_I8 || a->kv_dtype == OR_FP8) && (!a->k_scale || !a->v_scale)) return -1;
+    if ((a->kv_dtype == OR_I8 || a->kv_dtype == OR_FP8 || a->kv_dtype == OR_NVFP4) && (!a->k_scale || !a->v_scale))
+        return -1;
     return 0;
 }
 

@@ -20,6 +20,32 @@ import numpy as np
 from workloads import bf16_bits_to_f32
 
 
+# NVFP4 rows: D/2 code bytes + D/16 block scales, padded to 16 bytes
+_NVFP4_D = {48: 64, 80: 128, 144: 256}
+
+
+def _e2m1(codes: np.ndarray) -> np.ndarray:
+    """FP4 E2M1 values: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0."""
+    s = np.where(codes & 8, -1.0, 1.0)
+    e = (codes >> 1) & 3
+    m = (codes & 1).astype(np.float64)
+    mag = np.where(e == 0, 0.5 * m, (1.0 + 0.5 * m) * np.exp2(e.astype(np.float64) - 1.0))
+    return s * mag
+
+
+def _nvfp4_f64(a: np.ndarray, scale: np.ndarray, D: int) -> np.ndarray:
+    """Decoded NVFP4 rows: E2M1 codes times their E4M3 block scale (decoded by
+    torch's float8_e4m3fn) times the row's fp32 scale."""
+    import torch
+
+    lo = (a[..., : D // 2] & 15).astype(np.int64)
+    hi = (a[..., : D // 2] >> 4).astype(np.int64)
+    codes = np.stack([lo, hi], axis=-1).reshape(a.shape[:-1] + (D,))
+    bsc = torch.from_numpy(np.ascontiguousarray(a[..., D // 2: D // 2 + D // 16])).view(torch.float8_e4m3fn)
+    bsc = bsc.to(torch.float64).numpy()
+    return _e2m1(codes) * np.repeat(bsc, 16, axis=-1) * scale.astype(np.float64)[..., None]
+
+
 def as_f64(a: np.ndarray, scale: Optional[np.ndarray] = None) -> np.ndarray:
     """Values of a cache/query array as float64 (int8 codes, or FP8 codes
     decoded by torch's float8_e4m3fn, times their row scale)."""
@@ -28,6 +54,8 @@ def as_f64(a: np.ndarray, scale: Optional[np.ndarray] = None) -> np.ndarray:
     if a.dtype == np.int8:
         assert scale is not None
         return a.astype(np.float64) * scale.astype(np.float64)[..., None]
+    if a.dtype == np.uint8 and a.shape[-1] in _NVFP4_D:
+        return _nvfp4_f64(a, scale, _NVFP4_D[a.shape[-1]])
     if a.dtype == np.uint8:
         import torch
 

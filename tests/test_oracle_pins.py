@@ -4,8 +4,8 @@ Each test checks the oracle against something it does not share code with:
 Decimal brute force, closed forms, dense attention via numpy, torch SDPA,
 invariances (block permutation, GQA as repeated MHA, causal rows as a virtual
 batch, split = unsplit, shared prefix = private copies, linearity, poison),
-hand-derived int8 and FP8 (OCP E4M3) quantiser cases, and torch's float8_e4m3fn
-conversions. A dropped term, wrong sign or index, or a
+hand-derived int8, FP8 (OCP E4M3) and NVFP4 quantiser cases, and torch's
+float8_e4m3fn conversions. A dropped term, wrong sign or index, or a
 transposed operand in the oracle fails at least one of them.
 """
 from __future__ import annotations
@@ -112,10 +112,10 @@ def test_uniform_weights_give_the_mean(how):
 
 
 # ------------------------------------------------------------ library / dense
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8", "fp8"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8", "fp8", "nvfp4"])
 def test_paged_equals_dense_contiguous(dtype):
-    spec = scaled("gqa_bf16", B=3, Tq=2, Hq=8, Hkv=2, D=32, seq_lens=(2, 200), src_dtype="f32",
-                  cache_dtype=dtype, q_dtype="bf16")
+    spec = scaled("gqa_bf16", B=3, Tq=2, Hq=8, Hkv=2, D=64 if dtype == "nvfp4" else 32, seq_lens=(2, 200),
+                  src_dtype="f32", cache_dtype=dtype, q_dtype="bf16")
     w = generate(spec, seed=4)
     cache = oracle_cache(w)
     out, lse = oracle_decode(w, cache)
@@ -219,9 +219,9 @@ def test_linear_in_values():
     assert np.max(np.abs(outs[2] - (2 * outs[0] + 0.5 * outs[1]))) <= 1e-12
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8", "fp8"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8", "fp8", "nvfp4"])
 def test_poisoned_slots_are_never_read(dtype):
-    spec = small(B=3, Tq=2, seq_lens=(5, 77), cache_dtype=dtype, src_dtype="f32")
+    spec = small(B=3, Tq=2, seq_lens=(5, 77), cache_dtype=dtype, src_dtype="f32", D=64 if dtype == "nvfp4" else 16)
     w = generate(spec, seed=14)
     clean = oracle_decode(w, oracle_cache(w, poison=False))
     dirty = oracle_decode(w, oracle_cache(w, poison=True))
@@ -426,6 +426,91 @@ def test_fp8_quantiser_bound_and_range():
     e = np.maximum(np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -30))), -6)
     half_step = 2.0 ** (e - 4)
     assert np.all(np.abs(y - vals) <= half_step + np.abs(y) * 2.0 ** -23)
+
+
+# ------------------------------------------------------------------- NVFP4
+def _nvfp4_golden():
+    with open(os.path.join(GOLDEN, "nvfp4_cases.json")) as f:
+        return json.load(f)
+
+
+def test_e2m1_golden_values_and_closed_form():
+    g = _nvfp4_golden()
+    for c in g["e2m1_values"]:
+        got = oracle.e2m1_value(c["code"])
+        assert got == c["value"] and np.signbit(got) == np.signbit(c["value"]), c
+    # closed form: (-1)^s * (e == 0 ? m / 2 : (1 + m / 2) * 2^(e - 1)) for code = s e e m
+    for code in range(16):
+        s_, e, m = code >> 3, (code >> 1) & 3, code & 1
+        want = (m / 2 if e == 0 else (1 + m / 2) * 2.0 ** (e - 1)) * (-1) ** s_
+        assert oracle.e2m1_value(code) == want
+
+
+def test_e2m1_rounding_golden_and_round_trip():
+    for c in _nvfp4_golden()["e2m1_rounding"]:
+        assert oracle.e2m1_encode(c["y"]) == c["code"], c["why"]
+    for code in range(16):
+        assert oracle.e2m1_encode(oracle.e2m1_value(code)) == code, code
+    # monotone in |y|, saturating, and never further from y than half a step
+    ys = np.linspace(0, 8, 4001, dtype=np.float32)
+    codes = [oracle.e2m1_encode(float(y)) for y in ys]
+    vals = np.array([oracle.e2m1_value(c) for c in codes])
+    assert np.all(np.diff(vals) >= 0) and vals.max() == 6.0
+    steps = np.array([0.5, 0.5, 0.5, 0.5, 1.0, 1.0, 2.0])  # gaps between consecutive magnitudes
+    edges = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6.0])
+    inside = ys <= 6
+    gap = steps[np.clip(np.searchsorted(edges, ys[inside], side="right") - 1, 0, 6)]
+    assert np.all(np.abs(vals[inside] - ys[inside]) <= gap / 2)
+
+
+def test_nvfp4_golden_row():
+    row = _nvfp4_golden()["row"]
+    D = 128
+    x = np.zeros(D, np.float32)
+    for b, blk in enumerate(row["blocks"]):
+        x[16 * b: 16 * b + len(blk["x"])] = blk["x"]
+    nb = 1
+    k, v, ks, vs = oracle.alloc_cache(nb, BLOCK_SIZE, 1, D, "nvfp4")
+    oracle.cache_write(x[None, None, :], x[None, None, :], np.array([0]), k, v, ks, vs)
+    r = k[0, 0, 0]
+    assert ks[0, 0, 0] == np.float32(row["row_scale"])
+    codes = np.stack([r[: D // 2] & 15, r[: D // 2] >> 4], axis=-1).reshape(D)
+    for b, blk in enumerate(row["blocks"]):
+        assert r[D // 2 + b] == blk["scale_code"], (b, r[D // 2 + b])
+        n = len(blk["codes"])
+        assert codes[16 * b: 16 * b + n].tolist() == blk["codes"], (b, blk)
+        assert np.all(codes[16 * b + n: 16 * b + 16] == 0)
+    assert np.all(r[D // 2 + D // 16:] == 0)  # padding
+
+
+def test_nvfp4_quantiser_bound():
+    rng = np.random.default_rng(43)
+    D = 256
+    x = rng.standard_normal((512, 1, D), dtype=np.float32)
+    x[:16] *= np.float32(1e-20)
+    x[16:32, :, :128] *= np.float32(1e4)  # blocks of very different magnitudes in one row
+    nb = 512 // BLOCK_SIZE
+    k, v, ks, vs = oracle.alloc_cache(nb, BLOCK_SIZE, 1, D, "nvfp4")
+    oracle.cache_write(x, x, np.arange(512), k, v, ks, vs)
+    rows = k.reshape(512, -1)
+    S = ks.reshape(512).astype(np.float64)
+    lo, hi = rows[:, : D // 2] & 15, rows[:, : D // 2] >> 4
+    codes = np.stack([lo, hi], -1).reshape(512, D)
+    e2 = np.array([oracle.e2m1_value(c) for c in range(16)])
+    sb = np.array([oracle.fp8_value(c) for c in range(256)])[rows[:, D // 2: D // 2 + D // 16]]
+    db = (np.repeat(sb, 16, axis=1) * S[:, None]).astype(np.float32).astype(np.float64)
+    y = x[:, 0].astype(np.float64) / np.where(db == 0, 1, db)
+    got = e2[codes]
+    # |y - value| <= half the E2M1 step at |y| (1/4 below 2, 1/2 below 4, 1 above),
+    # or the excess past 6 where a block scale rounded down
+    half = np.where(np.abs(y) < 2, 0.25, np.where(np.abs(y) < 4, 0.5, 1.0))
+    err = np.abs(y - got)
+    ok = (err <= half + np.abs(y) * 2.0 ** -22) | ((np.abs(y) > 6) & (np.abs(got) == 6))
+    assert np.all(ok | (db == 0))
+    # every row's largest magnitude lands on +-6 in a block scaled by 448 S
+    for i in range(512):
+        j = int(np.argmax(np.abs(x[i, 0])))
+        assert abs(got[i, j]) == 6.0 and sb[i, j // 16] == 448.0
 
 
 def test_bf16_and_f32_copies():

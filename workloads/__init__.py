@@ -45,7 +45,7 @@ import numpy as np
 BLOCK_SIZE = 16
 SLACK_BLOCKS = 64
 
-DTYPES = ("f32", "bf16", "i8", "fp8")
+DTYPES = ("f32", "bf16", "i8", "fp8", "nvfp4")
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -77,7 +77,7 @@ class Spec:
     seq_lens: Tuple[int, int]  # (lo, hi); lo == hi means constant
     q_dtype: str  # "f32" | "bf16"
     src_dtype: str  # dtype of the K/V source rows handed to the cache writer
-    cache_dtype: str  # "f32" | "bf16" | "i8" | "fp8" (OCP E4M3 codes)
+    cache_dtype: str  # "f32" | "bf16" | "i8" | "fp8" (OCP E4M3 codes) | "nvfp4"
     pool_blocks: int = 0  # >0: fixed pool size (tiny case); 0: sum of blocks + slack
     peaked_frac: float = 0.0  # fraction of key positions scaled by peak_factor
     peak_factor: float = 8.0
@@ -134,6 +134,17 @@ SPECS: Dict[str, Spec] = {
         "verify_fp8", B=4, Tq=8, Hq=24, Hkv=4, D=256, seq_lens=(16384, 32768),
         q_dtype="bf16", src_dtype="bf16", cache_dtype="fp8", shared_prefix=4096,
         description="speculative verify, 8 query tokens, 4096-token shared prefix, FP8 KV",
+    ),
+    # NVFP4 KV variants (E2M1 codes, E4M3 scale per 16 elements, fp32 row scale)
+    "nvfp4_250k": Spec(
+        "nvfp4_250k", B=1, Tq=1, Hq=24, Hkv=4, D=256, seq_lens=(250000, 250000),
+        q_dtype="bf16", src_dtype="f32", cache_dtype="nvfp4",
+        description="NVFP4-KV ultra-long decode, 250000 tokens, fp32 N(0,1) source",
+    ),
+    "verify_nvfp4": Spec(
+        "verify_nvfp4", B=4, Tq=8, Hq=24, Hkv=4, D=256, seq_lens=(16384, 32768),
+        q_dtype="bf16", src_dtype="bf16", cache_dtype="nvfp4", shared_prefix=4096,
+        description="speculative verify, 8 query tokens, 4096-token shared prefix, NVFP4 KV",
     ),
 }
 
@@ -323,6 +334,9 @@ def scaled(spec: Spec | str, **changes) -> Spec:
 
 def kv_bytes_per_token(spec: Spec) -> int:
     """Bytes of K and V (plus int8/FP8 scales) one context token costs per step."""
+    if spec.cache_dtype == "nvfp4":
+        # codes and block scales (D/2 + D/16 bytes), plus the fp32 row scale
+        return 2 * spec.Hkv * (spec.D // 2 + spec.D // 16 + 4)
     elt = {"f32": 4, "bf16": 2, "i8": 1, "fp8": 1}[spec.cache_dtype]
     b = 2 * spec.Hkv * spec.D * elt
     if spec.cache_dtype in ("i8", "fp8"):
