@@ -50,11 +50,13 @@ def algorithmic_bytes(w) -> dict:
     """Bytes the method must move per decode step (the split-K workspace is
     implementation overhead and is reported apart)."""
     sp = w.spec
-    elt = {"f32": 4, "bf16": 2, "i8": 1, "fp8": 1}[sp.cache_dtype]
     qelt = 4 if sp.q_dtype == "f32" else 2
     L = w.seq_lens.astype(np.int64)
-    kv = int(L.sum()) * sp.Hkv * sp.D * 2 * elt
-    scales = int(L.sum()) * sp.Hkv * 2 * 4 if sp.cache_dtype in ("i8", "fp8") else 0
+    if sp.cache_dtype == "nvfp4":  # E2M1 codes and E4M3 block scales (row padding excluded)
+        kv = int(L.sum()) * sp.Hkv * 2 * (sp.D // 2 + sp.D // 16)
+    else:
+        kv = int(L.sum()) * sp.Hkv * sp.D * 2 * {"f32": 4, "bf16": 2, "i8": 1, "fp8": 1}[sp.cache_dtype]
+    scales = int(L.sum()) * sp.Hkv * 2 * 4 if sp.cache_dtype in ("i8", "fp8", "nvfp4") else 0
     table = int(((L + 15) // 16).sum()) * 4
     q = sp.B * sp.Tq * sp.Hq * sp.D * qelt
     out = sp.B * sp.Tq * sp.Hq * (sp.D + 1) * 4
@@ -310,19 +312,22 @@ def main():
     w = generate(spec)
     log("generated %s in %.1f s" % (spec.name, time.time() - t0))
     sp = w.spec
-    TD = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "fp8": torch.float8_e4m3fn}
+    TD = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "fp8": torch.float8_e4m3fn,
+          "nvfp4": torch.float4_e2m1fn_x2}
 
     def up(a, dt):
         if dt == "bf16":
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    shape = (w.num_blocks, BLOCK_SIZE, sp.Hkv, sp.D)
-    kc = torch.zeros(shape, dtype=torch.uint8 if sp.cache_dtype == "fp8" else TD[sp.cache_dtype], device=dev)
-    kc = kc.view(TD[sp.cache_dtype])
+    row = (sp.D // 2 + sp.D // 16 + 15) // 16 * 16 if sp.cache_dtype == "nvfp4" else sp.D
+    shape = (w.num_blocks, BLOCK_SIZE, sp.Hkv, row)
+    byte_codes = sp.cache_dtype in ("fp8", "nvfp4")
+    kc = torch.zeros(shape, dtype=torch.uint8 if byte_codes else TD[sp.cache_dtype], device=dev)
     vc = torch.zeros_like(kc)
+    kc, vc = kc.view(TD[sp.cache_dtype]), vc.view(TD[sp.cache_dtype])
     ks = vs = None
-    if sp.cache_dtype in ("i8", "fp8"):
+    if sp.cache_dtype in ("i8", "fp8", "nvfp4"):
         ks = torch.zeros(shape[:3], dtype=torch.float32, device=dev)
         vs = torch.zeros_like(ks)
     N = w.slot_mapping.shape[0]

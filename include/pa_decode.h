@@ -38,9 +38,14 @@
  *    Query head h reads kv head h / (Hq / Hkv).
  *  - Supported: block_size 16; D in {64, 128, 256}; 1 <= Tq <= 16;
  *    Hq % Hkv == 0 and Hq / Hkv <= 64; q in {f32, bf16}; caches in
- *    {f32, bf16, i8, fp8}; out in {f32, bf16}. q, caches and out must be
- *    16-byte aligned; one KV block (16 * Hkv * D * element bytes) must be
- *    below 2^31 bytes.
+ *    {f32, bf16, i8, fp8, nvfp4}; out in {f32, bf16}. q, caches and out must
+ *    be 16-byte aligned; one KV block (16 * Hkv * row bytes) must be below
+ *    2^31 bytes.
+ *  - An NVFP4 cache row holds D/2 bytes of E2M1 code pairs (element 2i in
+ *    the low nibble of byte i), then D/16 E4M3 block scales (one per 16
+ *    consecutive elements), then zero padding to a multiple of 16 bytes
+ *    (48, 80 or 144 bytes for D = 64, 128, 256): caches are
+ *    [num_blocks, block_size, Hkv, row bytes].
  */
 #ifndef PA_DECODE_H
 #define PA_DECODE_H
@@ -55,7 +60,11 @@ extern "C" {
 /* PA_FP8: OCP FP8 E4M3 codes (sign, 4 exponent bits biased by 7, 3 mantissa
  * bits, no infinities, largest finite 448), the FP8 KV cache of the nvllm
  * page ("Acknowledgments", b12x: FP8 KV dequantised inline). */
-typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2, PA_FP8 = 3 } pa_dtype;
+/* PA_NVFP4: NVFP4 (the KV format of the vllm-sm12x-nvfp4-dflash2 page,
+ * "What makes this stack different"): FP4 E2M1 codes (magnitudes 0, 0.5, 1,
+ * 1.5, 2, 3, 4, 6) with an E4M3 scale per 16 elements and an fp32 scale per
+ * (token, kv head). */
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2, PA_FP8 = 3, PA_NVFP4 = 4 } pa_dtype;
 
 enum {
     PA_OK = 0,
@@ -80,14 +89,18 @@ enum {
  *   k_src, v_src   [num_tokens, Hkv, D] in src_dtype (f32 or bf16)
  *   slot_mapping   [num_tokens] int64, slot = block * block_size + offset
  *   k_cache, v_cache  caches in cache_dtype; k_scale, v_scale required iff
- *                  cache_dtype is PA_I8 or PA_FP8 (else pass NULL)
+ *                  cache_dtype is PA_I8, PA_FP8 or PA_NVFP4 (else pass NULL)
  * Conversions: same dtype copies bits; bf16 -> f32 widens exactly;
  * f32 -> bf16 rounds to nearest even; -> i8 is symmetric per (token, kv
  * head): s = fp32(max|x| / 127), code = clamp(rint_even(fp32(x / s)), -127,
  * 127); -> fp8 likewise against 448: s = fp32(max|x| / 448), code = the
  * E4M3 value nearest to fp32(x / s), ties to the even code, saturating at
- * +-448, the sign bit that of the quotient; for both, s = 0 with all codes 0
- * for an all-zero row. Bit-exact. Source values must be finite.
+ * +-448, the sign bit that of the quotient; -> nvfp4: S = fp32(max|x| / 2688)
+ * (the row's fp32 scale), per 16-element block u = fp32(fp32(max|x_b| / 6) /
+ * S), block scale = the E4M3 code of u (as for fp8), d = fp32(value * S), code
+ * = the E2M1 value nearest to fp32(x / d), ties to the even code, saturating
+ * at +-6, 0 where d = 0; for all three, an all-zero row gives scale 0 and all
+ * codes 0. Bit-exact. Source values must be finite.
  * Slots must lie in [0, num_blocks * block_size) and be distinct within one
  * call. num_tokens == 0 is a no-op.
  */
@@ -103,7 +116,7 @@ int pa_cache_write(const void* k_src, const void* v_src, pa_dtype src_dtype, con
  *   lse[b,t,h]   = log sum_j exp(softmax_scale * q . K_j),
  * where K_j, V_j are the rows of logical position j of sequence b, read
  * through block_table[b][j / block_size] (int8 and fp8: the code's value
- * times its row's scale). n <= 0 gives
+ * times its row's scale; nvfp4: times its block scale too). n <= 0 gives
  * out = 0 and lse = -inf. seq_lens counts the Tq new tokens, whose K/V must
  * already be in the cache (pa_cache_write). Arithmetic is fp32 (16-bit
  * operands: bf16, int8 codes and fp8 values widened exactly; fp32

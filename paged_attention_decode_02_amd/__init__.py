@@ -31,7 +31,8 @@ _lock = threading.Lock()
 _lib = None
 
 # FP8 caches hold OCP E4M3 codes (torch.float8_e4m3fn storage)
-DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.int8: 2, torch.float8_e4m3fn: 3}
+# NVFP4 caches: torch.float4_e2m1fn_x2 storage, [num_blocks, 16, Hkv, row bytes]
+DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.int8: 2, torch.float8_e4m3fn: 3, torch.float4_e2m1fn_x2: 4}
 
 EXPORTS = (
     "pa_cache_write", "pa_decode", "pa_decode_splitk_reduce", "pa_decode_workspace_bytes",
@@ -134,7 +135,8 @@ def cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_
         _dev(t, n)
     if slot_mapping.dtype != torch.int64:
         raise ValueError("slot_mapping must be int64")
-    nb, bs, Hkv, D = k_cache.shape
+    nb, bs, Hkv, _ = k_cache.shape
+    D = k.shape[-1]
     _check(_L().pa_cache_write(_ptr(k), _ptr(v), _code(k), _ptr(slot_mapping), slot_mapping.numel(),
                                _ptr(k_cache), _ptr(v_cache), _code(k_cache), _ptr(k_scale), _ptr(v_scale), nb, bs,
                                Hkv, D, _stream(stream, k_cache)))

@@ -7,9 +7,13 @@
 // and s = 0, codes 0 for an all-zero row. The FP8 variant (FP8 KV: nvllm
 // page, "Acknowledgments", b12x) stores OCP E4M3 codes the same way against
 // 448, the largest finite E4M3 magnitude: s = fp32(max|x| / 448), code = the
-// E4M3 value nearest to fp32(x / s), ties to even, saturating. Both
-// divisions are correctly rounded binary32 divisions, so the codes are
-// bit-exact.
+// E4M3 value nearest to fp32(x / s), ties to even, saturating. The NVFP4
+// variant (the KV format of the vllm-sm12x-nvfp4-dflash2 page, "What makes
+// this stack different") stores E2M1 codes with an E4M3 scale per 16
+// elements and an fp32 row scale: S = fp32(max|x| / 2688), per block
+// u = fp32(fp32(max|x_b| / 6) / S), s_b = E4M3(u), d_b = fp32(value(s_b) * S),
+// code = the E2M1 value nearest to fp32(x / d_b), ties to even. Every
+// division is correctly rounded binary32, so the codes are bit-exact.
 // A negative slot skips the token (padded rows must not write into other
 // requests' slots: vllm-sm70 page, "Known limitations").
 //
@@ -46,7 +50,42 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
         float x[EPL];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) x[e] = elem_f32<SRC_BF16 ? KV_BF16 : KV_F32>(raw[which], e);
-        if constexpr (CT == KV_F32) {
+        if constexpr (CT == KV_NVFP4) {
+            constexpr int RBQ = nvfp4_row_bytes(D);
+            constexpr int LPB = 16 / EPL;  // lanes per 16-element block
+            unsigned char* row = reinterpret_cast<unsigned char*>(cache) + dst_row * RBQ;
+            float la = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) la = fmaxf(la, fabsf(x[e]));
+            const float amax = wave_max(la);
+            float bmax = la;
+#pragma unroll
+            for (int off = 1; off < LPB; off <<= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, off));
+            const float S = __fdiv_rn(amax, 2688.0f);
+            uint32_t sb = 0;  // E4M3 code of the block scale
+            float d = 0.0f;   // the block's effective scale
+            if (amax != 0.0f) {
+                sb = f32x4_to_fp8x4(__fdiv_rn(__fdiv_rn(bmax, 6.0f), S), 0.0f, 0.0f, 0.0f) & 0xFFu;
+                d = __fmul_rn(fp8_value(sb), S);
+            }
+            uint32_t nib = 0;  // the lane's codes, element e in bits 4e .. 4e + 3
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const uint32_t c = d != 0.0f ? f32_to_e2m1(__fdiv_rn(x[e], d)) : 0u;
+                nib |= c << (4 * e);
+            }
+            if constexpr (EPL == 4) {
+                *reinterpret_cast<uint16_t*>(row + 2 * lane) = (uint16_t)nib;
+            } else if constexpr (EPL == 2) {
+                row[lane] = (unsigned char)nib;
+            } else {  // one element per lane: lane pairs share a byte
+                const uint32_t hi = __shfl_xor(nib, 1);
+                if ((lane & 1) == 0) row[lane / 2] = (unsigned char)(nib | (hi << 4));
+            }
+            if (lane % LPB == 0) row[D / 2 + lane / LPB] = (unsigned char)sb;
+            if (lane < RBQ - D / 2 - D / 16) row[D / 2 + D / 16 + lane] = 0;  // padding
+            if (lane == 0) (which ? p.v_scale : p.k_scale)[dst_row] = S;
+        } else if constexpr (CT == KV_F32) {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) reinterpret_cast<float*>(cache)[dst_off + e] = x[e];
         } else if constexpr (CT == KV_BF16) {
@@ -135,6 +174,7 @@ hipError_t launch_cache_write(int cache_type, const CacheWriteParams& p, hipStre
     case KV_BF16: return launch_ct<KV_BF16>(p.D, p, stream);
     case KV_I8: return launch_ct<KV_I8>(p.D, p, stream);
     case KV_FP8: return launch_ct<KV_FP8>(p.D, p, stream);
+    case KV_NVFP4: return launch_ct<KV_NVFP4>(p.D, p, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -103,11 +103,12 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 template <int KVT, int D, int NT, int QS>
 __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
-    static_assert(KVT == KV_BF16 || KVT == KV_I8 || KVT == KV_FP8, "bf16, int8 or fp8 caches");
+    static_assert(KVT == KV_BF16 || KVT == KV_I8 || KVT == KV_FP8 || KVT == KV_NVFP4, "bf16, int8, fp8 or nvfp4");
     static_assert(NT >= 1 && NT <= kW, "one row tile per wave");
     constexpr bool I8 = KVT == KV_I8;
     constexpr bool F8 = KVT == KV_FP8;
-    constexpr bool QNT = I8 || F8;  // codes with a per-(token, kv head) scale; f16 PV
+    constexpr bool F4 = KVT == KV_NVFP4;
+    constexpr bool QNT = I8 || F8 || F4;  // codes with a per-(token, kv head) scale; f16 PV
     constexpr int E = Elt<KVT>::bytes;
     constexpr int KS = D / 32;                 // k-steps of the score product
     constexpr int DW = D / kW;                 // output dims per wave
@@ -118,13 +119,14 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     constexpr int S2 = 2;
     // Global loads: wave w moves rows 4w .. 4w+3 of a block's K and V tiles,
     // as runs of whole rows (RB bytes each), GB bytes per lane and load
-    constexpr int RB = D * E;                        // bytes of one cache row
+    constexpr int RB = F4 ? D / 2 : D * E;           // code bytes of one cache row
+    constexpr int RBQ = kv_row_bytes<KVT>(D);        // row stride (nvfp4: + block scales, padding)
     constexpr int GB = RB / 16 >= 16 ? 16 : RB / 16;  // bytes per lane per load
     constexpr int NL = RB / 16 / GB;                 // loads per lane per tile
     // LDS tiles, row-major; keys as 16-bit elements (int8 codes widened to
     // f16), values as stored; the row pads spread the operand reads over banks
     constexpr int KRS = 2 * D + 16;  // bytes per staged key row
-    constexpr int VRS = RB + 32;     // bytes per staged value row
+    constexpr int VRS = (F4 ? 2 * D : RB) + 32;  // bytes per staged value row (nvfp4: f16)
 
     // [stage][block of the pair] ...
     __shared__ __align__(16) unsigned char kst[2][2][kBlockSize][KRS];  // staged keys
@@ -255,9 +257,9 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
         for (int nd = 0; nd < NDT; ++nd) o[t][nd] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int32_t* table = p.block_table + (int64_t)b * p.max_blocks;
-    const int64_t tok_stride = (int64_t)p.Hkv * D * E;
-    const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (int64_t)g * D * E;
-    const char* vbase = reinterpret_cast<const char*>(p.v_cache) + (int64_t)g * D * E;
+    const int64_t tok_stride = (int64_t)p.Hkv * RBQ;
+    const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (int64_t)g * RBQ;
+    const char* vbase = reinterpret_cast<const char*>(p.v_cache) + (int64_t)g * RBQ;
     const int j0 = start / kBlockSize, jend = (end + kBlockSize - 1) / kBlockSize;
     // physical block of logical block j (clamped to the partition)
     auto phys_of = [&](int j) -> int64_t { return (int64_t)table[j < jend ? j : jend - 1]; };
@@ -296,6 +298,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     const int npair = (jend - j0 + 1) / 2;
     struct Blk {
         Raw<GB> k[NL], v[NL];
+        Raw<1> ksb[F4 ? NL : 1], vsb[F4 ? NL : 1];  // nvfp4: block scale of the lane's 2 GB elements
         float sc;  // int8: lane l < 16 the key scale, 16 <= l < 32 the value scale of token l % 16
     };
     Blk ring[S2][2];
@@ -309,6 +312,11 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
             const int64_t off = (ph * kBlockSize + row_of(i)) * tok_stride + col_of(i);
             load_raw<GB, true>(dst.k[i], kbase + off);
             load_raw<GB, true>(dst.v[i], vbase + off);
+            if constexpr (F4) {
+                const int64_t sb = off - col_of(i) + RB + col_of(i) / 8;  // elements 2 col / 16
+                load_raw<1, true>(dst.ksb[i], kbase + sb);
+                load_raw<1, true>(dst.vsb[i], vbase + sb);
+            }
         }
         dst.sc = 1.0f;
         if constexpr (QNT) {
@@ -337,6 +345,27 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
                     *reinterpret_cast<u32x4*>(dst) = u32x4{f[0], f[1], f[2], f[3]};
                 } else {
                     *reinterpret_cast<u32x2*>(dst) = u32x2{f[0], f[1]};
+                }
+            } else if constexpr (F4) {
+                // E2M1 code pairs times the block scale -> bf16 (exact: at most
+                // 6 significant bits), four output bytes per code byte
+                const float sc = fp8_value(src.ksb[i].w[0]);
+                uint32_t f[GB];
+#pragma unroll
+                for (int b2 = 0; b2 < GB; ++b2) {
+                    const uint32_t wd = src.k[i].w[b2 / 4];
+                    const pa_f32x2 e = (b2 & 3) == 0 ? fp4x2_to_f32<0>(wd) : (b2 & 3) == 1 ? fp4x2_to_f32<1>(wd)
+                                       : (b2 & 3) == 2 ? fp4x2_to_f32<2>(wd) : fp4x2_to_f32<3>(wd);
+                    f[b2] = pack_bf16_rne(e.x * sc, e.y * sc);
+                }
+                unsigned char* d4 = &kst[stage][h][row_of(i)][col_of(i) * 4];
+                if constexpr (GB == 8) {
+                    reinterpret_cast<u32x4*>(d4)[0] = u32x4{f[0], f[1], f[2], f[3]};
+                    reinterpret_cast<u32x4*>(d4)[1] = u32x4{f[4], f[5], f[6], f[7]};
+                } else if constexpr (GB == 4) {
+                    *reinterpret_cast<u32x4*>(d4) = u32x4{f[0], f[1], f[2], f[3]};
+                } else {
+                    *reinterpret_cast<u32x2*>(d4) = u32x2{f[0], f[1]};
                 }
             } else if constexpr (F8) {
                 // E4M3 codes -> bf16 (exact), two output bytes per code
@@ -370,6 +399,29 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     auto store_v = [&](const Blk& src, int stage, int h) {
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
+            if constexpr (F4) {
+                // E2M1 code pairs times the block scale -> f16 (exact), read
+                // back by the 16-bit transposing LDS read as bf16 tiles are
+                const float sc = fp8_value(src.vsb[i].w[0]);
+                uint32_t f[GB];
+#pragma unroll
+                for (int b2 = 0; b2 < GB; ++b2) {
+                    const uint32_t wd = src.v[i].w[b2 / 4];
+                    const pa_f32x2 e = (b2 & 3) == 0 ? fp4x2_to_f32<0>(wd) : (b2 & 3) == 1 ? fp4x2_to_f32<1>(wd)
+                                       : (b2 & 3) == 2 ? fp4x2_to_f32<2>(wd) : fp4x2_to_f32<3>(wd);
+                    f[b2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(e.x * sc, e.y * sc));
+                }
+                unsigned char* d4 = &vst[stage][h][row_of(i)][col_of(i) * 4];
+                if constexpr (GB == 8) {
+                    reinterpret_cast<u32x4*>(d4)[0] = u32x4{f[0], f[1], f[2], f[3]};
+                    reinterpret_cast<u32x4*>(d4)[1] = u32x4{f[4], f[5], f[6], f[7]};
+                } else if constexpr (GB == 4) {
+                    *reinterpret_cast<u32x4*>(d4) = u32x4{f[0], f[1], f[2], f[3]};
+                } else {
+                    *reinterpret_cast<u32x2*>(d4) = u32x2{f[0], f[1]};
+                }
+                continue;
+            }
             unsigned char* dst = &vst[stage][h][row_of(i)][col_of(i)];
             if constexpr (GB == 16)
                 *reinterpret_cast<u32x4*>(dst) = u32x4{src.v[i].w[0], src.v[i].w[1], src.v[i].w[2], src.v[i].w[3]};
@@ -651,7 +703,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
             for (int nd = 0; nd < NDT; ++nd) {
                 float v = o[t][nd][i];
                 if constexpr (I8) v = (v - bias) * vsh_inv;
-                if constexpr (F8) v *= vsh_inv;
+                if constexpr (F8 || F4) v *= vsh_inv;
                 v *= inv;
                 const int d = wv * DW + 16 * nd + l16;
                 if (p.NP == 1) {
@@ -704,6 +756,8 @@ hipError_t launch_decode_mfma(int kv_type, int D, int NT, const DecodeParams& p,
     if (kv_type == KV_BF16) return qs == 1 ? by_d<KV_BF16, 1>(D, NT, p, stream) : by_d<KV_BF16, 2>(D, NT, p, stream);
     if (kv_type == KV_I8) return qs == 1 ? by_d<KV_I8, 1>(D, NT, p, stream) : by_d<KV_I8, 2>(D, NT, p, stream);
     if (kv_type == KV_FP8) return qs == 1 ? by_d<KV_FP8, 1>(D, NT, p, stream) : by_d<KV_FP8, 2>(D, NT, p, stream);
+    if (kv_type == KV_NVFP4)
+        return qs == 1 ? by_d<KV_NVFP4, 1>(D, NT, p, stream) : by_d<KV_NVFP4, 2>(D, NT, p, stream);
     return hipErrorInvalidValue;
 }
 

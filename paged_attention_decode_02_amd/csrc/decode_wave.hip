@@ -86,6 +86,12 @@ __device__ __forceinline__ float dot2_f16_first(uint32_t a, uint32_t b) {
     return r;
 }
 
+// Two floats as an f16 pair, rounded toward zero (exact for the values
+// packed here).
+__device__ __forceinline__ half2_t pkrtz_h2(float a, float b) {
+    return __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
 constexpr uint32_t kMagic = 0x64646464u;  // f16 0x64xx = 1024 + xx
 constexpr float kCodeBias = 1152.0f;      // 1024 + 128
 
@@ -148,12 +154,15 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 template <int KVT, int D, int GT, int QS>
 __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p) {
-    static_assert(KVT == KV_BF16 || KVT == KV_I8 || KVT == KV_FP8, "bf16, int8 or fp8 caches");
+    static_assert(KVT == KV_BF16 || KVT == KV_I8 || KVT == KV_FP8 || KVT == KV_NVFP4, "bf16, int8, fp8 or nvfp4");
     constexpr bool I8 = KVT == KV_I8;
     constexpr bool F8 = KVT == KV_FP8;
-    constexpr bool QNT = I8 || F8;  // codes with a per-(token, kv head) scale
+    constexpr bool F4 = KVT == KV_NVFP4;
+    constexpr bool QNT = I8 || F8 || F4;  // codes with a per-(token, kv head) scale
     constexpr int E = Elt<KVT>::bytes;
-    constexpr int KB = D * E / 16;  // key bytes per lane per token (QK layout)
+    constexpr int RBC = F4 ? D / 2 : D * E;      // code bytes of a row
+    constexpr int RBQ = kv_row_bytes<KVT>(D);    // row stride (nvfp4: + block scales, padding)
+    constexpr int KB = RBC / 16;    // key bytes per lane per token (QK layout)
     constexpr int KW = KB / 4;      // ... in dwords
     constexpr int QW = D / 32;      // q dwords (element pairs) per head per lane
     constexpr int NI = Split<GT>::kItems;
@@ -162,13 +171,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     // row, TPW rows per wave step. 512-byte rows with up to 6 heads use 16-byte
     // loads (measured faster there; more heads would not fit their outputs in
     // registers), everything else one row per wave (at least 4 bytes a lane).
-    constexpr int RB = D * E;  // row bytes
+    constexpr int RB = RBC;  // code bytes of a row
     constexpr int VB = (RB >= 512 && GT <= 6) ? 16 : (RB / 64 > 4 ? RB / 64 : 4);  // value bytes per lane per token
     constexpr int LPT = RB / VB;
     constexpr int TPW = 64 / LPT;
-    constexpr int EV = VB / E;    // value elements per lane per token
+    constexpr int EV = F4 ? 2 * VB : VB / E;  // value elements per lane per token
     constexpr int STEPS = kBlockSize / TPW;
-    static_assert(KB >= 4 && VB >= 4, "layout");
+    static_assert((F4 ? KB >= 2 : KB >= 4) && VB >= 4, "layout");
+    static_assert(!F4 || VB == 4, "nvfp4: a lane's value codes lie in one 16-element block");
     static_assert(STEPS % 2 == 0, "PV pairs tokens");
 
     __shared__ __align__(16) uint32_t pbuf_all[kWaves][kBlockSize / 2 * GP];
@@ -358,7 +368,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     // KV addressing: a buffer resource per block (scalar) plus per-lane
     // offsets that do not change from block to block; the host keeps a
     // block's bytes below 2^31
-    const int tok_stride = p.Hkv * D * E;  // bytes between consecutive tokens of a block
+    const int tok_stride = p.Hkv * RBQ;  // bytes between consecutive tokens of a block
     const int blk_bytes = kBlockSize * tok_stride;
     const char* kcache = reinterpret_cast<const char*>(p.k_cache);
     const char* vcache = reinterpret_cast<const char*>(p.v_cache);
@@ -385,10 +395,17 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     // K registers: register s holds slot s ^ sx (token 4 * (s ^ sx) + r)
     Raw<KB> kr[4];
     Raw<VB> vr[STEPS];
+    // nvfp4 block scales (E4M3 codes) of the lane's keys per slot and of its
+    // values per step: a lane's D/16 key elements and VB*2 value elements
+    // each lie in one 16-element block
+    Raw<1> ksb[F4 ? 4 : 1], vsb[F4 ? STEPS : 1];
     int koff[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) koff[s] = (4 * (s ^ sx) + r) * tok_stride + g * D * E + c16 * KB;
-    const int voff = 2 * vgrp * tok_stride + g * D * E + vl * VB;  // + the step's uniform token offset
+    for (int s = 0; s < 4; ++s) koff[s] = (4 * (s ^ sx) + r) * tok_stride + g * RBQ + c16 * KB;
+    const int voff = 2 * vgrp * tok_stride + g * RBQ + vl * VB;  // + the step's uniform token offset
+    // offsets of those block scales from the codes' offsets
+    const int ksb_off = RBC + c16 * (D / 16) / 16 - c16 * KB;
+    const int vsb_off = RBC + vl * VB * 2 / 16 - vl * VB;
     const int soff = (my_tok * p.Hkv + g) * 4;  // scale of the lane's token within a block's scales
     const int jw = j0 + sub;  // this wave's first block; it takes every WPH-th block
     int64_t phys = jw < jend ? (int64_t)table[jw] : 0;
@@ -396,12 +413,21 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
         const auto rs = range_rsrc(kcache + ph * blk_bytes, blk_bytes);
 #pragma unroll
         for (int s = 0; s < 4; ++s) load_buf<KB>(kr[s], rs, koff[s], 0);
+        if constexpr (F4) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) load_buf<1>(ksb[s], rs, koff[s] + ksb_off, 0);
+        }
     };
     auto load_v = [&](int64_t ph) {
         const auto rs = range_rsrc(vcache + ph * blk_bytes, blk_bytes);
 #pragma unroll
         for (int st = 0; st < STEPS; ++st)
             load_buf<VB>(vr[st], rs, voff, (2 * TPW * (st >> 1) + (st & 1)) * tok_stride);
+        if constexpr (F4) {
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st)
+                load_buf<1>(vsb[st], rs, voff + vsb_off, (2 * TPW * (st >> 1) + (st & 1)) * tok_stride);
+        }
     };
     if (jw < jend) load_k(phys);
 
@@ -445,6 +471,21 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
                             acc = dot2_f16(ql[h][2 * w + 1], f16pair_hi(u), acc);
                         }
                     }
+                } else if constexpr (F4) {
+                    // code byte b -> elements 2b, 2b + 1 as an exact bf16 pair;
+                    // the block scale multiplies the lane's partial sum
+#pragma unroll
+                    for (int b2 = 0; b2 < KB; ++b2) {
+                        const uint32_t wd = kr[s].w[b2 / 4];
+                        const pa_f32x2 f = (b2 & 3) == 0 ? fp4x2_to_f32<0>(wd)
+                                           : (b2 & 3) == 1 ? fp4x2_to_f32<1>(wd)
+                                           : (b2 & 3) == 2 ? fp4x2_to_f32<2>(wd)
+                                                           : fp4x2_to_f32<3>(wd);
+                        const uint32_t kp = pack_bf16_rne(f.x, f.y);
+                        acc = b2 == 0 ? dot2_bf16_first(qv[h][0], kp) : dot2_bf16(qv[h][b2], kp, acc);
+                        if constexpr (QS == 2) acc = dot2_bf16(ql[h][b2], kp, acc);
+                    }
+                    acc *= fp8_value(ksb[s].w[0]);
                 } else if constexpr (F8) {
 #pragma unroll
                     for (int w = 0; w < KW; ++w) {
@@ -572,6 +613,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
                     const bool ok = pos0 + tok_of(st) < end;
 #pragma unroll
                     for (int w = 0; w < VB / 4; ++w) vr[st].w[w] = ok ? vr[st].w[w] : 0u;
+                    if constexpr (F4) vsb[st].w[0] = ok ? vsb[st].w[0] : 0u;
                 }
             }
         }
@@ -598,6 +640,26 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
                         o[h][4 * w + 1] = dot2_f16(pp[h], f1, o[h][4 * w + 1]);
                         o[h][4 * w + 2] = dot2_f16(pp[h], f2, o[h][4 * w + 2]);
                         o[h][4 * w + 3] = dot2_f16(pp[h], f3, o[h][4 * w + 3]);
+                    }
+                } else if constexpr (F4) {
+                    // element e of tokens tk and tk + 1 times their block
+                    // scales as an f16 pair (exact: at most 6 significant bits)
+                    // (the codes packed first, then one packed f16 multiply
+                    // by the two tokens' scales)
+                    const half2_t sab = pkrtz_h2(fp8_value(vsb[st].w[0]), fp8_value(vsb[st + 1].w[0]));
+#pragma unroll
+                    for (int b2 = 0; b2 < 4; ++b2) {
+                        const pa_f32x2 a = b2 == 0 ? fp4x2_to_f32<0>(A) : b2 == 1 ? fp4x2_to_f32<1>(A)
+                                           : b2 == 2 ? fp4x2_to_f32<2>(A) : fp4x2_to_f32<3>(A);
+                        const pa_f32x2 bb = b2 == 0 ? fp4x2_to_f32<0>(B) : b2 == 1 ? fp4x2_to_f32<1>(B)
+                                            : b2 == 2 ? fp4x2_to_f32<2>(B) : fp4x2_to_f32<3>(B);
+                        const uint32_t f0 = __builtin_bit_cast(uint32_t, pkrtz_h2(a.x, bb.x) * sab);
+                        const uint32_t f1 = __builtin_bit_cast(uint32_t, pkrtz_h2(a.y, bb.y) * sab);
+#pragma unroll
+                        for (int h = 0; h < GT; ++h) {
+                            o[h][2 * b2 + 0] = dot2_f16(pp[h], f0, o[h][2 * b2 + 0]);
+                            o[h][2 * b2 + 1] = dot2_f16(pp[h], f1, o[h][2 * b2 + 1]);
+                        }
                     }
                 } else if constexpr (F8) {
                     // element e of tokens tk and tk + 1 as an f16 pair (exact:
@@ -669,7 +731,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
             for (int e = 0; e < EV; ++e) {
                 float acc = o[h][e];
                 if constexpr (I8) acc = (acc - kCodeBias * sh[h] * (1.0f / DUP)) * vsh_inv;
-                if constexpr (F8) acc *= vsh_inv;
+                if constexpr (F8 || F4) acc *= vsh_inv;
                 merge_o[wv][h][vl * EV + e] = acc;
             }
         }
@@ -771,6 +833,8 @@ hipError_t launch_decode_wave(int kv_type, int D, int GT, const DecodeParams& p,
     if (kv_type == KV_BF16) return qs == 1 ? by_d<KV_BF16, 1>(D, GT, p, stream) : by_d<KV_BF16, 2>(D, GT, p, stream);
     if (kv_type == KV_I8) return qs == 1 ? by_d<KV_I8, 1>(D, GT, p, stream) : by_d<KV_I8, 2>(D, GT, p, stream);
     if (kv_type == KV_FP8) return qs == 1 ? by_d<KV_FP8, 1>(D, GT, p, stream) : by_d<KV_FP8, 2>(D, GT, p, stream);
+    if (kv_type == KV_NVFP4)
+        return qs == 1 ? by_d<KV_NVFP4, 1>(D, GT, p, stream) : by_d<KV_NVFP4, 2>(D, GT, p, stream);
     return hipErrorInvalidValue;
 }
 

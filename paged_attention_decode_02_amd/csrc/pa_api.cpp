@@ -64,10 +64,18 @@ int waves_per_wg(pa_dtype kv_dtype) { return kv_dtype == PA_F32 ? 1 : 4; }
 
 // The matrix-core kernel takes all G*Tq rows of a kv head at once when they
 // fill at least one 16-row MFMA tile (bf16 and int8 caches).
-bool kv_supported(pa_dtype t) { return t == PA_F32 || t == PA_BF16 || t == PA_I8 || t == PA_FP8; }
+bool kv_supported(pa_dtype t) {
+    return t == PA_F32 || t == PA_BF16 || t == PA_I8 || t == PA_FP8 || t == PA_NVFP4;
+}
 
-// caches stored as 8-bit codes with one fp32 scale per (token, kv head)
-bool quantised(pa_dtype t) { return t == PA_I8 || t == PA_FP8; }
+// caches stored as codes with one fp32 scale per (token, kv head)
+bool quantised(pa_dtype t) { return t == PA_I8 || t == PA_FP8 || t == PA_NVFP4; }
+
+// bytes of one cache row of D elements
+int64_t row_bytes(pa_dtype t, int32_t D) {
+    if (t == PA_NVFP4) return (D / 2 + D / 16 + 15) / 16 * 16;
+    return (int64_t)D * (t == PA_F32 ? 4 : t == PA_BF16 ? 2 : 1);
+}
 
 bool use_mfma(int32_t Tq, int32_t Hq, int32_t Hkv, pa_dtype kv_dtype) {
     return kv_dtype != PA_F32 && (int64_t)(Hq / Hkv) * Tq >= 16;
@@ -105,7 +113,7 @@ int wgs_per_cu(pa_dtype kv_dtype, int32_t D, int GT, bool mfma) {
 // many for the reduce). Elsewhere one kv head, its blocks shared by the four
 // waves (short contexts need the finer split).
 int heads_per_wg(pa_dtype kv_dtype, int32_t D, int GT, int32_t Hkv) {
-    if ((kv_dtype == PA_I8 || kv_dtype == PA_FP8) && D * GT > 512) return Hkv % 2 == 0 ? 2 : 1;
+    if ((kv_dtype == PA_I8 || kv_dtype == PA_FP8 || kv_dtype == PA_NVFP4) && D * GT > 512) return Hkv % 2 == 0 ? 2 : 1;
     if (wgs_per_cu(kv_dtype, D, GT, false) != 1) return 1;
     return Hkv % 4 == 0 ? 4 : (Hkv % 2 == 0 ? 2 : 1);
 }
@@ -222,7 +230,7 @@ int pa_cache_write(const void* k_src, const void* v_src, pa_dtype src_dtype, con
     if (src_dtype != PA_F32 && src_dtype != PA_BF16)
         return fail(PA_ERR_DTYPE, "source dtype %d not in {f32, bf16}", (int)src_dtype);
     if (!kv_supported(cache_dtype))
-        return fail(PA_ERR_DTYPE, "cache dtype %d not in {f32, bf16, i8, fp8}", (int)cache_dtype);
+        return fail(PA_ERR_DTYPE, "cache dtype %d not in {f32, bf16, i8, fp8, nvfp4}", (int)cache_dtype);
     if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens=%lld must be >= 0", (long long)num_tokens);
     if (num_blocks < 1) return fail(PA_ERR_SHAPE, "num_blocks=%lld must be >= 1", (long long)num_blocks);
     if (block_size < 1 || Hkv < 1 || D < 1)
@@ -231,7 +239,7 @@ int pa_cache_write(const void* k_src, const void* v_src, pa_dtype src_dtype, con
     if (!supported_d(D)) return fail(PA_ERR_UNSUPPORTED, "D=%d not in {64, 128, 256}", D);
     if (!k_cache || !v_cache) return fail(PA_ERR_NULL, "k_cache/v_cache is NULL");
     if (quantised(cache_dtype) && (!k_scale || !v_scale))
-        return fail(PA_ERR_NULL, "int8/fp8 caches need k_scale and v_scale");
+        return fail(PA_ERR_NULL, "int8/fp8/nvfp4 caches need k_scale and v_scale");
     if (num_tokens == 0) return ok();
     if (!k_src || !v_src || !slot_mapping) return fail(PA_ERR_NULL, "k_src/v_src/slot_mapping is NULL");
     if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -263,14 +271,15 @@ int pa_decode(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq
     int rc = check_dims(B, Tq, Hq, Hkv, D);
     if (rc) return rc;
     if (q_dtype != PA_F32 && q_dtype != PA_BF16) return fail(PA_ERR_DTYPE, "q dtype %d not in {f32, bf16}", (int)q_dtype);
-    if (!kv_supported(kv_dtype)) return fail(PA_ERR_DTYPE, "kv dtype %d not in {f32, bf16, i8, fp8}", (int)kv_dtype);
+    if (!kv_supported(kv_dtype))
+        return fail(PA_ERR_DTYPE, "kv dtype %d not in {f32, bf16, i8, fp8, nvfp4}", (int)kv_dtype);
     if (out_dtype != PA_F32 && out_dtype != PA_BF16)
         return fail(PA_ERR_DTYPE, "out dtype %d not in {f32, bf16}", (int)out_dtype);
     if (block_size < 1) return fail(PA_ERR_SHAPE, "block_size=%d must be >= 1", block_size);
     if (block_size != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size=%d (only 16)", block_size);
     if (num_blocks < 1) return fail(PA_ERR_SHAPE, "num_blocks=%lld must be >= 1", (long long)num_blocks);
     // kernels address within one KV block with 32-bit offsets
-    const int64_t blk_bytes = (int64_t)kBlock * Hkv * D * (kv_dtype == PA_F32 ? 4 : kv_dtype == PA_BF16 ? 2 : 1);
+    const int64_t blk_bytes = (int64_t)kBlock * Hkv * row_bytes(kv_dtype, D);
     if (blk_bytes >= ((int64_t)1 << 31))
         return fail(PA_ERR_UNSUPPORTED, "a KV block of %lld bytes (Hkv=%d) exceeds 2^31", (long long)blk_bytes, Hkv);
     if (max_blocks_per_seq < 1) return fail(PA_ERR_SHAPE, "max_blocks_per_seq=%d must be >= 1", max_blocks_per_seq);
@@ -283,7 +292,7 @@ int pa_decode(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
         return fail(PA_ERR_NULL, "q, caches, block_table, seq_lens and out must be non-NULL");
     if (quantised(kv_dtype) && (!k_scale || !v_scale))
-        return fail(PA_ERR_NULL, "int8/fp8 caches need k_scale and v_scale");
+        return fail(PA_ERR_NULL, "int8/fp8/nvfp4 caches need k_scale and v_scale");
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
         return fail(PA_ERR_ALIGN, "q, caches and out must be 16-byte aligned");
 

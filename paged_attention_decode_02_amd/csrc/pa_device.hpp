@@ -8,7 +8,8 @@
 
 namespace pa {
 
-enum KvType : int { KV_F32 = 0, KV_BF16 = 1, KV_I8 = 2, KV_FP8 = 3 };  // KV_FP8: OCP E4M3 codes
+// KV_FP8: OCP E4M3 codes; KV_NVFP4: E2M1 code pairs + E4M3 scale per 16 elements
+enum KvType : int { KV_F32 = 0, KV_BF16 = 1, KV_I8 = 2, KV_FP8 = 3, KV_NVFP4 = 4 };
 
 constexpr int kBlockSize = 16;  // tokens per KV block
 constexpr int kWave = 64;
@@ -17,8 +18,18 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 template <int KVT>
 struct Elt {
-    static constexpr int bytes = KVT == KV_F32 ? 4 : (KVT == KV_BF16 ? 2 : 1);
+    static constexpr int bytes = KVT == KV_F32 ? 4 : (KVT == KV_BF16 ? 2 : 1);  // NVFP4: see nvfp4_row_bytes
 };
+
+// NVFP4 cache row: D/2 bytes of E2M1 code pairs (element 2i in the low nibble
+// of byte i), then the D/16 E4M3 block scales, then zero padding to 16 bytes.
+__host__ __device__ constexpr int nvfp4_row_bytes(int D) { return (D / 2 + D / 16 + 15) / 16 * 16; }
+
+// Bytes of one cache row of D elements.
+template <int KVT>
+__host__ __device__ constexpr int kv_row_bytes(int D) {
+    return KVT == KV_NVFP4 ? nvfp4_row_bytes(D) : D * Elt<KVT>::bytes;
+}
 
 // ---------------------------------------------------------------- raw loads
 // Load NB bytes (NB in {2, 4, 8, 16, 32, 64}) from a 16-byte-aligned (NB>=16)
@@ -59,9 +70,11 @@ __device__ __forceinline__ void load_raw(Raw<NB>& r, const void* p) {
         r.w[1] = v.y;
     } else if constexpr (NB == 4) {
         r.w[0] = ld<uint32_t, NT>(reinterpret_cast<const uint32_t*>(p));
-    } else {
-        static_assert(NB == 2, "unsupported load width");
+    } else if constexpr (NB == 2) {
         r.w[0] = ld<uint16_t, NT>(reinterpret_cast<const uint16_t*>(p));
+    } else {
+        static_assert(NB == 1, "unsupported load width");
+        r.w[0] = ld<uint8_t, NT>(reinterpret_cast<const uint8_t*>(p));
     }
 }
 
@@ -93,9 +106,13 @@ __device__ __forceinline__ void load_buf(Raw<NB>& r, __amdgpu_buffer_rsrc_t rs, 
         const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, kNT);
         r.w[0] = v.x;
         r.w[1] = v.y;
-    } else {
-        static_assert(NB == 4, "unsupported load width");
+    } else if constexpr (NB == 4) {
         r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, kNT);
+    } else if constexpr (NB == 2) {
+        r.w[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, kNT);
+    } else {
+        static_assert(NB == 1, "unsupported load width");
+        r.w[0] = __builtin_amdgcn_raw_buffer_load_b8(rs, voff, soff, kNT);
     }
 }
 
@@ -123,6 +140,28 @@ typedef __attribute__((ext_vector_type(2))) float pa_f32x2;
 template <bool HI>
 __device__ __forceinline__ pa_f32x2 fp8x2_to_f32(uint32_t w) {
     return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+}
+
+// Two FP4 E2M1 codes of w (byte SEL: element 2 SEL in the low nibble, 2 SEL + 1
+// in the high nibble) as fp32, exact. The conversion's scale operand takes
+// only a power of two (probed), so block scales are applied separately.
+template <int SEL>
+__device__ __forceinline__ pa_f32x2 fp4x2_to_f32(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+// The value of one E4M3 code (the low byte of b), exact.
+__device__ __forceinline__ float fp8_value(uint32_t b) { return fp8x2_to_f32<false>(b).x; }
+
+// fp32 -> FP4 E2M1 code (0..15): nearest magnitude of {0, 0.5, 1, 1.5, 2, 3,
+// 4, 6}, ties to the even code, sign from y, saturating at 6. The magnitude
+// code counts the decision points |y| has passed; at the tie points (0.25,
+// 0.75, ...) the comparison is strict or not so that the even code wins.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float y) {
+    const float a = fabsf(y);
+    const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+                       (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+    return m | (__float_as_uint(y) >> 31 << 3);
 }
 
 // Four fp32 values -> four OCP E4M3 codes (byte i = code of v[i]), nearest

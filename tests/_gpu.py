@@ -11,11 +11,13 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+import oracle
 import paged_attention_decode_02_amd as pa
 from _host import POISON_CODE
 from workloads import BLOCK_SIZE, Workload
 
-TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "fp8": torch.float8_e4m3fn}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "fp8": torch.float8_e4m3fn,
+            "nvfp4": torch.float4_e2m1fn_x2}
 
 
 def dev():
@@ -33,16 +35,17 @@ def dev_to_host(t: torch.Tensor) -> np.ndarray:
     t = t.detach().cpu()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
-    if t.dtype == torch.float8_e4m3fn:
+    if t.dtype in (torch.float8_e4m3fn, torch.float4_e2m1fn_x2):
         return t.view(torch.uint8).numpy()
     return t.numpy()
 
 
 def poisoned_cache(w: Workload):
     sp = w.spec
-    shape = (w.num_blocks, BLOCK_SIZE, sp.Hkv, sp.D)
+    row = oracle.nvfp4_row_bytes(sp.D) if sp.cache_dtype == "nvfp4" else sp.D
+    shape = (w.num_blocks, BLOCK_SIZE, sp.Hkv, row)
     dt = TORCH_DT[sp.cache_dtype]
-    if sp.cache_dtype in ("i8", "fp8"):
+    if sp.cache_dtype in ("i8", "fp8", "nvfp4"):
         k = torch.full(shape, POISON_CODE, dtype=torch.uint8, device=dev()).view(dt)
         ks = torch.full(shape[:3], float("nan"), dtype=torch.float32, device=dev())
         return k, k.clone(), ks, ks.clone()

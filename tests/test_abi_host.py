@@ -58,6 +58,7 @@ def decode_args(**over):
     (dict(num_partitions=None), -1),
     (dict(kv_dtype=2), -1),  # int8 without scales
     (dict(kv_dtype=3), -1),  # fp8 without scales
+    (dict(kv_dtype=4), -1),  # nvfp4 without scales
     (dict(q_dtype=2), -3),
     (dict(kv_dtype=7), -3),
     (dict(out_dtype=2), -3),
@@ -125,6 +126,7 @@ def test_workspace_size_and_partition_choice(lib):
     (dict(k_cache=None), -1),
     (dict(cache_dtype=2), -1),
     (dict(cache_dtype=3), -1),  # fp8 without scales
+    (dict(cache_dtype=4), -1),  # nvfp4 without scales
     (dict(num_tokens=-1), -2),
     (dict(k_src=ctypes.c_void_p(0x1008)), -7),
 ])

@@ -15,6 +15,7 @@ import torch
 
 import paged_attention_decode_02_amd as pa
 from _gpu import cache_bytes_equal, dev, dev_to_host, gpu_cache, gpu_decode, gpu_inputs, host_to_dev
+import oracle
 from _host import oracle_cache, oracle_decode
 from workloads import BLOCK_SIZE, SPECS, generate, scaled
 
@@ -22,7 +23,7 @@ pytestmark = pytest.mark.gpu
 
 # fp8: the int8 bound (the oracle dequantises the same codes, so the bound
 # covers only the kernel's 16-bit operands and fp32 sums, as for int8)
-TOL = {"f32": 1e-2, "bf16": 1e-2, "i8": 2e-2, "fp8": 2e-2}
+TOL = {"f32": 1e-2, "bf16": 1e-2, "i8": 2e-2, "fp8": 2e-2, "nvfp4": 2e-2}
 LSE_TOL = 1e-3
 
 
@@ -61,7 +62,7 @@ def run_workload(w, partition_size=0, check_cache=True):
 
 # ------------------------------------------------------------ full workloads
 @pytest.mark.parametrize("name", ["tiny_f32", "gqa_bf16", "long64k_bf16", "int8_250k", "verify_bf16", "verify_i8",
-                                  "fp8_250k", "verify_fp8"])
+                                  "fp8_250k", "verify_fp8", "nvfp4_250k", "verify_nvfp4"])
 def test_named_workload_full_size(name):
     w = generate(name)
     run_workload(w, partition_size=SPECS[name].partition_size)
@@ -73,7 +74,7 @@ def test_named_workload_full_size(name):
 
 
 # ------------------------------------------------------------ dtype / shape grid
-@pytest.mark.parametrize("kv", ["f32", "bf16", "i8", "fp8"])
+@pytest.mark.parametrize("kv", ["f32", "bf16", "i8", "fp8", "nvfp4"])
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("qdt", ["f32", "bf16"])
 def test_dtype_and_head_dim_grid(kv, D, qdt):
@@ -97,7 +98,7 @@ def test_partition_sizes(P):
 
 @pytest.mark.parametrize("Hkv", [1, 2, 3, 4, 6, 8])
 @pytest.mark.parametrize("P", [16, 0])
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "nvfp4"])
 def test_kv_heads_per_workgroup(Hkv, P, kv):
     # D=256, 6 heads per group: a workgroup takes 4 (bf16) or 2 (int8, fp8)
     # kv heads, or fewer as Hkv allows, one or more waves each; ragged and
@@ -118,7 +119,7 @@ def test_reduce_splits_columns_of_few_rows(D):
 
 
 @pytest.mark.parametrize("Tq", [2, 3, 8, 16])
-@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "nvfp4"])
 def test_query_tokens_causal(Tq, kv):
     spec = scaled("verify_bf16", B=3, Tq=Tq, Hq=8, Hkv=2, D=128, seq_lens=(Tq, 900), shared_prefix=0,
                   cache_dtype=kv)
@@ -266,7 +267,6 @@ def test_fp8_cache_write_of_hand_derived_rows():
     """The hand-derived E4M3 rows (ties to even, subnormals, saturation, signed
     zero, all-zero row) written by the GPU equal the oracle writer's bits."""
     import json
-    import oracle
 
     with open(os.path.join(os.path.dirname(__file__), "golden", "fp8_e4m3_cases.json")) as f:
         rows = json.load(f)["rows"]
@@ -291,8 +291,37 @@ def test_fp8_cache_write_of_hand_derived_rows():
         assert dev_to_host(k)[0, i, 0, :len(c["codes"])].tolist() == c["codes"], c["why"]
 
 
+def test_nvfp4_cache_write_of_the_hand_derived_row():
+    """The hand-derived NVFP4 row (ties to even, saturation, block scales
+    rounded to E4M3, zero blocks, padding) written by the GPU equals the oracle
+    writer's bytes and the hand-derived codes."""
+    import json
+
+    with open(os.path.join(os.path.dirname(__file__), "golden", "nvfp4_cases.json")) as f:
+        row = json.load(f)["row"]
+    D = 128
+    x = np.zeros((1, 1, D), np.float32)
+    for b, blk in enumerate(row["blocks"]):
+        x[0, 0, 16 * b: 16 * b + len(blk["x"])] = blk["x"]
+    hk, hv, hks, hvs = oracle.alloc_cache(1, BLOCK_SIZE, 1, D, "nvfp4")
+    oracle.cache_write(x, x, np.arange(1), hk, hv, hks, hvs)
+    RBQ = oracle.nvfp4_row_bytes(D)
+    k = torch.full((1, BLOCK_SIZE, 1, RBQ), 0x55, dtype=torch.uint8, device=dev()).view(torch.float4_e2m1fn_x2)
+    v = k.clone()
+    ks = torch.zeros((1, BLOCK_SIZE, 1), dtype=torch.float32, device=dev())
+    vs = ks.clone()
+    src = torch.from_numpy(x).to(dev())
+    pa.cache_write(src, src, torch.zeros(1, dtype=torch.int64, device=dev()), k, v, ks, vs)
+    torch.cuda.synchronize()
+    assert np.array_equal(dev_to_host(k)[0, 0], hk[0, 0]) and np.array_equal(dev_to_host(v)[0, 0], hv[0, 0])
+    assert ks.cpu().numpy()[0, 0, 0] == hks[0, 0, 0] == np.float32(row["row_scale"])
+    r = dev_to_host(k)[0, 0, 0]
+    for b, blk in enumerate(row["blocks"]):
+        assert r[D // 2 + b] == blk["scale_code"], b
+
+
 def test_cache_write_skips_negative_slots_and_writes_bits():
-    for cache_dtype in ("f32", "bf16", "i8", "fp8"):
+    for cache_dtype in ("f32", "bf16", "i8", "fp8", "nvfp4"):
         for src in ("f32", "bf16"):
             spec = scaled("gqa_bf16", B=2, Hq=4, Hkv=2, D=64, seq_lens=(30, 70), src_dtype=src,
                           cache_dtype=cache_dtype)
@@ -318,7 +347,8 @@ def test_cache_write_skips_negative_slots_and_writes_bits():
             b_ = w.row_seq[sk_rows]
             p_ = w.row_pos[sk_rows]
             sslots = w.block_table[b_, p_ // BLOCK_SIZE].astype(np.int64) * BLOCK_SIZE + p_ % BLOCK_SIZE
-            kc = dev_to_host(cache[0]).reshape(-1, spec.Hkv, spec.D)[sslots]
+            kc = dev_to_host(cache[0])
+            kc = kc.reshape(-1, spec.Hkv, kc.shape[-1])[sslots]
             if kc.dtype in (np.int8, np.uint8):
                 assert np.all(kc == 127)
             elif kc.dtype == np.uint16:
@@ -328,8 +358,8 @@ def test_cache_write_skips_negative_slots_and_writes_bits():
 
 
 # ------------------------------------------------------------ matrix-core path
-# G * Tq >= 16 rows per kv head (bf16 / int8 / fp8 caches) run on the MFMA kernel.
-@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
+# G * Tq >= 16 rows per kv head (bf16 / int8 / fp8 / nvfp4 caches) run on the MFMA kernel.
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "nvfp4"])
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("G, Tq", [(6, 8), (16, 1), (8, 16), (2, 8), (24, 3)])
 def test_mfma_rows(kv, D, G, Tq):
@@ -340,7 +370,7 @@ def test_mfma_rows(kv, D, G, Tq):
 
 
 @pytest.mark.parametrize("qdt", ["f32", "bf16"])
-@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "nvfp4"])
 def test_mfma_query_dtype_and_partitions(qdt, kv):
     spec = scaled("verify_bf16", B=3, Tq=8, Hq=12, Hkv=2, D=128, seq_lens=(8, 3000), shared_prefix=0,
                   cache_dtype=kv, q_dtype=qdt, src_dtype="f32")
