@@ -320,7 +320,7 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    row = (sp.D // 2 + sp.D // 16 + 15) // 16 * 16 if sp.cache_dtype == "nvfp4" else sp.D
+    row = sp.D // 2 + sp.D // 16 if sp.cache_dtype == "nvfp4" else sp.D  # nvfp4: bytes per (token, head)
     shape = (w.num_blocks, BLOCK_SIZE, sp.Hkv, row)
     byte_codes = sp.cache_dtype in ("fp8", "nvfp4")
     kc = torch.zeros(shape, dtype=torch.uint8 if byte_codes else TD[sp.cache_dtype], device=dev)

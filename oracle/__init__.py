@@ -92,18 +92,21 @@ def max_threads() -> int:
     return int(_load().pa_oracle_max_threads())
 
 
-NVFP4_HEAD_DIMS = (64, 128, 256)  # where a row's byte count (48, 80, 144) differs from D
+NVFP4_HEAD_DIMS = (64, 128, 256)  # where the bytes per (token, head), 36, 72, 144, differ from D
 
 
 def nvfp4_row_bytes(D: int) -> int:
-    """Bytes of one NVFP4 cache row: D/2 code bytes, D/16 block scales, padding to 16."""
+    """NVFP4 storage bytes per (token, kv head): D/2 of codes and D/16 of block
+    scales. An NVFP4 cache is a uint8 array [num_blocks, 16, Hkv, 9 D / 16]
+    whose blocks hold all code rows first and then the block-scale planes
+    (the layout is described in pa_oracle.c), so [b, t, h] is not row (t, h)."""
     if D not in NVFP4_HEAD_DIMS:
         raise ValueError("NVFP4 caches need D in %s" % (NVFP4_HEAD_DIMS,))
-    return (D // 2 + D // 16 + 15) // 16 * 16
+    return D // 2 + D // 16
 
 
 def _cache_dtype(cache: np.ndarray, D: int) -> str:
-    """Cache dtype; uint8 rows of nvfp4_row_bytes(D) bytes (not D) are NVFP4."""
+    """Cache dtype; uint8 arrays whose last dim is nvfp4_row_bytes(D), not D, are NVFP4."""
     if cache.dtype == np.uint8 and D in NVFP4_HEAD_DIMS and cache.shape[-1] != D:
         assert cache.shape[-1] == nvfp4_row_bytes(D), cache.shape
         return "nvfp4"

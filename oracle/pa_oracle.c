@@ -53,9 +53,13 @@
  *    code = the E2M1 value nearest to fp32(x / d_b), ties to the even code,
  *    the sign bit that of the quotient (magnitudes past 6 saturate), or 0
  *    where d_b = 0; amax = 0 gives S = 0 and every code and block scale 0.
- *    Dequantised value: value(code) * value(s_b) * S, exact in fp64. A cache
- *    row is D/2 bytes of code pairs (element 2i in the low nibble of byte i),
- *    then the D/16 block scales, then zero bytes up to a multiple of 16.
+ *    Dequantised value: value(code) * value(s_b) * S, exact in fp64.
+ *    Storage (this library's own; the pages fix none): a block of 16 tokens
+ *    and Hkv heads takes 9 * Hkv * D bytes. First the code rows of its
+ *    16 * Hkv (token, head) pairs, D/2 bytes each in (token, head) order,
+ *    element 2i in the low nibble of byte i; then one plane of D bytes per
+ *    head with that head's block scales: the scale of elements 16k .. 16k + 15
+ *    of token t at byte 16k + 4 (t mod 4) + t / 4 of the plane.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
  */
@@ -69,9 +73,21 @@
 
 enum { OR_F32 = 0, OR_BF16 = 1, OR_I8 = 2, OR_FP8 = 3, OR_NVFP4 = 4 };
 
-/* Bytes of one NVFP4 cache row: D/2 code bytes, D/16 block scales, padding
- * to a multiple of 16. */
-int pa_oracle_nvfp4_row_bytes(int D) { return (D / 2 + D / 16 + 15) / 16 * 16; }
+/* NVFP4 storage bytes per (token, kv head): D/2 of codes, D/16 of block
+ * scales (a block of 16 tokens is 16 * Hkv times this). */
+int pa_oracle_nvfp4_row_bytes(int D) { return D / 2 + D / 16; }
+
+/* Byte offsets, in an NVFP4 cache, of row `row`'s codes and of the scale of
+ * its elements 16k .. 16k + 15 (row = (block * 16 + t) * Hkv + h). */
+static int64_t nvfp4_code_offset(int64_t row, int Hkv, int D) {
+    const int64_t per = 16 * (int64_t)Hkv, blk = row / per;
+    return blk * 9 * Hkv * (int64_t)D + (row % per) * (D / 2);
+}
+static int64_t nvfp4_scale_offset(int64_t row, int Hkv, int D, int k) {
+    const int64_t per = 16 * (int64_t)Hkv, blk = row / per;
+    const int64_t t = (row % per) / Hkv, h = row % Hkv;
+    return blk * 9 * Hkv * (int64_t)D + per * (D / 2) + h * D + 16 * k + 4 * (t % 4) + t / 4;
+}
 
 static float bits_to_float(uint32_t u) {
     float f;
@@ -174,8 +190,9 @@ static double elem(const void* base, int dtype, int64_t i) {
 }
 
 /* Element d of cache row `row` (row = (block * bs + offset) * Hkv + g),
- * dequantised: for int8 and FP8 the exact product value(code) * scale in fp64. */
-static double cache_elem(const void* cache, int dtype, const float* scale, int64_t row, int D, int d) {
+ * dequantised: for int8, FP8 and NVFP4 the exact product of the code's value
+ * and its scales in fp64. */
+static double cache_elem(const void* cache, int dtype, const float* scale, int64_t row, int Hkv, int D, int d) {
     int64_t i = row * (int64_t)D + d;
     switch (dtype) {
     case OR_F32: return (double)((const float*)cache)[i];
@@ -183,9 +200,11 @@ static double cache_elem(const void* cache, int dtype, const float* scale, int64
     case OR_I8: return (double)((const int8_t*)cache)[i] * (double)scale[row];
     case OR_FP8: return pa_oracle_fp8_value(((const uint8_t*)cache)[i]) * (double)scale[row];
     case OR_NVFP4: {
-        const uint8_t* r = (const uint8_t*)cache + row * (int64_t)pa_oracle_nvfp4_row_bytes(D);
-        const int code = (d & 1) ? r[d / 2] >> 4 : r[d / 2] & 15;
-        return pa_oracle_e2m1_value(code) * pa_oracle_fp8_value(r[D / 2 + d / 16]) * (double)scale[row];
+        const uint8_t* c = (const uint8_t*)cache;
+        const uint8_t pair = c[nvfp4_code_offset(row, Hkv, D) + d / 2];
+        const int code = (d & 1) ? pair >> 4 : pair & 15;
+        return pa_oracle_e2m1_value(code) * pa_oracle_fp8_value(c[nvfp4_scale_offset(row, Hkv, D, d / 16)]) *
+               (double)scale[row];
     }
     default: return NAN;
     }
@@ -206,7 +225,7 @@ int pa_oracle_cache_write(const void* k_src, const void* v_src, int src_dtype, c
     if (cache_dtype != OR_F32 && cache_dtype != OR_BF16 && cache_dtype != OR_I8 && cache_dtype != OR_FP8 &&
         cache_dtype != OR_NVFP4)
         return -1;
-    if (cache_dtype == OR_NVFP4 && D % 16) return -1;
+    if (cache_dtype == OR_NVFP4 && (D % 16 || block_size != 16)) return -1;
     for (int64_t i = 0; i < num_tokens; ++i)
         if (slot_mapping[i] >= num_blocks * block_size) return -2;
     double fp8_mag[127];
@@ -261,9 +280,9 @@ int pa_oracle_cache_write(const void* k_src, const void* v_src, int src_dtype, c
                         ((uint8_t*)cache)[d0 + d] = (uint8_t)c;
                     }
                 } else if (cache_dtype == OR_NVFP4) {
-                    const int rb = pa_oracle_nvfp4_row_bytes(D);
-                    uint8_t* r = (uint8_t*)cache + row * (int64_t)rb;
-                    memset(r, 0, (size_t)rb);
+                    uint8_t* r = (uint8_t*)cache + nvfp4_code_offset(row, Hkv, D);
+                    memset(r, 0, (size_t)(D / 2));
+                    for (int k = 0; k < D / 16; ++k) ((uint8_t*)cache)[nvfp4_scale_offset(row, Hkv, D, k)] = 0;
                     float amax = 0.0f;
                     for (int d = 0; d < D; ++d) {
                         float ax = fabsf((float)elem(src, src_dtype, s0 + d));
@@ -280,7 +299,7 @@ int pa_oracle_cache_write(const void* k_src, const void* v_src, int src_dtype, c
                             }
                             const float t = bmax / 6.0f;
                             const int sb = fp8_encode_with(fp8_mag, t / S);
-                            r[D / 2 + b0 / 16] = (uint8_t)sb;
+                            ((uint8_t*)cache)[nvfp4_scale_offset(row, Hkv, D, b0 / 16)] = (uint8_t)sb;
                             const float db = (float)fp8_mag[sb & 127] * S; /* binary32 product */
                             for (int d = b0; d < b0 + 16; ++d) {
                                 const float x = (float)elem(src, src_dtype, s0 + d);
@@ -327,7 +346,7 @@ static void row_logits(const args_t* a, int b, int t, int h, int64_t n, double* 
         int64_t row = (blk * a->block_size + j % a->block_size) * a->Hkv + g;
         double dot = 0.0;
         for (int d = 0; d < a->D; ++d)
-            dot += elem(a->q, a->q_dtype, qoff + d) * cache_elem(a->k_cache, a->kv_dtype, a->k_scale, row, a->D, d);
+            dot += elem(a->q, a->q_dtype, qoff + d) * cache_elem(a->k_cache, a->kv_dtype, a->k_scale, row, a->Hkv, a->D, d);
         s[j] = (double)a->softmax_scale * dot;
     }
 }
@@ -335,7 +354,7 @@ static void row_logits(const args_t* a, int b, int t, int h, int64_t n, double* 
 static void value_row_axpy(const args_t* a, int b, int g, int64_t j, double w, double* acc) {
     int64_t blk = a->block_table[(int64_t)b * a->max_blocks + j / a->block_size];
     int64_t row = (blk * a->block_size + j % a->block_size) * a->Hkv + g;
-    for (int d = 0; d < a->D; ++d) acc[d] += w * cache_elem(a->v_cache, a->kv_dtype, a->v_scale, row, a->D, d);
+    for (int d = 0; d < a->D; ++d) acc[d] += w * cache_elem(a->v_cache, a->kv_dtype, a->v_scale, row, a->Hkv, a->D, d);
 }
 
 /* Number of keys query token t of sequence b sees (causal inside the Tq new
@@ -428,6 +447,7 @@ static int check_args(const args_t* a) {
     if (!a->q || !a->k_cache || !a->v_cache || !a->block_table || !a->seq_lens) return -1;
     if (a->B < 0 || a->Tq < 1 || a->Hq < 1 || a->Hkv < 1 || a->D < 1 || a->block_size < 1) return -2;
     if (a->Hq % a->Hkv) return -2;
+    if (a->kv_dtype == OR_NVFP4 && (a->D % 16 || a->block_size != 16)) return -2;
     if ((a->kv_dtype == OR_I8 || a->kv_dtype == OR_FP8 || a->kv_dtype == OR_NVFP4) && (!a->k_scale || !a->v_scale))
         return -1;
     return 0;

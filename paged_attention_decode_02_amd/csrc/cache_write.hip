@@ -51,9 +51,12 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) x[e] = elem_f32<SRC_BF16 ? KV_BF16 : KV_F32>(raw[which], e);
         if constexpr (CT == KV_NVFP4) {
-            constexpr int RBQ = nvfp4_row_bytes(D);
             constexpr int LPB = 16 / EPL;  // lanes per 16-element block
-            unsigned char* row = reinterpret_cast<unsigned char*>(cache) + dst_row * RBQ;
+            const int64_t blk = slot / kBlockSize;
+            const int t = (int)(slot % kBlockSize);
+            unsigned char* base = reinterpret_cast<unsigned char*>(cache) + blk * 9 * p.Hkv * D;
+            unsigned char* row = base + ((int64_t)t * p.Hkv + g) * (D / 2);
+            unsigned char* plane = base + (int64_t)kBlockSize * p.Hkv * (D / 2) + (int64_t)g * D;
             float la = 0.0f;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) la = fmaxf(la, fabsf(x[e]));
@@ -82,8 +85,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
                 const uint32_t hi = __shfl_xor(nib, 1);
                 if ((lane & 1) == 0) row[lane / 2] = (unsigned char)(nib | (hi << 4));
             }
-            if (lane % LPB == 0) row[D / 2 + lane / LPB] = (unsigned char)sb;
-            if (lane < RBQ - D / 2 - D / 16) row[D / 2 + D / 16 + lane] = 0;  // padding
+            if (lane % LPB == 0) plane[nvfp4_scale_byte(t, lane / LPB)] = (unsigned char)sb;
             if (lane == 0) (which ? p.v_scale : p.k_scale)[dst_row] = S;
         } else if constexpr (CT == KV_F32) {
 #pragma unroll

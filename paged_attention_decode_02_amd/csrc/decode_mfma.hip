@@ -120,7 +120,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     // Global loads: wave w moves rows 4w .. 4w+3 of a block's K and V tiles,
     // as runs of whole rows (RB bytes each), GB bytes per lane and load
     constexpr int RB = F4 ? D / 2 : D * E;           // code bytes of one cache row
-    constexpr int RBQ = kv_row_bytes<KVT>(D);        // row stride (nvfp4: + block scales, padding)
+    constexpr int RBQ = kv_code_row_bytes<KVT>(D);   // row stride within a block (code bytes)
     constexpr int GB = RB / 16 >= 16 ? 16 : RB / 16;  // bytes per lane per load
     constexpr int NL = RB / 16 / GB;                 // loads per lane per tile
     // LDS tiles, row-major; keys as 16-bit elements (int8 codes widened to
@@ -258,8 +258,12 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
 
     const int32_t* table = p.block_table + (int64_t)b * p.max_blocks;
     const int64_t tok_stride = (int64_t)p.Hkv * RBQ;
+    const int64_t blk_bytes = kBlockSize * (int64_t)p.Hkv * kv_row_bytes<KVT>(D);  // nvfp4: + scale planes
     const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (int64_t)g * RBQ;
     const char* vbase = reinterpret_cast<const char*>(p.v_cache) + (int64_t)g * RBQ;
+    // nvfp4: this head's scale plane in a block; byte 16 k + 4 r + q holds the
+    // scale of elements 16 k .. 16 k + 15 of token 4 q + r
+    const int64_t plane = kBlockSize * tok_stride + (int64_t)g * D - (int64_t)g * RBQ;  // from kbase
     const int j0 = start / kBlockSize, jend = (end + kBlockSize - 1) / kBlockSize;
     // physical block of logical block j (clamped to the partition)
     auto phys_of = [&](int j) -> int64_t { return (int64_t)table[j < jend ? j : jend - 1]; };
@@ -298,7 +302,9 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     const int npair = (jend - j0 + 1) / 2;
     struct Blk {
         Raw<GB> k[NL], v[NL];
-        Raw<1> ksb[F4 ? NL : 1], vsb[F4 ? NL : 1];  // nvfp4: block scale of the lane's 2 GB elements
+        // nvfp4: the scales of the lane's row (4 q + r, r = lane / 16) for
+        // q = 0..3 in the 16-element block of its 2 GB elements; q is the wave
+        Raw<4> ksw, vsw;
         float sc;  // int8: lane l < 16 the key scale, 16 <= l < 32 the value scale of token l % 16
     };
     Blk ring[S2][2];
@@ -309,14 +315,15 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     auto load_blk = [&](Blk& dst, int64_t ph) {
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            const int64_t off = (ph * kBlockSize + row_of(i)) * tok_stride + col_of(i);
+            const int64_t off = ph * blk_bytes + row_of(i) * tok_stride + col_of(i);
             load_raw<GB, true>(dst.k[i], kbase + off);
             load_raw<GB, true>(dst.v[i], vbase + off);
-            if constexpr (F4) {
-                const int64_t sb = off - col_of(i) + RB + col_of(i) / 8;  // elements 2 col / 16
-                load_raw<1, true>(dst.ksb[i], kbase + sb);
-                load_raw<1, true>(dst.vsb[i], vbase + sb);
-            }
+        }
+        if constexpr (F4) {
+            static_assert(NL == 1, "nvfp4: one load per lane per tile");
+            const int64_t sb = ph * blk_bytes + plane + 16 * (col_of(0) / 8) + 4 * (row_of(0) & 3);
+            load_raw<4, true>(dst.ksw, kbase + sb);
+            load_raw<4, true>(dst.vsw, vbase + sb);
         }
         dst.sc = 1.0f;
         if constexpr (QNT) {
@@ -349,7 +356,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
             } else if constexpr (F4) {
                 // E2M1 code pairs times the block scale -> bf16 (exact: at most
                 // 6 significant bits), four output bytes per code byte
-                const float sc = fp8_value(src.ksb[i].w[0]);
+                const float sc = fp8_value(src.ksw.w[0] >> (8 * wv));
                 uint32_t f[GB];
 #pragma unroll
                 for (int b2 = 0; b2 < GB; ++b2) {
@@ -402,7 +409,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
             if constexpr (F4) {
                 // E2M1 code pairs times the block scale -> f16 (exact), read
                 // back by the 16-bit transposing LDS read as bf16 tiles are
-                const float sc = fp8_value(src.vsb[i].w[0]);
+                const float sc = fp8_value(src.vsw.w[0] >> (8 * wv));
                 uint32_t f[GB];
 #pragma unroll
                 for (int b2 = 0; b2 < GB; ++b2) {

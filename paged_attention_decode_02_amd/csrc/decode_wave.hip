@@ -161,7 +161,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     constexpr bool QNT = I8 || F8 || F4;  // codes with a per-(token, kv head) scale
     constexpr int E = Elt<KVT>::bytes;
     constexpr int RBC = F4 ? D / 2 : D * E;      // code bytes of a row
-    constexpr int RBQ = kv_row_bytes<KVT>(D);    // row stride (nvfp4: + block scales, padding)
+    constexpr int RBQ = kv_code_row_bytes<KVT>(D);  // row stride within a block (code bytes)
     constexpr int KB = RBC / 16;    // key bytes per lane per token (QK layout)
     constexpr int KW = KB / 4;      // ... in dwords
     constexpr int QW = D / 32;      // q dwords (element pairs) per head per lane
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     // offsets that do not change from block to block; the host keeps a
     // block's bytes below 2^31
     const int tok_stride = p.Hkv * RBQ;  // bytes between consecutive tokens of a block
-    const int blk_bytes = kBlockSize * tok_stride;
+    const int blk_bytes = kBlockSize * p.Hkv * kv_row_bytes<KVT>(D);  // nvfp4: + the scale planes
     const char* kcache = reinterpret_cast<const char*>(p.k_cache);
     const char* vcache = reinterpret_cast<const char*>(p.v_cache);
     const int j0 = start / kBlockSize, jend = (end + kBlockSize - 1) / kBlockSize;
@@ -395,17 +395,23 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     // K registers: register s holds slot s ^ sx (token 4 * (s ^ sx) + r)
     Raw<KB> kr[4];
     Raw<VB> vr[STEPS];
-    // nvfp4 block scales (E4M3 codes) of the lane's keys per slot and of its
-    // values per step: a lane's D/16 key elements and VB*2 value elements
-    // each lie in one 16-element block
-    Raw<1> ksb[F4 ? 4 : 1], vsb[F4 ? STEPS : 1];
+    // nvfp4 block scales (E4M3 codes). A lane's D/16 key elements and 2 VB
+    // value elements each lie in one 16-element block k; in the head's scale
+    // plane of a block, byte 16 k + 4 r' + q' is token 4 q' + r', so the
+    // lane's keys (tokens 4 q' + r, q' = slot ^ sx) are the dword at 16 k + 4 r
+    // and its values (tokens 2 TPW (st >> 1) + 2 vgrp + (st & 1)) the bytes
+    // TPW/2 (st >> 1) + (vgrp >> 1) of the two dwords at 16 k + 8 (vgrp & 1)
+    Raw<4> ksw;
+    Raw<8> vsw;
     int koff[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) koff[s] = (4 * (s ^ sx) + r) * tok_stride + g * RBQ + c16 * KB;
     const int voff = 2 * vgrp * tok_stride + g * RBQ + vl * VB;  // + the step's uniform token offset
-    // offsets of those block scales from the codes' offsets
-    const int ksb_off = RBC + c16 * (D / 16) / 16 - c16 * KB;
-    const int vsb_off = RBC + vl * VB * 2 / 16 - vl * VB;
+    const int plane = kBlockSize * tok_stride + g * D;  // this head's block scales
+    const int ksw_off = plane + 16 * (c16 * KB / 8) + 4 * r;
+    const int vsw_off = plane + 16 * (vl * VB / 8) + 8 * (vgrp & 1);
+    // byte s of perm(ksw, ksw, ksel) is byte s ^ sx of ksw (slot s's scale)
+    const uint32_t ksel = 0x03020100u ^ (0x01010101u * (uint32_t)sx);
     const int soff = (my_tok * p.Hkv + g) * 4;  // scale of the lane's token within a block's scales
     const int jw = j0 + sub;  // this wave's first block; it takes every WPH-th block
     int64_t phys = jw < jend ? (int64_t)table[jw] : 0;
@@ -413,21 +419,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
         const auto rs = range_rsrc(kcache + ph * blk_bytes, blk_bytes);
 #pragma unroll
         for (int s = 0; s < 4; ++s) load_buf<KB>(kr[s], rs, koff[s], 0);
-        if constexpr (F4) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) load_buf<1>(ksb[s], rs, koff[s] + ksb_off, 0);
-        }
+        if constexpr (F4) load_buf<4>(ksw, rs, ksw_off, 0);
     };
     auto load_v = [&](int64_t ph) {
         const auto rs = range_rsrc(vcache + ph * blk_bytes, blk_bytes);
 #pragma unroll
         for (int st = 0; st < STEPS; ++st)
             load_buf<VB>(vr[st], rs, voff, (2 * TPW * (st >> 1) + (st & 1)) * tok_stride);
-        if constexpr (F4) {
-#pragma unroll
-            for (int st = 0; st < STEPS; ++st)
-                load_buf<1>(vsb[st], rs, voff + vsb_off, (2 * TPW * (st >> 1) + (st & 1)) * tok_stride);
-        }
+        if constexpr (F4) load_buf<8>(vsw, rs, vsw_off, 0);
     };
     if (jw < jend) load_k(phys);
 
@@ -454,6 +453,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
         if constexpr (MORE) phys_next = (int64_t)table[j + WPH];
 
         // ---------------------------------------------------------------- QK
+        float kscl[4] = {1.0f, 1.0f, 1.0f, 1.0f};  // nvfp4: block scale of the lane's keys per slot
+        if constexpr (F4) {
+            const uint32_t kp = __builtin_amdgcn_perm(ksw.w[0], ksw.w[0], ksel);
+            const pa_f32x2 lo = fp8x2_to_f32<false>(kp), hi = fp8x2_to_f32<true>(kp);
+            kscl[0] = lo.x;
+            kscl[1] = lo.y;
+            kscl[2] = hi.x;
+            kscl[3] = hi.y;
+        }
         float ps[4][GT];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -477,15 +485,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
 #pragma unroll
                     for (int b2 = 0; b2 < KB; ++b2) {
                         const uint32_t wd = kr[s].w[b2 / 4];
-                        const pa_f32x2 f = (b2 & 3) == 0 ? fp4x2_to_f32<0>(wd)
-                                           : (b2 & 3) == 1 ? fp4x2_to_f32<1>(wd)
-                                           : (b2 & 3) == 2 ? fp4x2_to_f32<2>(wd)
-                                                           : fp4x2_to_f32<3>(wd);
-                        const uint32_t kp = pack_bf16_rne(f.x, f.y);
+                        const uint32_t kp = (b2 & 3) == 0 ? fp4x2_to_bf16x2<0>(wd)
+                                            : (b2 & 3) == 1 ? fp4x2_to_bf16x2<1>(wd)
+                                            : (b2 & 3) == 2 ? fp4x2_to_bf16x2<2>(wd)
+                                                            : fp4x2_to_bf16x2<3>(wd);
                         acc = b2 == 0 ? dot2_bf16_first(qv[h][0], kp) : dot2_bf16(qv[h][b2], kp, acc);
                         if constexpr (QS == 2) acc = dot2_bf16(ql[h][b2], kp, acc);
                     }
-                    acc *= fp8_value(ksb[s].w[0]);
+                    acc *= kscl[s];
                 } else if constexpr (F8) {
 #pragma unroll
                     for (int w = 0; w < KW; ++w) {
@@ -606,6 +613,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
         // ---------------------------------------------------------------- PV
         // tokens past the end may hold anything (bf16: NaN or Inf times a zero
         // weight; fp8: NaN codes); int8 codes are always finite
+        // nvfp4: step st's value scale in byte TPW/2 (st >> 1) of vs[st & 1]
+        uint32_t vs[2] = {0u, 0u};
+        if constexpr (F4) {
+            const int sh = TPW > 2 ? 8 * (vgrp >> 1) : 0;
+            vs[0] = vsw.w[0] >> sh;
+            vs[1] = vsw.w[1] >> sh;
+        }
         if constexpr (!I8) {
             if (pos0 + kBlockSize > end) {
 #pragma unroll
@@ -613,7 +627,24 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
                     const bool ok = pos0 + tok_of(st) < end;
 #pragma unroll
                     for (int w = 0; w < VB / 4; ++w) vr[st].w[w] = ok ? vr[st].w[w] : 0u;
-                    if constexpr (F4) vsb[st].w[0] = ok ? vsb[st].w[0] : 0u;
+                    if constexpr (F4) vs[st & 1] &= ok ? 0xFFFFFFFFu : ~(0xFFu << (8 * (TPW / 2) * (st >> 1)));
+                }
+            }
+        }
+        // nvfp4: the scales of step pair (2 i, 2 i + 1) as an f16 pair (exact)
+        half2_t sabs[F4 ? STEPS / 2 : 1];
+        if constexpr (F4) {
+#pragma unroll
+            for (int i = 0; i < STEPS / 2; i += 2) {
+                constexpr int T2 = TPW / 2;
+                const uint32_t b0 = T2 * i, b1 = i + 1 < STEPS / 2 ? T2 * (i + 1) : 0;
+                // bytes (vs[0].b0, vs[1].b0, vs[0].b1, vs[1].b1)
+                const uint32_t x = __builtin_amdgcn_perm(vs[1], vs[0], b0 | (4 + b0) << 8 | b1 << 16 | (4 + b1) << 24);
+                const pa_f32x2 lo = fp8x2_to_f32<false>(x);
+                sabs[i] = pkrtz_h2(lo.x, lo.y);
+                if (i + 1 < STEPS / 2) {
+                    const pa_f32x2 hi = fp8x2_to_f32<true>(x);
+                    sabs[i + 1] = pkrtz_h2(hi.x, hi.y);
                 }
             }
         }
@@ -643,18 +674,21 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
                     }
                 } else if constexpr (F4) {
                     // element e of tokens tk and tk + 1 times their block
-                    // scales as an f16 pair (exact: at most 6 significant bits)
-                    // (the codes packed first, then one packed f16 multiply
-                    // by the two tokens' scales)
-                    const half2_t sab = pkrtz_h2(fp8_value(vsb[st].w[0]), fp8_value(vsb[st + 1].w[0]));
+                    // scales as an f16 pair (exact: at most 6 significant
+                    // bits): the two tokens' nibbles of each element are
+                    // paired in one byte (even elements in xe, odd in xo),
+                    // converted as an f16 pair and multiplied by the scales
+                    const half2_t sab = sabs[st >> 1];
+                    const uint32_t xe = (A & 0x0F0F0F0Fu) | ((B << 4) & 0xF0F0F0F0u);
+                    const uint32_t xo = ((A >> 4) & 0x0F0F0F0Fu) | (B & 0xF0F0F0F0u);
 #pragma unroll
                     for (int b2 = 0; b2 < 4; ++b2) {
-                        const pa_f32x2 a = b2 == 0 ? fp4x2_to_f32<0>(A) : b2 == 1 ? fp4x2_to_f32<1>(A)
-                                           : b2 == 2 ? fp4x2_to_f32<2>(A) : fp4x2_to_f32<3>(A);
-                        const pa_f32x2 bb = b2 == 0 ? fp4x2_to_f32<0>(B) : b2 == 1 ? fp4x2_to_f32<1>(B)
-                                            : b2 == 2 ? fp4x2_to_f32<2>(B) : fp4x2_to_f32<3>(B);
-                        const uint32_t f0 = __builtin_bit_cast(uint32_t, pkrtz_h2(a.x, bb.x) * sab);
-                        const uint32_t f1 = __builtin_bit_cast(uint32_t, pkrtz_h2(a.y, bb.y) * sab);
+                        const uint32_t pe = b2 == 0 ? fp4x2_to_f16x2<0>(xe) : b2 == 1 ? fp4x2_to_f16x2<1>(xe)
+                                            : b2 == 2 ? fp4x2_to_f16x2<2>(xe) : fp4x2_to_f16x2<3>(xe);
+                        const uint32_t po = b2 == 0 ? fp4x2_to_f16x2<0>(xo) : b2 == 1 ? fp4x2_to_f16x2<1>(xo)
+                                            : b2 == 2 ? fp4x2_to_f16x2<2>(xo) : fp4x2_to_f16x2<3>(xo);
+                        const uint32_t f0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, pe) * sab);
+                        const uint32_t f1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, po) * sab);
 #pragma unroll
                         for (int h = 0; h < GT; ++h) {
                             o[h][2 * b2 + 0] = dot2_f16(pp[h], f0, o[h][2 * b2 + 0]);

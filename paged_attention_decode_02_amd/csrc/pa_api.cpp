@@ -71,9 +71,9 @@ bool kv_supported(pa_dtype t) {
 // caches stored as codes with one fp32 scale per (token, kv head)
 bool quantised(pa_dtype t) { return t == PA_I8 || t == PA_FP8 || t == PA_NVFP4; }
 
-// bytes of one cache row of D elements
+// storage bytes per (token, kv head): a block is 16 Hkv times this
 int64_t row_bytes(pa_dtype t, int32_t D) {
-    if (t == PA_NVFP4) return (D / 2 + D / 16 + 15) / 16 * 16;
+    if (t == PA_NVFP4) return D / 2 + D / 16;
     return (int64_t)D * (t == PA_F32 ? 4 : t == PA_BF16 ? 2 : 1);
 }
 

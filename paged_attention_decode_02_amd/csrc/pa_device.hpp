@@ -21,11 +21,24 @@ struct Elt {
     static constexpr int bytes = KVT == KV_F32 ? 4 : (KVT == KV_BF16 ? 2 : 1);  // NVFP4: see nvfp4_row_bytes
 };
 
-// NVFP4 cache row: D/2 bytes of E2M1 code pairs (element 2i in the low nibble
-// of byte i), then the D/16 E4M3 block scales, then zero padding to 16 bytes.
-__host__ __device__ constexpr int nvfp4_row_bytes(int D) { return (D / 2 + D / 16 + 15) / 16 * 16; }
+// NVFP4 block of 16 tokens and Hkv heads (9 Hkv D bytes): the code rows of
+// its 16 Hkv (token, head) pairs, D/2 bytes each in (token, head) order with
+// element 2i in the low nibble of byte i, then one plane of D bytes per head
+// holding that head's E4M3 block scales, the scale of elements 16k .. 16k+15
+// of token t = 4q + r at byte 16k + 4r + q. Rows are 64-byte aligned for
+// D >= 128 and each head's scales of a block are one contiguous run, so no
+// 64-byte fetch is split between rows or between codes and scales; the
+// (r, q) order gives each lane of the decode its scales in one load.
+__host__ __device__ constexpr int nvfp4_row_bytes(int D) { return D / 2 + D / 16; }  // per (token, head)
+__host__ __device__ constexpr int nvfp4_scale_byte(int t, int k) { return 16 * k + 4 * (t & 3) + (t >> 2); }
 
-// Bytes of one cache row of D elements.
+// Code bytes of one cache row of D elements (the row stride within a block).
+template <int KVT>
+__host__ __device__ constexpr int kv_code_row_bytes(int D) {
+    return KVT == KV_NVFP4 ? D / 2 : D * Elt<KVT>::bytes;
+}
+
+// Storage bytes per (token, kv head); a block is 16 Hkv times this.
 template <int KVT>
 __host__ __device__ constexpr int kv_row_bytes(int D) {
     return KVT == KV_NVFP4 ? nvfp4_row_bytes(D) : D * Elt<KVT>::bytes;
@@ -148,6 +161,19 @@ __device__ __forceinline__ pa_f32x2 fp8x2_to_f32(uint32_t w) {
 template <int SEL>
 __device__ __forceinline__ pa_f32x2 fp4x2_to_f32(uint32_t w) {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+// Two FP4 E2M1 codes of w (byte SEL, as above) as a bf16 or an f16 pair (low
+// half from the low nibble), exact for every code byte except that a negative
+// zero comes out positive (probed over all 256 bytes); no sum of products can
+// tell the two zeros apart.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL));
+}
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_f16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL));
 }
 
 // The value of one E4M3 code (the low byte of b), exact.

@@ -4,6 +4,7 @@ from __future__ import annotations
 import numpy as np
 
 import oracle
+from _refs import nvfp4_token_bytes
 from workloads import BLOCK_SIZE, Workload
 
 POISON_CODE = 127
@@ -12,13 +13,18 @@ POISON_CODE = 127
 def poison_host(w: Workload, k, v, ks, vs) -> None:
     """Fill every cache slot that holds no source row with poison.
 
-    Float caches get NaN; int8 caches get code 127 with a NaN scale. A decode
-    that reads any of these slots produces NaN.
+    Float caches get NaN; int8, FP8 and NVFP4 caches get code 127 (an E4M3
+    NaN) in every byte of the slot, with a NaN scale. A decode that reads any
+    of these slots produces NaN.
     """
     slots = w.unused_slots()
     blk, off = slots // BLOCK_SIZE, slots % BLOCK_SIZE
+    sp = w.spec
     for c in (k, v):
-        if c.dtype == np.float32:
+        if sp.cache_dtype == "nvfp4":  # a token's bytes are spread over its block
+            idx = np.stack([nvfp4_token_bytes(sp.Hkv, sp.D, t) for t in range(BLOCK_SIZE)])
+            c.reshape(c.shape[0], -1)[blk[:, None], idx[off]] = POISON_CODE
+        elif c.dtype == np.float32:
             c[blk, off] = np.nan
         elif c.dtype == np.uint16:
             c[blk, off] = 0x7FC0  # bfloat16 quiet NaN

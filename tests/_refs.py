@@ -20,8 +20,24 @@ import numpy as np
 from workloads import bf16_bits_to_f32
 
 
-# NVFP4 rows: D/2 code bytes + D/16 block scales, padded to 16 bytes
-_NVFP4_D = {48: 64, 80: 128, 144: 256}
+# NVFP4 caches: uint8 [num_blocks, 16, Hkv, 9 D / 16], last dim -> D
+_NVFP4_D = {36: 64, 72: 128, 144: 256}
+
+
+def nvfp4_split(a: np.ndarray, D: int):
+    """E2M1 codes [nb, 16, Hkv, D] and E4M3 block-scale codes [nb, 16, Hkv, D/16]
+    of an NVFP4 cache. A block holds the code rows of its 16 * Hkv (token, head)
+    pairs first, D/2 bytes each in (token, head) order with element 2i in the
+    low nibble of byte i, then one plane of D bytes per head, the scale of
+    elements 16k .. 16k + 15 of token t = 4q + r at byte 16k + 4r + q."""
+    nb, bs, Hkv, rb = a.shape
+    assert bs == 16 and rb == D // 2 + D // 16, a.shape
+    flat = a.reshape(nb, -1)
+    cb = flat[:, : 16 * Hkv * D // 2].reshape(nb, 16, Hkv, D // 2).astype(np.int64)
+    codes = np.stack([cb & 15, cb >> 4], axis=-1).reshape(nb, 16, Hkv, D)
+    planes = flat[:, 16 * Hkv * D // 2:].reshape(nb, Hkv, D // 16, 4, 4)  # [b, h, k, r, q]
+    scales = planes.transpose(0, 4, 3, 1, 2).reshape(nb, 16, Hkv, D // 16)  # [b, q, r, h, k]
+    return codes, np.ascontiguousarray(scales)
 
 
 def _e2m1(codes: np.ndarray) -> np.ndarray:
@@ -33,16 +49,22 @@ def _e2m1(codes: np.ndarray) -> np.ndarray:
     return s * mag
 
 
+def nvfp4_token_bytes(Hkv: int, D: int, t: int) -> np.ndarray:
+    """Byte offsets, within an NVFP4 block, of token t's code rows (every
+    head) and block scales (the layout nvfp4_split reads)."""
+    codes = t * Hkv * (D // 2) + np.arange(Hkv * (D // 2))
+    h, k = np.meshgrid(np.arange(Hkv), np.arange(D // 16), indexing="ij")
+    scales = 16 * Hkv * (D // 2) + h * D + 16 * k + 4 * (t % 4) + t // 4
+    return np.concatenate([codes, scales.reshape(-1)])
+
+
 def _nvfp4_f64(a: np.ndarray, scale: np.ndarray, D: int) -> np.ndarray:
-    """Decoded NVFP4 rows: E2M1 codes times their E4M3 block scale (decoded by
-    torch's float8_e4m3fn) times the row's fp32 scale."""
+    """Decoded NVFP4 cache [nb, 16, Hkv, D]: E2M1 codes times their E4M3 block
+    scale (decoded by torch's float8_e4m3fn) times the row's fp32 scale."""
     import torch
 
-    lo = (a[..., : D // 2] & 15).astype(np.int64)
-    hi = (a[..., : D // 2] >> 4).astype(np.int64)
-    codes = np.stack([lo, hi], axis=-1).reshape(a.shape[:-1] + (D,))
-    bsc = torch.from_numpy(np.ascontiguousarray(a[..., D // 2: D // 2 + D // 16])).view(torch.float8_e4m3fn)
-    bsc = bsc.to(torch.float64).numpy()
+    codes, sc = nvfp4_split(a, D)
+    bsc = torch.from_numpy(sc).view(torch.float8_e4m3fn).to(torch.float64).numpy()
     return _e2m1(codes) * np.repeat(bsc, 16, axis=-1) * scale.astype(np.float64)[..., None]
 
 

@@ -17,6 +17,7 @@ import paged_attention_decode_02_amd as pa
 from _gpu import cache_bytes_equal, dev, dev_to_host, gpu_cache, gpu_decode, gpu_inputs, host_to_dev
 import oracle
 from _host import oracle_cache, oracle_decode
+from _refs import nvfp4_split, nvfp4_token_bytes
 from workloads import BLOCK_SIZE, SPECS, generate, scaled
 
 pytestmark = pytest.mark.gpu
@@ -293,8 +294,9 @@ def test_fp8_cache_write_of_hand_derived_rows():
 
 def test_nvfp4_cache_write_of_the_hand_derived_row():
     """The hand-derived NVFP4 row (ties to even, saturation, block scales
-    rounded to E4M3, zero blocks, padding) written by the GPU equals the oracle
-    writer's bytes and the hand-derived codes."""
+    rounded to E4M3, zero blocks) written by the GPU to token 5 of a block
+    equals the oracle writer's bytes and the hand-derived codes, and leaves
+    the other tokens' bytes of the block alone."""
     import json
 
     with open(os.path.join(os.path.dirname(__file__), "golden", "nvfp4_cases.json")) as f:
@@ -304,20 +306,32 @@ def test_nvfp4_cache_write_of_the_hand_derived_row():
     for b, blk in enumerate(row["blocks"]):
         x[0, 0, 16 * b: 16 * b + len(blk["x"])] = blk["x"]
     hk, hv, hks, hvs = oracle.alloc_cache(1, BLOCK_SIZE, 1, D, "nvfp4")
-    oracle.cache_write(x, x, np.arange(1), hk, hv, hks, hvs)
-    RBQ = oracle.nvfp4_row_bytes(D)
-    k = torch.full((1, BLOCK_SIZE, 1, RBQ), 0x55, dtype=torch.uint8, device=dev()).view(torch.float4_e2m1fn_x2)
+    hk[:] = 0x55
+    hv[:] = 0x55
+    oracle.cache_write(x, x, np.array([5]), hk, hv, hks, hvs)
+    RB = oracle.nvfp4_row_bytes(D)
+    k = torch.full((1, BLOCK_SIZE, 1, RB), 0x55, dtype=torch.uint8, device=dev()).view(torch.float4_e2m1fn_x2)
     v = k.clone()
     ks = torch.zeros((1, BLOCK_SIZE, 1), dtype=torch.float32, device=dev())
     vs = ks.clone()
     src = torch.from_numpy(x).to(dev())
-    pa.cache_write(src, src, torch.zeros(1, dtype=torch.int64, device=dev()), k, v, ks, vs)
+    pa.cache_write(src, src, torch.full((1,), 5, dtype=torch.int64, device=dev()), k, v, ks, vs)
     torch.cuda.synchronize()
-    assert np.array_equal(dev_to_host(k)[0, 0], hk[0, 0]) and np.array_equal(dev_to_host(v)[0, 0], hv[0, 0])
-    assert ks.cpu().numpy()[0, 0, 0] == hks[0, 0, 0] == np.float32(row["row_scale"])
-    r = dev_to_host(k)[0, 0, 0]
+    assert np.array_equal(dev_to_host(k), hk) and np.array_equal(dev_to_host(v), hv)
+    assert ks.cpu().numpy()[0, 5, 0] == hks[0, 5, 0] == np.float32(row["row_scale"])
+    codes, scales = nvfp4_split(dev_to_host(k), D)
     for b, blk in enumerate(row["blocks"]):
-        assert r[D // 2 + b] == blk["scale_code"], b
+        assert scales[0, 5, 0, b] == blk["scale_code"], b
+        assert codes[0, 5, 0, 16 * b: 16 * b + len(blk["codes"])].tolist() == blk["codes"], b
+
+
+def _slot_bytes(c: np.ndarray, slots: np.ndarray, spec) -> np.ndarray:
+    """The storage of the given slots: [n, Hkv(, last dim)] for rows and
+    scales, or for an NVFP4 cache the bytes of each token spread over its block."""
+    if c.ndim == 4 and spec.cache_dtype == "nvfp4":
+        idx = np.stack([nvfp4_token_bytes(spec.Hkv, spec.D, t) for t in range(BLOCK_SIZE)])
+        return c.reshape(c.shape[0], -1)[slots[:, None] // BLOCK_SIZE, idx[slots % BLOCK_SIZE]]
+    return c.reshape((-1, spec.Hkv) + c.shape[3:])[slots]
 
 
 def test_cache_write_skips_negative_slots_and_writes_bits():
@@ -332,12 +346,11 @@ def test_cache_write_skips_negative_slots_and_writes_bits():
             cache = gpu_cache(w)
             # skipped rows' slots stay poisoned on the GPU; compare only written slots
             written = w.slot_mapping[w.slot_mapping >= 0]
-            blk, off = written // BLOCK_SIZE, written % BLOCK_SIZE
             for g, h in zip(cache, host):
                 if g is None:
                     continue
-                a = dev_to_host(g)[blk, off]
-                hb = h[blk, off]
+                a = _slot_bytes(dev_to_host(g), written, spec)
+                hb = _slot_bytes(h, written, spec)
                 if a.dtype == np.float32:
                     assert np.array_equal(a.view(np.uint32), hb.view(np.uint32))
                 else:
@@ -347,8 +360,7 @@ def test_cache_write_skips_negative_slots_and_writes_bits():
             b_ = w.row_seq[sk_rows]
             p_ = w.row_pos[sk_rows]
             sslots = w.block_table[b_, p_ // BLOCK_SIZE].astype(np.int64) * BLOCK_SIZE + p_ % BLOCK_SIZE
-            kc = dev_to_host(cache[0])
-            kc = kc.reshape(-1, spec.Hkv, kc.shape[-1])[sslots]
+            kc = _slot_bytes(dev_to_host(cache[0]), sslots, spec)
             if kc.dtype in (np.int8, np.uint8):
                 assert np.all(kc == 127)
             elif kc.dtype == np.uint16:

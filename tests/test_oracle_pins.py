@@ -19,7 +19,7 @@ import pytest
 
 import oracle
 from _host import oracle_cache, oracle_decode, poison_host
-from _refs import as_f64, brute_decode, dense_decode, sdpa_decode
+from _refs import as_f64, brute_decode, dense_decode, nvfp4_split, sdpa_decode
 from workloads import BLOCK_SIZE, SPECS, bf16_bits, bf16_bits_to_f32, generate, scaled
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -471,16 +471,22 @@ def test_nvfp4_golden_row():
         x[16 * b: 16 * b + len(blk["x"])] = blk["x"]
     nb = 1
     k, v, ks, vs = oracle.alloc_cache(nb, BLOCK_SIZE, 1, D, "nvfp4")
-    oracle.cache_write(x[None, None, :], x[None, None, :], np.array([0]), k, v, ks, vs)
-    r = k[0, 0, 0]
-    assert ks[0, 0, 0] == np.float32(row["row_scale"])
-    codes = np.stack([r[: D // 2] & 15, r[: D // 2] >> 4], axis=-1).reshape(D)
+    k[:] = 0xEE  # bytes of other rows: left as they are
+    oracle.cache_write(x[None, None, :], x[None, None, :], np.array([5]), k, v, ks, vs)
+    assert ks[0, 5, 0] == np.float32(row["row_scale"])
+    all_codes, all_scales = nvfp4_split(k, D)
+    codes, scales = all_codes[0, 5, 0], all_scales[0, 5, 0]
     for b, blk in enumerate(row["blocks"]):
-        assert r[D // 2 + b] == blk["scale_code"], (b, r[D // 2 + b])
+        assert scales[b] == blk["scale_code"], (b, scales[b])
         n = len(blk["codes"])
         assert codes[16 * b: 16 * b + n].tolist() == blk["codes"], (b, blk)
         assert np.all(codes[16 * b + n: 16 * b + 16] == 0)
-    assert np.all(r[D // 2 + D // 16:] == 0)  # padding
+    # token 5 of the block owns D/2 code bytes and D/16 scale bytes, nothing else
+    untouched = np.ones(k.size, bool)
+    untouched[5 * D // 2: 6 * D // 2] = False
+    for kk in range(D // 16):
+        untouched[16 * D // 2 + 16 * kk + 4 * (5 % 4) + 5 // 4] = False
+    assert np.all(k.reshape(-1)[untouched] == 0xEE)
 
 
 def test_nvfp4_quantiser_bound():
@@ -492,12 +498,11 @@ def test_nvfp4_quantiser_bound():
     nb = 512 // BLOCK_SIZE
     k, v, ks, vs = oracle.alloc_cache(nb, BLOCK_SIZE, 1, D, "nvfp4")
     oracle.cache_write(x, x, np.arange(512), k, v, ks, vs)
-    rows = k.reshape(512, -1)
+    all_codes, all_scales = nvfp4_split(k, D)
+    codes, scale_codes = all_codes.reshape(512, D), all_scales.reshape(512, D // 16)
     S = ks.reshape(512).astype(np.float64)
-    lo, hi = rows[:, : D // 2] & 15, rows[:, : D // 2] >> 4
-    codes = np.stack([lo, hi], -1).reshape(512, D)
     e2 = np.array([oracle.e2m1_value(c) for c in range(16)])
-    sb = np.array([oracle.fp8_value(c) for c in range(256)])[rows[:, D // 2: D // 2 + D // 16]]
+    sb = np.array([oracle.fp8_value(c) for c in range(256)])[scale_codes]
     db = (np.repeat(sb, 16, axis=1) * S[:, None]).astype(np.float32).astype(np.float64)
     y = x[:, 0].astype(np.float64) / np.where(db == 0, 1, db)
     got = e2[codes]
