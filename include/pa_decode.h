@@ -41,11 +41,15 @@
  *    {f32, bf16, i8, fp8, nvfp4}; out in {f32, bf16}. q, caches and out must
  *    be 16-byte aligned; one KV block (16 * Hkv * row bytes) must be below
  *    2^31 bytes.
- *  - An NVFP4 cache row holds D/2 bytes of E2M1 code pairs (element 2i in
- *    the low nibble of byte i), then D/16 E4M3 block scales (one per 16
- *    consecutive elements), then zero padding to a multiple of 16 bytes
- *    (48, 80 or 144 bytes for D = 64, 128, 256): caches are
- *    [num_blocks, block_size, Hkv, row bytes].
+ *  - NVFP4 caches are bytes [num_blocks, block_size, Hkv, 9 D / 16] (row
+ *    bytes 36, 72, 144 for D = 64, 128, 256), but a block is not stored row
+ *    by row: first the code rows of its 16 * Hkv (token, head) pairs, D/2
+ *    bytes each in (token, head) order, element 2i in the low nibble of
+ *    byte i; then one plane of D bytes per kv head h (at 8 Hkv D + h D in
+ *    the block) with that head's E4M3 block scales, the scale of elements
+ *    16k .. 16k + 15 of token 4q + r at byte 16k + 4r + q of the plane.
+ *    Code rows are 64-byte aligned for D >= 128 and a head's block scales are
+ *    one contiguous run, so HBM fetches are never shared between rows.
  */
 #ifndef PA_DECODE_H
 #define PA_DECODE_H

@@ -31,7 +31,9 @@ _lock = threading.Lock()
 _lib = None
 
 # FP8 caches hold OCP E4M3 codes (torch.float8_e4m3fn storage)
-# NVFP4 caches: torch.float4_e2m1fn_x2 storage, [num_blocks, 16, Hkv, row bytes]
+# NVFP4 caches: torch.float4_e2m1fn_x2 storage, [num_blocks, 16, Hkv, 9 D / 16]
+# bytes whose blocks hold all code rows first, then one block-scale plane per
+# kv head (the layout include/pa_decode.h describes)
 DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.int8: 2, torch.float8_e4m3fn: 3, torch.float4_e2m1fn_x2: 4}
 
 EXPORTS = (
