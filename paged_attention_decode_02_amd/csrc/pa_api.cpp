@@ -77,8 +77,18 @@ int64_t row_bytes(pa_dtype t, int32_t D) {
     return (int64_t)D * (t == PA_F32 ? 4 : t == PA_BF16 ? 2 : 1);
 }
 
+// The matrix-core kernel reads a kv head's blocks once for all G * Tq rows;
+// the vector-ALU kernel once per query token, with work that grows with G.
+// Measured (kernel times, 16K-250K tokens, D 128 and 256): with Tq > 1 the
+// matrix cores take 0.17-0.86x the time for every group size and cache type;
+// with Tq = 1 they win from G = 16 (a full row tile), and for int8 caches
+// already from G = 6 (0.77-0.95x; the vector-ALU int8 decode is bound by its
+// code widening and dot products, the matrix-core one is not), while for
+// bf16, FP8 and NVFP4 below 16 rows the vector ALU is as fast or faster.
 bool use_mfma(int32_t Tq, int32_t Hq, int32_t Hkv, pa_dtype kv_dtype) {
-    return kv_dtype != PA_F32 && (int64_t)(Hq / Hkv) * Tq >= 16;
+    if (kv_dtype == PA_F32) return false;
+    const int64_t G = Hq / Hkv;
+    return Tq > 1 || G >= 16 || (kv_dtype == PA_I8 && G >= 6);
 }
 
 // Row tiles per workgroup and row chunks of the matrix-core kernel.

@@ -88,11 +88,14 @@ def test_workspace_size_and_partition_choice(lib):
     need = lib.pa_decode_workspace_bytes(4, 1, 24, 4, 256, 1, 65536, 2048)
     rows = 4 * 24
     assert need == rows * 32 * 256 * 4 + rows * 32 * 4
-    # int8 caches: two workgroups per CU (the int8 path needs the second wave
-    # per SIMD), each taking two kv heads: 252 partitions x 2 = 504 workgroups
-    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 2, 250000) == 992
-    # fp8 caches take the int8 launch shape
+    # int8 caches with G = 6 run on the matrix cores: two workgroups per CU,
+    # one per (kv head, partition): 127 partitions x 4 kv heads
+    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 2, 250000) == 1984
+    # fp8 caches with G = 6 stay on the vector ALU: two workgroups per CU, each
+    # taking two kv heads: 253 partitions x 2 = 506 workgroups
     assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 3, 250000) == 992
+    # int8 with G = 4 stays on the vector ALU
+    assert lib.pa_choose_partition_size(1, 1, 16, 4, 256, 2, 250000) == 992
     assert lib.pa_choose_partition_size(4, 8, 24, 4, 256, 3, 30321) == 960
     # small head chunks (batched GQA, D=128, 4 heads): four per CU
     assert lib.pa_choose_partition_size(8, 1, 32, 8, 128, 1, 3637) == 256
@@ -103,8 +106,10 @@ def test_workspace_size_and_partition_choice(lib):
     # one partition covers a short context: no workspace
     assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 1, 48) == 48
     assert lib.pa_decode_workspace_bytes(1, 1, 24, 4, 256, 1, 48, 0) == 0
-    # (two waves per kv head: at least 4 blocks each)
-    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 2, 200) == 128
+    # (vector ALU, two waves per kv head: at least 4 blocks each)
+    assert lib.pa_choose_partition_size(1, 1, 16, 4, 256, 2, 200) == 128
+    # (matrix cores: one partition covers 200 tokens)
+    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 2, 200) == 208
     # fp32 caches (one-wave workgroups) split even short contexts into blocks
     assert lib.pa_choose_partition_size(1, 1, 4, 1, 64, 0, 256) == 16
     assert lib.pa_decode_workspace_bytes(1, 1, 4, 1, 64, 0, 256, 0) == 4 * 16 * 64 * 4 + 256

@@ -370,10 +370,11 @@ def test_cache_write_skips_negative_slots_and_writes_bits():
 
 
 # ------------------------------------------------------------ matrix-core path
-# G * Tq >= 16 rows per kv head (bf16 / int8 / fp8 / nvfp4 caches) run on the MFMA kernel.
+# Tq > 1, G >= 16, and int8 with G >= 6 run on the MFMA kernel (bf16 / int8 /
+# fp8 / nvfp4 caches), including row counts below one 16-row tile.
 @pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "nvfp4"])
 @pytest.mark.parametrize("D", [64, 128, 256])
-@pytest.mark.parametrize("G, Tq", [(6, 8), (16, 1), (8, 16), (2, 8), (24, 3)])
+@pytest.mark.parametrize("G, Tq", [(6, 8), (16, 1), (8, 16), (2, 8), (24, 3), (1, 2), (1, 8), (5, 3), (6, 1)])
 def test_mfma_rows(kv, D, G, Tq):
     spec = scaled("verify_bf16", B=2, Tq=Tq, Hq=2 * G, Hkv=2, D=D, seq_lens=(Tq, 1300), shared_prefix=0,
                   cache_dtype=kv, src_dtype="bf16")
