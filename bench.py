@@ -330,7 +330,7 @@ def main():
     kc, vc = kc.view(TD[sp.cache_dtype]), vc.view(TD[sp.cache_dtype])
     ks = vs = None
     if sp.cache_dtype in ("i8", "fp8", "nvfp4"):
-        ks = torch.zeros(shape[:3], dtype=torch.float32, device=dev)
+        ks = torch.zeros((shape[0], sp.Hkv, BLOCK_SIZE), dtype=torch.float32, device=dev)  # [nb, Hkv, 16]
         vs = torch.zeros_like(ks)
     N = w.slot_mapping.shape[0]
     step = 1 << 20

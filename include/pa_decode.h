@@ -31,7 +31,9 @@
  *  - Layouts are dense row-major with the innermost dimension last:
  *      q        [B, Tq, Hq, D]
  *      caches   [num_blocks, block_size, Hkv, D]   (K and V separately)
- *      scales   [num_blocks, block_size, Hkv]      fp32, int8 caches only
+ *      scales   [num_blocks, Hkv, block_size]      fp32, int8 / FP8 / NVFP4 caches only;
+ *                                                  a kv head's scales of one block are one
+ *                                                  64-byte run, read whole by its workgroup
  *      table    [B, max_blocks_per_seq]            int32 physical block ids
  *      out      [B, Tq, Hq, D]
  *      lse      [B, Tq, Hq]                        fp32, natural log

@@ -6,8 +6,9 @@ shares no code with the HIP library (``pa_oracle.c`` includes nothing from it
 and is built by gcc, not hipcc).
 
 Functions take numpy arrays in the layouts the decode problem fixes:
-q [B, Tq, Hq, D]; caches [num_blocks, block_size, Hkv, D]; int8 and FP8 scales
-[num_blocks, block_size, Hkv]; block_table [B, max_blocks] int32; seq_lens [B]
+q [B, Tq, Hq, D]; caches [num_blocks, block_size, Hkv, D]; int8, FP8 and NVFP4
+scales [num_blocks, Hkv, block_size] (one per token and kv head, a kv head's
+scales of a block together); block_table [B, max_blocks] int32; seq_lens [B]
 int32. bfloat16 data is passed as its uint16 bit patterns, FP8 (OCP E4M3) as
 its uint8 codes.
 
@@ -133,8 +134,8 @@ def alloc_cache(num_blocks: int, block_size: int, Hkv: int, D: int, cache_dtype:
     v = np.zeros(shape, npdt)
     ks = vs = None
     if cache_dtype in ("i8", "fp8", "nvfp4"):
-        ks = np.zeros(shape[:3], np.float32)
-        vs = np.zeros(shape[:3], np.float32)
+        ks = np.zeros((num_blocks, Hkv, block_size), np.float32)  # a kv head's scales of a block together
+        vs = np.zeros((num_blocks, Hkv, block_size), np.float32)
     return k, v, ks, vs
 
 

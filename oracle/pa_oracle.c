@@ -189,22 +189,30 @@ static double elem(const void* base, int dtype, int64_t i) {
     }
 }
 
+/* Index of row `row`'s fp32 scale: scales are [num_blocks, Hkv, bs], a kv
+ * head's scales of one block contiguous. */
+static int64_t scale_index(int64_t row, int Hkv, int bs) {
+    const int64_t blk = row / ((int64_t)bs * Hkv), t = (row / Hkv) % bs, h = row % Hkv;
+    return (blk * Hkv + h) * bs + t;
+}
+
 /* Element d of cache row `row` (row = (block * bs + offset) * Hkv + g),
  * dequantised: for int8, FP8 and NVFP4 the exact product of the code's value
  * and its scales in fp64. */
-static double cache_elem(const void* cache, int dtype, const float* scale, int64_t row, int Hkv, int D, int d) {
+static double cache_elem(const void* cache, int dtype, const float* scale, int64_t row, int Hkv, int bs, int D,
+                         int d) {
     int64_t i = row * (int64_t)D + d;
     switch (dtype) {
     case OR_F32: return (double)((const float*)cache)[i];
     case OR_BF16: return bf16_to_double(((const uint16_t*)cache)[i]);
-    case OR_I8: return (double)((const int8_t*)cache)[i] * (double)scale[row];
-    case OR_FP8: return pa_oracle_fp8_value(((const uint8_t*)cache)[i]) * (double)scale[row];
+    case OR_I8: return (double)((const int8_t*)cache)[i] * (double)scale[scale_index(row, Hkv, bs)];
+    case OR_FP8: return pa_oracle_fp8_value(((const uint8_t*)cache)[i]) * (double)scale[scale_index(row, Hkv, bs)];
     case OR_NVFP4: {
         const uint8_t* c = (const uint8_t*)cache;
         const uint8_t pair = c[nvfp4_code_offset(row, Hkv, D) + d / 2];
         const int code = (d & 1) ? pair >> 4 : pair & 15;
         return pa_oracle_e2m1_value(code) * pa_oracle_fp8_value(c[nvfp4_scale_offset(row, Hkv, D, d / 16)]) *
-               (double)scale[row];
+               (double)scale[scale_index(row, Hkv, bs)];
     }
     default: return NAN;
     }
@@ -243,6 +251,7 @@ int pa_oracle_cache_write(const void* k_src, const void* v_src, int src_dtype, c
             for (int g = 0; g < Hkv; ++g) {
                 int64_t s0 = (i * Hkv + g) * (int64_t)D;
                 int64_t row = (blk * block_size + off) * Hkv + g;
+                int64_t srow = (blk * Hkv + g) * block_size + off; /* scales [num_blocks, Hkv, bs] */
                 int64_t d0 = row * (int64_t)D;
                 if (cache_dtype == OR_I8) {
                     float amax = 0.0f;
@@ -252,7 +261,7 @@ int pa_oracle_cache_write(const void* k_src, const void* v_src, int src_dtype, c
                         if (ax > amax) amax = ax;
                     }
                     float s = amax / 127.0f; /* binary32 division, correctly rounded */
-                    scale[row] = s;
+                    scale[srow] = s;
                     for (int d = 0; d < D; ++d) {
                         float x = (float)elem(src, src_dtype, s0 + d);
                         int c = 0;
@@ -272,7 +281,7 @@ int pa_oracle_cache_write(const void* k_src, const void* v_src, int src_dtype, c
                         if (ax > amax) amax = ax;
                     }
                     float s = amax / 448.0f; /* binary32 division, correctly rounded */
-                    scale[row] = s;
+                    scale[srow] = s;
                     for (int d = 0; d < D; ++d) {
                         float x = (float)elem(src, src_dtype, s0 + d);
                         int c = 0;
@@ -289,7 +298,7 @@ int pa_oracle_cache_write(const void* k_src, const void* v_src, int src_dtype, c
                         if (ax > amax) amax = ax;
                     }
                     const float S = amax / 2688.0f; /* 6 * 448, binary32 division */
-                    scale[row] = S;
+                    scale[srow] = S;
                     if (amax != 0.0f) {
                         for (int b0 = 0; b0 < D; b0 += 16) {
                             float bmax = 0.0f;
@@ -346,7 +355,7 @@ static void row_logits(const args_t* a, int b, int t, int h, int64_t n, double* 
         int64_t row = (blk * a->block_size + j % a->block_size) * a->Hkv + g;
         double dot = 0.0;
         for (int d = 0; d < a->D; ++d)
-            dot += elem(a->q, a->q_dtype, qoff + d) * cache_elem(a->k_cache, a->kv_dtype, a->k_scale, row, a->Hkv, a->D, d);
+            dot += elem(a->q, a->q_dtype, qoff + d) * cache_elem(a->k_cache, a->kv_dtype, a->k_scale, row, a->Hkv, a->block_size, a->D, d);
         s[j] = (double)a->softmax_scale * dot;
     }
 }
@@ -354,7 +363,7 @@ static void row_logits(const args_t* a, int b, int t, int h, int64_t n, double* 
 static void value_row_axpy(const args_t* a, int b, int g, int64_t j, double w, double* acc) {
     int64_t blk = a->block_table[(int64_t)b * a->max_blocks + j / a->block_size];
     int64_t row = (blk * a->block_size + j % a->block_size) * a->Hkv + g;
-    for (int d = 0; d < a->D; ++d) acc[d] += w * cache_elem(a->v_cache, a->kv_dtype, a->v_scale, row, a->Hkv, a->D, d);
+    for (int d = 0; d < a->D; ++d) acc[d] += w * cache_elem(a->v_cache, a->kv_dtype, a->v_scale, row, a->Hkv, a->block_size, a->D, d);
 }
 
 /* Number of keys query token t of sequence b sees (causal inside the Tq new

@@ -42,6 +42,8 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
     const int64_t slot = p.slots[i];
     if (slot < 0) return;  // wave-uniform
     const int64_t dst_row = slot * p.Hkv + g;  // (block * 16 + offset) * Hkv + g
+    // scales [num_blocks, Hkv, 16]: a kv head's scales of a block together
+    const int64_t srow = ((slot / kBlockSize) * p.Hkv + g) * kBlockSize + slot % kBlockSize;
     const int64_t dst_off = dst_row * D + lane * EPL;
 
 #pragma unroll
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
                 if ((lane & 1) == 0) row[lane / 2] = (unsigned char)(nib | (hi << 4));
             }
             if (lane % LPB == 0) plane[nvfp4_scale_byte(t, lane / LPB)] = (unsigned char)sb;
-            if (lane == 0) (which ? p.v_scale : p.k_scale)[dst_row] = S;
+            if (lane == 0) (which ? p.v_scale : p.k_scale)[srow] = S;
         } else if constexpr (CT == KV_F32) {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) reinterpret_cast<float*>(cache)[dst_off + e] = x[e];
@@ -143,7 +145,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(CacheWriteParams p) {
                 *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
             else
                 *dst = (int8_t)packed;
-            if (lane == 0) (which ? p.v_scale : p.k_scale)[dst_row] = s;
+            if (lane == 0) (which ? p.v_scale : p.k_scale)[srow] = s;
         }
     }
 }

@@ -279,7 +279,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
         float vmax = 0.0f;
         for (int j = j0 + (threadIdx.x >> 4); j < jend; j += 4 * kW) {
             const int pos = j * kBlockSize + l16;
-            if (pos < end) vmax = fmaxf(vmax, p.v_scale[((int64_t)table[j] * kBlockSize + l16) * p.Hkv + g]);
+            if (pos < end) vmax = fmaxf(vmax, p.v_scale[((int64_t)table[j] * p.Hkv + g) * kBlockSize + l16]);
         }
         vmax = wave_max(vmax);
         __syncthreads();
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
         if constexpr (QNT) {
             // one load for the block's 32 scales (lanes 32..63 repeat 0..31)
             const float* src = (lane & 16) ? p.v_scale : p.k_scale;
-            dst.sc = src[(ph * kBlockSize + l16) * p.Hkv + g];
+            dst.sc = src[(ph * p.Hkv + g) * kBlockSize + l16];
         }
     };
     auto store_k = [&](const Blk& src, int stage, int h) {

@@ -382,7 +382,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
         float vmax = 0.0f;
         for (int j = j0 + sub + WPH * (lane >> 4); j < jend; j += 4 * WPH) {
             const int64_t ph = table[j];
-            const float sv = p.v_scale[(ph * kBlockSize + c16) * p.Hkv + g];
+            const float sv = p.v_scale[(ph * p.Hkv + g) * kBlockSize + c16];
             const int pos = j * kBlockSize + c16;
             if (pos < end) vmax = fmaxf(vmax, sv);
         }
@@ -412,7 +412,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     const int vsw_off = plane + 16 * (vl * VB / 8) + 8 * (vgrp & 1);
     // byte s of perm(ksw, ksw, ksel) is byte s ^ sx of ksw (slot s's scale)
     const uint32_t ksel = 0x03020100u ^ (0x01010101u * (uint32_t)sx);
-    const int soff = (my_tok * p.Hkv + g) * 4;  // scale of the lane's token within a block's scales
+    const int soff = (g * kBlockSize + my_tok) * 4;  // scale of the lane's token within a block's scales
     const int jw = j0 + sub;  // this wave's first block; it takes every WPH-th block
     int64_t phys = jw < jend ? (int64_t)table[jw] : 0;
     auto load_k = [&](int64_t ph) {

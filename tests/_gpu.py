@@ -47,7 +47,7 @@ def poisoned_cache(w: Workload):
     dt = TORCH_DT[sp.cache_dtype]
     if sp.cache_dtype in ("i8", "fp8", "nvfp4"):
         k = torch.full(shape, POISON_CODE, dtype=torch.uint8, device=dev()).view(dt)
-        ks = torch.full(shape[:3], float("nan"), dtype=torch.float32, device=dev())
+        ks = torch.full((shape[0], sp.Hkv, BLOCK_SIZE), float("nan"), dtype=torch.float32, device=dev())
         return k, k.clone(), ks, ks.clone()
     if sp.cache_dtype == "bf16":
         k = torch.full(shape, 0x7FC0, dtype=torch.int16, device=dev()).view(torch.bfloat16)

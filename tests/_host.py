@@ -32,7 +32,7 @@ def poison_host(w: Workload, k, v, ks, vs) -> None:
             c[blk, off] = POISON_CODE
     for s in (ks, vs):
         if s is not None:
-            s[blk, off] = np.nan
+            s[blk, :, off] = np.nan  # scales [num_blocks, Hkv, 16]
 
 
 def oracle_cache(w: Workload, poison: bool = True):

@@ -65,7 +65,14 @@ def _nvfp4_f64(a: np.ndarray, scale: np.ndarray, D: int) -> np.ndarray:
 
     codes, sc = nvfp4_split(a, D)
     bsc = torch.from_numpy(sc).view(torch.float8_e4m3fn).to(torch.float64).numpy()
-    return _e2m1(codes) * np.repeat(bsc, 16, axis=-1) * scale.astype(np.float64)[..., None]
+    return _e2m1(codes) * np.repeat(bsc, 16, axis=-1) * _row_scales(scale)[..., None]
+
+
+def _row_scales(scale: np.ndarray) -> np.ndarray:
+    """fp32 scales [num_blocks, Hkv, 16] as float64 [num_blocks, 16, Hkv], the
+    cache's (block, token, head) order."""
+    assert scale.ndim == 3
+    return np.swapaxes(scale, 1, 2).astype(np.float64)
 
 
 def as_f64(a: np.ndarray, scale: Optional[np.ndarray] = None) -> np.ndarray:
@@ -75,7 +82,7 @@ def as_f64(a: np.ndarray, scale: Optional[np.ndarray] = None) -> np.ndarray:
         return bf16_bits_to_f32(a).reshape(a.shape).astype(np.float64)
     if a.dtype == np.int8:
         assert scale is not None
-        return a.astype(np.float64) * scale.astype(np.float64)[..., None]
+        return a.astype(np.float64) * _row_scales(scale)[..., None]
     if a.dtype == np.uint8 and a.shape[-1] in _NVFP4_D:
         return _nvfp4_f64(a, scale, _NVFP4_D[a.shape[-1]])
     if a.dtype == np.uint8:
@@ -83,7 +90,7 @@ def as_f64(a: np.ndarray, scale: Optional[np.ndarray] = None) -> np.ndarray:
 
         assert scale is not None
         vals = torch.from_numpy(np.ascontiguousarray(a)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
-        return vals * scale.astype(np.float64)[..., None]
+        return vals * _row_scales(scale)[..., None]
     return a.astype(np.float64)
 
 

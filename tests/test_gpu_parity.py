@@ -280,14 +280,14 @@ def test_fp8_cache_write_of_hand_derived_rows():
     oracle.cache_write(x, x, np.arange(N), hk, hv, hks, hvs)
     k = torch.zeros((1, BLOCK_SIZE, 1, D), dtype=torch.uint8, device=dev()).view(torch.float8_e4m3fn)
     v = k.clone()
-    ks = torch.zeros((1, BLOCK_SIZE, 1), dtype=torch.float32, device=dev())
+    ks = torch.zeros((1, 1, BLOCK_SIZE), dtype=torch.float32, device=dev())
     vs = ks.clone()
     src = torch.from_numpy(x).to(dev())
     pa.cache_write(src, src, torch.arange(N, dtype=torch.int64, device=dev()), k, v, ks, vs)
     torch.cuda.synchronize()
     assert np.array_equal(dev_to_host(k)[0, :N], hk[0, :N])
     assert np.array_equal(dev_to_host(v)[0, :N], hv[0, :N])
-    assert np.array_equal(ks.cpu().numpy()[0, :N].view(np.uint32), hks[0, :N].view(np.uint32))
+    assert np.array_equal(ks.cpu().numpy()[0, 0, :N].view(np.uint32), hks[0, 0, :N].view(np.uint32))
     for i, c in enumerate(rows):
         assert dev_to_host(k)[0, i, 0, :len(c["codes"])].tolist() == c["codes"], c["why"]
 
@@ -312,13 +312,13 @@ def test_nvfp4_cache_write_of_the_hand_derived_row():
     RB = oracle.nvfp4_row_bytes(D)
     k = torch.full((1, BLOCK_SIZE, 1, RB), 0x55, dtype=torch.uint8, device=dev()).view(torch.float4_e2m1fn_x2)
     v = k.clone()
-    ks = torch.zeros((1, BLOCK_SIZE, 1), dtype=torch.float32, device=dev())
+    ks = torch.zeros((1, 1, BLOCK_SIZE), dtype=torch.float32, device=dev())
     vs = ks.clone()
     src = torch.from_numpy(x).to(dev())
     pa.cache_write(src, src, torch.full((1,), 5, dtype=torch.int64, device=dev()), k, v, ks, vs)
     torch.cuda.synchronize()
     assert np.array_equal(dev_to_host(k), hk) and np.array_equal(dev_to_host(v), hv)
-    assert ks.cpu().numpy()[0, 5, 0] == hks[0, 5, 0] == np.float32(row["row_scale"])
+    assert ks.cpu().numpy()[0, 0, 5] == hks[0, 0, 5] == np.float32(row["row_scale"])
     codes, scales = nvfp4_split(dev_to_host(k), D)
     for b, blk in enumerate(row["blocks"]):
         assert scales[0, 5, 0, b] == blk["scale_code"], b
@@ -331,6 +331,8 @@ def _slot_bytes(c: np.ndarray, slots: np.ndarray, spec) -> np.ndarray:
     if c.ndim == 4 and spec.cache_dtype == "nvfp4":
         idx = np.stack([nvfp4_token_bytes(spec.Hkv, spec.D, t) for t in range(BLOCK_SIZE)])
         return c.reshape(c.shape[0], -1)[slots[:, None] // BLOCK_SIZE, idx[slots % BLOCK_SIZE]]
+    if c.ndim == 3:  # scales [num_blocks, Hkv, 16]
+        return np.swapaxes(c, 1, 2).reshape(-1, spec.Hkv)[slots]
     return c.reshape((-1, spec.Hkv) + c.shape[3:])[slots]
 
 

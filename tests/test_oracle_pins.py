@@ -153,9 +153,10 @@ def test_gqa_equals_repeated_kv_mha():
     k, v, ks, vs = oracle_cache(w)
     out, lse = oracle_decode(w, (k, v, ks, vs))
     G = spec.G
-    rep = lambda a: np.ascontiguousarray(np.repeat(a, G, axis=2))
+    rep = lambda a, axis=2: np.ascontiguousarray(np.repeat(a, G, axis=axis))
+    # scales [num_blocks, Hkv, 16]: kv heads on axis 1
     out2, lse2 = oracle.decode(w.q_array(), rep(k), rep(v), w.block_table, w.seq_lens, w.softmax_scale,
-                               rep(ks), rep(vs))
+                               rep(ks, 1), rep(vs, 1))
     assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
 
 
@@ -473,7 +474,7 @@ def test_nvfp4_golden_row():
     k, v, ks, vs = oracle.alloc_cache(nb, BLOCK_SIZE, 1, D, "nvfp4")
     k[:] = 0xEE  # bytes of other rows: left as they are
     oracle.cache_write(x[None, None, :], x[None, None, :], np.array([5]), k, v, ks, vs)
-    assert ks[0, 5, 0] == np.float32(row["row_scale"])
+    assert ks[0, 0, 5] == np.float32(row["row_scale"])
     all_codes, all_scales = nvfp4_split(k, D)
     codes, scales = all_codes[0, 5, 0], all_scales[0, 5, 0]
     for b, blk in enumerate(row["blocks"]):
