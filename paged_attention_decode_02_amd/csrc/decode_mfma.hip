@@ -117,6 +117,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     // block pairs in flight per wave (register ring depth); at least 2, as the
     // keys of pair i + 1 are staged while pair i's values are
     constexpr int S2 = 2;
+    static_assert(S2 == 2, "the unmasked-pair argument of the block loop assumes two pairs per check");
     // Global loads: wave w moves rows 4w .. 4w+3 of a block's K and V tiles,
     // as runs of whole rows (RB bytes each), GB bytes per lane and load
     constexpr int RB = F4 ? D / 2 : D * E;           // code bytes of one cache row
@@ -446,7 +447,10 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     // Lane l ends with row l16's tokens 4 lg + 0..3 of both blocks, which is
     // the A-operand layout of a 16x16x32 PV product whose k index 8 lg + e
     // means token 4 lg + e % 4 of block e / 4 of the pair.
-    auto scores = [&](int i) {
+    // INNER: the pair lies wholly before the partition's end and before every
+    // valid row's causal limit, so only invalid rows need masking
+    auto scores = [&](int i, auto inner) {
+        constexpr bool INNER = decltype(inner)::value;
         const int stage = i & 1;
         const int jp = j0 + 2 * i;
         // int8: key and value scales of the lane's 4 tokens in each block
@@ -494,7 +498,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
             const f32x4 s = acc[h][0] + acc[h][1];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const bool ok = (jp + h) * kBlockSize + 4 * lg + e < nvis;
+                const bool ok = INNER ? row_ok : (jp + h) * kBlockSize + 4 * lg + e < nvis;
                 float ksc = qpost;
                 if constexpr (QNT) ksc *= kraw[h][e];
                 sc[h][e] = ok ? (s[e] - corr) * ksc : -INFINITY;
@@ -532,7 +536,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const bool ok = (jp + h) * kBlockSize + 4 * lg + e < end;
+                    const bool ok = INNER || (jp + h) * kBlockSize + 4 * lg + e < end;
                     ph2[h][e] = (float)(_Float16)(ok ? pr[h][e] * vraw[h][e] * vsh : 0.0f);
                     spart += ph2[h][e];
                 }
@@ -550,7 +554,8 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     };
 
     // PV of pair i (all waves): weights and values from LDS stage i % 2
-    auto values = [&](int i) {
+    auto values = [&](int i, auto inner) {
+        constexpr bool INNER = decltype(inner)::value;
         const int stage = i & 1;
         const int jp = j0 + 2 * i;
         u32x4 bop[NDT];
@@ -572,7 +577,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
                     const pa_f32x2 lo = fp8x2_to_f32<false>(tw), hi = fp8x2_to_f32<true>(tw);
                     w = u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo.x, lo.y)),
                               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi.x, hi.y))};
-                    if (pos0 + kBlockSize > end) {  // tokens past the end may hold NaN codes
+                    if (!INNER && pos0 + kBlockSize > end) {  // tokens past the end may hold NaN codes
                         const int t0 = pos0 + 4 * lg;  // element k is token 4*lg + k
                         w.x = (t0 + 0 < end ? w.x & 0x0000FFFFu : 0u) | (t0 + 1 < end ? w.x & 0xFFFF0000u : 0u);
                         w.y = (t0 + 2 < end ? w.y & 0x0000FFFFu : 0u) | (t0 + 3 < end ? w.y & 0xFFFF0000u : 0u);
@@ -584,7 +589,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
                     const unsigned char* src =
                         &vst[stage][h][4 * lg + (l16 >> 2)][(wv * DW + 16 * nd + 4 * (l16 & 3)) * 2];
                     w = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)src));
-                    if (pos0 + kBlockSize > end) {  // tokens past the end may hold anything
+                    if (!INNER && pos0 + kBlockSize > end) {  // tokens past the end may hold anything
                         const int t0 = pos0 + 4 * lg;  // element k is token 4*lg + k
                         w.x = (t0 + 0 < end ? w.x & 0x0000FFFFu : 0u) | (t0 + 1 < end ? w.x & 0xFFFF0000u : 0u);
                         w.y = (t0 + 2 < end ? w.y & 0x0000FFFFu : 0u) | (t0 + 3 < end ? w.y & 0xFFFF0000u : 0u);
@@ -633,13 +638,19 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
         store_k(ring[0][0], 0, 0);
         store_k(ring[0][1], 0, 1);
         __syncthreads();
-        if (owner) scores(0);
+        if (owner) scores(0, std::false_type{});
     }
     // physical blocks of pair i + S2 at iteration i, not yet uniform
     int tp0 = (int)phys_of(j0 + 2 * S2), tp1 = (int)phys_of(j0 + 2 * S2 + 1);
     // iteration i: stage K(pair i+1) and V(pair i), barrier, scores of pair
     // i+1, PV of pair i. FULL: the pair this iteration requests starts inside
-    // the partition.
+    // the partition. The main loop runs S2 = 2 iterations per check of
+    // i + 2 S2 <= npair, so in both of them pair i ends at least 3 blocks
+    // before the partition's last block (its values need no mask), and in the
+    // first (X = 0) so does pair i + 1, which then also lies inside every
+    // valid row's causal range (at most Tq - 1 <= 15 tokens short of the end):
+    // its scores need no mask either. In the second, pair i + 1 may reach the
+    // block before the last, within that causal margin.
     auto iter = [&](int i, auto xc, auto full) __attribute__((always_inline)) {
         constexpr int X = decltype(xc)::value;  // slot of pair i: i % S2
         constexpr int Y = (X + 1) % S2;         // slot of pair i + 1
@@ -658,8 +669,8 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
             load_blk(ring[X][1], ph1);
         }
         __syncthreads();
-        if (owner && (FULL || i + 1 < npair)) scores(i + 1);
-        values(i);
+        if (owner && (FULL || i + 1 < npair)) scores(i + 1, std::integral_constant<bool, FULL && X == 0>{});
+        values(i, full);
         tp0 = tn0;
         tp1 = tn1;
         // keep the next iteration's table wait behind this iteration's work
