@@ -547,7 +547,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
         }
 
         // scores of the lane's items, log2 units; masked past the end
-        const bool tok_ok = pos0 + my_tok < end;
+        // a block followed by another of this wave (MORE) is not the
+        // partition's last and lies wholly before its end, which for this
+        // workgroup's one query token is also the causal limit
+        const bool tok_ok = MORE || pos0 + my_tok < end;
         float ksc = qpost;
         if constexpr (QNT) ksc *= kscale_raw;
         float sc[NI];
@@ -621,7 +624,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
             vs[1] = vsw.w[1] >> sh;
         }
         if constexpr (!I8) {
-            if (pos0 + kBlockSize > end) {
+            if (!MORE && pos0 + kBlockSize > end) {
 #pragma unroll
                 for (int st = 0; st < STEPS; ++st) {
                     const bool ok = pos0 + tok_of(st) < end;
