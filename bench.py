@@ -70,12 +70,12 @@ _COMMON = ("pa_device.hpp", "pa_internal.hpp")
 def decode_kernel(spec) -> tuple:
     """(name, sources) of the decode kernel that runs the workload, by the
     library's rule: the plain kernel for fp32 caches; the matrix-core kernel
-    for Tq > 1, for groups of 16+ query heads, and for int8 caches from 6;
+    for Tq > 1, for groups of 16+ query heads, and for int8 and FP8 caches from 6;
     the vector-ALU kernel otherwise."""
     if spec.cache_dtype == "f32":
         return "decode_valu_kernel", ("decode_valu.hip",) + _COMMON
     G = spec.Hq // spec.Hkv
-    if spec.Tq > 1 or G >= 16 or (spec.cache_dtype == "i8" and G >= 6):
+    if spec.Tq > 1 or G >= 16 or (spec.cache_dtype in ("i8", "fp8") and G >= 6):
         return "decode_mfma_kernel", ("decode_mfma.hip",) + _COMMON
     return "decode_wave_kernel", ("decode_wave.hip",) + _COMMON
 

@@ -81,14 +81,17 @@ int64_t row_bytes(pa_dtype t, int32_t D) {
 // the vector-ALU kernel once per query token, with work that grows with G.
 // Measured (kernel times, 16K-250K tokens, D 128 and 256): with Tq > 1 the
 // matrix cores take 0.17-0.86x the time for every group size and cache type;
-// with Tq = 1 they win from G = 16 (a full row tile), and for int8 caches
-// already from G = 6 (0.77-0.95x; the vector-ALU int8 decode is bound by its
-// code widening and dot products, the matrix-core one is not), while for
-// bf16, FP8 and NVFP4 below 16 rows the vector ALU is as fast or faster.
+// with Tq = 1 they win from G = 16 (a full row tile), and for int8 and FP8
+// caches already from G = 6 (int8 0.77-0.95x; FP8 at 250K tokens: step 112 ->
+// 105 us; the vector-ALU decode is bound by its code widening and dot
+// products, the matrix-core one is not). bf16 below 16 rows is a wash (64K:
+// decode 0.7% slower, step 1.3% faster through half the partitions; short
+// variable-length batches 5% slower) and NVFP4 is faster on the vector ALU
+// (250K: decode 92 against 103 us), so both stay there.
 bool use_mfma(int32_t Tq, int32_t Hq, int32_t Hkv, pa_dtype kv_dtype) {
     if (kv_dtype == PA_F32) return false;
     const int64_t G = Hq / Hkv;
-    return Tq > 1 || G >= 16 || (kv_dtype == PA_I8 && G >= 6);
+    return Tq > 1 || G >= 16 || ((kv_dtype == PA_I8 || kv_dtype == PA_FP8) && G >= 6);
 }
 
 // Row tiles per workgroup and row chunks of the matrix-core kernel.

@@ -91,9 +91,10 @@ def test_workspace_size_and_partition_choice(lib):
     # int8 caches with G = 6 run on the matrix cores: two workgroups per CU,
     # one per (kv head, partition): 127 partitions x 4 kv heads
     assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 2, 250000) == 1984
-    # fp8 caches with G = 6 stay on the vector ALU: two workgroups per CU, each
-    # taking two kv heads: 253 partitions x 2 = 506 workgroups
-    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 3, 250000) == 992
+    # so do fp8 caches; nvfp4 caches with G = 6 stay on the vector ALU: two
+    # workgroups per CU, each taking two kv heads: 253 partitions x 2
+    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 3, 250000) == 1984
+    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 4, 250000) == 992
     # int8 with G = 4 stays on the vector ALU
     assert lib.pa_choose_partition_size(1, 1, 16, 4, 256, 2, 250000) == 992
     assert lib.pa_choose_partition_size(4, 8, 24, 4, 256, 3, 30321) == 960

@@ -372,7 +372,7 @@ def test_cache_write_skips_negative_slots_and_writes_bits():
 
 
 # ------------------------------------------------------------ matrix-core path
-# Tq > 1, G >= 16, and int8 with G >= 6 run on the MFMA kernel (bf16 / int8 /
+# Tq > 1, G >= 16, and int8 / fp8 with G >= 6 run on the MFMA kernel (bf16 / int8 /
 # fp8 / nvfp4 caches), including row counts below one 16-row tile.
 @pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "nvfp4"])
 @pytest.mark.parametrize("D", [64, 128, 256])
