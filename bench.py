@@ -15,6 +15,9 @@ timed too and reported beside it; on this ROCm they are a few percent slower
 than eager launches.
 Default workload: long-context decode at 64K tokens per sequence (B=4,
 Hq=24, Hkv=4, D=256, bf16 KV).
+With --shared-prefix (workloads whose sequences share a prefix) the decode
+of a step is one pa_decode_shared_prefix call: a pass over the shared blocks
+for the whole batch, a pass over each sequence's own tokens, and their merge.
 
 Printed: ONE JSON line with the metric (algorithmic KV-read GB/s), the step
 time, a roofline object for the decode kernel (its algorithmic bytes per
@@ -65,6 +68,16 @@ def algorithmic_bytes(w) -> dict:
 
 
 _COMMON = ("pa_device.hpp", "pa_internal.hpp")
+
+
+def unique_bytes(w) -> int:
+    """Algorithmic bytes when the shared prefix is read once for the batch
+    (the shared-prefix decode): the prefix's tokens once, every sequence's own
+    tokens, plus the same table, q and out terms."""
+    sp = w.spec
+    ab = algorithmic_bytes(w)
+    per_tok = ab["kv"] // int(w.seq_lens.astype(np.int64).sum()) + ab["scales"] // int(w.seq_lens.sum())
+    return ab["total"] - (sp.B - 1) * sp.shared_prefix * per_tok
 
 
 def decode_kernel(spec) -> tuple:
@@ -269,6 +282,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--partition-size", type=int, default=0, help="0 = the library's heuristic")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="decode through pa_decode_shared_prefix (workloads with a shared prefix)")
+    ap.add_argument("--prefix-partition", type=int, default=0, help="--shared-prefix: prefix pass partition (0 = "
+                    "the library's choice)")
+    ap.add_argument("--tail-partition", type=int, default=0, help="--shared-prefix: tail pass partition (0 = the "
+                    "library's choice)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
@@ -309,6 +328,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     spec = SPECS[args.workload]
+    if args.shared_prefix and not spec.shared_prefix:
+        print("--shared-prefix needs a workload whose sequences share a prefix", file=sys.stderr)
+        sys.exit(2)
 
     t0 = time.time()
     w = generate(spec)
@@ -348,6 +370,12 @@ def main():
     P = args.partition_size or pa.choose_partition_size(sp.B, sp.Tq, sp.Hq, sp.Hkv, sp.D, TD[sp.cache_dtype],
                                                         w.max_seq_len)
     ws_bytes = pa.workspace_bytes(sp.B, sp.Tq, sp.Hq, sp.Hkv, sp.D, TD[sp.cache_dtype], w.max_seq_len, P)
+    prefix_table = None
+    if args.shared_prefix:
+        ws_bytes = pa.shared_prefix_workspace_bytes(sp.B, sp.Tq, sp.Hq, sp.Hkv, sp.D, TD[sp.cache_dtype],
+                                                    w.max_seq_len, sp.shared_prefix, args.prefix_partition,
+                                                    args.tail_partition)
+        prefix_table = torch.from_numpy(np.ascontiguousarray(w.block_table[0, : sp.shared_prefix // 16])).to(dev)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty((sp.B, sp.Tq, sp.Hq, sp.D), dtype=torch.float32, device=dev)
     lse = torch.empty((sp.B, sp.Tq, sp.Hq), dtype=torch.float32, device=dev)
@@ -362,6 +390,14 @@ def main():
         pa.cache_write(new_k, new_v, new_slots, kc, vc, ks, vs)
         if ev is not None:
             ev[1].record(stream)
+        if args.shared_prefix:
+            pa.decode_shared_prefix(q, kc, vc, prefix_table, sp.shared_prefix, table, lens, w.max_seq_len,
+                                    w.softmax_scale, ks, vs, args.prefix_partition, args.tail_partition, out=out,
+                                    lse=lse, workspace=ws)
+            if ev is not None:
+                ev[2].record(stream)
+                ev[3].record(stream)
+            return
         state["np"] = pa.decode_partials(q, kc, vc, table, lens, w.max_seq_len, w.softmax_scale, out, lse, ks, vs,
                                          P, ws)
         if ev is not None:
@@ -448,6 +484,11 @@ def main():
     ws_traffic = 0
     if state["np"] > 1:
         ws_traffic = 2 * sp.B * sp.Tq * sp.Hq * state["np"] * (sp.D + 1) * 4
+    if args.shared_prefix:
+        ws_traffic = 2 * ws_bytes
+        # the call's three kernels against the bytes it must read: the shared
+        # prefix once, each sequence's own tokens
+        achieved = unique_bytes(w) / (dec_avg_ms * 1e-3) / 1e9
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -468,8 +509,12 @@ def main():
             "block_size": BLOCK_SIZE, "seq_lens": "%d..%d" % (w.seq_lens.min(), w.seq_lens.max()),
             "kv_dtype": sp.cache_dtype, "q_dtype": sp.q_dtype, "partition_size": P,
             "num_partitions": state["np"], "algorithmic_bytes_per_step": ab["total"],
+            "shared_prefix": sp.shared_prefix,
+            "prefix_partition": args.prefix_partition if args.shared_prefix else None,
+            "tail_partition": args.tail_partition if args.shared_prefix else None,
             "splitk_workspace_bytes_per_step": ws_traffic,
         },
+        "path": "shared_prefix" if args.shared_prefix else "decode",
         "timing": "eager launches, K steps between two device synchronisations",
         "graph_us_per_step": round(graph_ms * 1e3, 2) if graph_ms is not None else None,
         "breakdown_us": {
@@ -480,13 +525,14 @@ def main():
             "decode_plus_reduce_after_flush": round(1e3 * float(np.median(cold)), 2),
         },
         "roofline": {
-            "kernel": decode_kernel(sp)[0],
+            "kernel": ("pa_decode_shared_prefix: prefix pass, tail pass and merge, against the bytes with the "
+                       "prefix read once" if args.shared_prefix else decode_kernel(sp)[0]),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": committed_traffic(sp),
+            "traffic": None if args.shared_prefix else committed_traffic(sp),
             "kernel_source_digest": kernel_source_digest(sp),
         },
     }

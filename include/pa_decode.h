@@ -171,6 +171,52 @@ int pa_decode_splitk_reduce(const void* workspace, int32_t num_partitions, int32
                             int32_t Tq, int32_t Hq, int32_t D, const int32_t* seq_lens, void* out,
                             pa_dtype out_dtype, float* lse, void* stream);
 
+/*
+ * pa_decode_shared_prefix — pa_decode for a batch whose sequences all begin
+ * with the same prefix_len tokens stored in the same physical blocks (prefix
+ * caching: vllm-sm12x-nvfp4-dflash2 page, "What makes this stack different",
+ * capacity-first profile; 1Cat-vLLM docs index, feature list). Computes
+ * exactly what pa_decode computes (same out and lse definitions, same
+ * tolerances), but reads the shared blocks once per kv head and group of 64
+ * query rows for the whole batch instead of once per sequence:
+ *  1. prefix pass: the Tq * (Hq / Hkv) query rows of every sequence that use
+ *     kv head g form one row set (B * Tq * Hq / Hkv rows) on the matrix
+ *     cores, against keys 0 .. prefix_len - 1 read through prefix_table;
+ *  2. tail pass: each sequence against its own keys prefix_len ..
+ *     seq_lens[b] - 1 through block_table[b][prefix_len / 16 ..], causal mask
+ *     as in pa_decode;
+ *  3. the log-sum-exp merge of both passes' partials (as in
+ *     pa_decode_splitk_reduce) into out and lse.
+ * Arguments as for pa_decode, plus:
+ *   prefix_table     [prefix_len / 16] int32 physical block ids of the shared
+ *                    tokens (a row of block_table may serve); each in
+ *                    [0, num_blocks). May be NULL when prefix_len == 0.
+ *   prefix_len       (host) shared tokens, a multiple of 16, with
+ *                    prefix_len + Tq <= max_seq_len.
+ *   prefix_partition, tail_partition  split-K partition sizes of the two
+ *                    passes (multiples of 16), 0 = the library's choice.
+ *   workspace        >= pa_decode_shared_prefix_workspace_bytes with the same
+ *                    arguments; 16-byte aligned; NULL allowed when that is 0.
+ * Device contract (trusted, as for pa_decode): every sequence's query tokens
+ * lie after the prefix, prefix_len + Tq <= seq_lens[b] <= max_seq_len; the
+ * blocks block_table[b][0 .. prefix_len / 16 - 1] are not read. Always
+ * writes out (and lse if non-NULL): no separate reduce call. fp32 caches
+ * return PA_ERR_UNSUPPORTED.
+ */
+int pa_decode_shared_prefix(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv,
+                            int32_t D, const void* k_cache, const void* v_cache, pa_dtype kv_dtype,
+                            const float* k_scale, const float* v_scale, int64_t num_blocks, int32_t block_size,
+                            const int32_t* prefix_table, int32_t prefix_len, const int32_t* block_table,
+                            int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                            float softmax_scale, int32_t prefix_partition, int32_t tail_partition, void* out,
+                            pa_dtype out_dtype, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pa_decode_shared_prefix needs for these arguments (0
+ * when one partition covers everything, or for invalid arguments). */
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D,
+                                               pa_dtype kv_dtype, int32_t max_seq_len, int32_t prefix_len,
+                                               int32_t prefix_partition, int32_t tail_partition);
+
 /* Bytes of workspace pa_decode needs (0 when one partition covers
  * max_seq_len). partition_size 0 means the heuristic's choice, as in
  * pa_decode; the caller must pass the same arguments to both. Returns 0 for

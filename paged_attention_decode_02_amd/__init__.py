@@ -10,6 +10,8 @@ not been built the functions raise; there is no fallback.
                       softmax_scale, k_scale=None, v_scale=None, partition_size=0)
     np_ = decode_partials(...)        # the split-K kernel alone
     splitk_reduce(workspace, np_, partition_size, seq_lens, out, lse)
+    out, lse = decode_shared_prefix(q, k_cache, v_cache, prefix_table, prefix_len, block_table,
+                                    seq_lens, max_seq_len, softmax_scale, ...)
 """
 from __future__ import annotations
 
@@ -22,7 +24,8 @@ import torch
 
 __all__ = [
     "PaError", "cache_write", "decode", "decode_partials", "splitk_reduce", "workspace_bytes",
-    "choose_partition_size", "library_path", "load", "DTYPE_CODE",
+    "choose_partition_size", "library_path", "load", "DTYPE_CODE", "decode_shared_prefix",
+    "shared_prefix_workspace_bytes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -39,6 +42,7 @@ DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.int8: 2, torch.float8_e
 EXPORTS = (
     "pa_cache_write", "pa_decode", "pa_decode_splitk_reduce", "pa_decode_workspace_bytes",
     "pa_choose_partition_size", "pa_decode_check", "pa_cache_write_check", "pa_last_error",
+    "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes",
 )
 
 
@@ -79,6 +83,11 @@ def load():
         lib.pa_decode_check.restype = ctypes.c_int
         lib.pa_cache_write_check.argtypes = [P, I64, I64, I32, P, P]
         lib.pa_cache_write_check.restype = ctypes.c_int
+        lib.pa_decode_shared_prefix.argtypes = [P, I32, I32, I32, I32, I32, I32, P, P, I32, P, P, I64, I32, P, I32,
+                                                P, I32, P, I32, F, I32, I32, P, I32, P, P, SZ, P]
+        lib.pa_decode_shared_prefix.restype = ctypes.c_int
+        lib.pa_decode_shared_prefix_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32, I32, I32]
+        lib.pa_decode_shared_prefix_workspace_bytes.restype = SZ
         lib.pa_last_error.argtypes = []
         lib.pa_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -246,4 +255,47 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_
                           k_scale, v_scale, P, workspace, stream)
     if np_ > 1:
         splitk_reduce(workspace, np_, P, seq_lens, out, lse, stream)
+    return out, lse
+
+
+def shared_prefix_workspace_bytes(B: int, Tq: int, Hq: int, Hkv: int, D: int, kv_dtype: torch.dtype,
+                                  max_seq_len: int, prefix_len: int, prefix_partition: int = 0,
+                                  tail_partition: int = 0) -> int:
+    return int(load().pa_decode_shared_prefix_workspace_bytes(B, Tq, Hq, Hkv, D, DTYPE_CODE[kv_dtype], max_seq_len,
+                                                              prefix_len, prefix_partition, tail_partition))
+
+
+def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, prefix_table: torch.Tensor,
+                         prefix_len: int, block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                         softmax_scale: float, k_scale: Optional[torch.Tensor] = None,
+                         v_scale: Optional[torch.Tensor] = None, prefix_partition: int = 0, tail_partition: int = 0,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32,
+                         stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Decode of a batch whose sequences share their first prefix_len tokens
+    (blocks prefix_table [prefix_len / 16]); same result as decode(). Missing
+    out/lse/workspace tensors are allocated with torch."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (prefix_table, "prefix_table"),
+                 (block_table, "block_table"), (seq_lens, "seq_lens"), (out, "out"), (lse, "lse"),
+                 (k_scale, "k_scale"), (v_scale, "v_scale"), (workspace, "workspace")):
+        _dev(t, n)
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or prefix_table.dtype != torch.int32:
+        raise ValueError("prefix_table, block_table and seq_lens must be int32")
+    B, Tq, Hq, D = q.shape
+    nb, bs, Hkv, _ = k_cache.shape
+    if out is None:
+        out = torch.empty((B, Tq, Hq, D), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = shared_prefix_workspace_bytes(B, Tq, Hq, Hkv, D, k_cache.dtype, max_seq_len, prefix_len,
+                                               prefix_partition, tail_partition)
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_L().pa_decode_shared_prefix(
+        _ptr(q), _code(q), B, Tq, Hq, Hkv, D, _ptr(k_cache), _ptr(v_cache), _code(k_cache), _ptr(k_scale),
+        _ptr(v_scale), nb, bs, _ptr(prefix_table), int(prefix_len), _ptr(block_table), block_table.shape[1],
+        _ptr(seq_lens), int(max_seq_len), float(softmax_scale), int(prefix_partition), int(tail_partition),
+        _ptr(out), _code(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream, q)))
     return out, lse

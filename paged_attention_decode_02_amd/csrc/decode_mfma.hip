@@ -101,8 +101,18 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 }  // namespace
 
+// Two workgroups per CU (two waves per SIMD) need at most 256 registers per
+// lane of the unified VGPR/AGPR file. At D = 256 the instances with four row
+// tiles, or three with fp32 queries, exceed that unless bounded, and fit
+// without spills when bounded; the bf16, int8 and fp8 ones with four tiles
+// and fp32 queries would spill and keep one workgroup per CU.
 template <int KVT, int D, int NT, int QS>
-__global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
+constexpr int mfma_min_waves() {
+    return (D == 256 && NT + QS >= 5 && !(NT == 4 && QS == 2 && KVT != KV_NVFP4)) ? 2 : 1;
+}
+
+template <int KVT, int D, int NT, int QS>
+__global__ __launch_bounds__(64 * kW, (mfma_min_waves<KVT, D, NT, QS>())) void decode_mfma_kernel(DecodeParams p) {
     static_assert(KVT == KV_BF16 || KVT == KV_I8 || KVT == KV_FP8 || KVT == KV_NVFP4, "bf16, int8, fp8 or nvfp4");
     static_assert(NT >= 1 && NT <= kW, "one row tile per wave");
     constexpr bool I8 = KVT == KV_I8;
@@ -151,20 +161,27 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
     const int g = wg % p.Hkv;
     const int b = wg / p.Hkv;
 
-    const int G = p.G, Tq = p.Tq, R = G * Tq;
+    // Row r of the row set: sequence b + r / (Tq G) (stacked rows span the
+    // batch, whose grid coordinate b is then 0), token t, head g G + h'.
+    const int G = p.G, Tq = p.Tq, TG = G * Tq;
+    const int R = p.stacked ? p.B * TG : TG;
     const int row0 = rc * 16 * NT;
-    const int L = p.seq_lens[b];
-    const int rlast = min(R, row0 + 16 * NT) - 1;  // largest t is in the last row
-    const int n_chunk = L - Tq + rlast / G + 1;
+    const int rlast = min(R, row0 + 16 * NT) - 1;  // one sequence: largest t is in the last row
+    // keys of the row set: a sequence's own from kv_begin on (causal end
+    // L - Tq + t), or the shared list's first prefix_len, visible to all rows
+    const int L = p.stacked ? p.prefix_len : p.seq_lens[b] - p.kv_begin;
+    const int n_chunk = p.stacked ? L : L - Tq + rlast / G + 1;
     const int start = part * p.P;
+    const int64_t wpart = p.part_base + part;  // workspace partition
 
-    auto row_out = [&](int r) -> int64_t {  // flat (b, t, h) row id of chunk row r
-        const int t = r / G, hh = r % G;
-        return ((int64_t)b * Tq + t) * p.Hq + g * G + hh;
+    auto row_out = [&](int r) -> int64_t {  // flat (b, t, h) row id of row r
+        const int bb = b + r / TG, rr = r % TG;
+        const int t = rr / G, hh = rr % G;
+        return ((int64_t)bb * Tq + t) * p.Hq + g * G + hh;
     };
 
     if (start >= n_chunk) {
-        if (p.NP == 1) {
+        if (p.np_stride == 1) {
             for (int r = row0; r <= rlast; ++r) {
                 const int64_t rid = row_out(r);
                 for (int d = threadIdx.x; d < D; d += 64 * kW) {
@@ -175,6 +192,9 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
                 }
                 if (p.lse != nullptr && threadIdx.x == 0) p.lse[rid] = -INFINITY;
             }
+        } else if (p.fill_empty) {
+            for (int r = row0 + (int)threadIdx.x; r <= rlast; r += 64 * kW)
+                p.ws_lse[row_out(r) * p.np_stride + wpart] = -INFINITY;
         }
         return;
     }
@@ -248,7 +268,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
 
     // ------------------------------------------------------- softmax state
     // owner, score layout: lane holds row myrow, tokens 4*lg + i of a block
-    const int nvis = row_ok ? min(end, L - Tq + myrow / G + 1) : 0;
+    const int nvis = !row_ok ? 0 : p.stacked ? end : min(end, L - Tq + myrow / G + 1);
     float mref = -INFINITY, lpart = 0.0f, spart = 0.0f;
     // output layout: lane holds rows 16*t + 4*lg + i, dim wv*DW + 16*nd + l16
     f32x4 o[NT][NDT];
@@ -257,7 +277,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
         for (int nd = 0; nd < NDT; ++nd) o[t][nd] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int32_t* table = p.block_table + (int64_t)b * p.max_blocks;
+    const int32_t* table = p.stacked ? p.block_table : p.block_table + (int64_t)b * p.max_blocks + p.kv_begin / kBlockSize;
     const int64_t tok_stride = (int64_t)p.Hkv * RBQ;
     const int64_t blk_bytes = kBlockSize * (int64_t)p.Hkv * kv_row_bytes<KVT>(D);  // nvfp4: + scale planes
     const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (int64_t)g * RBQ;
@@ -699,10 +719,10 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
             if (myrow < R) {
                 const float lse2 = l > 0.0f ? (mref + log2f(l)) * kLn2 : -INFINITY;
                 const int64_t rid = row_out(myrow);
-                if (p.NP == 1) {
+                if (p.np_stride == 1) {
                     if (p.lse != nullptr) p.lse[rid] = lse2;
                 } else {
-                    p.ws_lse[rid * p.NP + part] = lse2;
+                    p.ws_lse[rid * p.np_stride + wpart] = lse2;
                 }
             }
         }
@@ -724,13 +744,13 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
                 if constexpr (F8 || F4) v *= vsh_inv;
                 v *= inv;
                 const int d = wv * DW + 16 * nd + l16;
-                if (p.NP == 1) {
+                if (p.np_stride == 1) {
                     if (p.out_bf16)
                         reinterpret_cast<uint16_t*>(p.out)[rid * D + d] = f32_to_bf16(v);
                     else
                         reinterpret_cast<float*>(p.out)[rid * D + d] = v;
                 } else {
-                    p.ws_o[(rid * p.NP + part) * D + d] = v;
+                    p.ws_o[(rid * p.np_stride + wpart) * D + d] = v;
                 }
             }
         }
@@ -740,7 +760,7 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeParams p) {
 namespace {
 template <int KVT, int D, int NT, int QS>
 hipError_t launch_one(const DecodeParams& p, hipStream_t s) {
-    const int64_t grid = (int64_t)p.NP * p.nchunk * p.Hkv * p.B;
+    const int64_t grid = (int64_t)p.NP * p.nchunk * p.Hkv * (p.stacked ? 1 : p.B);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((decode_mfma_kernel<KVT, D, NT, QS>), dim3((unsigned)grid), dim3(64 * kW), 0, s, p);

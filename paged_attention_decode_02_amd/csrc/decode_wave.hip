@@ -216,13 +216,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     const int t = wg % p.Tq;
     const int b = wg / p.Tq;
 
-    const int n = p.seq_lens[b] - p.Tq + t + 1;
+    // keys visible to query token t, counted from the sequence's token kv_begin
+    const int n = p.seq_lens[b] - p.kv_begin - p.Tq + t + 1;
     const int start = part * p.P;
+    const int64_t wpart = p.part_base + part;  // workspace partition
     const int hbase = g * p.G + chunk * GT;
     const int nh = min(GT, p.G - chunk * GT);
     const int64_t rowbase = ((int64_t)b * p.Tq + t) * p.Hq + hbase;  // flat row id of head hbase
     if (start >= n) {
-        if (p.NP == 1) {
+        if (p.np_stride == 1) {
             for (int r2 = 0; r2 < nh; ++r2) {
                 for (int d = sub * 64 + lane; d < D; d += 64 * WPH) {
                     if (p.out_bf16)
@@ -232,6 +234,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
                 }
                 if (p.lse != nullptr && sub == 0 && lane == 0) p.lse[rowbase + r2] = -INFINITY;
             }
+        } else if (p.fill_empty && sub == 0 && lane < nh) {
+            p.ws_lse[(rowbase + lane) * p.np_stride + wpart] = -INFINITY;
         }
         return;
     }
@@ -364,7 +368,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
         sloc[j] = 0.0f;
     }
 
-    const int32_t* table = p.block_table + (int64_t)b * p.max_blocks;
+    const int32_t* table = p.block_table + (int64_t)b * p.max_blocks + p.kv_begin / kBlockSize;
     // KV addressing: a buffer resource per block (scalar) plus per-lane
     // offsets that do not change from block to block; the host keeps a
     // block's bytes below 2^31
@@ -812,20 +816,20 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
             for (int k = 0; k < kWaves; ++k)
                 if (k < WPH) acc += wt[k] * merge_o[w0 + k][h][d];
             const float val = acc * inv;
-            if (p.NP == 1) {
+            if (p.np_stride == 1) {
                 if (p.out_bf16)
                     reinterpret_cast<uint16_t*>(p.out)[rowid * D + d] = f32_to_bf16(val);
                 else
                     reinterpret_cast<float*>(p.out)[rowid * D + d] = val;
             } else {
-                p.ws_o[(rowid * p.NP + part) * D + d] = val;
+                p.ws_o[(rowid * p.np_stride + wpart) * D + d] = val;
             }
         }
         if (lane == 0) {
-            if (p.NP == 1) {
+            if (p.np_stride == 1) {
                 if (p.lse != nullptr) p.lse[rowid] = lse2;
             } else {
-                p.ws_lse[rowid * p.NP + part] = lse2;
+                p.ws_lse[rowid * p.np_stride + wpart] = lse2;
             }
         }
     }

@@ -94,11 +94,13 @@ bool use_mfma(int32_t Tq, int32_t Hq, int32_t Hkv, pa_dtype kv_dtype) {
     return Tq > 1 || G >= 16 || ((kv_dtype == PA_I8 || kv_dtype == PA_FP8) && G >= 6);
 }
 
-// Row tiles per workgroup and row chunks of the matrix-core kernel.
+// Row tiles per workgroup and row chunks of the matrix-core kernel: at most
+// four tiles (one per wave) per chunk, the tiles spread evenly over the
+// chunks (96 rows: two chunks of three tiles, not four and two).
 void row_chunks(int32_t R, int* NT, int* nchunk) {
-    const int tiles = (R + 15) / 16;
-    *NT = tiles <= 4 ? tiles : 4;
-    *nchunk = (tiles + *NT - 1) / *NT;
+    const int tiles = R > 16 ? (R + 15) / 16 : 1;  // an empty batch still sizes one tile
+    *nchunk = (tiles + 3) / 4;
+    *NT = (tiles + *nchunk - 1) / *nchunk;
 }
 
 // Workgroups of the decode resident per CU that the partition heuristic aims
@@ -131,6 +133,23 @@ int heads_per_wg(pa_dtype kv_dtype, int32_t D, int GT, int32_t Hkv) {
     return Hkv % 4 == 0 ? 4 : (Hkv % 2 == 0 ? 2 : 1);
 }
 
+// Partition length for a context of len tokens when every partition index
+// launches per_partition workgroups: enough partitions that the launch fills
+// the GPU once at wgs workgroups per CU, each a multiple of gran tokens and at
+// least min_p long, and one partition when that covers the context.
+int32_t split_len(int64_t len, int64_t per_partition, int wgs, int64_t gran, int64_t min_p) {
+    const int64_t target = (int64_t)kCUs * wgs;  // workgroups that fill the GPU once
+    if (per_partition < 1) per_partition = 1;   // an empty batch (B = 0)
+    int64_t want_np = (target + per_partition - 1) / per_partition;
+    if (want_np < 1) want_np = 1;
+    int64_t P = (len + want_np - 1) / want_np;
+    P = (P + gran - 1) / gran * gran;
+    if (P < min_p) P = min_p;
+    const int64_t whole = (len + kBlock - 1) / kBlock * kBlock;
+    if (P >= whole) P = whole;  // one partition covers everything
+    return (int32_t)P;
+}
+
 int32_t partition_for(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
                       int32_t max_seq_len) {
     if (max_seq_len <= kBlock) return kBlock;
@@ -148,18 +167,22 @@ int32_t partition_for(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D,
         if (kv_dtype != PA_F32) wph = 4 / hpg;
     }
     const int wpw = waves_per_wg(kv_dtype);
-    const int64_t gran = (int64_t)kBlock * wph;  // one block per wave of a kv head at least
-    const int64_t target = (int64_t)kCUs * wgs_per_cu(kv_dtype, D, GT, mfma);  // workgroups that fill the GPU once
-    int64_t want_np = (target + per_partition - 1) / per_partition;
-    if (want_np < 1) want_np = 1;
-    int64_t P = (max_seq_len + want_np - 1) / want_np;
-    P = (P + gran - 1) / gran * gran;
-    // four-wave workgroups keep partitions long enough to bound the split-K
-    // partials; one-wave (fp32-cache) workgroups split short contexts finely
-    if (wpw > 1 && P < kMinPartition * wph / 4) P = kMinPartition * wph / 4;
-    const int64_t whole = ((int64_t)max_seq_len + kBlock - 1) / kBlock * kBlock;
-    if (P >= whole) P = whole;  // one partition covers everything
-    return (int32_t)P;
+    // one block per wave of a kv head at least; four-wave workgroups keep
+    // partitions long enough to bound the split-K partials, one-wave
+    // (fp32-cache) workgroups split short contexts finely
+    const int64_t gran = (int64_t)kBlock * wph;
+    const int64_t min_p = wpw > 1 ? (int64_t)kMinPartition * wph / 4 : 0;
+    return split_len(max_seq_len, per_partition, wgs_per_cu(kv_dtype, D, GT, mfma), gran, min_p);
+}
+
+// Prefix pass of the shared-prefix decode: the matrix-core kernel takes the
+// B * Tq * G rows of a kv head as one row set, so a partition index launches
+// Hkv * (row chunks) workgroups.
+int32_t prefix_partition_for(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t prefix_len) {
+    if (prefix_len <= kBlock) return kBlock;
+    int NT, nchunk;
+    row_chunks(B * Tq * (Hq / Hkv), &NT, &nchunk);
+    return split_len(prefix_len, (int64_t)Hkv * nchunk, 2, (int64_t)kBlock * 4, kMinPartition);
 }
 
 int check_dims(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D) {
@@ -171,6 +194,126 @@ int check_dims(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D) {
     if (Hq / Hkv > kMaxGroup) return fail(PA_ERR_UNSUPPORTED, "group Hq/Hkv=%d exceeds %d", Hq / Hkv, kMaxGroup);
     if (D < 1) return fail(PA_ERR_SHAPE, "D=%d must be >= 1", D);
     if (!supported_d(D)) return fail(PA_ERR_UNSUPPORTED, "D=%d not in {64, 128, 256}", D);
+    return PA_OK;
+}
+
+// Checks shared by the decode entry points (everything but partitioning and
+// the workspace).
+int check_decode_args(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D,
+                      const void* k_cache, const void* v_cache, pa_dtype kv_dtype, const float* k_scale,
+                      const float* v_scale, int64_t num_blocks, int32_t block_size, const int32_t* block_table,
+                      int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len, const void* out,
+                      pa_dtype out_dtype) {
+    int rc = check_dims(B, Tq, Hq, Hkv, D);
+    if (rc) return rc;
+    if (q_dtype != PA_F32 && q_dtype != PA_BF16) return fail(PA_ERR_DTYPE, "q dtype %d not in {f32, bf16}", (int)q_dtype);
+    if (!kv_supported(kv_dtype))
+        return fail(PA_ERR_DTYPE, "kv dtype %d not in {f32, bf16, i8, fp8, nvfp4}", (int)kv_dtype);
+    if (out_dtype != PA_F32 && out_dtype != PA_BF16)
+        return fail(PA_ERR_DTYPE, "out dtype %d not in {f32, bf16}", (int)out_dtype);
+    if (block_size < 1) return fail(PA_ERR_SHAPE, "block_size=%d must be >= 1", block_size);
+    if (block_size != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size=%d (only 16)", block_size);
+    if (num_blocks < 1) return fail(PA_ERR_SHAPE, "num_blocks=%lld must be >= 1", (long long)num_blocks);
+    // kernels address within one KV block with 32-bit offsets
+    const int64_t blk_bytes = (int64_t)kBlock * Hkv * row_bytes(kv_dtype, D);
+    if (blk_bytes >= ((int64_t)1 << 31))
+        return fail(PA_ERR_UNSUPPORTED, "a KV block of %lld bytes (Hkv=%d) exceeds 2^31", (long long)blk_bytes, Hkv);
+    if (max_blocks_per_seq < 1) return fail(PA_ERR_SHAPE, "max_blocks_per_seq=%d must be >= 1", max_blocks_per_seq);
+    if (max_seq_len < 0) return fail(PA_ERR_SHAPE, "max_seq_len=%d must be >= 0", max_seq_len);
+    if ((int64_t)max_blocks_per_seq * block_size < max_seq_len)
+        return fail(PA_ERR_SHAPE, "block table too short: %d blocks * %d < max_seq_len %d", max_blocks_per_seq,
+                    block_size, max_seq_len);
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
+        return fail(PA_ERR_NULL, "q, caches, block_table, seq_lens and out must be non-NULL");
+    if (quantised(kv_dtype) && (!k_scale || !v_scale))
+        return fail(PA_ERR_NULL, "int8/fp8/nvfp4 caches need k_scale and v_scale");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return fail(PA_ERR_ALIGN, "q, caches and out must be 16-byte aligned");
+    return PA_OK;
+}
+
+// Decode parameters common to every launch of one call (no partitioning,
+// no workspace, no offsets).
+pa::DecodeParams base_params(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv,
+                             const void* k_cache, const void* v_cache, const float* k_scale, const float* v_scale,
+                             const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                             float softmax_scale, void* out, pa_dtype out_dtype, float* lse) {
+    pa::DecodeParams p{};
+    p.q = q;
+    p.q_bf16 = q_dtype == PA_BF16;
+    p.B = B;
+    p.Tq = Tq;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.G = Hq / Hkv;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.block_table = block_table;
+    p.max_blocks = max_blocks_per_seq;
+    p.seq_lens = seq_lens;
+    p.qk_scale_log2 = softmax_scale * 1.4426950408889634f;
+    p.out = out;
+    p.out_bf16 = out_dtype == PA_BF16;
+    p.lse = lse;
+    return p;
+}
+
+// Workspace sections: o [rows, np, D], then lse [rows, np], each 256-byte aligned.
+void set_workspace(pa::DecodeParams& p, void* workspace, size_t rows, int32_t np, int32_t D) {
+    p.ws_o = reinterpret_cast<float*>(workspace);
+    p.ws_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + align256(rows * np * D * sizeof(float)));
+}
+
+// Kernel choice and launch shape for one decode launch: fp32 caches take the
+// plain fp32 kernel; bf16, int8, fp8 and nvfp4 the matrix-core kernel where
+// use_mfma says so (always for stacked rows), else the packed-dot kernel.
+hipError_t dispatch(pa::DecodeParams p, pa_dtype kv_dtype, int32_t D, hipStream_t stream) {
+    const bool mfma = p.stacked || use_mfma(p.Tq, p.Hq, p.Hkv, kv_dtype);
+    int GT, nchunk;
+    if (mfma)
+        row_chunks(p.G * p.Tq * (p.stacked ? p.B : 1), &GT, &nchunk);  // GT = row tiles per workgroup
+    else
+        head_chunks(p.G, &GT, &nchunk);
+    p.nchunk = nchunk;
+    p.hpg = (mfma || kv_dtype == PA_F32) ? 1 : heads_per_wg(kv_dtype, D, GT, p.Hkv);
+    return kv_dtype == PA_F32 ? pa::launch_decode_valu((int)kv_dtype, D, GT, p, stream)
+           : mfma             ? pa::launch_decode_mfma((int)kv_dtype, D, GT, p, stream)
+                              : pa::launch_decode_wave((int)kv_dtype, D, GT, p, stream);
+}
+
+// Partitioning of a shared-prefix decode: the prefix pass's partitions come
+// first in each row's workspace, the tail pass's after them.
+struct SharedPrefixPlan {
+    int32_t p_prefix, np_prefix, p_tail, np_tail, np_total;
+    size_t ws_bytes;
+};
+
+int plan_shared_prefix(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
+                       int32_t max_seq_len, int32_t prefix_len, int32_t prefix_partition, int32_t tail_partition,
+                       SharedPrefixPlan* pl) {
+    int rc = check_dims(B, Tq, Hq, Hkv, D);
+    if (rc) return rc;
+    if (!kv_supported(kv_dtype)) return fail(PA_ERR_DTYPE, "kv dtype %d not supported", (int)kv_dtype);
+    if (prefix_len < 0 || prefix_len % kBlock)
+        return fail(PA_ERR_SHAPE, "prefix_len=%d must be a non-negative multiple of %d", prefix_len, kBlock);
+    if (max_seq_len < (int64_t)prefix_len + Tq)
+        return fail(PA_ERR_SHAPE, "max_seq_len=%d leaves no room for %d query tokens after a %d-token prefix",
+                    max_seq_len, Tq, prefix_len);
+    if (prefix_partition < 0 || prefix_partition % kBlock || tail_partition < 0 || tail_partition % kBlock)
+        return fail(PA_ERR_SHAPE, "partition sizes %d, %d must be 0 or positive multiples of %d", prefix_partition,
+                    tail_partition, kBlock);
+    const int32_t tail_len = max_seq_len - prefix_len;
+    pl->p_prefix = prefix_partition ? prefix_partition : prefix_partition_for(B, Tq, Hq, Hkv, prefix_len);
+    pl->np_prefix = prefix_len > 0 ? (prefix_len + pl->p_prefix - 1) / pl->p_prefix : 0;
+    pl->p_tail = tail_partition ? tail_partition : partition_for(B, Tq, Hq, Hkv, D, kv_dtype, tail_len);
+    pl->np_tail = (int32_t)(((int64_t)tail_len + pl->p_tail - 1) / pl->p_tail);
+    const int64_t total = (int64_t)pl->np_prefix + pl->np_tail;
+    if (total > 0x7FFFFFFF) return fail(PA_ERR_SHAPE, "too many partitions");
+    pl->np_total = (int32_t)total;
+    const size_t rows = (size_t)B * Tq * Hq;
+    pl->ws_bytes = pl->np_total > 1 ? align256(rows * total * D * sizeof(float)) + align256(rows * total * sizeof(float)) : 0;
     return PA_OK;
 }
 
@@ -281,33 +424,12 @@ int pa_decode(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq
               int32_t partition_size, void* out, pa_dtype out_dtype, float* lse, void* workspace,
               size_t workspace_bytes, int32_t* num_partitions, void* stream) {
     if (!num_partitions) return fail(PA_ERR_NULL, "num_partitions is NULL");
-    int rc = check_dims(B, Tq, Hq, Hkv, D);
+    int rc = check_decode_args(q, q_dtype, B, Tq, Hq, Hkv, D, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                               num_blocks, block_size, block_table, max_blocks_per_seq, seq_lens, max_seq_len,
+                               out, out_dtype);
     if (rc) return rc;
-    if (q_dtype != PA_F32 && q_dtype != PA_BF16) return fail(PA_ERR_DTYPE, "q dtype %d not in {f32, bf16}", (int)q_dtype);
-    if (!kv_supported(kv_dtype))
-        return fail(PA_ERR_DTYPE, "kv dtype %d not in {f32, bf16, i8, fp8, nvfp4}", (int)kv_dtype);
-    if (out_dtype != PA_F32 && out_dtype != PA_BF16)
-        return fail(PA_ERR_DTYPE, "out dtype %d not in {f32, bf16}", (int)out_dtype);
-    if (block_size < 1) return fail(PA_ERR_SHAPE, "block_size=%d must be >= 1", block_size);
-    if (block_size != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size=%d (only 16)", block_size);
-    if (num_blocks < 1) return fail(PA_ERR_SHAPE, "num_blocks=%lld must be >= 1", (long long)num_blocks);
-    // kernels address within one KV block with 32-bit offsets
-    const int64_t blk_bytes = (int64_t)kBlock * Hkv * row_bytes(kv_dtype, D);
-    if (blk_bytes >= ((int64_t)1 << 31))
-        return fail(PA_ERR_UNSUPPORTED, "a KV block of %lld bytes (Hkv=%d) exceeds 2^31", (long long)blk_bytes, Hkv);
-    if (max_blocks_per_seq < 1) return fail(PA_ERR_SHAPE, "max_blocks_per_seq=%d must be >= 1", max_blocks_per_seq);
-    if (max_seq_len < 0) return fail(PA_ERR_SHAPE, "max_seq_len=%d must be >= 0", max_seq_len);
-    if ((int64_t)max_blocks_per_seq * block_size < max_seq_len)
-        return fail(PA_ERR_SHAPE, "block table too short: %d blocks * %d < max_seq_len %d", max_blocks_per_seq,
-                    block_size, max_seq_len);
     if (partition_size < 0 || partition_size % kBlock)
         return fail(PA_ERR_SHAPE, "partition_size=%d must be 0 or a positive multiple of %d", partition_size, kBlock);
-    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
-        return fail(PA_ERR_NULL, "q, caches, block_table, seq_lens and out must be non-NULL");
-    if (quantised(kv_dtype) && (!k_scale || !v_scale))
-        return fail(PA_ERR_NULL, "int8/fp8/nvfp4 caches need k_scale and v_scale");
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
-        return fail(PA_ERR_ALIGN, "q, caches and out must be 16-byte aligned");
 
     const int32_t P = partition_size ? partition_size : partition_for(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len);
     const int64_t NP64 = max_seq_len > 0 ? ((int64_t)max_seq_len + P - 1) / P : 1;
@@ -319,46 +441,96 @@ int pa_decode(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq
     *num_partitions = NP;
     if (B == 0) return ok();
 
-    const int32_t G = Hq / Hkv;
-    const bool mfma = use_mfma(Tq, Hq, Hkv, kv_dtype);
-    int GT, nchunk;
-    if (mfma)
-        row_chunks(G * Tq, &GT, &nchunk);  // GT = row tiles per workgroup
-    else
-        head_chunks(G, &GT, &nchunk);
-    pa::DecodeParams p{};
-    p.q = q;
-    p.q_bf16 = q_dtype == PA_BF16;
-    p.B = B;
-    p.Tq = Tq;
-    p.Hq = Hq;
-    p.Hkv = Hkv;
-    p.G = G;
-    p.k_cache = k_cache;
-    p.v_cache = v_cache;
-    p.k_scale = k_scale;
-    p.v_scale = v_scale;
-    p.block_table = block_table;
-    p.max_blocks = max_blocks_per_seq;
-    p.seq_lens = seq_lens;
-    p.qk_scale_log2 = softmax_scale * 1.4426950408889634f;
+    pa::DecodeParams p = base_params(q, q_dtype, B, Tq, Hq, Hkv, k_cache, v_cache, k_scale, v_scale, block_table,
+                                     max_blocks_per_seq, seq_lens, softmax_scale, out, out_dtype, lse);
     p.P = P;
     p.NP = NP;
-    p.nchunk = nchunk;
-    p.hpg = (mfma || kv_dtype == PA_F32) ? 1 : heads_per_wg(kv_dtype, D, GT, Hkv);
-    p.out = out;
-    p.out_bf16 = out_dtype == PA_BF16;
-    p.lse = lse;
-    if (NP > 1) {
-        const size_t rows = (size_t)B * Tq * Hq;
-        p.ws_o = reinterpret_cast<float*>(workspace);
-        p.ws_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + align256(rows * NP * D * sizeof(float)));
-    }
-    // fp32 caches take the plain fp32 kernel; bf16, int8 and fp8 the packed-dot kernel
-    hipError_t e = kv_dtype == PA_F32 ? pa::launch_decode_valu((int)kv_dtype, D, GT, p, (hipStream_t)stream)
-                   : mfma             ? pa::launch_decode_mfma((int)kv_dtype, D, GT, p, (hipStream_t)stream)
-                                      : pa::launch_decode_wave((int)kv_dtype, D, GT, p, (hipStream_t)stream);
+    p.np_stride = NP;
+    if (NP > 1) set_workspace(p, workspace, (size_t)B * Tq * Hq, NP, D);
+    hipError_t e = dispatch(p, kv_dtype, D, (hipStream_t)stream);
     if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "decode launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D,
+                                               pa_dtype kv_dtype, int32_t max_seq_len, int32_t prefix_len,
+                                               int32_t prefix_partition, int32_t tail_partition) {
+    SharedPrefixPlan pl;
+    if (plan_shared_prefix(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len, prefix_len, prefix_partition, tail_partition,
+                           &pl))
+        return 0;
+    return pl.ws_bytes;
+}
+
+int pa_decode_shared_prefix(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv,
+                            int32_t D, const void* k_cache, const void* v_cache, pa_dtype kv_dtype,
+                            const float* k_scale, const float* v_scale, int64_t num_blocks, int32_t block_size,
+                            const int32_t* prefix_table, int32_t prefix_len, const int32_t* block_table,
+                            int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                            float softmax_scale, int32_t prefix_partition, int32_t tail_partition, void* out,
+                            pa_dtype out_dtype, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_decode_args(q, q_dtype, B, Tq, Hq, Hkv, D, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                               num_blocks, block_size, block_table, max_blocks_per_seq, seq_lens, max_seq_len,
+                               out, out_dtype);
+    if (rc) return rc;
+    if (kv_dtype == PA_F32)
+        return fail(PA_ERR_UNSUPPORTED, "shared-prefix decode takes bf16, int8, fp8 or nvfp4 caches, not f32");
+    SharedPrefixPlan pl;
+    rc = plan_shared_prefix(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len, prefix_len, prefix_partition, tail_partition,
+                            &pl);
+    if (rc) return rc;
+    if (prefix_len > 0 && !prefix_table) return fail(PA_ERR_NULL, "prefix_table is NULL");
+    if (pl.np_total > 1 && (!workspace || workspace_bytes < pl.ws_bytes))
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.ws_bytes,
+                    workspace ? workspace_bytes : 0);
+    if (pl.np_total > 1 && !aligned16(workspace)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (B == 0) return ok();
+
+    const size_t rows = (size_t)B * Tq * Hq;
+    pa::DecodeParams p = base_params(q, q_dtype, B, Tq, Hq, Hkv, k_cache, v_cache, k_scale, v_scale, block_table,
+                                     max_blocks_per_seq, seq_lens, softmax_scale, out, out_dtype, lse);
+    p.np_stride = pl.np_total;
+    p.fill_empty = pl.np_total > 1;
+    if (pl.np_total > 1) set_workspace(p, workspace, rows, pl.np_total, D);
+    hipError_t e = hipSuccess;
+    if (pl.np_prefix > 0) {
+        // all rows of a kv head against the shared blocks, partitions 0 .. np_prefix - 1
+        pa::DecodeParams pp = p;
+        pp.stacked = 1;
+        pp.prefix_len = prefix_len;
+        pp.block_table = prefix_table;
+        pp.max_blocks = prefix_len / kBlock;
+        pp.P = pl.p_prefix;
+        pp.NP = pl.np_prefix;
+        pp.part_base = 0;
+        e = dispatch(pp, kv_dtype, D, (hipStream_t)stream);
+        if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "shared-prefix pass launch failed: %s", hipGetErrorString(e));
+    }
+    // each sequence's own keys after the prefix, with the causal mask
+    p.kv_begin = prefix_len;
+    p.P = pl.p_tail;
+    p.NP = pl.np_tail;
+    p.part_base = pl.np_prefix;
+    e = dispatch(p, kv_dtype, D, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "tail pass launch failed: %s", hipGetErrorString(e));
+    if (pl.np_total > 1) {
+        pa::ReduceParams r{};
+        r.ws_o = p.ws_o;
+        r.ws_lse = p.ws_lse;
+        r.NP = pl.np_total;
+        r.P = pl.p_tail;
+        r.B = B;
+        r.Tq = Tq;
+        r.Hq = Hq;
+        r.D = D;
+        r.seq_lens = seq_lens;
+        r.out = out;
+        r.out_bf16 = out_dtype == PA_BF16;
+        r.lse = lse;
+        r.all_parts = 1;
+        e = pa::launch_splitk_reduce(r, (hipStream_t)stream);
+        if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "reduce launch failed: %s", hipGetErrorString(e));
+    }
     return ok();
 }
 

@@ -26,8 +26,19 @@ struct DecodeParams {
     void* out;
     int out_bf16;
     float* lse;
-    float* ws_o;    // [B, Tq, Hq, NP, D] when NP > 1
-    float* ws_lse;  // [B, Tq, Hq, NP]
+    float* ws_o;    // [B, Tq, Hq, np_stride, D] when np_stride > 1
+    float* ws_lse;  // [B, Tq, Hq, np_stride]
+    // Partials of several launches may share one workspace: this launch's
+    // partition i is workspace partition part_base + i of np_stride per row.
+    // np_stride == 1: one partition covers the row, out/lse are written.
+    int np_stride;
+    int part_base;
+    int fill_empty;  // partitions with no visible key still write lse = -inf
+    int kv_begin;    // keys start at this token of every sequence (a multiple of 16)
+    // MFMA kernel only: the Tq * G rows of all B sequences form one row set
+    // that attends to keys 0 .. prefix_len - 1 of the block list block_table
+    int stacked;
+    int prefix_len;
 };
 
 struct ReduceParams {
@@ -35,6 +46,7 @@ struct ReduceParams {
     const float* ws_lse;
     int NP, P, B, Tq, Hq, D;
     int cs;  // column splits: workgroups per row, each taking D / cs output elements
+    int all_parts;  // every partition was written (empty ones with lse = -inf): merge all NP
     const int32_t* seq_lens;
     void* out;
     int out_bf16;

@@ -78,8 +78,10 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(ReduceParams p)
             lv[k] = lse_row[i];
         }
     }
+    // partitions that hold keys of the row (all of them when every partition
+    // was written, which the shared-prefix decode's two passes do)
     const int n = p.seq_lens[b] - p.Tq + t + 1;
-    const int np = n > 0 ? min((n + p.P - 1) / p.P, p.NP) : 0;
+    const int np = p.all_parts ? p.NP : n > 0 ? min((n + p.P - 1) / p.P, p.NP) : 0;
 
     // the slices' preloaded partitions are 0 .. kPre * S - 1; the rest is read here
     float mx = -INFINITY;

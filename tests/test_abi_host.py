@@ -174,3 +174,64 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(pa, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         pa.load()
+
+
+def shared_args(**over):
+    args = dict(q=A, q_dtype=1, B=4, Tq=8, Hq=24, Hkv=4, D=256, k_cache=A, v_cache=A, kv_dtype=1, k_scale=None,
+                v_scale=None, num_blocks=4096, block_size=16, prefix_table=A, prefix_len=4096, block_table=A,
+                max_blocks=1896, seq_lens=A, max_seq_len=30321, scale=0.0625, prefix_partition=0, tail_partition=0,
+                out=A, out_dtype=0, lse=None, workspace=None, workspace_bytes=0, stream=None)
+    args.update(over)
+    return list(args.values())
+
+
+@pytest.mark.parametrize("over, code", [
+    (dict(q=None), -1),
+    (dict(prefix_table=None), -1),
+    (dict(kv_dtype=0), -4),  # fp32 caches: no matrix-core prefix pass
+    (dict(kv_dtype=2), -1),  # int8 without scales
+    (dict(prefix_len=4008), -2),  # not whole blocks
+    (dict(prefix_len=-16), -2),
+    (dict(prefix_len=30320), -2),  # no room for 8 query tokens
+    (dict(prefix_partition=100), -2),
+    (dict(tail_partition=-16), -2),
+    (dict(Tq=17), -4),
+    (dict(max_blocks=100), -2),
+    (dict(workspace=ctypes.c_void_p(0x1008), workspace_bytes=1 << 30), -7),
+    (dict(), -5),  # partials of both passes need a workspace
+])
+def test_shared_prefix_rejects_bad_arguments(lib, over, code):
+    rc = lib.pa_decode_shared_prefix(*shared_args(**over))
+    assert rc == code, lib.pa_last_error()
+    assert lib.pa_last_error()
+
+
+def test_shared_prefix_plan_and_workspace(lib):
+    # the speculative-verify workload: the prefix pass takes the 4 * 8 * 6 =
+    # 192 rows of a kv head in 3 chunks of 64, so 12 workgroups per partition;
+    # 512 workgroups would want 43 partitions, 96 tokens each: the minimum of
+    # 256 gives 16. The tail pass (26225 tokens at most) is a plain decode:
+    # 32 partitions of 832 tokens (4 sequences x 4 kv heads x 32 = 512).
+    rows = 4 * 8 * 24
+    need = lib.pa_decode_shared_prefix_workspace_bytes(4, 8, 24, 4, 256, 1, 30321, 4096, 0, 0)
+    assert need == rows * 48 * 256 * 4 + rows * 48 * 4
+    assert lib.pa_choose_partition_size(4, 8, 24, 4, 256, 1, 30321 - 4096) == 832
+    # given sizes: 4096 / 1024 + ceil(26225 / 512) = 4 + 52 partitions
+    need = lib.pa_decode_shared_prefix_workspace_bytes(4, 8, 24, 4, 256, 1, 30321, 4096, 1024, 512)
+    assert need == rows * 56 * 256 * 4 + rows * 56 * 4
+    # no prefix and one tail partition: out is written directly, no workspace
+    assert lib.pa_decode_shared_prefix_workspace_bytes(1, 1, 24, 4, 256, 1, 48, 0, 0, 0) == 0
+    # invalid arguments size nothing
+    assert lib.pa_decode_shared_prefix_workspace_bytes(4, 8, 24, 4, 256, 1, 30321, 4008, 0, 0) == 0
+    # B == 0 with enough workspace: accepted, nothing launched
+    rc = lib.pa_decode_shared_prefix(*shared_args(B=0, workspace=A, workspace_bytes=1 << 30))
+    assert rc == 0, lib.pa_last_error()
+
+
+def test_empty_batch_with_the_heuristic(lib):
+    # B = 0 sizes no workgroups: the heuristic must not divide by them
+    for kv in (0, 1, 2):
+        assert lib.pa_choose_partition_size(0, 1, 24, 4, 256, kv, 65536) > 0
+        assert lib.pa_choose_partition_size(0, 8, 24, 4, 256, kv, 65536) > 0
+    rc = lib.pa_decode(*decode_args(B=0, partition_size=0, workspace=A, workspace_bytes=1 << 30))
+    assert rc == 0, lib.pa_last_error()

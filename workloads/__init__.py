@@ -146,6 +146,15 @@ SPECS: Dict[str, Spec] = {
         q_dtype="bf16", src_dtype="bf16", cache_dtype="nvfp4", shared_prefix=4096,
         description="speculative verify, 8 query tokens, 4096-token shared prefix, NVFP4 KV",
     ),
+    # A batch of decodes that share a long prefix (prefix caching: the
+    # vllm-sm12x-nvfp4-dflash2 page's capacity-first profile; the 1Cat-vLLM
+    # docs index's feature list): 16 sequences whose first 32768 tokens sit in
+    # the same physical blocks, each with 1024..4096 tokens of its own
+    "prefix32k_bf16": Spec(
+        "prefix32k_bf16", B=16, Tq=1, Hq=24, Hkv=4, D=256, seq_lens=(33792, 36864),
+        q_dtype="bf16", src_dtype="bf16", cache_dtype="bf16", shared_prefix=32768,
+        description="16 decodes sharing a 32768-token prefix, 1-4K own tokens each, bf16 KV",
+    ),
 }
 
 
