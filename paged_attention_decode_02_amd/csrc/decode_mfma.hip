@@ -162,7 +162,8 @@ __global__ __launch_bounds__(64 * kW, (mfma_min_waves<KVT, D, NT, QS>())) void d
     const int b = wg / p.Hkv;
 
     // Row r of the row set: sequence b + r / (Tq G) (stacked rows span the
-    // batch, whose grid coordinate b is then 0), token t, head g G + h'.
+    // batch, whose grid coordinate b is then 0), token (r / G) % Tq, head
+    // g G + r % G.
     const int G = p.G, Tq = p.Tq, TG = G * Tq;
     const int R = p.stacked ? p.B * TG : TG;
     const int row0 = rc * 16 * NT;
@@ -174,10 +175,12 @@ __global__ __launch_bounds__(64 * kW, (mfma_min_waves<KVT, D, NT, QS>())) void d
     const int start = part * p.P;
     const int64_t wpart = p.part_base + part;  // workspace partition
 
-    auto row_out = [&](int r) -> int64_t {  // flat (b, t, h) row id of row r
-        const int bb = b + r / TG, rr = r % TG;
-        const int t = rr / G, hh = rr % G;
-        return ((int64_t)bb * Tq + t) * p.Hq + g * G + hh;
+    // flat (b, t, h) row id of row r: with u = r / G, b Tq + u is the
+    // sequence times Tq plus the token, also for stacked rows (b = 0 there,
+    // u = sequence * Tq + token)
+    auto row_out = [&](int r) -> int64_t {
+        const int u = r / G, hh = r % G;
+        return ((int64_t)b * Tq + u) * p.Hq + g * G + hh;
     };
 
     if (start >= n_chunk) {
