@@ -93,30 +93,34 @@ def decode_kernel(spec) -> tuple:
     return "decode_wave_kernel", ("decode_wave.hip",) + _COMMON
 
 
-def kernel_source_digest(spec) -> str:
-    """Digest of the decode kernel's sources (ties committed counters to code)."""
+_SHARED_SOURCES = ("decode_mfma.hip", "decode_wave.hip", "splitk_reduce.hip") + _COMMON
+
+
+def kernel_source_digest(spec, shared: bool = False) -> str:
+    """Digest of the decode kernel's sources (ties committed counters to code);
+    shared: the kernels of a pa_decode_shared_prefix call."""
     h = hashlib.sha256()
-    for f in decode_kernel(spec)[1]:
+    for f in (_SHARED_SOURCES if shared else decode_kernel(spec)[1]):
         p = os.path.join(ROOT, "paged_attention_decode_02_amd", "csrc", f)
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
 
-def committed_traffic(spec):
+def committed_traffic(spec, shared: bool = False):
     """Per-launch HBM bytes (read + write) from the committed rocprofv3 counter
     summary, or None when it is missing or was taken on other kernel sources."""
-    p = os.path.join(ROOT, "profiles", "decode_%s_hbm_traffic.md" % spec.name)
+    p = os.path.join(ROOT, "profiles", "decode_%s%s_hbm_traffic.md" % (spec.name, "_shared" if shared else ""))
     if not os.path.exists(p):
         return None
     text = open(p).read()
     m = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
-    if not m or not t or m.group(1) != kernel_source_digest(spec):
+    if not m or not t or m.group(1) != kernel_source_digest(spec, shared):
         return None
     return int(t.group(1))
 
 
-def summarize_counters(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int) -> str:
+def summarize_counters(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int, shared: bool = False) -> str:
     """Markdown summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE).
 
     Both counters are in KiB per dispatch. Each is scaled by what it reads for
@@ -142,20 +146,30 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, copy_bytes
     ff, fw = kib / copy_f, kib / copy_w
     spec = SPECS[workload]
     kname = decode_kernel(spec)[0]
-    dk = [k for k in fetch if kname in k]
-    assert len(dk) == 1, dk
-    f_kib = sum(fetch[dk[0]]) / len(fetch[dk[0]])
-    w_kib = sum(write[dk[0]]) / len(write[dk[0]])
+    if shared:
+        # the pa_decode_shared_prefix call: both decode passes and the merge,
+        # each kernel's mean per dispatch (one dispatch of each per call)
+        dk = sorted(k for k in fetch if "decode_" in k or "splitk_reduce" in k)
+        assert 2 <= len(dk) <= 3, dk
+        kname = "pa_decode_shared_prefix (%s)" % ", ".join(k.replace("void ", "").split("(")[0] for k in dk)
+    else:
+        dk = [k for k in fetch if kname in k]
+        assert len(dk) == 1, dk
+    f_kib = sum(sum(fetch[k]) / len(fetch[k]) for k in dk)
+    w_kib = sum(sum(write[k]) / len(write[k]) for k in dk)
     read_b = int(round(f_kib * ff * 1024))
     write_b = int(round(w_kib * fw * 1024))
-    algo = algorithmic_bytes(generate(spec))["total"]
+    w = generate(spec)
+    algo = unique_bytes(w) if shared else algorithmic_bytes(w)["total"]
+    extra = " --shared-prefix" if shared else ""
     lines = [
         "# HBM traffic of %s on %s" % (kname, workload), "",
         "Counters from two rocprofv3 runs (one MI355X, repository root as the working directory):", "",
     ] + [
-        "    rocprofv3 --pmc %s --output-format csv -d gpurun_out/pmc_%s -o run -- python -u bench.py "
-        "--workload %s --steps 5 --warmup 1 --no-cpu-baseline --copy-calibration-mb %d" % (
-            c, c.split("_")[0].lower(), workload, copy_bytes >> 20) for c in ("FETCH_SIZE", "WRITE_SIZE")
+        "    rocprofv3 --pmc %s --output-format csv -d gpurun_out/pmc_%s_%s%s -o run -- python -u bench.py "
+        "--workload %s%s --steps 5 --warmup 1 --no-cpu-baseline --copy-calibration-mb %d" % (
+            c, c.split("_")[0].lower(), workload, "_shared" if shared else "", workload, extra, copy_bytes >> 20)
+        for c in ("FETCH_SIZE", "WRITE_SIZE")
     ] + [
         "",
         "Both counters are KiB per dispatch; each is scaled by what it reads for a plain device copy of",
@@ -163,18 +177,19 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, copy_bytes
         "| quantity | value |", "|---|---|",
         "| copy kernel (%d MiB) FETCH_SIZE / WRITE_SIZE, KiB | %.1f / %.1f |" % (copy_bytes >> 20, copy_f, copy_w),
         "| scale factors (bytes per counted byte), read / write | %.4f / %.4f |" % (ff, fw),
-        "| decode FETCH_SIZE / WRITE_SIZE per dispatch, KiB (mean of %d) | %.1f / %.1f |" % (
-            len(fetch[dk[0]]), f_kib, w_kib),
-        "| decode HBM read / write per launch, bytes (scaled) | %d / %d |" % (read_b, write_b),
-        "| algorithmic bytes per launch | %d |" % algo,
+        "| decode FETCH_SIZE / WRITE_SIZE per %s, KiB (mean of %d) | %.1f / %.1f |" % (
+            "call" if shared else "dispatch", len(fetch[dk[0]]), f_kib, w_kib),
+        "| decode HBM read / write per %s, bytes (scaled) | %d / %d |" % ("call" if shared else "launch", read_b,
+                                                                        write_b),
+        "| algorithmic bytes per %s | %d |" % ("call (shared prefix once)" if shared else "launch", algo),
         "| traffic / algorithmic | %.4f |" % ((read_b + write_b) / algo), "",
         "hbm_bytes_per_launch: %d" % (read_b + write_b),
-        "kernel_source_digest: %s" % kernel_source_digest(spec), "",
+        "kernel_source_digest: %s" % kernel_source_digest(spec, shared), "",
     ]
     return "\n".join(lines)
 
 
-def summarize_trace(trace_csv: str, workload: str, command: str, tail_cold: int = 20) -> str:
+def summarize_trace(trace_csv: str, workload: str, command: str, tail_cold: int = 20, shared: bool = False) -> str:
     """Markdown summary of a rocprofv3 --kernel-trace CSV of one bench.py run.
 
     Per kernel: dispatch count and mean / median / min / max duration. The last
@@ -210,6 +225,16 @@ def summarize_trace(trace_csv: str, workload: str, command: str, tail_cold: int 
         a = np.array(v)
         lines.append("| %s | %d | %.2f | %.2f | %.2f | %.2f | %.1f%% |" % (
             short(k), len(a), a.mean(), np.median(a), a.min(), a.max(), 100.0 * a.sum() / total))
+    if shared:
+        # one pa_decode_shared_prefix call per step: both passes and the merge
+        parts = sorted(k for k in dur if "decode_" in k or "splitk_reduce" in k)
+        means = [float(np.mean(dur[k][:-tail_cold])) for k in parts]
+        lines += ["", "Without the last %d dispatches of each (the cache-flushed side steps), one "
+                  "pa_decode_shared_prefix call:" % tail_cold, "",
+                  "| kernel of the call | mean |", "|---|---:|"]
+        lines += ["| %s | %.2f |" % (short(k), m) for k, m in zip(parts, means)]
+        lines += ["", "shared_prefix_call_mean_us: %.2f" % sum(means), ""]
+        return "\n".join(lines)
     dk = [k for k in dur if spec_kernel in k]
     if len(dk) == 1 and len(dur[dk[0]]) > tail_cold:
         a = np.array(dur[dk[0]][:-tail_cold])
@@ -303,11 +328,12 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_trace:
-        print(summarize_trace(args.summarize_trace[0], args.workload, args.summarize_trace[1]))
+        print(summarize_trace(args.summarize_trace[0], args.workload, args.summarize_trace[1],
+                              shared=args.shared_prefix))
         return
     if args.summarize_counters:
         print(summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.workload,
-                                 (args.copy_calibration_mb or 512) << 20))
+                                 (args.copy_calibration_mb or 512) << 20, shared=args.shared_prefix))
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -476,19 +502,19 @@ def main():
     del flush
 
     ab = algorithmic_bytes(w)
+    # the shared-prefix call must read the prefix once: its bytes are the
+    # unique ones (the per-sequence total is reported beside them)
+    step_bytes = unique_bytes(w) if args.shared_prefix else ab["total"]
     eager_ms = wall * 1e3 / args.steps
     ms_per_step = eager_ms
-    value = ab["total"] / (ms_per_step * 1e-3) / 1e9
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dec_avg_ms = float(np.mean(dk))
-    achieved = ab["total"] / (dec_avg_ms * 1e-3) / 1e9
+    achieved = step_bytes / (dec_avg_ms * 1e-3) / 1e9
     ws_traffic = 0
     if state["np"] > 1:
         ws_traffic = 2 * sp.B * sp.Tq * sp.Hq * state["np"] * (sp.D + 1) * 4
     if args.shared_prefix:
         ws_traffic = 2 * ws_bytes
-        # the call's three kernels against the bytes it must read: the shared
-        # prefix once, each sequence's own tokens
-        achieved = unique_bytes(w) / (dec_avg_ms * 1e-3) / 1e9
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -507,8 +533,11 @@ def main():
         "config": {
             "workload": sp.name, "B": sp.B, "Tq": sp.Tq, "Hq": sp.Hq, "Hkv": sp.Hkv, "D": sp.D,
             "block_size": BLOCK_SIZE, "seq_lens": "%d..%d" % (w.seq_lens.min(), w.seq_lens.max()),
-            "kv_dtype": sp.cache_dtype, "q_dtype": sp.q_dtype, "partition_size": P,
-            "num_partitions": state["np"], "algorithmic_bytes_per_step": ab["total"],
+            "kv_dtype": sp.cache_dtype, "q_dtype": sp.q_dtype,
+            "partition_size": None if args.shared_prefix else P,
+            "num_partitions": None if args.shared_prefix else state["np"],
+            "algorithmic_bytes_per_step": step_bytes,
+            "per_sequence_bytes_per_step": ab["total"],
             "shared_prefix": sp.shared_prefix,
             "prefix_partition": args.prefix_partition if args.shared_prefix else None,
             "tail_partition": args.tail_partition if args.shared_prefix else None,
@@ -532,8 +561,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None if args.shared_prefix else committed_traffic(sp),
-            "kernel_source_digest": kernel_source_digest(sp),
+            "traffic": committed_traffic(sp, args.shared_prefix),
+            "kernel_source_digest": kernel_source_digest(sp, args.shared_prefix),
         },
     }
     if args.copy_calibration_mb:

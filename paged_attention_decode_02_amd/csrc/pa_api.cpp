@@ -270,6 +270,9 @@ void set_workspace(pa::DecodeParams& p, void* workspace, size_t rows, int32_t np
 // plain fp32 kernel; bf16, int8, fp8 and nvfp4 the matrix-core kernel where
 // use_mfma says so (always for stacked rows), else the packed-dot kernel.
 hipError_t dispatch(pa::DecodeParams p, pa_dtype kv_dtype, int32_t D, hipStream_t stream) {
+    // the fp32-cache kernel knows no shared workspace, key offset or stacked rows
+    if (kv_dtype == PA_F32 && (p.np_stride != p.NP || p.part_base || p.fill_empty || p.kv_begin || p.stacked))
+        return hipErrorInvalidValue;
     const bool mfma = p.stacked || use_mfma(p.Tq, p.Hq, p.Hkv, kv_dtype);
     int GT, nchunk;
     if (mfma)

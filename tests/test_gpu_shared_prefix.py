@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import paged_attention_decode_02_amd as pa
-from _gpu import cache_bytes_equal, dev, gpu_cache, gpu_decode, gpu_inputs
+from _gpu import cache_bytes_equal, dev, gpu_cache, gpu_decode, gpu_inputs, host_to_dev
 from _host import oracle_cache, oracle_decode
 from test_gpu_parity import check, say
 from workloads import SPECS, generate, scaled
@@ -156,3 +156,46 @@ def test_host_checks():
         pa.decode_shared_prefix(q, k, v, pt, 256, tab, lens, w.max_seq_len, w.softmax_scale,
                                 workspace=torch.empty(256, dtype=torch.uint8, device=dev()))
     assert e.value.code == -5
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+def test_shared_prefix_step_captured_in_a_graph(kv):
+    """cache_write + the shared-prefix decode (three kernels) recorded in one
+    HIP graph: every replay, with new query values written eagerly in between,
+    equals an eager run bit for bit."""
+    spec = scaled("verify_bf16", B=4, Tq=8, Hq=24, Hkv=4, D=256, seq_lens=(2048 + 8, 4000), shared_prefix=2048,
+                  cache_dtype=kv, src_dtype="bf16")
+    w = generate(spec, seed=14)
+    cache = gpu_cache(w)
+    k, v, ks, vs = cache
+    q, table, lens = gpu_inputs(w)
+    rows = w.step_rows()
+    new_k = host_to_dev(w.k_src[rows], spec.src_dtype)
+    new_v = host_to_dev(w.v_src[rows], spec.src_dtype)
+    new_slots = torch.from_numpy(w.slot_mapping[rows]).to(dev())
+    prefix_table = torch.from_numpy(np.ascontiguousarray(w.block_table[0, :2048 // 16])).to(dev())
+    nbytes = pa.shared_prefix_workspace_bytes(spec.B, spec.Tq, spec.Hq, spec.Hkv, spec.D, k.dtype, w.max_seq_len,
+                                              2048)
+    ws = torch.empty(max(256, nbytes), dtype=torch.uint8, device=dev())
+    out = torch.empty((spec.B, spec.Tq, spec.Hq, spec.D), dtype=torch.float32, device=dev())
+    lse = torch.empty((spec.B, spec.Tq, spec.Hq), dtype=torch.float32, device=dev())
+
+    def step():
+        pa.cache_write(new_k, new_v, new_slots, k, v, ks, vs)
+        pa.decode_shared_prefix(q, k, v, prefix_table, 2048, table, lens, w.max_seq_len, w.softmax_scale, ks, vs,
+                                out=out, lse=lse, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for i in range(4):
+        q.copy_(q.roll(1, dims=2))
+        g.replay()
+        torch.cuda.synchronize()
+        got_o, got_l = out.clone(), lse.clone()
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(got_o, out) and torch.equal(got_l, lse), "replay %d differs from eager" % i
