@@ -40,9 +40,9 @@
  *    Query head h reads kv head h / (Hq / Hkv).
  *  - Supported: block_size 16; D in {64, 128, 256}; 1 <= Tq <= 16;
  *    Hq % Hkv == 0 and Hq / Hkv <= 64; q in {f32, bf16}; caches in
- *    {f32, bf16, i8, fp8, nvfp4}; out in {f32, bf16}. q, caches and out must
- *    be 16-byte aligned; one KV block (16 * Hkv * row bytes) must be below
- *    2^31 bytes.
+ *    {f32, bf16, i8, fp8, nvfp4} (the shared-prefix decode: not f32); out
+ *    in {f32, bf16}. q, caches and out must be 16-byte aligned; one KV block
+ *    (16 * Hkv * row bytes) must be below 2^31 bytes.
  *  - NVFP4 caches are bytes [num_blocks, block_size, Hkv, 9 D / 16] (row
  *    bytes 36, 72, 144 for D = 64, 128, 256), but a block is not stored row
  *    by row: first the code rows of its 16 * Hkv (token, head) pairs, D/2

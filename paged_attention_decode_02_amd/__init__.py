@@ -265,7 +265,8 @@ def shared_prefix_workspace_bytes(B: int, Tq: int, Hq: int, Hkv: int, D: int, kv
                                                               prefix_len, prefix_partition, tail_partition))
 
 
-def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, prefix_table: torch.Tensor,
+def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         prefix_table: Optional[torch.Tensor],
                          prefix_len: int, block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
                          softmax_scale: float, k_scale: Optional[torch.Tensor] = None,
                          v_scale: Optional[torch.Tensor] = None, prefix_partition: int = 0, tail_partition: int = 0,
@@ -273,14 +274,19 @@ def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
                          workspace: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32,
                          stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Decode of a batch whose sequences share their first prefix_len tokens
-    (blocks prefix_table [prefix_len / 16]); same result as decode(). Missing
-    out/lse/workspace tensors are allocated with torch."""
+    (blocks prefix_table [prefix_len / 16] int32, None when prefix_len is 0);
+    same result as decode(). Missing out/lse/workspace tensors are allocated
+    with torch."""
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (prefix_table, "prefix_table"),
                  (block_table, "block_table"), (seq_lens, "seq_lens"), (out, "out"), (lse, "lse"),
                  (k_scale, "k_scale"), (v_scale, "v_scale"), (workspace, "workspace")):
         _dev(t, n)
-    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or prefix_table.dtype != torch.int32:
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or (
+            prefix_table is not None and prefix_table.dtype != torch.int32):
         raise ValueError("prefix_table, block_table and seq_lens must be int32")
+    if prefix_table is not None and prefix_table.numel() < prefix_len // 16:
+        raise ValueError("prefix_table holds %d blocks, prefix_len %d needs %d" % (
+            prefix_table.numel(), prefix_len, prefix_len // 16))
     B, Tq, Hq, D = q.shape
     nb, bs, Hkv, _ = k_cache.shape
     if out is None:
