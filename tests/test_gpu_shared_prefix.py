@@ -150,7 +150,7 @@ def test_host_checks():
         pa.decode_shared_prefix(q, k, v, pt, 250, tab, lens, w.max_seq_len, w.softmax_scale)
     assert e.value.code == -2
     with pytest.raises(pa.PaError) as e:  # no room for the query tokens
-        pa.decode_shared_prefix(q, k, v, tab[0, :56].contiguous(), 896, tab, lens, 898, w.softmax_scale)
+        pa.decode_shared_prefix(q, k, v, tab[0, :52].contiguous(), 832, tab, lens, 834, w.softmax_scale)
     assert e.value.code == -2
     with pytest.raises(ValueError):  # a prefix table shorter than the prefix (caught by the binding)
         pa.decode_shared_prefix(q, k, v, pt, 512, tab, lens, w.max_seq_len, w.softmax_scale)
