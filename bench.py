@@ -309,6 +309,9 @@ def main():
     ap.add_argument("--partition-size", type=int, default=0, help="0 = the library's heuristic")
     ap.add_argument("--shared-prefix", action="store_true",
                     help="decode through pa_decode_shared_prefix (workloads with a shared prefix)")
+    ap.add_argument("--batch", type=int, default=0, help="override the workload's B (0 = as named)")
+    ap.add_argument("--lengths", default="", help="override the workload's sequence lengths, LO:HI")
+    ap.add_argument("--prefix", type=int, default=-1, help="override the workload's shared prefix (tokens)")
     ap.add_argument("--prefix-partition", type=int, default=0, help="--shared-prefix: prefix pass partition (0 = "
                     "the library's choice)")
     ap.add_argument("--tail-partition", type=int, default=0, help="--shared-prefix: tail pass partition (0 = the "
@@ -344,7 +347,7 @@ def main():
     import torch
 
     import paged_attention_decode_02_amd as pa
-    from workloads import BLOCK_SIZE, SPECS, generate
+    from workloads import BLOCK_SIZE, SPECS, generate, scaled
 
     if not os.path.exists(pa.library_path()):
         import __graft_entry__
@@ -354,6 +357,16 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     spec = SPECS[args.workload]
+    changes = {}
+    if args.batch:
+        changes["B"] = args.batch
+    if args.lengths:
+        lo, hi = (int(x) for x in args.lengths.split(":"))
+        changes["seq_lens"] = (lo, hi)
+    if args.prefix >= 0:
+        changes["shared_prefix"] = args.prefix
+    if changes:  # a workload of its own: no committed counters apply
+        spec = scaled(spec, name=spec.name + "_custom", **changes)
     if args.shared_prefix and not spec.shared_prefix:
         print("--shared-prefix needs a workload whose sequences share a prefix", file=sys.stderr)
         sys.exit(2)
