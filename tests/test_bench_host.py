@@ -1,0 +1,45 @@
+"""bench.py's host-side pieces (CPU only): the byte counts behind its metric and
+its refusal to run on more than one GPU."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+from workloads import SPECS, generate, scaled
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_algorithmic_bytes_of_the_64k_workload():
+    # 4 x 65536 tokens x 4 kv heads x 256 x 2 (K, V) x 2 bytes, the table, q and out
+    w = generate(scaled("long64k_bf16", D=8, Hq=2, Hkv=1, seq_lens=(100, 100)))
+    ab = bench.algorithmic_bytes(w)
+    L = int(w.seq_lens.sum())
+    assert ab["kv"] == L * 1 * 8 * 2 * 2
+    assert ab["table"] == int(((w.seq_lens + 15) // 16).sum()) * 4
+    assert ab["total"] == ab["kv"] + ab["scales"] + ab["table"] + ab["q"] + ab["out"]
+    full = SPECS["long64k_bf16"]
+    assert 4 * 65536 * full.Hkv * full.D * 2 * 2 == 1073741824
+
+
+def test_unique_bytes_count_the_shared_prefix_once():
+    for kv in ("bf16", "i8", "nvfp4"):
+        spec = scaled("verify_bf16", B=3, Tq=2, Hq=4, Hkv=2, D=64, seq_lens=(300, 400), shared_prefix=256,
+                      cache_dtype=kv, src_dtype="f32")
+        w = generate(spec, seed=1)
+        ab = bench.algorithmic_bytes(w)
+        per_token = (ab["kv"] + ab["scales"]) // int(w.seq_lens.sum())
+        assert (ab["kv"] + ab["scales"]) % int(w.seq_lens.sum()) == 0
+        assert bench.unique_bytes(w) == ab["total"] - 2 * 256 * per_token
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
