@@ -98,8 +98,9 @@ def test_workspace_size_and_partition_choice(lib):
     # int8 with G = 4 stays on the vector ALU
     assert lib.pa_choose_partition_size(1, 1, 16, 4, 256, 2, 250000) == 992
     assert lib.pa_choose_partition_size(4, 8, 24, 4, 256, 3, 30321) == 960
-    # small head chunks (batched GQA, D=128, 4 heads): four per CU
-    assert lib.pa_choose_partition_size(8, 1, 32, 8, 128, 1, 3637) == 256
+    # small head chunks (batched GQA, D=128, 4 heads): eight per CU aimed at,
+    # and half the usual minimum partition
+    assert lib.pa_choose_partition_size(8, 1, 32, 8, 128, 1, 3637) == 128
     # speculative verify on the matrix cores: two per CU
     assert lib.pa_choose_partition_size(4, 8, 24, 4, 256, 1, 30321) == 960
     # the same shape with fp32 caches uses one-wave workgroups, eight per CU
