@@ -100,7 +100,8 @@ def test_tails_of_only_the_query_tokens_and_no_prefix():
     spec = scaled("verify_bf16", B=4, Tq=8, Hq=12, Hkv=2, D=128, seq_lens=(776, 776), shared_prefix=768)
     run_shared(generate(spec, seed=8, seq_lens=[776, 776, 777, 800]), parts=((0, 0), (16, 16)))
     spec0 = scaled(spec, shared_prefix=0, seq_lens=(8, 900))
-    run_shared(generate(spec0, seed=9, seq_lens=[8, 9, 400, 900]), parts=((0, 0), (0, 16)))
+    # (0, 1024): one tail partition and no prefix, so out is written directly
+    run_shared(generate(spec0, seed=9, seq_lens=[8, 9, 400, 900]), parts=((0, 0), (0, 16), (0, 1024)))
 
 
 def test_shared_entries_of_the_block_table_are_not_read():
