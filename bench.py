@@ -80,17 +80,18 @@ def unique_bytes(w) -> int:
     return ab["total"] - (sp.B - 1) * sp.shared_prefix * per_tok
 
 
+_KERNEL_SOURCES = {"decode_valu_kernel": "decode_valu.hip", "decode_mfma_kernel": "decode_mfma.hip",
+                   "decode_wave_kernel": "decode_wave.hip"}
+_CODES = {"f32": 0, "bf16": 1, "i8": 2, "fp8": 3, "nvfp4": 4}
+
+
 def decode_kernel(spec) -> tuple:
-    """(name, sources) of the decode kernel that runs the workload, by the
-    library's rule: the plain kernel for fp32 caches; the matrix-core kernel
-    for Tq > 1, for groups of 16+ query heads, and for int8 and FP8 caches from 6;
-    the vector-ALU kernel otherwise."""
-    if spec.cache_dtype == "f32":
-        return "decode_valu_kernel", ("decode_valu.hip",) + _COMMON
-    G = spec.Hq // spec.Hkv
-    if spec.Tq > 1 or G >= 16 or (spec.cache_dtype in ("i8", "fp8") and G >= 6):
-        return "decode_mfma_kernel", ("decode_mfma.hip",) + _COMMON
-    return "decode_wave_kernel", ("decode_wave.hip",) + _COMMON
+    """(name, sources) of the decode kernel that runs the workload, as the
+    library itself chooses it (pa_decode_kernel_name)."""
+    import paged_attention_decode_02_amd as pa
+
+    name = pa.load().pa_decode_kernel_name(spec.Tq, spec.Hq, spec.Hkv, _CODES[spec.cache_dtype]).decode()
+    return name, (_KERNEL_SOURCES[name],) + _COMMON
 
 
 _SHARED_SOURCES = ("decode_mfma.hip", "decode_wave.hip", "splitk_reduce.hip") + _COMMON
@@ -247,39 +248,48 @@ def summarize_trace(trace_csv: str, workload: str, command: str, tail_cold: int 
             "decode_mean_us_warm: %.2f" % a.mean(),
         ]
         # the decode dispatches by bench phase: W warm-up steps, K eager steps
-        # (the metric), K eager steps with events (the roofline), W + K graph
-        # replays, one eager check step, then the cache-flushed steps
+        # (the metric), K eager steps with events between the kernels, K
+        # back-to-back decode launches (the roofline), one eager step, W + K
+        # graph replays, one eager check step, then the cache-flushed steps
         m_steps = re.search(r"--steps (\d+)", command)
         m_warm = re.search(r"--warmup (\d+)", command)
         if m_steps and m_warm:
             K, W = int(m_steps.group(1)), int(m_warm.group(1))
             d = np.array(dur[dk[0]])
-            if len(d) >= W + 3 * K + W + 1:
-                phases = [("eager steps (the metric's timed region)", W, W + K),
-                          ("eager steps with events (the roofline's launches)", W + K, W + 2 * K),
-                          ("graph replays", W + 2 * K + W, W + 3 * K + W)]
+            g0 = W + 3 * K + 1 + W
+            phases = [("eager steps (the metric's timed region)", W, W + K),
+                      ("eager steps with events between the kernels", W + K, W + 2 * K),
+                      ("back-to-back decode launches (the roofline's launches)", W + 2 * K, W + 3 * K)]
+            if len(d) >= g0 + K + 1:
+                phases.append(("graph replays", g0, g0 + K))
+            if len(d) >= W + 3 * K:
                 lines += ["", "| decode dispatches by phase | dispatches | mean | median |", "|---|---:|---:|---:|"]
                 for name, i0, i1 in phases:
                     x = d[i0:i1]
                     lines.append("| %s | %d | %.2f | %.2f |" % (name, len(x), x.mean(), np.median(x)))
-                lines += ["", "decode_mean_us_event_timed_launches: %.2f" % d[W + K:W + 2 * K].mean()]
+                lines += ["", "decode_mean_us_roofline_launches: %.2f" % d[W + 2 * K:W + 3 * K].mean()]
     lines.append("")
     return "\n".join(lines)
 
 
-def run_cpu_baseline(w, bytes_per_step: int, budget_s: float) -> dict:
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rows_per_s(w, k, v, ks, vs, threads: int, budget_s: float, tag: str) -> tuple:
+    """(rows, seconds) of oracle work on (b, t, h) rows in sequence-major order,
+    in chunks of one row per thread, cycling over the step until the budget is
+    used (at least one chunk)."""
     import oracle
-    from workloads import BLOCK_SIZE
 
     sp = w.spec
-    t0 = time.time()
-    k, v, ks, vs = oracle.alloc_cache(w.num_blocks, BLOCK_SIZE, sp.Hkv, sp.D, sp.cache_dtype)
-    oracle.cache_write(w.k_src, w.v_src, w.slot_mapping, k, v, ks, vs)
-    log("cpu baseline: oracle cache built in %.1f s" % (time.time() - t0))
     rows_total = sp.B * sp.Tq * sp.Hq
-    # (b, t, h) rows in sequence-major order, in chunks of one row per thread,
-    # cycling over the step until the time budget is used (at least one chunk)
-    threads = oracle.max_threads()
     chunk = max(1, min(rows_total, threads))
     done, spent, next_log = 0, 0.0, 1.0
     q = w.q_array()
@@ -290,87 +300,100 @@ def run_cpu_baseline(w, bytes_per_step: int, budget_s: float) -> dict:
         spent += time.perf_counter() - t
         done += rows.size
         if spent >= next_log:
-            log("cpu baseline: %d rows (%.2f steps), %.1f s" % (done, done / rows_total, spent))
+            log("cpu baseline (%s): %d rows (%.2f steps), %.1f s" % (tag, done, done / rows_total, spent))
             next_log = spent + 1.0
+    return done, spent
+
+
+def run_cpu_baseline(w, bytes_per_step: int, budget_s: float, budget_1t_s: float) -> dict:
+    import oracle
+    from workloads import BLOCK_SIZE
+
+    sp = w.spec
+    t0 = time.time()
+    k, v, ks, vs = oracle.alloc_cache(w.num_blocks, BLOCK_SIZE, sp.Hkv, sp.D, sp.cache_dtype)
+    oracle.cache_write(w.k_src, w.v_src, w.slot_mapping, k, v, ks, vs)
+    log("cpu baseline: oracle cache built in %.1f s" % (time.time() - t0))
+    rows_total = sp.B * sp.Tq * sp.Hq
+    threads = oracle.max_threads()
+    done, spent = _oracle_rows_per_s(w, k, v, ks, vs, threads, budget_s, "%d threads" % threads)
     # the sample covers whole sequences' rows in proportion; scale it to one step
     step_s = spent * rows_total / done
-    return {"value": round(bytes_per_step / step_s / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle", "ms_per_step": round(step_s * 1e3, 3),
-            "sample": "%d (b,t,h) rows of %s (%.2f steps of %d rows) in %.1f s, fp64 oracle, %d OpenMP threads, "
-                      "scaled to one step" % (done, sp.name, done / rows_total, rows_total, spent, threads)}
+    res = {"value": round(bytes_per_step / step_s / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+           "kind": "oracle", "ms_per_step": round(step_s * 1e3, 3), "cpu_model": cpu_model(),
+           "sample": "%d (b,t,h) rows of %s (%.2f steps of %d rows) in %.1f s, fp64 oracle, %d OpenMP threads, "
+                     "scaled to one step" % (done, sp.name, done / rows_total, rows_total, spent, threads)}
+    if budget_1t_s > 0:
+        d1, s1 = _oracle_rows_per_s(w, k, v, ks, vs, 1, budget_1t_s, "1 thread")
+        step1 = s1 * rows_total / d1
+        res["value_1thread"] = round(bytes_per_step / step1 / 1e9, 4)
+        res["ms_per_step_1thread"] = round(step1 * 1e3, 3)
+        res["sample_1thread"] = "%d rows in %.1f s on one thread, scaled to one step" % (d1, s1)
+    return res
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--partition-size", type=int, default=0, help="0 = the library's heuristic")
-    ap.add_argument("--shared-prefix", action="store_true",
-                    help="decode through pa_decode_shared_prefix (workloads with a shared prefix)")
-    ap.add_argument("--batch", type=int, default=0, help="override the workload's B (0 = as named)")
-    ap.add_argument("--lengths", default="", help="override the workload's sequence lengths, LO:HI")
-    ap.add_argument("--prefix", type=int, default=-1, help="override the workload's shared prefix (tokens)")
-    ap.add_argument("--prefix-partition", type=int, default=0, help="--shared-prefix: prefix pass partition (0 = "
-                    "the library's choice)")
-    ap.add_argument("--tail-partition", type=int, default=0, help="--shared-prefix: tail pass partition (0 = the "
-                    "library's choice)")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
-    ap.add_argument("--flush-mb", type=int, default=512, help="flush buffer for the cold-cache side measurement")
-    ap.add_argument("--copy-calibration-mb", type=int, default=0,
-                    help="after the benchmark, run 3 plain device copies of this many MiB (a kernel of known "
-                         "traffic for scaling rocprofv3's FETCH_SIZE/WRITE_SIZE counters)")
-    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="print the HBM-traffic summary of two rocprofv3 --pmc counter CSVs and exit")
-    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "COMMAND"),
-                    help="print the kernel-duration summary of a rocprofv3 --kernel-trace CSV made by COMMAND "
-                         "and exit")
-    args = ap.parse_args()
+def _sysfs_clock(name: str, top: bool = False):
+    """Current (or, with top, highest) level in MHz of a DPM clock table in
+    sysfs, or None."""
+    import glob
 
-    if args.summarize_trace:
-        print(summarize_trace(args.summarize_trace[0], args.workload, args.summarize_trace[1],
-                              shared=args.shared_prefix))
-        return
-    if args.summarize_counters:
-        print(summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.workload,
-                                 (args.copy_calibration_mb or 512) << 20, shared=args.shared_prefix))
-        return
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/" + name)):
+        try:
+            levels = []
+            for line in open(path):
+                m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                if m:
+                    levels.append(int(m.group(1)))
+                    if not top and line.rstrip().endswith("*"):
+                        return levels[-1]
+            if top and levels:
+                return max(levels)
+        except OSError:
+            continue
+    return None
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this decode library runs on a single MI355X "
-              "(multi-GPU sharding is not built); use --gpus 1", file=sys.stderr)
-        sys.exit(2)
 
+def device_record(pa) -> dict:
+    """The device and build the figures were taken on."""
+    import torch
+
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        pass
+    info = {}
+    bi = os.path.join(os.path.dirname(pa.library_path()), "build_info.json")
+    if os.path.exists(bi):
+        info = json.load(open(bi))
+    return {
+        "name": props.name, "gcn_arch": getattr(props, "gcnArchName", None),
+        "compute_units": props.multi_processor_count, "library_compute_units": pa.device_cu_count(),
+        "total_memory_gib": round(props.total_memory / 2**30, 1),
+        "sclk_mhz_now": _sysfs_clock("pp_dpm_sclk"), "sclk_mhz_max": _sysfs_clock("pp_dpm_sclk", True),
+        "mclk_mhz_now": _sysfs_clock("pp_dpm_mclk"), "mclk_mhz_max": _sysfs_clock("pp_dpm_mclk", True),
+        "rocm": rocm, "torch_hip": getattr(torch.version, "hip", None),
+        "git_head_at_build": info.get("git_head"), "library_source_digest": info.get("source_digest"),
+    }
+
+
+def pct(a, q):
+    return round(1e3 * float(np.percentile(np.asarray(a), q)), 2)
+
+
+def measure(args, spec, partition_size: int, shared: bool, graph: bool, cold: bool, cpu_budget: float,
+            cpu_budget_1t: float) -> dict:
+    """Time one workload: K eager steps between two synchronisations (the
+    metric), K eager steps with HIP events between the kernels (breakdown,
+    per-step percentiles, the decode kernel's roofline), optionally K graph
+    replays, cache-flushed side steps and the CPU oracle baseline."""
     import torch
 
     import paged_attention_decode_02_amd as pa
-    from workloads import BLOCK_SIZE, SPECS, generate, scaled
+    from workloads import BLOCK_SIZE, generate
 
-    if not os.path.exists(pa.library_path()):
-        import __graft_entry__
-
-        __graft_entry__.build()
-    pa.load()
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    spec = SPECS[args.workload]
-    changes = {}
-    if args.batch:
-        changes["B"] = args.batch
-    if args.lengths:
-        lo, hi = (int(x) for x in args.lengths.split(":"))
-        changes["seq_lens"] = (lo, hi)
-    if args.prefix >= 0:
-        changes["shared_prefix"] = args.prefix
-    if changes:  # a workload of its own: no committed counters apply
-        spec = scaled(spec, name=spec.name + "_custom", **changes)
-    if args.shared_prefix and not spec.shared_prefix:
-        print("--shared-prefix needs a workload whose sequences share a prefix", file=sys.stderr)
-        sys.exit(2)
-
     t0 = time.time()
     w = generate(spec)
     log("generated %s in %.1f s" % (spec.name, time.time() - t0))
@@ -406,11 +429,11 @@ def main():
     q = up(w.q_array(), sp.q_dtype)
     table = torch.from_numpy(w.block_table).to(dev)
     lens = torch.from_numpy(w.seq_lens).to(dev)
-    P = args.partition_size or pa.choose_partition_size(sp.B, sp.Tq, sp.Hq, sp.Hkv, sp.D, TD[sp.cache_dtype],
-                                                        w.max_seq_len)
+    P = partition_size or pa.choose_partition_size(sp.B, sp.Tq, sp.Hq, sp.Hkv, sp.D, TD[sp.cache_dtype],
+                                                   w.max_seq_len)
     ws_bytes = pa.workspace_bytes(sp.B, sp.Tq, sp.Hq, sp.Hkv, sp.D, TD[sp.cache_dtype], w.max_seq_len, P)
     prefix_table = None
-    if args.shared_prefix:
+    if shared:
         ws_bytes = pa.shared_prefix_workspace_bytes(sp.B, sp.Tq, sp.Hq, sp.Hkv, sp.D, TD[sp.cache_dtype],
                                                     w.max_seq_len, sp.shared_prefix, args.prefix_partition,
                                                     args.tail_partition)
@@ -429,7 +452,7 @@ def main():
         pa.cache_write(new_k, new_v, new_slots, kc, vc, ks, vs)
         if ev is not None:
             ev[1].record(stream)
-        if args.shared_prefix:
+        if shared:
             pa.decode_shared_prefix(q, kc, vc, prefix_table, sp.shared_prefix, table, lens, w.max_seq_len,
                                     w.softmax_scale, ks, vs, args.prefix_partition, args.tail_partition, out=out,
                                     lse=lse, workspace=ws)
@@ -473,111 +496,129 @@ def main():
     rk = [e[2].elapsed_time(e[3]) for e in evs]
     step_ms = [e[0].elapsed_time(e[3]) for e in evs]
 
+    # ---- the decode kernel's average launch duration for the roofline: K
+    # launches of the decode alone (the pa_decode_shared_prefix call: K
+    # calls), back to back between two HIP events on the launch stream. An
+    # event between every two kernels adds marker packets that lengthen each
+    # interval by a few microseconds; back-to-back launches of one kernel are
+    # what a sustained decode runs. The decode leaves its inputs unchanged, so
+    # repeating it alone is the same work.
+    def decode_only():
+        if shared:
+            pa.decode_shared_prefix(q, kc, vc, prefix_table, sp.shared_prefix, table, lens, w.max_seq_len,
+                                    w.softmax_scale, ks, vs, args.prefix_partition, args.tail_partition, out=out,
+                                    lse=lse, workspace=ws)
+        else:
+            pa.decode_partials(q, kc, vc, table, lens, w.max_seq_len, w.softmax_scale, out, lse, ks, vs, P, ws)
+
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    d0.record(stream)
+    for i in range(args.steps):
+        decode_only()
+    d1.record(stream)
+    torch.cuda.synchronize()
+    dec_loop_ms = d0.elapsed_time(d1) / args.steps
+    one_step()  # leave out/lse as a whole step writes them
+    torch.cuda.synchronize()
+
     # ---- K replays of the step recorded in a HIP graph (decode runs under
     # graph capture in serving; the library allocates and synchronises
     # nothing, so the graph holds exactly the step's kernels)
-    graph = None
     graph_ms = None
-    if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
             one_step()
         torch.cuda.synchronize()
         for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-        ge0, ge1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g.replay()
         torch.cuda.synchronize()
         g_start = time.perf_counter()
-        ge0.record(stream)
         for _ in range(args.steps):
-            graph.replay()
-        ge1.record(stream)
+            g.replay()
         torch.cuda.synchronize()
-        g_wall = time.perf_counter() - g_start
-        graph_ms = g_wall * 1e3 / args.steps
+        graph_ms = (time.perf_counter() - g_start) * 1e3 / args.steps
         # the replays must reproduce an eager step bit for bit
         ref_o, ref_l = out.clone(), lse.clone()
         one_step()
         torch.cuda.synchronize()
         if not (torch.equal(ref_o, out) and torch.equal(ref_l, lse)):
             raise RuntimeError("graph replay differs from the eager step")
+        del g
 
     # ---- side measurement: every step after a flush of the caches (not the metric)
-    flush = torch.empty(args.flush_mb << 20, dtype=torch.uint8, device=dev)
-    cold = []
-    for i in range(min(20, args.steps)):
-        flush.fill_(i & 0xFF)
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        one_step(e)
-        torch.cuda.synchronize()
-        cold.append(e[1].elapsed_time(e[3]))
-    del flush
+    cold_ms = []
+    if cold:
+        flush = torch.empty(args.flush_mb << 20, dtype=torch.uint8, device=dev)
+        for i in range(min(20, args.steps)):
+            flush.fill_(i & 0xFF)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            one_step(e)
+            torch.cuda.synchronize()
+            cold_ms.append(e[1].elapsed_time(e[3]))
+        del flush
 
     ab = algorithmic_bytes(w)
     # the shared-prefix call must read the prefix once: its bytes are the
     # unique ones (the per-sequence total is reported beside them)
-    step_bytes = unique_bytes(w) if args.shared_prefix else ab["total"]
-    eager_ms = wall * 1e3 / args.steps
-    ms_per_step = eager_ms
+    step_bytes = unique_bytes(w) if shared else ab["total"]
+    ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    dec_avg_ms = float(np.mean(dk))
+    dec_avg_ms = dec_loop_ms
     achieved = step_bytes / (dec_avg_ms * 1e-3) / 1e9
     ws_traffic = 0
     if state["np"] > 1:
         ws_traffic = 2 * sp.B * sp.Tq * sp.Hq * state["np"] * (sp.D + 1) * 4
-    if args.shared_prefix:
+    if shared:
         ws_traffic = 2 * ws_bytes
-    result = {
-        "metric": METRIC,
+    res = {
         "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": sp.cache_dtype,
-        "data": "synthetic",
         "config": {
             "workload": sp.name, "B": sp.B, "Tq": sp.Tq, "Hq": sp.Hq, "Hkv": sp.Hkv, "D": sp.D,
             "block_size": BLOCK_SIZE, "seq_lens": "%d..%d" % (w.seq_lens.min(), w.seq_lens.max()),
             "kv_dtype": sp.cache_dtype, "q_dtype": sp.q_dtype,
-            "partition_size": None if args.shared_prefix else P,
-            "num_partitions": None if args.shared_prefix else state["np"],
+            "partition_size": None if shared else P,
+            "num_partitions": None if shared else state["np"],
             "algorithmic_bytes_per_step": step_bytes,
             "per_sequence_bytes_per_step": ab["total"],
             "shared_prefix": sp.shared_prefix,
-            "prefix_partition": args.prefix_partition if args.shared_prefix else None,
-            "tail_partition": args.tail_partition if args.shared_prefix else None,
+            "prefix_partition": args.prefix_partition if shared else None,
+            "tail_partition": args.tail_partition if shared else None,
             "splitk_workspace_bytes_per_step": ws_traffic,
         },
-        "path": "shared_prefix" if args.shared_prefix else "decode",
-        "timing": "eager launches, K steps between two device synchronisations",
+        "path": "shared_prefix" if shared else "decode",
         "graph_us_per_step": round(graph_ms * 1e3, 2) if graph_ms is not None else None,
+        "step_us_event_timed": {"p10": pct(step_ms, 10), "median": pct(step_ms, 50), "p90": pct(step_ms, 90),
+                                "min": pct(step_ms, 0), "steps": len(step_ms)},
+        "decode_us_back_to_back": round(1e3 * dec_loop_ms, 2),
         "breakdown_us": {
+            "note": "per-step HIP events between the kernels (each interval includes a marker packet)",
             "cache_write": round(1e3 * float(np.mean(cw)), 2),
-            "decode": round(1e3 * dec_avg_ms, 2),
+            "decode": round(1e3 * float(np.mean(dk)), 2),
+            "decode_p10_median_p90": [pct(dk, 10), pct(dk, 50), pct(dk, 90)],
             "reduce": round(1e3 * float(np.mean(rk)), 2),
             "step_events": round(1e3 * float(np.median(step_ms)), 2),
-            "decode_plus_reduce_after_flush": round(1e3 * float(np.median(cold)), 2),
         },
         "roofline": {
             "kernel": ("pa_decode_shared_prefix: prefix pass, tail pass and merge, against the bytes with the "
-                       "prefix read once" if args.shared_prefix else decode_kernel(sp)[0]),
+                       "prefix read once" if shared else decode_kernel(sp)[0]),
+            "timing": "K back-to-back launches between two HIP events on the launch stream",
+            "launch_us": round(1e3 * dec_loop_ms, 2),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": committed_traffic(sp, args.shared_prefix),
-            "kernel_source_digest": kernel_source_digest(sp, args.shared_prefix),
+            "traffic": committed_traffic(sp, shared) if not partition_size or partition_size == P else None,
+            "kernel_source_digest": kernel_source_digest(sp, shared),
         },
     }
+    if cold_ms:
+        res["breakdown_us"]["decode_plus_reduce_after_flush"] = round(1e3 * float(np.median(cold_ms)), 2)
     if args.copy_calibration_mb:
         n = args.copy_calibration_mb << 20
         src = torch.ones(n // 4, dtype=torch.float32, device=dev)
@@ -585,10 +626,132 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        result["copy_calibration_bytes"] = n
+        res["copy_calibration_bytes"] = n
         del src, dst
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = run_cpu_baseline(w, ab["total"], args.cpu_budget)
+    del kc, vc, ks, vs, ws
+    torch.cuda.empty_cache()
+    if cpu_budget > 0:
+        res["cpu_baseline"] = run_cpu_baseline(w, ab["total"], cpu_budget, cpu_budget_1t)
+    return res
+
+
+# Side figures of the default run (each its own timed pass, reported under its
+# own key): the 250K-token int8 decode, the second workload the >= 70% bar
+# applies to, and the 64K workload at the 512-token partitions it names.
+EXTRAS = (("int8_250k", "int8_250k", 0, True), ("long64k_bf16_p512", "long64k_bf16", 512, False))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--partition-size", type=int, default=0, help="0 = the library's heuristic")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="decode through pa_decode_shared_prefix (workloads with a shared prefix)")
+    ap.add_argument("--batch", type=int, default=0, help="override the workload's B (0 = as named)")
+    ap.add_argument("--lengths", default="", help="override the workload's sequence lengths, LO:HI")
+    ap.add_argument("--prefix", type=int, default=-1, help="override the workload's shared prefix (tokens)")
+    ap.add_argument("--prefix-partition", type=int, default=0, help="--shared-prefix: prefix pass partition (0 = "
+                    "the library's choice)")
+    ap.add_argument("--tail-partition", type=int, default=0, help="--shared-prefix: tail pass partition (0 = the "
+                    "library's choice)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--cpu-budget-1thread", type=float, default=3.0,
+                    help="seconds of single-thread oracle work for the CPU baseline's 1-thread figure")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay side measurement")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="default run: skip the side workloads (int8 250K, 64K at 512-token partitions)")
+    ap.add_argument("--flush-mb", type=int, default=512, help="flush buffer for the cold-cache side measurement")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="after the benchmark, run 3 plain device copies of this many MiB (a kernel of known "
+                         "traffic for scaling rocprofv3's FETCH_SIZE/WRITE_SIZE counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM-traffic summary of two rocprofv3 --pmc counter CSVs and exit")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "COMMAND"),
+                    help="print the kernel-duration summary of a rocprofv3 --kernel-trace CSV made by COMMAND "
+                         "and exit")
+    args = ap.parse_args()
+    explicit_workload = any(a == "--workload" or a.startswith("--workload=") for a in sys.argv[1:])
+
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace[0], args.workload, args.summarize_trace[1],
+                              shared=args.shared_prefix))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.workload,
+                                 (args.copy_calibration_mb or 512) << 20, shared=args.shared_prefix))
+        return
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this decode library runs on a single MI355X "
+              "(multi-GPU sharding is not built); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_attention_decode_02_amd as pa
+    from workloads import SPECS, scaled
+
+    if not os.path.exists(pa.library_path()):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    pa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = SPECS[args.workload]
+    changes = {}
+    if args.batch:
+        changes["B"] = args.batch
+    if args.lengths:
+        lo, hi = (int(x) for x in args.lengths.split(":"))
+        changes["seq_lens"] = (lo, hi)
+    if args.prefix >= 0:
+        changes["shared_prefix"] = args.prefix
+    if changes:  # a workload of its own: no committed counters apply
+        spec = scaled(spec, name=spec.name + "_custom", **changes)
+    if args.shared_prefix and not spec.shared_prefix:
+        print("--shared-prefix needs a workload whose sequences share a prefix", file=sys.stderr)
+        sys.exit(2)
+
+    cpu = 0.0 if args.no_cpu_baseline else args.cpu_budget
+    cpu1 = 0.0 if args.no_cpu_baseline else args.cpu_budget_1thread
+    main_res = measure(args, spec, args.partition_size, args.shared_prefix, not args.no_graph, True, cpu, cpu1)
+    result = {
+        "metric": METRIC,
+        "value": main_res.pop("value"),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res.pop("ms_per_step"),
+        "us_per_step": main_res.pop("us_per_step"),
+        "pct_hbm_peak": main_res.pop("pct_hbm_peak"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.cache_dtype,
+        "data": "synthetic",
+        "config": main_res.pop("config"),
+        "timing": "eager launches, K steps between two device synchronisations",
+    }
+    cpu_res = main_res.pop("cpu_baseline", None)
+    roof = main_res.pop("roofline")
+    result.update(main_res)
+    result["roofline"] = roof
+    if cpu_res is not None:
+        result["cpu_baseline"] = cpu_res
+    result["device"] = device_record(pa)
+    if not explicit_workload and not args.no_extras and not changes and not args.partition_size:
+        for key, name, P, with_cpu in EXTRAS:
+            log("side workload %s (%s, P=%s)" % (key, name, P or "heuristic"))
+            r = measure(args, SPECS[name], P, False, False, False, cpu if with_cpu else 0.0,
+                        cpu1 if with_cpu else 0.0)
+            r["dtype"] = SPECS[name].cache_dtype
+            result[key] = r
     print(json.dumps(result), flush=True)
 
 

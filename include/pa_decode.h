@@ -34,6 +34,11 @@
  *      scales   [num_blocks, Hkv, block_size]      fp32, int8 / FP8 / NVFP4 caches only;
  *                                                  a kv head's scales of one block are one
  *                                                  64-byte run, read whole by its workgroup
+ *                                                  (head-major inside a block, not token-major
+ *                                                  [num_blocks, block_size, Hkv]: a token-major
+ *                                                  64-byte line holds four tokens of every kv
+ *                                                  head and was fetched by every head's
+ *                                                  workgroup)
  *      table    [B, max_blocks_per_seq]            int32 physical block ids
  *      out      [B, Tq, Hq, D]
  *      lse      [B, Tq, Hq]                        fp32, natural log
@@ -137,8 +142,9 @@ int pa_cache_write(const void* k_src, const void* v_src, pa_dtype src_dtype, con
  *   partition_size tokens per split-K partition, a multiple of block_size,
  *                  or 0 to let pa_choose_partition_size pick it.
  *   out, lse       outputs; lse may be NULL.
- *   workspace      device scratch of workspace_bytes >= pa_decode_workspace_bytes
- *                  (may be NULL when that size is 0).
+ *   workspace      device scratch of workspace_bytes >= pa_decode_workspace_bytes,
+ *                  16-byte aligned (may be NULL when that size is 0;
+ *                  PA_ERR_ALIGN otherwise).
  *   num_partitions (host, out) NP = ceil(max_seq_len / P).
  * When *num_partitions == 1 the kernel writes out/lse directly. Otherwise it
  * writes per-partition results to the workspace and leaves out/lse untouched:
@@ -229,9 +235,30 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv,
  * groups) fills the GPU's compute units while keeping the split-K workspace
  * small (the stream-K rationale of the nvllm page, "SM120 Stream-K Decode
  * Optimization": split the long dimension when the batch alone cannot fill
- * the machine). Returns a negative PA_ERR_* code for invalid arguments. */
+ * the machine). The compute units are those of the calling thread's current
+ * HIP device (pa_device_cu_count). Returns a negative PA_ERR_* code for
+ * invalid arguments. */
 int32_t pa_choose_partition_size(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
                                  int32_t max_seq_len);
+
+/* The same heuristic for a device of num_cus compute units (>= 1): what
+ * pa_choose_partition_size returns on such a device. A sizing aid for callers
+ * that plan for another device, and the heuristic's host-side test hook. */
+int32_t pa_choose_partition_size_for_cus(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D,
+                                         pa_dtype kv_dtype, int32_t max_seq_len, int32_t num_cus);
+
+/* Compute units of the calling thread's current HIP device, as the heuristic
+ * uses them (hipDeviceAttributeMultiprocessorCount, read once per device; a
+ * partitioned GPU reports its partition's share). With no visible device: 256,
+ * the MI355X figure. */
+int32_t pa_device_cu_count(void);
+
+/* Name of the decode kernel pa_decode launches for these arguments:
+ * "decode_wave_kernel" (vector ALU, one query token, small groups),
+ * "decode_mfma_kernel" (matrix cores: Tq > 1, groups of 16+ query heads, int8
+ * and FP8 caches from groups of 6) or "decode_valu_kernel" (fp32 caches); ""
+ * for invalid arguments. A static string; nothing is launched. */
+const char* pa_decode_kernel_name(int32_t Tq, int32_t Hq, int32_t Hkv, pa_dtype kv_dtype);
 
 /*
  * pa_decode_check — debug-time validation of the device data pa_decode

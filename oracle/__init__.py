@@ -89,8 +89,16 @@ def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
 
 
+_MAX_THREADS = []
+
+
 def max_threads() -> int:
-    return int(_load().pa_oracle_max_threads())
+    """OpenMP threads available to the oracle, read on the first call: a
+    decode with an explicit thread count changes OpenMP's default for later
+    parallel regions, so later reads would see that count instead."""
+    if not _MAX_THREADS:
+        _MAX_THREADS.append(int(_load().pa_oracle_max_threads()))
+    return _MAX_THREADS[0]
 
 
 NVFP4_HEAD_DIMS = (64, 128, 256)  # where the bytes per (token, head), 36, 72, 144, differ from D

@@ -24,8 +24,9 @@ import torch
 
 __all__ = [
     "PaError", "cache_write", "decode", "decode_partials", "splitk_reduce", "workspace_bytes",
-    "choose_partition_size", "library_path", "load", "DTYPE_CODE", "decode_shared_prefix",
-    "shared_prefix_workspace_bytes",
+    "choose_partition_size", "choose_partition_size_for_cus", "device_cu_count", "decode_kernel_name",
+    "library_path", "load", "DTYPE_CODE", "decode_shared_prefix", "shared_prefix_workspace_bytes",
+    "validate_decode_args", "validate_cache_write_args",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,7 +43,8 @@ DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.int8: 2, torch.float8_e
 EXPORTS = (
     "pa_cache_write", "pa_decode", "pa_decode_splitk_reduce", "pa_decode_workspace_bytes",
     "pa_choose_partition_size", "pa_decode_check", "pa_cache_write_check", "pa_last_error",
-    "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes",
+    "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes", "pa_choose_partition_size_for_cus",
+    "pa_device_cu_count", "pa_decode_kernel_name",
 )
 
 
@@ -88,6 +90,12 @@ def load():
         lib.pa_decode_shared_prefix.restype = ctypes.c_int
         lib.pa_decode_shared_prefix_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32, I32, I32]
         lib.pa_decode_shared_prefix_workspace_bytes.restype = SZ
+        lib.pa_choose_partition_size_for_cus.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32]
+        lib.pa_choose_partition_size_for_cus.restype = I32
+        lib.pa_device_cu_count.argtypes = []
+        lib.pa_device_cu_count.restype = I32
+        lib.pa_decode_kernel_name.argtypes = [I32, I32, I32, I32]
+        lib.pa_decode_kernel_name.restype = ctypes.c_char_p
         lib.pa_last_error.argtypes = []
         lib.pa_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -137,6 +145,82 @@ def _code(t: torch.Tensor) -> int:
         raise ValueError("unsupported dtype %s" % t.dtype)
 
 
+QUANTISED = (torch.int8, torch.float8_e4m3fn, torch.float4_e2m1fn_x2)
+
+
+def _row_elems(cache_dtype: torch.dtype, D: int) -> int:
+    """Last dimension of a cache tensor for head size D (NVFP4: bytes of codes
+    and block scales per (token, kv head))."""
+    return 9 * D // 16 if cache_dtype == torch.float4_e2m1fn_x2 else D
+
+
+def _shape_err(msg: str):
+    raise ValueError(msg)
+
+
+def _check_cache_pair(k_cache, v_cache, k_scale, v_scale, D: int):
+    """Shared checks of the paged caches and their row scales; returns (nb, Hkv)."""
+    if k_cache.dim() != 4 or tuple(k_cache.shape) != tuple(v_cache.shape) or k_cache.dtype != v_cache.dtype:
+        _shape_err("k_cache and v_cache must be 4-D tensors of one shape and dtype, got %s %s / %s %s" % (
+            tuple(k_cache.shape), k_cache.dtype, tuple(v_cache.shape), v_cache.dtype))
+    if k_cache.dtype not in DTYPE_CODE:
+        _shape_err("unsupported cache dtype %s" % k_cache.dtype)
+    nb, bs, Hkv, row = k_cache.shape
+    if bs != 16:
+        _shape_err("block_size (cache dim 1) must be 16, got %d" % bs)
+    if row != _row_elems(k_cache.dtype, D):
+        _shape_err("cache rows hold %d elements, head size %d needs %d" % (row, D, _row_elems(k_cache.dtype, D)))
+    if k_cache.dtype in QUANTISED:
+        for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+            if t is None:
+                _shape_err("%s caches need %s" % (k_cache.dtype, n))
+            if t.dtype != torch.float32 or tuple(t.shape) != (nb, Hkv, 16):
+                _shape_err("%s must be float32 [%d, %d, 16], got %s %s" % (n, nb, Hkv, t.dtype, tuple(t.shape)))
+    return nb, Hkv
+
+
+def validate_decode_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, out=None, lse=None,
+                         k_scale=None, v_scale=None) -> None:
+    """Shape and dtype checks of a decode call (the C ABI sees only pointers,
+    so a mismatched tensor would be read out of bounds on the device). Raises
+    ValueError; looks at metadata only, so it runs on CPU tensors too."""
+    if q.dim() != 4 or q.dtype not in (torch.float32, torch.bfloat16):
+        _shape_err("q must be a 4-D float32 or bfloat16 tensor [B, Tq, Hq, D], got %s %s" % (
+            tuple(q.shape), q.dtype))
+    B, Tq, Hq, D = q.shape
+    nb, Hkv = _check_cache_pair(k_cache, v_cache, k_scale, v_scale, D)
+    if Hq % Hkv:
+        _shape_err("Hq=%d is not a multiple of the caches' Hkv=%d" % (Hq, Hkv))
+    if block_table.dim() != 2 or block_table.dtype != torch.int32 or block_table.shape[0] != B:
+        _shape_err("block_table must be int32 [B=%d, max_blocks], got %s %s" % (B, block_table.dtype,
+                                                                                tuple(block_table.shape)))
+    if block_table.shape[1] * 16 < max_seq_len:
+        _shape_err("block_table has %d blocks per sequence, max_seq_len %d needs %d" % (
+            block_table.shape[1], max_seq_len, (max_seq_len + 15) // 16))
+    if seq_lens.dim() != 1 or seq_lens.dtype != torch.int32 or seq_lens.numel() != B:
+        _shape_err("seq_lens must be int32 [B=%d], got %s %s" % (B, seq_lens.dtype, tuple(seq_lens.shape)))
+    if out is not None and (tuple(out.shape) != (B, Tq, Hq, D) or out.dtype not in (torch.float32, torch.bfloat16)):
+        _shape_err("out must be float32 or bfloat16 [%d, %d, %d, %d], got %s %s" % (B, Tq, Hq, D, out.dtype,
+                                                                                   tuple(out.shape)))
+    if lse is not None and (tuple(lse.shape) != (B, Tq, Hq) or lse.dtype != torch.float32):
+        _shape_err("lse must be float32 [%d, %d, %d], got %s %s" % (B, Tq, Hq, lse.dtype, tuple(lse.shape)))
+
+
+def validate_cache_write_args(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None) -> None:
+    """Shape and dtype checks of a cache write (metadata only; raises ValueError)."""
+    if k.dim() != 3 or tuple(k.shape) != tuple(v.shape) or k.dtype != v.dtype or k.dtype not in (
+            torch.float32, torch.bfloat16):
+        _shape_err("k and v must be float32 or bfloat16 [N, Hkv, D] of one shape, got %s %s / %s %s" % (
+            tuple(k.shape), k.dtype, tuple(v.shape), v.dtype))
+    N, Hkv, D = k.shape
+    _, cHkv = _check_cache_pair(k_cache, v_cache, k_scale, v_scale, D)
+    if cHkv != Hkv:
+        _shape_err("source rows have Hkv=%d, the caches %d" % (Hkv, cHkv))
+    if slot_mapping.dim() != 1 or slot_mapping.dtype != torch.int64 or slot_mapping.numel() != N:
+        _shape_err("slot_mapping must be int64 [N=%d], got %s %s" % (N, slot_mapping.dtype,
+                                                                      tuple(slot_mapping.shape)))
+
+
 def cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
                 v_cache: torch.Tensor, k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
                 stream=None) -> None:
@@ -144,8 +228,7 @@ def cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_
     for t, n in ((k, "k"), (v, "v"), (slot_mapping, "slot_mapping"), (k_cache, "k_cache"), (v_cache, "v_cache"),
                  (k_scale, "k_scale"), (v_scale, "v_scale")):
         _dev(t, n)
-    if slot_mapping.dtype != torch.int64:
-        raise ValueError("slot_mapping must be int64")
+    validate_cache_write_args(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale)
     nb, bs, Hkv, _ = k_cache.shape
     D = k.shape[-1]
     _check(_L().pa_cache_write(_ptr(k), _ptr(v), _code(k), _ptr(slot_mapping), slot_mapping.numel(),
@@ -167,6 +250,26 @@ def choose_partition_size(B: int, Tq: int, Hq: int, Hkv: int, D: int, kv_dtype: 
     return P
 
 
+def choose_partition_size_for_cus(B: int, Tq: int, Hq: int, Hkv: int, D: int, kv_dtype: torch.dtype,
+                                  max_seq_len: int, num_cus: int) -> int:
+    """The partition heuristic for a device of num_cus compute units."""
+    P = int(load().pa_choose_partition_size_for_cus(B, Tq, Hq, Hkv, D, DTYPE_CODE[kv_dtype], max_seq_len,
+                                                    num_cus))
+    if P < 0:
+        _check(P)
+    return P
+
+
+def device_cu_count() -> int:
+    """Compute units of the current HIP device as the heuristic uses them."""
+    return int(load().pa_device_cu_count())
+
+
+def decode_kernel_name(Tq: int, Hq: int, Hkv: int, kv_dtype: torch.dtype) -> str:
+    """Name of the decode kernel pa_decode launches for these arguments."""
+    return load().pa_decode_kernel_name(Tq, Hq, Hkv, DTYPE_CODE[kv_dtype]).decode()
+
+
 def decode_partials(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, softmax_scale: float,
                     out: torch.Tensor, lse: Optional[torch.Tensor] = None, k_scale=None, v_scale=None,
                     partition_size: int = 0, workspace: Optional[torch.Tensor] = None, stream=None) -> int:
@@ -179,8 +282,7 @@ def decode_partials(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int
                  (seq_lens, "seq_lens"), (out, "out"), (lse, "lse"), (k_scale, "k_scale"), (v_scale, "v_scale"),
                  (workspace, "workspace")):
         _dev(t, n)
-    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
-        raise ValueError("block_table and seq_lens must be int32")
+    validate_decode_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, out, lse, k_scale, v_scale)
     B, Tq, Hq, D = q.shape
     nb, bs, Hkv, _ = k_cache.shape
     np_ = ctypes.c_int32(0)
@@ -197,7 +299,16 @@ def splitk_reduce(workspace: torch.Tensor, num_partitions: int, partition_size: 
     """Merge split-K partials (layout of include/pa_decode.h) into out/lse."""
     for t, n in ((workspace, "workspace"), (seq_lens, "seq_lens"), (out, "out"), (lse, "lse")):
         _dev(t, n)
+    if out.dim() != 4 or seq_lens.dtype != torch.int32 or seq_lens.numel() != out.shape[0]:
+        raise ValueError("out must be [B, Tq, Hq, D] and seq_lens int32 [B]")
+    if lse is not None and tuple(lse.shape) != tuple(out.shape[:3]):
+        raise ValueError("lse must be [B, Tq, Hq]")
     B, Tq, Hq, D = out.shape
+    rows = B * Tq * Hq
+    need = ((rows * num_partitions * D * 4 + 255) // 256 * 256) + rows * num_partitions * 4
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace holds %d bytes, %d partitions need %d" % (
+            workspace.numel() * workspace.element_size(), num_partitions, need))
     _check(_L().pa_decode_splitk_reduce(_ptr(workspace), int(num_partitions), int(partition_size), B, Tq, Hq, D,
                                         _ptr(seq_lens), _ptr(out), _code(out), _ptr(lse), _stream(stream, out)))
 
@@ -281,9 +392,9 @@ def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
                  (block_table, "block_table"), (seq_lens, "seq_lens"), (out, "out"), (lse, "lse"),
                  (k_scale, "k_scale"), (v_scale, "v_scale"), (workspace, "workspace")):
         _dev(t, n)
-    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or (
-            prefix_table is not None and prefix_table.dtype != torch.int32):
-        raise ValueError("prefix_table, block_table and seq_lens must be int32")
+    validate_decode_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, out, lse, k_scale, v_scale)
+    if prefix_table is not None and prefix_table.dtype != torch.int32:
+        raise ValueError("prefix_table must be int32")
     if prefix_table is not None and prefix_table.numel() < prefix_len // 16:
         raise ValueError("prefix_table holds %d blocks, prefix_len %d needs %d" % (
             prefix_table.numel(), prefix_len, prefix_len // 16))

@@ -9,6 +9,8 @@ from __future__ import annotations
 
 import concurrent.futures
 import glob
+import hashlib
+import json
 import os
 import shutil
 import subprocess
@@ -59,7 +61,30 @@ def build(jobs: int = 0) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
     os.replace(tmp, LIB_PATH)
+    _write_build_info(srcs)
     return LIB_PATH
+
+
+def _write_build_info(srcs) -> None:
+    """Record what the library was built from (the commit, when this is a git
+    checkout, and a digest of the sources), next to the library: runs on a
+    copy of the tree without its history can still name their build."""
+    h = hashlib.sha256()
+    for src in srcs + [os.path.join(HERE, "..", "include", "pa_decode.h")]:
+        h.update(open(src, "rb").read())
+    head = None
+    try:
+        r = subprocess.run(["git", "-C", HERE, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=10)
+        if r.returncode == 0:
+            head = r.stdout.strip()
+            d = subprocess.run(["git", "-C", HERE, "status", "--porcelain", "--untracked-files=no"],
+                               capture_output=True, text=True, timeout=10)
+            if d.returncode == 0 and d.stdout.strip():
+                head += "+uncommitted"
+    except (OSError, subprocess.SubprocessError):
+        pass
+    with open(os.path.join(LIB_DIR, "build_info.json"), "w") as f:
+        json.dump({"git_head": head, "source_digest": h.hexdigest()[:16]}, f)
 
 
 if __name__ == "__main__":

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -38,11 +39,34 @@ bool supported_d(int32_t D) { return D == 64 || D == 128 || D == 256; }
 constexpr int kBlock = 16;
 constexpr int kMaxTq = 16;
 constexpr int kMaxGroup = 64;
-constexpr int kCUs = 256;          // MI355X compute units
+constexpr int kDefaultCUs = 256;   // MI355X compute units; used when no HIP device is visible
+constexpr int kMaxDevices = 64;
 constexpr int kWavesPerCU = 8;     // resident one-wave (fp32-cache) workgroups per CU
 constexpr int kMinPartition = 256; // tokens; bounds the split-K partial traffic
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Compute units of the calling thread's current HIP device, read once per
+// device (a property query: nothing is enqueued and no device memory is
+// read, so the first call may come from inside a graph capture). A
+// partitioned GPU exposes fewer CUs per device and gets grids sized for them.
+// Without a visible device (sizing on a host with no GPU) the MI355X count.
+int device_cus() {
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();  // leave no error behind for the caller's next check
+        return kDefaultCUs;
+    }
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        n = kDefaultCUs;
+    }
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
 
 // Head-chunk width of the VALU decode for a query group of G heads, and the
 // number of chunks a kv head's group is split into.
@@ -138,8 +162,8 @@ int heads_per_wg(pa_dtype kv_dtype, int32_t D, int GT, int32_t Hkv) {
 // launches per_partition workgroups: enough partitions that the launch fills
 // the GPU once at wgs workgroups per CU, each a multiple of gran tokens and at
 // least min_p long, and one partition when that covers the context.
-int32_t split_len(int64_t len, int64_t per_partition, int wgs, int64_t gran, int64_t min_p) {
-    const int64_t target = (int64_t)kCUs * wgs;  // workgroups that fill the GPU once
+int32_t split_len(int64_t len, int64_t per_partition, int wgs, int64_t gran, int64_t min_p, int cus) {
+    const int64_t target = (int64_t)cus * wgs;  // workgroups that fill the GPU once
     if (per_partition < 1) per_partition = 1;   // an empty batch (B = 0)
     int64_t want_np = (target + per_partition - 1) / per_partition;
     if (want_np < 1) want_np = 1;
@@ -152,7 +176,7 @@ int32_t split_len(int64_t len, int64_t per_partition, int wgs, int64_t gran, int
 }
 
 int32_t partition_for(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
-                      int32_t max_seq_len) {
+                      int32_t max_seq_len, int cus) {
     if (max_seq_len <= kBlock) return kBlock;
     int GT = 0, nchunk, wph = waves_per_wg(kv_dtype);  // waves per kv head
     int64_t per_partition;  // workgroups per partition index
@@ -178,17 +202,17 @@ int32_t partition_for(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D,
     // step 25.3 -> 23.4 us, 8-16K 84.0 -> 72.0 us; the matrix-core decode of
     // short verify batches was 9-10% slower with the finer minimum)
     if (!mfma && D * GT <= 512) min_p /= 2;
-    return split_len(max_seq_len, per_partition, wgs_per_cu(kv_dtype, D, GT, mfma), gran, min_p);
+    return split_len(max_seq_len, per_partition, wgs_per_cu(kv_dtype, D, GT, mfma), gran, min_p, cus);
 }
 
 // Prefix pass of the shared-prefix decode: the matrix-core kernel takes the
 // B * Tq * G rows of a kv head as one row set, so a partition index launches
 // Hkv * (row chunks) workgroups.
-int32_t prefix_partition_for(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t prefix_len) {
+int32_t prefix_partition_for(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t prefix_len, int cus) {
     if (prefix_len <= kBlock) return kBlock;
     int NT, nchunk;
     row_chunks(B * Tq * (Hq / Hkv), &NT, &nchunk);
-    return split_len(prefix_len, (int64_t)Hkv * nchunk, 2, (int64_t)kBlock * 4, kMinPartition);
+    return split_len(prefix_len, (int64_t)Hkv * nchunk, 2, (int64_t)kBlock * 4, kMinPartition, cus);
 }
 
 int check_dims(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D) {
@@ -314,9 +338,10 @@ int plan_shared_prefix(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D
         return fail(PA_ERR_SHAPE, "partition sizes %d, %d must be 0 or positive multiples of %d", prefix_partition,
                     tail_partition, kBlock);
     const int32_t tail_len = max_seq_len - prefix_len;
-    pl->p_prefix = prefix_partition ? prefix_partition : prefix_partition_for(B, Tq, Hq, Hkv, prefix_len);
+    const int cus = device_cus();
+    pl->p_prefix = prefix_partition ? prefix_partition : prefix_partition_for(B, Tq, Hq, Hkv, prefix_len, cus);
     pl->np_prefix = prefix_len > 0 ? (prefix_len + pl->p_prefix - 1) / pl->p_prefix : 0;
-    pl->p_tail = tail_partition ? tail_partition : partition_for(B, Tq, Hq, Hkv, D, kv_dtype, tail_len);
+    pl->p_tail = tail_partition ? tail_partition : partition_for(B, Tq, Hq, Hkv, D, kv_dtype, tail_len, cus);
     pl->np_tail = (int32_t)(((int64_t)tail_len + pl->p_tail - 1) / pl->p_tail);
     const int64_t total = (int64_t)pl->np_prefix + pl->np_tail;
     if (total > 0x7FFFFFFF) return fail(PA_ERR_SHAPE, "too many partitions");
@@ -367,14 +392,28 @@ int pa_cache_write_check(const int64_t* slot_mapping, int64_t num_tokens, int64_
     return ok();
 }
 
-int32_t pa_choose_partition_size(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
-                                 int32_t max_seq_len) {
+int32_t pa_choose_partition_size_for_cus(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D,
+                                         pa_dtype kv_dtype, int32_t max_seq_len, int32_t num_cus) {
     int rc = check_dims(B, Tq, Hq, Hkv, D);
     if (rc) return rc;
     if (!kv_supported(kv_dtype)) return fail(PA_ERR_DTYPE, "kv dtype %d not supported", (int)kv_dtype);
     if (max_seq_len < 0) return fail(PA_ERR_SHAPE, "max_seq_len=%d must be >= 0", max_seq_len);
+    if (num_cus < 1) return fail(PA_ERR_SHAPE, "num_cus=%d must be >= 1", num_cus);
     ok();
-    return partition_for(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len);
+    return partition_for(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len, num_cus);
+}
+
+int32_t pa_choose_partition_size(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
+                                 int32_t max_seq_len) {
+    return pa_choose_partition_size_for_cus(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len, device_cus());
+}
+
+int32_t pa_device_cu_count(void) { return device_cus(); }
+
+const char* pa_decode_kernel_name(int32_t Tq, int32_t Hq, int32_t Hkv, pa_dtype kv_dtype) {
+    if (Tq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || !kv_supported(kv_dtype)) return "";
+    if (kv_dtype == PA_F32) return "decode_valu_kernel";
+    return use_mfma(Tq, Hq, Hkv, kv_dtype) ? "decode_mfma_kernel" : "decode_wave_kernel";
 }
 
 size_t pa_decode_workspace_bytes(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
@@ -382,7 +421,8 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv,
     if (check_dims(B, Tq, Hq, Hkv, D) || max_seq_len < 0 || partition_size < 0 || partition_size % kBlock)
         return 0;
     if (!kv_supported(kv_dtype)) return 0;
-    const int32_t P = partition_size ? partition_size : partition_for(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len);
+    const int32_t P =
+        partition_size ? partition_size : partition_for(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len, device_cus());
     const int64_t NP = max_seq_len > 0 ? ((int64_t)max_seq_len + P - 1) / P : 1;
     if (NP <= 1) return 0;
     const size_t rows = (size_t)B * Tq * Hq;
@@ -440,13 +480,16 @@ int pa_decode(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq
     if (partition_size < 0 || partition_size % kBlock)
         return fail(PA_ERR_SHAPE, "partition_size=%d must be 0 or a positive multiple of %d", partition_size, kBlock);
 
-    const int32_t P = partition_size ? partition_size : partition_for(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len);
+    const int32_t P =
+        partition_size ? partition_size : partition_for(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len, device_cus());
     const int64_t NP64 = max_seq_len > 0 ? ((int64_t)max_seq_len + P - 1) / P : 1;
     if (NP64 > 0x7FFFFFFF) return fail(PA_ERR_SHAPE, "too many partitions");
     const int32_t NP = (int32_t)NP64;
     const size_t need = pa_decode_workspace_bytes(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len, P);
     if (NP > 1 && (!workspace || workspace_bytes < need))
         return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+    // the reduce that must follow reads the partials as 16-byte vectors
+    if (NP > 1 && !aligned16(workspace)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
     *num_partitions = NP;
     if (B == 0) return ok();
 

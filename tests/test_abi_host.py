@@ -236,3 +236,47 @@ def test_empty_batch_with_the_heuristic(lib):
         assert lib.pa_choose_partition_size(0, 8, 24, 4, 256, kv, 65536) > 0
     rc = lib.pa_decode(*decode_args(B=0, partition_size=0, workspace=A, workspace_bytes=1 << 30))
     assert rc == 0, lib.pa_last_error()
+
+
+def test_decode_rejects_a_misaligned_workspace_before_launching(lib):
+    # several partitions: the reduce that must follow reads 16-byte vectors,
+    # so the decode refuses the workspace before any launch
+    rc = lib.pa_decode(*decode_args(partition_size=256, workspace=ctypes.c_void_p(0x1008),
+                                    workspace_bytes=1 << 30))
+    assert rc == -7, lib.pa_last_error()
+    # one partition needs no workspace, aligned or not (B = 0: nothing launched)
+    rc = lib.pa_decode(*decode_args(B=0, partition_size=1008, workspace=ctypes.c_void_p(0x1008),
+                                    workspace_bytes=1 << 30))
+    assert rc == 0, lib.pa_last_error()
+
+
+def test_heuristic_follows_the_device_compute_units(lib):
+    # no device on this host: the MI355X count, and the plain heuristic equals
+    # the injected one at 256 CUs
+    assert lib.pa_device_cu_count() == 256
+    for args in ((4, 1, 24, 4, 256, 1, 65536), (1, 1, 24, 4, 256, 2, 250000), (4, 8, 24, 4, 256, 1, 30321),
+                 (8, 1, 32, 8, 128, 1, 3637)):
+        assert lib.pa_choose_partition_size_for_cus(*args, 256) == lib.pa_choose_partition_size(*args)
+    # the 64K workload fills one four-wave workgroup per CU: 4 sequences need
+    # 64 partitions on 256 CUs, 32 on 128 (a partitioned GPU), 76 on 304
+    assert lib.pa_choose_partition_size_for_cus(4, 1, 24, 4, 256, 1, 65536, 256) == 1024
+    assert lib.pa_choose_partition_size_for_cus(4, 1, 24, 4, 256, 1, 65536, 128) == 2048
+    assert lib.pa_choose_partition_size_for_cus(4, 1, 24, 4, 256, 1, 65536, 304) == 864
+    assert lib.pa_choose_partition_size_for_cus(4, 1, 24, 4, 256, 1, 65536, 32) == 8192
+    # int8 250K on the matrix cores (two workgroups per CU, 4 kv heads): 64
+    # CUs hold 128 workgroups, 32 partitions of ceil(250000 / 32) tokens
+    # rounded up to whole blocks of the 4 waves (64 tokens)
+    assert lib.pa_choose_partition_size_for_cus(1, 1, 24, 4, 256, 2, 250000, 64) == 7872
+    assert lib.pa_choose_partition_size_for_cus(4, 1, 24, 4, 256, 1, 65536, 0) == -2
+
+
+def test_kernel_name_query(lib):
+    assert lib.pa_decode_kernel_name(1, 24, 4, 1) == b"decode_wave_kernel"   # bf16, G = 6
+    assert lib.pa_decode_kernel_name(1, 24, 4, 2) == b"decode_mfma_kernel"   # int8, G = 6
+    assert lib.pa_decode_kernel_name(1, 16, 4, 2) == b"decode_wave_kernel"   # int8, G = 4
+    assert lib.pa_decode_kernel_name(8, 24, 4, 1) == b"decode_mfma_kernel"   # Tq > 1
+    assert lib.pa_decode_kernel_name(1, 64, 4, 1) == b"decode_mfma_kernel"   # G = 16
+    assert lib.pa_decode_kernel_name(1, 24, 4, 4) == b"decode_wave_kernel"   # nvfp4, G = 6
+    assert lib.pa_decode_kernel_name(2, 4, 1, 0) == b"decode_valu_kernel"    # fp32 caches
+    assert lib.pa_decode_kernel_name(1, 7, 2, 1) == b""
+

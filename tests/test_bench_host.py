@@ -43,3 +43,22 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_bench_names_the_kernel_the_library_launches():
+    import paged_attention_decode_02_amd as pa
+
+    for name, spec in SPECS.items():
+        kname, srcs = bench.decode_kernel(spec)
+        assert kname == pa.decode_kernel_name(spec.Tq, spec.Hq, spec.Hkv, bench_dtype(spec.cache_dtype)), name
+        assert srcs[0] == kname.replace("_kernel", ".hip"), (kname, srcs)
+    assert bench.decode_kernel(SPECS["long64k_bf16"])[0] == "decode_wave_kernel"
+    assert bench.decode_kernel(SPECS["int8_250k"])[0] == "decode_mfma_kernel"
+    assert bench.decode_kernel(SPECS["tiny_f32"])[0] == "decode_valu_kernel"
+
+
+def bench_dtype(name):
+    import torch
+
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "fp8": torch.float8_e4m3fn,
+            "nvfp4": torch.float4_e2m1fn_x2}[name]

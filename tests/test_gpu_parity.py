@@ -120,11 +120,22 @@ def test_reduce_splits_columns_of_few_rows(D):
 
 
 @pytest.mark.parametrize("Tq", [2, 3, 8, 16])
-@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "nvfp4"])
+@pytest.mark.parametrize("kv", ["f32", "bf16", "i8", "fp8", "nvfp4"])
 def test_query_tokens_causal(Tq, kv):
     spec = scaled("verify_bf16", B=3, Tq=Tq, Hq=8, Hkv=2, D=128, seq_lens=(Tq, 900), shared_prefix=0,
                   cache_dtype=kv)
     run_workload(generate(spec, seed=Tq), partition_size=256)
+
+
+@pytest.mark.parametrize("Tq", [1, 3])
+def test_f32_cache_head_chunks_and_empty_rows(Tq):
+    # the fp32-cache kernel with a group of 12 query heads (two head chunks of
+    # at most 8), rows with no key and ragged lengths, several partitions
+    spec = scaled("gqa_bf16", B=4, Tq=Tq, Hq=24, Hkv=2, D=64, seq_lens=(0, 700), src_dtype="f32",
+                  cache_dtype="f32", q_dtype="f32")
+    w = generate(spec, seed=40 + Tq, seq_lens=[0, Tq, 37, 700])
+    for P in (16, 0):
+        run_workload(w, partition_size=P)
 
 
 def test_empty_and_short_rows():
