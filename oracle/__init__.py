@@ -77,6 +77,12 @@ def _load():
             lib.pa_oracle_e2m1_encode.restype = I
             lib.pa_oracle_nvfp4_row_bytes.argtypes = [I]
             lib.pa_oracle_nvfp4_row_bytes.restype = I
+            lib.pa_oracle_sparse_mean_keys.argtypes = [P, I, P, I, I, I, P, I, P, I, I, I, P]
+            lib.pa_oracle_sparse_mean_keys.restype = I
+            lib.pa_oracle_sparse_select.argtypes = [P, I, I, I, I, I, I, F, P, I, P, I, I, I, P, P, P]
+            lib.pa_oracle_sparse_select.restype = I
+            lib.pa_oracle_decode_subset.argtypes = dec + [P, P, I, I, P, P, I]
+            lib.pa_oracle_decode_subset.restype = I
             _lib = lib
     return _lib
 
@@ -224,3 +230,101 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_table:
     if rc != 0:
         raise ValueError("oracle decode failed: %d" % rc)
     return out, lse
+
+
+# ---------------------------------------------------------------- sparse decode
+def num_sparse_blocks(L: int, sparse_block: int) -> int:
+    return (int(L) + sparse_block - 1) // sparse_block
+
+
+def sparse_max_selected(max_seq_len: int, sparse_block: int, top_blocks: int) -> int:
+    """Largest number of sparse blocks one (sequence, kv head) can select: the
+    top_blocks, or the (at most two) blocks holding the query tokens."""
+    return min(num_sparse_blocks(max_seq_len, sparse_block), max(top_blocks, 2))
+
+
+def sparse_mean_keys(k_cache: np.ndarray, block_table: np.ndarray, seq_lens: np.ndarray, sparse_block: int,
+                     max_sblocks: int, k_scale: Optional[np.ndarray] = None, D: Optional[int] = None) -> np.ndarray:
+    """fp64 mean keys [B, max_sblocks, Hkv, D] of every sparse block below each
+    sequence's length (NaN elsewhere)."""
+    lib = _load()
+    nb, bs, Hkv, row = k_cache.shape
+    D = D or row
+    kv_dt = _cache_dtype(k_cache, D)
+    table = _c(block_table, np.int32)
+    lens = _c(seq_lens, np.int32)
+    B = lens.shape[0]
+    out = np.full((B, max_sblocks, Hkv, D), np.nan)
+    rc = lib.pa_oracle_sparse_mean_keys(_ptr(np.ascontiguousarray(k_cache)), DTYPE_CODE[kv_dt], _ptr(k_scale), bs,
+                                        Hkv, D, _ptr(table), table.shape[1], _ptr(lens), B, sparse_block,
+                                        max_sblocks, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle sparse_mean_keys failed: %d" % rc)
+    return out
+
+
+def sparse_select(q: np.ndarray, mean_k: np.ndarray, seq_lens: np.ndarray, softmax_scale: float, sparse_block: int,
+                  top_blocks: int, max_sel: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Selected sparse blocks per (b, kv head): (selected [B, Hkv, max_sel]
+    int32, increasing, -1 padded; count [B, Hkv]; candidate scores [B, Hkv,
+    max_sblocks] fp64, NaN for the kept blocks and past the end). mean_k is
+    [B, max_sblocks, Hkv, D] (fp64, or the GPU's fp32 widened)."""
+    lib = _load()
+    q = np.ascontiguousarray(q)
+    B, Tq, Hq, D = q.shape
+    mk = _c(mean_k, np.float64)
+    _, max_sblocks, Hkv, _ = mk.shape
+    lens = _c(seq_lens, np.int32)
+    sel = np.full((B, Hkv, max_sel), -1, dtype=np.int32)
+    cnt = np.zeros((B, Hkv), dtype=np.int32)
+    scores = np.full((B, Hkv, max_sblocks), np.nan)
+    rc = lib.pa_oracle_sparse_select(_ptr(q), DTYPE_CODE[_dtype_of(q)], B, Tq, Hq, Hkv, D,
+                                     ctypes.c_float(softmax_scale), _ptr(mk), max_sblocks, _ptr(lens), sparse_block,
+                                     top_blocks, max_sel, _ptr(sel), _ptr(cnt), _ptr(scores))
+    if rc != 0:
+        raise ValueError("oracle sparse_select failed: %d" % rc)
+    return sel, cnt, scores
+
+
+def decode_subset(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_table: np.ndarray,
+                  seq_lens: np.ndarray, softmax_scale: float, selected: np.ndarray, count: np.ndarray,
+                  sparse_block: int, k_scale: Optional[np.ndarray] = None, v_scale: Optional[np.ndarray] = None,
+                  nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """fp64 decode of every row over the keys of its kv head's selected sparse
+    blocks (causal rule as in decode)."""
+    lib = _load()
+    q = np.ascontiguousarray(q)
+    B, Tq, Hq, D = q.shape
+    nb, bs, Hkv, _ = k_cache.shape
+    table = _c(block_table, np.int32)
+    lens = _c(seq_lens, np.int32)
+    sel = _c(selected, np.int32)
+    cnt = _c(count, np.int32)
+    assert sel.shape[:2] == (B, Hkv) and cnt.shape == (B, Hkv)
+    kv_dt = _cache_dtype(k_cache, D)
+    out = np.full((B, Tq, Hq, D), np.nan)
+    lse = np.full((B, Tq, Hq), np.nan)
+    common = [_ptr(q), DTYPE_CODE[_dtype_of(q)], B, Tq, Hq, Hkv, D, _ptr(np.ascontiguousarray(k_cache)),
+              _ptr(np.ascontiguousarray(v_cache)), DTYPE_CODE[kv_dt], _ptr(k_scale), _ptr(v_scale), bs,
+              _ptr(table), table.shape[1], _ptr(lens), ctypes.c_float(softmax_scale)]
+    rc = lib.pa_oracle_decode_subset(*common, _ptr(sel), _ptr(cnt), sel.shape[2], sparse_block, _ptr(out), _ptr(lse),
+                                     nthreads)
+    if rc != 0:
+        raise ValueError("oracle decode_subset failed: %d" % rc)
+    return out, lse
+
+
+def decode_sparse(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_table: np.ndarray,
+                  seq_lens: np.ndarray, softmax_scale: float, sparse_block: int, top_blocks: int,
+                  k_scale: Optional[np.ndarray] = None, v_scale: Optional[np.ndarray] = None):
+    """The whole sparse decode: mean keys, selection, decode over the selected
+    blocks. Returns (out, lse, selected, count, mean_k)."""
+    B, Tq, Hq, D = q.shape
+    L = int(np.max(seq_lens)) if len(seq_lens) else 0
+    nsb = max(1, num_sparse_blocks(L, sparse_block))
+    mk = sparse_mean_keys(k_cache, block_table, seq_lens, sparse_block, nsb, k_scale, D)
+    sel, cnt, _ = sparse_select(q, mk, seq_lens, softmax_scale, sparse_block, top_blocks,
+                                sparse_max_selected(L, sparse_block, top_blocks) or 1)
+    out, lse = decode_subset(q, k_cache, v_cache, block_table, seq_lens, softmax_scale, sel, cnt, sparse_block,
+                             k_scale, v_scale)
+    return out, lse, sel, cnt, mk

@@ -61,6 +61,29 @@
  *    head with that head's block scales: the scale of elements 16k .. 16k + 15
  *    of token t at byte 16k + 4 (t mod 4) + t / 4 of the plane.
  *
+ *
+ * Sparse block-selection decode (vllm-sm70 page: "Changes relative to
+ * 1Cat-vLLM", item 8, sparse-decode mean keys refreshed for every request of a
+ * decode batch; "Known limitations", the sparse decode selection supports at
+ * most 4096 key blocks, a 262,144-token table at 64-token blocks). The pages
+ * name the parts, not the rule; the reading taken here:
+ *  - a sequence's positions form sparse blocks of SB tokens (a multiple of
+ *    the 16-token cache block; 64 on the page): block j = [SB j, SB j + SB)
+ *    below L_b, ceil(L_b / SB) <= 4096 of them;
+ *  - the mean key of block j for kv head g is the plain mean of its keys
+ *    (dequantised for quantised caches) over the block's tokens below L_b;
+ *  - the blocks holding any query token (positions L_b - Tq .. L_b - 1: one or
+ *    two blocks, as Tq <= 16 <= SB) are always selected ("kept");
+ *  - every other block j (all lie before the kept ones) scores
+ *    s_j = max over the query rows (t, h) of kv head g of
+ *    softmax_scale * q[b, t, h] . mean_key[b, j, g];
+ *  - top_blocks - (kept count) of them with the largest scores are
+ *    selected, ties to the lower index (at least the kept blocks are
+ *    selected; every block when top_blocks >= ceil(L_b / SB));
+ *  - row (b, t, h) attends, with the exact softmax, to the keys of the
+ *    selected blocks of its kv head at positions p <= L_b - Tq + t (the same
+ *    causal rule as the plain decode).
+ *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
  */
 #include <math.h>
@@ -504,6 +527,181 @@ int pa_oracle_decode_split(ORACLE_ARGS, int partition_size, const int64_t* rows,
     ORACLE_PACK;
     if (partition_size < 1) return -2;
     return run(&a, rows, num_rows, partition_size, out, lse, nthreads);
+}
+
+/* ------------------------------------------------------------------------
+ * Sparse block-selection decode (the reading in the header).
+ * ---------------------------------------------------------------------- */
+
+/* Mean keys: out[((b * max_sblocks + j) * Hkv + g) * D + d] (fp64) for every
+ * sparse block j < ceil(L_b / SB) of every sequence; other entries untouched.
+ * Returns -2 when a sequence has more than max_sblocks blocks. */
+int pa_oracle_sparse_mean_keys(const void* k_cache, int kv_dtype, const float* k_scale, int block_size, int Hkv,
+                               int D, const int32_t* block_table, int max_blocks, const int32_t* seq_lens, int B,
+                               int sparse_block, int max_sblocks, double* out) {
+    if (!k_cache || !block_table || !seq_lens || !out) return -1;
+    if (sparse_block < block_size || sparse_block % block_size || B < 0 || Hkv < 1 || D < 1) return -2;
+    for (int b = 0; b < B; ++b) {
+        const int64_t L = seq_lens[b];
+        const int64_t nsb = (L + sparse_block - 1) / sparse_block;
+        if (nsb > max_sblocks) return -2;
+        for (int64_t j = 0; j < nsb; ++j) {
+            const int64_t p0 = j * sparse_block, p1 = p0 + sparse_block < L ? p0 + sparse_block : L;
+            for (int g = 0; g < Hkv; ++g) {
+                double* m = out + ((b * (int64_t)max_sblocks + j) * Hkv + g) * D;
+                for (int d = 0; d < D; ++d) m[d] = 0.0;
+                for (int64_t p = p0; p < p1; ++p) {
+                    const int64_t blk = block_table[(int64_t)b * max_blocks + p / block_size];
+                    const int64_t row = (blk * block_size + p % block_size) * Hkv + g;
+                    for (int d = 0; d < D; ++d)
+                        m[d] += cache_elem(k_cache, kv_dtype, k_scale, row, Hkv, block_size, D, d);
+                }
+                for (int d = 0; d < D; ++d) m[d] /= (double)(p1 - p0);
+            }
+        }
+    }
+    return 0;
+}
+
+/* First sparse block holding a query token of sequence b (the kept blocks
+ * run from it to the last block); the number of blocks is ceil(L / SB). */
+static int64_t first_kept_block(int64_t L, int Tq, int sparse_block) {
+    int64_t first_q = L - Tq;
+    if (first_q < 0) first_q = 0;
+    return first_q / sparse_block;
+}
+
+/* Selection for every (b, g): selected[(b * Hkv + g) * max_sel + i] = the
+ * i-th selected sparse block in increasing order, -1 after the last; count
+ * [b * Hkv + g] = how many. scores[(b * Hkv + g) * max_sblocks + j] = s_j of
+ * every candidate block (NaN for kept blocks and past the end). mean_k:
+ * fp64 [B, max_sblocks, Hkv, D]. Returns -2 if max_sel is too small. */
+int pa_oracle_sparse_select(const void* q, int q_dtype, int B, int Tq, int Hq, int Hkv, int D, float softmax_scale,
+                            const double* mean_k, int max_sblocks, const int32_t* seq_lens, int sparse_block,
+                            int top_blocks, int max_sel, int32_t* selected, int32_t* count, double* scores) {
+    if (!q || !mean_k || !seq_lens || !selected || !count || !scores) return -1;
+    if (Hq % Hkv || top_blocks < 1 || sparse_block < 1) return -2;
+    const int G = Hq / Hkv;
+    for (int b = 0; b < B; ++b) {
+        const int64_t L = seq_lens[b];
+        const int64_t nsb = (L + sparse_block - 1) / sparse_block;
+        if (nsb > max_sblocks) return -2;
+        const int64_t kept0 = L > 0 ? first_kept_block(L, Tq, sparse_block) : 0;
+        for (int g = 0; g < Hkv; ++g) {
+            double* sc = scores + ((int64_t)b * Hkv + g) * max_sblocks;
+            int32_t* sel = selected + ((int64_t)b * Hkv + g) * max_sel;
+            for (int64_t j = 0; j < max_sblocks; ++j) sc[j] = NAN;
+            for (int i = 0; i < max_sel; ++i) sel[i] = -1;
+            /* candidate scores: the largest over the group's query rows */
+            for (int64_t j = 0; j < kept0; ++j) {
+                const double* m = mean_k + (((int64_t)b * max_sblocks + j) * Hkv + g) * D;
+                double best = -INFINITY;
+                for (int t = 0; t < Tq; ++t)
+                    for (int hh = 0; hh < G; ++hh) {
+                        const int64_t qoff = (((int64_t)b * Tq + t) * Hq + g * G + hh) * D;
+                        double dot = 0.0;
+                        for (int d = 0; d < D; ++d) dot += elem(q, q_dtype, qoff + d) * m[d];
+                        const double v = (double)softmax_scale * dot;
+                        if (v > best) best = v;
+                    }
+                sc[j] = best;
+            }
+            /* take the top candidates one at a time: the largest score, the
+             * lower index on a tie */
+            int64_t want = (int64_t)top_blocks - (nsb - kept0);
+            if (want < 0) want = 0;
+            if (want > kept0) want = kept0;
+            char* taken = (char*)calloc((size_t)(nsb > 0 ? nsb : 1), 1);
+            for (int64_t k = 0; k < want; ++k) {
+                int64_t arg = -1;
+                for (int64_t j = 0; j < kept0; ++j)
+                    if (!taken[j] && (arg < 0 || sc[j] > sc[arg])) arg = j;
+                taken[arg] = 1;
+            }
+            for (int64_t j = kept0; j < nsb; ++j) taken[j] = 1;
+            int64_t n = 0;
+            for (int64_t j = 0; j < nsb; ++j)
+                if (taken[j]) {
+                    if (n >= max_sel) {
+                        free(taken);
+                        return -2;
+                    }
+                    sel[n++] = (int32_t)j;
+                }
+            count[(int64_t)b * Hkv + g] = (int32_t)n;
+            free(taken);
+        }
+    }
+    return 0;
+}
+
+/* Attention of row r over the keys of the listed sparse blocks of its kv head
+ * that lie at positions <= L_b - Tq + t, softmax materialised in full, keys
+ * taken in increasing position order. */
+static void decode_row_subset(const args_t* a, int64_t r, const int32_t* selected, const int32_t* count, int max_sel,
+                              int sparse_block, double* out, double* lse) {
+    const int h = (int)(r % a->Hq), t = (int)((r / a->Hq) % a->Tq), b = (int)(r / ((int64_t)a->Hq * a->Tq));
+    const int G = a->Hq / a->Hkv, g = h / G;
+    double* o = out + r * a->D;
+    const int64_t n = visible_keys(a, b, t), L = a->seq_lens[b];
+    const int32_t* sel = selected + ((int64_t)b * a->Hkv + g) * max_sel;
+    const int cnt = count[(int64_t)b * a->Hkv + g];
+    for (int d = 0; d < a->D; ++d) o[d] = 0.0;
+    /* visible positions of the selected blocks */
+    int64_t m = 0;
+    int64_t* pos = (int64_t*)malloc(((size_t)cnt * sparse_block + 1) * sizeof(int64_t));
+    for (int i = 0; i < cnt; ++i)
+        for (int64_t p = (int64_t)sel[i] * sparse_block; p < (int64_t)(sel[i] + 1) * sparse_block; ++p)
+            if (p < n && p < L) pos[m++] = p;
+    if (m == 0) {
+        lse[r] = -INFINITY;
+        free(pos);
+        return;
+    }
+    const int64_t qoff = (((int64_t)b * a->Tq + t) * a->Hq + h) * a->D;
+    double* s = (double*)malloc((size_t)m * sizeof(double));
+    for (int64_t k = 0; k < m; ++k) {
+        const int64_t blk = a->block_table[(int64_t)b * a->max_blocks + pos[k] / a->block_size];
+        const int64_t row = (blk * a->block_size + pos[k] % a->block_size) * a->Hkv + g;
+        double dot = 0.0;
+        for (int d = 0; d < a->D; ++d)
+            dot += elem(a->q, a->q_dtype, qoff + d) *
+                   cache_elem(a->k_cache, a->kv_dtype, a->k_scale, row, a->Hkv, a->block_size, a->D, d);
+        s[k] = (double)a->softmax_scale * dot;
+    }
+    double M = -INFINITY;
+    for (int64_t k = 0; k < m; ++k)
+        if (s[k] > M) M = s[k];
+    double Z = 0.0;
+    for (int64_t k = 0; k < m; ++k) {
+        s[k] = exp(s[k] - M);
+        Z += s[k];
+    }
+    for (int64_t k = 0; k < m; ++k) value_row_axpy(a, b, g, pos[k], s[k], o);
+    for (int d = 0; d < a->D; ++d) o[d] /= Z;
+    lse[r] = M + log(Z);
+    free(s);
+    free(pos);
+}
+
+/* Decode over the listed sparse blocks (selected / count as written by
+ * pa_oracle_sparse_select, or a selection read back from the GPU). */
+int pa_oracle_decode_subset(ORACLE_ARGS, const int32_t* selected, const int32_t* count, int max_sel,
+                            int sparse_block, double* out, double* lse, int nthreads) {
+    ORACLE_PACK;
+    int rc = check_args(&a);
+    if (rc) return rc;
+    if (!selected || !count) return -1;
+    if (sparse_block < 1 || max_sel < 0) return -2;
+    const int64_t total = (int64_t)B * Tq * Hq;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < total; ++r) decode_row_subset(&a, r, selected, count, max_sel, sparse_block, out, lse);
+    return 0;
 }
 
 int pa_oracle_max_threads(void) {
