@@ -288,6 +288,33 @@ int pa_decode_check(const int32_t* block_table, int32_t max_blocks_per_seq, cons
 int pa_cache_write_check(const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks, int32_t block_size,
                          int32_t* status, void* stream);
 
+/*
+ * pa_decode_noalloc — pa_decode followed by pa_decode_splitk_reduce, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the split-K partials
+ * go to a scratch array that the library owns, PA_NOALLOC_SCRATCH_BYTES per
+ * GPU, held from the library's first use on that GPU until the process ends.
+ * Arguments, results and errors as for pa_decode, minus the workspace: out
+ * (and lse when non-NULL) are always written, whatever the partition count.
+ * Calls whose partials need more than PA_NOALLOC_SCRATCH_BYTES
+ * (pa_decode_workspace_bytes with the same arguments) return
+ * PA_ERR_WORKSPACE before any launch. No allocation of any kind: no hipMalloc,
+ * no hipFree, no allocating library routine. The first call on a device
+ * resolves the scratch's device address there (hipGetSymbolAddress); make it
+ * outside a graph capture. Every call on one GPU shares that GPU's scratch:
+ * calls that overlap in time on one GPU (different streams, or different
+ * host threads without ordering) race on it and give wrong results; calls on
+ * one stream are ordered and safe. Nothing in the scratch needs to start at
+ * zero: each call writes every partial its reduce reads.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int pa_decode_noalloc(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D,
+                      const void* k_cache, const void* v_cache, pa_dtype kv_dtype, const float* k_scale,
+                      const float* v_scale, int64_t num_blocks, int32_t block_size, const int32_t* block_table,
+                      int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                      float softmax_scale, int32_t partition_size, void* out, pa_dtype out_dtype, float* lse,
+                      void* stream);
+
 /* Message for the calling thread's last non-zero return ("" if none). */
 const char* pa_last_error(void);
 

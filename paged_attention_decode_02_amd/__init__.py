@@ -26,7 +26,7 @@ __all__ = [
     "PaError", "cache_write", "decode", "decode_partials", "splitk_reduce", "workspace_bytes",
     "choose_partition_size", "choose_partition_size_for_cus", "device_cu_count", "decode_kernel_name",
     "library_path", "load", "DTYPE_CODE", "decode_shared_prefix", "shared_prefix_workspace_bytes",
-    "validate_decode_args", "validate_cache_write_args",
+    "validate_decode_args", "validate_cache_write_args", "decode_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,8 +44,11 @@ EXPORTS = (
     "pa_cache_write", "pa_decode", "pa_decode_splitk_reduce", "pa_decode_workspace_bytes",
     "pa_choose_partition_size", "pa_decode_check", "pa_cache_write_check", "pa_last_error",
     "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes", "pa_choose_partition_size_for_cus",
-    "pa_device_cu_count", "pa_decode_kernel_name",
+    "pa_device_cu_count", "pa_decode_kernel_name", "pa_decode_noalloc",
 )
+
+# size of the library-owned scratch of pa_decode_noalloc (PA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class PaError(RuntimeError):
@@ -96,6 +99,9 @@ def load():
         lib.pa_device_cu_count.restype = I32
         lib.pa_decode_kernel_name.argtypes = [I32, I32, I32, I32]
         lib.pa_decode_kernel_name.restype = ctypes.c_char_p
+        lib.pa_decode_noalloc.argtypes = [P, I32, I32, I32, I32, I32, I32, P, P, I32, P, P, I64, I32, P, I32, P, I32,
+                                          F, I32, P, I32, P, P]
+        lib.pa_decode_noalloc.restype = ctypes.c_int
         lib.pa_last_error.argtypes = []
         lib.pa_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -367,6 +373,24 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_
     if np_ > 1:
         splitk_reduce(workspace, np_, P, seq_lens, out, lse, stream)
     return out, lse
+
+
+def decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, softmax_scale: float,
+                   out: torch.Tensor, lse: Optional[torch.Tensor] = None, k_scale=None, v_scale=None,
+                   partition_size: int = 0, stream=None) -> None:
+    """pa_decode_noalloc: decode and (when needed) the reduce, with the split-K
+    partials in the library's own scratch; out/lse are written. Neither the
+    library nor this function allocates: out (and lse) come from the caller."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_table, "block_table"),
+                 (seq_lens, "seq_lens"), (out, "out"), (lse, "lse"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _dev(t, n)
+    validate_decode_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, out, lse, k_scale, v_scale)
+    B, Tq, Hq, D = q.shape
+    nb, bs, Hkv, _ = k_cache.shape
+    _check(_L().pa_decode_noalloc(_ptr(q), _code(q), B, Tq, Hq, Hkv, D, _ptr(k_cache), _ptr(v_cache), _code(k_cache),
+                                  _ptr(k_scale), _ptr(v_scale), nb, bs, _ptr(block_table), block_table.shape[1],
+                                  _ptr(seq_lens), int(max_seq_len), float(softmax_scale), int(partition_size),
+                                  _ptr(out), _code(out), _ptr(lse), _stream(stream, q)))
 
 
 def shared_prefix_workspace_bytes(B: int, Tq: int, Hq: int, Hkv: int, D: int, kv_dtype: torch.dtype,

@@ -353,6 +353,40 @@ int plan_shared_prefix(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D
 
 }  // namespace
 
+// Library-owned scratch of pa_decode_noalloc (the split-K partials), one copy
+// per GPU the library runs on, held until the process ends. In host code the
+// name is only a host-side handle: the device address of the copy on the
+// current device comes from hipGetSymbolAddress, and only that address is
+// passed to kernels.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of the current device's scratch copy, resolved once per
+// device (on the first pa_decode_noalloc call with that device current).
+int scratch_address(void** out) {
+    static std::atomic<void*> addr[kMaxDevices];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return fail(PA_ERR_LAUNCH, "no usable HIP device (%s, device %d)", hipGetErrorString(e), dev);
+    }
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return fail(PA_ERR_LAUNCH, "scratch address on device %d: %s", dev, hipGetErrorString(e));
+        }
+        addr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return PA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* pa_last_error(void) { return g_err.c_str(); }
@@ -616,6 +650,39 @@ int pa_decode_splitk_reduce(const void* workspace, int32_t num_partitions, int32
     p.lse = lse;
     hipError_t e = pa::launch_splitk_reduce(p, (hipStream_t)stream);
     if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "reduce launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int pa_decode_noalloc(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D,
+                      const void* k_cache, const void* v_cache, pa_dtype kv_dtype, const float* k_scale,
+                      const float* v_scale, int64_t num_blocks, int32_t block_size, const int32_t* block_table,
+                      int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                      float softmax_scale, int32_t partition_size, void* out, pa_dtype out_dtype, float* lse,
+                      void* stream) {
+    int rc = check_decode_args(q, q_dtype, B, Tq, Hq, Hkv, D, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                               num_blocks, block_size, block_table, max_blocks_per_seq, seq_lens, max_seq_len,
+                               out, out_dtype);
+    if (rc) return rc;
+    if (partition_size < 0 || partition_size % kBlock)
+        return fail(PA_ERR_SHAPE, "partition_size=%d must be 0 or a positive multiple of %d", partition_size, kBlock);
+    const int32_t P =
+        partition_size ? partition_size : partition_for(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len, device_cus());
+    const size_t need = pa_decode_workspace_bytes(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len, P);
+    if (need > (size_t)PA_NOALLOC_SCRATCH_BYTES)
+        return fail(PA_ERR_WORKSPACE,
+                    "the split-K partials need %zu bytes, above the %u-byte library scratch of pa_decode_noalloc "
+                    "(use pa_decode with a workspace, or a larger partition_size)",
+                    need, (unsigned)PA_NOALLOC_SCRATCH_BYTES);
+    if (B == 0) return ok();
+    void* ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc) return rc;
+    int32_t np = 0;
+    rc = pa_decode(q, q_dtype, B, Tq, Hq, Hkv, D, k_cache, v_cache, kv_dtype, k_scale, v_scale, num_blocks, block_size,
+                   block_table, max_blocks_per_seq, seq_lens, max_seq_len, softmax_scale, P, out, out_dtype, lse, ws,
+                   need, &np, stream);
+    if (rc) return rc;
+    if (np > 1) return pa_decode_splitk_reduce(ws, np, P, B, Tq, Hq, D, seq_lens, out, out_dtype, lse, stream);
     return ok();
 }
 

@@ -280,3 +280,15 @@ def test_kernel_name_query(lib):
     assert lib.pa_decode_kernel_name(2, 4, 1, 0) == b"decode_valu_kernel"    # fp32 caches
     assert lib.pa_decode_kernel_name(1, 7, 2, 1) == b""
 
+
+def test_noalloc_rejects_partials_beyond_its_scratch(lib):
+    # 64 x 16 x 64 rows x 64 partitions x 1 KiB of partials: far above the
+    # 32 MiB library scratch, refused before any device is touched
+    args = decode_args(B=64, Tq=16, Hq=64, Hkv=4, D=256, max_seq_len=65536, max_blocks=4096, partition_size=1024)
+    args = args[:23] + [None]  # pa_decode_noalloc: no workspace, size or partition count; then the stream
+    rc = lib.pa_decode_noalloc(*args)
+    assert rc == -5, lib.pa_last_error()
+    assert b"scratch" in lib.pa_last_error()
+    assert pa.NOALLOC_SCRATCH_BYTES == 32 << 20
+    text = open(HEADER).read()
+    assert "#define PA_NOALLOC_SCRATCH_BYTES (32u << 20)" in text
