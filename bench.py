@@ -81,7 +81,7 @@ def unique_bytes(w) -> int:
 
 
 _KERNEL_SOURCES = {"decode_valu_kernel": "decode_valu.hip", "decode_mfma_kernel": "decode_mfma.hip",
-                   "decode_wave_kernel": "decode_wave.hip"}
+                   "decode_wave_kernel": "decode_wave.hip", "decode_stream_kernel": "decode_stream.hip"}
 _CODES = {"f32": 0, "bf16": 1, "i8": 2, "fp8": 3, "nvfp4": 4}
 
 
@@ -268,6 +268,55 @@ def summarize_trace(trace_csv: str, workload: str, command: str, tail_cold: int 
                     x = d[i0:i1]
                     lines.append("| %s | %d | %.2f | %.2f |" % (name, len(x), x.mean(), np.median(x)))
                 lines += ["", "decode_mean_us_roofline_launches: %.2f" % d[W + 2 * K:W + 3 * K].mean()]
+    lines.append("")
+    return "\n".join(lines)
+
+
+def summarize_sq(runs, workload: str) -> str:
+    """Markdown table of SQ counters per decode dispatch, from one or more
+    (label, kernel-name substring, counter CSV, command) runs; counts are
+    normalised per 16-token block and kv head of the workload."""
+    import csv
+    import collections
+
+    from workloads import SPECS, generate
+
+    w = generate(SPECS[workload])
+    blocks = int(((w.seq_lens.astype(np.int64) + 15) // 16).sum()) * w.spec.Hkv
+    names = ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+             "SQ_INSTS_VMEM_RD", "SQ_INSTS_SALU", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+             "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_LDS_BANK_CONFLICT"]
+    cols = []
+    cmds = []
+    for label, kname, paths, cmd in runs:
+        vals = collections.defaultdict(list)
+        for path in paths:
+            for r in csv.DictReader(open(path)):
+                if kname in r["Kernel_Name"]:
+                    vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
+        cols.append((label, {k: sum(v) / len(v) for k, v in vals.items()}))
+        cmds += ["    " + c for c in cmd]
+    lines = ["# SQ counters of the decode kernel on %s" % workload, "",
+             "Counters per decode dispatch (mean over the dispatches of each run), from rocprofv3 runs of at most",
+             "8 SQ counters each (one MI355X, repository root as the working directory):", ""] + cmds + [
+             "", "Per block: divided by the workload's %d (16-token block, kv head) pairs. Wave-cycle counters "
+             "count in units of 4 cycles." % blocks, "",
+             "| counter | " + " | ".join("%s: per dispatch | per block" % c[0] for c in cols) + " |",
+             "|---|" + "---:|---:|" * len(cols)]
+    for n in names:
+        row = []
+        for _, v in cols:
+            x = v.get(n)
+            row += ["—", "—"] if x is None else ["%.0f" % x, "%.1f" % (x / blocks)]
+        lines.append("| %s | %s |" % (n, " | ".join(row)))
+    for label, v in cols:
+        if v.get("SQ_WAVE_CYCLES") and v.get("SQ_WAIT_ANY") is not None:
+            lines.append("")
+            lines.append("%s: waiting %.0f%% of wave time (SQ_WAIT_ANY / SQ_WAVE_CYCLES), VALU active %.0f%%, "
+                         "MFMA busy cycles per block %.0f." % (
+                             label, 100 * v["SQ_WAIT_ANY"] / v["SQ_WAVE_CYCLES"],
+                             100 * v.get("SQ_ACTIVE_INST_VALU", 0) / v["SQ_WAVE_CYCLES"],
+                             v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / blocks))
     lines.append("")
     return "\n".join(lines)
 

@@ -255,9 +255,14 @@ int32_t pa_device_cu_count(void);
 
 /* Name of the decode kernel pa_decode launches for these arguments:
  * "decode_wave_kernel" (vector ALU, one query token, small groups),
- * "decode_mfma_kernel" (matrix cores: Tq > 1, groups of 16+ query heads, int8
- * and FP8 caches from groups of 6) or "decode_valu_kernel" (fp32 caches); ""
- * for invalid arguments. A static string; nothing is launched. */
+ * "decode_stream_kernel" (matrix cores, int8 and FP8 caches whose G * Tq rows
+ * of a kv head fit one 16-row tile, from groups of 6 at one query token;
+ * each wave streams its own blocks; partitions of at most 4096 tokens, a
+ * larger given partition_size takes the next kernel), "decode_mfma_kernel"
+ * (matrix cores: Tq > 1, groups of 16+ query heads, int8 and FP8 caches with
+ * more rows) or "decode_valu_kernel" (fp32 caches); "" for invalid arguments.
+ * The name is the one for the heuristic's partition size. A static string;
+ * nothing is launched. */
 const char* pa_decode_kernel_name(int32_t Tq, int32_t Hq, int32_t Hkv, pa_dtype kv_dtype);
 
 /*

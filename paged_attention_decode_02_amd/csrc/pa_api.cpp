@@ -118,6 +118,31 @@ bool use_mfma(int32_t Tq, int32_t Hq, int32_t Hkv, pa_dtype kv_dtype) {
     return Tq > 1 || G >= 16 || ((kv_dtype == PA_I8 || kv_dtype == PA_FP8) && G >= 6);
 }
 
+// The streaming matrix-core kernel (each wave runs its own blocks, keys and
+// values copied straight into LDS) takes the quantised caches when all rows
+// of a kv head fit one 16-row tile; its partitions hold at most
+// kStreamMaxPartition tokens (larger given sizes use the tiled kernel).
+bool stream_kernel(int32_t Tq, int32_t Hq, int32_t Hkv, pa_dtype kv_dtype) {
+    return use_mfma(Tq, Hq, Hkv, kv_dtype) && (kv_dtype == PA_I8 || kv_dtype == PA_FP8) &&
+           (int64_t)(Hq / Hkv) * Tq <= 16;
+}
+
+// kv heads per workgroup of the streaming kernel, one wave each when 4: the
+// workgroup then reads whole token rows of every block (measured at 250K
+// int8 tokens: 91.3 -> 84.9 us against one head per workgroup, the heads'
+// 256-byte slices of each 1 KB row read by four different workgroups).
+// Per-head block tables (sparse decode) take one head per workgroup.
+int stream_hpg(int32_t Hkv, bool head_tables) {
+    if (head_tables) return 1;
+    return Hkv % 4 == 0 ? 4 : Hkv % 2 == 0 ? 2 : 1;
+}
+
+// Longest partition the streaming kernel takes (its per-wave table window
+// of 256 blocks, the waves of a head sharing a partition's blocks).
+int32_t stream_max_partition(pa_dtype kv_dtype, int32_t D, int hpg) {
+    return pa::kStreamMaxPartition * (pa::stream_waves((int)kv_dtype, D) / hpg);
+}
+
 // Row tiles per workgroup and row chunks of the matrix-core kernel: at most
 // four tiles (one per wave) per chunk, the tiles spread evenly over the
 // chunks (96 rows: two chunks of three tiles, not four and two).
@@ -178,6 +203,15 @@ int32_t split_len(int64_t len, int64_t per_partition, int wgs, int64_t gran, int
 int32_t partition_for(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
                       int32_t max_seq_len, int cus) {
     if (max_seq_len <= kBlock) return kBlock;
+    if (stream_kernel(Tq, Hq, Hkv, kv_dtype)) {
+        // one workgroup per CU (its LDS stages fill the CU), each partition at
+        // least 4 blocks per wave
+        const int hpg = stream_hpg(Hkv, false), wph = pa::stream_waves((int)kv_dtype, D) / hpg;
+        int32_t P = split_len(max_seq_len, (int64_t)B * (Hkv / hpg), 1, (int64_t)kBlock * wph,
+                              (int64_t)4 * kBlock * wph, cus);
+        const int32_t cap = stream_max_partition(kv_dtype, D, hpg);
+        return P > cap ? cap : P;
+    }
     int GT = 0, nchunk, wph = waves_per_wg(kv_dtype);  // waves per kv head
     int64_t per_partition;  // workgroups per partition index
     const bool mfma = use_mfma(Tq, Hq, Hkv, kv_dtype);
@@ -311,6 +345,13 @@ hipError_t dispatch(pa::DecodeParams p, pa_dtype kv_dtype, int32_t D, hipStream_
         head_chunks(p.G, &GT, &nchunk);
     p.nchunk = nchunk;
     p.hpg = (mfma || kv_dtype == PA_F32) ? 1 : heads_per_wg(kv_dtype, D, GT, p.Hkv);
+    if (!p.stacked && stream_kernel(p.Tq, p.Hq, p.Hkv, kv_dtype)) {
+        const int hpg = stream_hpg(p.Hkv, p.head_tables != 0);
+        if (p.P <= stream_max_partition(kv_dtype, D, hpg)) {
+            p.hpg = hpg;
+            return pa::launch_decode_stream((int)kv_dtype, D, p, stream);
+        }
+    }
     return kv_dtype == PA_F32 ? pa::launch_decode_valu((int)kv_dtype, D, GT, p, stream)
            : mfma             ? pa::launch_decode_mfma((int)kv_dtype, D, GT, p, stream)
                               : pa::launch_decode_wave((int)kv_dtype, D, GT, p, stream);
@@ -447,6 +488,7 @@ int32_t pa_device_cu_count(void) { return device_cus(); }
 const char* pa_decode_kernel_name(int32_t Tq, int32_t Hq, int32_t Hkv, pa_dtype kv_dtype) {
     if (Tq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || !kv_supported(kv_dtype)) return "";
     if (kv_dtype == PA_F32) return "decode_valu_kernel";
+    if (stream_kernel(Tq, Hq, Hkv, kv_dtype)) return "decode_stream_kernel";
     return use_mfma(Tq, Hq, Hkv, kv_dtype) ? "decode_mfma_kernel" : "decode_wave_kernel";
 }
 

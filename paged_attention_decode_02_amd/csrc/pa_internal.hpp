@@ -39,6 +39,10 @@ struct DecodeParams {
     // that attends to keys 0 .. prefix_len - 1 of the block list block_table
     int stacked;
     int prefix_len;
+    // Per-head block tables: row b * Hkv + g of block_table and seq_lens
+    // belongs to kv head g of sequence b (the sparse decode's compacted
+    // tables); one kv head per workgroup.
+    int head_tables;
 };
 
 struct ReduceParams {
@@ -88,6 +92,21 @@ hipError_t launch_decode_valu(int kv_type, int D, int GT, const DecodeParams& p,
 hipError_t launch_decode_wave(int kv_type, int D, int GT, const DecodeParams& p, hipStream_t stream);
 // NT: 16-row tiles per workgroup (1..4); p.nchunk = row chunks of 16*NT rows
 hipError_t launch_decode_mfma(int kv_type, int D, int NT, const DecodeParams& p, hipStream_t stream);
+// one tile of G * Tq <= 16 rows on the matrix cores, each wave streaming its
+// own blocks; p.hpg kv heads per workgroup (1, 2 or 4) of stream_waves waves
+// (a head's waves share its blocks); partitions of at most
+// kStreamMaxPartition * (waves per head) tokens.
+// Waves per workgroup and LDS stages per wave (the block being computed and
+// those in flight), one workgroup per CU, measured at 250K tokens: int8, four
+// waves (one per SIMD) with three stages each (85.6 us; eight waves with two
+// stages: 92.1); FP8, whose key widening is heavier, eight waves with two
+// stages (91.0 us; four waves with three: 104.9), the second wave on a SIMD
+// hiding the first's latencies. bf16 with D = 256 (16 KB per stage) fits
+// four waves with two stages.
+constexpr int stream_waves(int kv_type, int D) { return kv_type == 3 ? 8 : 4; }
+constexpr int stream_stages(int kv_type, int D) { return kv_type == 2 ? 3 : 2; }
+constexpr int kStreamMaxPartition = 4096;
+hipError_t launch_decode_stream(int kv_type, int D, const DecodeParams& p, hipStream_t stream);
 hipError_t launch_splitk_reduce(const ReduceParams& p, hipStream_t stream);
 hipError_t launch_cache_write(int cache_type, const CacheWriteParams& p, hipStream_t stream);
 hipError_t launch_decode_check(const DecodeCheckParams& p, hipStream_t stream);

@@ -88,12 +88,13 @@ def test_workspace_size_and_partition_choice(lib):
     need = lib.pa_decode_workspace_bytes(4, 1, 24, 4, 256, 1, 65536, 2048)
     rows = 4 * 24
     assert need == rows * 32 * 256 * 4 + rows * 32 * 4
-    # int8 caches with G = 6 run on the matrix cores: two workgroups per CU,
-    # one per (kv head, partition): 127 partitions x 4 kv heads
-    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 2, 250000) == 1984
-    # so do fp8 caches; nvfp4 caches with G = 6 stay on the vector ALU: two
+    # int8 caches with G = 6 run on the streaming matrix-core kernel: one
+    # workgroup per CU taking all 4 kv heads (one wave each): 253 partitions
+    # of 992 tokens
+    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 2, 250000) == 992
+    # so do fp8 caches (two waves per head); nvfp4 caches with G = 6 stay on the vector ALU: two
     # workgroups per CU, each taking two kv heads: 253 partitions x 2
-    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 3, 250000) == 1984
+    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 3, 250000) == 992
     assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 4, 250000) == 992
     # int8 with G = 4 stays on the vector ALU
     assert lib.pa_choose_partition_size(1, 1, 16, 4, 256, 2, 250000) == 992
@@ -110,8 +111,10 @@ def test_workspace_size_and_partition_choice(lib):
     assert lib.pa_decode_workspace_bytes(1, 1, 24, 4, 256, 1, 48, 0) == 0
     # (vector ALU, two waves per kv head: at least 4 blocks each)
     assert lib.pa_choose_partition_size(1, 1, 16, 4, 256, 2, 200) == 128
-    # (matrix cores: one partition covers 200 tokens)
-    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 2, 200) == 208
+    # (streaming kernel: at least 4 blocks per wave; int8 one wave per head,
+    # FP8 two)
+    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 2, 200) == 64
+    assert lib.pa_choose_partition_size(1, 1, 24, 4, 256, 3, 200) == 128
     # fp32 caches (one-wave workgroups) split even short contexts into blocks
     assert lib.pa_choose_partition_size(1, 1, 4, 1, 64, 0, 256) == 16
     assert lib.pa_decode_workspace_bytes(1, 1, 4, 1, 64, 0, 256, 0) == 4 * 16 * 64 * 4 + 256
@@ -263,16 +266,24 @@ def test_heuristic_follows_the_device_compute_units(lib):
     assert lib.pa_choose_partition_size_for_cus(4, 1, 24, 4, 256, 1, 65536, 128) == 2048
     assert lib.pa_choose_partition_size_for_cus(4, 1, 24, 4, 256, 1, 65536, 304) == 864
     assert lib.pa_choose_partition_size_for_cus(4, 1, 24, 4, 256, 1, 65536, 32) == 8192
-    # int8 250K on the matrix cores (two workgroups per CU, 4 kv heads): 64
-    # CUs hold 128 workgroups, 32 partitions of ceil(250000 / 32) tokens
-    # rounded up to whole blocks of the 4 waves (64 tokens)
-    assert lib.pa_choose_partition_size_for_cus(1, 1, 24, 4, 256, 2, 250000, 64) == 7872
+    # int8 250K on the streaming kernel (one workgroup of all 4 kv heads per
+    # CU, one wave per head): 64 CUs take 64 partitions of ceil(250000 / 64)
+    # tokens rounded up to whole blocks; 16 CUs would want 15632, above the
+    # 4096-token cap (256 blocks per wave); FP8 (two waves per head) rounds to
+    # 32 tokens and is capped at 8192
+    assert lib.pa_choose_partition_size_for_cus(1, 1, 24, 4, 256, 2, 250000, 64) == 3920
+    assert lib.pa_choose_partition_size_for_cus(1, 1, 24, 4, 256, 2, 250000, 16) == 4096
+    assert lib.pa_choose_partition_size_for_cus(1, 1, 24, 4, 256, 3, 250000, 64) == 3936
+    assert lib.pa_choose_partition_size_for_cus(1, 1, 24, 4, 256, 3, 250000, 16) == 8192
     assert lib.pa_choose_partition_size_for_cus(4, 1, 24, 4, 256, 1, 65536, 0) == -2
 
 
 def test_kernel_name_query(lib):
     assert lib.pa_decode_kernel_name(1, 24, 4, 1) == b"decode_wave_kernel"   # bf16, G = 6
-    assert lib.pa_decode_kernel_name(1, 24, 4, 2) == b"decode_mfma_kernel"   # int8, G = 6
+    assert lib.pa_decode_kernel_name(1, 24, 4, 2) == b"decode_stream_kernel"  # int8, G = 6: one row tile
+    assert lib.pa_decode_kernel_name(1, 24, 4, 3) == b"decode_stream_kernel"  # fp8, G = 6
+    assert lib.pa_decode_kernel_name(2, 16, 2, 2) == b"decode_stream_kernel"  # int8, 2 x 8 rows
+    assert lib.pa_decode_kernel_name(8, 24, 4, 2) == b"decode_mfma_kernel"    # int8, 48 rows
     assert lib.pa_decode_kernel_name(1, 16, 4, 2) == b"decode_wave_kernel"   # int8, G = 4
     assert lib.pa_decode_kernel_name(8, 24, 4, 1) == b"decode_mfma_kernel"   # Tq > 1
     assert lib.pa_decode_kernel_name(1, 64, 4, 1) == b"decode_mfma_kernel"   # G = 16

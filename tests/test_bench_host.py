@@ -53,7 +53,8 @@ def test_bench_names_the_kernel_the_library_launches():
         assert kname == pa.decode_kernel_name(spec.Tq, spec.Hq, spec.Hkv, bench_dtype(spec.cache_dtype)), name
         assert srcs[0] == kname.replace("_kernel", ".hip"), (kname, srcs)
     assert bench.decode_kernel(SPECS["long64k_bf16"])[0] == "decode_wave_kernel"
-    assert bench.decode_kernel(SPECS["int8_250k"])[0] == "decode_mfma_kernel"
+    assert bench.decode_kernel(SPECS["int8_250k"])[0] == "decode_stream_kernel"
+    assert bench.decode_kernel(SPECS["verify_i8"])[0] == "decode_mfma_kernel"
     assert bench.decode_kernel(SPECS["tiny_f32"])[0] == "decode_valu_kernel"
 
 
