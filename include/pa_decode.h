@@ -294,6 +294,77 @@ int pa_cache_write_check(const int64_t* slot_mapping, int64_t num_tokens, int64_
                          int32_t* status, void* stream);
 
 /*
+ * Sparse block-selection decode (vllm-sm70 page: "Changes relative to
+ * 1Cat-vLLM", item 8, per-block sparse-decode mean keys refreshed for every
+ * request of a decode batch; "Known limitations", a selection over at most
+ * 4096 key blocks, a 262,144-token table at 64-token blocks). The pages give
+ * no selection rule; the one implemented:
+ *  - a sequence's positions form sparse blocks of sparse_block tokens (a
+ *    multiple of 16, at most 4096; 64 on the page): block j = positions
+ *    sparse_block * j .. sparse_block * (j + 1) - 1 below the length; at most
+ *    4096 blocks per sequence (PA_ERR_UNSUPPORTED beyond);
+ *  - a block's mean key per kv head is the plain mean of its keys below the
+ *    length (quantised caches: dequantised values), in fp32;
+ *  - the blocks holding a query token (positions L - Tq .. L - 1) are always
+ *    selected; every other block j scores the largest, over the Tq * G query
+ *    rows of the kv head, of softmax_scale * q . mean_key[j], and the
+ *    top_blocks - (kept blocks) best are selected, ties to the lower index;
+ *  - each query row attends with the exact softmax to the keys of its kv
+ *    head's selected blocks that the plain causal rule lets it see.
+ * With top_blocks >= the block count the result is pa_decode's.
+ */
+
+/*
+ * pa_sparse_mean_keys — refresh the mean keys of the sparse blocks that hold
+ * each sequence's newest num_new tokens (positions seq_lens[b] - num_new ..
+ * seq_lens[b] - 1; num_new >= max_seq_len rebuilds every block): call after
+ * pa_cache_write of a decode step with num_new = Tq for every request of the
+ * batch. mean_k: [B, max_sparse_blocks, Hkv, D] fp32, caller-owned, row b
+ * belonging to the sequence in row b of block_table; entries of blocks at or
+ * past a sequence's ceil(seq_lens[b] / sparse_block) are not written.
+ * Requires max_sparse_blocks >= ceil(max_seq_len / sparse_block). Sums run in
+ * fp32 in position order (deterministic).
+ */
+int pa_sparse_mean_keys(const void* k_cache, pa_dtype kv_dtype, const float* k_scale, int64_t num_blocks,
+                        int32_t block_size, int32_t Hkv, int32_t D, const int32_t* block_table,
+                        int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
+                        int32_t sparse_block, int32_t num_new, float* mean_k, int32_t max_sparse_blocks,
+                        void* stream);
+
+/*
+ * pa_decode_sparse — the decode over each (sequence, kv head)'s selected
+ * sparse blocks. Arguments as for pa_decode (caches bf16, int8, fp8 or
+ * nvfp4; fp32 caches return PA_ERR_UNSUPPORTED), plus:
+ *   mean_k, max_sparse_blocks  the mean keys (pa_sparse_mean_keys), current
+ *                  for every block below each sequence's length
+ *   sparse_block, top_blocks   the selection (top_blocks >= 1)
+ *   partition_size split-K partition over the selected keys (0: heuristic)
+ *   selected       optional (may be NULL) [B, Hkv, S] int32 output, S =
+ *                  min(ceil(max_seq_len / sparse_block), max(top_blocks, 2)):
+ *                  the selected blocks in increasing order, -1 after the last
+ *   workspace      >= pa_decode_sparse_workspace_bytes with the same
+ *                  arguments, 16-byte aligned: scores, the compacted block
+ *                  tables (the selected blocks' cache blocks in order, one row
+ *                  per (sequence, kv head)) and the split-K partials.
+ * Always writes out (and lse if non-NULL). Runs a score kernel, a selection
+ * kernel, the decode kernel pa_decode would choose (one kv head per
+ * workgroup) over the compacted tables, and the LSE reduce.
+ */
+int pa_decode_sparse(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D,
+                     const void* k_cache, const void* v_cache, pa_dtype kv_dtype, const float* k_scale,
+                     const float* v_scale, int64_t num_blocks, int32_t block_size, const int32_t* block_table,
+                     int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+                     const float* mean_k, int32_t max_sparse_blocks, int32_t sparse_block, int32_t top_blocks,
+                     int32_t partition_size, void* out, pa_dtype out_dtype, float* lse, int32_t* selected,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pa_decode_sparse needs for these arguments (0 for
+ * invalid arguments). */
+size_t pa_decode_sparse_workspace_bytes(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
+                                        int32_t max_seq_len, int32_t sparse_block, int32_t top_blocks,
+                                        int32_t partition_size);
+
+/*
  * pa_decode_noalloc — pa_decode followed by pa_decode_splitk_reduce, for
  * callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): the split-K partials

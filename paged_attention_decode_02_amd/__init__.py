@@ -27,6 +27,7 @@ __all__ = [
     "choose_partition_size", "choose_partition_size_for_cus", "device_cu_count", "decode_kernel_name",
     "library_path", "load", "DTYPE_CODE", "decode_shared_prefix", "shared_prefix_workspace_bytes",
     "validate_decode_args", "validate_cache_write_args", "decode_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "sparse_mean_keys", "decode_sparse", "sparse_workspace_bytes", "sparse_max_selected",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,7 +45,8 @@ EXPORTS = (
     "pa_cache_write", "pa_decode", "pa_decode_splitk_reduce", "pa_decode_workspace_bytes",
     "pa_choose_partition_size", "pa_decode_check", "pa_cache_write_check", "pa_last_error",
     "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes", "pa_choose_partition_size_for_cus",
-    "pa_device_cu_count", "pa_decode_kernel_name", "pa_decode_noalloc",
+    "pa_device_cu_count", "pa_decode_kernel_name", "pa_decode_noalloc", "pa_sparse_mean_keys", "pa_decode_sparse",
+    "pa_decode_sparse_workspace_bytes",
 )
 
 # size of the library-owned scratch of pa_decode_noalloc (PA_NOALLOC_SCRATCH_BYTES)
@@ -102,6 +104,13 @@ def load():
         lib.pa_decode_noalloc.argtypes = [P, I32, I32, I32, I32, I32, I32, P, P, I32, P, P, I64, I32, P, I32, P, I32,
                                           F, I32, P, I32, P, P]
         lib.pa_decode_noalloc.restype = ctypes.c_int
+        lib.pa_sparse_mean_keys.argtypes = [P, I32, P, I64, I32, I32, I32, P, I32, P, I32, I32, I32, I32, P, I32, P]
+        lib.pa_sparse_mean_keys.restype = ctypes.c_int
+        lib.pa_decode_sparse.argtypes = [P, I32, I32, I32, I32, I32, I32, P, P, I32, P, P, I64, I32, P, I32, P, I32, F,
+                                         P, I32, I32, I32, I32, P, I32, P, P, P, SZ, P]
+        lib.pa_decode_sparse.restype = ctypes.c_int
+        lib.pa_decode_sparse_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32, I32, I32]
+        lib.pa_decode_sparse_workspace_bytes.restype = SZ
         lib.pa_last_error.argtypes = []
         lib.pa_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -391,6 +400,74 @@ def decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int,
                                   _ptr(k_scale), _ptr(v_scale), nb, bs, _ptr(block_table), block_table.shape[1],
                                   _ptr(seq_lens), int(max_seq_len), float(softmax_scale), int(partition_size),
                                   _ptr(out), _code(out), _ptr(lse), _stream(stream, q)))
+
+
+def sparse_max_selected(max_seq_len: int, sparse_block: int, top_blocks: int) -> int:
+    """S: selected sparse blocks per (sequence, kv head) at most."""
+    nsb = (int(max_seq_len) + sparse_block - 1) // sparse_block
+    return min(nsb, max(top_blocks, 2))
+
+
+def sparse_mean_keys(k_cache, block_table, seq_lens, max_seq_len: int, sparse_block: int, num_new: int,
+                     mean_k: torch.Tensor, k_scale=None, stream=None) -> None:
+    """Refresh the mean keys [B, max_sparse_blocks, Hkv, D] (fp32) of the
+    sparse blocks holding each sequence's newest num_new tokens."""
+    for t, n in ((k_cache, "k_cache"), (block_table, "block_table"), (seq_lens, "seq_lens"), (mean_k, "mean_k"),
+                 (k_scale, "k_scale")):
+        _dev(t, n)
+    nb, bs, Hkv, row = k_cache.shape
+    D = row * 16 // 9 if k_cache.dtype == torch.float4_e2m1fn_x2 else row
+    B = block_table.shape[0]
+    if mean_k.dtype != torch.float32 or mean_k.dim() != 4 or mean_k.shape[0] != B or tuple(mean_k.shape[2:]) != (
+            Hkv, D):
+        raise ValueError("mean_k must be float32 [B=%d, max_sparse_blocks, %d, %d]" % (B, Hkv, D))
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or seq_lens.numel() != B:
+        raise ValueError("block_table and seq_lens must be int32 with B rows")
+    _check(_L().pa_sparse_mean_keys(_ptr(k_cache), _code(k_cache), _ptr(k_scale), nb, bs, Hkv, D, _ptr(block_table),
+                                    block_table.shape[1], _ptr(seq_lens), B, int(max_seq_len), int(sparse_block),
+                                    int(num_new), _ptr(mean_k), mean_k.shape[1], _stream(stream, k_cache)))
+
+
+def sparse_workspace_bytes(B: int, Tq: int, Hq: int, Hkv: int, D: int, kv_dtype: torch.dtype, max_seq_len: int,
+                           sparse_block: int, top_blocks: int, partition_size: int = 0) -> int:
+    return int(load().pa_decode_sparse_workspace_bytes(B, Tq, Hq, Hkv, D, DTYPE_CODE[kv_dtype], max_seq_len,
+                                                       sparse_block, top_blocks, partition_size))
+
+
+def decode_sparse(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, softmax_scale: float,
+                  mean_k: torch.Tensor, sparse_block: int, top_blocks: int, k_scale=None, v_scale=None,
+                  partition_size: int = 0, out=None, lse=None, selected=None, workspace=None,
+                  out_dtype: torch.dtype = torch.float32, stream=None):
+    """Sparse block-selection decode; returns (out, lse). selected, when given,
+    receives [B, Hkv, S] int32 block ids (increasing, -1 after the last)."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_table, "block_table"),
+                 (seq_lens, "seq_lens"), (mean_k, "mean_k"), (out, "out"), (lse, "lse"), (k_scale, "k_scale"),
+                 (v_scale, "v_scale"), (selected, "selected"), (workspace, "workspace")):
+        _dev(t, n)
+    validate_decode_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, out, lse, k_scale, v_scale)
+    B, Tq, Hq, D = q.shape
+    nb, bs, Hkv, _ = k_cache.shape
+    if mean_k.dtype != torch.float32 or mean_k.dim() != 4 or (mean_k.shape[0], mean_k.shape[2], mean_k.shape[3]) != (
+            B, Hkv, D):
+        raise ValueError("mean_k must be float32 [B, max_sparse_blocks, Hkv, D]")
+    S = sparse_max_selected(max_seq_len, sparse_block, top_blocks)
+    if selected is not None and (selected.dtype != torch.int32 or tuple(selected.shape) != (B, Hkv, S)):
+        raise ValueError("selected must be int32 [%d, %d, %d]" % (B, Hkv, S))
+    if out is None:
+        out = torch.empty((B, Tq, Hq, D), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=q.device)
+    nbytes = sparse_workspace_bytes(B, Tq, Hq, Hkv, D, k_cache.dtype, max_seq_len, sparse_block, top_blocks,
+                                    partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_L().pa_decode_sparse(
+        _ptr(q), _code(q), B, Tq, Hq, Hkv, D, _ptr(k_cache), _ptr(v_cache), _code(k_cache), _ptr(k_scale),
+        _ptr(v_scale), nb, bs, _ptr(block_table), block_table.shape[1], _ptr(seq_lens), int(max_seq_len),
+        float(softmax_scale), _ptr(mean_k), mean_k.shape[1], int(sparse_block), int(top_blocks), int(partition_size),
+        _ptr(out), _code(out), _ptr(lse), _ptr(selected), _ptr(workspace), ws_bytes, _stream(stream, q)))
+    return out, lse
 
 
 def shared_prefix_workspace_bytes(B: int, Tq: int, Hq: int, Hkv: int, D: int, kv_dtype: torch.dtype,

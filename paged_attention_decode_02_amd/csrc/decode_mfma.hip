@@ -170,7 +170,9 @@ __global__ __launch_bounds__(64 * kW, (mfma_min_waves<KVT, D, NT, QS>())) void d
     const int rlast = min(R, row0 + 16 * NT) - 1;  // one sequence: largest t is in the last row
     // keys of the row set: a sequence's own from kv_begin on (causal end
     // L - Tq + t), or the shared list's first prefix_len, visible to all rows
-    const int L = p.stacked ? p.prefix_len : p.seq_lens[b] - p.kv_begin;
+    // per-head tables: row b Hkv + g of the table and lengths
+    const int hrow = p.head_tables ? b * p.Hkv + g : b;
+    const int L = p.stacked ? p.prefix_len : p.seq_lens[hrow] - p.kv_begin;
     const int n_chunk = p.stacked ? L : L - Tq + rlast / G + 1;
     const int start = part * p.P;
     const int64_t wpart = p.part_base + part;  // workspace partition
@@ -280,7 +282,8 @@ __global__ __launch_bounds__(64 * kW, (mfma_min_waves<KVT, D, NT, QS>())) void d
 #pragma unroll
         for (int nd = 0; nd < NDT; ++nd) o[t][nd] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int32_t* table = p.stacked ? p.block_table : p.block_table + (int64_t)b * p.max_blocks + p.kv_begin / kBlockSize;
+    const int32_t* table =
+        p.stacked ? p.block_table : p.block_table + (int64_t)hrow * p.max_blocks + p.kv_begin / kBlockSize;
     const int64_t tok_stride = (int64_t)p.Hkv * RBQ;
     const int64_t blk_bytes = kBlockSize * (int64_t)p.Hkv * kv_row_bytes<KVT>(D);  // nvfp4: + scale planes
     const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (int64_t)g * RBQ;

@@ -217,7 +217,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
     const int b = wg / p.Tq;
 
     // keys visible to query token t, counted from the sequence's token kv_begin
-    const int n = p.seq_lens[b] - p.kv_begin - p.Tq + t + 1;
+    // (per-head tables: row b Hkv + g of the table and lengths; one kv head
+    // per workgroup then)
+    const int hrow = p.head_tables ? b * p.Hkv + g : b;
+    const int n = p.seq_lens[hrow] - p.kv_begin - p.Tq + t + 1;
     const int start = part * p.P;
     const int64_t wpart = p.part_base + part;  // workspace partition
     const int hbase = g * p.G + chunk * GT;
@@ -368,7 +371,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_wave_kernel(DecodeParams p
         sloc[j] = 0.0f;
     }
 
-    const int32_t* table = p.block_table + (int64_t)b * p.max_blocks + p.kv_begin / kBlockSize;
+    const int32_t* table = p.block_table + (int64_t)hrow * p.max_blocks + p.kv_begin / kBlockSize;
     // KV addressing: a buffer resource per block (scalar) plus per-lane
     // offsets that do not change from block to block; the host keeps a
     // block's bytes below 2^31

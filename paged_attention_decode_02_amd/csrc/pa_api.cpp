@@ -200,13 +200,15 @@ int32_t split_len(int64_t len, int64_t per_partition, int wgs, int64_t gran, int
     return (int32_t)P;
 }
 
+// head_tables: every (sequence, kv head) has a block table row of its own
+// (the sparse decode's compacted tables), so a workgroup takes one kv head.
 int32_t partition_for(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
-                      int32_t max_seq_len, int cus) {
+                      int32_t max_seq_len, int cus, bool head_tables = false) {
     if (max_seq_len <= kBlock) return kBlock;
     if (stream_kernel(Tq, Hq, Hkv, kv_dtype)) {
         // one workgroup per CU (its LDS stages fill the CU), each partition at
         // least 4 blocks per wave
-        const int hpg = stream_hpg(Hkv, false), wph = pa::stream_waves((int)kv_dtype, D) / hpg;
+        const int hpg = stream_hpg(Hkv, head_tables), wph = pa::stream_waves((int)kv_dtype, D) / hpg;
         int32_t P = split_len(max_seq_len, (int64_t)B * (Hkv / hpg), 1, (int64_t)kBlock * wph,
                               (int64_t)4 * kBlock * wph, cus);
         const int32_t cap = stream_max_partition(kv_dtype, D, hpg);
@@ -221,7 +223,7 @@ int32_t partition_for(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D,
         per_partition = (int64_t)B * Hkv * nchunk;
     } else {
         head_chunks(Hq / Hkv, &GT, &nchunk);
-        const int hpg = kv_dtype == PA_F32 ? 1 : heads_per_wg(kv_dtype, D, GT, Hkv);
+        const int hpg = (kv_dtype == PA_F32 || head_tables) ? 1 : heads_per_wg(kv_dtype, D, GT, Hkv);
         per_partition = (int64_t)B * Tq * (Hkv / hpg) * nchunk;
         if (kv_dtype != PA_F32) wph = 4 / hpg;
     }
@@ -344,7 +346,7 @@ hipError_t dispatch(pa::DecodeParams p, pa_dtype kv_dtype, int32_t D, hipStream_
     else
         head_chunks(p.G, &GT, &nchunk);
     p.nchunk = nchunk;
-    p.hpg = (mfma || kv_dtype == PA_F32) ? 1 : heads_per_wg(kv_dtype, D, GT, p.Hkv);
+    p.hpg = (mfma || kv_dtype == PA_F32 || p.head_tables) ? 1 : heads_per_wg(kv_dtype, D, GT, p.Hkv);
     if (!p.stacked && stream_kernel(p.Tq, p.Hq, p.Hkv, kv_dtype)) {
         const int hpg = stream_hpg(p.Hkv, p.head_tables != 0);
         if (p.P <= stream_max_partition(kv_dtype, D, hpg)) {
@@ -389,6 +391,47 @@ int plan_shared_prefix(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D
     pl->np_total = (int32_t)total;
     const size_t rows = (size_t)B * Tq * Hq;
     pl->ws_bytes = pl->np_total > 1 ? align256(rows * total * D * sizeof(float)) + align256(rows * total * sizeof(float)) : 0;
+    return PA_OK;
+}
+
+// Sizes of a sparse decode: blocks per sequence, selected blocks, compacted
+// table width, partitioning and the workspace sections (scores, compacted
+// tables, compacted lengths, split-K partials), each 256-byte aligned.
+struct SparsePlan {
+    int32_t nsb_max, max_sel, ctab_width, max_len, P, NP;
+    size_t off_ctab, off_clen, off_part, ws_bytes;
+};
+
+int plan_sparse(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype, int32_t max_seq_len,
+                int32_t sparse_block, int32_t top_blocks, int32_t partition_size, SparsePlan* pl) {
+    int rc = check_dims(B, Tq, Hq, Hkv, D);
+    if (rc) return rc;
+    if (!kv_supported(kv_dtype)) return fail(PA_ERR_DTYPE, "kv dtype %d not supported", (int)kv_dtype);
+    if (kv_dtype == PA_F32) return fail(PA_ERR_UNSUPPORTED, "the sparse decode takes bf16, int8, fp8 or nvfp4 caches");
+    if (max_seq_len < 0) return fail(PA_ERR_SHAPE, "max_seq_len=%d must be >= 0", max_seq_len);
+    if (sparse_block < kBlock || sparse_block % kBlock || sparse_block > 4096)
+        return fail(PA_ERR_SHAPE, "sparse_block=%d must be a multiple of %d in [16, 4096]", sparse_block, kBlock);
+    if (top_blocks < 1) return fail(PA_ERR_SHAPE, "top_blocks=%d must be >= 1", top_blocks);
+    if (partition_size < 0 || partition_size % kBlock)
+        return fail(PA_ERR_SHAPE, "partition_size=%d must be 0 or a positive multiple of %d", partition_size, kBlock);
+    const int64_t nsb = ((int64_t)max_seq_len + sparse_block - 1) / sparse_block;
+    if (nsb > pa::kSparseMaxBlocks)
+        return fail(PA_ERR_UNSUPPORTED, "%lld sparse blocks of %d tokens exceed the selection's %d",
+                    (long long)nsb, sparse_block, pa::kSparseMaxBlocks);
+    pl->nsb_max = (int32_t)nsb;
+    pl->max_sel = (int32_t)(nsb < (top_blocks > 2 ? top_blocks : 2) ? nsb : (top_blocks > 2 ? top_blocks : 2));
+    pl->ctab_width = pl->max_sel * (sparse_block / kBlock);
+    pl->max_len = pl->max_sel * sparse_block;
+    if ((int64_t)pl->max_len > 0x7FFFFFFF) return fail(PA_ERR_SHAPE, "selection too long");
+    pl->P = partition_size ? partition_size
+                           : partition_for(B, Tq, Hq, Hkv, D, kv_dtype, pl->max_len, device_cus(), true);
+    pl->NP = pl->max_len > 0 ? (pl->max_len + pl->P - 1) / pl->P : 1;
+    const size_t bg = (size_t)B * Hkv, rows = (size_t)B * Tq * Hq;
+    pl->off_ctab = align256(bg * (size_t)(pl->nsb_max > 0 ? pl->nsb_max : 1) * sizeof(float));
+    pl->off_clen = pl->off_ctab + align256(bg * (size_t)(pl->ctab_width > 0 ? pl->ctab_width : 1) * sizeof(int32_t));
+    pl->off_part = pl->off_clen + align256(bg * sizeof(int32_t));
+    pl->ws_bytes = pl->off_part;
+    if (pl->NP > 1) pl->ws_bytes += align256(rows * pl->NP * D * sizeof(float)) + align256(rows * pl->NP * sizeof(float));
     return PA_OK;
 }
 
@@ -692,6 +735,140 @@ int pa_decode_splitk_reduce(const void* workspace, int32_t num_partitions, int32
     p.lse = lse;
     hipError_t e = pa::launch_splitk_reduce(p, (hipStream_t)stream);
     if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "reduce launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int pa_sparse_mean_keys(const void* k_cache, pa_dtype kv_dtype, const float* k_scale, int64_t num_blocks,
+                        int32_t block_size, int32_t Hkv, int32_t D, const int32_t* block_table,
+                        int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t B, int32_t max_seq_len,
+                        int32_t sparse_block, int32_t num_new, float* mean_k, int32_t max_sparse_blocks,
+                        void* stream) {
+    if (!kv_supported(kv_dtype)) return fail(PA_ERR_DTYPE, "kv dtype %d not supported", (int)kv_dtype);
+    if (B < 0 || Hkv < 1 || num_blocks < 1 || max_seq_len < 0 || max_blocks_per_seq < 1)
+        return fail(PA_ERR_SHAPE, "B=%d, Hkv=%d, num_blocks=%lld, max_seq_len=%d, max_blocks_per_seq=%d out of range", B,
+                    Hkv, (long long)num_blocks, max_seq_len, max_blocks_per_seq);
+    if (block_size != kBlock) return fail(PA_ERR_UNSUPPORTED, "block_size=%d (only 16)", block_size);
+    if (!supported_d(D)) return fail(PA_ERR_UNSUPPORTED, "D=%d not in {64, 128, 256}", D);
+    if ((int64_t)max_blocks_per_seq * kBlock < max_seq_len)
+        return fail(PA_ERR_SHAPE, "block table too short: %d blocks for max_seq_len %d", max_blocks_per_seq, max_seq_len);
+    if (sparse_block < kBlock || sparse_block % kBlock || sparse_block > 4096)
+        return fail(PA_ERR_SHAPE, "sparse_block=%d must be a multiple of %d in [16, 4096]", sparse_block, kBlock);
+    if (num_new < 1) return fail(PA_ERR_SHAPE, "num_new=%d must be >= 1", num_new);
+    const int64_t nsb = ((int64_t)max_seq_len + sparse_block - 1) / sparse_block;
+    if (max_sparse_blocks < nsb)
+        return fail(PA_ERR_SHAPE, "max_sparse_blocks=%d below the %lld blocks of max_seq_len", max_sparse_blocks,
+                    (long long)nsb);
+    if (!k_cache || !block_table || !seq_lens || !mean_k)
+        return fail(PA_ERR_NULL, "k_cache, block_table, seq_lens and mean_k must be non-NULL");
+    if (quantised(kv_dtype) && !k_scale) return fail(PA_ERR_NULL, "int8/fp8/nvfp4 caches need k_scale");
+    if (B == 0 || nsb == 0) return ok();
+    // the blocks touched by the newest num_new tokens: at most ceil(num_new / SB) + 1
+    int64_t nref = ((int64_t)num_new + sparse_block - 1) / sparse_block + 1;
+    if (nref > nsb) nref = nsb;
+    pa::SparseParams p{};
+    p.B = B;
+    p.Hkv = Hkv;
+    p.D = D;
+    p.k_cache = k_cache;
+    p.k_scale = k_scale;
+    p.block_table = block_table;
+    p.max_blocks = max_blocks_per_seq;
+    p.seq_lens = seq_lens;
+    p.sparse_block = sparse_block;
+    p.num_new = num_new;
+    p.mean_k = mean_k;
+    p.max_sblocks = max_sparse_blocks;
+    hipError_t e = pa::launch_sparse_mean((int)kv_dtype, p, (int)nref, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "sparse mean-key launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t pa_decode_sparse_workspace_bytes(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
+                                        int32_t max_seq_len, int32_t sparse_block, int32_t top_blocks,
+                                        int32_t partition_size) {
+    SparsePlan pl;
+    if (plan_sparse(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len, sparse_block, top_blocks, partition_size, &pl)) return 0;
+    return pl.ws_bytes;
+}
+
+int pa_decode_sparse(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D,
+                     const void* k_cache, const void* v_cache, pa_dtype kv_dtype, const float* k_scale,
+                     const float* v_scale, int64_t num_blocks, int32_t block_size, const int32_t* block_table,
+                     int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+                     const float* mean_k, int32_t max_sparse_blocks, int32_t sparse_block, int32_t top_blocks,
+                     int32_t partition_size, void* out, pa_dtype out_dtype, float* lse, int32_t* selected,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_decode_args(q, q_dtype, B, Tq, Hq, Hkv, D, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                               num_blocks, block_size, block_table, max_blocks_per_seq, seq_lens, max_seq_len,
+                               out, out_dtype);
+    if (rc) return rc;
+    SparsePlan pl;
+    rc = plan_sparse(B, Tq, Hq, Hkv, D, kv_dtype, max_seq_len, sparse_block, top_blocks, partition_size, &pl);
+    if (rc) return rc;
+    if (!mean_k) return fail(PA_ERR_NULL, "mean_k must be non-NULL");
+    if (max_sparse_blocks < pl.nsb_max)
+        return fail(PA_ERR_SHAPE, "max_sparse_blocks=%d below the %d blocks of max_seq_len", max_sparse_blocks,
+                    pl.nsb_max);
+    if (!workspace || workspace_bytes < pl.ws_bytes)
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.ws_bytes,
+                    workspace ? workspace_bytes : 0);
+    if (!aligned16(workspace)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (B == 0) return ok();
+    char* ws = reinterpret_cast<char*>(workspace);
+    pa::SparseParams sp{};
+    sp.q = q;
+    sp.q_bf16 = q_dtype == PA_BF16;
+    sp.B = B;
+    sp.Tq = Tq;
+    sp.Hq = Hq;
+    sp.Hkv = Hkv;
+    sp.D = D;
+    sp.block_table = block_table;
+    sp.max_blocks = max_blocks_per_seq;
+    sp.seq_lens = seq_lens;
+    sp.softmax_scale = softmax_scale;
+    sp.sparse_block = sparse_block;
+    sp.top_blocks = top_blocks;
+    sp.mean_k = const_cast<float*>(mean_k);
+    sp.max_sblocks = max_sparse_blocks;
+    sp.scores = reinterpret_cast<float*>(ws);
+    sp.nsb_max = pl.nsb_max;
+    sp.max_sel = pl.max_sel;
+    sp.sel_out = selected;
+    sp.ctab = reinterpret_cast<int32_t*>(ws + pl.off_ctab);
+    sp.ctab_width = pl.ctab_width;
+    sp.clen = reinterpret_cast<int32_t*>(ws + pl.off_clen);
+    hipError_t e = pa::launch_sparse_select(sp, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "sparse selection launch failed: %s", hipGetErrorString(e));
+    // the decode over each (sequence, kv head)'s compacted table
+    pa::DecodeParams p = base_params(q, q_dtype, B, Tq, Hq, Hkv, k_cache, v_cache, k_scale, v_scale, sp.ctab,
+                                     pl.ctab_width, sp.clen, softmax_scale, out, out_dtype, lse);
+    p.head_tables = 1;
+    p.P = pl.P;
+    p.NP = pl.NP;
+    p.np_stride = pl.NP;
+    if (pl.NP > 1) set_workspace(p, ws + pl.off_part, (size_t)B * Tq * Hq, pl.NP, D);
+    e = dispatch(p, kv_dtype, D, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "sparse decode launch failed: %s", hipGetErrorString(e));
+    if (pl.NP > 1) {
+        pa::ReduceParams r{};
+        r.ws_o = p.ws_o;
+        r.ws_lse = p.ws_lse;
+        r.NP = pl.NP;
+        r.P = pl.P;
+        r.B = B;
+        r.Tq = Tq;
+        r.Hq = Hq;
+        r.D = D;
+        r.Hkv = Hkv;
+        r.head_lens = 1;
+        r.seq_lens = sp.clen;
+        r.out = out;
+        r.out_bf16 = out_dtype == PA_BF16;
+        r.lse = lse;
+        e = pa::launch_splitk_reduce(r, (hipStream_t)stream);
+        if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "reduce launch failed: %s", hipGetErrorString(e));
+    }
     return ok();
 }
 

@@ -51,10 +51,37 @@ struct ReduceParams {
     int NP, P, B, Tq, Hq, D;
     int cs;  // column splits: workgroups per row, each taking D / cs output elements
     int all_parts;  // every partition was written (empty ones with lse = -inf): merge all NP
+    int Hkv;        // with head_lens: seq_lens[b * Hkv + kv head] is the length of the row's kv head
+    int head_lens;
     const int32_t* seq_lens;
     void* out;
     int out_bf16;
     float* lse;
+};
+
+// Sparse block-selection decode: mean keys, scores, selection, compacted tables.
+struct SparseParams {
+    const void* q;
+    int q_bf16;
+    int B, Tq, Hq, Hkv, D;
+    const void* k_cache;
+    const float* k_scale;
+    const int32_t* block_table;
+    int max_blocks;
+    const int32_t* seq_lens;
+    float softmax_scale;
+    int sparse_block;  // tokens per sparse block (a multiple of 16)
+    int top_blocks;    // sparse blocks selected per (sequence, kv head), the kept ones included
+    int num_new;       // mean keys: refresh the blocks holding each sequence's last num_new tokens
+    float* mean_k;     // [B, max_sblocks, Hkv, D]
+    int max_sblocks;
+    float* scores;     // [B * Hkv, nsb_max] candidate scores
+    int nsb_max;       // sparse blocks of the longest sequence
+    int max_sel;       // selected blocks per (sequence, kv head) at most
+    int32_t* sel_out;  // optional [B, Hkv, max_sel] selected blocks, increasing, -1 after
+    int32_t* ctab;     // [B * Hkv, ctab_width] compacted block tables
+    int ctab_width;    // max_sel * sparse_block / 16
+    int32_t* clen;     // [B * Hkv] compacted lengths
 };
 
 struct CacheWriteParams {
@@ -111,6 +138,11 @@ hipError_t launch_splitk_reduce(const ReduceParams& p, hipStream_t stream);
 hipError_t launch_cache_write(int cache_type, const CacheWriteParams& p, hipStream_t stream);
 hipError_t launch_decode_check(const DecodeCheckParams& p, hipStream_t stream);
 hipError_t launch_slots_check(const SlotsCheckParams& p, hipStream_t stream);
+
+hipError_t launch_sparse_mean(int kv_type, const SparseParams& p, int nref, hipStream_t stream);
+// scores of the candidate blocks, then the selection and compacted tables
+hipError_t launch_sparse_select(const SparseParams& p, hipStream_t stream);
+constexpr int kSparseMaxBlocks = 4096;  // sparse blocks per sequence at most
 
 // Valid head-chunk widths of the VALU decode instances.
 bool decode_valu_has_gt(int GT);

@@ -60,6 +60,8 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_rows_kernel(ReducePara
     const int csi = blockIdx.x % p.cs;
     const int t = (int)((rowid / p.Hq) % p.Tq);
     const int b = (int)(rowid / ((int64_t)p.Hq * p.Tq));
+    // per-head lengths: entry b Hkv + kv head of the row's query head
+    const int hl = p.head_lens ? b * p.Hkv + (int)(rowid % p.Hq) / (p.Hq / p.Hkv) : b;
     const float* lse_row = p.ws_lse + rowid * p.NP;
     const float4* o_row = reinterpret_cast<const float4*>(p.ws_o + rowid * p.NP * p.D);
     const int DQ = p.D / 4;     // float4 columns of the row
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_rows_kernel(ReducePara
     }
     // partitions that hold keys of the row (all of them when every partition
     // was written, which the shared-prefix decode's two passes do)
-    const int n = p.seq_lens[b] - p.Tq + t + 1;
+    const int n = p.seq_lens[hl] - p.Tq + t + 1;
     const int np = p.all_parts ? p.NP : n > 0 ? min((n + p.P - 1) / p.P, p.NP) : 0;
 
     // the slices' preloaded partitions are 0 .. kPreRow * S - 1; the rest is read here
@@ -155,6 +157,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceParams p) {
     const int csi = (int)(wid % p.cs);
     const int t = (int)((rowid / p.Hq) % p.Tq);
     const int b = (int)(rowid / ((int64_t)p.Hq * p.Tq));
+    const int hl = p.head_lens ? b * p.Hkv + (int)(rowid % p.Hq) / (p.Hq / p.Hkv) : b;
     const int c = lane % CW, s = lane / CW;
     const int DQ = p.D / 4;       // float4 columns of the row
     const int q = csi * CW + c;   // this lane's column
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceParams p) {
     float lm = lane < p.NP ? lse_row[lane] : -INFINITY;  // the row's maximum, 64 partitions per load
     // partitions that hold keys of the row (all of them when every partition
     // was written, which the shared-prefix decode's two passes do)
-    const int n = p.seq_lens[b] - p.Tq + t + 1;
+    const int n = p.seq_lens[hl] - p.Tq + t + 1;
     const int np = p.all_parts ? p.NP : n > 0 ? min((n + p.P - 1) / p.P, p.NP) : 0;
 
     float mx = lane < np ? lm : -INFINITY;

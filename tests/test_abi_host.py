@@ -303,3 +303,74 @@ def test_noalloc_rejects_partials_beyond_its_scratch(lib):
     assert pa.NOALLOC_SCRATCH_BYTES == 32 << 20
     text = open(HEADER).read()
     assert "#define PA_NOALLOC_SCRATCH_BYTES (32u << 20)" in text
+
+
+def sparse_args(**over):
+    args = dict(q=A, q_dtype=1, B=1, Tq=1, Hq=24, Hkv=4, D=256, k_cache=A, v_cache=A, kv_dtype=2, k_scale=A,
+                v_scale=A, num_blocks=16000, block_size=16, block_table=A, max_blocks=15625, seq_lens=A,
+                max_seq_len=250000, scale=0.0625, mean_k=A, max_sblocks=3907, sparse_block=64, top_blocks=512,
+                partition_size=0, out=A, out_dtype=0, lse=None, selected=None, workspace=None, workspace_bytes=0,
+                stream=None)
+    args.update(over)
+    return list(args.values())
+
+
+@pytest.mark.parametrize("over, code", [
+    (dict(mean_k=None, workspace=A, workspace_bytes=1 << 30), -1),
+    (dict(kv_dtype=0, k_scale=None, v_scale=None), -4),          # fp32 caches
+    (dict(sparse_block=40), -2),                                  # not whole cache blocks
+    (dict(sparse_block=8192), -2),
+    (dict(top_blocks=0), -2),
+    (dict(max_sblocks=3906, workspace=A, workspace_bytes=1 << 30), -2),
+    (dict(sparse_block=16), -4),                                  # 15625 blocks > 4096
+    (dict(), -5),                                                 # no workspace
+    (dict(workspace=ctypes.c_void_p(0x1008), workspace_bytes=1 << 30), -7),
+])
+def test_sparse_decode_rejects_bad_arguments(lib, over, code):
+    rc = lib.pa_decode_sparse(*sparse_args(**over))
+    assert rc == code, lib.pa_last_error()
+    assert lib.pa_last_error()
+
+
+def test_sparse_workspace_plan(lib):
+    # int8 250K, 64-token sparse blocks, 512 selected: scores of 3907 blocks
+    # for 4 kv heads, compacted tables of 512 * 4 cache blocks, lengths, and
+    # the partials over at most 32768 selected keys
+    n = lib.pa_decode_sparse_workspace_bytes(1, 1, 24, 4, 256, 2, 250000, 64, 512, 0)
+    P = lib.pa_choose_partition_size(1, 1, 24, 4, 256, 2, 32768)
+    al = lambda x: (x + 255) // 256 * 256
+    # (the per-head tables give one kv head per workgroup, so the heuristic
+    # splits finer than pa_choose_partition_size for the same length)
+    parts = n - (al(4 * 3907 * 4) + al(4 * 2048 * 4) + al(4 * 4))
+    assert parts > 0 and parts % 256 == 0
+    rows = 24
+    np_ = None
+    for Pc in range(16, 32769, 16):
+        k = (32768 + Pc - 1) // Pc
+        if al(rows * k * 256 * 4) + al(rows * k * 4) == parts:
+            np_ = k
+            break
+    assert np_ is not None and np_ > 1
+    # every block selected: at most the 4096 blocks of max_seq_len
+    assert lib.pa_decode_sparse_workspace_bytes(1, 1, 24, 4, 256, 2, 1000, 64, 100, 1024) == \
+        al(4 * 16 * 4) + al(4 * 64 * 4) + al(4 * 4)
+    assert lib.pa_decode_sparse_workspace_bytes(1, 1, 24, 4, 256, 0, 1000, 64, 100, 0) == 0  # fp32: invalid
+
+
+def test_sparse_mean_keys_rejects_bad_arguments(lib):
+    args = dict(k_cache=A, kv_dtype=2, k_scale=A, num_blocks=64, block_size=16, Hkv=2, D=128, block_table=A,
+                max_blocks=64, seq_lens=A, B=2, max_seq_len=1000, sparse_block=64, num_new=1, mean_k=A,
+                max_sblocks=16, stream=None)
+
+    def call(**over):
+        a = dict(args)
+        a.update(over)
+        return lib.pa_sparse_mean_keys(*a.values())
+
+    assert call(k_scale=None) == -1
+    assert call(mean_k=None) == -1
+    assert call(max_sblocks=15) == -2
+    assert call(num_new=0) == -2
+    assert call(sparse_block=24) == -2
+    assert call(D=96) == -4
+    assert call(B=0) == 0  # nothing to do, nothing launched
