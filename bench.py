@@ -431,12 +431,46 @@ def pct(a, q):
     return round(1e3 * float(np.percentile(np.asarray(a), q)), 2)
 
 
+def sparse_step_bytes(w, sel, SB: int) -> dict:
+    """Algorithmic bytes of one sparse step: the mean keys the scores read
+    (every block below each length, fp32), the K/V bytes of the selected
+    blocks' tokens below each length, the keys the mean refresh re-reads (the
+    sparse blocks holding the newest Tq tokens), table entries, q and out."""
+    from workloads import kv_bytes_per_token
+
+    sp = w.spec
+    per_tok = kv_bytes_per_token(sp) // sp.Hkv  # K + V (+ scales) of one token and kv head
+    kv = 0
+    for b in range(sp.B):
+        L = int(w.seq_lens[b])
+        for g in range(sp.Hkv):
+            for j in sel[b, g]:
+                if j < 0:
+                    break
+                kv += max(0, min(L, (int(j) + 1) * SB) - int(j) * SB) * per_tok
+    nsb = (w.seq_lens.astype(np.int64) + SB - 1) // SB
+    mean_read = int(nsb.sum()) * sp.Hkv * sp.D * 4
+    refresh = 0
+    for b in range(sp.B):
+        L = int(w.seq_lens[b])
+        if L > 0:
+            first = max(L - sp.Tq, 0) // SB
+            toks = sum(min(L, (j + 1) * SB) - j * SB for j in range(first, int(nsb[b])))
+            refresh += toks * sp.Hkv * (per_tok // 2)
+    elt_q = 4 if sp.q_dtype == "f32" else 2
+    qo = sp.B * sp.Tq * sp.Hq * sp.D * (elt_q + 4)
+    total = kv + mean_read + refresh + qo
+    return {"kv_selected": kv, "mean_keys": mean_read, "mean_refresh": refresh, "q_out": qo, "total": total}
+
+
 def measure(args, spec, partition_size: int, shared: bool, graph: bool, cold: bool, cpu_budget: float,
-            cpu_budget_1t: float) -> dict:
+            cpu_budget_1t: float, sparse=None) -> dict:
     """Time one workload: K eager steps between two synchronisations (the
     metric), K eager steps with HIP events between the kernels (breakdown,
     per-step percentiles, the decode kernel's roofline), optionally K graph
-    replays, cache-flushed side steps and the CPU oracle baseline."""
+    replays, cache-flushed side steps and the CPU oracle baseline. sparse =
+    (sparse_block, top_blocks) times the sparse block-selection step instead
+    (cache write, mean-key refresh, pa_decode_sparse)."""
     import torch
 
     import paged_attention_decode_02_amd as pa
@@ -487,6 +521,16 @@ def measure(args, spec, partition_size: int, shared: bool, graph: bool, cold: bo
                                                     w.max_seq_len, sp.shared_prefix, args.prefix_partition,
                                                     args.tail_partition)
         prefix_table = torch.from_numpy(np.ascontiguousarray(w.block_table[0, : sp.shared_prefix // 16])).to(dev)
+    mean_k = sel = None
+    if sparse:
+        SB, top = sparse
+        nsb = (w.max_seq_len + SB - 1) // SB
+        ws_bytes = pa.sparse_workspace_bytes(sp.B, sp.Tq, sp.Hq, sp.Hkv, sp.D, TD[sp.cache_dtype], w.max_seq_len,
+                                             SB, top, partition_size)
+        mean_k = torch.zeros((sp.B, nsb, sp.Hkv, sp.D), dtype=torch.float32, device=dev)
+        sel = torch.full((sp.B, sp.Hkv, pa.sparse_max_selected(w.max_seq_len, SB, top)), -1, dtype=torch.int32,
+                         device=dev)
+        pa.sparse_mean_keys(kc, table, lens, w.max_seq_len, SB, w.max_seq_len, mean_k, ks)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty((sp.B, sp.Tq, sp.Hq, sp.D), dtype=torch.float32, device=dev)
     lse = torch.empty((sp.B, sp.Tq, sp.Hq), dtype=torch.float32, device=dev)
@@ -499,8 +543,17 @@ def measure(args, spec, partition_size: int, shared: bool, graph: bool, cold: bo
         if ev is not None:
             ev[0].record(stream)
         pa.cache_write(new_k, new_v, new_slots, kc, vc, ks, vs)
+        if sparse:
+            pa.sparse_mean_keys(kc, table, lens, w.max_seq_len, sparse[0], sp.Tq, mean_k, ks)
         if ev is not None:
             ev[1].record(stream)
+        if sparse:
+            pa.decode_sparse(q, kc, vc, table, lens, w.max_seq_len, w.softmax_scale, mean_k, sparse[0], sparse[1],
+                             ks, vs, partition_size, out=out, lse=lse, selected=sel, workspace=ws)
+            if ev is not None:
+                ev[2].record(stream)
+                ev[3].record(stream)
+            return
         if shared:
             pa.decode_shared_prefix(q, kc, vc, prefix_table, sp.shared_prefix, table, lens, w.max_seq_len,
                                     w.softmax_scale, ks, vs, args.prefix_partition, args.tail_partition, out=out,
@@ -553,7 +606,10 @@ def measure(args, spec, partition_size: int, shared: bool, graph: bool, cold: bo
     # what a sustained decode runs. The decode leaves its inputs unchanged, so
     # repeating it alone is the same work.
     def decode_only():
-        if shared:
+        if sparse:
+            pa.decode_sparse(q, kc, vc, table, lens, w.max_seq_len, w.softmax_scale, mean_k, sparse[0], sparse[1],
+                             ks, vs, partition_size, out=out, lse=lse, selected=sel, workspace=ws)
+        elif shared:
             pa.decode_shared_prefix(q, kc, vc, prefix_table, sp.shared_prefix, table, lens, w.max_seq_len,
                                     w.softmax_scale, ks, vs, args.prefix_partition, args.tail_partition, out=out,
                                     lse=lse, workspace=ws)
@@ -612,6 +668,27 @@ def measure(args, spec, partition_size: int, shared: bool, graph: bool, cold: bo
     # the shared-prefix call must read the prefix once: its bytes are the
     # unique ones (the per-sequence total is reported beside them)
     step_bytes = unique_bytes(w) if shared else ab["total"]
+    sparse_rec = None
+    if sparse:
+        # the selection the timed steps made, its bytes, and how far the
+        # sparse output lies from the library's full decode of the same step
+        seln = sel.cpu().numpy()
+        sb = sparse_step_bytes(w, seln, sparse[0])
+        step_bytes = sb["total"]
+        s_out, s_lse = out.clone(), lse.clone()
+        f_out, f_lse = pa.decode(q, kc, vc, table, lens, w.max_seq_len, w.softmax_scale, ks, vs)
+        torch.cuda.synchronize()
+        dev_out = (s_out - f_out).abs()
+        sparse_rec = {
+            "sparse_block": sparse[0], "top_blocks": sparse[1],
+            "selected_blocks_per_head": [int((seln >= 0).sum(axis=2).min()), int((seln >= 0).sum(axis=2).max())],
+            "bytes": sb,
+            "full_decode_bytes": ab["total"],
+            "vs_full_decode": {"max_abs_out": round(float(dev_out.max()), 6),
+                               "mean_abs_out": round(float(dev_out.mean()), 6),
+                               "max_abs_lse": round(float((s_lse - f_lse).abs().max()), 6)},
+        }
+        del f_out, f_lse
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dec_avg_ms = dec_loop_ms
@@ -639,7 +716,7 @@ def measure(args, spec, partition_size: int, shared: bool, graph: bool, cold: bo
             "tail_partition": args.tail_partition if shared else None,
             "splitk_workspace_bytes_per_step": ws_traffic,
         },
-        "path": "shared_prefix" if shared else "decode",
+        "path": "sparse" if sparse else ("shared_prefix" if shared else "decode"),
         "graph_us_per_step": round(graph_ms * 1e3, 2) if graph_ms is not None else None,
         "step_us_event_timed": {"p10": pct(step_ms, 10), "median": pct(step_ms, 50), "p90": pct(step_ms, 90),
                                 "min": pct(step_ms, 0), "steps": len(step_ms)},
@@ -653,7 +730,9 @@ def measure(args, spec, partition_size: int, shared: bool, graph: bool, cold: bo
             "step_events": round(1e3 * float(np.median(step_ms)), 2),
         },
         "roofline": {
-            "kernel": ("pa_decode_shared_prefix: prefix pass, tail pass and merge, against the bytes with the "
+            "kernel": ("pa_decode_sparse: scores, selection, decode and merge, against the bytes of the mean "
+                       "keys and the selected blocks" if sparse else
+                       "pa_decode_shared_prefix: prefix pass, tail pass and merge, against the bytes with the "
                        "prefix read once" if shared else decode_kernel(sp)[0]),
             "timing": "K back-to-back launches between two HIP events on the launch stream",
             "launch_us": round(1e3 * dec_loop_ms, 2),
@@ -662,10 +741,16 @@ def measure(args, spec, partition_size: int, shared: bool, graph: bool, cold: bo
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": committed_traffic(sp, shared) if not partition_size or partition_size == P else None,
+            "traffic": (None if sparse else committed_traffic(sp, shared)
+                        if not partition_size or partition_size == P else None),
             "kernel_source_digest": kernel_source_digest(sp, shared),
         },
     }
+    if sparse_rec:
+        res["sparse"] = sparse_rec
+        res["breakdown_us"]["note"] += "; sparse: cache_write holds the mean-key refresh, decode the whole call"
+        res["config"]["partition_size"] = partition_size or None
+        res["config"]["num_partitions"] = None
     if cold_ms:
         res["breakdown_us"]["decode_plus_reduce_after_flush"] = round(1e3 * float(np.median(cold_ms)), 2)
     if args.copy_calibration_mb:
@@ -686,8 +771,11 @@ def measure(args, spec, partition_size: int, shared: bool, graph: bool, cold: bo
 
 # Side figures of the default run (each its own timed pass, reported under its
 # own key): the 250K-token int8 decode, the second workload the >= 70% bar
-# applies to, and the 64K workload at the 512-token partitions it names.
-EXTRAS = (("int8_250k", "int8_250k", 0, True), ("long64k_bf16_p512", "long64k_bf16", 512, False))
+# applies to, the 64K workload at the 512-token partitions it names, and the
+# sparse block-selection step on the 250K int8 cache (512 blocks of 64 tokens
+# per kv head, 13% of the context).
+EXTRAS = (("int8_250k", "int8_250k", 0, True, None), ("long64k_bf16_p512", "long64k_bf16", 512, False, None),
+          ("int8_250k_sparse_top512", "int8_250k", 0, False, (64, 512)))
 
 
 def main():
@@ -699,6 +787,10 @@ def main():
     ap.add_argument("--partition-size", type=int, default=0, help="0 = the library's heuristic")
     ap.add_argument("--shared-prefix", action="store_true",
                     help="decode through pa_decode_shared_prefix (workloads with a shared prefix)")
+    ap.add_argument("--sparse-top", type=int, default=0,
+                    help="time the sparse block-selection step (mean-key refresh, pa_decode_sparse) keeping this "
+                         "many sparse blocks per (sequence, kv head); 0 = the plain decode")
+    ap.add_argument("--sparse-block", type=int, default=64, help="--sparse-top: tokens per sparse block")
     ap.add_argument("--batch", type=int, default=0, help="override the workload's B (0 = as named)")
     ap.add_argument("--lengths", default="", help="override the workload's sequence lengths, LO:HI")
     ap.add_argument("--prefix", type=int, default=-1, help="override the workload's shared prefix (tokens)")
@@ -762,13 +854,18 @@ def main():
         changes["shared_prefix"] = args.prefix
     if changes:  # a workload of its own: no committed counters apply
         spec = scaled(spec, name=spec.name + "_custom", **changes)
+    if args.shared_prefix and args.sparse_top:
+        print("--shared-prefix and --sparse-top are separate paths", file=sys.stderr)
+        sys.exit(2)
     if args.shared_prefix and not spec.shared_prefix:
         print("--shared-prefix needs a workload whose sequences share a prefix", file=sys.stderr)
         sys.exit(2)
 
     cpu = 0.0 if args.no_cpu_baseline else args.cpu_budget
     cpu1 = 0.0 if args.no_cpu_baseline else args.cpu_budget_1thread
-    main_res = measure(args, spec, args.partition_size, args.shared_prefix, not args.no_graph, True, cpu, cpu1)
+    sparse = (args.sparse_block, args.sparse_top) if args.sparse_top else None
+    main_res = measure(args, spec, args.partition_size, args.shared_prefix, not args.no_graph, not sparse,
+                       0.0 if sparse else cpu, 0.0 if sparse else cpu1, sparse)
     result = {
         "metric": METRIC,
         "value": main_res.pop("value"),
@@ -794,11 +891,11 @@ def main():
     if cpu_res is not None:
         result["cpu_baseline"] = cpu_res
     result["device"] = device_record(pa)
-    if not explicit_workload and not args.no_extras and not changes and not args.partition_size:
-        for key, name, P, with_cpu in EXTRAS:
+    if not explicit_workload and not args.no_extras and not changes and not args.partition_size and not sparse:
+        for key, name, P, with_cpu, sp_sel in EXTRAS:
             log("side workload %s (%s, P=%s)" % (key, name, P or "heuristic"))
             r = measure(args, SPECS[name], P, False, False, False, cpu if with_cpu else 0.0,
-                        cpu1 if with_cpu else 0.0)
+                        cpu1 if with_cpu else 0.0, sp_sel)
             r["dtype"] = SPECS[name].cache_dtype
             result[key] = r
     print(json.dumps(result), flush=True)

@@ -171,6 +171,9 @@ int pa_decode(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, int32_t Hq
  * then lse [B, Tq, Hq, NP] at the next 256-byte boundary. Row (b, t, h)
  * reads partitions i < ceil(max(n, 0) / partition_size) with
  * n = seq_lens[b] - Tq + t + 1, which are exactly the ones pa_decode writes.
+ * One log-sum-exp per partition stands for the (max, sum) pair a merge could
+ * also take (lse_i = m_i + log l_i): the decode forms it once per partition
+ * and the merge reads one scalar instead of two.
  * workspace and out must be 16-byte aligned (PA_ERR_ALIGN otherwise).
  */
 int pa_decode_splitk_reduce(const void* workspace, int32_t num_partitions, int32_t partition_size, int32_t B,
@@ -225,7 +228,9 @@ size_t pa_decode_shared_prefix_workspace_bytes(int32_t B, int32_t Tq, int32_t Hq
 
 /* Bytes of workspace pa_decode needs (0 when one partition covers
  * max_seq_len). partition_size 0 means the heuristic's choice, as in
- * pa_decode; the caller must pass the same arguments to both. Returns 0 for
+ * pa_decode; the caller must pass the same arguments to both. Hkv and
+ * kv_dtype are among them because the heuristic's partition size, and so the
+ * partition count, depends on the kernel and grid they select. Returns 0 for
  * invalid arguments (pa_decode then reports the error). */
 size_t pa_decode_workspace_bytes(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dtype kv_dtype,
                                  int32_t max_seq_len, int32_t partition_size);

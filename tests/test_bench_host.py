@@ -63,3 +63,32 @@ def bench_dtype(name):
 
     return {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "fp8": torch.float8_e4m3fn,
             "nvfp4": torch.float4_e2m1fn_x2}[name]
+
+
+def test_sparse_step_bytes_with_every_block_selected():
+    # every sparse block of every (sequence, kv head) selected: the K/V bytes
+    # are the full decode's; the mean keys add one fp32 row per block and head
+    for kv in ("bf16", "i8", "nvfp4"):
+        spec = scaled("int8_250k", B=3, Tq=2, Hq=4, Hkv=2, D=64, seq_lens=(100, 300), cache_dtype=kv,
+                      src_dtype="f32")
+        w = generate(spec, seed=3)
+        SB = 32
+        nsb = (w.seq_lens + SB - 1) // SB
+        sel = np.full((spec.B, spec.Hkv, int(nsb.max())), -1, dtype=np.int32)
+        for b in range(spec.B):
+            sel[b, :, :nsb[b]] = np.arange(nsb[b])
+        sb = bench.sparse_step_bytes(w, sel, SB)
+        ab = bench.algorithmic_bytes(w)
+        assert sb["kv_selected"] == ab["kv"] + ab["scales"]
+        assert sb["mean_keys"] == int(nsb.sum()) * spec.Hkv * spec.D * 4
+        # the refresh re-reads the keys of the blocks holding the last Tq tokens
+        per_key = (ab["kv"] + ab["scales"]) // int(w.seq_lens.sum()) // 2
+        refresh = sum(min(int(L), (j + 1) * SB) - j * SB for L in w.seq_lens
+                      for j in range((int(L) - spec.Tq) // SB, (int(L) + SB - 1) // SB))
+        assert sb["mean_refresh"] == refresh * per_key
+        # half the blocks: half-ish the K/V bytes, never more than the full set
+        sel2 = sel.copy()
+        sel2[:, :, 1::2] = -1
+        sel2 = np.sort(np.where(sel2 < 0, 1 << 30, sel2), axis=2)
+        sel2[sel2 == 1 << 30] = -1
+        assert bench.sparse_step_bytes(w, sel2, SB)["kv_selected"] < sb["kv_selected"]

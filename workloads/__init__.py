@@ -110,7 +110,7 @@ SPECS: Dict[str, Spec] = {
     ),
     "int8_250k": Spec(
         "int8_250k", B=1, Tq=1, Hq=24, Hkv=4, D=256, seq_lens=(250000, 250000),
-        q_dtype="bf16", src_dtype="f32", cache_dtype="i8",
+        q_dtype="bf16", src_dtype="f32", cache_dtype="i8", partition_size=512,
         description="int8-KV ultra-long decode, 250000 tokens, fp32 N(0,1) source",
     ),
     "verify_bf16": Spec(
