@@ -328,7 +328,7 @@ int pa_cache_write_check(const int64_t* slot_mapping, int64_t num_tokens, int64_
  * belonging to the sequence in row b of block_table; entries of blocks at or
  * past a sequence's ceil(seq_lens[b] / sparse_block) are not written.
  * Requires max_sparse_blocks >= ceil(max_seq_len / sparse_block). Sums run in
- * fp32 in position order (deterministic).
+ * fp32 in a fixed order (the same result on every call).
  */
 int pa_sparse_mean_keys(const void* k_cache, pa_dtype kv_dtype, const float* k_scale, int64_t num_blocks,
                         int32_t block_size, int32_t Hkv, int32_t D, const int32_t* block_table,

@@ -409,8 +409,9 @@ int plan_sparse(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv, int32_t D, pa_dt
     if (!kv_supported(kv_dtype)) return fail(PA_ERR_DTYPE, "kv dtype %d not supported", (int)kv_dtype);
     if (kv_dtype == PA_F32) return fail(PA_ERR_UNSUPPORTED, "the sparse decode takes bf16, int8, fp8 or nvfp4 caches");
     if (max_seq_len < 0) return fail(PA_ERR_SHAPE, "max_seq_len=%d must be >= 0", max_seq_len);
-    if (sparse_block < kBlock || sparse_block % kBlock || sparse_block > 4096)
-        return fail(PA_ERR_SHAPE, "sparse_block=%d must be a multiple of %d in [16, 4096]", sparse_block, kBlock);
+    if (sparse_block < kBlock || sparse_block % kBlock || sparse_block > pa::kSparseMaxBlockTokens)
+        return fail(PA_ERR_SHAPE, "sparse_block=%d must be a multiple of %d in [16, %d]", sparse_block, kBlock,
+                    pa::kSparseMaxBlockTokens);
     if (top_blocks < 1) return fail(PA_ERR_SHAPE, "top_blocks=%d must be >= 1", top_blocks);
     if (partition_size < 0 || partition_size % kBlock)
         return fail(PA_ERR_SHAPE, "partition_size=%d must be 0 or a positive multiple of %d", partition_size, kBlock);
@@ -751,8 +752,9 @@ int pa_sparse_mean_keys(const void* k_cache, pa_dtype kv_dtype, const float* k_s
     if (!supported_d(D)) return fail(PA_ERR_UNSUPPORTED, "D=%d not in {64, 128, 256}", D);
     if ((int64_t)max_blocks_per_seq * kBlock < max_seq_len)
         return fail(PA_ERR_SHAPE, "block table too short: %d blocks for max_seq_len %d", max_blocks_per_seq, max_seq_len);
-    if (sparse_block < kBlock || sparse_block % kBlock || sparse_block > 4096)
-        return fail(PA_ERR_SHAPE, "sparse_block=%d must be a multiple of %d in [16, 4096]", sparse_block, kBlock);
+    if (sparse_block < kBlock || sparse_block % kBlock || sparse_block > pa::kSparseMaxBlockTokens)
+        return fail(PA_ERR_SHAPE, "sparse_block=%d must be a multiple of %d in [16, %d]", sparse_block, kBlock,
+                    pa::kSparseMaxBlockTokens);
     if (num_new < 1) return fail(PA_ERR_SHAPE, "num_new=%d must be >= 1", num_new);
     const int64_t nsb = ((int64_t)max_seq_len + sparse_block - 1) / sparse_block;
     if (max_sparse_blocks < nsb)

@@ -143,6 +143,7 @@ hipError_t launch_sparse_mean(int kv_type, const SparseParams& p, int nref, hipS
 // scores of the candidate blocks, then the selection and compacted tables
 hipError_t launch_sparse_select(const SparseParams& p, hipStream_t stream);
 constexpr int kSparseMaxBlocks = 4096;  // sparse blocks per sequence at most
+constexpr int kSparseMaxBlockTokens = 4096;  // tokens per sparse block at most
 
 // Valid head-chunk widths of the VALU decode instances.
 bool decode_valu_has_gt(int GT);

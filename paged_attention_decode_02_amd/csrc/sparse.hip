@@ -15,19 +15,25 @@
 //
 // Kernels:
 //  - sparse_mean_kernel: one workgroup per (sequence, refreshed block, kv
-//    head); thread d sums element d over the block's tokens in position
-//    order (fp32) and divides by their count;
-//  - sparse_score_kernel: one workgroup per (sequence and kv head, 32
-//    candidate blocks): the candidates' mean keys and 16 query rows at a
-//    time are staged in LDS (padded rows, coalesced loads), each thread takes
-//    one candidate and two rows, dot products in fp32 in dimension order;
+//    head); a thread takes 4 consecutive elements of every (256 / (D / 4))-th
+//    token of the block, all its loads issued before the sums (the block's
+//    table entries staged in LDS first); the per-thread sums (fp32, token
+//    order) are combined in thread order, so the result is deterministic;
+//  - sparse_score_kernel: one workgroup per (sequence and kv head, 64
+//    candidate blocks), 16 candidates per wave; a lane quad holds one
+//    candidate's mean key in registers (interleaved 16-byte pieces, loaded at
+//    once), the query rows are staged 16 at a time in LDS, and each row's dot
+//    product is summed over the quad by two shuffles;
 //  - sparse_select_kernel: one workgroup per (sequence, kv head): a radix
-//    select over the candidates' scores (4 passes of 8 bits on the
-//    order-preserving integer image of the fp32 score) finds the threshold,
-//    ties at the threshold go to the lower block index (a prefix count in
-//    block order), the selected blocks are compacted in increasing order with
-//    the kept blocks last, and their cache blocks written as one block table
-//    row with the compacted length.
+//    select over the candidates' scores finds the threshold: on the
+//    order-preserving integer image of the fp32 score less the smallest one
+//    (which spreads scores of one sign and exponent over the bins), 11-bit
+//    digits from the highest bit that varies, each digit found by a
+//    wave-parallel suffix count over the 2048 bins; ties at the threshold go
+//    to the lower block index (a prefix count in block order), the selected
+//    blocks are compacted in increasing order with the kept blocks last, and
+//    their cache blocks written as one block table row with the compacted
+//    length.
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -35,51 +41,64 @@ namespace pa {
 
 namespace {
 
-// Element d of the key row of (physical block ph, token off, kv head g).
+// Elements d0 .. d0 + 3 (d0 a multiple of 4) of the key row of (physical
+// block ph, token off, kv head g), dequantised.
 template <int KVT>
-__device__ __forceinline__ float key_elem(const void* cache, const float* scale, int64_t ph, int off, int g, int Hkv,
-                                          int D, int d) {
+__device__ __forceinline__ float4 key4(const void* cache, const float* scale, int64_t ph, int off, int g, int Hkv,
+                                       int D, int d0) {
     if constexpr (KVT == KV_NVFP4) {
         const uint8_t* blk = reinterpret_cast<const uint8_t*>(cache) + ph * kBlockSize * Hkv * nvfp4_row_bytes(D);
-        const uint32_t code = blk[(int64_t)(off * Hkv + g) * (D / 2) + d / 2];
-        const pa_f32x2 e = fp4x2_to_f32<0>(code);
-        const uint32_t sb = blk[(int64_t)kBlockSize * Hkv * (D / 2) + (int64_t)g * D + nvfp4_scale_byte(off, d / 16)];
-        return ((d & 1) ? e.y : e.x) * fp8_value(sb) * scale[(ph * Hkv + g) * kBlockSize + off];
+        const uint32_t codes =
+            *reinterpret_cast<const uint16_t*>(blk + (int64_t)(off * Hkv + g) * (D / 2) + d0 / 2);
+        const uint32_t sb = blk[(int64_t)kBlockSize * Hkv * (D / 2) + (int64_t)g * D + nvfp4_scale_byte(off, d0 / 16)];
+        const float f = fp8_value(sb) * scale[(ph * Hkv + g) * kBlockSize + off];
+        const pa_f32x2 lo = fp4x2_to_f32<0>(codes), hi = fp4x2_to_f32<1>(codes);
+        return make_float4(lo.x * f, lo.y * f, hi.x * f, hi.y * f);
     } else {
         const int64_t row = (ph * kBlockSize + off) * Hkv + g;
         if constexpr (KVT == KV_F32) {
-            return reinterpret_cast<const float*>(cache)[row * D + d];
+            return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(cache) + row * D + d0);
         } else if constexpr (KVT == KV_BF16) {
-            return bf16_to_f32(reinterpret_cast<const uint16_t*>(cache)[row * D + d]);
+            const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(cache) + row * D + d0);
+            return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                               __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
         } else {
-            const uint32_t code = reinterpret_cast<const uint8_t*>(cache)[row * D + d];
-            const float s = scale[(ph * Hkv + g) * kBlockSize + off];
-            if constexpr (KVT == KV_I8)
-                return (float)(int8_t)code * s;
-            else
-                return fp8_value(code) * s;
+            const uint32_t c = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(cache) + row * D + d0);
+            const float sc = scale[(ph * Hkv + g) * kBlockSize + off];
+            if constexpr (KVT == KV_I8) {
+                return make_float4((float)(int8_t)c * sc, (float)(int8_t)(c >> 8) * sc, (float)(int8_t)(c >> 16) * sc,
+                                   (float)(int8_t)(c >> 24) * sc);
+            } else {
+                const pa_f32x2 lo = fp8x2_to_f32<false>(c), hi = fp8x2_to_f32<true>(c);
+                return make_float4(lo.x * sc, lo.y * sc, hi.x * sc, hi.y * sc);
+            }
         }
     }
 }
 
-// Order-preserving unsigned image of a float (larger float, larger key).
+// Order-preserving unsigned image of a float (larger float, larger key; the
+// two zeros map to one key, as they compare equal).
 __device__ __forceinline__ uint32_t order_key(float f) {
-    const uint32_t u = __float_as_uint(f);
+    const uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 // First sparse block holding a query token of a sequence of L tokens.
 __device__ __forceinline__ int first_kept(int L, int Tq, int SB) { return (L - Tq > 0 ? L - Tq : 0) / SB; }
 
-constexpr int kScoreTile = 32;   // candidate blocks per score workgroup
+constexpr int kScoreCands = 64;  // candidate blocks per score workgroup (16 per wave)
 constexpr int kScoreRows = 16;   // query rows staged at a time
 constexpr int kSelThreads = 1024;
 constexpr int kSelPer = 4;       // candidates per select thread (4096 in all)
-
+constexpr int kSelBits = 11;     // radix digit of the select
+constexpr int kSelBins = 1 << kSelBits;
+constexpr int kMeanUnroll = 8;   // token loads a mean-key thread keeps in flight
 }  // namespace
 
 template <int KVT>
 __global__ __launch_bounds__(256) void sparse_mean_kernel(SparseParams p) {
+    __shared__ int32_t tab[kSparseMaxBlockTokens / kBlockSize];
+    __shared__ __align__(16) float part[256 * 4];  // [token lane][D]: 256 / (D / 4) lanes of D floats
     const int b = blockIdx.x, k = blockIdx.y, g = blockIdx.z;
     const int L = p.seq_lens[b];
     if (L <= 0) return;
@@ -87,78 +106,111 @@ __global__ __launch_bounds__(256) void sparse_mean_kernel(SparseParams p) {
     const int nsb = (L + SB - 1) / SB;
     const int j = (L - p.num_new > 0 ? L - p.num_new : 0) / SB + k;  // blocks holding the newest tokens
     if (j >= nsb) return;
-    const int p0 = j * SB, p1 = min(p0 + SB, L);
+    const int p0 = j * SB, p1 = min(p0 + SB, L), n = p1 - p0;
+    const int D = p.D, DG = D / 4, lanes = 256 / DG;
+    const int tid = threadIdx.x, tl = tid / DG, d0 = (tid % DG) * 4;
     const int32_t* table = p.block_table + (int64_t)b * p.max_blocks;
-    float* dst = p.mean_k + (((int64_t)b * p.max_sblocks + j) * p.Hkv + g) * p.D;
-    for (int d = threadIdx.x; d < p.D; d += blockDim.x) {
+    for (int x = tid; x < (n + kBlockSize - 1) / kBlockSize; x += 256) tab[x] = table[p0 / kBlockSize + x];
+    __syncthreads();
+    float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int t0 = tl; t0 < n; t0 += lanes * kMeanUnroll) {
+        float4 v[kMeanUnroll];
+#pragma unroll
+        for (int u = 0; u < kMeanUnroll; ++u) {  // tokens past n reread token n - 1, not summed
+            const int t = min(t0 + u * lanes, n - 1);
+            v[u] = key4<KVT>(p.k_cache, p.k_scale, (int64_t)tab[t / kBlockSize], t % kBlockSize, g, p.Hkv, D, d0);
+        }
+#pragma unroll
+        for (int u = 0; u < kMeanUnroll; ++u) {
+            if (t0 + u * lanes < n) {
+                s.x += v[u].x;
+                s.y += v[u].y;
+                s.z += v[u].z;
+                s.w += v[u].w;
+            }
+        }
+    }
+    *reinterpret_cast<float4*>(&part[tl * D + d0]) = s;
+    __syncthreads();
+    float* dst = p.mean_k + (((int64_t)b * p.max_sblocks + j) * p.Hkv + g) * D;
+    if (tid < D) {
         float sum = 0.0f;
-        for (int pos = p0; pos < p1; ++pos)
-            sum += key_elem<KVT>(p.k_cache, p.k_scale, (int64_t)table[pos / kBlockSize], pos % kBlockSize, g, p.Hkv,
-                                 p.D, d);
-        dst[d] = sum / (float)(p1 - p0);
+        for (int l = 0; l < lanes; ++l) sum += part[l * D + tid];
+        dst[tid] = sum / (float)n;
     }
 }
 
+template <int D>
 __global__ __launch_bounds__(256) void sparse_score_kernel(SparseParams p) {
-    // mean keys of the tile's candidates, rows padded by 4 floats (the
-    // threads of a wave read 32 different rows at one column)
-    __shared__ __align__(16) float mk[kScoreTile][256 + 4];
-    __shared__ __align__(16) float qs[kScoreRows][256];
-    __shared__ float red[256 / kScoreTile][kScoreTile];
+    __shared__ __align__(16) float qs[kScoreRows][D];
+    constexpr int NI = D / 16;  // 16-byte pieces of a candidate's mean key per lane
     const int bg = blockIdx.x, b = bg / p.Hkv, g = bg % p.Hkv;
     const int L = p.seq_lens[b];
     const int kept0 = L > 0 ? first_kept(L, p.Tq, p.sparse_block) : 0;
-    const int j0 = blockIdx.y * kScoreTile;
+    const int j0 = blockIdx.y * kScoreCands;
     if (j0 >= kept0) return;
-    const int D = p.D, G = p.Hq / p.Hkv, R = p.Tq * G;
-    const int tid = threadIdx.x;
-    for (int x = tid; x < kScoreTile * D; x += 256) {
-        const int c = x / D, d = x % D;
-        mk[c][d] = j0 + c < kept0 ? p.mean_k[(((int64_t)b * p.max_sblocks + j0 + c) * p.Hkv + g) * D + d] : 0.0f;
-    }
-    const int c = tid % kScoreTile, rg = tid / kScoreTile;  // candidate, row group (8)
+    const int G = p.Hq / p.Hkv, R = p.Tq * G;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int c = j0 + (tid >> 6) * 16 + (lane >> 2), kq = lane & 3;  // candidate, quarter
+    const bool valid = c < kept0;
+    // this lane's part of the candidate's mean key: elements 16 i + 4 kq .. + 3
+    // (an invalid candidate reads candidate 0's row and discards it)
+    const float* src = p.mean_k + (((int64_t)b * p.max_sblocks + (valid ? c : 0)) * p.Hkv + g) * D + 4 * kq;
+    float4 m[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) m[i] = *reinterpret_cast<const float4*>(src + 16 * i);
     float best = -INFINITY;
     for (int r0 = 0; r0 < R; r0 += kScoreRows) {
-        __syncthreads();
-        for (int x = tid; x < kScoreRows * D; x += 256) {
-            const int r = r0 + x / D, d = x % D;
-            float v = 0.0f;
-            if (r < R) {
-                const int64_t qoff = (((int64_t)b * p.Tq + r / G) * p.Hq + g * G + r % G) * D + d;
-                v = p.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(p.q)[qoff])
-                             : reinterpret_cast<const float*>(p.q)[qoff];
-            }
-            qs[x / D][d] = v;
-        }
-        __syncthreads();
+        // stage rows r0 .. r0 + 15 (rows past R as zeros): every load issued
+        // before the first store
+        constexpr int NU = kScoreRows * D / 256;
+        float v[NU];
+        if (p.q_bf16) {
+            const uint16_t* q = reinterpret_cast<const uint16_t*>(p.q);
 #pragma unroll
-        for (int k = 0; k < kScoreRows / 8; ++k) {
-            const int rr = rg + 8 * k;
-            if (r0 + rr >= R) continue;
-            float dot = 0.0f;
-            for (int d = 0; d < D; d += 4) {
-                const float4 a = *reinterpret_cast<const float4*>(&qs[rr][d]);
-                const float4 m = *reinterpret_cast<const float4*>(&mk[c][d]);
-                dot = fmaf(a.x, m.x, dot);
-                dot = fmaf(a.y, m.y, dot);
-                dot = fmaf(a.z, m.z, dot);
-                dot = fmaf(a.w, m.w, dot);
+            for (int u = 0; u < NU; ++u) {
+                const int x = tid + 256 * u, r = r0 + x / D, rc = r < R ? r : R - 1;
+                v[u] = bf16_to_f32(q[(((int64_t)b * p.Tq + rc / G) * p.Hq + g * G + rc % G) * D + x % D]);
             }
-            best = fmaxf(best, p.softmax_scale * dot);
+        } else {
+            const float* q = reinterpret_cast<const float*>(p.q);
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                const int x = tid + 256 * u, r = r0 + x / D, rc = r < R ? r : R - 1;
+                v[u] = q[(((int64_t)b * p.Tq + rc / G) * p.Hq + g * G + rc % G) * D + x % D];
+            }
+        }
+        __syncthreads();  // the previous rows' reads are done
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int x = tid + 256 * u;
+            qs[x / D][x % D] = r0 + x / D < R ? v[u] : 0.0f;
+        }
+        __syncthreads();
+        const int nr = min(kScoreRows, R - r0);
+        for (int rr = 0; rr < nr; ++rr) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const float4 a = *reinterpret_cast<const float4*>(&qs[rr][16 * i + 4 * kq]);
+                acc = fmaf(a.x, m[i].x, acc);
+                acc = fmaf(a.y, m[i].y, acc);
+                acc = fmaf(a.z, m[i].z, acc);
+                acc = fmaf(a.w, m[i].w, acc);
+            }
+            acc += __shfl_xor(acc, 1);
+            acc += __shfl_xor(acc, 2);
+            best = fmaxf(best, p.softmax_scale * acc);
         }
     }
-    red[rg][c] = best;
-    __syncthreads();
-    if (rg == 0 && j0 + c < kept0) {
-        float m = red[0][c];
-        for (int k = 1; k < 256 / kScoreTile; ++k) m = fmaxf(m, red[k][c]);
-        p.scores[(int64_t)bg * p.nsb_max + j0 + c] = m;
-    }
+    if (kq == 0 && valid) p.scores[(int64_t)bg * p.nsb_max + c] = best;
 }
 
 namespace {
-// exclusive prefix sum over the workgroup (kSelThreads threads), in thread order
+// exclusive prefix sum over the workgroup (kSelThreads threads), in thread
+// order; *total receives the sum
 __device__ int block_exclusive_scan(int v, int* wsum, int* total) {
+    constexpr int kWaves = kSelThreads / 64;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     int x = v;
 #pragma unroll
@@ -168,14 +220,16 @@ __device__ int block_exclusive_scan(int v, int* wsum, int* total) {
     }
     if (lane == 63) wsum[w] = x;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int acc = 0;
-        for (int i = 0; i < kSelThreads / 64; ++i) {
-            const int t = wsum[i];
-            wsum[i] = acc;
-            acc += t;
+    if (w == 0) {
+        const int t = lane < kWaves ? wsum[lane] : 0;
+        int xs = t;
+#pragma unroll
+        for (int o = 1; o < kWaves; o <<= 1) {
+            const int y = __shfl_up(xs, o);
+            if (lane >= o) xs += y;
         }
-        *total = acc;
+        if (lane < kWaves) wsum[lane] = xs - t;
+        if (lane == kWaves - 1) *total = xs;
     }
     __syncthreads();
     const int r = x - v + wsum[w];
@@ -185,14 +239,14 @@ __device__ int block_exclusive_scan(int v, int* wsum, int* total) {
 }  // namespace
 
 __global__ __launch_bounds__(kSelThreads) void sparse_select_kernel(SparseParams p) {
-    __shared__ int hist[256];
+    __shared__ __align__(16) int hist[kSelBins];
     __shared__ int lsel[kSelThreads * kSelPer];  // the selected blocks in increasing order
     __shared__ int wsum[kSelThreads / 64];
     __shared__ int total;
-    __shared__ uint32_t s_prefix;
+    __shared__ uint32_t s_prefix, s_min, s_max;
     __shared__ int s_remaining;
     const int bg = blockIdx.x, b = bg / p.Hkv;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int SB = p.sparse_block, SBB = SB / kBlockSize;
     const int L = p.seq_lens[b];
     const int nsb = L > 0 ? (L + SB - 1) / SB : 0;
@@ -200,54 +254,117 @@ __global__ __launch_bounds__(kSelThreads) void sparse_select_kernel(SparseParams
     const int nkept = nsb - kept0;
     int want = p.top_blocks - nkept;
     want = want < 0 ? 0 : want > kept0 ? kept0 : want;
+    const bool partial = want > 0 && want < kept0;  // uniform over the workgroup
 
     // this thread's candidates: blocks kSelPer tid .. kSelPer tid + kSelPer - 1
+    // (every load issued unconditionally, from a clamped index, before any use)
+    const int jmax = p.nsb_max > 0 ? p.nsb_max - 1 : 0;
+    float sc[kSelPer];
+#pragma unroll
+    for (int i = 0; i < kSelPer; ++i) sc[i] = p.scores[(int64_t)bg * p.nsb_max + min(kSelPer * tid + i, jmax)];
     uint32_t key[kSelPer];
 #pragma unroll
-    for (int i = 0; i < kSelPer; ++i) {
-        const int j = kSelPer * tid + i;
-        key[i] = j < kept0 ? order_key(p.scores[(int64_t)bg * p.nsb_max + j]) : 0u;
-    }
+    for (int i = 0; i < kSelPer; ++i) key[i] = kSelPer * tid + i < kept0 ? order_key(sc[i]) : 0u;
     // threshold T: the want-th largest key (want candidates have key >= T and
-    // fewer than want have key > T), by 8-bit digits from the top
-    if (tid == 0) {
-        s_prefix = 0u;
-        s_remaining = want;
-    }
-    uint32_t mask = 0u;
-    if (want > 0 && want < kept0) {
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
-            __syncthreads();
-            const uint32_t prefix = s_prefix;
+    // fewer than want have key > T), found on rel = key - (smallest key) by
+    // kSelBits-bit digits from the highest bit in which the keys differ
+    uint32_t T = 0u;
+    int need_eq = 0;  // keys == T to take, in block order
+    if (partial) {
+        uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
-            for (int i = 0; i < kSelPer; ++i) {
-                const int j = kSelPer * tid + i;
-                if (j < kept0 && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> shift) & 0xFF], 1);
+        for (int i = 0; i < kSelPer; ++i)
+            if (kSelPer * tid + i < kept0) {
+                lo = min(lo, key[i]);
+                hi = max(hi, key[i]);
             }
-            __syncthreads();
-            if (tid == 0) {
-                int rem = s_remaining, dgt = 255;
-                for (; dgt > 0; --dgt) {
-                    if (hist[dgt] >= rem) break;
-                    rem -= hist[dgt];
-                }
-                s_prefix = prefix | ((uint32_t)dgt << shift);
-                s_remaining = rem;  // keys equal to the final prefix still to take
-            }
-            mask |= 0xFFu << shift;
-            __syncthreads();
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
+            hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
         }
+        if (tid == 0) {
+            s_min = 0xFFFFFFFFu;
+            s_max = 0u;
+        }
+        __syncthreads();
+        if (lane == 0) {
+            atomicMin(&s_min, lo);
+            atomicMax(&s_max, hi);
+        }
+        __syncthreads();
+        const uint32_t kmin = s_min, span = s_max - kmin;
+        const int nbits = span ? 32 - __clz(span) : 0;
+        uint32_t rel[kSelPer];
+#pragma unroll
+        for (int i = 0; i < kSelPer; ++i) rel[i] = key[i] - kmin;
+        uint32_t prefix = 0u, mask = 0u;
+        int rem = want;
+        for (int top = nbits; top > 0; top -= kSelBits) {
+            const int shift = top > kSelBits ? top - kSelBits : 0;
+            const uint32_t dmask = (1u << (top - shift)) - 1u;
+            for (int i = tid; i < kSelBins; i += kSelThreads) hist[i] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < kSelPer; ++i)
+                if (kSelPer * tid + i < kept0 && (rel[i] & mask) == prefix)
+                    atomicAdd(&hist[(rel[i] >> shift) & dmask], 1);
+            __syncthreads();
+            if (tid < 64) {
+                // lane owns bins 32 lane .. 32 lane + 31; suffix(d) = keys
+                // with digit >= d; the digit is the highest d with
+                // suffix(d) >= rem
+                int c[32], tot = 0;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int4 h = *reinterpret_cast<const int4*>(&hist[32 * lane + 4 * k]);
+                    c[4 * k] = h.x;
+                    c[4 * k + 1] = h.y;
+                    c[4 * k + 2] = h.z;
+                    c[4 * k + 3] = h.w;
+                    tot += h.x + h.y + h.z + h.w;
+                }
+                int incl = tot;  // keys in the bins of this lane and the lanes above
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int y = __shfl_down(incl, o);
+                    if (lane + o < 64) incl += y;
+                }
+                int run = incl - tot, best = -1, rem_at = rem;
+#pragma unroll
+                for (int k = 31; k >= 0; --k) {
+                    run += c[k];
+                    if (best < 0 && run >= rem) {
+                        best = 32 * lane + k;
+                        rem_at = rem - (run - c[k]);
+                    }
+                }
+                int bb = best;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) bb = max(bb, __shfl_xor(bb, o));
+                if (best >= 0 && best == bb) {
+                    s_prefix = prefix | ((uint32_t)best << shift);
+                    s_remaining = rem_at;
+                } else if (bb < 0 && lane == 0) {  // unreachable: suffix(0) counts every key left
+                    s_prefix = prefix;
+                    s_remaining = rem;
+                }
+            }
+            __syncthreads();
+            prefix = s_prefix;
+            rem = s_remaining;
+            mask |= dmask << shift;
+        }
+        T = kmin + prefix;
+        need_eq = rem;
     }
-    const uint32_t T = s_prefix;
-    const int need_eq = s_remaining;  // with want in (0, kept0): keys == T to take, in block order
     // selection flags in block order: all candidates (want == kept0), none
     // (want == 0), or key > T and the first need_eq keys == T
     int eq_cnt = 0;
 #pragma unroll
     for (int i = 0; i < kSelPer; ++i) {
         const int j = kSelPer * tid + i;
-        eq_cnt += (want > 0 && want < kept0 && j < kept0 && key[i] == T) ? 1 : 0;
+        eq_cnt += (partial && j < kept0 && key[i] == T) ? 1 : 0;
     }
     int eq_before = block_exclusive_scan(eq_cnt, wsum, &total);
     bool flag[kSelPer];
@@ -283,9 +400,18 @@ __global__ __launch_bounds__(kSelThreads) void sparse_select_kernel(SparseParams
     // compacted table row: the cache blocks of the selected blocks in order
     const int32_t* table = p.block_table + (int64_t)b * p.max_blocks;
     int32_t* ct = p.ctab + (int64_t)bg * p.ctab_width;
-    for (int x = tid; x < count * SBB; x += kSelThreads) {
-        const int jb = lsel[x / SBB] * SBB + x % SBB;  // logical cache block
-        ct[x] = jb < p.max_blocks ? table[jb] : 0;     // past the table: never read (beyond the length)
+    const int nct = count * SBB;
+    for (int x0 = tid; x0 < nct; x0 += 4 * kSelThreads) {
+        int32_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int x = x0 + u * kSelThreads;
+            const int jb = x < nct ? lsel[x / SBB] * SBB + x % SBB : 0;  // logical cache block
+            v[u] = x < nct && jb < p.max_blocks ? table[jb] : 0;        // past the table: never read
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (x0 + u * kSelThreads < nct) ct[x0 + u * kSelThreads] = v[u];
     }
     if (tid == 0) p.clen[bg] = count > 0 ? (count - 1) * SB + (L - (nsb - 1) * SB) : 0;
     if (p.sel_out != nullptr)
@@ -309,11 +435,16 @@ hipError_t launch_sparse_mean(int kv_type, const SparseParams& p, int nref, hipS
 
 hipError_t launch_sparse_select(const SparseParams& p, hipStream_t s) {
     if (p.B <= 0) return hipSuccess;
-    if (p.D > 256 || p.nsb_max > kSelThreads * kSelPer) return hipErrorInvalidValue;
+    if (p.nsb_max > kSelThreads * kSelPer) return hipErrorInvalidValue;
     const unsigned bgs = (unsigned)(p.B * p.Hkv);
-    const unsigned tiles = (unsigned)((p.nsb_max + kScoreTile - 1) / kScoreTile);
+    const unsigned tiles = (unsigned)((p.nsb_max + kScoreCands - 1) / kScoreCands);
     if (tiles > 0) {
-        hipLaunchKernelGGL(sparse_score_kernel, dim3(bgs, tiles), dim3(256), 0, s, p);
+        switch (p.D) {
+        case 64: hipLaunchKernelGGL(sparse_score_kernel<64>, dim3(bgs, tiles), dim3(256), 0, s, p); break;
+        case 128: hipLaunchKernelGGL(sparse_score_kernel<128>, dim3(bgs, tiles), dim3(256), 0, s, p); break;
+        case 256: hipLaunchKernelGGL(sparse_score_kernel<256>, dim3(bgs, tiles), dim3(256), 0, s, p); break;
+        default: return hipErrorInvalidValue;
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -1,6 +1,6 @@
 """GPU parity of the sparse block-selection decode against the fp64 oracle.
 
-Mean keys: GPU (fp32 sums in position order) against the oracle's fp64 means,
+Mean keys: GPU (fp32 sums in a fixed order) against the oracle's fp64 means,
 for every cache type, full builds and the per-step refresh of the blocks
 holding the newest tokens. Selection: where floating point decides which
 blocks are taken, the GPU's choice is checked for validity against the
