@@ -198,8 +198,8 @@ __global__ __launch_bounds__(256) void sparse_score_kernel(SparseParams p) {
                 acc = fmaf(a.z, m[i].z, acc);
                 acc = fmaf(a.w, m[i].w, acc);
             }
-            acc += __shfl_xor(acc, 1);
-            acc += __shfl_xor(acc, 2);
+            acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xF, 0xF, true));  // quad [1,0,3,2]
+            acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0x4E, 0xF, 0xF, true));  // quad [2,3,0,1]
             best = fmaxf(best, p.softmax_scale * acc);
         }
     }
@@ -207,46 +207,72 @@ __global__ __launch_bounds__(256) void sparse_score_kernel(SparseParams p) {
 }
 
 namespace {
-// exclusive prefix sum over the workgroup (kSelThreads threads), in thread
-// order; *total receives the sum
-__device__ int block_exclusive_scan(int v, int* wsum, int* total) {
-    constexpr int kWaves = kSelThreads / 64;
+constexpr int kSelWaves = kSelThreads / 64;
+
+// Wave-level scans and reductions on DPP (vector-ALU lane moves), not on LDS
+// permutes. dpp<CTRL, ROWS>(x, id): lane l receives the lane CTRL names, or
+// id where the source is outside the row or the row is not in ROWS.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp(int x, int id) {
+    return __builtin_amdgcn_update_dpp(id, x, CTRL, ROWS, 0xF, false);
+}
+
+// inclusive prefix sum over the 64 lanes (within rows of 16 by shifts, then
+// the row totals broadcast to the rows above)
+__device__ __forceinline__ int wave_incl_sum(int x) {
+    x += dpp<0x111>(x, 0);  // row_shr:1
+    x += dpp<0x112>(x, 0);  // row_shr:2
+    x += dpp<0x114>(x, 0);  // row_shr:4
+    x += dpp<0x118>(x, 0);  // row_shr:8
+    x += dpp<0x142, 0xA>(x, 0);  // row_bcast:15 into rows 1 and 3
+    x += dpp<0x143, 0xC>(x, 0);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+// unsigned minimum / maximum over the 64 lanes, in every lane (each row
+// reduced by quad and mirror moves, the four row results read as scalars)
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_minmax(uint32_t x) {
+    auto op = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : min(a, b); };
+    x = op(x, (uint32_t)dpp<0xB1>((int)x, 0));   // quad_perm [1, 0, 3, 2]
+    x = op(x, (uint32_t)dpp<0x4E>((int)x, 0));   // quad_perm [2, 3, 0, 1]
+    x = op(x, (uint32_t)dpp<0x141>((int)x, 0));  // row_half_mirror
+    x = op(x, (uint32_t)dpp<0x140>((int)x, 0));  // row_mirror
+    const uint32_t r0 = __builtin_amdgcn_readlane(x, 0), r1 = __builtin_amdgcn_readlane(x, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(x, 32), r3 = __builtin_amdgcn_readlane(x, 48);
+    return op(op(r0, r1), op(r2, r3));
+}
+
+// Exclusive prefix sum of v over the workgroup in thread order, with one
+// barrier: a shuffle scan inside each wave, the wave totals through LDS
+// (wsum: kSelWaves ints, free for reuse only after the caller's next
+// barrier). *total receives the sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const int x = wave_incl_sum(v);
     if (lane == 63) wsum[w] = x;
     __syncthreads();
-    if (w == 0) {
-        const int t = lane < kWaves ? wsum[lane] : 0;
-        int xs = t;
+    int before = 0, all = 0;
 #pragma unroll
-        for (int o = 1; o < kWaves; o <<= 1) {
-            const int y = __shfl_up(xs, o);
-            if (lane >= o) xs += y;
-        }
-        if (lane < kWaves) wsum[lane] = xs - t;
-        if (lane == kWaves - 1) *total = xs;
+    for (int i = 0; i < kSelWaves; ++i) {
+        const int t = wsum[i];
+        before += i < w ? t : 0;
+        all += t;
     }
-    __syncthreads();
-    const int r = x - v + wsum[w];
-    __syncthreads();
-    return r;
+    *total = all;
+    return before + x - v;
 }
 }  // namespace
 
 __global__ __launch_bounds__(kSelThreads) void sparse_select_kernel(SparseParams p) {
-    __shared__ __align__(16) int hist[kSelBins];
-    __shared__ int lsel[kSelThreads * kSelPer];  // the selected blocks in increasing order
-    __shared__ int wsum[kSelThreads / 64];
-    __shared__ int total;
-    __shared__ uint32_t s_prefix, s_min, s_max;
-    __shared__ int s_remaining;
+    __shared__ __align__(16) int hist[2][kSelBins];     // double-buffered digit counts
+    __shared__ int lsel[kSelThreads * kSelPer];         // the selected blocks in increasing order
+    __shared__ int wsum[2][kSelWaves];                  // scan totals (two scans in flight)
+    __shared__ uint32_t wmin[kSelWaves], wmax[kSelWaves];
+    __shared__ uint32_t s_prefix;
+    __shared__ int s_remaining, s_eq;
     const int bg = blockIdx.x, b = bg / p.Hkv;
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int SB = p.sparse_block, SBB = SB / kBlockSize;
     const int L = p.seq_lens[b];
     const int nsb = L > 0 ? (L + SB - 1) / SB : 0;
@@ -269,7 +295,8 @@ __global__ __launch_bounds__(kSelThreads) void sparse_select_kernel(SparseParams
     // fewer than want have key > T), found on rel = key - (smallest key) by
     // kSelBits-bit digits from the highest bit in which the keys differ
     uint32_t T = 0u;
-    int need_eq = 0;  // keys == T to take, in block order
+    int need_eq = 0;       // keys == T to take, in block order
+    bool all_eq = true;    // every key == T is taken (no tie to break)
     if (partial) {
         uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
@@ -278,95 +305,100 @@ __global__ __launch_bounds__(kSelThreads) void sparse_select_kernel(SparseParams
                 lo = min(lo, key[i]);
                 hi = max(hi, key[i]);
             }
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
-            hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
-        }
-        if (tid == 0) {
-            s_min = 0xFFFFFFFFu;
-            s_max = 0u;
-        }
-        __syncthreads();
+        lo = wave_minmax<false>(lo);
+        hi = wave_minmax<true>(hi);
         if (lane == 0) {
-            atomicMin(&s_min, lo);
-            atomicMax(&s_max, hi);
+            wmin[wv] = lo;
+            wmax[wv] = hi;
         }
+        for (int i = tid; i < kSelBins; i += kSelThreads) hist[0][i] = 0;
         __syncthreads();
-        const uint32_t kmin = s_min, span = s_max - kmin;
+#pragma unroll
+        for (int i = 0; i < kSelWaves; ++i) {
+            lo = min(lo, wmin[i]);
+            hi = max(hi, wmax[i]);
+        }
+        const uint32_t kmin = lo, span = hi - lo;
         const int nbits = span ? 32 - __clz(span) : 0;
         uint32_t rel[kSelPer];
 #pragma unroll
         for (int i = 0; i < kSelPer; ++i) rel[i] = key[i] - kmin;
         uint32_t prefix = 0u, mask = 0u;
-        int rem = want;
-        for (int top = nbits; top > 0; top -= kSelBits) {
+        int rem = want, eq = -1, buf = 0;
+        for (int top = nbits; top > 0; top -= kSelBits, buf ^= 1) {
             const int shift = top > kSelBits ? top - kSelBits : 0;
             const uint32_t dmask = (1u << (top - shift)) - 1u;
-            for (int i = tid; i < kSelBins; i += kSelThreads) hist[i] = 0;
-            __syncthreads();
+            int* h = hist[buf];
 #pragma unroll
             for (int i = 0; i < kSelPer; ++i)
-                if (kSelPer * tid + i < kept0 && (rel[i] & mask) == prefix)
-                    atomicAdd(&hist[(rel[i] >> shift) & dmask], 1);
+                if (kSelPer * tid + i < kept0 && (rel[i] & mask) == prefix) atomicAdd(&h[(rel[i] >> shift) & dmask], 1);
+            // the other buffer, last read by the previous pass's search, for the next pass
+            for (int i = tid; i < kSelBins; i += kSelThreads) hist[buf ^ 1][i] = 0;
             __syncthreads();
             if (tid < 64) {
                 // lane owns bins 32 lane .. 32 lane + 31; suffix(d) = keys
-                // with digit >= d; the digit is the highest d with
-                // suffix(d) >= rem
+                // with digit >= d, non-increasing in d; the digit is the
+                // highest d with suffix(d) >= rem
                 int c[32], tot = 0;
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
-                    const int4 h = *reinterpret_cast<const int4*>(&hist[32 * lane + 4 * k]);
-                    c[4 * k] = h.x;
-                    c[4 * k + 1] = h.y;
-                    c[4 * k + 2] = h.z;
-                    c[4 * k + 3] = h.w;
-                    tot += h.x + h.y + h.z + h.w;
+                    const int4 v = *reinterpret_cast<const int4*>(&h[32 * lane + 4 * k]);
+                    c[4 * k] = v.x;
+                    c[4 * k + 1] = v.y;
+                    c[4 * k + 2] = v.z;
+                    c[4 * k + 3] = v.w;
+                    tot += v.x + v.y + v.z + v.w;
                 }
-                int incl = tot;  // keys in the bins of this lane and the lanes above
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const int y = __shfl_down(incl, o);
-                    if (lane + o < 64) incl += y;
-                }
-                int run = incl - tot, best = -1, rem_at = rem;
+                const int incl = wave_incl_sum(tot);
+                int run = __builtin_amdgcn_readlane(incl, 63) - incl;  // keys in the bins of the lanes above
+                int sfx[32];
 #pragma unroll
                 for (int k = 31; k >= 0; --k) {
                     run += c[k];
-                    if (best < 0 && run >= rem) {
-                        best = 32 * lane + k;
-                        rem_at = rem - (run - c[k]);
-                    }
+                    sfx[k] = run;
                 }
-                int bb = best;
+                int best = -1, rem_at = rem, cnt = 0;
 #pragma unroll
-                for (int o = 1; o < 64; o <<= 1) bb = max(bb, __shfl_xor(bb, o));
-                if (best >= 0 && best == bb) {
+                for (int k = 0; k < 32; ++k) {  // the last k that qualifies is the highest
+                    const bool ok = sfx[k] >= rem;
+                    best = ok ? 32 * lane + k : best;
+                    rem_at = ok ? rem - (sfx[k] - c[k]) : rem_at;
+                    cnt = ok ? c[k] : cnt;
+                }
+                // the qualifying bins are a prefix: the highest lane holding one has the digit
+                const uint64_t any = __ballot(best >= 0);
+                const int hl = any ? 63 - __clzll((long long)any) : -1;
+                if (lane == hl) {
                     s_prefix = prefix | ((uint32_t)best << shift);
                     s_remaining = rem_at;
-                } else if (bb < 0 && lane == 0) {  // unreachable: suffix(0) counts every key left
+                    s_eq = cnt;
+                } else if (hl < 0 && lane == 0) {  // unreachable: suffix(0) counts every key left
                     s_prefix = prefix;
                     s_remaining = rem;
+                    s_eq = -1;
                 }
             }
             __syncthreads();
             prefix = s_prefix;
             rem = s_remaining;
+            eq = s_eq;
             mask |= dmask << shift;
         }
         T = kmin + prefix;
         need_eq = rem;
+        // keys == T: the last pass's bin count (every key when all are equal)
+        all_eq = (nbits == 0 ? want == kept0 : eq == rem);
     }
     // selection flags in block order: all candidates (want == kept0), none
-    // (want == 0), or key > T and the first need_eq keys == T
-    int eq_cnt = 0;
+    // (want == 0), or key > T and the first need_eq keys == T (a prefix count
+    // in block order, only when some keys == T are left out)
+    int eq_before = 0, tmp;
+    if (partial && !all_eq) {
+        int eq_cnt = 0;
 #pragma unroll
-    for (int i = 0; i < kSelPer; ++i) {
-        const int j = kSelPer * tid + i;
-        eq_cnt += (partial && j < kept0 && key[i] == T) ? 1 : 0;
+        for (int i = 0; i < kSelPer; ++i) eq_cnt += (kSelPer * tid + i < kept0 && key[i] == T) ? 1 : 0;
+        eq_before = block_exclusive_scan(eq_cnt, wsum[0], &tmp);
     }
-    int eq_before = block_exclusive_scan(eq_cnt, wsum, &total);
     bool flag[kSelPer];
     int nflag = 0;
 #pragma unroll
@@ -380,7 +412,7 @@ __global__ __launch_bounds__(kSelThreads) void sparse_select_kernel(SparseParams
                 if (key[i] > T)
                     f = true;
                 else if (key[i] == T) {
-                    f = eq_before < need_eq;
+                    f = all_eq || eq_before < need_eq;
                     ++eq_before;
                 }
             }
@@ -388,8 +420,8 @@ __global__ __launch_bounds__(kSelThreads) void sparse_select_kernel(SparseParams
         flag[i] = f;
         nflag += f ? 1 : 0;
     }
-    const int pos0 = block_exclusive_scan(nflag, wsum, &total);
-    const int nsel = total;  // == want
+    int nsel;
+    const int pos0 = block_exclusive_scan(nflag, wsum[1], &nsel);  // nsel == want
     const int count = nsel + nkept;
     int pos = pos0;
 #pragma unroll
