@@ -630,7 +630,7 @@ def measure(args, spec, partition_size: int, shared: bool, graph: bool, cold: bo
     # ---- K replays of the step recorded in a HIP graph (decode runs under
     # graph capture in serving; the library allocates and synchronises
     # nothing, so the graph holds exactly the step's kernels)
-    graph_ms = None
+    graph_ms = graph10_ms = None
     if graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -644,6 +644,22 @@ def measure(args, spec, partition_size: int, shared: bool, graph: bool, cold: bo
             g.replay()
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - g_start) * 1e3 / args.steps
+        # the same steps, ten per graph: each graph launch leaves the GPU idle
+        # for a few microseconds before its first kernel, which ten steps share
+        g10 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g10):
+            for _ in range(10):
+                one_step()
+        torch.cuda.synchronize()
+        g10.replay()
+        torch.cuda.synchronize()
+        n10 = max(1, args.steps // 10)
+        g_start = time.perf_counter()
+        for _ in range(n10):
+            g10.replay()
+        torch.cuda.synchronize()
+        graph10_ms = (time.perf_counter() - g_start) * 1e3 / (10 * n10)
+        del g10
         # the replays must reproduce an eager step bit for bit
         ref_o, ref_l = out.clone(), lse.clone()
         one_step()
@@ -718,6 +734,7 @@ def measure(args, spec, partition_size: int, shared: bool, graph: bool, cold: bo
         },
         "path": "sparse" if sparse else ("shared_prefix" if shared else "decode"),
         "graph_us_per_step": round(graph_ms * 1e3, 2) if graph_ms is not None else None,
+        "graph_10_steps_us_per_step": round(graph10_ms * 1e3, 2) if graph10_ms is not None else None,
         "step_us_event_timed": {"p10": pct(step_ms, 10), "median": pct(step_ms, 50), "p90": pct(step_ms, 90),
                                 "min": pct(step_ms, 0), "steps": len(step_ms)},
         "decode_us_back_to_back": round(1e3 * dec_loop_ms, 2),
