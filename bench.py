@@ -463,6 +463,89 @@ def sparse_step_bytes(w, sel, SB: int) -> dict:
     return {"kv_selected": kv, "mean_keys": mean_read, "mean_refresh": refresh, "q_out": qo, "total": total}
 
 
+INTERLEAVE_FORMS = ("eager_step", "graph_step", "graph_10_steps", "eager_decode", "graph_decode")
+
+
+def graph_interleave(args, step, dec) -> dict:
+    """Graph launches against eager launches, interleaved: each round runs K
+    eager steps, K replays of a one-step graph, K / 10 replays of a ten-step
+    graph, K eager decodes and K replays of a one-decode graph, each form
+    timed between two synchronisations (microseconds per step or decode).
+    The three graphs are captured once and replayed once before the rounds,
+    so under a kernel trace the decode dispatches follow a fixed layout
+    (summarize_interleave)."""
+    import torch
+
+    K, R = args.steps, args.graph_interleave
+    gs, g10, gd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gs):
+        step()
+    with torch.cuda.graph(g10):
+        for _ in range(10):
+            step()
+    with torch.cuda.graph(gd):
+        dec()
+    torch.cuda.synchronize()
+    gs.replay()
+    g10.replay()
+    gd.replay()
+    torch.cuda.synchronize()
+    forms = {"eager_step": (step, K, 1), "graph_step": (gs.replay, K, 1), "graph_10_steps": (g10.replay, K // 10, 10),
+             "eager_decode": (dec, K, 1), "graph_decode": (gd.replay, K, 1)}
+    rounds = []
+    for _ in range(R):
+        rec = {}
+        for name in INTERLEAVE_FORMS:
+            fn, n, per = forms[name]
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(n):
+                fn()
+            torch.cuda.synchronize()
+            rec[name] = round((time.perf_counter() - t0) * 1e6 / (n * per), 2)
+        rounds.append(rec)
+        log("interleave round %d: %s" % (len(rounds), rec))
+    return {"graph_interleave": {"steps_per_form": K, "rounds": rounds, "unit": "us per step (decode forms: per decode)"}}
+
+
+def summarize_interleave(trace_csv: str, command: str, K: int, W: int, R: int) -> str:
+    """Decode durations and the idle time before each decode, by form and
+    round, from a kernel trace of `bench.py --graph-interleave R`."""
+    import csv
+
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    ks = [(r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows
+          if r["Kernel_Name"].replace("void ", "").startswith("pa::")]
+    dec = [i for i, k in enumerate(ks) if "decode_" in k[0]]
+    lines = ["# Graph launches against eager launches, interleaved", "",
+             "Command (one MI355X, repository root as the working directory):", "", "    " + command, "",
+             "From `%s`: %d warm-up steps, one warm replay of each graph, then %d rounds of the five forms "
+             "(%d steps or decodes each; the ten-step graph %d replays). Microseconds, medians over each "
+             "phase: the decode kernel's duration, and the idle time between the previous kernel's end and "
+             "the decode's start (`gap before`), between the decode's end and the next kernel's start "
+             "(`gap after`), and from one decode's start to the next one's (`period`: a step, or a "
+             "decode, with every gap)." % (os.path.basename(trace_csv), W, R, K, K // 10), "",
+             "| round | form | decodes | decode µs | gap before | gap after | period |",
+             "|---|---|---:|---:|---:|---:|---:|"]
+    i = W + 12
+    for r in range(R):
+        for name in INTERLEAVE_FORMS:
+            n = (K // 10) * 10 if name == "graph_10_steps" else K
+            ids = dec[i:i + n]
+            i += n
+            if len(ids) < n or not ids:
+                lines.append("| %d | %s | trace too short | | | |" % (r + 1, name))
+                continue
+            d = np.array([(ks[j][2] - ks[j][1]) * 1e-3 for j in ids])
+            gb = np.array([(ks[j][1] - ks[j - 1][2]) * 1e-3 for j in ids if j > 0])
+            ga = np.array([(ks[j + 1][1] - ks[j][2]) * 1e-3 for j in ids if j + 1 < len(ks)])
+            per = np.diff(np.array([ks[j][1] for j in ids])) * 1e-3
+            lines.append("| %d | %s | %d | %.2f | %.2f | %.2f | %.2f |" % (
+                r + 1, name, n, np.median(d), np.median(gb), np.median(ga), np.median(per) if len(per) else 0.0))
+    lines.append("")
+    return "\n".join(lines)
+
+
 def measure(args, spec, partition_size: int, shared: bool, graph: bool, cold: bool, cpu_budget: float,
             cpu_budget_1t: float, sparse=None) -> dict:
     """Time one workload: K eager steps between two synchronisations (the
@@ -574,6 +657,12 @@ def measure(args, spec, partition_size: int, shared: bool, graph: bool, cold: bo
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
+
+    if getattr(args, "graph_interleave", 0):
+        if shared or sparse:
+            raise SystemExit("--graph-interleave times the plain decode step")
+        return graph_interleave(args, one_step, lambda: pa.decode_partials(
+            q, kc, vc, table, lens, w.max_seq_len, w.softmax_scale, out, lse, ks, vs, P, ws))
 
     # ---- timed region for the metric: K eager steps between two synchronisations
     torch.cuda.synchronize()
@@ -828,6 +917,11 @@ def main():
                          "traffic for scaling rocprofv3's FETCH_SIZE/WRITE_SIZE counters)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the HBM-traffic summary of two rocprofv3 --pmc counter CSVs and exit")
+    ap.add_argument("--graph-interleave", type=int, default=0, metavar="ROUNDS",
+                    help="instead of the benchmark: ROUNDS rounds of eager steps, one-step graph replays, "
+                         "ten-step graph replays, eager decodes and one-decode graph replays, K each (a JSON line)")
+    ap.add_argument("--summarize-interleave", nargs=2, metavar=("TRACE_CSV", "COMMAND"),
+                    help="print the per-form summary of a kernel trace of --graph-interleave and exit")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "COMMAND"),
                     help="print the kernel-duration summary of a rocprofv3 --kernel-trace CSV made by COMMAND "
                          "and exit")
@@ -837,6 +931,10 @@ def main():
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace[0], args.workload, args.summarize_trace[1],
                               shared=args.shared_prefix))
+        return
+    if args.summarize_interleave:
+        print(summarize_interleave(args.summarize_interleave[0], args.summarize_interleave[1], args.steps,
+                                   args.warmup, args.graph_interleave or 2))
         return
     if args.summarize_counters:
         print(summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.workload,
@@ -880,6 +978,11 @@ def main():
 
     cpu = 0.0 if args.no_cpu_baseline else args.cpu_budget
     cpu1 = 0.0 if args.no_cpu_baseline else args.cpu_budget_1thread
+    if args.graph_interleave:
+        r = measure(args, spec, args.partition_size, False, True, False, 0.0, 0.0)
+        r.update({"workload": spec.name, "device": device_record(pa)})
+        print(json.dumps(r), flush=True)
+        return
     sparse = (args.sparse_block, args.sparse_top) if args.sparse_top else None
     main_res = measure(args, spec, args.partition_size, args.shared_prefix, not args.no_graph, not sparse,
                        0.0 if sparse else cpu, 0.0 if sparse else cpu1, sparse)

@@ -92,3 +92,44 @@ def test_sparse_step_bytes_with_every_block_selected():
         sel2 = np.sort(np.where(sel2 < 0, 1 << 30, sel2), axis=2)
         sel2[sel2 == 1 << 30] = -1
         assert bench.sparse_step_bytes(w, sel2, SB)["kv_selected"] < sb["kv_selected"]
+
+
+def test_interleave_summary_splits_the_trace_by_form(tmp_path):
+    # a synthetic kernel trace in the layout of --graph-interleave: W warm-up
+    # steps, one warm replay of each graph (1 + 10 + 1 decodes), then rounds
+    # of the five forms; the decode of form f in round r lasts 100 + 10 f + r us
+    K, W, R = 20, 3, 2
+    rows, t = [], 0
+
+    def kern(name, dur, gap=0.0):
+        nonlocal t
+        t += int(gap * 1000)
+        rows.append({"Kernel_Name": "void pa::%s(pa::P)" % name, "Start_Timestamp": t, "End_Timestamp": t + int(dur * 1000)})
+        t += int(dur * 1000)
+
+    for _ in range(W + 12):
+        kern("decode_wave_kernel<1, 256, 6, 4>", 50.0)
+    for r in range(R):
+        for f, name in enumerate(bench.INTERLEAVE_FORMS):
+            n = (K // 10) * 10 if name == "graph_10_steps" else K
+            for _ in range(n):
+                if "step" in name:
+                    kern("cache_write_kernel<1, 256, true>", 2.0, gap=8.0 if name == "graph_step" else 0.0)
+                kern("decode_wave_kernel<1, 256, 6, 4>", 100.0 + 10 * f + r, gap=5.0 if name == "graph_decode" else 0.0)
+                if "step" in name:
+                    kern("splitk_reduce_kernel<4>", 4.0)
+    path = tmp_path / "run_kernel_trace.csv"
+    with open(path, "w") as fh:
+        fh.write("Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        for rw in rows:
+            fh.write('"%s",%d,%d\n' % (rw["Kernel_Name"], rw["Start_Timestamp"], rw["End_Timestamp"]))
+    md = bench.summarize_interleave(str(path), "cmd", K, W, R)
+    for r in range(R):
+        for f, name in enumerate(bench.INTERLEAVE_FORMS):
+            n = (K // 10) * 10 if name == "graph_10_steps" else K
+            gap_before = 5.0 if name == "graph_decode" else 0.0
+            assert "| %d | %s | %d | %.2f | %.2f |" % (r + 1, name, n, 100.0 + 10 * f + r, gap_before) in md, (r, name)
+            # period: the decode plus the step's other kernels and gaps
+            period = 100.0 + 10 * f + r + gap_before + (14.0 if name == "graph_step" else 6.0 if "step" in name else 0.0)
+            line = [ln for ln in md.splitlines() if ln.startswith("| %d | %s |" % (r + 1, name))][0]
+            assert line.endswith("| %.2f |" % period), (line, period)
