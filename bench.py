@@ -847,8 +847,8 @@ def measure(args, spec, partition_size: int, shared: bool, graph: bool, cold: bo
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": (None if sparse else committed_traffic(sp, shared)
-                        if not partition_size or partition_size == P else None),
+            # the committed counters were taken at the library's partition size
+            "traffic": None if sparse or partition_size else committed_traffic(sp, shared),
             "kernel_source_digest": kernel_source_digest(sp, shared),
         },
     }
