@@ -167,10 +167,11 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, copy_bytes
         "# HBM traffic of %s on %s" % (kname, workload), "",
         "Counters from two rocprofv3 runs (one MI355X, repository root as the working directory):", "",
     ] + [
-        "    rocprofv3 --pmc %s --output-format csv -d gpurun_out/pmc_%s_%s%s -o run -- python -u bench.py "
+        # the output directory is the one the counter file sits in
+        "    rocprofv3 --pmc %s --output-format csv -d %s -o run -- python -u bench.py "
         "--workload %s%s --steps 5 --warmup 1 --no-cpu-baseline --copy-calibration-mb %d" % (
-            c, c.split("_")[0].lower(), workload, "_shared" if shared else "", workload, extra, copy_bytes >> 20)
-        for c in ("FETCH_SIZE", "WRITE_SIZE")
+            c, os.path.relpath(os.path.dirname(os.path.abspath(path))), workload, extra, copy_bytes >> 20)
+        for c, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv))
     ] + [
         "",
         "Both counters are KiB per dispatch; each is scaled by what it reads for a plain device copy of",

@@ -23,7 +23,7 @@
 //    candidate blocks), 16 candidates per wave; a lane quad holds one
 //    candidate's mean key in registers (interleaved 16-byte pieces, loaded at
 //    once), the query rows are staged 16 at a time in LDS, and each row's dot
-//    product is summed over the quad by two shuffles;
+//    product is summed over the quad by two DPP lane moves;
 //  - sparse_select_kernel: one workgroup per (sequence, kv head): a radix
 //    select over the candidates' scores finds the threshold: on the
 //    order-preserving integer image of the fp32 score less the smallest one
@@ -392,12 +392,12 @@ __global__ __launch_bounds__(kSelThreads) void sparse_select_kernel(SparseParams
     // selection flags in block order: all candidates (want == kept0), none
     // (want == 0), or key > T and the first need_eq keys == T (a prefix count
     // in block order, only when some keys == T are left out)
-    int eq_before = 0, tmp;
+    int eq_before = 0, eq_total;
     if (partial && !all_eq) {
         int eq_cnt = 0;
 #pragma unroll
         for (int i = 0; i < kSelPer; ++i) eq_cnt += (kSelPer * tid + i < kept0 && key[i] == T) ? 1 : 0;
-        eq_before = block_exclusive_scan(eq_cnt, wsum[0], &tmp);
+        eq_before = block_exclusive_scan(eq_cnt, wsum[0], &eq_total);
     }
     bool flag[kSelPer];
     int nflag = 0;
