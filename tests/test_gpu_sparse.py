@@ -194,3 +194,14 @@ def test_all_blocks_selected_is_the_plain_decode(kv):
 def test_full_size_sparse(name, SB, top):
     w = generate(name)
     run_sparse(w, SB, top)
+
+
+@pytest.mark.parametrize("SB, lens, top", [(16, [65536, 40000], 300), (4096, [9000, 4097], 2)])
+def test_sparse_size_limits(SB, lens, top):
+    # 4096 sparse blocks of 16 tokens (the selection's largest candidate set),
+    # and sparse blocks of 4096 tokens (the longest the mean-key kernel stages)
+    spec = scaled("gqa_bf16", B=2, Tq=2, Hq=2, Hkv=1, D=64, seq_lens=(min(lens), max(lens)), cache_dtype="i8",
+                  src_dtype="f32")
+    w = generate(spec, seed=140 + SB, seq_lens=lens)
+    assert oracle.num_sparse_blocks(w.max_seq_len, SB) <= 4096
+    run_sparse(w, SB, top)
