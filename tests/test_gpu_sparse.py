@@ -19,7 +19,7 @@ import torch
 
 import oracle
 import paged_attention_decode_02_amd as pa
-from _gpu import dev, dev_to_host, gpu_cache, gpu_inputs
+from _gpu import dev, dev_to_host, gpu_cache, gpu_inputs, host_to_dev
 from _host import oracle_cache
 from _refs import as_f64
 from workloads import generate, scaled
@@ -205,3 +205,46 @@ def test_sparse_size_limits(SB, lens, top):
     w = generate(spec, seed=140 + SB, seq_lens=lens)
     assert oracle.num_sparse_blocks(w.max_seq_len, SB) <= 4096
     run_sparse(w, SB, top)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+def test_sparse_step_in_a_graph(kv):
+    # cache write, mean-key refresh and the sparse decode recorded in one HIP
+    # graph; new queries between replays; every replay equals an eager step
+    spec = scaled("gqa_bf16", B=3, Tq=2, Hq=12, Hkv=2, D=128, seq_lens=(200, 1500), cache_dtype=kv, src_dtype="f32")
+    w = generate(spec, seed=150)
+    k, v, ks, vs = gpu_cache(w)
+    q, table, lens = gpu_inputs(w)
+    rows = w.step_rows()
+    new_k = host_to_dev(w.k_src[rows], spec.src_dtype)
+    new_v = host_to_dev(w.v_src[rows], spec.src_dtype)
+    new_slots = torch.from_numpy(np.ascontiguousarray(w.slot_mapping[rows])).to(dev())
+    SB, top = 64, 6
+    mk = gpu_mean_keys(w, (k, v, ks, vs), SB)
+    S = pa.sparse_max_selected(w.max_seq_len, SB, top)
+    ws = torch.empty(pa.sparse_workspace_bytes(spec.B, spec.Tq, spec.Hq, spec.Hkv, spec.D, k.dtype, w.max_seq_len,
+                                               SB, top), dtype=torch.uint8, device=dev())
+    out = torch.empty((spec.B, spec.Tq, spec.Hq, spec.D), dtype=torch.float32, device=dev())
+    lse = torch.empty((spec.B, spec.Tq, spec.Hq), dtype=torch.float32, device=dev())
+    sel = torch.empty((spec.B, spec.Hkv, S), dtype=torch.int32, device=dev())
+
+    def step():
+        pa.cache_write(new_k, new_v, new_slots, k, v, ks, vs)
+        pa.sparse_mean_keys(k, table, lens, w.max_seq_len, SB, spec.Tq, mk, ks)
+        pa.decode_sparse(q, k, v, table, lens, w.max_seq_len, w.softmax_scale, mk, SB, top, ks, vs, out=out, lse=lse,
+                         selected=sel, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for i in range(4):
+        q.copy_(q.roll(1, dims=2))  # new queries between replays (eager work)
+        g.replay()
+        torch.cuda.synchronize()
+        got = (out.clone(), lse.clone(), sel.clone())
+        step()  # eager
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], out) and torch.equal(got[1], lse) and torch.equal(got[2], sel), i
