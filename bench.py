@@ -251,24 +251,32 @@ def summarize_trace(trace_csv: str, workload: str, command: str, tail_cold: int 
         # the decode dispatches by bench phase: W warm-up steps, K eager steps
         # (the metric), K eager steps with events between the kernels, K
         # back-to-back decode launches (the roofline), one eager step, W + K
-        # graph replays, one eager check step, then the cache-flushed steps
+        # one-step graph replays, ten-step graph replays (one warm, K / 10
+        # timed), one eager check step, then the cache-flushed steps. The
+        # clock-settle steps before the warm-up vary in number, so the
+        # phases are placed from the end of the trace.
         m_steps = re.search(r"--steps (\d+)", command)
         m_warm = re.search(r"--warmup (\d+)", command)
         if m_steps and m_warm:
             K, W = int(m_steps.group(1)), int(m_warm.group(1))
             d = np.array(dur[dk[0]])
-            g0 = W + 3 * K + 1 + W
-            phases = [("eager steps (the metric's timed region)", W, W + K),
-                      ("eager steps with events between the kernels", W + K, W + 2 * K),
-                      ("back-to-back decode launches (the roofline's launches)", W + 2 * K, W + 3 * K)]
-            if len(d) >= g0 + K + 1:
-                phases.append(("graph replays", g0, g0 + K))
-            if len(d) >= W + 3 * K:
-                lines += ["", "| decode dispatches by phase | dispatches | mean | median |", "|---|---:|---:|---:|"]
+            graph = "--no-graph" not in command
+            n_after = W + 3 * K + 1 + (W + K + 10 + 10 * max(1, K // 10) + 1 if graph else 0) + min(20, K)
+            o = len(d) - n_after  # settle steps
+            g0 = o + W + 3 * K + 1 + W
+            phases = [("eager steps (the metric's timed region)", o + W, o + W + K),
+                      ("eager steps with events between the kernels", o + W + K, o + W + 2 * K),
+                      ("back-to-back decode launches (the roofline's launches)", o + W + 2 * K, o + W + 3 * K)]
+            if graph:
+                phases.append(("graph replays, one step per graph", g0, g0 + K))
+                phases.append(("graph replays, ten steps per graph", g0 + K + 10, g0 + K + 10 + 10 * max(1, K // 10)))
+            if o >= 0:
+                lines += ["", "%d clock-settle steps before the warm-up." % o, "",
+                          "| decode dispatches by phase | dispatches | mean | median |", "|---|---:|---:|---:|"]
                 for name, i0, i1 in phases:
                     x = d[i0:i1]
                     lines.append("| %s | %d | %.2f | %.2f |" % (name, len(x), x.mean(), np.median(x)))
-                lines += ["", "decode_mean_us_roofline_launches: %.2f" % d[W + 2 * K:W + 3 * K].mean()]
+                lines += ["", "decode_mean_us_roofline_launches: %.2f" % d[o + W + 2 * K:o + W + 3 * K].mean()]
     lines.append("")
     return "\n".join(lines)
 
@@ -528,7 +536,8 @@ def summarize_interleave(trace_csv: str, command: str, K: int, W: int, R: int) -
              "decode, with every gap)." % (os.path.basename(trace_csv), W, R, K, K // 10), "",
              "| round | form | decodes | decode µs | gap before | gap after | period |",
              "|---|---|---:|---:|---:|---:|---:|"]
-    i = W + 12
+    per_round = 4 * K + (K // 10) * 10
+    i = len(dec) - R * per_round  # after the clock-settle and warm-up steps and the graphs' warm replays
     for r in range(R):
         for name in INTERLEAVE_FORMS:
             n = (K // 10) * 10 if name == "graph_10_steps" else K
@@ -655,6 +664,18 @@ def measure(args, spec, partition_size: int, shared: bool, graph: bool, cold: bo
         if ev is not None:
             ev[3].record(stream)
 
+    # Clock settle: an idle GPU comes back at a low clock and needs ~20 ms of
+    # sustained work to reach its decode clock (runs of the same step right
+    # after an idle period are 4-6% slower for that long). Untimed steps
+    # until settle_ms have passed, then the W warm-up steps, then the timed
+    # steps; the step count is reported beside the result.
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_ms * 1e-3:
+        for _ in range(10):
+            one_step()
+        torch.cuda.synchronize()
+        settle_steps += 10
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
@@ -823,6 +844,8 @@ def measure(args, spec, partition_size: int, shared: bool, graph: bool, cold: bo
             "splitk_workspace_bytes_per_step": ws_traffic,
         },
         "path": "sparse" if sparse else ("shared_prefix" if shared else "decode"),
+        "clock_settle": {"ms": args.settle_ms, "untimed_steps": settle_steps,
+                         "note": "untimed steps before the warm-up steps, until the GPU leaves its idle clock"},
         "graph_us_per_step": round(graph_ms * 1e3, 2) if graph_ms is not None else None,
         "graph_10_steps_us_per_step": round(graph10_ms * 1e3, 2) if graph10_ms is not None else None,
         "step_us_event_timed": {"p10": pct(step_ms, 10), "median": pct(step_ms, 50), "p90": pct(step_ms, 90),
@@ -890,6 +913,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=30.0,
+                    help="untimed steps for this long before the warm-up steps (the GPU's clock ramp from idle)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--partition-size", type=int, default=0, help="0 = the library's heuristic")
     ap.add_argument("--shared-prefix", action="store_true",

@@ -133,3 +133,31 @@ def test_interleave_summary_splits_the_trace_by_form(tmp_path):
             period = 100.0 + 10 * f + r + gap_before + (14.0 if name == "graph_step" else 6.0 if "step" in name else 0.0)
             line = [ln for ln in md.splitlines() if ln.startswith("| %d | %s |" % (r + 1, name))][0]
             assert line.endswith("| %.2f |" % period), (line, period)
+
+
+def test_trace_summary_places_phases_after_any_number_of_settle_steps(tmp_path):
+    # decode durations by phase in the layout of one bench.py run: S clock-settle
+    # steps (any S), W warm-up, K eager, K with events, K back-to-back decodes,
+    # one eager step, W + K one-step graph replays, 10 + 10 (K / 10) ten-step
+    # graph decodes, one check step, 20 cache-flushed steps
+    K, W = 50, 5
+    phases = [("settle", 37, 300.0), ("warm", W, 290.0), ("eager", K, 171.0), ("events", K, 163.0), ("b2b", K, 162.0),
+              ("one", 1, 280.0), ("gwarm", W, 280.0), ("graph", K, 176.0), ("g10warm", 10, 280.0),
+              ("g10", 10 * (K // 10), 165.0), ("check", 1, 280.0), ("cold", 20, 200.0)]
+    path = tmp_path / "run_kernel_trace.csv"
+    t = 0
+    with open(path, "w") as fh:
+        fh.write("Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        for _, n, dur in phases:
+            for _ in range(n):
+                fh.write('"void pa::decode_wave_kernel<1, 256, 6, 4>(pa::DecodeParams)",%d,%d\n' % (t, t + int(dur * 1000)))
+                t += int(dur * 1000) + 1000
+    cmd = "rocprofv3 -- python -u bench.py --workload long64k_bf16 --steps %d --warmup %d --no-cpu-baseline" % (K, W)
+    md = bench.summarize_trace(str(path), "long64k_bf16", cmd)
+    assert "37 clock-settle steps before the warm-up." in md
+    for label, dur in (("eager steps (the metric's timed region)", 171.0),
+                       ("eager steps with events between the kernels", 163.0),
+                       ("back-to-back decode launches (the roofline's launches)", 162.0),
+                       ("graph replays, one step per graph", 176.0), ("graph replays, ten steps per graph", 165.0)):
+        assert "| %s | 50 | %.2f | %.2f |" % (label, dur, dur) in md, label
+    assert "decode_mean_us_roofline_launches: 162.00" in md
