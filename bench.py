@@ -6,13 +6,17 @@ A step is one pass of the whole decode hot path over one batch: pa_cache_write
 of the B*Tq new tokens' K/V rows, the split-K decode kernel, and (when there
 is more than one partition) the log-sum-exp reduce. Inputs are synthetic and
 seeded (workloads.generate) and already resident in HBM when timing starts.
-The metric times K eager steps between two device synchronisations (the
-host enqueues ahead of the GPU, so this is the GPU's sustained step
-throughput); a second pass of K eager steps with HIP events between the
-kernels gives the per-kernel breakdown and the decode kernel's roofline. K
-replays of the step recorded in one HIP graph (as decode runs in serving) are
-timed too and reported beside it; on this ROCm they are a few percent slower
-than eager launches.
+Untimed steps run for --settle-ms (the GPU's clock ramp from idle), then W
+warm-up steps. The metric times K eager steps between two device
+synchronisations (the host enqueues ahead of the GPU, so this is the GPU's
+sustained step throughput); a second pass of K eager steps with HIP events
+between the kernels gives the per-kernel breakdown, and K back-to-back
+launches of the decode alone its roofline. Replays of the step recorded in a
+HIP graph (as decode runs in serving), one and ten steps per graph, are timed
+too and reported beside it: each graph launch idles the GPU for a few
+microseconds, which ten steps share.
+--sparse-top N times the sparse block-selection step instead, and
+--graph-interleave R alternates the eager and graph forms (no metric line).
 Default workload: long-context decode at 64K tokens per sequence (B=4,
 Hq=24, Hkv=4, D=256, bf16 KV).
 With --shared-prefix (workloads whose sequences share a prefix) the decode
