@@ -260,8 +260,8 @@ int32_t pa_device_cu_count(void);
 
 /* Name of the decode kernel pa_decode launches for these arguments:
  * "decode_wave_kernel" (vector ALU, one query token, small groups),
- * "decode_stream_kernel" (matrix cores, int8 and FP8 caches whose G * Tq rows
- * of a kv head fit one 16-row tile, from groups of 6 at one query token;
+ * "decode_stream_kernel" (matrix cores, int8, FP8 and NVFP4 caches whose
+ * G * Tq rows of a kv head fit one 16-row tile, from groups of 6 at one query token;
  * each wave streams its own blocks; partitions of at most 4096 tokens, a
  * larger given partition_size takes the next kernel), "decode_mfma_kernel"
  * (matrix cores: Tq > 1, groups of 16+ query heads, int8 and FP8 caches with

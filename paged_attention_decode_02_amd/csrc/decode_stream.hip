@@ -1,10 +1,12 @@
 // Split-K paged decode on the matrix cores for one tile of query rows
 // (G * Tq <= 16 rows of a kv head), with every wave streaming its own blocks.
 //
-// The long int8 and FP8 decodes (the split-K paged decode with an int8 KV
-// cache of the vllm-sm70 page, "Why", Attention bullet; FP8 KV dequantised
-// inline, nvllm page, "Acknowledgments", b12x) have one 16-row tile per kv
-// head: 6 query heads at one query token. A workgroup of four waves takes one
+// The long int8, FP8 and NVFP4 decodes (the split-K paged decode with an
+// int8 KV cache of the vllm-sm70 page, "Why", Attention bullet; FP8 KV
+// dequantised inline, nvllm page, "Acknowledgments", b12x; the all-NVFP4
+// stack of the vllm-sm12x-nvfp4-dflash2 page, "What makes this stack
+// different") have one 16-row tile per kv head: 6 query heads at one query
+// token. A workgroup of four waves takes one
 // split-K partition of one kv head; wave w takes blocks w, w + 4, ... of the
 // partition and runs the whole block itself, so the waves never wait for
 // each other inside the loop:
@@ -14,14 +16,17 @@
 //    while block i is computed;
 //  - S^T = K Q^T on v_mfma_f32_16x16x32 (keys read from LDS in the A-operand
 //    layout, int8 codes widened to f16 as 1024 + code + 128, FP8 codes to
-//    bf16; the queries stay in registers as B operands); lane l holds row
+//    bf16, NVFP4 code pairs to f16 times their E4M3 block scale (exact); the
+//    queries stay in registers as B operands); lane l holds row
 //    l % 16 and tokens 4 (l / 16) + 0..3, which is the A-operand layout of
 //    the PV product, so the weights never leave the registers;
 //  - online softmax in log2 units with a per-row reference raised only when a
 //    score beats it by 2^8;
 //  - O += P V on v_mfma_f32_16x16x16 over all D output columns, the V operand
 //    (4 tokens of one column per lane) from LDS: a 4x4 byte transpose inside
-//    each lane quad (int8 / FP8) or the transposing LDS read of gfx950 (bf16).
+//    each lane quad (int8 / FP8) or the transposing LDS read of gfx950 (bf16;
+//    NVFP4 after the block's values are widened with their block scales into
+//    a per-wave f16 tile).
 // Quantised values: weight times value scale in f16, against a per-wave
 // power-of-two reference of the value scales that is raised (O rescaled
 // exactly) when a block's scale passes it, so no pass over the scales is
@@ -41,6 +46,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
@@ -86,6 +92,25 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Order this wave's LDS accesses across lanes (its LDS operations execute in
+// issue order; this keeps the compiler from moving them across).
+__device__ __forceinline__ void wave_lds_order() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// NVFP4: a byte of two E2M1 codes times an f16 block-scale pair, as an f16
+// pair (exact: at most 6 significant bits, 2^-10 to 2688).
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_scaled_f16x2(uint32_t w, f16x2 sc) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, fp4x2_to_f16x2<SEL>(w)) * sc);
+}
+__device__ __forceinline__ f16x2 e4m3_f16x2(uint32_t code) {
+    const _Float16 h = (_Float16)fp8_value(code);
+    return f16x2{h, h};
+}
+
 // Buffer loads whose data goes straight to LDS: lane l's 16 (or 4) bytes at
 // rsrc + voff land at lds + 16 l (4 l); nontemporal. (Plain functions: the
 // builtin is device-only, and a template kernel that names it directly gets
@@ -112,30 +137,44 @@ __device__ __forceinline__ int swz_v(int r) { return CPR >= 16 ? 4 * (r & 3) : C
 
 template <int KVT, int D, int QS, int HPG>
 __global__ __launch_bounds__(64 * stream_waves(KVT, D), 1) void decode_stream_kernel(DecodeParams p) {
-    static_assert(KVT == KV_BF16 || KVT == KV_I8 || KVT == KV_FP8, "bf16, int8 or fp8");
+    static_assert(KVT == KV_BF16 || KVT == KV_I8 || KVT == KV_FP8 || KVT == KV_NVFP4, "bf16, int8, fp8 or nvfp4");
     constexpr bool I8 = KVT == KV_I8;
     constexpr bool F8 = KVT == KV_FP8;
-    constexpr bool QNT = I8 || F8;
+    constexpr bool F4 = KVT == KV_NVFP4;
+    constexpr bool QNT = I8 || F8 || F4;  // codes with a per-(token, kv head) scale
+    constexpr bool H16 = I8 || F4;        // f16 products: queries scaled into f16
     constexpr int E = Elt<KVT>::bytes;
-    constexpr int RB = D * E;          // bytes of one cache row
+    constexpr int RB = kv_code_row_bytes<KVT>(D);  // code bytes of one cache row
     constexpr int CPR = RB / 16;       // 16-byte chunks per row
-    constexpr int RPI = 64 / CPR;      // rows per LDS-destined load instruction
-    constexpr int NI = 16 / RPI;       // such instructions per 16-row tile
+    constexpr int RPI = 64 / CPR;      // rows per LDS-destined load instruction (16 CPR lanes active if > 16)
+    constexpr int NI = RPI > 16 ? 1 : 16 / RPI;  // such instructions per 16-row tile
     constexpr int TILE = 16 * RB;      // bytes of a staged tile
+    // nvfp4: the values of the block being computed, widened to f16 (times
+    // their block scales) in a per-wave row-major tile laid out like a bf16
+    // tile (rows of 2 D bytes, 16-byte chunks swizzled by swz_v), so the PV
+    // takes its operands with the transposing LDS read
+    constexpr int RB16 = 2 * D, CPR16 = RB16 / 16;
     constexpr int KS = D / 32;         // k-steps of the score product
     constexpr int NDT = D / 16;        // 16-column output tiles
     constexpr int NQ = QS == 2 ? 2 : 1;
-    constexpr int NVM = 2 * NI + (QNT ? 2 : 0);  // vector-memory operations per block
+    constexpr int NVM = 2 * NI + (QNT ? 2 : 0) + (F4 ? 2 : 0);  // vector-memory operations per block
     constexpr int NST = stream_stages(KVT, D);    // LDS stages per wave
     constexpr int kW = stream_waves(KVT, D);      // waves per workgroup
     constexpr int WPH = kW / HPG;                 // waves per kv head
-    static_assert(RPI >= 1 && NI * RPI == 16, "tile split");
+    static_assert(RPI >= 1 && (NI * RPI == 16 || (NI == 1 && RPI > 16)), "tile split");
     static_assert(HPG == 1 || HPG == 2 || HPG == 4, "kv heads per workgroup");
     static_assert((NST - 1) * NVM < 64, "vmcnt range");
 
-    // [wave][stage][K, V][16 rows x RB], rows swizzled by 16-byte chunk;
-    // after the block loop the same bytes hold the merge's partial outputs
-    __shared__ __align__(16) unsigned char stg[kW][NST][2][TILE];
+    // per wave: [stage][K, V][16 rows x RB], rows swizzled by 16-byte chunk,
+    // then (nvfp4) the widened value tile [16 rows x RB16]; after the block
+    // loop the same bytes hold the merge's partial outputs ([16 rows][D]
+    // floats: the region is at least that large when waves merge)
+    constexpr int WAVE_TILES = NST * 2 * TILE + (F4 ? 16 * RB16 : 0);
+    constexpr int WAVE_STG = (WPH > 1 && 16 * D * 4 > WAVE_TILES) ? 16 * D * 4 : WAVE_TILES;
+    __shared__ __align__(16) unsigned char stg[kW][WAVE_STG];
+    // nvfp4: [wave][stage][K, V] the block's E4M3 scale plane of the wave's
+    // head (D bytes)
+    __shared__ __align__(16) unsigned char spl[F4 ? kW : 1][NST][2][F4 ? D : 16];
     // quantised: [wave][stage][K, V] the block's 16 scales (dword loads of all
     // 64 lanes land here; lanes past the 64-byte run write zeros)
     __shared__ __align__(16) float sst[kW][NST][2][QNT ? 64 : 1];
@@ -224,7 +263,7 @@ __global__ __launch_bounds__(64 * stream_waves(KVT, D), 1) void decode_stream_ke
     }
     float qpost = p.qk_scale_log2;
     float qscale = 1.0f;
-    if constexpr (I8) {
+    if constexpr (H16) {
         // one power of two for all rows puts max|q| in [2^14, 2^15) (f16)
         qmax = wave_max(qmax);
         const int e2 = qmax > 0.0f ? 14 - ilogbf(qmax) : 0;
@@ -239,11 +278,13 @@ __global__ __launch_bounds__(64 * stream_waves(KVT, D), 1) void decode_stream_ke
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const float x0 = qx[ks][2 * k] * qscale, x1 = qx[ks][2 * k + 1] * qscale;
-            if constexpr (I8) {
+            if constexpr (H16) {
                 hi[k] = pack_f16x2(x0, x1);
                 lo[k] = pack_f16x2(x0 - f16lo(hi[k]), x1 - f16hi(hi[k]));
-                corr += f16lo(hi[k]) + f16hi(hi[k]);
-                if constexpr (QS == 2) corr += f16lo(lo[k]) + f16hi(lo[k]);
+                if constexpr (I8) {
+                    corr += f16lo(hi[k]) + f16hi(hi[k]);
+                    if constexpr (QS == 2) corr += f16lo(lo[k]) + f16hi(lo[k]);
+                }
             } else {
                 hi[k] = pack_bf16_rne(x0, x1);
                 lo[k] = pack_bf16_rne(x0 - bf16_to_f32((uint16_t)hi[k]), x1 - bf16_to_f32((uint16_t)(hi[k] >> 16)));
@@ -268,7 +309,8 @@ __global__ __launch_bounds__(64 * stream_waves(KVT, D), 1) void decode_stream_ke
 
     const int32_t* table = p.block_table + (int64_t)hrow * p.max_blocks + p.kv_begin / kBlockSize;
     const int tok_stride = p.Hkv * RB;                 // bytes between tokens of a block
-    const int blk_bytes = kBlockSize * tok_stride;     // bytes of a KV block (all heads)
+    const int blk_bytes = kBlockSize * p.Hkv * kv_row_bytes<KVT>(D);  // bytes of a KV block (all heads)
+    const int plane_off = kBlockSize * tok_stride + g * D;  // nvfp4: this head's scale plane in a block
     const char* kcache = reinterpret_cast<const char*>(p.k_cache);
     const char* vcache = reinterpret_cast<const char*>(p.v_cache);
     const int j0 = start / kBlockSize, jend = (end + kBlockSize - 1) / kBlockSize;
@@ -286,7 +328,7 @@ __global__ __launch_bounds__(64 * stream_waves(KVT, D), 1) void decode_stream_ke
         voff_k[c] = r * tok_stride + g * RB + 16 * (ldpos ^ swz_k<CPR>(r));
         voff_v[c] = r * tok_stride + g * RB + 16 * (ldpos ^ swz_v<CPR>(r));
     }
-    unsigned char* my_stage = &stg[wv][0][0][0];
+    unsigned char* my_stage = &stg[wv][0];
 
     // physical blocks of this wave's blocks: register k, lane l holds block
     // 64 k + l's (the launcher keeps a wave at 256 blocks or fewer); read per
@@ -309,10 +351,18 @@ __global__ __launch_bounds__(64 * stream_waves(KVT, D), 1) void decode_stream_ke
         const auto rv = range_rsrc(vcache + ph * blk_bytes, blk_bytes);
         unsigned char* kst = my_stage + (stage * 2 + 0) * TILE;
         unsigned char* vst = my_stage + (stage * 2 + 1) * TILE;
+        if (RPI <= 16 || lane < 16 * CPR) {  // a tile of fewer than 1024 bytes: its lanes only
 #pragma unroll
-        for (int c = 0; c < NI; ++c) lds_load16(rk, kst + 1024 * c, voff_k[c]);
+            for (int c = 0; c < NI; ++c) lds_load16(rk, kst + 1024 * c, voff_k[c]);
 #pragma unroll
-        for (int c = 0; c < NI; ++c) lds_load16(rv, vst + 1024 * c, voff_v[c]);
+            for (int c = 0; c < NI; ++c) lds_load16(rv, vst + 1024 * c, voff_v[c]);
+        }
+        if constexpr (F4) {
+            if (lane < D / 16) {  // the D-byte scale planes, 16 bytes a lane
+                lds_load16(rk, &spl[wv][stage][0][0], plane_off + 16 * lane);
+                lds_load16(rv, &spl[wv][stage][1][0], plane_off + 16 * lane);
+            }
+        }
         if constexpr (QNT) {
             const int64_t s0 = (ph * p.Hkv + g) * kBlockSize;
             const auto rks = range_rsrc(p.k_scale + s0, 4 * kBlockSize);
@@ -332,7 +382,30 @@ __global__ __launch_bounds__(64 * stream_waves(KVT, D), 1) void decode_stream_ke
 
         // -------------------------------------------------------------- QK
         f32x4 acc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
-        if constexpr (E == 1) {
+        if constexpr (F4) {
+            // 16 codes per read (8 bytes): dims 64 m + 16 lg .. + 15 of token
+            // l16 = k-steps 2m and 2m + 1, one 16-element block of one scale
+            const unsigned char* sk = &spl[wv][stage][0][0];
+#pragma unroll
+            for (int m = 0; m < KS / 2; ++m) {
+                const int cb = 32 * m + 8 * lg;  // code byte of the first dim
+                const u32x2 raw = *reinterpret_cast<const u32x2*>(kst + l16 * RB + 16 * ((cb >> 4) ^ swz_k<CPR>(l16)) +
+                                                                   (cb & 15));
+                const f16x2 sc2 = e4m3_f16x2(sk[nvfp4_scale_byte(l16, 4 * m + lg)]);
+                u32x4 a[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    a[h] = u32x4{fp4x2_scaled_f16x2<0>(raw[h], sc2), fp4x2_scaled_f16x2<1>(raw[h], sc2),
+                                 fp4x2_scaled_f16x2<2>(raw[h], sc2), fp4x2_scaled_f16x2<3>(raw[h], sc2)};
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int q2 = 0; q2 < NQ; ++q2)
+                        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a[h]),
+                                                                        __builtin_bit_cast(f16x8, qreg[q2][2 * m + h]),
+                                                                        acc[h], 0, 0, 0);
+            }
+        } else if constexpr (E == 1) {
             // 16 codes per read: k-steps 2m and 2m + 1 of token l16
 #pragma unroll
             for (int m = 0; m < KS / 2; ++m) {
@@ -474,7 +547,49 @@ __global__ __launch_bounds__(64 * stream_waves(KVT, D), 1) void decode_stream_ke
         }
 
         // ---------------------------------------------------------------- PV
-        if constexpr (E == 1) {
+        if constexpr (F4) {
+            // widen the block's values into the wave's f16 tile: lane (token
+            // vt, quarter vq) takes dims DQ vq .. DQ vq + DQ - 1, block scale
+            // by block (16 dims, 8 code bytes)
+            constexpr int DQ = D / 4, NB16 = DQ / 16;
+            const int vt = lane >> 2, vq = lane & 3;
+            const unsigned char* sv = &spl[wv][stage][1][0];
+            unsigned char* wt = my_stage + NST * 2 * TILE;
+            wave_lds_order();  // the previous block's reads of the tile are done
+#pragma unroll
+            for (int j = 0; j < NB16; ++j) {
+                const int blk16 = vq * NB16 + j;  // 16-element block of the row
+                const int cb = 8 * blk16;         // its first code byte
+                const u32x2 raw = *reinterpret_cast<const u32x2*>(vst + vt * RB + 16 * ((cb >> 4) ^ swz_v<CPR>(vt)) +
+                                                                   (cb & 15));
+                const f16x2 sc2 = e4m3_f16x2(sv[nvfp4_scale_byte(vt, blk16)]);
+                const u32x4 w0 = u32x4{fp4x2_scaled_f16x2<0>(raw[0], sc2), fp4x2_scaled_f16x2<1>(raw[0], sc2),
+                                       fp4x2_scaled_f16x2<2>(raw[0], sc2), fp4x2_scaled_f16x2<3>(raw[0], sc2)};
+                const u32x4 w1 = u32x4{fp4x2_scaled_f16x2<0>(raw[1], sc2), fp4x2_scaled_f16x2<1>(raw[1], sc2),
+                                       fp4x2_scaled_f16x2<2>(raw[1], sc2), fp4x2_scaled_f16x2<3>(raw[1], sc2)};
+                // dims 16 blk16 .. + 7 and + 8 .. + 15: 16-byte chunks 2 blk16 and 2 blk16 + 1 of the f16 row
+                *reinterpret_cast<u32x4*>(wt + vt * RB16 + 16 * ((2 * blk16) ^ swz_v<CPR16>(vt))) = w0;
+                *reinterpret_cast<u32x4*>(wt + vt * RB16 + 16 * ((2 * blk16 + 1) ^ swz_v<CPR16>(vt))) = w1;
+            }
+            wave_lds_order();  // every lane's widened values are in the tile
+            // transposing LDS read, as for bf16 values: lane 4 r' + c' of a
+            // 16-lane group names token 4 lg + r', dims 16 t + 4 c' .. + 3;
+            // lane i receives dim 16 t + i of the group's 4 tokens
+            const int vr = 4 * lg + (l16 >> 2), cq = l16 & 3;
+#pragma unroll
+            for (int t = 0; t < NDT; ++t) {
+                const int c = 2 * t + (cq >> 1);
+                const unsigned char* src = wt + vr * RB16 + 16 * (c ^ swz_v<CPR16>(vr)) + 8 * (cq & 1);
+                u32x2 bop = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)src));
+                if (MASK) {  // tokens past the end may hold NaN block scales
+                    const int t0 = pos0 + 4 * lg;
+                    bop.x = (t0 + 0 < end ? bop.x & 0x0000FFFFu : 0u) | (t0 + 1 < end ? bop.x & 0xFFFF0000u : 0u);
+                    bop.y = (t0 + 2 < end ? bop.y & 0x0000FFFFu : 0u) | (t0 + 3 < end ? bop.y & 0xFFFF0000u : 0u);
+                }
+                o[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, pa), __builtin_bit_cast(f16x4, bop),
+                                                             o[t], 0, 0, 0);
+            }
+        } else if constexpr (E == 1) {
             // lane (quad q, position i): token 4 lg + i, chunks 4 m + q; after
             // the quad transpose of dword w, dim 16 (4 m + q) + 4 w + i of
             // tokens 4 lg .. 4 lg + 3 = column 4 q + i of tile 4 m + w
@@ -577,7 +692,7 @@ __global__ __launch_bounds__(64 * stream_waves(KVT, D), 1) void decode_stream_ke
     sp += __shfl_xor(sp, 32);
     // output column of tile t for this lane
     auto dim_of = [&](int t) {
-        return E == 1 ? 64 * (t >> 2) + 16 * (l16 >> 2) + 4 * (t & 3) + (l16 & 3) : 16 * t + l16;
+        return (E == 1 && !F4) ? 64 * (t >> 2) + 16 * (l16 >> 2) + 4 * (t & 3) + (l16 & 3) : 16 * t + l16;
     };
     const float vfin = QNT ? vref * (1.0f / kVScaleRoom) : 1.0f;  // undoes the value-scale reference
     if constexpr (WPH == 1) {
@@ -621,7 +736,7 @@ __global__ __launch_bounds__(64 * stream_waves(KVT, D), 1) void decode_stream_ke
     } else {
         // the WPH waves of each head merge through LDS
         __syncthreads();  // every wave is done with its staged tiles: reuse them
-        float* ow = reinterpret_cast<float*>(&stg[wv][0][0][0]);  // [16 rows][D], unnormalised
+        float* ow = reinterpret_cast<float*>(&stg[wv][0]);  // [16 rows][D], unnormalised
         if (lg == 0) {
             mst[wv][0][l16] = mref;
             mst[wv][1][l16] = l;
@@ -649,7 +764,7 @@ __global__ __launch_bounds__(64 * stream_waves(KVT, D), 1) void decode_stream_ke
                 const float wt = exp2_guarded(mst[w0 + k][0][row] - mb);
                 lsum += wt * mst[w0 + k][1][row];
                 lrs += wt * mst[w0 + k][2][row];
-                acc += wt * reinterpret_cast<const float*>(&stg[w0 + k][0][0][0])[row * D + d];
+                acc += wt * reinterpret_cast<const float*>(&stg[w0 + k][0])[row * D + d];
             }
             const float lnorm = QNT ? lsum : lrs;
             const float val = lnorm > 0.0f ? acc / lnorm : 0.0f;
@@ -716,6 +831,7 @@ hipError_t launch_decode_stream(int kv_type, int D, const DecodeParams& p, hipSt
     if (kv_type == KV_BF16) return qs == 1 ? by_d<KV_BF16, 1>(D, p, stream) : by_d<KV_BF16, 2>(D, p, stream);
     if (kv_type == KV_I8) return qs == 1 ? by_d<KV_I8, 1>(D, p, stream) : by_d<KV_I8, 2>(D, p, stream);
     if (kv_type == KV_FP8) return qs == 1 ? by_d<KV_FP8, 1>(D, p, stream) : by_d<KV_FP8, 2>(D, p, stream);
+    if (kv_type == KV_NVFP4) return qs == 1 ? by_d<KV_NVFP4, 1>(D, p, stream) : by_d<KV_NVFP4, 2>(D, p, stream);
     return hipErrorInvalidValue;
 }
 

@@ -111,7 +111,8 @@ int64_t row_bytes(pa_dtype t, int32_t D) {
 // products, the matrix-core one is not). bf16 below 16 rows is a wash (64K:
 // decode 0.7% slower, step 1.3% faster through half the partitions; short
 // variable-length batches 5% slower) and NVFP4 is faster on the vector ALU
-// (250K: decode 92 against 103 us), so both stay there.
+// than on the tiled kernel (250K: decode 92 against 103 us), so both stay
+// off it below a full tile (NVFP4 from G = 6 takes the streaming kernel).
 bool use_mfma(int32_t Tq, int32_t Hq, int32_t Hkv, pa_dtype kv_dtype) {
     if (kv_dtype == PA_F32) return false;
     const int64_t G = Hq / Hkv;
@@ -120,11 +121,15 @@ bool use_mfma(int32_t Tq, int32_t Hq, int32_t Hkv, pa_dtype kv_dtype) {
 
 // The streaming matrix-core kernel (each wave runs its own blocks, keys and
 // values copied straight into LDS) takes the quantised caches when all rows
-// of a kv head fit one 16-row tile; its partitions hold at most
-// kStreamMaxPartition tokens (larger given sizes use the tiled kernel).
+// of a kv head fit one 16-row tile: int8 and FP8 where the matrix cores are
+// chosen, NVFP4 from G = 6 or Tq > 1 (250K tokens, G = 6: decode 90.9 us
+// against 96.7 on the vector ALU); its partitions hold at most
+// kStreamMaxPartition tokens (larger given sizes use the next kernel).
 bool stream_kernel(int32_t Tq, int32_t Hq, int32_t Hkv, pa_dtype kv_dtype) {
-    return use_mfma(Tq, Hq, Hkv, kv_dtype) && (kv_dtype == PA_I8 || kv_dtype == PA_FP8) &&
-           (int64_t)(Hq / Hkv) * Tq <= 16;
+    if ((int64_t)(Hq / Hkv) * Tq > 16) return false;
+    if (kv_dtype == PA_I8 || kv_dtype == PA_FP8) return use_mfma(Tq, Hq, Hkv, kv_dtype);
+    if (kv_dtype == PA_NVFP4) return Tq > 1 || Hq / Hkv >= 6;
+    return false;
 }
 
 // kv heads per workgroup of the streaming kernel, one wave each when 4: the

@@ -128,9 +128,11 @@ hipError_t launch_decode_mfma(int kv_type, int D, int NT, const DecodeParams& p,
 // waves (one per SIMD) with three stages each (85.6 us; eight waves with two
 // stages: 92.1); FP8, whose key widening is heavier, eight waves with two
 // stages (91.0 us; four waves with three: 104.9), the second wave on a SIMD
-// hiding the first's latencies. bf16 with D = 256 (16 KB per stage) fits
-// four waves with two stages.
-constexpr int stream_waves(int kv_type, int D) { return kv_type == 3 ? 8 : 4; }
+// hiding the first's latencies; NVFP4 (keys and values widened with their
+// block scales) likewise eight waves with two stages (90.9 us; four waves
+// with three: 117.3, with two: 128.5). bf16 with D = 256 (16 KB per stage)
+// fits four waves with two stages.
+constexpr int stream_waves(int kv_type, int D) { return kv_type == 3 || kv_type == 4 ? 8 : 4; }
 constexpr int stream_stages(int kv_type, int D) { return kv_type == 2 ? 3 : 2; }
 constexpr int kStreamMaxPartition = 4096;
 hipError_t launch_decode_stream(int kv_type, int D, const DecodeParams& p, hipStream_t stream);

@@ -287,7 +287,9 @@ def test_kernel_name_query(lib):
     assert lib.pa_decode_kernel_name(1, 16, 4, 2) == b"decode_wave_kernel"   # int8, G = 4
     assert lib.pa_decode_kernel_name(8, 24, 4, 1) == b"decode_mfma_kernel"   # Tq > 1
     assert lib.pa_decode_kernel_name(1, 64, 4, 1) == b"decode_mfma_kernel"   # G = 16
-    assert lib.pa_decode_kernel_name(1, 24, 4, 4) == b"decode_wave_kernel"   # nvfp4, G = 6
+    assert lib.pa_decode_kernel_name(1, 24, 4, 4) == b"decode_stream_kernel"  # nvfp4, G = 6
+    assert lib.pa_decode_kernel_name(1, 16, 4, 4) == b"decode_wave_kernel"   # nvfp4, G = 4
+    assert lib.pa_decode_kernel_name(8, 24, 4, 4) == b"decode_mfma_kernel"   # nvfp4, 48 rows
     assert lib.pa_decode_kernel_name(2, 4, 1, 0) == b"decode_valu_kernel"    # fp32 caches
     assert lib.pa_decode_kernel_name(1, 7, 2, 1) == b""
 

@@ -1,6 +1,6 @@
-"""GPU parity of the streaming matrix-core decode (int8 and FP8 caches whose
-G * Tq rows of a kv head fit one 16-row tile: each wave runs its own blocks,
-keys and values copied straight into LDS) against the fp64 oracle.
+"""GPU parity of the streaming matrix-core decode (int8, FP8 and NVFP4 caches
+whose G * Tq rows of a kv head fit one 16-row tile: each wave runs its own
+blocks, keys and values copied straight into LDS) against the fp64 oracle.
 
 Beyond the shared grid in test_gpu_parity.py: value scales spread over 2^12
 (the per-wave value-scale reference is raised and the output rescaled),
@@ -49,19 +49,21 @@ def parity(w, P, tol=2e-2, rel=0.0):
     assert lerr <= 1e-3
 
 
-@pytest.mark.parametrize("kv", ["i8", "fp8"])
+TORCH_KV = {"i8": torch.int8, "fp8": torch.float8_e4m3fn, "nvfp4": torch.float4_e2m1fn_x2}
+
+
+@pytest.mark.parametrize("kv", ["i8", "fp8", "nvfp4"])
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("qdt", ["bf16", "f32"])
 def test_head_sizes_and_query_types(kv, D, qdt):
-    assert pa.decode_kernel_name(1, 12, 2, {"i8": torch.int8, "fp8": torch.float8_e4m3fn}[kv]) == \
-        "decode_stream_kernel"
+    assert pa.decode_kernel_name(1, 12, 2, TORCH_KV[kv]) == "decode_stream_kernel"
     spec = scaled("int8_250k", B=3, Tq=1, Hq=12, Hkv=2, D=D, seq_lens=(1, 3000), cache_dtype=kv, q_dtype=qdt)
     w = generate(spec, seed=50 + D, seq_lens=[1, 777, 3000])
     for P in (64, 512, 0):
         parity(w, P)
 
 
-@pytest.mark.parametrize("kv", ["i8", "fp8"])
+@pytest.mark.parametrize("kv", ["i8", "fp8", "nvfp4"])
 @pytest.mark.parametrize("Tq, G", [(2, 8), (4, 4), (16, 1), (3, 5)])
 def test_causal_rows_in_one_tile(kv, Tq, G):
     spec = scaled("int8_250k", B=4, Tq=Tq, Hq=2 * G, Hkv=2, D=128, seq_lens=(Tq, 900), cache_dtype=kv)
@@ -70,7 +72,7 @@ def test_causal_rows_in_one_tile(kv, Tq, G):
         parity(w, P)
 
 
-@pytest.mark.parametrize("kv", ["i8", "fp8"])
+@pytest.mark.parametrize("kv", ["i8", "fp8", "nvfp4"])
 def test_value_scales_spread_over_many_octaves(kv):
     # value rows scaled per token by 2^u, u uniform in [-6, 6]; a few all-zero
     # key and value rows (scale 0): the waves' value-scale references are
@@ -88,9 +90,10 @@ def test_value_scales_spread_over_many_octaves(kv):
         parity(w, P, tol=2e-2, rel=2e-3)
 
 
-def test_short_partitions_leave_waves_idle():
+@pytest.mark.parametrize("kv", ["i8", "nvfp4"])
+def test_short_partitions_leave_waves_idle(kv):
     # partitions of 16 and 32 tokens: one or two of the four waves have blocks
-    spec = scaled("int8_250k", B=2, Tq=1, Hq=6, Hkv=1, D=128, seq_lens=(5, 200))
+    spec = scaled("int8_250k", B=2, Tq=1, Hq=6, Hkv=1, D=128, seq_lens=(5, 200), cache_dtype=kv)
     w = generate(spec, seed=80, seq_lens=[5, 200])
     for P in (16, 32, 48):
         parity(w, P)
