@@ -28,6 +28,7 @@ __all__ = [
     "library_path", "load", "DTYPE_CODE", "decode_shared_prefix", "shared_prefix_workspace_bytes",
     "validate_decode_args", "validate_cache_write_args", "decode_noalloc", "NOALLOC_SCRATCH_BYTES",
     "sparse_mean_keys", "decode_sparse", "sparse_workspace_bytes", "sparse_max_selected",
+    "Prepared", "prepare_cache_write", "prepare_decode_partials", "prepare_splitk_reduce", "prepare_decode",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -326,6 +327,121 @@ def splitk_reduce(workspace: torch.Tensor, num_partitions: int, partition_size: 
             workspace.numel() * workspace.element_size(), num_partitions, need))
     _check(_L().pa_decode_splitk_reduce(_ptr(workspace), int(num_partitions), int(partition_size), B, Tq, Hq, D,
                                         _ptr(seq_lens), _ptr(out), _code(out), _ptr(lse), _stream(stream, out)))
+
+
+class Prepared:
+    """Library calls whose tensors were checked and whose arguments were
+    marshalled once: calling the object launches the same work again on the
+    current stream of the tensors' device (or on ``stream``) without per-call
+    checks, as a serving loop with buffers at fixed addresses (or a captured
+    graph) would. The tensors must stay alive and keep their shapes and
+    dtypes while it is used; their contents may change between calls."""
+
+    __slots__ = ("_calls", "_device", "_keep", "num_partitions")
+
+    def __init__(self, calls, device: int, keep, num_partitions: int = 1):
+        self._calls = calls  # [(library function, converted arguments before the stream)]
+        self._device = device
+        self._keep = keep  # the tensors behind the pointers
+        self.num_partitions = num_partitions
+
+    def __call__(self, stream=None) -> None:
+        s = stream.cuda_stream if stream is not None else (
+            _raw_stream(self._device) if _raw_stream is not None else torch.cuda.current_stream().cuda_stream)
+        for fn, args in self._calls:
+            rc = fn(*args, s)
+            if rc != 0:
+                _check(rc)
+
+
+_CARG = type(ctypes.byref(ctypes.c_int32()))  # what ctypes.byref returns
+
+
+def _marshal(fn, args):
+    """Convert each argument but the trailing stream to fn's ctypes type once."""
+    conv = []
+    for typ, a in zip(fn.argtypes, args):
+        conv.append(a if isinstance(a, (typ, _CARG)) else typ(a))
+    return fn, tuple(conv)
+
+
+def prepare_cache_write(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None) -> Prepared:
+    """cache_write with its checks and argument marshalling done once."""
+    for t, n in ((k, "k"), (v, "v"), (slot_mapping, "slot_mapping"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _dev(t, n)
+    validate_cache_write_args(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale)
+    nb, bs, Hkv, _ = k_cache.shape
+    call = _marshal(_L().pa_cache_write, (_ptr(k), _ptr(v), _code(k), _ptr(slot_mapping), slot_mapping.numel(),
+                                          _ptr(k_cache), _ptr(v_cache), _code(k_cache), _ptr(k_scale), _ptr(v_scale),
+                                          nb, bs, Hkv, k.shape[-1]))
+    return Prepared([call], k_cache.get_device(), (k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale))
+
+
+def prepare_decode_partials(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, softmax_scale: float,
+                            out: torch.Tensor, lse: Optional[torch.Tensor] = None, k_scale=None, v_scale=None,
+                            partition_size: int = 0, workspace: Optional[torch.Tensor] = None) -> Prepared:
+    """decode_partials with its checks and argument marshalling done once;
+    ``.num_partitions`` is the NP every call produces (ceil(max_seq_len / P))."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (block_table, "block_table"),
+                 (seq_lens, "seq_lens"), (out, "out"), (lse, "lse"), (k_scale, "k_scale"), (v_scale, "v_scale"),
+                 (workspace, "workspace")):
+        _dev(t, n)
+    validate_decode_args(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, out, lse, k_scale, v_scale)
+    B, Tq, Hq, D = q.shape
+    nb, bs, Hkv, _ = k_cache.shape
+    P = partition_size or choose_partition_size(B, Tq, Hq, Hkv, D, k_cache.dtype, max_seq_len)
+    NP = (int(max_seq_len) + P - 1) // P if max_seq_len > 0 else 1
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if NP > 1 and ws_bytes < workspace_bytes(B, Tq, Hq, Hkv, D, k_cache.dtype, max_seq_len, P):
+        raise ValueError("workspace holds %d bytes, %d partitions need %d" % (
+            ws_bytes, NP, workspace_bytes(B, Tq, Hq, Hkv, D, k_cache.dtype, max_seq_len, P)))
+    np_out = ctypes.c_int32(0)
+    call = _marshal(_L().pa_decode, (_ptr(q), _code(q), B, Tq, Hq, Hkv, D, _ptr(k_cache), _ptr(v_cache),
+                                     _code(k_cache), _ptr(k_scale), _ptr(v_scale), nb, bs, _ptr(block_table),
+                                     block_table.shape[1], _ptr(seq_lens), int(max_seq_len), float(softmax_scale),
+                                     int(P), _ptr(out), _code(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                     ctypes.byref(np_out)))
+    prep = Prepared([call], q.get_device(), (q, k_cache, v_cache, block_table, seq_lens, out, lse, k_scale, v_scale,
+                                            workspace, np_out), NP)
+    return prep
+
+
+def prepare_splitk_reduce(workspace: torch.Tensor, num_partitions: int, partition_size: int, seq_lens: torch.Tensor,
+                          out: torch.Tensor, lse: Optional[torch.Tensor] = None) -> Prepared:
+    """splitk_reduce with its checks and argument marshalling done once."""
+    for t, n in ((workspace, "workspace"), (seq_lens, "seq_lens"), (out, "out"), (lse, "lse")):
+        _dev(t, n)
+    if out.dim() != 4 or seq_lens.dtype != torch.int32 or seq_lens.numel() != out.shape[0]:
+        raise ValueError("out must be [B, Tq, Hq, D] and seq_lens int32 [B]")
+    if lse is not None and tuple(lse.shape) != tuple(out.shape[:3]):
+        raise ValueError("lse must be [B, Tq, Hq]")
+    B, Tq, Hq, D = out.shape
+    rows = B * Tq * Hq
+    need = ((rows * num_partitions * D * 4 + 255) // 256 * 256) + rows * num_partitions * 4
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace holds %d bytes, %d partitions need %d" % (
+            workspace.numel() * workspace.element_size(), num_partitions, need))
+    call = _marshal(_L().pa_decode_splitk_reduce, (_ptr(workspace), int(num_partitions), int(partition_size), B, Tq,
+                                                   Hq, D, _ptr(seq_lens), _ptr(out), _code(out), _ptr(lse)))
+    return Prepared([call], out.get_device(), (workspace, seq_lens, out, lse))
+
+
+def prepare_decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, softmax_scale: float,
+                   out: torch.Tensor, lse: torch.Tensor, k_scale=None, v_scale=None, partition_size: int = 0,
+                   workspace: Optional[torch.Tensor] = None) -> Prepared:
+    """decode (the split-K kernel, then the reduce when there is more than one
+    partition) with its checks and argument marshalling done once."""
+    dec = prepare_decode_partials(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, softmax_scale, out, lse,
+                                  k_scale, v_scale, partition_size, workspace)
+    calls, keep = list(dec._calls), [dec._keep]
+    if dec.num_partitions > 1:
+        B, Tq, Hq, D = q.shape
+        P = partition_size or choose_partition_size(B, Tq, Hq, k_cache.shape[2], D, k_cache.dtype, max_seq_len)
+        red = prepare_splitk_reduce(workspace, dec.num_partitions, P, seq_lens, out, lse)
+        calls += red._calls
+        keep.append(red._keep)
+    return Prepared(calls, q.get_device(), keep, dec.num_partitions)
 
 
 def decode_check(block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, num_blocks: int,

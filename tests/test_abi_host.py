@@ -376,3 +376,25 @@ def test_sparse_mean_keys_rejects_bad_arguments(lib):
     assert call(sparse_block=24) == -2
     assert call(D=96) == -4
     assert call(B=0) == 0  # nothing to do, nothing launched
+
+
+def test_prepared_call_marshalling(lib):
+    # arguments converted once to the entry point's ctypes types; the
+    # trailing stream stays for the call
+    import ctypes
+
+    import paged_attention_decode_02_amd as pa
+
+    pa.load()
+    out_np = ctypes.c_int32(0)
+    fn, args = pa._marshal(pa.load().pa_decode, (0x1000, 1, 2, 1, 8, 2, 128, 0x2000, 0x3000, 1, None, None, 64, 16,
+                                                 0x4000, 8, 0x5000, 100, 0.125, 0, 0x6000, 0, None, None, 0,
+                                                 ctypes.byref(out_np)))
+    assert fn is pa.load().pa_decode and len(args) == len(fn.argtypes) - 1
+    assert isinstance(args[0], ctypes.c_void_p) and args[0].value == 0x1000
+    assert isinstance(args[2], ctypes.c_int32) and args[2].value == 2
+    assert isinstance(args[10], ctypes.c_void_p) and args[10].value is None
+    assert isinstance(args[12], ctypes.c_int64) and args[12].value == 64
+    assert isinstance(args[18], ctypes.c_float) and args[18].value == 0.125
+    assert isinstance(args[24], ctypes.c_size_t)
+    assert isinstance(args[25], pa._CARG)
