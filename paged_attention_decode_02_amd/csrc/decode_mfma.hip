@@ -20,9 +20,11 @@
 //    result layout (lane l: tokens 4*(l/16)+i of row l%16) is exactly the
 //    A-operand layout of the PV product, so no shuffle is needed;
 //  - every wave accumulates O[row][d] += P[row][token] V[token][d]
-//    (v_mfma_f32_16x16x16 bf16 / f16) for its quarter of the output dims; the
-//    V operand (4 tokens of one dim per lane) comes from the transposing LDS
-//    read of gfx950 (bf16) or a byte transpose inside each lane quad (int8).
+//    (v_mfma_f32_16x16x32 bf16 / f16 over a block pair's 32 tokens) for its
+//    quarter of the output dims; the V operand (8 tokens of one dim per lane)
+//    comes from the transposing LDS reads of gfx950: the 16-bit one (bf16,
+//    NVFP4 widened to f16) or the 8-bit one (int8 / FP8 codes, both blocks'
+//    tokens in one read).
 // The scores of block j+1 and the PV of block j share one iteration, so one
 // workgroup barrier per block covers the staged tiles and the weights.
 // int8 caches: codes become f16 (1024 + code + 128) by a byte permute, queries
@@ -56,11 +58,6 @@ constexpr float kCodeBias = 1152.0f;  // 1024 + 128
 __device__ __forceinline__ uint32_t f16pair_lo(uint32_t u) { return __builtin_amdgcn_perm(kMagic, u, 0x04010400u); }
 __device__ __forceinline__ uint32_t f16pair_hi(uint32_t u) { return __builtin_amdgcn_perm(kMagic, u, 0x04030402u); }
 
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
-}
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
 }
@@ -72,19 +69,11 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
 __device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)w); }
 __device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
-// 4x4 transpose of bytes inside a lane quad: lane i (= lane & 3) holds
-// elements (i, 0..3) in one dword, afterwards lane j holds (0..3, j).
-__device__ __forceinline__ uint32_t quad_transpose8(uint32_t w, int i) {
-    const int b1 = (i >> 1) & 1, b0 = i & 1;
-    const uint32_t recv = dpp_u32<kDppQuadXor2>(w);
-    const uint32_t u = __builtin_amdgcn_perm(recv, w, b1 ? 0x03020706u : 0x05040100u);
-    const uint32_t pu = dpp_u32<kDppQuadXor1>(u);
-    return __builtin_amdgcn_perm(pu, u, b0 ? 0x03070105u : 0x06020400u);
-}
-
 // 4 x bf16 in LDS, the operand type of the transposing LDS read
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_gcc;
 typedef __attribute__((address_space(3))) bf16x4_gcc lds_bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2_gcc;
+typedef __attribute__((address_space(3))) i32x2_gcc lds_i32x2;
 
 template <int I>
 using ic = std::integral_constant<int, I>;
@@ -138,10 +127,14 @@ __global__ __launch_bounds__(64 * kW, (mfma_min_waves<KVT, D, NT, QS>())) void d
     // f16), values as stored; the row pads spread the operand reads over banks
     constexpr int KRS = 2 * D + 16;  // bytes per staged key row
     constexpr int VRS = (F4 ? 2 * D : RB) + 32;  // bytes per staged value row (nvfp4: f16)
+    // int8 / FP8: 16 bytes between the pair's two value blocks, so that the
+    // 8-bit transposing reads of PV (4 rows of each block per 16 lanes) meet
+    // no bank twice
+    constexpr int VBP = (I8 || F8) ? 16 : 0;
 
     // [stage][block of the pair] ...
     __shared__ __align__(16) unsigned char kst[2][2][kBlockSize][KRS];  // staged keys
-    __shared__ __align__(16) unsigned char vst[2][2][kBlockSize][VRS];  // staged values
+    __shared__ __align__(16) unsigned char vst[2][2][kBlockSize * VRS + VBP];  // staged values, rows of VRS bytes
     __shared__ __align__(16) u32x4 pst[2][NT][64];  // weights of a pair's 32 tokens (A operands of PV)
     __shared__ __align__(16) float sst[2][2][32];   // int8: key then value scales of a block's tokens
     __shared__ __align__(16) float ast[2][NT][16];  // per-row rescale factors
@@ -152,6 +145,7 @@ __global__ __launch_bounds__(64 * kW, (mfma_min_waves<KVT, D, NT, QS>())) void d
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int l16 = lane & 15, lg = lane >> 4;
     const bool owner = wv < NT;  // computes the scores of row tile wv
+    auto vrow = [&](int stage, int h, int row) { return &vst[stage][h][row * VRS]; };
 
     int wg = blockIdx.x;
     const int part = wg % p.NP;
@@ -445,7 +439,7 @@ __global__ __launch_bounds__(64 * kW, (mfma_min_waves<KVT, D, NT, QS>())) void d
                                        : (b2 & 3) == 2 ? fp4x2_to_f32<2>(wd) : fp4x2_to_f32<3>(wd);
                     f[b2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(e.x * sc, e.y * sc));
                 }
-                unsigned char* d4 = &vst[stage][h][row_of(i)][col_of(i) * 4];
+                unsigned char* d4 = vrow(stage, h, row_of(i)) + col_of(i) * 4;
                 if constexpr (GB == 8) {
                     reinterpret_cast<u32x4*>(d4)[0] = u32x4{f[0], f[1], f[2], f[3]};
                     reinterpret_cast<u32x4*>(d4)[1] = u32x4{f[4], f[5], f[6], f[7]};
@@ -456,7 +450,7 @@ __global__ __launch_bounds__(64 * kW, (mfma_min_waves<KVT, D, NT, QS>())) void d
                 }
                 continue;
             }
-            unsigned char* dst = &vst[stage][h][row_of(i)][col_of(i)];
+            unsigned char* dst = vrow(stage, h, row_of(i)) + col_of(i);
             if constexpr (GB == 16)
                 *reinterpret_cast<u32x4*>(dst) = u32x4{src.v[i].w[0], src.v[i].w[1], src.v[i].w[2], src.v[i].w[3]};
             else if constexpr (GB == 8)
@@ -465,9 +459,9 @@ __global__ __launch_bounds__(64 * kW, (mfma_min_waves<KVT, D, NT, QS>())) void d
                 *reinterpret_cast<uint32_t*>(dst) = src.v[i].w[0];
         }
     };
-    // int8 V operand source of this lane: token vtok, 4 codes at dims vdim + 16 nd
-    const int vtok = 4 * lg + (l16 & 3);
-    const int vdim = wv * DW + 4 * (l16 >> 2);
+    // int8 / FP8 V operands: lane 2 r8 + c8 of a 16-lane group names row r8 of
+    // the 8-bit transposing read
+    const int r8 = l16 >> 1, c8 = l16 & 1;
 
     // scores, softmax and weights of pair i into LDS stage i % 2 (owners only).
     // Lane l ends with row l16's tokens 4 lg + 0..3 of both blocks, which is
@@ -587,42 +581,54 @@ __global__ __launch_bounds__(64 * kW, (mfma_min_waves<KVT, D, NT, QS>())) void d
         u32x4 bop[NDT];
 #pragma unroll
         for (int nd = 0; nd < NDT; ++nd) {
+            if constexpr (I8 || F8) {
+                // 8-bit transposing LDS read: lane 2 r8 + c8 of a 16-lane
+                // group names token 4 lg + r8 % 4 of block r8 / 4 of the pair,
+                // dims wv DW + 16 nd + 8 c8 .. + 7; lane i receives dim
+                // wv DW + 16 nd + i of the group's 4 tokens of the first block
+                // (bytes 0..3) and of the second (bytes 4..7): k index 8 lg + e
+                // of the PV product
+                const unsigned char* src = vrow(stage, r8 >> 2, 4 * lg + (r8 & 3)) + wv * DW + 16 * nd + 8 * c8;
+                const u32x2 raw = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)src));
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int pos0 = (jp + h) * kBlockSize;
-                u32x2 w;
-                if constexpr (I8) {
-                    // codes of token vtok, dims vdim + 16 nd .. + 3, transposed in the lane quad
-                    const uint32_t raw = *reinterpret_cast<const uint32_t*>(&vst[stage][h][vtok][vdim + 16 * nd]);
-                    const uint32_t tw = quad_transpose8(raw, l16 & 3) ^ 0x80808080u;
-                    w = u32x2{f16pair_lo(tw), f16pair_hi(tw)};
-                } else if constexpr (F8) {
-                    // as for int8, then the 4 tokens' codes of one dim as two exact f16 pairs
-                    const uint32_t raw = *reinterpret_cast<const uint32_t*>(&vst[stage][h][vtok][vdim + 16 * nd]);
-                    const uint32_t tw = quad_transpose8(raw, l16 & 3);
-                    const pa_f32x2 lo = fp8x2_to_f32<false>(tw), hi = fp8x2_to_f32<true>(tw);
-                    w = u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo.x, lo.y)),
-                              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi.x, hi.y))};
-                    if (!INNER && pos0 + kBlockSize > end) {  // tokens past the end may hold NaN codes
-                        const int t0 = pos0 + 4 * lg;  // element k is token 4*lg + k
-                        w.x = (t0 + 0 < end ? w.x & 0x0000FFFFu : 0u) | (t0 + 1 < end ? w.x & 0xFFFF0000u : 0u);
-                        w.y = (t0 + 2 < end ? w.y & 0x0000FFFFu : 0u) | (t0 + 3 < end ? w.y & 0xFFFF0000u : 0u);
+                for (int h = 0; h < 2; ++h) {
+                    u32x2 w;
+                    if constexpr (I8) {
+                        const uint32_t tw = raw[h] ^ 0x80808080u;
+                        w = u32x2{f16pair_lo(tw), f16pair_hi(tw)};
+                    } else {
+                        // the 4 tokens' codes of one dim as two exact f16 pairs
+                        const pa_f32x2 lo = fp8x2_to_f32<false>(raw[h]), hi = fp8x2_to_f32<true>(raw[h]);
+                        w = u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo.x, lo.y)),
+                                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi.x, hi.y))};
+                        const int pos0 = (jp + h) * kBlockSize;
+                        if (!INNER && pos0 + kBlockSize > end) {  // tokens past the end may hold NaN codes
+                            const int t0 = pos0 + 4 * lg;  // element k is token 4*lg + k
+                            w.x = (t0 + 0 < end ? w.x & 0x0000FFFFu : 0u) | (t0 + 1 < end ? w.x & 0xFFFF0000u : 0u);
+                            w.y = (t0 + 2 < end ? w.y & 0x0000FFFFu : 0u) | (t0 + 3 < end ? w.y & 0xFFFF0000u : 0u);
+                        }
                     }
-                } else {
+                    bop[nd][2 * h] = w.x;
+                    bop[nd][2 * h + 1] = w.y;
+                }
+            } else {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int pos0 = (jp + h) * kBlockSize;
                     // transposing LDS read: lane 4r + c of a 16-lane group names
                     // row (token) 4 lg + r, dims 4c .. 4c + 3 of the 16-dim tile;
                     // lane i receives dim i of the group's 4 tokens
                     const unsigned char* src =
-                        &vst[stage][h][4 * lg + (l16 >> 2)][(wv * DW + 16 * nd + 4 * (l16 & 3)) * 2];
-                    w = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)src));
+                        vrow(stage, h, 4 * lg + (l16 >> 2)) + (wv * DW + 16 * nd + 4 * (l16 & 3)) * 2;
+                    u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)src));
                     if (!INNER && pos0 + kBlockSize > end) {  // tokens past the end may hold anything
                         const int t0 = pos0 + 4 * lg;  // element k is token 4*lg + k
                         w.x = (t0 + 0 < end ? w.x & 0x0000FFFFu : 0u) | (t0 + 1 < end ? w.x & 0xFFFF0000u : 0u);
                         w.y = (t0 + 2 < end ? w.y & 0x0000FFFFu : 0u) | (t0 + 3 < end ? w.y & 0xFFFF0000u : 0u);
                     }
+                    bop[nd][2 * h] = w.x;
+                    bop[nd][2 * h + 1] = w.y;
                 }
-                bop[nd][2 * h] = w.x;
-                bop[nd][2 * h + 1] = w.y;
             }
         }
         // every tile's flag, factors and weights requested at once

@@ -24,9 +24,10 @@
 //    score beats it by 2^8;
 //  - O += P V on v_mfma_f32_16x16x16 over all D output columns, the V operand
 //    (4 tokens of one column per lane) from LDS: a 4x4 byte transpose inside
-//    each lane quad (int8 / FP8) or the transposing LDS read of gfx950 (bf16;
-//    NVFP4 after the block's values are widened with their block scales into
-//    a per-wave f16 tile).
+//    each lane quad (int8), the 8-bit transposing LDS read of gfx950 (FP8, one
+//    read for two column tiles) or its 16-bit one (bf16; NVFP4 after the
+//    block's values are widened with their block scales into a per-wave f16
+//    tile).
 // Quantised values: weight times value scale in f16, against a per-wave
 // power-of-two reference of the value scales that is raised (O rescaled
 // exactly) when a block's scale passes it, so no pass over the scales is
@@ -53,6 +54,8 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_gcc;
 typedef __attribute__((address_space(3))) bf16x4_gcc lds_bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2_gcc;
+typedef __attribute__((address_space(3))) i32x2_gcc lds_i32x2;
 
 constexpr uint32_t kMagic = 0x64646464u;
 constexpr float kCodeBias = 1152.0f;  // 1024 + 128
@@ -132,6 +135,17 @@ template <int CPR>
 __device__ __forceinline__ int swz_k(int r) { return r % CPR; }
 template <int CPR>
 __device__ __forceinline__ int swz_v(int r) { return CPR >= 16 ? 4 * (r & 3) : CPR == 8 ? 4 * ((r >> 1) & 1) : 0; }
+// FP8 value tiles, read by the 8-bit transposing LDS read: a 16-lane group
+// reads tokens 4 lg + 0..3 at chunks t and t + 1 (t even), 8 bytes a lane;
+// the swizzle puts the group's 16 pieces in distinct banks, and those of the
+// groups lg and lg + 1 apart (whether the LDS serves 16 or 32 lanes of the
+// read at a time)
+template <int CPR>
+__device__ __forceinline__ int swz_v8(int r) {
+    return CPR >= 16 ? (2 * (r & 3)) ^ (8 * ((r >> 2) & 1))
+           : CPR == 8 ? (2 * (r & 3)) ^ (2 * ((r >> 2) & 1))
+                      : (2 * ((r >> 1) & 1)) ^ (2 * ((r >> 2) & 1));
+}
 
 }  // namespace
 
@@ -143,6 +157,10 @@ __global__ __launch_bounds__(64 * stream_waves(KVT, D), 1) void decode_stream_ke
     constexpr bool F4 = KVT == KV_NVFP4;
     constexpr bool QNT = I8 || F8 || F4;  // codes with a per-(token, kv head) scale
     constexpr bool H16 = I8 || F4;        // f16 products: queries scaled into f16
+    // FP8 values by the 8-bit transposing read. (For int8 the quad transpose
+    // is kept: with one wave per SIMD the transposing reads made the 250K
+    // decode slower, 85.5 -> 91-101 us, where FP8 gained 91.0 -> 88.5.)
+    constexpr bool VT8 = F8;
     constexpr int E = Elt<KVT>::bytes;
     constexpr int RB = kv_code_row_bytes<KVT>(D);  // code bytes of one cache row
     constexpr int CPR = RB / 16;       // 16-byte chunks per row
@@ -326,7 +344,7 @@ __global__ __launch_bounds__(64 * stream_waves(KVT, D), 1) void decode_stream_ke
     for (int c = 0; c < NI; ++c) {
         const int r = RPI * c + ldrow;
         voff_k[c] = r * tok_stride + g * RB + 16 * (ldpos ^ swz_k<CPR>(r));
-        voff_v[c] = r * tok_stride + g * RB + 16 * (ldpos ^ swz_v<CPR>(r));
+        voff_v[c] = r * tok_stride + g * RB + 16 * (ldpos ^ (VT8 ? swz_v8<CPR>(r) : swz_v<CPR>(r)));
     }
     unsigned char* my_stage = &stg[wv][0];
 
@@ -589,8 +607,33 @@ __global__ __launch_bounds__(64 * stream_waves(KVT, D), 1) void decode_stream_ke
                 o[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, pa), __builtin_bit_cast(f16x4, bop),
                                                              o[t], 0, 0, 0);
             }
+        } else if constexpr (VT8) {
+            // 8-bit transposing LDS read, two 16-column tiles per read: lane
+            // 2 r8 + c8 of a 16-lane group names token 4 lg + r8 % 4 and dims
+            // 16 (t + r8 / 4) + 8 c8 .. + 7; lane i receives dim 16 t + i of
+            // the group's 4 tokens in bytes 0..3 and dim 16 (t + 1) + i in
+            // bytes 4..7
+            const int r8 = l16 >> 1, c8 = l16 & 1, vr = 4 * lg + (r8 & 3);
+#pragma unroll
+            for (int t = 0; t < NDT; t += 2) {
+                const unsigned char* src = vst + vr * RB + 16 * ((t + (r8 >> 2)) ^ swz_v8<CPR>(vr)) + 8 * c8;
+                const u32x2 raw = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)src));
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const pa_f32x2 x0 = fp8x2_to_f32<false>(raw[h]), x1 = fp8x2_to_f32<true>(raw[h]);
+                    u32x2 bop = u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x0.x, x0.y)),
+                                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x1.x, x1.y))};
+                    if (MASK) {  // tokens past the end may hold NaN codes
+                        const int t0 = pos0 + 4 * lg;  // element k is token 4 lg + k
+                        bop.x = (t0 + 0 < end ? bop.x & 0x0000FFFFu : 0u) | (t0 + 1 < end ? bop.x & 0xFFFF0000u : 0u);
+                        bop.y = (t0 + 2 < end ? bop.y & 0x0000FFFFu : 0u) | (t0 + 3 < end ? bop.y & 0xFFFF0000u : 0u);
+                    }
+                    o[t + h] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, pa),
+                                                                     __builtin_bit_cast(f16x4, bop), o[t + h], 0, 0, 0);
+                }
+            }
         } else if constexpr (E == 1) {
-            // lane (quad q, position i): token 4 lg + i, chunks 4 m + q; after
+            // int8: lane (quad q, position i): token 4 lg + i, chunks 4 m + q; after
             // the quad transpose of dword w, dim 16 (4 m + q) + 4 w + i of
             // tokens 4 lg .. 4 lg + 3 = column 4 q + i of tile 4 m + w
             const int i4 = l16 & 3, qd = l16 >> 2, vr = 4 * lg + i4;
@@ -599,21 +642,8 @@ __global__ __launch_bounds__(64 * stream_waves(KVT, D), 1) void decode_stream_ke
                 const u32x4 raw = *reinterpret_cast<const u32x4*>(vst + vr * RB + 16 * ((4 * m + qd) ^ swz_v<CPR>(vr)));
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    uint32_t tw = quad_transpose8(raw[w], i4);
-                    u32x2 bop;
-                    if constexpr (I8) {
-                        tw ^= 0x80808080u;
-                        bop = u32x2{f16pair_lo(tw), f16pair_hi(tw)};
-                    } else {
-                        const pa_f32x2 x0 = fp8x2_to_f32<false>(tw), x1 = fp8x2_to_f32<true>(tw);
-                        bop = u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x0.x, x0.y)),
-                                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x1.x, x1.y))};
-                        if (MASK) {  // tokens past the end may hold NaN codes
-                            const int t0 = pos0 + 4 * lg;  // element k is token 4 lg + k
-                            bop.x = (t0 + 0 < end ? bop.x & 0x0000FFFFu : 0u) | (t0 + 1 < end ? bop.x & 0xFFFF0000u : 0u);
-                            bop.y = (t0 + 2 < end ? bop.y & 0x0000FFFFu : 0u) | (t0 + 3 < end ? bop.y & 0xFFFF0000u : 0u);
-                        }
-                    }
+                    const uint32_t tw = quad_transpose8(raw[w], i4) ^ 0x80808080u;
+                    const u32x2 bop = u32x2{f16pair_lo(tw), f16pair_hi(tw)};
                     o[4 * m + w] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, pa),
                                                                          __builtin_bit_cast(f16x4, bop), o[4 * m + w],
                                                                          0, 0, 0);
@@ -692,7 +722,7 @@ __global__ __launch_bounds__(64 * stream_waves(KVT, D), 1) void decode_stream_ke
     sp += __shfl_xor(sp, 32);
     // output column of tile t for this lane
     auto dim_of = [&](int t) {
-        return (E == 1 && !F4) ? 64 * (t >> 2) + 16 * (l16 >> 2) + 4 * (t & 3) + (l16 & 3) : 16 * t + l16;
+        return I8 ? 64 * (t >> 2) + 16 * (l16 >> 2) + 4 * (t & 3) + (l16 & 3) : 16 * t + l16;
     };
     const float vfin = QNT ? vref * (1.0f / kVScaleRoom) : 1.0f;  // undoes the value-scale reference
     if constexpr (WPH == 1) {
