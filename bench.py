@@ -27,7 +27,10 @@ Printed: ONE JSON line with the metric (algorithmic KV-read GB/s), the step
 time, a roofline object for the decode kernel (its algorithmic bytes per
 launch over its average launch time, measured with HIP events on the launch
 stream) and a CPU baseline (the fp64 oracle timed on this host on a bounded
-sample of the same workload).
+sample of the same workload). The device's streaming-read ceiling (a 2 GiB
+buffer read once per launch with the decode kernels' loads, pa_read_probe) is
+measured after the metric and reported beside the vendor peak: the step's
+GB/s and the decode's roofline as fractions of both.
 """
 from __future__ import annotations
 
@@ -438,6 +441,48 @@ def device_record(pa) -> dict:
         "rocm": rocm, "torch_hip": getattr(torch.version, "hip", None),
         "git_head_at_build": info.get("git_head"), "library_source_digest": info.get("source_digest"),
     }
+
+
+READ_CEILING_WGS_PER_CU = (8, 32, 64)
+
+
+def read_ceiling(pa, mib: int, launches: int) -> dict:
+    """The device's streaming-read ceiling: pa_read_probe (every byte of a
+    mib-MiB buffer read once with the decode kernels' nontemporal 16-byte
+    loads) at 8, 32 and 64 workgroups per CU, each launched `launches` times
+    back to back between two HIP events on the launch stream; the ceiling is
+    the fastest configuration's median launch. The probe's word sums are
+    checked against the buffer's first."""
+    import torch
+
+    n = mib << 20
+    dev = torch.device("cuda:0")
+    buf = torch.randint(-2**31, 2**31 - 1, (n // 4,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    mask = (1 << 32) - 1
+    want = int(buf.to(torch.int64).bitwise_and(mask).sum().item()) & mask
+    per, ok = {}, True
+    for wpc in READ_CEILING_WGS_PER_CU:
+        wgs = wpc * pa.device_cu_count()
+        sink = torch.zeros(wgs, dtype=torch.int32, device=dev)
+        pa.read_probe(buf, sink, stream=stream)
+        ok = ok and (int(sink.to(torch.int64).bitwise_and(mask).sum().item()) & mask) == want
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+        for a, b in ev:
+            a.record(stream)
+            pa.read_probe(buf, sink, stream=stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        per[wpc] = float(np.median([1e3 * a.elapsed_time(b) for a, b in ev]))
+    best = min(per, key=per.get)
+    gbps = n / (per[best] * 1e-6) / 1e9
+    del buf
+    return {"gb_per_s": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBS, 4), "bytes": n,
+            "launches_per_config": launches, "median_us": round(per[best], 2),
+            "median_us_by_workgroups_per_cu": {str(k): round(v, 2) for k, v in per.items()},
+            "kernel": "read_probe_kernel: nontemporal 16-byte buffer loads, 4 in flight per thread, "
+                      "%d workgroups of 256 per CU" % best,
+            "checksum_ok": ok}
 
 
 def pct(a, q):
@@ -947,6 +992,8 @@ def main():
                     help="seconds of single-thread oracle work for the CPU baseline's 1-thread figure")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay side measurement")
+    ap.add_argument("--read-ceiling-mb", type=int, default=2048,
+                    help="buffer of the streaming-read ceiling measurement (MiB; 0 skips it)")
     ap.add_argument("--no-extras", action="store_true",
                     help="default run: skip the side workloads (int8 250K, 64K at 512-token partitions)")
     ap.add_argument("--flush-mb", type=int, default=512, help="flush buffer for the cold-cache side measurement")
@@ -1049,6 +1096,12 @@ def main():
     if cpu_res is not None:
         result["cpu_baseline"] = cpu_res
     result["device"] = device_record(pa)
+    if args.read_ceiling_mb > 0:
+        log("streaming-read ceiling (%d MiB)" % args.read_ceiling_mb)
+        rc = read_ceiling(pa, args.read_ceiling_mb, 20)
+        result["read_ceiling"] = rc
+        result["pct_of_read_ceiling"] = round(100.0 * result["value"] / rc["gb_per_s"], 1)
+        roof["frac_of_read_ceiling"] = round(roof["achieved"] / rc["gb_per_s"], 4)
     if not explicit_workload and not args.no_extras and not changes and not args.partition_size and not sparse:
         for key, name, P, with_cpu, sp_sel in EXTRAS:
             log("side workload %s (%s, P=%s)" % (key, name, P or "heuristic"))

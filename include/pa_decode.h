@@ -397,6 +397,25 @@ int pa_decode_noalloc(const void* q, pa_dtype q_dtype, int32_t B, int32_t Tq, in
                       void* stream);
 
 /* Message for the calling thread's last non-zero return ("" if none). */
+/*
+ * pa_read_probe — measurement helper, not part of the decode path: the
+ * streaming-read ceiling against which a decode's read rate is judged (the
+ * decode is a streaming scan of its KV bytes). Reads every byte of buf once
+ * with the decode kernels' load (nontemporal 16-byte buffer loads) in
+ * `workgroups` workgroups of 256 threads, each taking every workgroups-th
+ * 16 KB segment, and writes into sink[i] the 32-bit wrap-around sum of the
+ * 32-bit words workgroup i read: the sum over sink[0 .. workgroups - 1] is
+ * the sum of every word of buf, a check that each was read exactly once.
+ *   buf         device, 16-byte aligned; bytes a multiple of 16 (0: sink zeros)
+ *   sink        device, workgroups uint32 (the caller's)
+ *   workgroups  1 .. 65535 (the caller sizes the grid to the device: 8 to 64
+ *               per CU all read at 6.9-7.1 TB/s on an MI355X)
+ * Errors: PA_ERR_NULL (buf with bytes > 0, or sink NULL), PA_ERR_ALIGN,
+ * PA_ERR_SHAPE (bytes not a multiple of 16, workgroups out of range),
+ * PA_ERR_LAUNCH. Allocates nothing; capture-safe like every entry point.
+ */
+int pa_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups, void* stream);
+
 const char* pa_last_error(void);
 
 #ifdef __cplusplus

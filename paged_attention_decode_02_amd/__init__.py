@@ -29,6 +29,7 @@ __all__ = [
     "validate_decode_args", "validate_cache_write_args", "decode_noalloc", "NOALLOC_SCRATCH_BYTES",
     "sparse_mean_keys", "decode_sparse", "sparse_workspace_bytes", "sparse_max_selected",
     "Prepared", "prepare_cache_write", "prepare_decode_partials", "prepare_splitk_reduce", "prepare_decode",
+    "read_probe",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -47,7 +48,7 @@ EXPORTS = (
     "pa_choose_partition_size", "pa_decode_check", "pa_cache_write_check", "pa_last_error",
     "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes", "pa_choose_partition_size_for_cus",
     "pa_device_cu_count", "pa_decode_kernel_name", "pa_decode_noalloc", "pa_sparse_mean_keys", "pa_decode_sparse",
-    "pa_decode_sparse_workspace_bytes",
+    "pa_decode_sparse_workspace_bytes", "pa_read_probe",
 )
 
 # size of the library-owned scratch of pa_decode_noalloc (PA_NOALLOC_SCRATCH_BYTES)
@@ -112,6 +113,8 @@ def load():
         lib.pa_decode_sparse.restype = ctypes.c_int
         lib.pa_decode_sparse_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32, I32, I32]
         lib.pa_decode_sparse_workspace_bytes.restype = SZ
+        lib.pa_read_probe.argtypes = [P, SZ, P, I32, P]
+        lib.pa_read_probe.restype = ctypes.c_int
         lib.pa_last_error.argtypes = []
         lib.pa_last_error.restype = ctypes.c_char_p
         _lib = lib
@@ -456,6 +459,20 @@ def decode_check(block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len:
     _check(load().pa_decode_check(_ptr(block_table), max_blocks, _ptr(seq_lens), B, int(max_seq_len),
                                   int(num_blocks), _ptr(status), _stream(stream, status)))
     return status
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> torch.Tensor:
+    """Streaming-read ceiling probe (measurement only): reads every byte of the
+    contiguous device tensor buf once with the decode kernels' loads, in
+    sink.numel() workgroups; sink (uint32 or int32, device) receives per
+    workgroup the wrap-around sum of the 32-bit words it read. Unsynchronised."""
+    for t, n in ((buf, "buf"), (sink, "sink")):
+        _dev(t, n)
+    if sink.dtype not in (torch.int32, torch.uint32):
+        raise ValueError("sink must be int32 or uint32")
+    nbytes = buf.numel() * buf.element_size()
+    _check(load().pa_read_probe(_ptr(buf), nbytes, _ptr(sink), sink.numel(), _stream(stream, buf)))
+    return sink
 
 
 def cache_write_check(slot_mapping: torch.Tensor, num_blocks: int, block_size: int = 16,

@@ -534,6 +534,16 @@ int32_t pa_choose_partition_size(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv,
 
 int32_t pa_device_cu_count(void) { return device_cus(); }
 
+int pa_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups, void* stream) {
+    if (!sink || (bytes > 0 && !buf)) return fail(PA_ERR_NULL, "sink (and buf when bytes > 0) must be non-NULL");
+    if (bytes % 16) return fail(PA_ERR_SHAPE, "bytes=%zu must be a multiple of 16", bytes);
+    if (workgroups < 1 || workgroups > 65535) return fail(PA_ERR_SHAPE, "workgroups=%d not in 1 .. 65535", workgroups);
+    if (!aligned16(buf)) return fail(PA_ERR_ALIGN, "buf must be 16-byte aligned");
+    hipError_t e = pa::launch_read_probe(buf, (int64_t)bytes, sink, workgroups, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "read_probe launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 const char* pa_decode_kernel_name(int32_t Tq, int32_t Hq, int32_t Hkv, pa_dtype kv_dtype) {
     if (Tq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || !kv_supported(kv_dtype)) return "";
     if (kv_dtype == PA_F32) return "decode_valu_kernel";

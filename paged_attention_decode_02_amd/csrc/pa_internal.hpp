@@ -147,6 +147,9 @@ hipError_t launch_sparse_select(const SparseParams& p, hipStream_t stream);
 constexpr int kSparseMaxBlocks = 4096;  // sparse blocks per sequence at most
 constexpr int kSparseMaxBlockTokens = 4096;  // tokens per sparse block at most
 
+// Read-bandwidth probe (every 16-byte chunk of buf once, per-workgroup word sums into sink).
+hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int workgroups, hipStream_t stream);
+
 // Valid head-chunk widths of the VALU decode instances.
 bool decode_valu_has_gt(int GT);
 

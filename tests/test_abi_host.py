@@ -398,3 +398,17 @@ def test_prepared_call_marshalling(lib):
     assert isinstance(args[18], ctypes.c_float) and args[18].value == 0.125
     assert isinstance(args[24], ctypes.c_size_t)
     assert isinstance(args[25], pa._CARG)
+
+
+@pytest.mark.parametrize("args, code", [
+    ((A, 4096, None, 8), -1),                         # no sink
+    ((None, 4096, A, 8), -1),                         # no buffer to read
+    ((A, 4100, A, 8), -2),                            # not whole 16-byte chunks
+    ((A, 4096, A, 0), -2),                            # no workgroup
+    ((A, 4096, A, 65536), -2),
+    ((ctypes.c_void_p(0x1008), 4096, A, 8), -7),      # misaligned buffer
+])
+def test_read_probe_rejects_bad_arguments(lib, args, code):
+    rc = lib.pa_read_probe(*args, None)
+    assert rc == code, lib.pa_last_error()
+    assert lib.pa_last_error()
