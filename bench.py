@@ -74,6 +74,19 @@ def algorithmic_bytes(w) -> dict:
             "total": kv + scales + table + q + out}
 
 
+def algorithmic_flops(w) -> int:
+    """Multiply-adds of the attention itself, counted as 2 flops each: QK and
+    PV take 2 D each per (query row, visible key), 4 D in all; query token t
+    of sequence b sees L_b - Tq + t + 1 keys (the causal rule counted
+    exactly, not bounded by L_b)."""
+    sp = w.spec
+    keys = 0
+    for L in w.seq_lens.astype(np.int64):
+        for t in range(sp.Tq):
+            keys += max(0, int(L) - sp.Tq + t + 1)
+    return 4 * sp.D * sp.Hq * keys
+
+
 _COMMON = ("pa_device.hpp", "pa_internal.hpp")
 
 
@@ -895,6 +908,8 @@ def measure(args, spec, partition_size: int, shared: bool, graph: bool, cold: bo
             "num_partitions": None if shared else state["np"],
             "algorithmic_bytes_per_step": step_bytes,
             "per_sequence_bytes_per_step": ab["total"],
+            "algorithmic_flops_per_step": None if sparse else algorithmic_flops(w),
+            "flop_per_byte": None if sparse else round(algorithmic_flops(w) / step_bytes, 2),
             "shared_prefix": sp.shared_prefix,
             "prefix_partition": args.prefix_partition if shared else None,
             "tail_partition": args.tail_partition if shared else None,

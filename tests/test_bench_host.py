@@ -26,6 +26,19 @@ def test_algorithmic_bytes_of_the_64k_workload():
     assert 4 * 65536 * full.Hkv * full.D * 2 * 2 == 1073741824
 
 
+def test_algorithmic_flops_count_each_query_tokens_visible_keys():
+    # one decode token: 4 D Hq flops per key of every sequence; the 64K
+    # workload's 4 x 65536 keys x 24 heads x 256 x 4 = 6.44 GFLOP
+    w = generate(scaled("long64k_bf16", D=8, Hq=2, Hkv=1, seq_lens=(100, 130)))
+    assert bench.algorithmic_flops(w) == 4 * 8 * 2 * int(w.seq_lens.sum())
+    full = SPECS["long64k_bf16"]
+    assert 4 * full.D * full.Hq * 4 * 65536 == 6442450944
+    # Tq query tokens: token t sees L - Tq + t + 1 keys (L - 3, L - 2, L - 1, L for Tq = 4)
+    w = generate(scaled("verify_bf16", B=2, Tq=4, Hq=4, Hkv=2, D=16, seq_lens=(50, 60), shared_prefix=0))
+    keys = sum(4 * int(L) - 6 for L in w.seq_lens)
+    assert bench.algorithmic_flops(w) == 4 * 16 * 4 * keys
+
+
 def test_unique_bytes_count_the_shared_prefix_once():
     for kv in ("bf16", "i8", "nvfp4"):
         spec = scaled("verify_bf16", B=3, Tq=2, Hq=4, Hkv=2, D=64, seq_lens=(300, 400), shared_prefix=256,
