@@ -15,9 +15,10 @@
 // 64 / CW) takes partitions s, s + SL, ... . Each lane accumulates its
 // partitions in increasing order and the slices are combined by a fixed
 // butterfly, so the result is deterministic. The first kPre partitions of
-// every lane (and the LSEs that give the row's maximum) are requested before
-// the row's length is known, so a row costs one memory round trip; partitions
-// past the row's visible length are masked afterwards.
+// every lane, with their LSEs, are requested before the row's length is
+// known, and the row's maximum is taken from them, so a row of up to kPre
+// SL partitions costs one memory round trip; partitions past the row's
+// visible length are masked afterwards.
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -176,14 +177,18 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceParams p) {
             lv[k] = lse_row[i];
         }
     }
-    float lm = lane < p.NP ? lse_row[lane] : -INFINITY;  // the row's maximum, 64 partitions per load
     // partitions that hold keys of the row (all of them when every partition
     // was written, which the shared-prefix decode's two passes do)
     const int n = p.seq_lens[hl] - p.Tq + t + 1;
     const int np = p.all_parts ? p.NP : n > 0 ? min((n + p.P - 1) / p.P, p.NP) : 0;
 
-    float mx = lane < np ? lm : -INFINITY;
-    for (int i = lane + 64; i < np; i += 64) mx = fmaxf(mx, lse_row[i]);
+    // the row's largest LSE: the preloaded partitions (kPre SL of them, every
+    // partition of most rows) from registers, any later ones loaded here
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kPre; ++k)
+        if (s + k * SL < np) mx = fmaxf(mx, lv[k]);
+    for (int i = kPre * SL + lane; i < np; i += 64) mx = fmaxf(mx, lse_row[i]);
     const float M = wave_max(mx);
     const float mref = M == -INFINITY ? 0.0f : M;
 
