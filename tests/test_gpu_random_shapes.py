@@ -15,7 +15,7 @@ from workloads import generate, scaled
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 40
+N_CASES = 200
 
 
 def case(i: int) -> dict:
