@@ -2,9 +2,10 @@
 and tiled matrix-core, fp32) chosen by the library's own rule, against the
 fp64 oracle, with random cache and query dtypes, head sizes, group sizes,
 query tokens, ragged lengths (some shorter than a block, some a whole number
-of blocks) and given or heuristic partition sizes, some with 1% peaked keys.
-The configurations are drawn once from a fixed seed, so a failure names a
-reproducible case."""
+of blocks) and given or heuristic partition sizes, some with 1% peaked keys;
+and the shared-prefix call on random batches, prefixes and partition sizes
+(its reference is the same plain definition). The configurations are drawn
+from fixed seeds, so a failure names a reproducible case."""
 from __future__ import annotations
 
 import numpy as np
@@ -47,3 +48,37 @@ def test_random_shape(i):
     print("random case %d: %s" % (i, c), flush=True)
     w = generate(spec, seed=2000 + i, seq_lens=c["lens"])
     run_workload(w, partition_size=c["P"])
+
+
+# ------------------------------------------------------------ shared prefix
+N_SHARED = 60
+
+
+def shared_case(i: int) -> dict:
+    rng = np.random.default_rng(5000 + i)
+    kv = str(rng.choice(["bf16", "i8", "fp8", "nvfp4"]))
+    D = int(rng.choice([64, 128, 256]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16]))
+    Tq = int(rng.choice([1, 1, 2, 3, 5, 8, 16]))
+    B = int(rng.integers(1, 7))
+    prefix = 16 * int(rng.integers(1, 80))
+    # every query token after the prefix: prefix + Tq <= L
+    lens = [int(x) for x in rng.integers(prefix + Tq, prefix + Tq + int(rng.integers(1, 1500)), size=B)]
+    pp = int(rng.choice([0, 0, 16, 64, 16 * int(rng.integers(1, 40))]))
+    tp = int(rng.choice([0, 0, 16, 128, 16 * int(rng.integers(1, 40))]))
+    return dict(kv=kv, D=D, Hkv=Hkv, Hq=G * Hkv, Tq=Tq, B=B, prefix=prefix, lens=lens, pp=pp, tp=tp,
+                q=str(rng.choice(["f32", "bf16"])))
+
+
+@pytest.mark.parametrize("i", range(N_SHARED))
+def test_random_shared_prefix(i):
+    from test_gpu_shared_prefix import run_shared
+
+    c = shared_case(i)
+    spec = scaled("verify_bf16", name="random_shared%d" % i, B=c["B"], Tq=c["Tq"], Hq=c["Hq"], Hkv=c["Hkv"],
+                  D=c["D"], seq_lens=(min(c["lens"]), max(c["lens"])), shared_prefix=c["prefix"],
+                  cache_dtype=c["kv"], q_dtype=c["q"], src_dtype="f32")
+    print("random shared-prefix case %d: %s" % (i, c), flush=True)
+    w = generate(spec, seed=6000 + i, seq_lens=c["lens"])
+    run_shared(w, parts=((c["pp"], c["tp"]),))
