@@ -3,9 +3,12 @@ and tiled matrix-core, fp32) chosen by the library's own rule, against the
 fp64 oracle, with random cache and query dtypes, head sizes, group sizes,
 query tokens, ragged lengths (some shorter than a block, some a whole number
 of blocks) and given or heuristic partition sizes, some with 1% peaked keys;
-and the shared-prefix call on random batches, prefixes and partition sizes
-(its reference is the same plain definition). The configurations are drawn
-from fixed seeds, so a failure names a reproducible case."""
+the shared-prefix call on random batches, prefixes and partition sizes (its
+reference is the same plain definition); and the sparse block-selection decode
+on random sparse-block sizes, selection sizes and empty sequences (the
+selection checked against its validity rule, the output against the oracle on
+the GPU's own selection). The configurations are drawn from fixed seeds, so a
+failure names a reproducible case."""
 from __future__ import annotations
 
 import numpy as np
@@ -82,3 +85,38 @@ def test_random_shared_prefix(i):
     print("random shared-prefix case %d: %s" % (i, c), flush=True)
     w = generate(spec, seed=6000 + i, seq_lens=c["lens"])
     run_shared(w, parts=((c["pp"], c["tp"]),))
+
+
+# ------------------------------------------------------------ sparse selection
+N_SPARSE = 60
+
+
+def sparse_case(i: int) -> dict:
+    rng = np.random.default_rng(7000 + i)
+    kv = str(rng.choice(["bf16", "i8", "fp8", "nvfp4"]))
+    D = int(rng.choice([64, 128, 256]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 6, 8, 12]))
+    Tq = int(rng.choice([1, 1, 2, 4, 8]))
+    B = int(rng.integers(1, 5))
+    SB = int(rng.choice([16, 32, 64, 128, 256]))
+    lens = [int(x) for x in rng.integers(Tq, 3000, size=B)]
+    if rng.random() < 0.2:  # an empty sequence
+        lens[0] = 0
+    top = int(rng.choice([1, 2, 5, 17, 64, 200]))
+    P = int(rng.choice([0, 0, 64, 16 * int(rng.integers(1, 64))]))
+    return dict(kv=kv, D=D, Hkv=Hkv, Hq=G * Hkv, Tq=Tq, B=B, SB=SB, lens=lens, top=top, P=P,
+                peaked=bool(rng.random() < 0.3))
+
+
+@pytest.mark.parametrize("i", range(N_SPARSE))
+def test_random_sparse(i):
+    from test_gpu_sparse import run_sparse
+
+    c = sparse_case(i)
+    spec = scaled("gqa_bf16", name="random_sparse%d" % i, B=c["B"], Tq=c["Tq"], Hq=c["Hq"], Hkv=c["Hkv"], D=c["D"],
+                  seq_lens=(min(c["lens"]), max(c["lens"])), cache_dtype=c["kv"], src_dtype="f32",
+                  peaked_frac=0.01 if c["peaked"] else 0.0)
+    print("random sparse case %d: %s" % (i, c), flush=True)
+    w = generate(spec, seed=8000 + i, seq_lens=c["lens"])
+    run_sparse(w, c["SB"], c["top"], P=c["P"])
