@@ -395,6 +395,20 @@ def test_mfma_rows(kv, D, G, Tq):
     run_workload(w, partition_size=256)
 
 
+# the largest group (64 query heads per kv head) and query tile (16 tokens)
+# the library takes, alone and together (1024 rows per kv head), on every
+# cache type, with ragged lengths and a row shorter than the query tile
+@pytest.mark.parametrize("kv", ["f32", "bf16", "i8", "fp8", "nvfp4"])
+@pytest.mark.parametrize("G, Tq, D", [(64, 1, 256), (1, 16, 256), (64, 16, 128), (64, 16, 64)])
+def test_group_and_query_token_limits(kv, G, Tq, D):
+    spec = scaled("verify_bf16", name="limits_%s_G%d_T%d" % (kv, G, Tq), B=2, Tq=Tq, Hq=G, Hkv=1, D=D,
+                  seq_lens=(Tq, 400), shared_prefix=0, cache_dtype=kv, src_dtype="f32",
+                  q_dtype="f32" if kv == "f32" else "bf16")
+    w = generate(spec, seed=G + Tq + D, seq_lens=[Tq, 400])
+    run_workload(w, partition_size=0)
+    run_workload(w, partition_size=64, check_cache=False)
+
+
 @pytest.mark.parametrize("qdt", ["f32", "bf16"])
 @pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "nvfp4"])
 def test_mfma_query_dtype_and_partitions(qdt, kv):
