@@ -701,7 +701,15 @@ __global__ __launch_bounds__(64 * kW, (mfma_min_waves<KVT, D, NT, QS>())) void d
             load_blk(ring[X][1], ph1);
         }
         __syncthreads();
-        if (owner && (FULL || i + 1 < npair)) scores(i + 1, std::integral_constant<bool, FULL && X == 0>{});
+        // the owners' scores and softmax are the per-pair chain that every
+        // wave's next barrier waits on: they issue ahead of the other
+        // workgroup's waves on the same SIMD (measured: quantised verify
+        // decodes 1.5-5% faster, bf16 unchanged)
+        if (owner && (FULL || i + 1 < npair)) {
+            __builtin_amdgcn_s_setprio(3);
+            scores(i + 1, std::integral_constant<bool, FULL && X == 0>{});
+            __builtin_amdgcn_s_setprio(0);
+        }
         values(i, full);
         tp0 = tn0;
         tp1 = tn1;
