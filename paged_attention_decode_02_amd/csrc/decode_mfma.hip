@@ -683,12 +683,18 @@ __global__ __launch_bounds__(64 * kW, (mfma_min_waves<KVT, D, NT, QS>())) void d
     // valid row's causal range (at most Tq - 1 <= 15 tokens short of the end):
     // its scores need no mask either. In the second, pair i + 1 may reach the
     // block before the last, within that causal margin.
+    // issue priorities of the other phases per cache type (measured): bf16
+    // stores its staged tiles and requests the next ones ahead of the other
+    // workgroup's waves, the quantised caches run their PV ahead
+    constexpr int kStagePrio = KVT == KV_BF16 ? 2 : 0;
+    constexpr int kPvPrio = QNT ? 1 : 0;
     auto iter = [&](int i, auto xc, auto full) __attribute__((always_inline)) {
         constexpr int X = decltype(xc)::value;  // slot of pair i: i % S2
         constexpr int Y = (X + 1) % S2;         // slot of pair i + 1
         constexpr bool FULL = decltype(full)::value;
         const int jn = j0 + 2 * (i + 1 + S2);
         const int tn0 = table[jn < jend ? jn : jend - 1], tn1 = table[jn + 1 < jend ? jn + 1 : jend - 1];
+        if constexpr (kStagePrio != 0) __builtin_amdgcn_s_setprio(kStagePrio);
         if (FULL || i + 1 < npair) {
             store_k(ring[Y][0], (i + 1) & 1, 0);
             store_k(ring[Y][1], (i + 1) & 1, 1);
@@ -700,17 +706,19 @@ __global__ __launch_bounds__(64 * kW, (mfma_min_waves<KVT, D, NT, QS>())) void d
             load_blk(ring[X][0], ph0);
             load_blk(ring[X][1], ph1);
         }
+        if constexpr (kStagePrio != 0) __builtin_amdgcn_s_setprio(0);
         __syncthreads();
         // the owners' scores and softmax are the per-pair chain that every
         // wave's next barrier waits on: they issue ahead of the other
-        // workgroup's waves on the same SIMD (measured: quantised verify
-        // decodes 1.5-5% faster, bf16 unchanged)
+        // workgroup's waves on the same SIMD
         if (owner && (FULL || i + 1 < npair)) {
             __builtin_amdgcn_s_setprio(3);
             scores(i + 1, std::integral_constant<bool, FULL && X == 0>{});
             __builtin_amdgcn_s_setprio(0);
         }
+        if constexpr (kPvPrio != 0) __builtin_amdgcn_s_setprio(kPvPrio);
         values(i, full);
+        if constexpr (kPvPrio != 0) __builtin_amdgcn_s_setprio(0);
         tp0 = tn0;
         tp1 = tn1;
         // keep the next iteration's table wait behind this iteration's work
