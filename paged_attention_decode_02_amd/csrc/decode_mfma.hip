@@ -470,6 +470,8 @@ __global__ __launch_bounds__(64 * kW, (mfma_min_waves<KVT, D, NT, QS>())) void d
     // INNER: the pair lies wholly before the partition's end and before every
     // valid row's causal limit, so only invalid rows need masking
     auto scores = [&](int i, auto inner) {
+        // bf16: the scheduler's MFMA / exp interleaving for the scores (measured)
+        if constexpr (KVT == KV_BF16) __builtin_amdgcn_iglp_opt(3);
         constexpr bool INNER = decltype(inner)::value;
         const int stage = i & 1;
         const int jp = j0 + 2 * i;
@@ -575,6 +577,8 @@ __global__ __launch_bounds__(64 * kW, (mfma_min_waves<KVT, D, NT, QS>())) void d
 
     // PV of pair i (all waves): weights and values from LDS stage i % 2
     auto values = [&](int i, auto inner) {
+        // quantised caches: the scheduler's LDS-read / MFMA interleaving for the PV (measured)
+        if constexpr (QNT) __builtin_amdgcn_iglp_opt(0);
         constexpr bool INNER = decltype(inner)::value;
         const int stage = i & 1;
         const int jp = j0 + 2 * i;
