@@ -224,6 +224,37 @@ def test_permuted_table_and_reruns_are_bitwise_identical():
     assert torch.equal(a, c2) and torch.equal(la, l2)
 
 
+@pytest.mark.parametrize("kv, Tq, G", [("i8", 1, 6), ("fp8", 1, 6), ("nvfp4", 1, 6), ("bf16", 8, 6), ("i8", 8, 6),
+                                       ("fp8", 8, 6), ("nvfp4", 8, 6), ("f32", 1, 4), ("bf16", 1, 4)])
+def test_every_kernel_is_deterministic_and_placement_independent(kv, Tq, G):
+    # each decode kernel (streaming, tiled, fp32, vector ALU) gives the same
+    # bits on reruns and with its blocks moved to other places in the pool
+    spec = scaled("verify_bf16", name="determinism_%s_T%d" % (kv, Tq), B=3, Tq=Tq, Hq=2 * G, Hkv=2, D=128,
+                  seq_lens=(Tq, 2500), shared_prefix=0, cache_dtype=kv, src_dtype="f32",
+                  q_dtype="f32" if kv == "f32" else "bf16", peaked_frac=0.01)
+    w = generate(spec, seed=31 + Tq + G, seq_lens=[Tq, 1300, 2500])
+    cache = gpu_cache(w)
+    a, la = gpu_decode(w, cache, 128)
+    for _ in range(3):
+        b, lb = gpu_decode(w, cache, 128)
+        assert torch.equal(a, b) and torch.equal(la, lb)
+    perm = torch.from_numpy(np.random.default_rng(9).permutation(w.num_blocks)).to(dev())
+    moved = []
+    for c in cache:
+        if c is None:
+            moved.append(None)
+            continue
+        m = torch.empty_like(c)
+        if c.dtype in (torch.float8_e4m3fn, torch.float4_e2m1fn_x2):  # byte codes: move the bytes
+            m.view(torch.uint8)[perm] = c.view(torch.uint8)
+        else:
+            m[perm] = c
+        moved.append(m)
+    w.block_table = perm.cpu().numpy()[w.block_table].astype(np.int32)
+    c2, l2 = gpu_decode(w, tuple(moved), 128)
+    assert torch.equal(a, c2) and torch.equal(la, l2)
+
+
 def test_splitk_reduce_entry_point_matches_decode():
     """decode_partials + splitk_reduce called separately give decode()'s bits."""
     spec = scaled("gqa_bf16", B=2, Tq=2, Hq=8, Hkv=2, D=128, seq_lens=(500, 1500))
