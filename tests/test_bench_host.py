@@ -174,3 +174,28 @@ def test_trace_summary_places_phases_after_any_number_of_settle_steps(tmp_path):
                        ("graph replays, one step per graph", 176.0), ("graph replays, ten steps per graph", 165.0)):
         assert "| %s | 50 | %.2f | %.2f |" % (label, dur, dur) in md, label
     assert "decode_mean_us_roofline_launches: 162.00" in md
+
+
+def test_sq_summary_normalises_per_block_and_skips_other_kernels(tmp_path):
+    # two counter passes of a synthetic rocprofv3 CSV: two decode dispatches
+    # per counter (their mean is reported), a reduce dispatch that must be
+    # ignored; per-block values divide by the workload's (16-token block, kv
+    # head) pairs
+    w = generate(SPECS["verify_i8"])
+    blocks = int(((w.seq_lens.astype(np.int64) + 15) // 16).sum()) * w.spec.Hkv
+    a, b = tmp_path / "a.csv", tmp_path / "b.csv"
+    hdr = "Kernel_Name,Counter_Name,Counter_Value\n"
+    # kernel names hold commas: quoted, as rocprofv3 writes them
+    a.write_text(hdr + "".join('"pa::decode_mfma_kernel<2, 256, 3, 1>(pa::DecodeParams)",%s,%d\n' % (n, v)
+                               for n, vals in (("SQ_WAVE_CYCLES", (1000 * blocks, 3000 * blocks)),
+                                               ("SQ_INSTS_VALU", (500 * blocks, 500 * blocks)))
+                               for v in vals)
+                 + '"pa::splitk_reduce_rows_kernel<256>(pa::ReduceParams)",SQ_INSTS_VALU,999999999\n')
+    b.write_text(hdr + "".join('"pa::decode_mfma_kernel<2, 256, 3, 1>(pa::DecodeParams)",SQ_WAIT_ANY,%d\n' % v
+                               for v in (800 * blocks, 800 * blocks)))
+    md = bench.summarize_sq([("k", "decode_mfma_kernel", [str(a), str(b)], ["cmd a", "cmd b"])], "verify_i8")
+    assert "| SQ_WAVE_CYCLES | %d | 2000.0 |" % (2000 * blocks) in md
+    assert "| SQ_INSTS_VALU | %d | 500.0 |" % (500 * blocks) in md
+    assert "| SQ_INSTS_MFMA | — | — |" in md  # not collected
+    assert "waiting 40% of wave time" in md  # 800 / 2000
+    assert "    cmd a" in md and "    cmd b" in md
